@@ -44,7 +44,9 @@
  *               Jacobian, gl_k = m_k * (gm_k - sum_j m_j gm_j).
  *
  * Non-finite values: a NaN offset makes that sample NaN; an infinite offset
- * puts the sample outside the map, so it contributes 0.  Arithmetic is fp64
+ * puts the sample outside the map, where B = 0, so it contributes m_k * 0
+ * (0 for a finite m_k, NaN for a NaN or infinite one, as IEEE arithmetic
+ * evaluates the definition).  Arithmetic is fp64
  * throughout; inputs given in 16-bit or fp32 are widened exactly by the
  * caller.
  */
@@ -160,8 +162,11 @@ static void forward_pixel(const ref_problem *p, int64_t Ho, int64_t Wo, const do
                     yrow[g * Cg + c] = NAN;
                 continue;
             }
-            if (st == 0)
+            if (st == 0) { /* B = 0 for a sample infinitely far away */
+                for (int64_t c = 0; c < Cg; ++c)
+                    yrow[g * Cg + c] += m[k] * 0.0;
                 continue;
+            }
             for (int64_t c = 0; c < Cg; ++c) {
                 double b = 0.0;
                 for (int a = 0; a < 2; ++a)
@@ -233,8 +238,11 @@ void ref_backward(const ref_problem *p, const double *x, const double *off, cons
                             gm[k] = go[0] = go[1] = NAN;
                             continue;
                         }
-                        if (st == 0)
+                        if (st == 0) { /* B = 0 and dB = 0 far away */
+                            go[0] = s * m[k] * 0.0;
+                            go[1] = s * m[k] * 0.0;
                             continue;
+                        }
                         /* d(1-|py-yc|)/dpy: -1 for yc = y0, +1 for yc = y0+1
                          * (one-sided from the right at integers). */
                         const double dsy[2] = {-1.0, 1.0}, dsx[2] = {-1.0, 1.0};
