@@ -1,0 +1,190 @@
+// dcn_api.hip -- the C ABI declared in include/dcn.h: problem validation,
+// splitting a batch into launchable chunks of images, and the launches.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "dcn_launch.hpp"
+
+namespace {
+
+thread_local char g_hip_message[256] = "HIP error";
+
+constexpr int64_t kMaxBytes31 = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxExtent = int64_t(1) << 24;
+
+int64_t out_extent(int64_t in, int64_t k, int64_t stride, int64_t pad, int64_t dil) {
+  const int64_t span = in + 2 * pad - dil * (k - 1) - 1;
+  return span < 0 ? 0 : span / stride + 1;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == DCN_F32 ? 4 : 2; }
+
+// Every check of dcn_check, in a fixed order; fills ho/wo on success.
+int validate(const dcn_problem *p, int64_t *ho_out, int64_t *wo_out) {
+  if (!p) return DCN_ERR_NULL;
+  if (p->struct_size != sizeof(dcn_problem)) return DCN_ERR_ABI;
+  if (p->n < 0 || p->h <= 0 || p->w <= 0 || p->c <= 0 || p->groups <= 0) return DCN_ERR_SHAPE;
+  if (p->c % p->groups != 0) return DCN_ERR_SHAPE;
+  if (p->kernel_h <= 0 || p->kernel_w <= 0 || p->stride_h <= 0 || p->stride_w <= 0 ||
+      p->dilation_h <= 0 || p->dilation_w <= 0 || p->pad_h < 0 || p->pad_w < 0)
+    return DCN_ERR_SHAPE;
+  if (p->softmax != 0 && p->softmax != 1) return DCN_ERR_ARG;
+  if (!isfinite(p->offset_scale)) return DCN_ERR_ARG;
+  if (p->h > kMaxExtent || p->w > kMaxExtent || p->pad_h > kMaxExtent || p->pad_w > kMaxExtent ||
+      (int64_t)p->dilation_h * p->kernel_h > kMaxExtent ||
+      (int64_t)p->dilation_w * p->kernel_w > kMaxExtent)
+    return DCN_ERR_TOO_LARGE;
+  const int64_t ho = out_extent(p->h, p->kernel_h, p->stride_h, p->pad_h, p->dilation_h);
+  const int64_t wo = out_extent(p->w, p->kernel_w, p->stride_w, p->pad_w, p->dilation_w);
+  if (ho < 1 || wo < 1) return DCN_ERR_SHAPE;
+  if (p->dtype != DCN_F32 && p->dtype != DCN_F16 && p->dtype != DCN_BF16) return DCN_ERR_UNSUPPORTED;
+  if (p->c / p->groups != dcn::kGroupChannels) return DCN_ERR_UNSUPPORTED;
+  if ((int64_t)p->kernel_h * p->kernel_w > dcn::kMaxPoints) return DCN_ERR_UNSUPPORTED;
+  const int64_t img_bytes = (int64_t)p->h * p->w * p->c * elem_bytes(p->dtype);
+  const int64_t img_pg = ho * wo * p->groups;
+  if (img_bytes > kMaxBytes31 || img_pg * dcn::kGroupChannels > kMaxBytes31) return DCN_ERR_TOO_LARGE;
+  if (ho_out) *ho_out = ho;
+  if (wo_out) *wo_out = wo;
+  return DCN_OK;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int hip_fail(hipError_t e) {
+  snprintf(g_hip_message, sizeof(g_hip_message), "HIP error %d: %s", (int)e, hipGetErrorString(e));
+  return DCN_ERR_HIP;
+}
+
+// Geometry shared by every chunk of one call; the caller fills the pointers.
+dcn::FwdParams geometry(const dcn_problem *p, int64_t ho, int64_t wo) {
+  dcn::FwdParams f{};
+  f.H = p->h;
+  f.W = p->w;
+  f.C = p->c;
+  f.G = p->groups;
+  f.Ho = (int32_t)ho;
+  f.Wo = (int32_t)wo;
+  f.KH = p->kernel_h;
+  f.KW = p->kernel_w;
+  f.SH = p->stride_h;
+  f.SW = p->stride_w;
+  f.PH = p->pad_h;
+  f.PW = p->pad_w;
+  f.DH = p->dilation_h;
+  f.DW = p->dilation_w;
+  f.scale = p->offset_scale;
+  f.div_g = dcn::make_fast_div((uint32_t)p->groups);
+  f.div_wo = dcn::make_fast_div((uint32_t)wo);
+  f.div_ho = dcn::make_fast_div((uint32_t)ho);
+  return f;
+}
+
+// Images per launch: every chunk keeps its input below 2^31 bytes and its
+// pixel-group count (times 16) below 2^31, the reach of 32-bit offsets.
+int64_t images_per_chunk(const dcn_problem *p, int64_t ho, int64_t wo) {
+  const int64_t img_bytes = (int64_t)p->h * p->w * p->c * elem_bytes(p->dtype);
+  const int64_t img_pg16 = ho * wo * p->groups * dcn::kGroupChannels;
+  int64_t per = kMaxBytes31 / img_bytes;
+  const int64_t per2 = kMaxBytes31 / img_pg16;
+  if (per2 < per) per = per2;
+  return per < 1 ? 1 : per;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dcn_abi_version(void) { return DCN_ABI_VERSION; }
+
+int dcn_check(const dcn_problem *p, int64_t *ho, int64_t *wo) { return validate(p, ho, wo); }
+
+int dcn_forward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
+                void *output, void *hip_stream) {
+  int64_t ho = 0, wo = 0;
+  const int st = validate(p, &ho, &wo);
+  if (st != DCN_OK) return st;
+  if (p->n == 0) return DCN_OK;
+  if (!input || !offset || !mask || !output) return DCN_ERR_NULL;
+  if (!aligned16(input) || !aligned16(offset) || !aligned16(mask) || !aligned16(output))
+    return DCN_ERR_ALIGN;
+
+  const int eb = elem_bytes(p->dtype);
+  const int64_t K = (int64_t)p->kernel_h * p->kernel_w;
+  const int64_t img_in = (int64_t)p->h * p->w * p->c * eb;
+  const int64_t img_pg = ho * wo * p->groups;
+  const int64_t per = images_per_chunk(p, ho, wo);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  dcn::FwdParams f = geometry(p, ho, wo);
+  for (int64_t n0 = 0; n0 < p->n; n0 += per) {
+    const int64_t nc = (p->n - n0 < per) ? p->n - n0 : per;
+    f.input = static_cast<const char *>(input) + n0 * img_in;
+    f.offset = static_cast<const char *>(offset) + n0 * img_pg * K * 2 * eb;
+    f.mask = static_cast<const char *>(mask) + n0 * img_pg * K * eb;
+    f.output = static_cast<char *>(output) + n0 * img_pg * dcn::kGroupChannels * eb;
+    f.in_bytes = (uint32_t)(nc * img_in);
+    f.pg_total = (uint32_t)(nc * img_pg);
+    const hipError_t e = dcn::launch_forward(p->dtype, p->softmax, f, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return DCN_OK;
+}
+
+int dcn_backward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
+                 const void *grad_output, void *grad_input, void *grad_offset, void *grad_mask,
+                 void *hip_stream) {
+  int64_t ho = 0, wo = 0;
+  const int st = validate(p, &ho, &wo);
+  if (st != DCN_OK) return st;
+  if (p->dtype != DCN_F32) return DCN_ERR_UNSUPPORTED;
+  if (p->n == 0) return DCN_OK;
+  if (!input || !offset || !mask || !grad_output || !grad_input || !grad_offset || !grad_mask)
+    return DCN_ERR_NULL;
+  if (!aligned16(input) || !aligned16(offset) || !aligned16(mask) || !aligned16(grad_output) ||
+      !aligned16(grad_input) || !aligned16(grad_offset) || !aligned16(grad_mask))
+    return DCN_ERR_ALIGN;
+
+  const int64_t K = (int64_t)p->kernel_h * p->kernel_w;
+  const int64_t img_in = (int64_t)p->h * p->w * p->c * 4;
+  const int64_t img_pg = ho * wo * p->groups;
+  const int64_t per = images_per_chunk(p, ho, wo);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+
+  hipError_t e = dcn::launch_zero(grad_input, (uint64_t)(p->n * img_in), stream);
+  if (e != hipSuccess) return hip_fail(e);
+  dcn::BwdParams b{};
+  b.f = geometry(p, ho, wo);
+  for (int64_t n0 = 0; n0 < p->n; n0 += per) {
+    const int64_t nc = (p->n - n0 < per) ? p->n - n0 : per;
+    b.f.input = static_cast<const char *>(input) + n0 * img_in;
+    b.f.offset = static_cast<const float *>(offset) + n0 * img_pg * K * 2;
+    b.f.mask = static_cast<const float *>(mask) + n0 * img_pg * K;
+    b.f.output = nullptr;
+    b.f.in_bytes = (uint32_t)(nc * img_in);
+    b.f.pg_total = (uint32_t)(nc * img_pg);
+    b.grad_out = static_cast<const float *>(grad_output) + n0 * img_pg * dcn::kGroupChannels;
+    b.grad_in = static_cast<char *>(grad_input) + n0 * img_in;
+    b.grad_offset = static_cast<float *>(grad_offset) + n0 * img_pg * K * 2;
+    b.grad_mask = static_cast<float *>(grad_mask) + n0 * img_pg * K;
+    e = dcn::launch_backward(p->softmax, b, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return DCN_OK;
+}
+
+const char *dcn_status_string(int status) {
+  switch (status) {
+    case DCN_OK: return "ok";
+    case DCN_ERR_NULL: return "null pointer for a problem or a non-empty tensor";
+    case DCN_ERR_SHAPE: return "invalid shape (dims, C % groups, kernel/stride/dilation/pad, or empty output)";
+    case DCN_ERR_UNSUPPORTED: return "unsupported dtype, channels per group, point count, or 16-bit backward";
+    case DCN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case DCN_ERR_TOO_LARGE: return "a size exceeds the 32-bit index range of one image";
+    case DCN_ERR_HIP: return g_hip_message;
+    case DCN_ERR_ABI: return "dcn_problem.struct_size does not match this library";
+    case DCN_ERR_ARG: return "invalid argument value (softmax flag or offset_scale)";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+// dcn_backward.hip -- gfx950 backward kernel of the DCNv3/DCNv4 sampling core
+// (fp32), plus the fill kernel that clears grad_input before the scatter.
+//
+// Derivatives of the forward (wmrh.cn/news/61976, section 二 steps 2-4):
+//   out_c = sum_k m_k * B_k[c],  B_k[c] = sum over the 4 corners of
+//           (1-|py-yc|)(1-|px-xc|) X[yc, xc, c]  (zero outside the map)
+//   grad_input  : every in-map corner receives m_k * w_corner * gy_c
+//                 (scattered with fp32 atomics: many samples hit one pixel);
+//   grad_offset : s * m_k * sum_c gy_c * dB_k[c]/d(px, py), stored (x, y);
+//                 dB/dpy = sum_xc wx * (X[y0+1, xc] - X[y0, xc]) and likewise
+//                 for px (one-sided from the right at integer coordinates);
+//   grad_mask   : gm_k = sum_c gy_c * B_k[c], then through the softmax
+//                 Jacobian, gl_k = m_k * (gm_k - sum_j m_j gm_j), for DCNv3.
+//
+// Mapping: a quad of lanes per pixel-group, 4 contiguous channels per lane
+// (16-byte corner loads and grad_out loads).  The three per-point channel sums
+// are reduced across the quad with two DPP quad permutes.  The grad_input
+// scatter uses raw buffer atomics: a corner outside the map carries a byte
+// offset beyond the buffer, and the hardware drops that atomic.
+#include "dcn_device.hpp"
+
+namespace dcn {
+
+namespace {
+
+constexpr int kQuad = 4;
+
+// Sum of v over the 4 lanes of a quad (DPP quad_perm [1,0,3,2] then [2,3,0,1]).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  return v;
+}
+
+}  // namespace
+
+template <int KH_, int KW_, bool SOFTMAX>
+__global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
+  const FwdParams &p = bp.f;
+  constexpr int CG = kGroupChannels;
+  constexpr int CPL = CG / kQuad;
+  constexpr int BLOCK_PG = kBlock / kQuad;
+  constexpr bool FIXED = KH_ > 0;
+  const int KH = FIXED ? KH_ : p.KH;
+  const int KW = FIXED ? KW_ : p.KW;
+  const int K = KH * KW;
+
+  extern __shared__ __align__(16) unsigned char lds[];
+  float *lds_off = reinterpret_cast<float *>(lds);
+  float *lds_mask = lds_off + BLOCK_PG * K * 2;
+  float *lds_gm = lds_mask + BLOCK_PG * K;
+
+  const uint32_t blk = xcd_block(blockIdx.x, gridDim.x);
+  const uint32_t pg0 = blk * BLOCK_PG;
+  const uint32_t npg = min((uint32_t)BLOCK_PG, p.pg_total - pg0);
+  stage_to_lds(lds_off, static_cast<const float *>(p.offset) + (uint64_t)pg0 * K * 2, npg * K * 8);
+  stage_to_lds(lds_mask, static_cast<const float *>(p.mask) + (uint64_t)pg0 * K, npg * K * 4);
+  __syncthreads();
+
+  const uint32_t lp = threadIdx.x / kQuad;
+  const uint32_t sub = threadIdx.x % kQuad;
+  // Whole quads leave together, so the DPP partners of a live lane are live.
+  if (lp >= npg) return;
+  const uint32_t pg = pg0 + lp;
+
+  const uint32_t pix = fast_div(pg, p.div_g);
+  const uint32_t g = pg - pix * (uint32_t)p.G;
+  const uint32_t t = fast_div(pix, p.div_wo);
+  const uint32_t wo = pix - t * (uint32_t)p.Wo;
+  const uint32_t n = fast_div(t, p.div_ho);
+  const uint32_t ho = t - n * (uint32_t)p.Ho;
+
+  const uint32_t mrow = lp * K;
+  float mx = 0.f, inv = 1.f;
+  if constexpr (SOFTMAX) {
+    mx = -INFINITY;
+    for (int k = 0; k < K; ++k) mx = fmaxf(mx, lds_mask[mrow + k]);
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) sum += __expf(lds_mask[mrow + k] - mx);
+    inv = __builtin_amdgcn_rcpf(sum);
+  }
+  auto weight = [&](int k) -> float {
+    if constexpr (SOFTMAX) return __expf(lds_mask[mrow + k] - mx) * inv;
+    else return lds_mask[mrow + k];
+  };
+
+  const float4 gy4 = *reinterpret_cast<const float4 *>(static_cast<const float *>(bp.grad_out) +
+                                                       (uint64_t)pg * CG + sub * CPL);
+  const float gy[CPL] = {gy4.x, gy4.y, gy4.z, gy4.w};
+
+  constexpr uint32_t kBytes = 4;
+  const uint32_t pix_bytes = (uint32_t)p.C * kBytes;
+  const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
+  const uint32_t base = n * (uint32_t)p.H * row_bytes + (g * CG + sub * CPL) * kBytes;
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
+  const __amdgpu_buffer_rsrc_t rgx = make_rsrc(bp.grad_in, p.in_bytes);
+  const int by = (int)ho * p.SH - p.PH;
+  const int bx = (int)wo * p.SW - p.PW;
+  const float s = p.scale;
+  float2 *goff = static_cast<float2 *>(bp.grad_offset) + (uint64_t)pg * K;
+
+  auto point = [&](const int ii, const int jj) {
+    const int k = ii * KW + jj;
+    const float dx = s * lds_off[(mrow + k) * 2];
+    const float dy = s * lds_off[(mrow + k) * 2 + 1];
+    const bool nan_loc = (dx != dx) | (dy != dy);
+    // Clamp first (|s*offset| >= 2^24 is far outside any map, and an infinite
+    // offset must not turn the fraction into Inf - Inf), then split into an
+    // integer part and an exact fraction in [0, 1).
+    const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
+    const float cy = __builtin_amdgcn_fmed3f(dy, -16777216.f, 16777216.f);
+    const float fx = floorf(cx), fy = floorf(cy);
+    const float lx = cx - fx, ly = cy - fy;
+    const int x0 = bx + jj * p.DW + (int)fx;
+    const int y0 = by + ii * p.DH + (int)fy;
+    const float mk = weight(k);
+    const float hx = 1.f - lx, hy = 1.f - ly;
+
+    // A NaN location reads and scatters nothing (its gradients are NaN).
+    const bool vy0 = !nan_loc && (uint32_t)y0 < (uint32_t)p.H;
+    const bool vy1 = !nan_loc && (uint32_t)(y0 + 1) < (uint32_t)p.H;
+    const bool vx0 = (uint32_t)x0 < (uint32_t)p.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)p.W;
+    const uint32_t a00r = base + (uint32_t)y0 * row_bytes + (uint32_t)x0 * pix_bytes;
+    const uint32_t a00 = (vy0 && vx0) ? a00r : kOutOfRange;
+    const uint32_t a01 = (vy0 && vx1) ? a00r + pix_bytes : kOutOfRange;
+    const uint32_t a10 = (vy1 && vx0) ? a00r + row_bytes : kOutOfRange;
+    const uint32_t a11 = (vy1 && vx1) ? a00r + row_bytes + pix_bytes : kOutOfRange;
+
+    uint32_t q00[CPL], q01[CPL], q10[CPL], q11[CPL];
+    buffer_load_words<CPL>(rin, a00, q00);
+    buffer_load_words<CPL>(rin, a01, q01);
+    buffer_load_words<CPL>(rin, a10, q10);
+    buffer_load_words<CPL>(rin, a11, q11);
+
+    float gb = 0.f, gdy = 0.f, gdx = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float v00 = __uint_as_float(q00[c]), v01 = __uint_as_float(q01[c]);
+      const float v10 = __uint_as_float(q10[c]), v11 = __uint_as_float(q11[c]);
+      const float top = hx * v00 + lx * v01;   // row y0 along x
+      const float bot = hx * v10 + lx * v11;   // row y0+1 along x
+      gb = fmaf(gy[c], hy * top + ly * bot, gb);
+      gdy = fmaf(gy[c], bot - top, gdy);
+      gdx = fmaf(gy[c], hy * (v01 - v00) + ly * (v11 - v10), gdx);
+    }
+    gb = quad_sum(gb);
+    gdy = quad_sum(gdy);
+    gdx = quad_sum(gdx);
+    // After the quad sums every lane of the quad holds the same totals; each
+    // lane keeps gm_k in its pixel-group's LDS row (the same value from all
+    // four lanes), lane 0 writes the offset gradient.
+    lds_gm[mrow + k] = nan_loc ? __builtin_nanf("") : gb;
+    if (sub == 0) {
+      goff[k] = nan_loc ? make_float2(__builtin_nanf(""), __builtin_nanf(""))
+                        : make_float2(s * mk * gdx, s * mk * gdy);
+    }
+
+    // Scatter m_k * w_corner * gy_c into grad_input.
+    const float w00 = mk * hy * hx, w01 = mk * hy * lx, w10 = mk * ly * hx, w11 = mk * ly * lx;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w00 * gy[c], rgx, (int)(a00 + 4u * c), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w01 * gy[c], rgx, (int)(a01 + 4u * c), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w10 * gy[c], rgx, (int)(a10 + 4u * c), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w11 * gy[c], rgx, (int)(a11 + 4u * c), 0, 0);
+    }
+  };
+  if constexpr (FIXED) {
+#pragma unroll
+    for (int ii = 0; ii < KH_; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < KW_; ++jj) point(ii, jj);
+  } else {
+    for (int ii = 0; ii < KH; ++ii)
+      for (int jj = 0; jj < KW; ++jj) point(ii, jj);
+  }
+
+  // grad_mask: raw gm_k for DCNv4, through the softmax Jacobian for DCNv3.
+  // Lane `sub` of the quad writes the points k = sub, sub+4, ...
+  float dot = 0.f;
+  if constexpr (SOFTMAX) {
+    for (int k = 0; k < K; ++k) dot = fmaf(weight(k), lds_gm[mrow + k], dot);
+  }
+  float *gmask = static_cast<float *>(bp.grad_mask) + (uint64_t)pg * K;
+  for (int k = sub; k < K; k += kQuad) {
+    const float gmk = lds_gm[mrow + k];
+    gmask[k] = SOFTMAX ? weight(k) * (gmk - dot) : gmk;
+  }
+}
+
+// Fill nbytes (a multiple of 16) at a 16-byte-aligned address with zeros.
+__global__ void __launch_bounds__(kBlock) dcn_zero_kernel(uint4 *dst, uint64_t n16) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = make_uint4(0, 0, 0, 0);
+}
+
+namespace {
+
+template <int KH, int KW, bool SM>
+hipError_t launch_one(const BwdParams &p, hipStream_t s) {
+  constexpr int BLOCK_PG = kBlock / kQuad;
+  const int K = p.f.KH * p.f.KW;
+  const size_t lds = (size_t)BLOCK_PG * K * 4 * sizeof(float);
+  const uint32_t blocks = (p.f.pg_total + BLOCK_PG - 1) / BLOCK_PG;
+  hipLaunchKernelGGL((dcn_bwd_kernel<KH, KW, SM>), dim3(blocks), dim3(kBlock), lds, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s) {
+  if (p.f.KH == 3 && p.f.KW == 3)
+    return softmax ? launch_one<3, 3, true>(p, s) : launch_one<3, 3, false>(p, s);
+  return softmax ? launch_one<0, 0, true>(p, s) : launch_one<0, 0, false>(p, s);
+}
+
+hipError_t launch_zero(void *dst, uint64_t bytes, hipStream_t s) {
+  const uint64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  uint64_t blocks = (n16 + kBlock - 1) / kBlock;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(dcn_zero_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, s,
+                     static_cast<uint4 *>(dst), n16);
+  return hipGetLastError();
+}
+
+}  // namespace dcn

@@ -1,0 +1,147 @@
+// dcn_device.hpp -- device-side building blocks shared by the forward and
+// backward kernels of the DCN core (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dcn_launch.hpp"
+
+namespace dcn {
+
+// ---------------------------------------------------------------- raw buffers
+// A raw buffer resource (stride 0, num_records in bytes).  Loads whose byte
+// offset lies beyond num_records return 0 and stores/atomics there are
+// dropped by the hardware, which is how corners outside the feature map are
+// read as zero without a branch: their offset is set to kOutOfRange.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw-buffer format word
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
+// Load NW 32-bit words (NW in {1, 2, 4, 8, 16}) at byte offset voff.
+template <int NW>
+__device__ __forceinline__ void buffer_load_words(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                  uint32_t (&w)[NW]) {
+  if constexpr (NW == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+  } else if constexpr (NW == 2) {
+    auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+  } else {
+    static_assert(NW % 4 == 0, "word count");
+#pragma unroll
+    for (int q = 0; q < NW / 4; ++q) {
+      auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 16u * q), 0, 0);
+      w[4 * q + 0] = v[0];
+      w[4 * q + 1] = v[1];
+      w[4 * q + 2] = v[2];
+      w[4 * q + 3] = v[3];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- I/O types
+template <int DT> struct Io;
+template <> struct Io<DCN_F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerWord = 1;
+  __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w); }
+  __device__ static __forceinline__ float one(const void *p, int64_t i) {
+    return static_cast<const float *>(p)[i];
+  }
+};
+template <> struct Io<DCN_F16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerWord = 2;
+  __device__ static __forceinline__ float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  __device__ static __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+  __device__ static __forceinline__ float one(const void *p, int64_t i) {
+    return (float)static_cast<const _Float16 *>(p)[i];
+  }
+  __device__ static __forceinline__ uint32_t pack(float a, float b) {
+    uint32_t l = __builtin_bit_cast(uint16_t, (_Float16)a);
+    uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)b);
+    return l | (h << 16);
+  }
+};
+template <> struct Io<DCN_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerWord = 2;
+  __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static __forceinline__ float one(const void *p, int64_t i) {
+    return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
+  }
+  __device__ static __forceinline__ uint32_t pack(float a, float b) {
+    uint32_t l = __builtin_bit_cast(uint16_t, (__bf16)a);
+    uint32_t h = __builtin_bit_cast(uint16_t, (__bf16)b);
+    return l | (h << 16);
+  }
+};
+
+// Widen NW words into NW * kPerWord floats.
+template <int DT, int NW>
+__device__ __forceinline__ void unpack(const uint32_t (&w)[NW], float (&v)[NW * Io<DT>::kPerWord]) {
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    if constexpr (DT == DCN_F32) {
+      v[i] = Io<DT>::lo(w[i]);
+    } else {
+      v[2 * i] = Io<DT>::lo(w[i]);
+      v[2 * i + 1] = Io<DT>::hi(w[i]);
+    }
+  }
+}
+
+// Narrow NV floats into NV / kPerWord words (round to nearest even).
+template <int DT, int NV>
+__device__ __forceinline__ void pack_words(const float (&v)[NV], uint32_t (&w)[NV / Io<DT>::kPerWord]) {
+#pragma unroll
+  for (int i = 0; i < NV / Io<DT>::kPerWord; ++i) {
+    if constexpr (DT == DCN_F32) {
+      w[i] = __float_as_uint(v[i]);
+    } else {
+      w[i] = Io<DT>::pack(v[2 * i], v[2 * i + 1]);
+    }
+  }
+}
+
+// Store NW words to a 16-byte-aligned global address (vector stores).
+template <int NW>
+__device__ __forceinline__ void store_words(void *dst, const uint32_t (&w)[NW]) {
+  if constexpr (NW == 1) {
+    *static_cast<uint32_t *>(dst) = w[0];
+  } else if constexpr (NW == 2) {
+    *static_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+  } else {
+    static_assert(NW % 4 == 0, "word count");
+#pragma unroll
+    for (int q = 0; q < NW / 4; ++q)
+      static_cast<uint4 *>(dst)[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+  }
+}
+
+// Copy nbytes (a multiple of 2) from 16-byte-aligned global memory into LDS,
+// with the whole block cooperating.  16-byte vector copies for the bulk,
+// 2-byte copies for the tail.
+__device__ __forceinline__ void stage_to_lds(void *lds, const void *src, uint32_t nbytes) {
+  const uint32_t n16 = nbytes / 16;
+  const uint4 *s4 = static_cast<const uint4 *>(src);
+  uint4 *d4 = static_cast<uint4 *>(lds);
+  for (uint32_t i = threadIdx.x; i < n16; i += blockDim.x) d4[i] = s4[i];
+  const uint32_t done = n16 * 16;
+  const uint16_t *s2 = static_cast<const uint16_t *>(src);
+  uint16_t *d2 = static_cast<uint16_t *>(lds);
+  for (uint32_t i = done / 2 + threadIdx.x; i < nbytes / 2; i += blockDim.x) d2[i] = s2[i];
+}
+
+}  // namespace dcn

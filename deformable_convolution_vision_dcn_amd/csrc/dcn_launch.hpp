@@ -1,0 +1,44 @@
+// dcn_launch.hpp -- the library's internal interface between the C ABI
+// (validation, chunking) and the kernels.  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dcn.h"
+#include "index_math.hpp"
+
+namespace dcn {
+
+constexpr int kGroupChannels = 16;  // channels per group with a kernel
+constexpr int kMaxPoints = 64;      // kernel_h * kernel_w upper bound
+constexpr int kBlock = 256;         // threads per block of every kernel
+
+// One launch covers a chunk of whole images whose input stays below 2^31
+// bytes, so every corner address fits a 32-bit buffer offset.
+struct FwdParams {
+  const void *input;   // chunk's first image
+  const void *offset;
+  const void *mask;
+  void *output;
+  uint32_t in_bytes;   // bytes of the chunk's input (buffer num_records)
+  uint32_t pg_total;   // pixel-groups (n, ho, wo, g) in the chunk
+  int32_t H, W, C, G, Ho, Wo;
+  int32_t KH, KW, SH, SW, PH, PW, DH, DW;
+  float scale;
+  FastDiv div_g, div_wo, div_ho;
+};
+
+struct BwdParams {
+  FwdParams f;             // input, offset, mask and geometry as in the forward
+  const void *grad_out;    // (chunk, Ho, Wo, C)
+  void *grad_in;           // (chunk, H, W, C), zeroed before the launch
+  void *grad_offset;       // (chunk, Ho, Wo, G, K, 2)
+  void *grad_mask;         // (chunk, Ho, Wo, G, K)
+};
+
+hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_t s);
+hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s);
+hipError_t launch_zero(void *dst, uint64_t bytes, hipStream_t s);
+
+}  // namespace dcn

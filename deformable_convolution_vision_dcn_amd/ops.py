@@ -1,0 +1,153 @@
+"""torch-tensor entry points with the C ABI's names.
+
+Marshalling only: shapes, dtypes, devices and contiguity are checked here (the
+C ABI receives bare pointers and cannot see extents), outputs are allocated
+with torch, and the call is enqueued on torch's current stream of the
+tensors' device.  Every step of the operation runs in the HIP library.
+
+Operation and layouts: see include/dcn.h (the DCNv3/DCNv4 sampling core of
+wmrh.cn/news/61976 section 二 and pnsm.cn/news/2029644.html section 2).
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _capi
+
+_DTYPES = {torch.float32: _capi.DCN_F32, torch.float16: _capi.DCN_F16,
+           torch.bfloat16: _capi.DCN_BF16}
+
+
+def _pair(v) -> Tuple[int, int]:
+    if isinstance(v, (tuple, list)):
+        return int(v[0]), int(v[1])
+    return int(v), int(v)
+
+
+def make_problem(x_shape, *, groups, kernel=3, stride=1, pad=1, dilation=1, offset_scale=2.0,
+                 softmax=True, dtype=torch.float32) -> _capi.dcn_problem:
+    """The dcn_problem of an (N, H, W, C) input and the operator's arguments."""
+    n, h, w, c = (int(v) for v in x_shape)
+    kh, kw = _pair(kernel)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    dh, dw = _pair(dilation)
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return _capi.make_problem(n=n, h=h, w=w, c=c, groups=int(groups), kernel_h=kh, kernel_w=kw,
+                              stride_h=sh, stride_w=sw, pad_h=ph, pad_w=pw, dilation_h=dh,
+                              dilation_w=dw, offset_scale=float(offset_scale),
+                              softmax=1 if softmax else 0, dtype=_DTYPES[dtype])
+
+
+def dcn_check(x_shape, **kw) -> Tuple[int, int]:
+    """Validate a problem in the library (host only); returns (Ho, Wo)."""
+    st, ho, wo = _capi.dcn_check(make_problem(x_shape, **kw))
+    _capi.raise_on(st)
+    return ho, wo
+
+
+def _expect(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shapes(x: torch.Tensor, groups, kernel, stride, pad, dilation, offset_scale, softmax):
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError("input must be a 4-D (N, H, W, C) tensor")
+    if x.device.type != "cuda":
+        raise ValueError("the DCN core runs on the GPU only: input must be a cuda tensor")
+    p = make_problem(x.shape, groups=groups, kernel=kernel, stride=stride, pad=pad,
+                     dilation=dilation, offset_scale=offset_scale, softmax=softmax, dtype=x.dtype)
+    st, ho, wo = _capi.dcn_check(p)
+    _capi.raise_on(st)
+    K = p.kernel_h * p.kernel_w
+    n = x.shape[0]
+    return p, {"offset": (n, ho, wo, groups, K, 2), "mask": (n, ho, wo, groups, K),
+               "out": (n, ho, wo, x.shape[3])}
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def dcn_forward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor, *, groups: int,
+                kernel=3, stride=1, pad=1, dilation=1, offset_scale: float = 2.0,
+                softmax: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Forward of the DCN core; returns (N, Ho, Wo, C) in x's dtype."""
+    p, shp = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax)
+    _expect(x, "input", x.shape, x.dtype, x.device)
+    _expect(offset, "offset", shp["offset"], x.dtype, x.device)
+    _expect(mask, "mask", shp["mask"], x.dtype, x.device)
+    if out is None:
+        out = torch.empty(shp["out"], dtype=x.dtype, device=x.device)
+    _expect(out, "out", shp["out"], x.dtype, x.device)
+    with torch.cuda.device(x.device):
+        st = _capi.dcn_forward(p, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
+                               out.data_ptr(), _stream(x.device))
+    _capi.raise_on(st)
+    return out
+
+
+def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
+                 grad_out: torch.Tensor, *, groups: int, kernel=3, stride=1, pad=1, dilation=1,
+                 offset_scale: float = 2.0, softmax: bool = True,
+                 grad_input: Optional[torch.Tensor] = None,
+                 grad_offset: Optional[torch.Tensor] = None,
+                 grad_mask: Optional[torch.Tensor] = None):
+    """Backward of the DCN core; returns (grad_input, grad_offset, grad_mask)."""
+    p, shp = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax)
+    _expect(x, "input", x.shape, x.dtype, x.device)
+    _expect(offset, "offset", shp["offset"], x.dtype, x.device)
+    _expect(mask, "mask", shp["mask"], x.dtype, x.device)
+    _expect(grad_out, "grad_out", shp["out"], x.dtype, x.device)
+    if grad_input is None:
+        grad_input = torch.empty_like(x)
+    if grad_offset is None:
+        grad_offset = torch.empty_like(offset)
+    if grad_mask is None:
+        grad_mask = torch.empty_like(mask)
+    _expect(grad_input, "grad_input", x.shape, x.dtype, x.device)
+    _expect(grad_offset, "grad_offset", shp["offset"], x.dtype, x.device)
+    _expect(grad_mask, "grad_mask", shp["mask"], x.dtype, x.device)
+    with torch.cuda.device(x.device):
+        st = _capi.dcn_backward(p, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
+                                grad_out.data_ptr(), grad_input.data_ptr(),
+                                grad_offset.data_ptr(), grad_mask.data_ptr(), _stream(x.device))
+    _capi.raise_on(st)
+    return grad_input, grad_offset, grad_mask
+
+
+class DCNCore(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run in the HIP library."""
+
+    @staticmethod
+    def forward(ctx, x, offset, mask, groups, kernel, stride, pad, dilation, offset_scale, softmax):
+        x, offset, mask = x.contiguous(), offset.contiguous(), mask.contiguous()
+        ctx.save_for_backward(x, offset, mask)
+        ctx.args = dict(groups=groups, kernel=kernel, stride=stride, pad=pad, dilation=dilation,
+                        offset_scale=offset_scale, softmax=softmax)
+        return dcn_forward(x, offset, mask, **ctx.args)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        x, offset, mask = ctx.saved_tensors
+        gx, goff, gm = dcn_backward(x, offset, mask, grad_out.contiguous(), **ctx.args)
+        return gx, goff, gm, None, None, None, None, None, None, None
+
+
+def dcn_core(x, offset, mask, *, groups, kernel=3, stride=1, pad=1, dilation=1,
+             offset_scale=2.0, softmax=True):
+    """Differentiable DCN core (fp32 backward)."""
+    return DCNCore.apply(x, offset, mask, groups, kernel, stride, pad, dilation, offset_scale,
+                         softmax)

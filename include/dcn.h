@@ -1,0 +1,125 @@
+/*
+ * dcn.h -- C ABI of the MI355X (gfx950) DCNv3/DCNv4 deformable-sampling core.
+ *
+ * The operation (defined on the page wmrh.cn/news/61976, "internimage_l_22k_384
+ * / DCNv3 core operator explained", section 二 steps 2-4 and section 三; the
+ * unnormalised DCNv4 variant and the NHWC layout on pnsm.cn/news/2029644.html,
+ * sections 2.2-2.3 and 3.3):
+ *
+ *   for every image n, output pixel (ho, wo), group g and kernel point
+ *   k = i*kernel_w + j (i along H, j along W):
+ *     py  = ho*stride_h - pad_h + i*dilation_h + offset_scale * offset[n,ho,wo,g,k,1]
+ *     px  = wo*stride_w - pad_w + j*dilation_w + offset_scale * offset[n,ho,wo,g,k,0]
+ *     m_k = softmax_k(mask[n,ho,wo,g,:])   if softmax != 0   (DCNv3)
+ *         = mask[n,ho,wo,g,k]              if softmax == 0   (DCNv4)
+ *     out[n,ho,wo,g*Cg+c] = sum_k m_k * bilinear(input[n,:,:,g*Cg+c], py, px)
+ *
+ *   bilinear() puts pixel centres at integer coordinates and reads zero outside
+ *   [0,H) x [0,W).  Ho = (H + 2*pad_h - dilation_h*(kernel_h-1) - 1)/stride_h + 1
+ *   (integer division; the same form gives Wo).  Cg = C / groups.
+ *
+ * Layouts (all tensors dense and contiguous, row-major, one dtype per call):
+ *   input        (N, H, W, C)                              NHWC
+ *   offset       (N, Ho, Wo, groups, kernel_h*kernel_w, 2) pair stored (x, y)
+ *   mask         (N, Ho, Wo, groups, kernel_h*kernel_w)    logits or weights
+ *   output       (N, Ho, Wo, C)                            NHWC
+ *   grad_*       the shape of the tensor it is the gradient of.
+ *
+ * Arithmetic: sampling locations, weights, the softmax and every accumulation
+ * are fp32 for every I/O dtype; 16-bit results are rounded to nearest-even.
+ *
+ * Ownership and execution: every tensor pointer is a DEVICE pointer owned by
+ * the caller.  The library allocates nothing, keeps no pointer after it
+ * returns and has no mutable global state, so calls are reentrant.  Work is
+ * enqueued on the caller's hipStream_t (NULL = the null stream) and the call
+ * returns without waiting: DCN_OK means "validated and enqueued".  Outputs are
+ * overwritten, never accumulated into, and must not alias any input.
+ *
+ * Errors: every entry point returns DCN_OK (0) or a negative dcn_status.
+ * Nothing is enqueued when a check fails.  N == 0 is valid and enqueues
+ * nothing.  There is no fallback path: an unsupported problem is an error.
+ */
+#ifndef DCN_MI355X_H
+#define DCN_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DCN_ABI_VERSION 1
+
+/* Element type of every tensor of one call. */
+typedef enum dcn_dtype {
+    DCN_F32 = 0,
+    DCN_F16 = 1,
+    DCN_BF16 = 2
+} dcn_dtype;
+
+typedef enum dcn_status {
+    DCN_OK = 0,
+    DCN_ERR_NULL = -1,        /* NULL problem, or NULL pointer for a non-empty tensor   */
+    DCN_ERR_SHAPE = -2,       /* a dim <= 0 (N may be 0), C % groups != 0, kernel,
+                                 stride or dilation < 1, pad < 0, or Ho/Wo < 1         */
+    DCN_ERR_UNSUPPORTED = -3, /* dtype, channels-per-group or point count without a
+                                 kernel, or a 16-bit backward                          */
+    DCN_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                */
+    DCN_ERR_TOO_LARGE = -5,   /* one image's input exceeds 2^31-1 bytes, H or W exceeds
+                                 2^24, or one image holds 2^31 or more pixel-groups    */
+    DCN_ERR_HIP = -6,         /* the HIP runtime refused a launch; see dcn_status_string */
+    DCN_ERR_ABI = -7,         /* problem->struct_size != sizeof(dcn_problem)            */
+    DCN_ERR_ARG = -8          /* softmax not 0/1, or offset_scale not finite            */
+} dcn_status;
+
+/* One problem description.  Set struct_size = sizeof(dcn_problem). */
+typedef struct dcn_problem {
+    uint32_t struct_size;
+    int32_t n, h, w, c, groups;
+    int32_t kernel_h, kernel_w;
+    int32_t stride_h, stride_w;
+    int32_t pad_h, pad_w;
+    int32_t dilation_h, dilation_w;
+    float offset_scale;   /* multiplies the learned offset only, not the grid   */
+    int32_t softmax;      /* 1 = DCNv3 (softmax over the points), 0 = DCNv4     */
+    int32_t dtype;        /* dcn_dtype                                          */
+} dcn_problem;
+
+/* Version of this ABI (DCN_ABI_VERSION of the built library). */
+int dcn_abi_version(void);
+
+/* Validate a problem on the host (no device call) and report the output
+ * extent.  ho / wo may be NULL.  Returns DCN_OK or the first failing check
+ * (also for problems that dcn_forward could not run: unsupported dtype,
+ * channels per group or point count, or sizes beyond the index width). */
+int dcn_check(const dcn_problem *p, int64_t *ho, int64_t *wo);
+
+/* Forward: output = DCN(input, offset, mask).  Enqueues one kernel launch per
+ * chunk of images (one chunk unless an image batch exceeds 2 GiB of input). */
+int dcn_forward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
+                void *output, void *hip_stream);
+
+/* Backward of the forward above for the gradient grad_output of output:
+ *   grad_input  = adjoint bilinear scatter of m_k * weight * grad_output
+ *                 (zeroed by the call itself, then accumulated with fp32
+ *                 atomics, so its low bits can vary from run to run),
+ *   grad_offset = offset_scale * m_k * sum_c grad_output_c * d(bilinear)/d(px, py),
+ *                 stored (x, y) like the offsets,
+ *   grad_mask   = gradient with respect to the mask tensor as passed: through
+ *                 the softmax Jacobian when softmax != 0.
+ * At integer sampling coordinates the derivative is the one-sided one from the
+ * right (the floor convention).  fp32 only (DCN_F32); other dtypes return
+ * DCN_ERR_UNSUPPORTED. */
+int dcn_backward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
+                 const void *grad_output, void *grad_input, void *grad_offset, void *grad_mask,
+                 void *hip_stream);
+
+/* Static description of a status code.  For DCN_ERR_HIP the string carries
+ * the HIP runtime's message from the calling thread's most recent failure. */
+const char *dcn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCN_MI355X_H */

@@ -1,0 +1,322 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Bars (the stated parity tolerances of this operator):
+  fp32            max |gpu - oracle| <= 1e-4, forward and backward;
+  bf16 / fp16     relative error 2e-2, checked elementwise as
+                  |gpu - oracle| <= 2e-2 * |oracle| + 1e-3 (an absolute floor
+                  for outputs near zero, where a pure ratio is ill-posed).
+The oracle sees exactly the values the GPU sees (16-bit inputs widened
+exactly) and is not rounded to the I/O dtype.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import deformable_convolution_vision_dcn_amd as dcn
+import oracle
+from deformable_convolution_vision_dcn_amd import synth
+from deformable_convolution_vision_dcn_amd.synth import Workload, normal, uniform
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+ATOL_F32 = 1e-4
+RTOL_16, ATOL_16 = 2e-2, 1e-3
+
+
+def _np(t):
+    return t.detach().cpu().double().numpy()
+
+
+def gate(got, ref, dtype, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    nan_ref, nan_got = np.isnan(ref), np.isnan(got)
+    assert np.array_equal(nan_ref, nan_got), f"{what}: NaN pattern differs"
+    g, r = got[~nan_ref], ref[~nan_ref]
+    if g.size == 0:
+        return
+    err = np.abs(g - r)
+    if dtype == "f32":
+        assert err.max() <= ATOL_F32, f"{what}: max abs error {err.max():.3e} > {ATOL_F32}"
+    else:
+        bound = RTOL_16 * np.abs(r) + ATOL_16
+        worst = int(np.argmax(err - bound))
+        assert np.all(err <= bound), (f"{what}: |gpu-ref| {err[worst]:.3e} > bound {bound[worst]:.3e}"
+                                      f" at ref {r[worst]:.4e}")
+
+
+def run_forward(wl, t):
+    x, off, m = (t[k].to(DEV) for k in ("x", "offset", "mask"))
+    y = dcn.dcn_forward(x, off, m, **wl.op_kwargs())
+    torch.cuda.synchronize()
+    return y
+
+
+def oracle_full(wl, t):
+    return oracle.forward(_np(t["x"]), _np(t["offset"]), _np(t["mask"]), **wl.op_kwargs())
+
+
+# --------------------------------------------------------------------------- forward, small
+
+SMALL = [
+    Workload("k3_ragged", n=2, h=13, w=11, c=48, groups=3, offset_dist=normal(2.0), seed=11),
+    Workload("k3_v4", n=2, h=13, w=11, c=48, groups=3, softmax=False, mask_dist=normal(0.5), seed=12),
+    Workload("k3_uniform3", n=3, h=9, w=10, c=32, groups=2, offset_dist=uniform(3.0), seed=13),
+    Workload("k3_stride2", n=2, h=15, w=17, c=32, groups=2, stride=(2, 2), pad=(1, 1), seed=14),
+    Workload("k3_dil2_pad2", n=1, h=12, w=14, c=64, groups=4, dilation=(2, 2), pad=(2, 2), seed=15),
+    Workload("k3_pad0_s1x2", n=2, h=10, w=12, c=16, groups=1, stride=(1, 2), pad=(0, 0), seed=16),
+    Workload("k5_generic", n=2, h=9, w=8, c=32, groups=2, kernel=(5, 5), pad=(2, 2), seed=17),
+    Workload("k3x5_generic_v4", n=1, h=8, w=11, c=48, groups=3, kernel=(3, 5), pad=(1, 2),
+             softmax=False, seed=18),
+    Workload("k1_generic", n=2, h=6, w=7, c=32, groups=2, kernel=(1, 1), pad=(0, 0), seed=19),
+    Workload("k7_generic_scale1p3", n=1, h=10, w=9, c=16, groups=1, kernel=(7, 7), pad=(3, 3),
+             offset_scale=1.3, seed=20),
+    Workload("one_pixel", n=1, h=1, w=1, c=16, groups=1, seed=21),
+    Workload("wide_many_groups", n=1, h=5, w=37, c=16 * 21, groups=21, seed=22),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_forward_small(wl, dtype):
+    wl = wl.replace(dtype=dtype)
+    print(f"forward {wl.name} {dtype}", flush=True)
+    t = synth.make_inputs(wl)
+    gate(_np(run_forward(wl, t)), oracle_full(wl, t), dtype, f"{wl.name}/{dtype}")
+
+
+# --------------------------------------------------------------------------- forward, full size
+
+def sampled_pixels(wl, count, seed=0):
+    ho, wo = wl.out_hw
+    total = wl.n * ho * wo
+    rng = np.random.default_rng(seed)
+    pix = set(rng.integers(0, total, size=min(count, total)).tolist())
+    for n in {0, wl.n - 1}:
+        for (h, w) in [(0, 0), (0, wo - 1), (ho - 1, 0), (ho - 1, wo - 1), (ho // 2, wo // 2)]:
+            pix.add((n * ho + h) * wo + w)
+    return np.array(sorted(pix), dtype=np.int64)
+
+
+def check_sampled(wl, t, y, pixels):
+    """Compare y (GPU, full) with the oracle at the given output pixels, one
+    image at a time so the oracle only widens that image's tensors."""
+    ho, wo = wl.out_hw
+    yn = y.view(-1, wl.c)
+    per_img = ho * wo
+    imgs = pixels // per_img
+    for n in np.unique(imgs):
+        sel = pixels[imgs == n]
+        sl = slice(int(n), int(n) + 1)
+        ref = oracle.forward_pixels(_np(t["x"][sl]), _np(t["offset"][sl]), _np(t["mask"][sl]),
+                                    sel - n * per_img, **wl.op_kwargs())
+        got = _np(yn[torch.from_numpy(sel).to(DEV)])
+        gate(got, ref, wl.dtype, f"{wl.name} image {n}")
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_named_workload_forward(name):
+    wl = synth.WORKLOADS[name]
+    print(f"forward {name} (full size)", flush=True)
+    t = synth.make_inputs(wl, with_grad=False)
+    y = run_forward(wl, t)
+    assert torch.isfinite(y).all()
+    if wl.samples <= 5_000_000:
+        gate(_np(y), oracle_full(wl, t), wl.dtype, name)
+    else:
+        check_sampled(wl, t, y, sampled_pixels(wl, 3000))
+
+
+def test_forward_multi_chunk():
+    """A batch whose input exceeds 2 GiB runs as several launches (chunks of
+    whole images); check pixels on both sides of the chunk boundary."""
+    wl = Workload("chunked", n=3, h=384, w=384, c=1280, groups=80, offset_dist=normal(1.5), seed=23)
+    assert wl.n * wl.h * wl.w * wl.c * 4 > 2 ** 31
+    print("forward chunked (3 x 384x384x1280 fp32)", flush=True)
+    t = synth.make_inputs(wl, with_grad=False)
+    y = run_forward(wl, t)
+    check_sampled(wl, t, y, sampled_pixels(wl, 600, seed=1))
+    del y, t
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- backward
+
+BWD = [
+    Workload("bwd_k3", n=2, h=13, w=11, c=48, groups=3, offset_dist=normal(2.0), seed=31),
+    Workload("bwd_k3_v4", n=2, h=12, w=10, c=32, groups=2, softmax=False, mask_dist=normal(0.5), seed=32),
+    Workload("bwd_k3_uniform3", n=1, h=9, w=10, c=32, groups=2, offset_dist=uniform(3.0), seed=33),
+    Workload("bwd_stride2_dil2", n=2, h=15, w=17, c=32, groups=2, stride=(2, 2), dilation=(2, 2),
+             pad=(2, 2), seed=34),
+    Workload("bwd_k5_generic", n=1, h=9, w=8, c=32, groups=2, kernel=(5, 5), pad=(2, 2), seed=35),
+    Workload("bwd_k3x5_generic_v4", n=1, h=8, w=11, c=16, groups=1, kernel=(3, 5), pad=(1, 2),
+             softmax=False, seed=36),
+    Workload("bwd_one_pixel", n=1, h=1, w=1, c=16, groups=1, seed=37),
+]
+
+
+def run_backward(wl, t):
+    x, off, m, gy = (t[k].to(DEV) for k in ("x", "offset", "mask", "grad_out"))
+    g = dcn.dcn_backward(x, off, m, gy, **wl.op_kwargs())
+    torch.cuda.synchronize()
+    return g
+
+
+def oracle_backward(wl, t):
+    return oracle.backward(_np(t["x"]), _np(t["offset"]), _np(t["mask"]), _np(t["grad_out"]),
+                           **wl.op_kwargs())
+
+
+@pytest.mark.parametrize("wl", BWD + [synth.WORKLOADS["hires_dcnv3_f32"], synth.WORKLOADS["tiny_dcnv3_f32"]],
+                         ids=lambda w: w.name)
+def test_backward(wl):
+    print(f"backward {wl.name}", flush=True)
+    t = synth.make_inputs(wl, with_grad=True)
+    gx, goff, gm = run_backward(wl, t)
+    rx, roff, rm = oracle_backward(wl, t)
+    gate(_np(gx), rx, "f32", f"{wl.name} grad_input")
+    gate(_np(goff), roff, "f32", f"{wl.name} grad_offset")
+    gate(_np(gm), rm, "f32", f"{wl.name} grad_mask")
+
+
+def test_backward_adjoint_at_stage1_size():
+    """At the stage-1 size (too big for a quick full oracle backward) the
+    grad_input is checked by the adjoint identity <F(x), g> = <x, F^T g>,
+    which holds at any size, and grad_offset / grad_mask on sampled rows."""
+    wl = synth.WORKLOADS["stage1_dcnv3_f32"].replace(backward=True)
+    print("backward stage1 (adjoint)", flush=True)
+    t = synth.make_inputs(wl, with_grad=True)
+    y = run_forward(wl, t)
+    gx, goff, gm = run_backward(wl, t)
+    x, gy = t["x"].to(DEV).double(), t["grad_out"].to(DEV).double()
+    terms = y.double() * gy
+    lhs = float(terms.sum())
+    rhs = float((x * gx.double()).sum())
+    # fp32 rounding of each term is ~1e-7 relative; bound by the sum of |terms|
+    assert abs(lhs - rhs) <= 1e-6 * float(terms.abs().sum()), (lhs, rhs)
+    # rows of image 0 and the last image, checked against the oracle on a
+    # one-image slice
+    for n in (0, wl.n - 1):
+        sl = slice(n, n + 1)
+        sub = {k: v[sl] for k, v in t.items()}
+        w1 = wl.replace(n=1)
+        rx, roff, rm = oracle_backward(w1, sub)
+        # grad_input of image n depends only on image n
+        gate(_np(gx[sl]), rx, "f32", f"stage1 grad_input image {n}")
+        gate(_np(goff[sl]), roff, "f32", f"stage1 grad_offset image {n}")
+        gate(_np(gm[sl]), rm, "f32", f"stage1 grad_mask image {n}")
+
+
+def test_autograd_function_matches_backward():
+    wl = BWD[0]
+    t = synth.make_inputs(wl, with_grad=True)
+    x, off, m, gy = (t[k].to(DEV).requires_grad_(k != "grad_out") for k in ("x", "offset", "mask", "grad_out"))
+    y = dcn.dcn_core(x, off, m, **wl.op_kwargs())
+    gx, goff, gm = torch.autograd.grad(y, (x, off, m), grad_outputs=gy)
+    rx, roff, rm = oracle_backward(wl, t)
+    gate(_np(gx), rx, "f32", "autograd grad_input")
+    gate(_np(goff), roff, "f32", "autograd grad_offset")
+    gate(_np(gm), rm, "f32", "autograd grad_mask")
+
+
+# --------------------------------------------------------------------------- edge cases
+
+def test_empty_batch():
+    x = torch.empty(0, 8, 8, 16, device=DEV)
+    off = torch.empty(0, 8, 8, 1, 9, 2, device=DEV)
+    m = torch.empty(0, 8, 8, 1, 9, device=DEV)
+    y = dcn.dcn_forward(x, off, m, groups=1)
+    assert y.shape == (0, 8, 8, 16)
+    gx, goff, gm = dcn.dcn_backward(x, off, m, torch.empty(0, 8, 8, 16, device=DEV), groups=1)
+    assert gx.shape == x.shape and goff.shape == off.shape and gm.shape == m.shape
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_far_offsets_give_exact_zeros(dtype):
+    wl = Workload("far", n=1, h=7, w=9, c=32, groups=2, dtype=dtype, seed=41)
+    t = synth.make_inputs(wl)
+    for big in (1e4, -1e4, float("inf"), -float("inf"), 3e38):
+        t["offset"] = torch.full_like(t["offset"], big)
+        y = run_forward(wl, t)
+        assert torch.all(y == 0), big
+
+
+def test_nan_offset_poisons_only_its_group():
+    wl = Workload("nan", n=1, h=6, w=5, c=32, groups=2, seed=42)
+    t = synth.make_inputs(wl, with_grad=True)
+    t["offset"][0, 2, 3, 1, 4, 0] = float("nan")
+    y = _np(run_forward(wl, t))
+    gate(y, oracle_full(wl, t), "f32", "nan offset forward")
+    assert np.isnan(y[0, 2, 3, 16:]).all() and np.isfinite(y).sum() == y.size - 16
+    gx, goff, gm = run_backward(wl, t)
+    rx, roff, rm = oracle_backward(wl, t)
+    gate(_np(gx), rx, "f32", "nan offset grad_input")
+    gate(_np(goff), roff, "f32", "nan offset grad_offset")
+    gate(_np(gm), rm, "f32", "nan offset grad_mask")
+
+
+def test_nan_input_propagates():
+    wl = Workload("nan_in", n=1, h=6, w=6, c=16, groups=1, seed=43)
+    t = synth.make_inputs(wl)
+    # integer s*offset = 0 everywhere: every sample hits pixel centres with
+    # weight exactly 1 at one corner, so the NaN reaches exactly the outputs
+    # whose 3x3 window covers it
+    t["offset"].zero_()
+    t["x"][0, 2, 3, 5] = float("nan")
+    y = _np(run_forward(wl, t))
+    ref = oracle_full(wl, t)
+    # corners with weight exactly 0 may or may not read the NaN: compare only
+    # where the oracle is finite, and require NaN where the oracle is NaN
+    assert np.all(np.isnan(y[np.isnan(ref)]))
+    fin = np.isfinite(ref) & np.isfinite(y)
+    assert np.abs(y[fin] - ref[fin]).max() <= ATOL_F32
+
+
+def test_integer_offsets_are_exact_gathers():
+    wl = Workload("int", n=2, h=11, w=9, c=32, groups=2, softmax=False, seed=44)
+    t = synth.make_inputs(wl)
+    rng = np.random.default_rng(5)
+    t["offset"] = torch.from_numpy((rng.integers(-3, 4, size=t["offset"].shape) / 2.0).astype(np.float32))
+    t["mask"] = torch.ones_like(t["mask"])
+    y = _np(run_forward(wl, t))
+    # with unit weights and pixel-centre samples the only rounding is the
+    # fp32 sum of 9 input values
+    assert np.abs(y - oracle_full(wl, t)).max() <= 4e-6
+
+
+def test_output_guard_bands_untouched():
+    wl = Workload("guard", n=2, h=9, w=7, c=48, groups=3, seed=45)
+    t = synth.make_inputs(wl)
+    x, off, m = (t[k].to(DEV) for k in ("x", "offset", "mask"))
+    numel = wl.n * wl.out_hw[0] * wl.out_hw[1] * wl.c
+    pad = 1024
+    buf = torch.full((numel + 2 * pad,), 12345.0, device=DEV)
+    out = buf[pad:pad + numel].view(wl.n, *wl.out_hw, wl.c)
+    dcn.dcn_forward(x, off, m, out=out, **wl.op_kwargs())
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[pad + numel:] == 12345.0)
+    gate(_np(out), oracle_full(wl, t), "f32", "guarded output")
+
+
+def test_forward_is_deterministic():
+    wl = synth.WORKLOADS["hires_dcnv3_f32"]
+    t = synth.make_inputs(wl, with_grad=False)
+    a = run_forward(wl, t)
+    b = run_forward(wl, t)
+    assert torch.equal(a, b)
+
+
+def test_runs_on_a_side_stream():
+    wl = SMALL[0]
+    t = synth.make_inputs(wl)
+    x, off, m = (t[k].to(DEV) for k in ("x", "offset", "mask"))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = dcn.dcn_forward(x, off, m, **wl.op_kwargs())
+    s.synchronize()
+    gate(_np(y), oracle_full(wl, t), "f32", "side stream")
