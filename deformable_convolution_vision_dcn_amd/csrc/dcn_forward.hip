@@ -208,6 +208,10 @@ hipError_t launch_dt(int softmax, const FwdParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
+#ifndef DCN_NO_TILED
+  const hipError_t t = launch_forward_tiled(dtype, softmax, p, s);
+  if (t != hipErrorNotSupported) return t;
+#endif
   switch (dtype) {
     case DCN_F32: return launch_dt<DCN_F32>(softmax, p, s);
     case DCN_F16: return launch_dt<DCN_F16>(softmax, p, s);

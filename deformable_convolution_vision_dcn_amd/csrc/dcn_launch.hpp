@@ -37,7 +37,17 @@ struct BwdParams {
   void *grad_mask;         // (chunk, Ho, Wo, G, K)
 };
 
+// Geometry of the LDS-tiled forward: one block per (image, output tile,
+// group); the input window of the tile (plus a halo of R pixels on every
+// side for the learned offsets) is staged into LDS.
+struct TileGeom {
+  int32_t span_h, span_w;    // staged window, in input pixels
+  int32_t tiles_x, tiles_per_img;
+  FastDiv div_g, div_tiles, div_tiles_x, div_span_w;
+};
+
 hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_t s);
+hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipStream_t s);
 hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_zero(void *dst, uint64_t bytes, hipStream_t s);
 
