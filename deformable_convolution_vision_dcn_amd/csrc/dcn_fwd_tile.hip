@@ -24,6 +24,7 @@
 // math.  Each lane then reads its 16-byte chunk of the four corners and does
 // 4 FMAs per channel per point.  The softmax over the nine logits is a quad
 // reduction (max, then sum of exponentials).
+#include <algorithm>
 #include <type_traits>
 
 #include "dcn_device.hpp"
@@ -105,6 +106,8 @@ __device__ __forceinline__ float load_one(const void *base, uint32_t e) {
 #define DCN_PIXB_16 40    // LDS bytes per staged 16-bit pixel slice (32 + pad)
 #endif
 
+constexpr int kTileMaxSpan = 1024;  // window pixels a block can stage
+
 template <int DT>
 constexpr int tile_pixel_stride() { return DT == DCN_F32 ? DCN_PIXB_F32 : DCN_PIXB_16; }
 
@@ -118,238 +121,277 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
   constexpr int PIXB = tile_pixel_stride<DT>();
   constexpr int QUADS = 512 / 4;
   constexpr int PASSES = TH * TW / QUADS;
+  constexpr int MAXPQ = kTileMaxSpan / QUADS;      // window pixels per quad
   constexpr int K = 9;
-  static_assert((TH * TW) % QUADS == 0, "tile must be a multiple of the quad count");
+  static_assert(PASSES == 2, "the pass sequence below assumes two passes");
   static_assert(PIXB % LANE_BYTES == 0 && PIXB % 8 == 0 && PIXB >= 4 * LANE_BYTES, "pixel stride");
 
   extern __shared__ __align__(16) unsigned char tile[];
 
-  // Logical block -> (n, tile, g); g varies fastest so the blocks that share
-  // an input window's cache lines (neighbouring groups) run together.
-  const uint32_t b = xcd_block(blockIdx.x, gridDim.x);
-  const uint32_t t = fast_div(b, tg.div_g);
-  const uint32_t g = b - t * (uint32_t)p.G;
-  const uint32_t n = fast_div(t, tg.div_tiles);
-  const uint32_t tile_id = t - n * (uint32_t)tg.tiles_per_img;
-  const uint32_t tyi = fast_div(tile_id, tg.div_tiles_x);
-  const uint32_t txi = tile_id - tyi * (uint32_t)tg.tiles_x;
-  const int r0 = (int)tyi * TH, c0 = (int)txi * TW;
-  const int Y0 = r0 * p.SH - p.PH - R;   // window origin in input coordinates
-  const int X0 = c0 * p.SW - p.PW - R;
-
   const uint32_t quad = threadIdx.x >> 2, sub = threadIdx.x & 3;
   const uint32_t pix_bytes = (uint32_t)p.C * io::kBytes;
   const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
-  const uint32_t chan = (g * CG + sub * CPL) * io::kBytes;
-  const uint32_t img = n * (uint32_t)p.H * row_bytes;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
-
-  // ---- own points' offsets and logits of every pass, requested before the
-  // window so that both latencies overlap.  Quad `quad` of pass `ps` owns
-  // output pixel pp = ps*QUADS + quad of the tile; lane `sub` owns the
-  // points k = sub + 4r.
-  float2 off[PASSES][3];
-  float lg[PASSES][3];
-  uint32_t pgs[PASSES];
-  bool live[PASSES];
-#pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps) {
-    const int pp = ps * QUADS + (int)quad;
-    const int ho = r0 + pp / TW, wo = c0 + pp % TW;
-    live[ps] = ho < p.Ho && wo < p.Wo;
-    pgs[ps] = (((n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + g;
-#pragma unroll
-    for (int r = 0; r < 3; ++r) {
-      const int k = (int)sub + 4 * r;
-      if (live[ps] && k < K) {
-        off[ps][r] = load_pair<DT>(p.offset, pgs[ps] * K + k);
-        lg[ps][r] = load_one<DT>(p.mask, pgs[ps] * K + k);
-      } else {
-        off[ps][r] = make_float2(0.f, 0.f);
-        lg[ps][r] = SOFTMAX ? -INFINITY : 0.f;
-      }
-    }
-  }
-
-  // ---- stage the window: one quad per pixel, 4 pixels in flight per lane
   const int span = tg.span_h * tg.span_w;
   const int row_lds = tg.span_w * PIXB;
-  for (int base = (int)quad; base < span; base += QUADS * 4) {
-    uint32_t w[4][NW];
+  const int zero_base = span * PIXB;
+  const int lim_y = tg.span_h - 2, lim_x = tg.span_w - 2;
+  const float s = p.scale;
+
+  // A zero block after the window: samples served from global memory (and
+  // NaN locations) read their main-path corners here, contributing w * 0.
+  // Written once; the first barrier of the item loop orders it.
+  for (int z = (int)threadIdx.x * 8; z < row_lds + 2 * PIXB; z += 512 * 8)
+    *reinterpret_cast<uint2 *>(tile + zero_base + z) = make_uint2(0, 0);
+
+  // Work item -> (n, tile, g); g varies fastest so the items that share an
+  // input window's cache lines (neighbouring groups) run close in time.
+  struct Item {
+    uint32_t g, n, img, chan;
+    int r0, c0, Y0, X0;
+  };
+  auto decode = [&](uint32_t it) {
+    Item I;
+    const uint32_t t = fast_div(it, tg.div_g);
+    I.g = it - t * (uint32_t)p.G;
+    I.n = fast_div(t, tg.div_tiles);
+    const uint32_t tile_id = t - I.n * (uint32_t)tg.tiles_per_img;
+    const uint32_t tyi = fast_div(tile_id, tg.div_tiles_x);
+    const uint32_t txi = tile_id - tyi * (uint32_t)tg.tiles_x;
+    I.r0 = (int)tyi * TH;
+    I.c0 = (int)txi * TW;
+    I.Y0 = I.r0 * p.SH - p.PH - R;  // window origin in input coordinates
+    I.X0 = I.c0 * p.SW - p.PW - R;
+    I.img = I.n * (uint32_t)p.H * row_bytes;
+    I.chan = (I.g * CG + sub * CPL) * io::kBytes;
+    return I;
+  };
+
+  // Window slices of an item, one quad per pixel: requested into registers
+  // while the previous item computes, written to LDS when it is done.
+  uint32_t win[MAXPQ][NW];
+  auto issue_window = [&](const Item &I) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = base + u * QUADS;
+    for (int u = 0; u < MAXPQ; ++u) {
+      const int idx = (int)quad + u * QUADS;
       uint32_t offb = kOutOfRange;
       if (idx < span) {
         const int sy = (int)fast_div((uint32_t)idx, tg.div_span_w);
         const int sx = idx - sy * tg.span_w;
-        const int gy = Y0 + sy, gx = X0 + sx;
+        const int gy = I.Y0 + sy, gx = I.X0 + sx;
         if ((uint32_t)gy < (uint32_t)p.H && (uint32_t)gx < (uint32_t)p.W)
-          offb = img + (uint32_t)gy * row_bytes + (uint32_t)gx * pix_bytes + chan;
+          offb = I.img + (uint32_t)gy * row_bytes + (uint32_t)gx * pix_bytes + I.chan;
       }
-      buffer_load_words<NW>(rin, offb, w[u]);
+      buffer_load_words<NW>(rin, offb, win[u]);
     }
+  };
+  auto store_window = [&]() {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = base + u * QUADS;
-      if (idx < span) lds_store<NW>(tile + idx * PIXB + sub * LANE_BYTES, w[u]);
+    for (int u = 0; u < MAXPQ; ++u) {
+      const int idx = (int)quad + u * QUADS;
+      if (idx < span) lds_store<NW>(tile + idx * PIXB + sub * LANE_BYTES, win[u]);
     }
-  }
-  // A zero block after the window: samples served from global memory (and
-  // NaN locations) read their main-path corners here, contributing w * 0.
-  const int zero_base = span * PIXB;
-  for (int z = (int)threadIdx.x * 8; z < row_lds + 2 * PIXB; z += 512 * 8)
-    *reinterpret_cast<uint2 *>(tile + zero_base + z) = make_uint2(0, 0);
-  __syncthreads();
+  };
 
-  const int lim_y = tg.span_h - 2, lim_x = tg.span_w - 2;
-  const float s = p.scale;
-
-  auto pass = [&](auto ps_tag) {
+  // Own points' offsets and logits of both passes: quad `quad` of pass ps
+  // owns output pixel pp = ps*QUADS + quad of the tile, lane `sub` the points
+  // k = sub + 4r.
+  float2 off_n[PASSES][3];
+  float lg_n[PASSES][3];
+  auto issue_pgdata = [&](const Item &I, auto ps_tag) {
     constexpr int ps = decltype(ps_tag)::value;
-    if (!live[ps]) return;  // whole quad leaves together
-    const int pp = ps * QUADS + (int)quad;
-    const int ho = r0 + pp / TW, wo = c0 + pp % TW;
-
-    float m[3];
-    if constexpr (SOFTMAX) {
-      const float mx = quad_max(fmaxf(fmaxf(lg[ps][0], lg[ps][1]), lg[ps][2]));
-      float e[3], sum = 0.f;
+    {
+      const int pp = ps * QUADS + (int)quad;
+      const int ho = I.r0 + pp / TW, wo = I.c0 + pp % TW;
+      const bool live = ho < p.Ho && wo < p.Wo;
+      const uint32_t pg = (((I.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + I.g;
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
-        e[r] = ((int)sub + 4 * r < K) ? __expf(lg[ps][r] - mx) : 0.f;
-        sum += e[r];
+        const int k = (int)sub + 4 * r;
+        if (live && k < K) {
+          off_n[ps][r] = load_pair<DT>(p.offset, pg * K + k);
+          lg_n[ps][r] = load_one<DT>(p.mask, pg * K + k);
+        } else {
+          off_n[ps][r] = make_float2(0.f, 0.f);
+          lg_n[ps][r] = SOFTMAX ? -INFINITY : 0.f;
+        }
       }
-      const float inv = __builtin_amdgcn_rcpf(quad_sum(sum));
-#pragma unroll
-      for (int r = 0; r < 3; ++r) m[r] = e[r] * inv;
-    } else {
-#pragma unroll
-      for (int r = 0; r < 3; ++r) m[r] = lg[ps][r];
     }
-
-    float acc[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-
-    // Round r: every lane prepares its own point k = sub + 4r (location,
-    // weights with the modulation folded in, window address), then the quad
-    // consumes the round's points one owner at a time.  The per-round inputs
-    // rotate through scalars (no run-time indexed arrays, so no scratch).
-    float2 o2 = off[ps][0], o2n = off[ps][1], o2nn = off[ps][2];
-    float mk = m[0], mkn = m[1], mknn = m[2];
-#pragma unroll 1
-    for (int r = 0; r < 3; ++r) {
-      const int k = (int)sub + 4 * r;
-      const int i = k >= 6 ? 2 : (k >= 3 ? 1 : 0);
-      const int j = k - 3 * i;
-      const float dx = s * o2.x, dy = s * o2.y;
-      const bool nan_loc = (dx != dx) | (dy != dy);
-      const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
-      const float cy = __builtin_amdgcn_fmed3f(dy, -16777216.f, 16777216.f);
-      const float fx = floorf(cx), fy = floorf(cy);
-      const float lx = cx - fx, ly = cy - fy;
-      const int x0 = wo * p.SW - p.PW + j * p.DW + (int)fx;
-      const int y0 = ho * p.SH - p.PH + i * p.DH + (int)fy;
-      const float wy0 = (1.f - ly) * mk, wy1 = ly * mk;
-      const float nanv = __builtin_nanf("");
-      const float W0 = nan_loc ? nanv : wy0 * (1.f - lx);
-      const float W1 = nan_loc ? nanv : wy0 * lx;
-      const float W2 = nan_loc ? nanv : wy1 * (1.f - lx);
-      const float W3 = nan_loc ? nanv : wy1 * lx;
-      const int ty = y0 - Y0, tx = x0 - X0;
-      const bool inside = !nan_loc && (uint32_t)ty <= (uint32_t)lim_y && (uint32_t)tx <= (uint32_t)lim_x;
-      const int A = inside ? ty * row_lds + tx * PIXB : zero_base;
-      // outside the window but touching the map: needs the global fix-up
-      const bool fb = !inside && !nan_loc && (uint32_t)(y0 + 1) <= (uint32_t)p.H &&
-                      (uint32_t)(x0 + 1) <= (uint32_t)p.W;
-
-      // Main path, no branches: gather the round's corners from LDS.
-      auto point = [&](auto o_tag) {
-        constexpr int O = decltype(o_tag)::value;
-        const int a = qbcast<O>(A);
-        const float w00 = qbcast<O>(W0), w01 = qbcast<O>(W1);
-        const float w10 = qbcast<O>(W2), w11 = qbcast<O>(W3);
-        uint32_t q00[NW], q01[NW], q10[NW], q11[NW];
-        const unsigned char *src = tile + a + sub * LANE_BYTES;
-        lds_load<NW>(src, q00);
-        lds_load<NW>(src + PIXB, q01);
-        lds_load<NW>(src + row_lds, q10);
-        lds_load<NW>(src + row_lds + PIXB, q11);
-        float v00[CPL], v01[CPL], v10[CPL], v11[CPL];
-        unpack<DT, NW>(q00, v00);
-        unpack<DT, NW>(q01, v01);
-        unpack<DT, NW>(q10, v10);
-        unpack<DT, NW>(q11, v11);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          acc[c] = fmaf(w00, v00[c], acc[c]);
-          acc[c] = fmaf(w01, v01[c], acc[c]);
-          acc[c] = fmaf(w10, v10[c], acc[c]);
-          acc[c] = fmaf(w11, v11[c], acc[c]);
-        }
-      };
-      // Fix-up for points whose corners left the window: global gathers,
-      // the buffer range check reading 0 for corners outside the map.
-      auto fixup = [&](auto o_tag) {
-        constexpr int O = decltype(o_tag)::value;
-        if (!qbcast<O>((int)fb)) return;
-        const float w00 = qbcast<O>(W0), w01 = qbcast<O>(W1);
-        const float w10 = qbcast<O>(W2), w11 = qbcast<O>(W3);
-        const int yb = qbcast<O>(y0), xb = qbcast<O>(x0);
-        const bool vy0 = (uint32_t)yb < (uint32_t)p.H, vy1 = (uint32_t)(yb + 1) < (uint32_t)p.H;
-        const bool vx0 = (uint32_t)xb < (uint32_t)p.W, vx1 = (uint32_t)(xb + 1) < (uint32_t)p.W;
-        const uint32_t a00 = img + (uint32_t)yb * row_bytes + (uint32_t)xb * pix_bytes + chan;
-        uint32_t q00[NW], q01[NW], q10[NW], q11[NW];
-        buffer_load_words<NW>(rin, (vy0 && vx0) ? a00 : kOutOfRange, q00);
-        buffer_load_words<NW>(rin, (vy0 && vx1) ? a00 + pix_bytes : kOutOfRange, q01);
-        buffer_load_words<NW>(rin, (vy1 && vx0) ? a00 + row_bytes : kOutOfRange, q10);
-        buffer_load_words<NW>(rin, (vy1 && vx1) ? a00 + row_bytes + pix_bytes : kOutOfRange, q11);
-        float v00[CPL], v01[CPL], v10[CPL], v11[CPL];
-        unpack<DT, NW>(q00, v00);
-        unpack<DT, NW>(q01, v01);
-        unpack<DT, NW>(q10, v10);
-        unpack<DT, NW>(q11, v11);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          acc[c] = fmaf(w00, v00[c], acc[c]);
-          acc[c] = fmaf(w01, v01[c], acc[c]);
-          acc[c] = fmaf(w10, v10[c], acc[c]);
-          acc[c] = fmaf(w11, v11[c], acc[c]);
-        }
-      };
-      using I0 = std::integral_constant<int, 0>;
-      using I1 = std::integral_constant<int, 1>;
-      using I2 = std::integral_constant<int, 2>;
-      using I3 = std::integral_constant<int, 3>;
-      point(I0{});
-      if (r < 2) {  // the last round holds only k = 8 (owner lane 0)
-        point(I1{});
-        point(I2{});
-        point(I3{});
-      }
-      if (__builtin_amdgcn_ballot_w64(fb) != 0) {  // rare: some quad of the wave left its window
-        fixup(I0{});
-        if (r < 2) {
-          fixup(I1{});
-          fixup(I2{});
-          fixup(I3{});
-        }
-      }
-      o2 = o2n;
-      o2n = o2nn;
-      mk = mkn;
-      mkn = mknn;
-    }
-
-    uint32_t outw[NW];
-    pack_words<DT, CPL>(acc, outw);
-    store_words<NW>(static_cast<unsigned char *>(p.output) + ((uint64_t)pgs[ps] * CG + sub * CPL) * io::kBytes,
-                    outw);
   };
-  static_assert(PASSES == 2, "the pass sequence below assumes two passes");
-  pass(std::integral_constant<int, 0>{});
-  pass(std::integral_constant<int, 1>{});
+
+  const uint32_t items = tg.items;
+  uint32_t item = xcd_block(blockIdx.x, gridDim.x);
+  Item cur = decode(item < items ? item : 0);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  if (item < items) {
+    issue_window(cur);
+    issue_pgdata(cur, P0{});
+    issue_pgdata(cur, P1{});
+  }
+
+  while (item < items) {
+    __syncthreads();  // every wave is done reading the previous window
+    store_window();
+    __syncthreads();  // the window is in LDS
+
+    // The next item's window is requested now and lands during this item's
+    // passes; its per-pass offsets/logits are requested as soon as this
+    // item's pass has consumed the registers they go to.
+    const uint32_t next = item + gridDim.x;
+    const bool more = next < items;  // block-uniform
+    const Item nx = decode(more ? next : item);
+    if (more) issue_window(nx);
+
+    auto pass = [&](auto ps_tag) {
+      constexpr int ps = decltype(ps_tag)::value;
+      const int pp = ps * QUADS + (int)quad;
+      const int ho = cur.r0 + pp / TW, wo = cur.c0 + pp % TW;
+      if (ho >= p.Ho || wo >= p.Wo) return;  // whole quad leaves together
+      const uint32_t pg = (((cur.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + cur.g;
+
+      float m[3];
+      if constexpr (SOFTMAX) {
+        const float mx = quad_max(fmaxf(fmaxf(lg_n[ps][0], lg_n[ps][1]), lg_n[ps][2]));
+        float e[3], sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          e[r] = ((int)sub + 4 * r < K) ? __expf(lg_n[ps][r] - mx) : 0.f;
+          sum += e[r];
+        }
+        const float inv = __builtin_amdgcn_rcpf(quad_sum(sum));
+#pragma unroll
+        for (int r = 0; r < 3; ++r) m[r] = e[r] * inv;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) m[r] = lg_n[ps][r];
+      }
+
+      float acc[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+
+      // Round r: every lane prepares its own point k = sub + 4r (location,
+      // weights with the modulation folded in, window address), then the
+      // quad consumes the round's points one owner at a time.  The per-round
+      // inputs rotate through scalars (no run-time indexed arrays).
+      float2 o2 = off_n[ps][0], o2n = off_n[ps][1], o2nn = off_n[ps][2];
+      float mk = m[0], mkn = m[1], mknn = m[2];
+#pragma unroll 1
+      for (int r = 0; r < 3; ++r) {
+        const int k = (int)sub + 4 * r;
+        const int i = k >= 6 ? 2 : (k >= 3 ? 1 : 0);
+        const int j = k - 3 * i;
+        const float dx = s * o2.x, dy = s * o2.y;
+        const bool nan_loc = (dx != dx) | (dy != dy);
+        const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
+        const float cy = __builtin_amdgcn_fmed3f(dy, -16777216.f, 16777216.f);
+        const float fx = floorf(cx), fy = floorf(cy);
+        const float lx = cx - fx, ly = cy - fy;
+        const int x0 = wo * p.SW - p.PW + j * p.DW + (int)fx;
+        const int y0 = ho * p.SH - p.PH + i * p.DH + (int)fy;
+        const float mkk = nan_loc ? __builtin_nanf("") : mk;  // NaN location: NaN weights
+        const float wy0 = (1.f - ly) * mkk, wy1 = ly * mkk;
+        const float W0 = wy0 * (1.f - lx), W1 = wy0 * lx;
+        const float W2 = wy1 * (1.f - lx), W3 = wy1 * lx;
+        const int ty = y0 - cur.Y0, tx = x0 - cur.X0;
+        const bool inside = !nan_loc && (uint32_t)ty <= (uint32_t)lim_y && (uint32_t)tx <= (uint32_t)lim_x;
+        const int A = inside ? (int)__umul24((uint32_t)ty, (uint32_t)row_lds) + tx * PIXB : zero_base;
+        // outside the window but touching the map: needs the global fix-up
+        const bool fb = !inside && !nan_loc && (uint32_t)(y0 + 1) <= (uint32_t)p.H &&
+                        (uint32_t)(x0 + 1) <= (uint32_t)p.W;
+
+        // Main path, no branches: gather the round's corners from LDS.
+        auto point = [&](auto o_tag) {
+          constexpr int O = decltype(o_tag)::value;
+          const int a = qbcast<O>(A);
+          const float w00 = qbcast<O>(W0), w01 = qbcast<O>(W1);
+          const float w10 = qbcast<O>(W2), w11 = qbcast<O>(W3);
+          uint32_t q00[NW], q01[NW], q10[NW], q11[NW];
+          const unsigned char *src = tile + a + sub * LANE_BYTES;
+          lds_load<NW>(src, q00);
+          lds_load<NW>(src + PIXB, q01);
+          lds_load<NW>(src + row_lds, q10);
+          lds_load<NW>(src + row_lds + PIXB, q11);
+          float v00[CPL], v01[CPL], v10[CPL], v11[CPL];
+          unpack<DT, NW>(q00, v00);
+          unpack<DT, NW>(q01, v01);
+          unpack<DT, NW>(q10, v10);
+          unpack<DT, NW>(q11, v11);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            acc[c] = fmaf(w00, v00[c], acc[c]);
+            acc[c] = fmaf(w01, v01[c], acc[c]);
+            acc[c] = fmaf(w10, v10[c], acc[c]);
+            acc[c] = fmaf(w11, v11[c], acc[c]);
+          }
+        };
+        // Fix-up for points whose corners left the window: global gathers,
+        // the buffer range check reading 0 for corners outside the map.
+        auto fixup = [&](auto o_tag) {
+          constexpr int O = decltype(o_tag)::value;
+          if (!qbcast<O>((int)fb)) return;
+          const float w00 = qbcast<O>(W0), w01 = qbcast<O>(W1);
+          const float w10 = qbcast<O>(W2), w11 = qbcast<O>(W3);
+          const int yb = qbcast<O>(y0), xb = qbcast<O>(x0);
+          const bool vy0 = (uint32_t)yb < (uint32_t)p.H, vy1 = (uint32_t)(yb + 1) < (uint32_t)p.H;
+          const bool vx0 = (uint32_t)xb < (uint32_t)p.W, vx1 = (uint32_t)(xb + 1) < (uint32_t)p.W;
+          const uint32_t a00 = cur.img + (uint32_t)yb * row_bytes + (uint32_t)xb * pix_bytes + cur.chan;
+          uint32_t q00[NW], q01[NW], q10[NW], q11[NW];
+          buffer_load_words<NW>(rin, (vy0 && vx0) ? a00 : kOutOfRange, q00);
+          buffer_load_words<NW>(rin, (vy0 && vx1) ? a00 + pix_bytes : kOutOfRange, q01);
+          buffer_load_words<NW>(rin, (vy1 && vx0) ? a00 + row_bytes : kOutOfRange, q10);
+          buffer_load_words<NW>(rin, (vy1 && vx1) ? a00 + row_bytes + pix_bytes : kOutOfRange, q11);
+          float v00[CPL], v01[CPL], v10[CPL], v11[CPL];
+          unpack<DT, NW>(q00, v00);
+          unpack<DT, NW>(q01, v01);
+          unpack<DT, NW>(q10, v10);
+          unpack<DT, NW>(q11, v11);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            acc[c] = fmaf(w00, v00[c], acc[c]);
+            acc[c] = fmaf(w01, v01[c], acc[c]);
+            acc[c] = fmaf(w10, v10[c], acc[c]);
+            acc[c] = fmaf(w11, v11[c], acc[c]);
+          }
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        point(I0{});
+        if (r < 2) {  // the last round holds only k = 8 (owner lane 0)
+          point(I1{});
+          point(I2{});
+          point(I3{});
+        }
+        if (__builtin_amdgcn_ballot_w64(fb) != 0) {  // rare: a quad of the wave left its window
+          fixup(I0{});
+          if (r < 2) {
+            fixup(I1{});
+            fixup(I2{});
+            fixup(I3{});
+          }
+        }
+        o2 = o2n;
+        o2n = o2nn;
+        mk = mkn;
+        mkn = mknn;
+      }
+
+      uint32_t outw[NW];
+      pack_words<DT, CPL>(acc, outw);
+      store_words<NW>(static_cast<unsigned char *>(p.output) + ((uint64_t)pg * CG + sub * CPL) * io::kBytes,
+                      outw);
+    };
+    pass(P0{});
+    if (more) issue_pgdata(nx, P0{});
+    pass(P1{});
+    if (more) issue_pgdata(nx, P1{});
+
+    item = next;
+    cur = nx;
+  }
 }
 
 namespace {
@@ -362,12 +404,18 @@ size_t tile_lds_bytes(const TileGeom &tg, int pixb) {
 }
 
 template <int DT, bool SM>
-hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, uint32_t blocks, hipStream_t s) {
+hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, kHalo>;
   const size_t lds = tile_lds_bytes(tg, tile_pixel_stride<DT>());
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kTileLdsLimit);
   if (attr != hipSuccess) return attr;
+  // Persistent blocks: two per CU, each walking work items blockIdx, +grid, ...
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const uint32_t blocks = std::min<uint32_t>(tg.items, 2u * (uint32_t)cus);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(512), lds, s, p, tg);
   return hipGetLastError();
 }
@@ -383,6 +431,7 @@ hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipS
   tg.span_w = (kTileW - 1) * p.SW + 2 * p.DW + 2 * kHalo + 2;
   const int pixb = dtype == DCN_F32 ? tile_pixel_stride<DCN_F32>() : tile_pixel_stride<DCN_F16>();
   if (tile_lds_bytes(tg, pixb) > (size_t)kTileLdsLimit) return hipErrorNotSupported;
+  if (tg.span_h * tg.span_w > kTileMaxSpan) return hipErrorNotSupported;
   const int tiles_y = (p.Ho + kTileH - 1) / kTileH;
   tg.tiles_x = (p.Wo + kTileW - 1) / kTileW;
   tg.tiles_per_img = tiles_y * tg.tiles_x;
@@ -393,11 +442,11 @@ hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipS
   tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
-  const uint32_t nb = (uint32_t)blocks;
+  tg.items = (uint32_t)blocks;
   switch (dtype) {
-    case DCN_F32: return softmax ? launch_tile<DCN_F32, true>(p, tg, nb, s) : launch_tile<DCN_F32, false>(p, tg, nb, s);
-    case DCN_F16: return softmax ? launch_tile<DCN_F16, true>(p, tg, nb, s) : launch_tile<DCN_F16, false>(p, tg, nb, s);
-    case DCN_BF16: return softmax ? launch_tile<DCN_BF16, true>(p, tg, nb, s) : launch_tile<DCN_BF16, false>(p, tg, nb, s);
+    case DCN_F32: return softmax ? launch_tile<DCN_F32, true>(p, tg, s) : launch_tile<DCN_F32, false>(p, tg, s);
+    case DCN_F16: return softmax ? launch_tile<DCN_F16, true>(p, tg, s) : launch_tile<DCN_F16, false>(p, tg, s);
+    case DCN_BF16: return softmax ? launch_tile<DCN_BF16, true>(p, tg, s) : launch_tile<DCN_BF16, false>(p, tg, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -43,6 +43,7 @@ struct BwdParams {
 struct TileGeom {
   int32_t span_h, span_w;    // staged window, in input pixels
   int32_t tiles_x, tiles_per_img;
+  uint32_t items;            // (image, tile, group) work items of the launch
   FastDiv div_g, div_tiles, div_tiles_x, div_span_w;
 };
 
