@@ -42,8 +42,8 @@ int validate(const dcn_problem *p, int64_t *ho_out, int64_t *wo_out) {
   if (p->c / p->groups != dcn::kGroupChannels) return DCN_ERR_UNSUPPORTED;
   if ((int64_t)p->kernel_h * p->kernel_w > dcn::kMaxPoints) return DCN_ERR_UNSUPPORTED;
   const int64_t img_bytes = (int64_t)p->h * p->w * p->c * elem_bytes(p->dtype);
-  const int64_t img_pg = ho * wo * p->groups;
-  if (img_bytes > kMaxBytes31 || img_pg * dcn::kGroupChannels > kMaxBytes31) return DCN_ERR_TOO_LARGE;
+  const int64_t img_out_bytes = ho * wo * p->c * elem_bytes(p->dtype);
+  if (img_bytes > kMaxBytes31 || img_out_bytes > kMaxBytes31) return DCN_ERR_TOO_LARGE;
   if (ho_out) *ho_out = ho;
   if (wo_out) *wo_out = wo;
   return DCN_OK;
@@ -80,13 +80,14 @@ dcn::FwdParams geometry(const dcn_problem *p, int64_t ho, int64_t wo) {
   return f;
 }
 
-// Images per launch: every chunk keeps its input below 2^31 bytes and its
-// pixel-group count (times 16) below 2^31, the reach of 32-bit offsets.
+// Images per launch: every chunk keeps its input and its output below 2^31
+// bytes, the reach of the kernels' 32-bit buffer offsets (pixel-group
+// indices then stay below 2^31 / 16 as well).
 int64_t images_per_chunk(const dcn_problem *p, int64_t ho, int64_t wo) {
   const int64_t img_bytes = (int64_t)p->h * p->w * p->c * elem_bytes(p->dtype);
-  const int64_t img_pg16 = ho * wo * p->groups * dcn::kGroupChannels;
+  const int64_t img_out_bytes = ho * wo * p->c * elem_bytes(p->dtype);
   int64_t per = kMaxBytes31 / img_bytes;
-  const int64_t per2 = kMaxBytes31 / img_pg16;
+  const int64_t per2 = kMaxBytes31 / img_out_bytes;
   if (per2 < per) per = per2;
   return per < 1 ? 1 : per;
 }

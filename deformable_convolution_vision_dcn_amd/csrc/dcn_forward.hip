@@ -23,11 +23,10 @@
 //    as zero -- zero padding without a branch.
 //  * Blocks are remapped so that each XCD owns a contiguous run of pixels and
 //    the overlapping sampling windows of neighbouring pixels meet in its L2.
-#include "dcn_device.hpp"
+#include <stdlib.h>
+#include <string.h>
 
-#ifndef DCN_FWD_LANES
-#define DCN_FWD_LANES 1
-#endif
+#include "dcn_device.hpp"
 
 namespace dcn {
 
@@ -195,23 +194,52 @@ hipError_t launch_one(const FwdParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Lanes per pixel-group of the untiled kernel: four (4 fp32 channels per lane)
+// for fp32, two (8 channels, one 16-byte load per corner) for 16-bit I/O.
 template <int DT>
 hipError_t launch_dt(int softmax, const FwdParams &p, hipStream_t s) {
+  constexpr int LANES = DT == DCN_F32 ? 4 : 2;
   const bool k33 = p.KH == 3 && p.KW == 3;
   if (k33) {
-    return softmax ? launch_one<DT, DCN_FWD_LANES, 3, 3, true>(p, s)
-                   : launch_one<DT, DCN_FWD_LANES, 3, 3, false>(p, s);
+    return softmax ? launch_one<DT, LANES, 3, 3, true>(p, s) : launch_one<DT, LANES, 3, 3, false>(p, s);
   }
-  return softmax ? launch_one<DT, 4, 0, 0, true>(p, s) : launch_one<DT, 4, 0, 0, false>(p, s);
+  return softmax ? launch_one<DT, LANES, 0, 0, true>(p, s) : launch_one<DT, LANES, 0, 0, false>(p, s);
+}
+
+// Forward path override for tests and measurements: DCN_MI355X_FWD_PATH =
+// "generic", "tiled" or "lane" tries that kernel first (and falls back to the
+// generic kernel where it does not apply).  Read at every call.
+enum class Path { kAuto, kGeneric, kTiled, kLane };
+
+Path path_override() {
+  const char *e = getenv("DCN_MI355X_FWD_PATH");
+  if (!e) return Path::kAuto;
+  if (!strcmp(e, "generic")) return Path::kGeneric;
+  if (!strcmp(e, "tiled")) return Path::kTiled;
+  if (!strcmp(e, "lane")) return Path::kLane;
+  return Path::kAuto;
 }
 
 }  // namespace
 
+// Kernel choice for 3x3 points that fit a tile window: fp32 runs the quad
+// tiled kernel (a quad of lanes per pixel-group), 16-bit I/O the
+// lane-per-pixel-group kernel, which needs a quarter of the address and
+// weight arithmetic and wins once a pixel's 16 channels are only 32 bytes.
+// Everything else runs the untiled kernel.
 hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
-#ifndef DCN_NO_TILED
-  const hipError_t t = launch_forward_tiled(dtype, softmax, p, s);
-  if (t != hipErrorNotSupported) return t;
-#endif
+  const Path forced = path_override();
+  const bool lane_first = forced == Path::kLane || (forced == Path::kAuto && dtype != DCN_F32);
+  if (forced != Path::kGeneric) {
+    if (lane_first) {
+      const hipError_t l = launch_forward_lane(dtype, softmax, p, s);
+      if (l != hipErrorNotSupported) return l;
+    }
+    if (forced != Path::kLane) {
+      const hipError_t t = launch_forward_tiled(dtype, softmax, p, s);
+      if (t != hipErrorNotSupported) return t;
+    }
+  }
   switch (dtype) {
     case DCN_F32: return launch_dt<DCN_F32>(softmax, p, s);
     case DCN_F16: return launch_dt<DCN_F16>(softmax, p, s);

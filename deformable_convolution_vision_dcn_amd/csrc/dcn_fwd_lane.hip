@@ -1,0 +1,403 @@
+// dcn_fwd_lane.hip -- LDS-tiled gfx950 forward kernel of the DCN core for
+// 3x3 kernel points, one lane per pixel-group (wmrh.cn/news/61976, section 二
+// steps 2-4 and section 三).
+//
+// The forward is a gather-reduce: per bilinear sample 64 fp32 FMAs (16
+// channels x 4 corners) against a few dozen instructions of location and
+// weight math.  With one lane per pixel-group that math is done exactly once
+// per sample and needs no cross-lane broadcast, so the instruction stream is
+// dominated by the FMAs themselves (vector fp32 issue is the binding limit on
+// this chip once the corners come from LDS).
+//
+// Block = 256 threads = one (image, 16x16 output tile, group) work item at a
+// time; blocks are persistent (two per CU) and walk items blockIdx, +grid, ...
+// The input window of an item (its regular 3x3 footprint plus a halo of R
+// pixels for the learned offsets, zero outside the map) is staged in LDS; the
+// next item's window, offsets and logits are requested into registers while
+// the current item computes.  A sample whose corners leave the window is
+// served from global memory behind a wave ballot (the buffer range check
+// supplying the zeros); the main path has no branches.
+//
+// LDS banking: a wave64 ds_read_b128 is served 16 lanes at a time from 64
+// banks.  Lane l reads the 16-byte chunks of a corner in the rotated order
+// (t + l) mod 4, so the four lanes that share a chunk position come from four
+// different pixels; the remaining conflicts are the random coincidences of
+// those pixels' bank quarters.
+#include <algorithm>
+
+#include "dcn_device.hpp"
+
+namespace dcn {
+
+#ifndef DCN_LANE_HALO
+#define DCN_LANE_HALO 6
+#endif
+
+constexpr int kLaneTile = 16;                 // output tile edge
+constexpr int kLaneHalo = DCN_LANE_HALO;      // window halo for the offsets
+constexpr int kLaneSpanUnit = kLaneTile + 2 * kLaneHalo + 3;
+constexpr int kLaneThreads = kLaneTile * kLaneTile;
+constexpr int kLaneMaxSpan = 1024;
+
+template <int DT>
+constexpr int lane_pixel_stride() { return DT == DCN_F32 ? 64 : 32; }
+
+namespace {
+
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+// The 9 (x, y) offset pairs of pixel-group pg as 18 fp32 values.
+template <int DT>
+__device__ __forceinline__ void load_offsets(const void *base, uint32_t pg, float (&o)[18]) {
+  if constexpr (DT == DCN_F32) {
+    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * 18;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src + 4 * q);
+      o[4 * q] = __uint_as_float(v[0]);
+      o[4 * q + 1] = __uint_as_float(v[1]);
+      o[4 * q + 2] = __uint_as_float(v[2]);
+      o[4 * q + 3] = __uint_as_float(v[3]);
+    }
+    const u32x2_a4 v = *reinterpret_cast<const u32x2_a4 *>(src + 16);
+    o[16] = __uint_as_float(v[0]);
+    o[17] = __uint_as_float(v[1]);
+  } else {
+    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * 9;
+    uint32_t w[9];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src + 4 * q);
+      w[4 * q] = v[0];
+      w[4 * q + 1] = v[1];
+      w[4 * q + 2] = v[2];
+      w[4 * q + 3] = v[3];
+    }
+    w[8] = src[8];
+#pragma unroll
+    for (int q = 0; q < 9; ++q) {
+      o[2 * q] = Io<DT>::lo(w[q]);
+      o[2 * q + 1] = Io<DT>::hi(w[q]);
+    }
+  }
+}
+
+// The 9 mask values of pixel-group pg as fp32.
+template <int DT>
+__device__ __forceinline__ void load_mask(const void *base, uint32_t pg, float (&m)[9]) {
+  if constexpr (DT == DCN_F32) {
+    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * 9;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src + 4 * q);
+      m[4 * q] = __uint_as_float(v[0]);
+      m[4 * q + 1] = __uint_as_float(v[1]);
+      m[4 * q + 2] = __uint_as_float(v[2]);
+      m[4 * q + 3] = __uint_as_float(v[3]);
+    }
+    m[8] = __uint_as_float(src[8]);
+  } else {
+    const uint16_t *src = static_cast<const uint16_t *>(base) + (uint64_t)pg * 9;
+#pragma unroll
+    for (int q = 0; q < 9; ++q) m[q] = Io<DT>::lo((uint32_t)src[q]);
+  }
+}
+
+__device__ __forceinline__ void lds_read16(const unsigned char *src, uint32_t (&w)[4]) {
+  const uint4 v = *reinterpret_cast<const uint4 *>(src);
+  w[0] = v.x;
+  w[1] = v.y;
+  w[2] = v.z;
+  w[3] = v.w;
+}
+
+}  // namespace
+
+template <int DT, bool SOFTMAX>
+__global__ void __launch_bounds__(kLaneThreads, 2) dcn_fwd_lane_kernel(FwdParams p, TileGeom tg) {
+  using io = Io<DT>;
+  constexpr int TS = kLaneTile, R = kLaneHalo, SPAN_W = kLaneSpanUnit;
+  constexpr int CG = kGroupChannels;
+  constexpr int PIXB = lane_pixel_stride<DT>();   // one pixel's 16-channel slice
+  constexpr int CHUNK = 16;                        // bytes per ds_read_b128
+  constexpr int NCH = PIXB / CHUNK;                // chunks per slice: 4 (fp32) or 2
+  constexpr int CPC = CHUNK / io::kBytes;          // channels per chunk: 4 or 8
+  constexpr int ROW = SPAN_W * PIXB;               // LDS bytes per window row
+  constexpr int SPAN = SPAN_W * SPAN_W;
+  constexpr int QUADS = kLaneThreads / NCH;        // lanes groups staging one pixel each
+  constexpr int SLOTS = (SPAN + QUADS - 1) / QUADS;
+  constexpr int LIM = SPAN_W - 2;
+  constexpr int ZERO = SPAN * PIXB;
+  constexpr int K = 9;
+
+  extern __shared__ __align__(16) unsigned char tile[];
+
+  const uint32_t lane = threadIdx.x;
+  const int oy = (int)lane / TS, ox = (int)lane % TS;
+  const uint32_t pix_bytes = (uint32_t)p.C * io::kBytes;
+  const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
+  const __amdgpu_buffer_rsrc_t rout = make_rsrc(p.output, p.pg_total * (uint32_t)(CG * io::kBytes));
+  const float s = p.scale;
+
+  // Zero block after the window (written once; ordered by the first barrier).
+  for (int z = (int)lane * 16; z < ROW + 2 * PIXB; z += kLaneThreads * 16)
+    *reinterpret_cast<uint4 *>(tile + ZERO + z) = make_uint4(0, 0, 0, 0);
+
+  // Staging: NCH lanes per pixel, SLOTS pixels per lane group.
+  const uint32_t sq = lane / NCH, sc = lane % NCH;
+
+  struct Item {
+    uint32_t g, n;
+    int Y0, X0, ho, wo;
+    bool live;
+    uint32_t pg;
+  };
+  auto decode = [&](uint32_t it) {
+    Item I;
+    const uint32_t t = fast_div(it, tg.div_g);
+    I.g = it - t * (uint32_t)p.G;
+    I.n = fast_div(t, tg.div_tiles);
+    const uint32_t tile_id = t - I.n * (uint32_t)tg.tiles_per_img;
+    const uint32_t tyi = fast_div(tile_id, tg.div_tiles_x);
+    const uint32_t txi = tile_id - tyi * (uint32_t)tg.tiles_x;
+    const int r0 = (int)tyi * TS, c0 = (int)txi * TS;
+    I.Y0 = r0 - p.PH - R;  // window origin (stride and dilation 1)
+    I.X0 = c0 - p.PW - R;
+    I.ho = r0 + oy;
+    I.wo = c0 + ox;
+    I.live = I.ho < p.Ho && I.wo < p.Wo;
+    I.pg = (((I.n * (uint32_t)p.Ho + I.ho) * (uint32_t)p.Wo + I.wo) * (uint32_t)p.G) + I.g;
+    return I;
+  };
+
+  uint32_t win[SLOTS][4];
+  auto issue_window = [&](const Item &I) {
+    const uint32_t base = I.n * (uint32_t)p.H * row_bytes + (I.g * CG) * io::kBytes + sc * CHUNK;
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u) {
+      const int idx = (int)sq + u * QUADS;
+      const int sy = idx / SPAN_W, sx = idx - sy * SPAN_W;  // constant divisor
+      const int gy = I.Y0 + sy, gx = I.X0 + sx;
+      const bool ok = idx < SPAN && (uint32_t)gy < (uint32_t)p.H && (uint32_t)gx < (uint32_t)p.W;
+      const uint32_t offb = ok ? base + (uint32_t)gy * row_bytes + (uint32_t)gx * pix_bytes : kOutOfRange;
+      buffer_load_words<4>(rin, offb, win[u]);
+    }
+  };
+  auto store_window = [&]() {
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u) {
+      const int idx = (int)sq + u * QUADS;
+      if (idx < SPAN)
+        *reinterpret_cast<uint4 *>(tile + idx * PIXB + sc * CHUNK) =
+            make_uint4(win[u][0], win[u][1], win[u][2], win[u][3]);
+    }
+  };
+
+  float off[18], msk[9];
+  // Unconditional (a dead lane reads pixel-group 0 and ignores it): every
+  // memory instruction of the item loop is issued on every path, so the
+  // compiler's wait counting stays exact and the window prefetch is only
+  // waited for where the LDS store needs it.
+  auto issue_pgdata = [&](const Item &I) {
+    const uint32_t pg = I.live ? I.pg : 0u;
+    load_offsets<DT>(p.offset, pg, off);
+    load_mask<DT>(p.mask, pg, msk);
+  };
+
+  // Per-lane chunk rotation (bank spreading) and its byte offsets.
+  int rot[NCH];
+#pragma unroll
+  for (int t = 0; t < NCH; ++t) rot[t] = ((t + (int)lane) % NCH) * CHUNK;
+
+  const uint32_t items = tg.items;
+  uint32_t item = xcd_block(blockIdx.x, gridDim.x);
+  Item cur = decode(item < items ? item : 0);
+  if (item < items) {
+    issue_window(cur);
+    issue_pgdata(cur);
+  }
+
+  while (item < items) {
+    __syncthreads();  // every wave is done with the previous window
+    store_window();
+    __syncthreads();  // the window is in LDS
+
+    // The next item's window lands in registers during this item's compute;
+    // its offsets and logits are requested once this item's are consumed.
+    // (Issued on the last item too, re-reading its own data, so that no
+    // branch changes the count of outstanding loads.)
+    const uint32_t next = item + gridDim.x;
+    const bool more = next < items;  // block-uniform
+    const Item nx = decode(more ? next : item);
+    issue_window(nx);
+
+    {
+      // modulation scalars
+      float m[K];
+      if constexpr (SOFTMAX) {
+        float mx = msk[0];
+#pragma unroll
+        for (int k = 1; k < K; ++k) mx = fmaxf(mx, msk[k]);
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          m[k] = __expf(msk[k] - mx);
+          sum += m[k];
+        }
+        const float inv = __builtin_amdgcn_rcpf(sum);
+#pragma unroll
+        for (int k = 0; k < K; ++k) m[k] *= inv;
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) m[k] = msk[k];
+      }
+
+      float acc[NCH][CPC];
+#pragma unroll
+      for (int t = 0; t < NCH; ++t)
+#pragma unroll
+        for (int c = 0; c < CPC; ++c) acc[t][c] = 0.f;
+
+      const uint32_t img = cur.n * (uint32_t)p.H * row_bytes;
+      const uint32_t chan = (cur.g * CG) * io::kBytes;
+
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int i = k / 3, j = k % 3;
+        const float dx = s * off[2 * k], dy = s * off[2 * k + 1];
+        const bool nan_loc = (dx != dx) | (dy != dy);
+        const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
+        const float cy = __builtin_amdgcn_fmed3f(dy, -16777216.f, 16777216.f);
+        const float fx = floorf(cx), fy = floorf(cy);
+        const float lx = cx - fx, ly = cy - fy;
+        // window coordinates: regular position oy + i + R (stride/dilation 1)
+        const int ty = oy + i + R + (int)fy, tx = ox + j + R + (int)fx;
+        const float mk = nan_loc ? __builtin_nanf("") : m[k];
+        const float wy0 = (1.f - ly) * mk, wy1 = ly * mk;
+        const float w00 = wy0 * (1.f - lx), w01 = wy0 * lx;
+        const float w10 = wy1 * (1.f - lx), w11 = wy1 * lx;
+        const bool inside = !nan_loc && (uint32_t)ty <= (uint32_t)LIM && (uint32_t)tx <= (uint32_t)LIM;
+        const int A = inside ? ty * ROW + tx * PIXB : ZERO;
+        const unsigned char *src = tile + A;
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+          const unsigned char *q = src + rot[t];
+          uint32_t v00[4], v01[4], v10[4], v11[4];
+          lds_read16(q, v00);
+          lds_read16(q + PIXB, v01);
+          lds_read16(q + ROW, v10);
+          lds_read16(q + ROW + PIXB, v11);
+          float f00[CPC], f01[CPC], f10[CPC], f11[CPC];
+          unpack<DT, 4>(v00, f00);
+          unpack<DT, 4>(v01, f01);
+          unpack<DT, 4>(v10, f10);
+          unpack<DT, 4>(v11, f11);
+#pragma unroll
+          for (int c = 0; c < CPC; ++c) {
+            acc[t][c] = fmaf(w00, f00[c], acc[t][c]);
+            acc[t][c] = fmaf(w01, f01[c], acc[t][c]);
+            acc[t][c] = fmaf(w10, f10[c], acc[t][c]);
+            acc[t][c] = fmaf(w11, f11[c], acc[t][c]);
+          }
+        }
+        // Corners outside the window but touching the map: global gathers
+        // (rare; the wave skips this when no lane needs it).
+        const bool fb = !inside && !nan_loc;
+        if (__builtin_amdgcn_ballot_w64(fb) != 0) {
+          if (fb) {
+            const int y0 = cur.Y0 + ty, x0 = cur.X0 + tx;
+            const bool vy0 = (uint32_t)y0 < (uint32_t)p.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)p.H;
+            const bool vx0 = (uint32_t)x0 < (uint32_t)p.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)p.W;
+            const uint32_t a00 = img + (uint32_t)y0 * row_bytes + (uint32_t)x0 * pix_bytes + chan;
+#pragma unroll
+            for (int t = 0; t < NCH; ++t) {
+              uint32_t v00[4], v01[4], v10[4], v11[4];
+              const uint32_t ct = (uint32_t)rot[t];
+              buffer_load_words<4>(rin, (vy0 && vx0) ? a00 + ct : kOutOfRange, v00);
+              buffer_load_words<4>(rin, (vy0 && vx1) ? a00 + pix_bytes + ct : kOutOfRange, v01);
+              buffer_load_words<4>(rin, (vy1 && vx0) ? a00 + row_bytes + ct : kOutOfRange, v10);
+              buffer_load_words<4>(rin, (vy1 && vx1) ? a00 + row_bytes + pix_bytes + ct : kOutOfRange, v11);
+              float f00[CPC], f01[CPC], f10[CPC], f11[CPC];
+              unpack<DT, 4>(v00, f00);
+              unpack<DT, 4>(v01, f01);
+              unpack<DT, 4>(v10, f10);
+              unpack<DT, 4>(v11, f11);
+#pragma unroll
+              for (int c = 0; c < CPC; ++c) {
+                acc[t][c] = fmaf(w00, f00[c], acc[t][c]);
+                acc[t][c] = fmaf(w01, f01[c], acc[t][c]);
+                acc[t][c] = fmaf(w10, f10[c], acc[t][c]);
+                acc[t][c] = fmaf(w11, f11[c], acc[t][c]);
+              }
+            }
+          }
+        }
+      }
+
+      // acc[t] holds the chunk at byte offset rot[t] of the 16-channel slice;
+      // a dead lane's store carries an out-of-range offset and is dropped.
+      const uint32_t obase = cur.live ? cur.pg * (uint32_t)(CG * io::kBytes) : kOutOfRange;
+#pragma unroll
+      for (int t = 0; t < NCH; ++t) {
+        uint32_t w[4];
+        pack_words<DT, CPC>(acc[t], w);
+        buffer_store_words<4>(rout, obase + (uint32_t)rot[t], w);
+      }
+    }
+    issue_pgdata(nx);
+
+    item = next;
+    cur = nx;
+  }
+}
+
+namespace {
+
+template <int DT, bool SM>
+hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
+  auto kern = dcn_fwd_lane_kernel<DT, SM>;
+  constexpr int PIXB = lane_pixel_stride<DT>();
+  const size_t lds = ((size_t)kLaneSpanUnit * kLaneSpanUnit + kLaneSpanUnit + 2) * PIXB;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const uint32_t per_cu = DT == DCN_F32 ? 2u : 4u;  // LDS-limited persistent blocks
+  const uint32_t blocks = std::min<uint32_t>(tg.items, per_cu * (uint32_t)cus);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kLaneThreads), lds, s, p, tg);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Stride 1, dilation 1, 3x3 points only; hipErrorNotSupported otherwise.
+hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
+  if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
+    return hipErrorNotSupported;
+  TileGeom tg{};
+  tg.span_h = tg.span_w = kLaneSpanUnit;
+  const int tiles_y = (p.Ho + kLaneTile - 1) / kLaneTile;
+  tg.tiles_x = (p.Wo + kLaneTile - 1) / kLaneTile;
+  tg.tiles_per_img = tiles_y * tg.tiles_x;
+  const int64_t imgs = p.pg_total / ((int64_t)p.Ho * p.Wo * p.G);
+  const int64_t items = imgs * tg.tiles_per_img * p.G;
+  if (items <= 0 || items >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  tg.items = (uint32_t)items;
+  tg.div_g = make_fast_div((uint32_t)p.G);
+  tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
+  tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
+  tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
+  switch (dtype) {
+    case DCN_F32: return softmax ? launch_lane<DCN_F32, true>(p, tg, s) : launch_lane<DCN_F32, false>(p, tg, s);
+    case DCN_F16: return softmax ? launch_lane<DCN_F16, true>(p, tg, s) : launch_lane<DCN_F16, false>(p, tg, s);
+    case DCN_BF16: return softmax ? launch_lane<DCN_BF16, true>(p, tg, s) : launch_lane<DCN_BF16, false>(p, tg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dcn

@@ -35,6 +35,11 @@
  * returns without waiting: DCN_OK means "validated and enqueued".  Outputs are
  * overwritten, never accumulated into, and must not alias any input.
  *
+ * Kernel choice: the forward picks its kernel from the problem (dtype, point
+ * count, stride, dilation, window size).  The environment variable
+ * DCN_MI355X_FWD_PATH = "generic" | "tiled" | "lane", read at every call,
+ * makes it try that kernel first; results agree to rounding either way.
+ *
  * Errors: every entry point returns DCN_OK (0) or a negative dcn_status.
  * Nothing is enqueued when a check fails.  N == 0 is valid and enqueues
  * nothing.  There is no fallback path: an unsupported problem is an error.
@@ -66,7 +71,7 @@ typedef enum dcn_status {
                                  kernel, or a 16-bit backward                          */
     DCN_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                */
     DCN_ERR_TOO_LARGE = -5,   /* one image's input exceeds 2^31-1 bytes, H or W exceeds
-                                 2^24, or one image holds 2^31 or more pixel-groups    */
+                                 2^24, or one image's output exceeds 2^31-1 bytes      */
     DCN_ERR_HIP = -6,         /* the HIP runtime refused a launch; see dcn_status_string */
     DCN_ERR_ABI = -7,         /* problem->struct_size != sizeof(dcn_problem)            */
     DCN_ERR_ARG = -8          /* softmax not 0/1, or offset_scale not finite            */

@@ -89,6 +89,27 @@ def test_forward_small(wl, dtype):
     gate(_np(run_forward(wl, t)), oracle_full(wl, t), dtype, f"{wl.name}/{dtype}")
 
 
+PATH_CASES = [
+    Workload("path_ragged", n=2, h=37, w=29, c=48, groups=3, offset_dist=normal(2.0), seed=41),
+    Workload("path_far", n=1, h=33, w=35, c=32, groups=2, offset_dist=uniform(5.0), seed=42),
+    Workload("path_v4", n=2, h=20, w=17, c=32, groups=2, softmax=False, mask_dist=normal(0.5),
+             seed=43),
+]
+
+
+@pytest.mark.parametrize("path", ["generic", "tiled", "lane"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("wl", PATH_CASES, ids=lambda w: w.name)
+def test_forward_each_kernel(wl, dtype, path, monkeypatch):
+    """Every forward kernel, forced in turn, on shapes spanning several
+    tiles with ragged edges and offsets that leave the tile windows."""
+    monkeypatch.setenv("DCN_MI355X_FWD_PATH", path)
+    wl = wl.replace(dtype=dtype)
+    print(f"forward {wl.name} {dtype} path={path}", flush=True)
+    t = synth.make_inputs(wl)
+    gate(_np(run_forward(wl, t)), oracle_full(wl, t), dtype, f"{wl.name}/{dtype}/{path}")
+
+
 # --------------------------------------------------------------------------- forward, full size
 
 def sampled_pixels(wl, count, seed=0):
