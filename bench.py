@@ -66,6 +66,13 @@ def backward_bytes(wl) -> int:
     return (2 * in_elems + pg * (cg + 6 * wl.points)) * 4
 
 
+def forward_kernel_name(wl) -> str:
+    """Kernel the library runs for this workload's forward (3x3 points,
+    stride and dilation 1): the quad tiled kernel for fp32, the
+    lane-per-pixel-group kernel for 16-bit I/O."""
+    return "dcn_fwd_tile_kernel" if wl.dtype == "f32" else "dcn_fwd_lane_kernel"
+
+
 def traffic_from_profile():
     """HBM bytes per launch measured by rocprofv3 counters, if the committed
     counter summary was taken on the current kernel sources."""
@@ -77,6 +84,82 @@ def traffic_from_profile():
     if not (m_hash and m_val) or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_val.group(1))
+
+
+def launch_stats(fn, stream, iters: int, flush=None):
+    """Per-launch times (ms) of fn() from HIP events on `stream`, one pair of
+    events per launch; with `flush`, it runs before each launch, outside the
+    events, so every launch starts from cold caches."""
+    import torch
+
+    times = []
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    pick = lambda q: times[min(len(times) - 1, int(q * len(times)))]
+    return {"median_ms": round(pick(0.5), 5), "min_ms": round(times[0], 5),
+            "p90_ms": round(pick(0.9), 5), "launches": iters}
+
+
+def summarize_counters(root: pathlib.Path, workload: str) -> str:
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE)
+    and two of its --copy-calibration mode into the committed counter
+    summary: HBM bytes per forward launch, each counter scaled by what it
+    reads for a plain device copy of known size."""
+    import csv
+
+    def per_dispatch(run: str, counter: str, match):
+        vals = {}
+        for f in root.glob(f"{run}/**/*counter_collection.csv"):
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] != counter or not match(row["Kernel_Name"]):
+                    continue
+                d = int(row["Dispatch_Id"])
+                vals[d] = vals.get(d, 0.0) + float(row["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no {counter} rows in {root / run}")
+        return [vals[d] for d in sorted(vals)]
+
+    is_fwd = lambda n: "dcn_fwd" in n
+    is_copy = lambda n: "copy" in n.lower()
+    fetch = per_dispatch("fetch", "FETCH_SIZE", is_fwd)
+    write = per_dispatch("write", "WRITE_SIZE", is_fwd)
+    cfetch = per_dispatch("copy_fetch", "FETCH_SIZE", is_copy)
+    cwrite = per_dispatch("copy_write", "WRITE_SIZE", is_copy)
+    copy_bytes = float(1 << 30)
+    kib = 1024.0
+    f_scale = copy_bytes / (sum(cfetch) / len(cfetch) * kib)
+    w_scale = copy_bytes / (sum(cwrite) / len(cwrite) * kib)
+    f_bytes = sum(fetch) / len(fetch) * kib * f_scale
+    w_bytes = sum(write) / len(write) * kib * w_scale
+    from deformable_convolution_vision_dcn_amd import synth
+
+    alg = forward_bytes(synth.WORKLOADS[workload])
+    lines = [
+        f"# HBM traffic of the forward kernel, workload {workload}",
+        f"kernel_source_sha256: {kernel_source_hash()}",
+        f"forward_dispatches_fetch: {len(fetch)}  write: {len(write)}",
+        f"FETCH_SIZE_KiB_per_dispatch_raw: {sum(fetch) / len(fetch):.1f}",
+        f"WRITE_SIZE_KiB_per_dispatch_raw: {sum(write) / len(write):.1f}",
+        f"copy_calibration: 1 GiB device copy, FETCH_SIZE {sum(cfetch) / len(cfetch):.1f} KiB, "
+        f"WRITE_SIZE {sum(cwrite) / len(cwrite):.1f} KiB per dispatch",
+        f"scale_fetch: {f_scale:.4f}",
+        f"scale_write: {w_scale:.4f}",
+        f"fetch_bytes_per_launch: {f_bytes:.0f}",
+        f"write_bytes_per_launch: {w_bytes:.0f}",
+        f"hbm_bytes_per_launch: {f_bytes + w_bytes:.0f}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_over_algorithmic: {(f_bytes + w_bytes) / alg:.3f}",
+    ]
+    return "\n".join(lines) + "\n"
 
 
 def cpu_baseline(wl, t, images: int):
@@ -109,7 +192,17 @@ def main() -> int:
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--cold-iters", type=int, default=50,
+                    help="forward launches timed one by one after a 512 MB cache flush")
+    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+                    help="write the counter summary from rocprofv3 runs under DIR and exit")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        text = summarize_counters(pathlib.Path(args.summarize_counters),
+                                  args.workload or "stage1_dcnv3_f32")
+        print(text, end="")
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -157,6 +250,14 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     launch_ms = ev0.elapsed_time(ev1) / args.steps  # one launch per step at these sizes
 
+    # Per-launch distributions: warm (back to back) and cold (a 512 MB write,
+    # twice the MALL and far above the L2s, before every launch).
+    fwd = lambda: dcn.dcn_forward(x, off, m, out=y, **kw)
+    scratch = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    warm = launch_stats(fwd, stream, max(args.cold_iters, 1))
+    cold = launch_stats(fwd, stream, max(args.cold_iters, 1), flush=lambda: scratch.fill_(1.0))
+    del scratch
+
     value = wl.samples / (ms_per_step * 1e-3) / 1e9
     fwd_bytes = forward_bytes(wl)
     achieved = fwd_bytes / (launch_ms * 1e-3) / 1e9
@@ -182,9 +283,14 @@ def main() -> int:
                    "samples_per_step": wl.samples},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "dcn_fwd_kernel",
+                     "traffic": traffic, "kernel": forward_kernel_name(wl),
                      "alg_bytes_per_launch": fwd_bytes,
                      "launch_ms": round(launch_ms, 5)},
+        "forward_launch": {
+            "warm": warm, "cold": cold,
+            "cold_GSamples_per_s": round(wl.samples / (cold["median_ms"] * 1e-3) / 1e9, 3),
+            "cold_alg_GB_per_s": round(fwd_bytes / (cold["median_ms"] * 1e-3) / 1e9, 1),
+            "note": "cold = 512 MB cache flush before each launch; median of per-launch HIP events"},
     }
 
     if not args.no_backward and wl.dtype == "f32":
