@@ -17,6 +17,9 @@
 // are reduced across the quad with two DPP quad permutes.  The grad_input
 // scatter uses raw buffer atomics: a corner outside the map carries a byte
 // offset beyond the buffer, and the hardware drops that atomic.
+#include <stdlib.h>
+#include <string.h>
+
 #include "dcn_device.hpp"
 
 namespace dcn {
@@ -210,6 +213,11 @@ hipError_t launch_one(const BwdParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s) {
+  const char *e = getenv("DCN_MI355X_BWD_PATH");
+  if (!(e && !strcmp(e, "generic"))) {
+    const hipError_t t = launch_backward_tiled(softmax, p, s);
+    if (t != hipErrorNotSupported) return t;
+  }
   if (p.f.KH == 3 && p.f.KW == 3)
     return softmax ? launch_one<3, 3, true>(p, s) : launch_one<3, 3, false>(p, s);
   return softmax ? launch_one<0, 0, true>(p, s) : launch_one<0, 0, false>(p, s);

@@ -10,7 +10,7 @@
 // this chip once the corners come from LDS).
 //
 // Block = 256 threads = one (image, 16x16 output tile, group) work item at a
-// time; blocks are persistent (two per CU) and walk items blockIdx, +grid, ...
+// time; blocks are persistent and each XCD walks one contiguous range of items.
 // The input window of an item (its regular 3x3 footprint plus a halo of R
 // pixels for the learned offsets, zero outside the map) is staged in LDS; the
 // next item's window, offsets and logits are requested into registers while
@@ -211,15 +211,16 @@ __global__ void __launch_bounds__(kLaneThreads, 2) dcn_fwd_lane_kernel(FwdParams
 #pragma unroll
   for (int t = 0; t < NCH; ++t) rot[t] = ((t + (int)lane) % NCH) * CHUNK;
 
-  const uint32_t items = tg.items;
-  uint32_t item = xcd_block(blockIdx.x, gridDim.x);
-  Item cur = decode(item < items ? item : 0);
-  if (item < items) {
+  const XcdWalk walk = xcd_walk(blockIdx.x, gridDim.x, tg.items);
+  const uint32_t end = walk.end;
+  uint32_t item = walk.first;
+  Item cur = decode(item < end ? item : 0);
+  if (item < end) {
     issue_window(cur);
     issue_pgdata(cur);
   }
 
-  while (item < items) {
+  while (item < end) {
     __syncthreads();  // every wave is done with the previous window
     store_window();
     __syncthreads();  // the window is in LDS
@@ -228,8 +229,8 @@ __global__ void __launch_bounds__(kLaneThreads, 2) dcn_fwd_lane_kernel(FwdParams
     // its offsets and logits are requested once this item's are consumed.
     // (Issued on the last item too, re-reading its own data, so that no
     // branch changes the count of outstanding loads.)
-    const uint32_t next = item + gridDim.x;
-    const bool more = next < items;  // block-uniform
+    const uint32_t next = item + walk.stride;
+    const bool more = next < end;  // block-uniform
     const Item nx = decode(more ? next : item);
     issue_window(nx);
 

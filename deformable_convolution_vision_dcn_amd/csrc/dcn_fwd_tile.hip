@@ -219,18 +219,19 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
     }
   };
 
-  const uint32_t items = tg.items;
-  uint32_t item = xcd_block(blockIdx.x, gridDim.x);
-  Item cur = decode(item < items ? item : 0);
+  const XcdWalk walk = xcd_walk(blockIdx.x, gridDim.x, tg.items);
+  const uint32_t end = walk.end;
+  uint32_t item = walk.first;
+  Item cur = decode(item < end ? item : 0);
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  if (item < items) {
+  if (item < end) {
     issue_window(cur);
     issue_pgdata(cur, P0{});
     issue_pgdata(cur, P1{});
   }
 
-  while (item < items) {
+  while (item < end) {
     __syncthreads();  // every wave is done reading the previous window
     store_window();
     __syncthreads();  // the window is in LDS
@@ -238,8 +239,8 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
     // The next item's window is requested now and lands during this item's
     // passes; its per-pass offsets/logits are requested as soon as this
     // item's pass has consumed the registers they go to.
-    const uint32_t next = item + gridDim.x;
-    const bool more = next < items;  // block-uniform
+    const uint32_t next = item + walk.stride;
+    const bool more = next < end;  // block-uniform
     const Item nx = decode(more ? next : item);
     if (more) issue_window(nx);
 
@@ -410,7 +411,7 @@ hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kTileLdsLimit);
   if (attr != hipSuccess) return attr;
-  // Persistent blocks: two per CU, each walking work items blockIdx, +grid, ...
+  // Persistent blocks: two per CU; each XCD walks one contiguous range of items.
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

@@ -45,4 +45,26 @@ DCN_HD inline uint32_t xcd_block(uint32_t b, uint32_t nb) {
   return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
 }
 
+// Work split of a persistent launch of nb blocks over `items` work items:
+// XCD x takes one contiguous range of items, sized in proportion to the
+// blocks it runs, and its blocks walk that range in step (first = start +
+// local block index, stride = blocks on the XCD).  Work items that are close
+// in index -- neighbouring tiles, whose input windows overlap -- are then
+// processed by one XCD close in time and share its L2, instead of being
+// dealt round-robin to all eight.
+struct XcdWalk {
+  uint32_t first, stride, end;
+};
+
+DCN_HD inline XcdWalk xcd_walk(uint32_t b, uint32_t nb, uint32_t items) {
+  constexpr uint32_t kXcd = 8;
+  const uint32_t x = b % kXcd, i = b / kXcd;
+  const uint32_t per = nb / kXcd, rem = nb % kXcd;
+  const uint32_t per_x = per + (x < rem ? 1u : 0u);
+  const uint32_t lo = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  const uint32_t start = static_cast<uint32_t>(uint64_t(items) * lo / nb);
+  const uint32_t end = static_cast<uint32_t>(uint64_t(items) * (lo + per_x) / nb);
+  return XcdWalk{start + i, per_x, end};
+}
+
 }  // namespace dcn

@@ -38,7 +38,8 @@
  * Kernel choice: the forward picks its kernel from the problem (dtype, point
  * count, stride, dilation, window size).  The environment variable
  * DCN_MI355X_FWD_PATH = "generic" | "tiled" | "lane", read at every call,
- * makes it try that kernel first; results agree to rounding either way.
+ * makes it try that kernel first; DCN_MI355X_BWD_PATH = "generic" does the
+ * same for the backward.  Results agree to rounding either way.
  *
  * Errors: every entry point returns DCN_OK (0) or a negative dcn_status.
  * Nothing is enqueued when a check fails.  N == 0 is valid and enqueues
@@ -114,7 +115,8 @@ int dcn_forward(const dcn_problem *p, const void *input, const void *offset, con
  *                 the softmax Jacobian when softmax != 0.
  * At integer sampling coordinates the derivative is the one-sided one from the
  * right (the floor convention).  fp32 only (DCN_F32); other dtypes return
- * DCN_ERR_UNSUPPORTED. */
+ * DCN_ERR_UNSUPPORTED.  Enqueues a fill kernel for grad_input and one
+ * backward launch per chunk of images. */
 int dcn_backward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
                  const void *grad_output, void *grad_input, void *grad_offset, void *grad_mask,
                  void *hip_stream);

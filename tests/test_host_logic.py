@@ -44,6 +44,24 @@ int main() {
       if (b >= 8 && xcd_block(b, nb) != xcd_block(b - 8, nb) + 1) { printf("xcd not contiguous nb=%u\n", nb); return 1; }
     }
   }
+  // xcd_walk: every item exactly once, each XCD's items one contiguous range
+  for (uint32_t nb = 1; nb <= 1100; nb += (nb < 40 ? 1 : 53)) {
+    for (uint32_t items : {0u, 1u, 7u, 8u, 9u, nb - 1, nb, nb + 1, 3 * nb + 5, 11520u, 100003u}) {
+      std::vector<int> seen(items, 0);
+      std::vector<uint32_t> lo(8, 0xffffffffu), hi(8, 0), cnt(8, 0);
+      for (uint32_t b = 0; b < nb; ++b) {
+        XcdWalk w = xcd_walk(b, nb, items);
+        if (w.stride == 0) { printf("zero stride nb=%u\n", nb); return 1; }
+        for (uint32_t it = w.first; it < w.end; it += w.stride) {
+          if (it >= items || seen[it]++) { printf("walk not a partition nb=%u items=%u\n", nb, items); return 1; }
+          uint32_t x = b % 8;
+          lo[x] = it < lo[x] ? it : lo[x]; hi[x] = it > hi[x] ? it : hi[x]; ++cnt[x];
+        }
+      }
+      for (uint32_t i = 0; i < items; ++i) if (!seen[i]) { printf("item %u missed nb=%u\n", i, nb); return 1; }
+      for (int x = 0; x < 8; ++x) if (cnt[x] && hi[x] - lo[x] + 1 != cnt[x]) { printf("xcd range gap nb=%u\n", nb); return 1; }
+    }
+  }
   printf("checked %ld bad %ld\n", checked, bad);
   return bad != 0;
 }

@@ -204,6 +204,34 @@ def test_backward(wl):
     gate(_np(gm), rm, "f32", f"{wl.name} grad_mask")
 
 
+BWD_PATH_CASES = [
+    Workload("bwdp_ragged", n=2, h=37, w=29, c=48, groups=3, offset_dist=normal(2.0), seed=51),
+    Workload("bwdp_far", n=1, h=33, w=35, c=32, groups=2, offset_dist=uniform(5.0), seed=52),
+    Workload("bwdp_v4", n=2, h=20, w=17, c=32, groups=2, softmax=False, mask_dist=normal(0.5),
+             seed=53),
+    Workload("bwdp_pad0", n=1, h=19, w=18, c=16, groups=1, pad=(0, 0), offset_dist=normal(3.0),
+             seed=54),
+]
+
+
+@pytest.mark.parametrize("path", ["generic", "tiled"])
+@pytest.mark.parametrize("wl", BWD_PATH_CASES, ids=lambda w: w.name)
+def test_backward_each_kernel(wl, path, monkeypatch):
+    """Both backward kernels, forced in turn, on multi-tile ragged shapes
+    whose offsets also leave the tile windows (the global fix-up path)."""
+    if path == "generic":
+        monkeypatch.setenv("DCN_MI355X_BWD_PATH", "generic")
+    else:
+        monkeypatch.delenv("DCN_MI355X_BWD_PATH", raising=False)
+    print(f"backward {wl.name} path={path}", flush=True)
+    t = synth.make_inputs(wl, with_grad=True)
+    gx, goff, gm = run_backward(wl, t)
+    rx, roff, rm = oracle_backward(wl, t)
+    gate(_np(gx), rx, "f32", f"{wl.name}/{path} grad_input")
+    gate(_np(goff), roff, "f32", f"{wl.name}/{path} grad_offset")
+    gate(_np(gm), rm, "f32", f"{wl.name}/{path} grad_mask")
+
+
 def test_backward_adjoint_at_stage1_size():
     """At the stage-1 size (too big for a quick full oracle backward) the
     grad_input is checked by the adjoint identity <F(x), g> = <x, F^T g>,
