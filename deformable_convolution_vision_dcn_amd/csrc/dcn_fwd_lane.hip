@@ -44,66 +44,6 @@ constexpr int lane_pixel_stride() { return DT == DCN_F32 ? 64 : 32; }
 
 namespace {
 
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
-
-// The 9 (x, y) offset pairs of pixel-group pg as 18 fp32 values.
-template <int DT>
-__device__ __forceinline__ void load_offsets(const void *base, uint32_t pg, float (&o)[18]) {
-  if constexpr (DT == DCN_F32) {
-    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * 18;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src + 4 * q);
-      o[4 * q] = __uint_as_float(v[0]);
-      o[4 * q + 1] = __uint_as_float(v[1]);
-      o[4 * q + 2] = __uint_as_float(v[2]);
-      o[4 * q + 3] = __uint_as_float(v[3]);
-    }
-    const u32x2_a4 v = *reinterpret_cast<const u32x2_a4 *>(src + 16);
-    o[16] = __uint_as_float(v[0]);
-    o[17] = __uint_as_float(v[1]);
-  } else {
-    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * 9;
-    uint32_t w[9];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src + 4 * q);
-      w[4 * q] = v[0];
-      w[4 * q + 1] = v[1];
-      w[4 * q + 2] = v[2];
-      w[4 * q + 3] = v[3];
-    }
-    w[8] = src[8];
-#pragma unroll
-    for (int q = 0; q < 9; ++q) {
-      o[2 * q] = Io<DT>::lo(w[q]);
-      o[2 * q + 1] = Io<DT>::hi(w[q]);
-    }
-  }
-}
-
-// The 9 mask values of pixel-group pg as fp32.
-template <int DT>
-__device__ __forceinline__ void load_mask(const void *base, uint32_t pg, float (&m)[9]) {
-  if constexpr (DT == DCN_F32) {
-    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * 9;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src + 4 * q);
-      m[4 * q] = __uint_as_float(v[0]);
-      m[4 * q + 1] = __uint_as_float(v[1]);
-      m[4 * q + 2] = __uint_as_float(v[2]);
-      m[4 * q + 3] = __uint_as_float(v[3]);
-    }
-    m[8] = __uint_as_float(src[8]);
-  } else {
-    const uint16_t *src = static_cast<const uint16_t *>(base) + (uint64_t)pg * 9;
-#pragma unroll
-    for (int q = 0; q < 9; ++q) m[q] = Io<DT>::lo((uint32_t)src[q]);
-  }
-}
-
 __device__ __forceinline__ void lds_read16(const unsigned char *src, uint32_t (&w)[4]) {
   const uint4 v = *reinterpret_cast<const uint4 *>(src);
   w[0] = v.x;

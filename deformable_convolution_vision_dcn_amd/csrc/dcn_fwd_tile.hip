@@ -111,7 +111,9 @@ constexpr int kTileMaxSpan = 1024;  // window pixels a block can stage
 template <int DT>
 constexpr int tile_pixel_stride() { return DT == DCN_F32 ? DCN_PIXB_F32 : DCN_PIXB_16; }
 
-template <int DT, bool SOFTMAX, int TH, int TW, int R>
+// UNIT: stride 1 and dilation 1, so the window geometry is a compile-time
+// constant (no run-time multiplies on the per-point path).
+template <int DT, bool SOFTMAX, int TH, int TW, int R, bool UNIT>
 __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdParams p, TileGeom tg) {
   using io = Io<DT>;
   constexpr int CG = kGroupChannels;
@@ -132,10 +134,15 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
   const uint32_t pix_bytes = (uint32_t)p.C * io::kBytes;
   const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
-  const int span = tg.span_h * tg.span_w;
-  const int row_lds = tg.span_w * PIXB;
+  constexpr int USPAN = TW + 2 * R + 3;  // window edge at stride 1, dilation 1
+  const int span_w = UNIT ? USPAN : tg.span_w;
+  const int span_h = UNIT ? (TH + 2 * R + 3) : tg.span_h;
+  const int span = span_h * span_w;
+  const int row_lds = span_w * PIXB;
   const int zero_base = span * PIXB;
-  const int lim_y = tg.span_h - 2, lim_x = tg.span_w - 2;
+  const int lim_y = span_h - 2, lim_x = span_w - 2;
+  const int SW = UNIT ? 1 : p.SW, SH = UNIT ? 1 : p.SH;
+  const int DW = UNIT ? 1 : p.DW, DH = UNIT ? 1 : p.DH;
   const float s = p.scale;
 
   // A zero block after the window: samples served from global memory (and
@@ -160,8 +167,8 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
     const uint32_t txi = tile_id - tyi * (uint32_t)tg.tiles_x;
     I.r0 = (int)tyi * TH;
     I.c0 = (int)txi * TW;
-    I.Y0 = I.r0 * p.SH - p.PH - R;  // window origin in input coordinates
-    I.X0 = I.c0 * p.SW - p.PW - R;
+    I.Y0 = I.r0 * SH - p.PH - R;  // window origin in input coordinates
+    I.X0 = I.c0 * SW - p.PW - R;
     I.img = I.n * (uint32_t)p.H * row_bytes;
     I.chan = (I.g * CG + sub * CPL) * io::kBytes;
     return I;
@@ -176,8 +183,8 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
       const int idx = (int)quad + u * QUADS;
       uint32_t offb = kOutOfRange;
       if (idx < span) {
-        const int sy = (int)fast_div((uint32_t)idx, tg.div_span_w);
-        const int sx = idx - sy * tg.span_w;
+        const int sy = UNIT ? idx / USPAN : (int)fast_div((uint32_t)idx, tg.div_span_w);
+        const int sx = idx - sy * span_w;
         const int gy = I.Y0 + sy, gx = I.X0 + sx;
         if ((uint32_t)gy < (uint32_t)p.H && (uint32_t)gx < (uint32_t)p.W)
           offb = I.img + (uint32_t)gy * row_bytes + (uint32_t)gx * pix_bytes + I.chan;
@@ -289,8 +296,8 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
         const float cy = __builtin_amdgcn_fmed3f(dy, -16777216.f, 16777216.f);
         const float fx = floorf(cx), fy = floorf(cy);
         const float lx = cx - fx, ly = cy - fy;
-        const int x0 = wo * p.SW - p.PW + j * p.DW + (int)fx;
-        const int y0 = ho * p.SH - p.PH + i * p.DH + (int)fy;
+        const int x0 = wo * SW - p.PW + j * DW + (int)fx;
+        const int y0 = ho * SH - p.PH + i * DH + (int)fy;
         const float mkk = nan_loc ? __builtin_nanf("") : mk;  // NaN location: NaN weights
         const float wy0 = (1.f - ly) * mkk, wy1 = ly * mkk;
         const float W0 = wy0 * (1.f - lx), W1 = wy0 * lx;
@@ -404,9 +411,9 @@ size_t tile_lds_bytes(const TileGeom &tg, int pixb) {
   return ((size_t)tg.span_h * tg.span_w + tg.span_w + 2) * pixb;  // window + zero block
 }
 
-template <int DT, bool SM>
+template <int DT, bool SM, bool UNIT>
 hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, kHalo>;
+  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, kHalo, UNIT>;
   const size_t lds = tile_lds_bytes(tg, tile_pixel_stride<DT>());
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kTileLdsLimit);
@@ -444,10 +451,19 @@ hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipS
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
   tg.items = (uint32_t)blocks;
+  const bool unit = p.SH == 1 && p.SW == 1 && p.DH == 1 && p.DW == 1;
+  if (unit) {
+    switch (dtype) {
+      case DCN_F32: return softmax ? launch_tile<DCN_F32, true, true>(p, tg, s) : launch_tile<DCN_F32, false, true>(p, tg, s);
+      case DCN_F16: return softmax ? launch_tile<DCN_F16, true, true>(p, tg, s) : launch_tile<DCN_F16, false, true>(p, tg, s);
+      case DCN_BF16: return softmax ? launch_tile<DCN_BF16, true, true>(p, tg, s) : launch_tile<DCN_BF16, false, true>(p, tg, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (dtype) {
-    case DCN_F32: return softmax ? launch_tile<DCN_F32, true>(p, tg, s) : launch_tile<DCN_F32, false>(p, tg, s);
-    case DCN_F16: return softmax ? launch_tile<DCN_F16, true>(p, tg, s) : launch_tile<DCN_F16, false>(p, tg, s);
-    case DCN_BF16: return softmax ? launch_tile<DCN_BF16, true>(p, tg, s) : launch_tile<DCN_BF16, false>(p, tg, s);
+    case DCN_F32: return softmax ? launch_tile<DCN_F32, true, false>(p, tg, s) : launch_tile<DCN_F32, false, false>(p, tg, s);
+    case DCN_F16: return softmax ? launch_tile<DCN_F16, true, false>(p, tg, s) : launch_tile<DCN_F16, false, false>(p, tg, s);
+    case DCN_BF16: return softmax ? launch_tile<DCN_BF16, true, false>(p, tg, s) : launch_tile<DCN_BF16, false, false>(p, tg, s);
     default: return hipErrorInvalidValue;
   }
 }
