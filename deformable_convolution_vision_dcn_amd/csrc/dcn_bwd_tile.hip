@@ -141,6 +141,9 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
   for (int k = 0; k < K; ++k) gb[k] = gdx[k] = gdy[k] = 0.f;
 
   const uint32_t sq = lane / 2, sc = lane % 2;
+  int cro[CH];  // byte offset of channel (c + lane) mod 8 within a pixel slice
+#pragma unroll
+  for (int c = 0; c < CH; ++c) cro[c] = (int)(((uint32_t)c + lane) % CH) * 4;
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {
     const uint32_t chan = (g * CG + h * CH + sc * 4) * 4u;  // this stager's 16 bytes
@@ -162,6 +165,20 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
         gyh[4 * q + 2] = v.z;
         gyh[4 * q + 3] = v.w;
       }
+    }
+    // The same 8 values rotated by this lane's position: gyr[c] = gyh[(c + lane) mod 8]
+    // (a 3-step barrel rotation), for the bank-spread scatter below.
+    float gyr[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) gyr[c] = gyh[c];
+#pragma unroll
+    for (int rs = 1; rs < CH; rs <<= 1) {
+      const bool on = (lane & (uint32_t)rs) != 0;
+      float t[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) t[c] = on ? gyr[(c + rs) % CH] : gyr[c];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) gyr[c] = t[c];
     }
 
     // Fixed-point scale of this half-window.  Every window pixel-channel
@@ -287,15 +304,20 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
       // window as scaled integers (a sample outside it adds into the sink
       // rows); the others, and every sample of a non-finite half, go to
       // grad_input with fp32 global atomics.
-      if (fixed) {
+      // At step c lane l adds channel (c + l) mod 8: with 32-byte pixel slices
+      // a common channel order would put every lane of an instruction in the
+      // same 8 of the 64 LDS banks.  Samples outside the window add nothing
+      // here (their lanes are masked off, so the sink rows see no traffic).
+      if (fixed && inside) {
         const float s00 = w00 * S, s01 = w01 * S, s10 = w10 * S, s11 = w11 * S;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-          const float gc = gyh[c];
-          lds_iadd(gwin + A + 4 * c, __float2int_rn(s00 * gc));
-          lds_iadd(gwin + A + PIXB + 4 * c, __float2int_rn(s01 * gc));
-          lds_iadd(gwin + A + ROW + 4 * c, __float2int_rn(s10 * gc));
-          lds_iadd(gwin + A + ROW + PIXB + 4 * c, __float2int_rn(s11 * gc));
+          const float gc = gyr[c];
+          unsigned char *d = gwin + A + cro[c];
+          lds_iadd(d, __float2int_rn(s00 * gc));
+          lds_iadd(d + PIXB, __float2int_rn(s01 * gc));
+          lds_iadd(d + ROW, __float2int_rn(s10 * gc));
+          lds_iadd(d + ROW + PIXB, __float2int_rn(s11 * gc));
         }
       }
       const bool gscatter = fixed ? fb : (live && !nan_loc);
