@@ -22,7 +22,8 @@
 //   * keeps the per-point channel sums (gm, d/dx, d/dy) of its pixel-group in
 //     registers, so the offset and mask gradients need no cross-lane step.
 // The 16 channels of a group go through LDS as two halves of 8 (32 bytes per
-// window pixel), which keeps the two windows at 62 KB and two blocks per CU.
+// window pixel), which keeps the two windows at 79 KB (halo 8) and two blocks
+// per CU.
 // Samples whose corners leave the window (|s * offset| beyond the halo) take
 // the global path behind a wave ballot: buffer loads for the corners and
 // buffer atomics for the scatter, the buffer range check turning corners
@@ -32,7 +33,10 @@
 namespace dcn {
 
 constexpr int kBwdTile = 16;
-constexpr int kBwdHalo = 6;
+#ifndef DCN_BWD_HALO
+#define DCN_BWD_HALO 8
+#endif
+constexpr int kBwdHalo = DCN_BWD_HALO;
 constexpr int kBwdSpan = kBwdTile + 2 * kBwdHalo + 3;     // window edge, pixels
 constexpr int kBwdPixB = 32;                              // 8 fp32 channels
 constexpr int kBwdRow = kBwdSpan * kBwdPixB;              // LDS bytes per window row
