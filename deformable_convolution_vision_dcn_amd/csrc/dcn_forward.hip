@@ -209,7 +209,7 @@ hipError_t launch_dt(int softmax, const FwdParams &p, hipStream_t s) {
 // Forward path override for tests and measurements: DCN_MI355X_FWD_PATH =
 // "generic", "tiled" or "lane" tries that kernel first (and falls back to the
 // generic kernel where it does not apply).  Read at every call.
-enum class Path { kAuto, kGeneric, kTiled, kLane, kPipe, kQuad };
+enum class Path { kAuto, kGeneric, kTiled, kLane };
 
 Path path_override() {
   const char *e = getenv("DCN_MI355X_FWD_PATH");
@@ -217,8 +217,6 @@ Path path_override() {
   if (!strcmp(e, "generic")) return Path::kGeneric;
   if (!strcmp(e, "tiled")) return Path::kTiled;
   if (!strcmp(e, "lane")) return Path::kLane;
-  if (!strcmp(e, "pipe")) return Path::kPipe;
-  if (!strcmp(e, "quad")) return Path::kQuad;
   return Path::kAuto;
 }
 
@@ -231,14 +229,6 @@ Path path_override() {
 // Everything else runs the untiled kernel.
 hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
   const Path forced = path_override();
-  if (forced == Path::kPipe) {
-    const hipError_t q = launch_forward_pipe(dtype, softmax, p, s);
-    if (q != hipErrorNotSupported) return q;
-  }
-  if (forced == Path::kQuad) {
-    const hipError_t q = launch_forward_quad(dtype, softmax, p, s);
-    if (q != hipErrorNotSupported) return q;
-  }
   const bool lane_first = forced == Path::kLane || (forced == Path::kAuto && dtype != DCN_F32);
   if (forced != Path::kGeneric) {
     if (lane_first) {

@@ -50,8 +50,6 @@ struct TileGeom {
 hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_t s);
 hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipStream_t s);
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s);
-hipError_t launch_forward_pipe(int dtype, int softmax, const FwdParams &p, hipStream_t s);
-hipError_t launch_forward_quad(int dtype, int softmax, const FwdParams &p, hipStream_t s);
 hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_tiled(int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_zero(void *dst, uint64_t bytes, hipStream_t s);

@@ -37,7 +37,7 @@
  *
  * Kernel choice: the forward picks its kernel from the problem (dtype, point
  * count, stride, dilation, window size).  The environment variable
- * DCN_MI355X_FWD_PATH = "generic" | "tiled" | "lane" | "pipe" | "quad", read at every call,
+ * DCN_MI355X_FWD_PATH = "generic" | "tiled" | "lane", read at every call,
  * makes it try that kernel first; DCN_MI355X_BWD_PATH = "generic" does the
  * same for the backward.  Results agree to rounding either way.
  *

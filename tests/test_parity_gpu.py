@@ -97,7 +97,7 @@ PATH_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["generic", "tiled", "lane", "pipe", "quad"])
+@pytest.mark.parametrize("path", ["generic", "tiled", "lane"])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("wl", PATH_CASES, ids=lambda w: w.name)
 def test_forward_each_kernel(wl, dtype, path, monkeypatch):
