@@ -19,9 +19,9 @@
 //
 // Per pixel-group one quad: lane `sub` owns channels [4*sub, 4*sub+4) and
 // computes the location, bilinear weights (modulation folded in) and LDS
-// address of the kernel points k = sub, sub+4, sub+8; DPP quad broadcasts
-// hand them to the other three lanes, so no lane repeats another's address
-// math.  Each lane then reads its 16-byte chunk of the four corners and does
+// address of the kernel points k = 2 sub, 2 sub + 1 (and k = 8 for sub 0);
+// DPP quad broadcasts hand them to the other three lanes, so no lane repeats
+// another's address math.  Each lane then reads its 16-byte chunk of the four corners and does
 // 4 FMAs per channel per point.  The softmax over the nine logits is a quad
 // reduction (max, then sum of exponentials).
 #include <algorithm>
@@ -201,27 +201,59 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
   };
 
   // Own points' offsets and logits of both passes: quad `quad` of pass ps
-  // owns output pixel pp = ps*QUADS + quad of the tile, lane `sub` the points
-  // k = sub + 4r.
+  // owns output pixel pp = ps*QUADS + quad of the tile; lane `sub` owns the
+  // points k = 2 sub, 2 sub + 1 (slots 0, 1) and lane 0 also k = 8 (slot 2),
+  // so a quad reads its pixel-group's offset and mask rows contiguously: one
+  // 16-byte and one 8-byte load per lane (fp32).
   float2 off_n[PASSES][3];
   float lg_n[PASSES][3];
   auto issue_pgdata = [&](const Item &I, auto ps_tag) {
     constexpr int ps = decltype(ps_tag)::value;
-    {
-      const int pp = ps * QUADS + (int)quad;
-      const int ho = I.r0 + pp / TW, wo = I.c0 + pp % TW;
-      const bool live = ho < p.Ho && wo < p.Wo;
-      const uint32_t pg = (((I.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + I.g;
+    typedef uint32_t u4 __attribute__((ext_vector_type(4), aligned(4)));
+    typedef uint32_t u2 __attribute__((ext_vector_type(2), aligned(4)));
+    const int pp = ps * QUADS + (int)quad;
+    const int ho = I.r0 + pp / TW, wo = I.c0 + pp % TW;
+    const bool live = ho < p.Ho && wo < p.Wo;
+    const uint32_t pg = live ? (((I.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + I.g : 0u;
+    const float dead_logit = SOFTMAX ? -INFINITY : 0.f;
+    if constexpr (DT == DCN_F32) {
+      const unsigned char *orow = static_cast<const unsigned char *>(p.offset) + (uint64_t)pg * (K * 8);
+      const unsigned char *mrow = static_cast<const unsigned char *>(p.mask) + (uint64_t)pg * (K * 4);
+      const u4 o = *reinterpret_cast<const u4 *>(orow + 16 * sub);
+      const u2 l = *reinterpret_cast<const u2 *>(mrow + 8 * sub);
+      off_n[ps][0] = make_float2(__uint_as_float(o[0]), __uint_as_float(o[1]));
+      off_n[ps][1] = make_float2(__uint_as_float(o[2]), __uint_as_float(o[3]));
+      lg_n[ps][0] = __uint_as_float(l[0]);
+      lg_n[ps][1] = __uint_as_float(l[1]);
+      if (sub == 0) {
+        const u2 o8 = *reinterpret_cast<const u2 *>(orow + 64);
+        off_n[ps][2] = make_float2(__uint_as_float(o8[0]), __uint_as_float(o8[1]));
+        lg_n[ps][2] = *reinterpret_cast<const float *>(mrow + 32);
+      } else {
+        off_n[ps][2] = make_float2(0.f, 0.f);
+        lg_n[ps][2] = dead_logit;
+      }
+    } else {
+      const uint32_t *orow = static_cast<const uint32_t *>(p.offset) + (uint64_t)pg * K;
+      const u2 o = *reinterpret_cast<const u2 *>(orow + 2 * sub);
+      off_n[ps][0] = make_float2(Io<DT>::lo(o[0]), Io<DT>::hi(o[0]));
+      off_n[ps][1] = make_float2(Io<DT>::lo(o[1]), Io<DT>::hi(o[1]));
+      lg_n[ps][0] = load_one<DT>(p.mask, pg * K + 2 * sub);
+      lg_n[ps][1] = load_one<DT>(p.mask, pg * K + 2 * sub + 1);
+      if (sub == 0) {
+        const uint32_t w8 = orow[8];
+        off_n[ps][2] = make_float2(Io<DT>::lo(w8), Io<DT>::hi(w8));
+        lg_n[ps][2] = load_one<DT>(p.mask, pg * K + 8);
+      } else {
+        off_n[ps][2] = make_float2(0.f, 0.f);
+        lg_n[ps][2] = dead_logit;
+      }
+    }
+    if (!live) {
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
-        const int k = (int)sub + 4 * r;
-        if (live && k < K) {
-          off_n[ps][r] = load_pair<DT>(p.offset, pg * K + k);
-          lg_n[ps][r] = load_one<DT>(p.mask, pg * K + k);
-        } else {
-          off_n[ps][r] = make_float2(0.f, 0.f);
-          lg_n[ps][r] = SOFTMAX ? -INFINITY : 0.f;
-        }
+        off_n[ps][r] = make_float2(0.f, 0.f);
+        lg_n[ps][r] = dead_logit;
       }
     }
   };
@@ -264,7 +296,7 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
         float e[3], sum = 0.f;
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
-          e[r] = ((int)sub + 4 * r < K) ? __expf(lg_n[ps][r] - mx) : 0.f;
+          e[r] = (r < 2 || sub == 0) ? __expf(lg_n[ps][r] - mx) : 0.f;
           sum += e[r];
         }
         const float inv = __builtin_amdgcn_rcpf(quad_sum(sum));
@@ -279,7 +311,7 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
 #pragma unroll
       for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
 
-      // Round r: every lane prepares its own point k = sub + 4r (location,
+      // Round r: every lane prepares its own point of slot r (location,
       // weights with the modulation folded in, window address), then the
       // quad consumes the round's points one owner at a time.  The per-round
       // inputs rotate through scalars (no run-time indexed arrays).
@@ -287,7 +319,7 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
       float mk = m[0], mkn = m[1], mknn = m[2];
 #pragma unroll 1
       for (int r = 0; r < 3; ++r) {
-        const int k = (int)sub + 4 * r;
+        const int k = r < 2 ? 2 * (int)sub + r : (sub == 0 ? 8 : K);  // K: no point
         const int i = k >= 6 ? 2 : (k >= 3 ? 1 : 0);
         const int j = k - 3 * i;
         const float dx = s * o2.x, dy = s * o2.y;
