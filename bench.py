@@ -159,6 +159,20 @@ def summarize_counters(root: pathlib.Path, workload: str) -> str:
         f"algorithmic_bytes_per_launch: {alg}",
         f"traffic_over_algorithmic: {(f_bytes + w_bytes) / alg:.3f}",
     ]
+    # Optional further runs of this script's timed forward: L2 hits / misses
+    # (run "l2") and instruction counters (run "sq"), mean per dispatch.
+    for run in ("l2", "sq"):
+        names = set()
+        for f in root.glob(f"{run}/**/*counter_collection.csv"):
+            for row in csv.DictReader(open(f)):
+                names.add(row["Counter_Name"])
+        vals = {n: per_dispatch(run, n, is_fwd) for n in sorted(names)}
+        for n, v in vals.items():
+            lines.append(f"{n}_per_dispatch: {sum(v) / len(v):.4e}")
+        if run == "l2" and "TCC_HIT_sum" in vals and "TCC_MISS_sum" in vals:
+            h = sum(vals["TCC_HIT_sum"]) / len(vals["TCC_HIT_sum"])
+            m = sum(vals["TCC_MISS_sum"]) / len(vals["TCC_MISS_sum"])
+            lines.append(f"l2_hit_rate: {h / (h + m):.3f}")
     return "\n".join(lines) + "\n"
 
 
