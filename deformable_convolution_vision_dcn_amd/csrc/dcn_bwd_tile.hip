@@ -391,7 +391,8 @@ template <bool SM>
 hipError_t launch_bwd_tile(const BwdParams &p, const TileGeom &tg, hipStream_t s) {
   auto kern = dcn_bwd_tile_kernel<SM>;
   const size_t lds = 2 * (size_t)kBwdWinBytes + 16;  // two windows + the wave bounds
-  static const hipError_t attr = hipFuncSetAttribute(
+  // Set on every launch: the limit is per device and setting it is idempotent.
+  const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(tg.items), dim3(kBwdThreads), lds, s, p, tg);

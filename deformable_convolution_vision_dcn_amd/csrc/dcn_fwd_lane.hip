@@ -301,7 +301,8 @@ hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   auto kern = dcn_fwd_lane_kernel<DT, SM>;
   constexpr int PIXB = lane_pixel_stride<DT>();
   const size_t lds = ((size_t)kLaneSpanUnit * kLaneSpanUnit + kLaneSpanUnit + 2) * PIXB;
-  static const hipError_t attr = hipFuncSetAttribute(
+  // Set on every launch: the limit is per device and setting it is idempotent.
+  const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   int dev = 0, cus = 0;

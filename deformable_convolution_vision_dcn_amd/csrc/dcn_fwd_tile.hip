@@ -447,7 +447,8 @@ template <int DT, bool SM, bool UNIT>
 hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, kHalo, UNIT>;
   const size_t lds = tile_lds_bytes(tg, tile_pixel_stride<DT>());
-  static const hipError_t attr = hipFuncSetAttribute(
+  // Set on every launch: the limit is per device and setting it is idempotent.
+  const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kTileLdsLimit);
   if (attr != hipSuccess) return attr;
   // Persistent blocks: two per CU; each XCD walks one contiguous range of items.

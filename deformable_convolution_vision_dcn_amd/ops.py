@@ -62,6 +62,21 @@ def _expect(t: torch.Tensor, name: str, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _overlaps(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """Whether the byte ranges of two tensors intersect."""
+    if a.numel() == 0 or b.numel() == 0:
+        return False
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    return a0 < b0 + b.numel() * b.element_size() and b0 < a0 + a.numel() * a.element_size()
+
+
+def _no_alias(outputs, inputs):
+    for oname, o in outputs:
+        for iname, i in inputs:
+            if _overlaps(o, i):
+                raise ValueError(f"{oname} overlaps {iname}: outputs must not alias other tensors")
+
+
 def _shapes(x: torch.Tensor, groups, kernel, stride, pad, dilation, offset_scale, softmax):
     if not isinstance(x, torch.Tensor) or x.dim() != 4:
         raise ValueError("input must be a 4-D (N, H, W, C) tensor")
@@ -92,6 +107,7 @@ def dcn_forward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor, *, gr
     if out is None:
         out = torch.empty(shp["out"], dtype=x.dtype, device=x.device)
     _expect(out, "out", shp["out"], x.dtype, x.device)
+    _no_alias([("out", out)], [("input", x), ("offset", offset), ("mask", mask)])
     with torch.cuda.device(x.device):
         st = _capi.dcn_forward(p, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
                                out.data_ptr(), _stream(x.device))
@@ -120,6 +136,10 @@ def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
     _expect(grad_input, "grad_input", x.shape, x.dtype, x.device)
     _expect(grad_offset, "grad_offset", shp["offset"], x.dtype, x.device)
     _expect(grad_mask, "grad_mask", shp["mask"], x.dtype, x.device)
+    outs = [("grad_input", grad_input), ("grad_offset", grad_offset), ("grad_mask", grad_mask)]
+    _no_alias(outs, [("input", x), ("offset", offset), ("mask", mask), ("grad_out", grad_out)])
+    for k, (a, ta) in enumerate(outs):
+        _no_alias([(a, ta)], outs[k + 1:])
     with torch.cuda.device(x.device):
         st = _capi.dcn_backward(p, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
                                 grad_out.data_ptr(), grad_input.data_ptr(),

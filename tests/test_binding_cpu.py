@@ -45,3 +45,18 @@ def test_package_does_not_import_the_oracle():
             "print('oracle' in sys.modules)\n")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert r.stdout.strip() == "False", r.stdout + r.stderr
+
+
+def test_overlap_detection():
+    """Outputs that share bytes with another tensor are refused before any
+    call (the check runs on byte ranges, so CPU tensors exercise it)."""
+    from deformable_convolution_vision_dcn_amd import ops
+
+    base = torch.zeros(1024)
+    a, b, c = base[:512], base[256:768], base[512:]
+    assert ops._overlaps(a, b) and ops._overlaps(b, c)
+    assert not ops._overlaps(a, c)
+    assert not ops._overlaps(a, torch.zeros(0))
+    with pytest.raises(ValueError, match="overlaps"):
+        ops._no_alias([("out", b)], [("input", a)])
+    ops._no_alias([("out", c)], [("input", a)])
