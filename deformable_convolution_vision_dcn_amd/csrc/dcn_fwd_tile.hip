@@ -177,12 +177,15 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
   // Window slices of an item, one quad per pixel: requested into registers
   // while the previous item computes, written to LDS when it is done.
   uint32_t win[MAXPQ][NW];
-  auto issue_window = [&](const Item &I) {
+  // Issued on every path (an item that does not exist loads nothing: every
+  // offset out of range), so that the compiler's count of outstanding loads
+  // stays exact and no wait covers a prefetch before it is needed.
+  auto issue_window = [&](const Item &I, bool valid) {
 #pragma unroll
     for (int u = 0; u < MAXPQ; ++u) {
       const int idx = (int)quad + u * QUADS;
       uint32_t offb = kOutOfRange;
-      if (idx < span) {
+      if (valid && idx < span) {
         const int sy = UNIT ? idx / USPAN : (int)fast_div((uint32_t)idx, tg.div_span_w);
         const int sx = idx - sy * span_w;
         const int gy = I.Y0 + sy, gx = I.X0 + sx;
@@ -203,57 +206,67 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
   // Own points' offsets and logits of both passes: quad `quad` of pass ps
   // owns output pixel pp = ps*QUADS + quad of the tile; lane `sub` owns the
   // points k = 2 sub, 2 sub + 1 (slots 0, 1) and lane 0 also k = 8 (slot 2),
-  // so a quad reads its pixel-group's offset and mask rows contiguously: one
-  // 16-byte and one 8-byte load per lane (fp32).
-  float2 off_n[PASSES][3];
-  float lg_n[PASSES][3];
-  auto issue_pgdata = [&](const Item &I, auto ps_tag) {
-    constexpr int ps = decltype(ps_tag)::value;
+  // so a quad reads its pixel-group's offset and mask rows contiguously.
+  // The rows are kept as loaded (raw words) and decoded where they are used:
+  // any arithmetic on them here would make the wave wait for the load at
+  // once.  Every lane loads every slot (a dead quad reads row 0), so the
+  // loads carry no conditions either.
+  //   fp32:   rw = x, y of k = 2 sub; x, y of 2 sub + 1; x, y of k = 8;
+  //           rl = logits of 2 sub, 2 sub + 1, 8.
+  //   16-bit: rw = (x, y) words of 2 sub, 2 sub + 1, 8; rl = logit halves.
+  constexpr int NRW = DT == DCN_F32 ? 6 : 3;
+  uint32_t rw[PASSES][NRW], rl[PASSES][3];
+  auto load_rows = [&](uint32_t pg, uint32_t (&w)[NRW], uint32_t (&l)[3]) {
     typedef uint32_t u4 __attribute__((ext_vector_type(4), aligned(4)));
     typedef uint32_t u2 __attribute__((ext_vector_type(2), aligned(4)));
-    const int pp = ps * QUADS + (int)quad;
-    const int ho = I.r0 + pp / TW, wo = I.c0 + pp % TW;
-    const bool live = ho < p.Ho && wo < p.Wo;
-    const uint32_t pg = live ? (((I.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + I.g : 0u;
-    const float dead_logit = SOFTMAX ? -INFINITY : 0.f;
     if constexpr (DT == DCN_F32) {
       const unsigned char *orow = static_cast<const unsigned char *>(p.offset) + (uint64_t)pg * (K * 8);
       const unsigned char *mrow = static_cast<const unsigned char *>(p.mask) + (uint64_t)pg * (K * 4);
       const u4 o = *reinterpret_cast<const u4 *>(orow + 16 * sub);
-      const u2 l = *reinterpret_cast<const u2 *>(mrow + 8 * sub);
-      off_n[ps][0] = make_float2(__uint_as_float(o[0]), __uint_as_float(o[1]));
-      off_n[ps][1] = make_float2(__uint_as_float(o[2]), __uint_as_float(o[3]));
-      lg_n[ps][0] = __uint_as_float(l[0]);
-      lg_n[ps][1] = __uint_as_float(l[1]);
-      if (sub == 0) {
-        const u2 o8 = *reinterpret_cast<const u2 *>(orow + 64);
-        off_n[ps][2] = make_float2(__uint_as_float(o8[0]), __uint_as_float(o8[1]));
-        lg_n[ps][2] = *reinterpret_cast<const float *>(mrow + 32);
-      } else {
-        off_n[ps][2] = make_float2(0.f, 0.f);
-        lg_n[ps][2] = dead_logit;
-      }
+      const u2 o8 = *reinterpret_cast<const u2 *>(orow + 64);
+      const u2 lg = *reinterpret_cast<const u2 *>(mrow + 8 * sub);
+      w[0] = o[0];
+      w[1] = o[1];
+      w[2] = o[2];
+      w[3] = o[3];
+      w[4] = o8[0];
+      w[5] = o8[1];
+      l[0] = lg[0];
+      l[1] = lg[1];
+      l[2] = *reinterpret_cast<const uint32_t *>(mrow + 32);
     } else {
       const uint32_t *orow = static_cast<const uint32_t *>(p.offset) + (uint64_t)pg * K;
+      const uint16_t *mrow = static_cast<const uint16_t *>(p.mask) + (uint64_t)pg * K;
       const u2 o = *reinterpret_cast<const u2 *>(orow + 2 * sub);
-      off_n[ps][0] = make_float2(Io<DT>::lo(o[0]), Io<DT>::hi(o[0]));
-      off_n[ps][1] = make_float2(Io<DT>::lo(o[1]), Io<DT>::hi(o[1]));
-      lg_n[ps][0] = load_one<DT>(p.mask, pg * K + 2 * sub);
-      lg_n[ps][1] = load_one<DT>(p.mask, pg * K + 2 * sub + 1);
-      if (sub == 0) {
-        const uint32_t w8 = orow[8];
-        off_n[ps][2] = make_float2(Io<DT>::lo(w8), Io<DT>::hi(w8));
-        lg_n[ps][2] = load_one<DT>(p.mask, pg * K + 8);
-      } else {
-        off_n[ps][2] = make_float2(0.f, 0.f);
-        lg_n[ps][2] = dead_logit;
-      }
+      w[0] = o[0];
+      w[1] = o[1];
+      w[2] = orow[8];
+      l[0] = mrow[2 * sub];
+      l[1] = mrow[2 * sub + 1];
+      l[2] = mrow[8];
     }
-    if (!live) {
+  };
+  auto issue_pgdata = [&](const Item &I, auto ps_tag) {
+    constexpr int ps = decltype(ps_tag)::value;
+    const int pp = ps * QUADS + (int)quad;
+    const int ho = I.r0 + pp / TW, wo = I.c0 + pp % TW;
+    const bool live = ho < p.Ho && wo < p.Wo;
+    const uint32_t pg = live ? (((I.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + I.g : 0u;
+    load_rows(pg, rw[ps], rl[ps]);
+  };
+  // Decoded offsets (x, y) and logits of three slots.
+  auto decode_rows = [&](const uint32_t (&w)[NRW], const uint32_t (&l)[3], float2 (&o)[3], float (&lg)[3]) {
+    if constexpr (DT == DCN_F32) {
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
-        off_n[ps][r] = make_float2(0.f, 0.f);
-        lg_n[ps][r] = dead_logit;
+        o[r] = make_float2(__uint_as_float(w[2 * r]), __uint_as_float(w[2 * r + 1]));
+        lg[r] = __uint_as_float(l[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        o[r] = make_float2(Io<DT>::lo(w[r]), Io<DT>::hi(w[r]));
+        lg[r] = Io<DT>::lo(l[r]);
       }
     }
   };
@@ -265,7 +278,7 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   if (item < end) {
-    issue_window(cur);
+    issue_window(cur, true);
     issue_pgdata(cur, P0{});
     issue_pgdata(cur, P1{});
   }
@@ -281,7 +294,7 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
     const uint32_t next = item + walk.stride;
     const bool more = next < end;  // block-uniform
     const Item nx = decode(more ? next : item);
-    if (more) issue_window(nx);
+    issue_window(nx, more);
 
     auto pass = [&](auto ps_tag) {
       constexpr int ps = decltype(ps_tag)::value;
@@ -290,13 +303,18 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
       if (ho >= p.Ho || wo >= p.Wo) return;  // whole quad leaves together
       const uint32_t pg = (((cur.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + cur.g;
 
-      float m[3];
+      // Offsets and modulation weights of the three slots (softmax over the
+      // quad's nine logits for DCNv3, the raw mask for DCNv4).
+      float2 offs[3];
+      float lgs[3], m[3];
+      decode_rows(rw[ps], rl[ps], offs, lgs);
+      if (sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 only
       if constexpr (SOFTMAX) {
-        const float mx = quad_max(fmaxf(fmaxf(lg_n[ps][0], lg_n[ps][1]), lg_n[ps][2]));
+        const float mx = quad_max(fmaxf(fmaxf(lgs[0], lgs[1]), lgs[2]));
         float e[3], sum = 0.f;
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
-          e[r] = (r < 2 || sub == 0) ? __expf(lg_n[ps][r] - mx) : 0.f;
+          e[r] = (r < 2 || sub == 0) ? __expf(lgs[r] - mx) : 0.f;
           sum += e[r];
         }
         const float inv = __builtin_amdgcn_rcpf(quad_sum(sum));
@@ -304,7 +322,7 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
         for (int r = 0; r < 3; ++r) m[r] = e[r] * inv;
       } else {
 #pragma unroll
-        for (int r = 0; r < 3; ++r) m[r] = lg_n[ps][r];
+        for (int r = 0; r < 3; ++r) m[r] = lgs[r];
       }
 
       float acc[CPL];
@@ -315,7 +333,7 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
       // weights with the modulation folded in, window address), then the
       // quad consumes the round's points one owner at a time.  The per-round
       // inputs rotate through scalars (no run-time indexed arrays).
-      float2 o2 = off_n[ps][0], o2n = off_n[ps][1], o2nn = off_n[ps][2];
+      float2 o2 = offs[0], o2n = offs[1], o2nn = offs[2];
       float mk = m[0], mkn = m[1], mknn = m[2];
 #pragma unroll 1
       for (int r = 0; r < 3; ++r) {
@@ -425,9 +443,9 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
                       outw);
     };
     pass(P0{});
-    if (more) issue_pgdata(nx, P0{});
+    issue_pgdata(nx, P0{});  // unconditional (see issue_window)
     pass(P1{});
-    if (more) issue_pgdata(nx, P1{});
+    issue_pgdata(nx, P1{});
 
     item = next;
     cur = nx;
