@@ -207,15 +207,17 @@ hipError_t launch_dt(int softmax, const FwdParams &p, hipStream_t s) {
 }
 
 // Forward path override for tests and measurements: DCN_MI355X_FWD_PATH =
-// "generic", "tiled" or "lane" tries that kernel first (and falls back to the
-// generic kernel where it does not apply).  Read at every call.
-enum class Path { kAuto, kGeneric, kTiled, kLane };
+// "generic", "tiled" (one group per work item), "pair" (two groups per work
+// item) or "lane" tries that kernel first (and falls back to the generic
+// kernel where it does not apply).  Read at every call.
+enum class Path { kAuto, kGeneric, kTiled, kPair, kLane };
 
 Path path_override() {
   const char *e = getenv("DCN_MI355X_FWD_PATH");
   if (!e) return Path::kAuto;
   if (!strcmp(e, "generic")) return Path::kGeneric;
   if (!strcmp(e, "tiled")) return Path::kTiled;
+  if (!strcmp(e, "pair")) return Path::kPair;
   if (!strcmp(e, "lane")) return Path::kLane;
   return Path::kAuto;
 }
@@ -223,7 +225,8 @@ Path path_override() {
 }  // namespace
 
 // Kernel choice for 3x3 points that fit a tile window: fp32 runs the quad
-// tiled kernel (a quad of lanes per pixel-group), 16-bit I/O the
+// tiled kernel (a quad of lanes per pixel-group; two groups per work item
+// where the group count is even), 16-bit I/O the
 // lane-per-pixel-group kernel, which needs a quarter of the address and
 // weight arithmetic and wins once a pixel's 16 channels are only 32 bytes.
 // Everything else runs the untiled kernel.
@@ -236,7 +239,8 @@ hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_
       if (l != hipErrorNotSupported) return l;
     }
     if (forced != Path::kLane) {
-      const hipError_t t = launch_forward_tiled(dtype, softmax, p, s);
+      const int gpi = forced == Path::kTiled ? 1 : (forced == Path::kPair ? 2 : 0);
+      const hipError_t t = launch_forward_tiled(dtype, softmax, p, s, gpi);
       if (t != hipErrorNotSupported) return t;
     }
   }

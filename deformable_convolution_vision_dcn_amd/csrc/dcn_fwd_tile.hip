@@ -43,6 +43,42 @@ __device__ __forceinline__ float qbcast(float v) {
   return __int_as_float(qbcast<O>(__float_as_int(v)));
 }
 
+// acc[c] += w(lane O of the quad) * v[c]: the broadcast rides on the FMA as a
+// DPP operand instead of a separate move.  The compiler does not look inside
+// asm for the DPP hazard (a VALU write of w then a DPP read of it needs two
+// wait states), hence the s_nop.
+#define DCN_FMA4_DPP(QP)                                                              \
+  asm("s_nop 1\n\t"                                                                  \
+      "v_fmac_f32_dpp %0, %4, %5 " QP " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %1, %4, %6 " QP " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %2, %4, %7 " QP " row_mask:0xf bank_mask:0xf\n\t"              \
+      "v_fmac_f32_dpp %3, %4, %8 " QP " row_mask:0xf bank_mask:0xf"                    \
+      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])                        \
+      : "v"(w), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]))
+template <int O>
+__device__ __forceinline__ void fma4_bcast(float (&acc)[4], float w, const float (&v)[4]) {
+  if constexpr (O == 0) DCN_FMA4_DPP("quad_perm:[0,0,0,0]");
+  if constexpr (O == 1) DCN_FMA4_DPP("quad_perm:[1,1,1,1]");
+  if constexpr (O == 2) DCN_FMA4_DPP("quad_perm:[2,2,2,2]");
+  if constexpr (O == 3) DCN_FMA4_DPP("quad_perm:[3,3,3,3]");
+}
+#undef DCN_FMA4_DPP
+
+// a(lane O of the quad) + b, the broadcast again a DPP operand.
+#define DCN_ADD_DPP(QP)                                                               \
+  asm("s_nop 1\n\tv_add_u32_dpp %0, %1, %2 " QP " row_mask:0xf bank_mask:0xf"         \
+      : "=v"(r) : "v"(a), "v"(b))
+template <int O>
+__device__ __forceinline__ uint32_t add_bcast(uint32_t a, uint32_t b) {
+  uint32_t r;
+  if constexpr (O == 0) DCN_ADD_DPP("quad_perm:[0,0,0,0]");
+  if constexpr (O == 1) DCN_ADD_DPP("quad_perm:[1,1,1,1]");
+  if constexpr (O == 2) DCN_ADD_DPP("quad_perm:[2,2,2,2]");
+  if constexpr (O == 3) DCN_ADD_DPP("quad_perm:[3,3,3,3]");
+  return r;
+}
+#undef DCN_ADD_DPP
+
 __device__ __forceinline__ float quad_max(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
@@ -62,6 +98,29 @@ __device__ __forceinline__ void lds_store(unsigned char *dst, const uint32_t (&w
     *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
   }
 }
+// Read NW words at LDS byte address `addr` (an address, not an offset from a
+// generic pointer, so no base is added on the per-point path).
+template <int NW>
+__device__ __forceinline__ void lds_load_at(uint32_t addr, uint32_t (&w)[NW]) {
+  typedef uint32_t V __attribute__((ext_vector_type(NW)));
+  typedef __attribute__((address_space(3))) const V L;
+  const V v = *(L *)(size_t)addr;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) w[i] = v[i];
+}
+
+// a * b + c on the 24-bit multiplier (full rate; a, b < 2^24).
+__device__ __forceinline__ uint32_t mad24(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t mul24(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_mul_u32_u24 %0, %2, %1" : "=v"(r) : "v"(a), "s"(b));
+  return r;
+}
+
 template <int NW>
 __device__ __forceinline__ void lds_load(const unsigned char *src, uint32_t (&w)[NW]) {
   if constexpr (NW == 4) {
@@ -106,31 +165,57 @@ __device__ __forceinline__ float load_one(const void *base, uint32_t e) {
 #define DCN_PIXB_16 40    // LDS bytes per staged 16-bit pixel slice (32 + pad)
 #endif
 
-constexpr int kTileMaxSpan = 1024;  // window pixels a block can stage
+#ifndef DCN_TILE_MAXSPAN
+#define DCN_TILE_MAXSPAN 1024
+#endif
+#ifndef DCN_PAIR_MAXSPAN
+#define DCN_PAIR_MAXSPAN 1152
+#endif
 
-template <int DT>
-constexpr int tile_pixel_stride() { return DT == DCN_F32 ? DCN_PIXB_F32 : DCN_PIXB_16; }
+// GP = groups per work item.  GP = 2 stages the two neighbouring groups of a
+// pixel together (one 128-byte line in fp32 instead of two half lines): half
+// the window requests per pixel-group, offset and mask rows of both groups
+// read by the same instructions, and a 1024-thread block per CU.
+template <int GP>
+constexpr int tile_max_span() { return GP == 1 ? DCN_TILE_MAXSPAN : DCN_PAIR_MAXSPAN; }
+
+template <int DT, int GP>
+constexpr int tile_pixel_stride() {
+  return GP == 2 ? 2 * kGroupChannels * Io<DT>::kBytes : (DT == DCN_F32 ? DCN_PIXB_F32 : DCN_PIXB_16);
+}
 
 // UNIT: stride 1 and dilation 1, so the window geometry is a compile-time
 // constant (no run-time multiplies on the per-point path).
-template <int DT, bool SOFTMAX, int TH, int TW, int R, bool UNIT>
-__global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdParams p, TileGeom tg) {
+template <int DT, bool SOFTMAX, int TH, int TW, int R, bool UNIT, int GP>
+__global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdParams p, TileGeom tg) {
   using io = Io<DT>;
   constexpr int CG = kGroupChannels;
   constexpr int CPL = 4;                           // channels per lane
   constexpr int NW = CPL * io::kBytes / 4;         // words per lane per corner
   constexpr int LANE_BYTES = CPL * io::kBytes;
-  constexpr int PIXB = tile_pixel_stride<DT>();
-  constexpr int QUADS = 512 / 4;
-  constexpr int PASSES = TH * TW / QUADS;
-  constexpr int MAXPQ = kTileMaxSpan / QUADS;      // window pixels per quad
+  constexpr int THREADS = 512 * GP;
+  constexpr int PIXB = tile_pixel_stride<DT, GP>();
+  constexpr int GBYTES = CG * io::kBytes;          // one group of one pixel
+  constexpr int QUADS = THREADS / 4;
+  constexpr int PIXPP = QUADS / GP;                // output pixels per pass
+  constexpr int PASSES = TH * TW / PIXPP;
+  constexpr int LPP = 4 * GP;                      // lanes per staged window pixel
+  constexpr int WPIX = THREADS / LPP;              // window pixels per slice
+  constexpr int MAXPQ = (tile_max_span<GP>() + WPIX - 1) / WPIX;  // slices per lane
   constexpr int K = 9;
   static_assert(PASSES == 2, "the pass sequence below assumes two passes");
-  static_assert(PIXB % LANE_BYTES == 0 && PIXB % 8 == 0 && PIXB >= 4 * LANE_BYTES, "pixel stride");
+  static_assert(PIXB % LANE_BYTES == 0 && PIXB % 8 == 0 && PIXB >= GP * 4 * LANE_BYTES, "pixel stride");
+  static_assert(GP == 1 || GP == 2, "one or two groups per item");
 
   extern __shared__ __align__(16) unsigned char tile[];
 
+  // Quad -> (output pixel of the pass, group of the item).  With two groups
+  // the four quads of a 16-lane LDS phase are two pixels x two groups, so
+  // their 64-byte corner reads fall in two bank halves per group.
   const uint32_t quad = threadIdx.x >> 2, sub = threadIdx.x & 3;
+  const uint32_t gsel = GP == 1 ? 0u : (quad >> 1) & 1u;
+  const uint32_t pix = GP == 1 ? quad : ((quad >> 2) << 1) | (quad & 1u);
+  const uint32_t wlane = threadIdx.x % LPP;        // 16-byte chunk of a window pixel
   const uint32_t pix_bytes = (uint32_t)p.C * io::kBytes;
   const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
@@ -145,22 +230,40 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
   const int DW = UNIT ? 1 : p.DW, DH = UNIT ? 1 : p.DH;
   const float s = p.scale;
 
+  // Window coordinates of the kernel point of each own slot before its
+  // offset, for pass 0 (pass 1 adds PIXPP / TW output rows), packed as three
+  // 10-bit fields (every coordinate is below the span, at most 1023).  The
+  // output pixel of the quad is (pix / TW, pix % TW) within its pass; slot r
+  // holds k = 2 sub + r (r < 2) or k = 8.
+  uint32_t bxp = 0, byp = 0;
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    const int k = r < 2 ? 2 * (int)sub + r : 8;
+    const int i = k / 3, j = k - 3 * (k / 3);
+    bxp |= (uint32_t)((int)(pix % TW) * SW + R + j * DW) << (10 * r);
+    byp |= (uint32_t)((int)(pix / TW) * SH + R + i * DH) << (10 * r);
+  }
+  typedef __attribute__((address_space(3))) unsigned char lds_byte;
+  const uint32_t lane_chunk = (uint32_t)(size_t)(lds_byte *)tile + gsel * GBYTES + sub * LANE_BYTES;
+
   // A zero block after the window: samples served from global memory (and
   // NaN locations) read their main-path corners here, contributing w * 0.
   // Written once; the first barrier of the item loop orders it.
-  for (int z = (int)threadIdx.x * 8; z < row_lds + 2 * PIXB; z += 512 * 8)
+  for (int z = (int)threadIdx.x * 8; z < row_lds + 2 * PIXB; z += THREADS * 8)
     *reinterpret_cast<uint2 *>(tile + zero_base + z) = make_uint2(0, 0);
 
-  // Work item -> (n, tile, g); g varies fastest so the items that share an
-  // input window's cache lines (neighbouring groups) run close in time.
+  // Work item -> (n, tile, first group g); g varies fastest so the items that
+  // share an input window's cache lines (neighbouring groups) run close in
+  // time.  chan: this quad's group and lane chunk (the fix-up gathers);
+  // wchan: this lane's chunk of a staged window pixel.
   struct Item {
-    uint32_t g, n, img, chan;
+    uint32_t g, n, img, chan, wchan;
     int r0, c0, Y0, X0;
   };
   auto decode = [&](uint32_t it) {
     Item I;
     const uint32_t t = fast_div(it, tg.div_g);
-    I.g = it - t * (uint32_t)p.G;
+    I.g = (it - t * ((uint32_t)p.G / GP)) * GP;
     I.n = fast_div(t, tg.div_tiles);
     const uint32_t tile_id = t - I.n * (uint32_t)tg.tiles_per_img;
     const uint32_t tyi = fast_div(tile_id, tg.div_tiles_x);
@@ -170,11 +273,12 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
     I.Y0 = I.r0 * SH - p.PH - R;  // window origin in input coordinates
     I.X0 = I.c0 * SW - p.PW - R;
     I.img = I.n * (uint32_t)p.H * row_bytes;
-    I.chan = (I.g * CG + sub * CPL) * io::kBytes;
+    I.chan = ((I.g + gsel) * CG + sub * CPL) * io::kBytes;
+    I.wchan = I.g * GBYTES + wlane * LANE_BYTES;
     return I;
   };
 
-  // Window slices of an item, one quad per pixel: requested into registers
+  // Window slices of an item, LPP lanes per pixel: requested into registers
   // while the previous item computes, written to LDS when it is done.
   uint32_t win[MAXPQ][NW];
   // Issued on every path (an item that does not exist loads nothing: every
@@ -183,14 +287,14 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
   auto issue_window = [&](const Item &I, bool valid) {
 #pragma unroll
     for (int u = 0; u < MAXPQ; ++u) {
-      const int idx = (int)quad + u * QUADS;
+      const int idx = (int)(threadIdx.x / LPP) + u * WPIX;
       uint32_t offb = kOutOfRange;
       if (valid && idx < span) {
         const int sy = UNIT ? idx / USPAN : (int)fast_div((uint32_t)idx, tg.div_span_w);
         const int sx = idx - sy * span_w;
         const int gy = I.Y0 + sy, gx = I.X0 + sx;
         if ((uint32_t)gy < (uint32_t)p.H && (uint32_t)gx < (uint32_t)p.W)
-          offb = I.img + (uint32_t)gy * row_bytes + (uint32_t)gx * pix_bytes + I.chan;
+          offb = I.img + (uint32_t)gy * row_bytes + (uint32_t)gx * pix_bytes + I.wchan;
       }
       buffer_load_words<NW>(rin, offb, win[u]);
     }
@@ -198,13 +302,13 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
   auto store_window = [&]() {
 #pragma unroll
     for (int u = 0; u < MAXPQ; ++u) {
-      const int idx = (int)quad + u * QUADS;
-      if (idx < span) lds_store<NW>(tile + idx * PIXB + sub * LANE_BYTES, win[u]);
+      const int idx = (int)(threadIdx.x / LPP) + u * WPIX;
+      if (idx < span) lds_store<NW>(tile + idx * PIXB + wlane * LANE_BYTES, win[u]);
     }
   };
 
-  // Own points' offsets and logits of both passes: quad `quad` of pass ps
-  // owns output pixel pp = ps*QUADS + quad of the tile; lane `sub` owns the
+  // Own points' offsets and logits of both passes: the quad owns output
+  // pixel pp = ps*PIXPP + pix of the tile, group g + gsel; lane `sub` owns the
   // points k = 2 sub, 2 sub + 1 (slots 0, 1) and lane 0 also k = 8 (slot 2),
   // so a quad reads its pixel-group's offset and mask rows contiguously.
   // The rows are kept as loaded (raw words) and decoded where they are used:
@@ -248,10 +352,10 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
   };
   auto issue_pgdata = [&](const Item &I, auto ps_tag) {
     constexpr int ps = decltype(ps_tag)::value;
-    const int pp = ps * QUADS + (int)quad;
+    const int pp = ps * PIXPP + (int)pix;
     const int ho = I.r0 + pp / TW, wo = I.c0 + pp % TW;
     const bool live = ho < p.Ho && wo < p.Wo;
-    const uint32_t pg = live ? (((I.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + I.g : 0u;
+    const uint32_t pg = live ? (((I.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + I.g + gsel : 0u;
     load_rows(pg, rw[ps], rl[ps]);
   };
   // Decoded offsets (x, y) and logits of three slots.
@@ -298,10 +402,10 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
 
     auto pass = [&](auto ps_tag) {
       constexpr int ps = decltype(ps_tag)::value;
-      const int pp = ps * QUADS + (int)quad;
+      const int pp = ps * PIXPP + (int)pix;
       const int ho = cur.r0 + pp / TW, wo = cur.c0 + pp % TW;
       if (ho >= p.Ho || wo >= p.Wo) return;  // whole quad leaves together
-      const uint32_t pg = (((cur.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + cur.g;
+      const uint32_t pg = (((cur.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + cur.g + gsel;
 
       // Offsets and modulation weights of the three slots (softmax over the
       // quad's nine logits for DCNv3, the raw mask for DCNv4).
@@ -331,67 +435,58 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
 
       // Round r: every lane prepares its own point of slot r (location,
       // weights with the modulation folded in, window address), then the
-      // quad consumes the round's points one owner at a time.  The per-round
-      // inputs rotate through scalars (no run-time indexed arrays).
+      // quad consumes the round's points one owner at a time, the owner's
+      // address and weights reaching the other lanes as DPP operands.  The
+      // per-round inputs rotate through scalars (no run-time indexed arrays).
       float2 o2 = offs[0], o2n = offs[1], o2nn = offs[2];
       float mk = m[0], mkn = m[1], mknn = m[2];
+      const int by_pass = ps * (PIXPP / TW) * SH;
 #pragma unroll 1
       for (int r = 0; r < 3; ++r) {
-        const int k = r < 2 ? 2 * (int)sub + r : (sub == 0 ? 8 : K);  // K: no point
-        const int i = k >= 6 ? 2 : (k >= 3 ? 1 : 0);
-        const int j = k - 3 * i;
         const float dx = s * o2.x, dy = s * o2.y;
         const bool nan_loc = (dx != dx) | (dy != dy);
         const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
         const float cy = __builtin_amdgcn_fmed3f(dy, -16777216.f, 16777216.f);
         const float fx = floorf(cx), fy = floorf(cy);
         const float lx = cx - fx, ly = cy - fy;
-        const int x0 = wo * SW - p.PW + j * DW + (int)fx;
-        const int y0 = ho * SH - p.PH + i * DH + (int)fy;
+        // window coordinates of the top-left corner
+        const int tx = (int)((bxp >> (10 * r)) & 1023u) + (int)fx;
+        const int ty = (int)((byp >> (10 * r)) & 1023u) + by_pass + (int)fy;
         const float mkk = nan_loc ? __builtin_nanf("") : mk;  // NaN location: NaN weights
-        const float wy0 = (1.f - ly) * mkk, wy1 = ly * mkk;
-        const float W0 = wy0 * (1.f - lx), W1 = wy0 * lx;
-        const float W2 = wy1 * (1.f - lx), W3 = wy1 * lx;
-        const int ty = y0 - cur.Y0, tx = x0 - cur.X0;
+        const float wy1 = ly * mkk, wy0 = mkk - wy1;
+        const float W1 = wy0 * lx, W0 = wy0 - W1;
+        const float W3 = wy1 * lx, W2 = wy1 - W3;
         const bool inside = !nan_loc && (uint32_t)ty <= (uint32_t)lim_y && (uint32_t)tx <= (uint32_t)lim_x;
-        const int A = inside ? (int)__umul24((uint32_t)ty, (uint32_t)row_lds) + tx * PIXB : zero_base;
+        const uint32_t A = inside ? mad24((uint32_t)ty, (uint32_t)row_lds, mul24((uint32_t)tx, PIXB)) : (uint32_t)zero_base;
         // outside the window but touching the map: needs the global fix-up
-        const bool fb = !inside && !nan_loc && (uint32_t)(y0 + 1) <= (uint32_t)p.H &&
-                        (uint32_t)(x0 + 1) <= (uint32_t)p.W;
+        const bool fb = !inside && !nan_loc && (uint32_t)(cur.Y0 + 1 + ty) <= (uint32_t)p.H &&
+                        (uint32_t)(cur.X0 + 1 + tx) <= (uint32_t)p.W;
 
         // Main path, no branches: gather the round's corners from LDS.
         auto point = [&](auto o_tag) {
           constexpr int O = decltype(o_tag)::value;
-          const int a = qbcast<O>(A);
-          const float w00 = qbcast<O>(W0), w01 = qbcast<O>(W1);
-          const float w10 = qbcast<O>(W2), w11 = qbcast<O>(W3);
           uint32_t q00[NW], q01[NW], q10[NW], q11[NW];
-          const unsigned char *src = tile + a + sub * LANE_BYTES;
-          lds_load<NW>(src, q00);
-          lds_load<NW>(src + PIXB, q01);
-          lds_load<NW>(src + row_lds, q10);
-          lds_load<NW>(src + row_lds + PIXB, q11);
+          const uint32_t src = add_bcast<O>(A, lane_chunk);
+          lds_load_at<NW>(src, q00);
+          lds_load_at<NW>(src + PIXB, q01);
+          lds_load_at<NW>(src + row_lds, q10);
+          lds_load_at<NW>(src + row_lds + PIXB, q11);
           float v00[CPL], v01[CPL], v10[CPL], v11[CPL];
           unpack<DT, NW>(q00, v00);
           unpack<DT, NW>(q01, v01);
           unpack<DT, NW>(q10, v10);
           unpack<DT, NW>(q11, v11);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            acc[c] = fmaf(w00, v00[c], acc[c]);
-            acc[c] = fmaf(w01, v01[c], acc[c]);
-            acc[c] = fmaf(w10, v10[c], acc[c]);
-            acc[c] = fmaf(w11, v11[c], acc[c]);
-          }
+          fma4_bcast<O>(acc, W0, v00);
+          fma4_bcast<O>(acc, W1, v01);
+          fma4_bcast<O>(acc, W2, v10);
+          fma4_bcast<O>(acc, W3, v11);
         };
         // Fix-up for points whose corners left the window: global gathers,
         // the buffer range check reading 0 for corners outside the map.
         auto fixup = [&](auto o_tag) {
           constexpr int O = decltype(o_tag)::value;
           if (!qbcast<O>((int)fb)) return;
-          const float w00 = qbcast<O>(W0), w01 = qbcast<O>(W1);
-          const float w10 = qbcast<O>(W2), w11 = qbcast<O>(W3);
-          const int yb = qbcast<O>(y0), xb = qbcast<O>(x0);
+          const int yb = qbcast<O>(ty) + cur.Y0, xb = qbcast<O>(tx) + cur.X0;
           const bool vy0 = (uint32_t)yb < (uint32_t)p.H, vy1 = (uint32_t)(yb + 1) < (uint32_t)p.H;
           const bool vx0 = (uint32_t)xb < (uint32_t)p.W, vx1 = (uint32_t)(xb + 1) < (uint32_t)p.W;
           const uint32_t a00 = cur.img + (uint32_t)yb * row_bytes + (uint32_t)xb * pix_bytes + cur.chan;
@@ -405,13 +500,10 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
           unpack<DT, NW>(q01, v01);
           unpack<DT, NW>(q10, v10);
           unpack<DT, NW>(q11, v11);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            acc[c] = fmaf(w00, v00[c], acc[c]);
-            acc[c] = fmaf(w01, v01[c], acc[c]);
-            acc[c] = fmaf(w10, v10[c], acc[c]);
-            acc[c] = fmaf(w11, v11[c], acc[c]);
-          }
+          fma4_bcast<O>(acc, W0, v00);
+          fma4_bcast<O>(acc, W1, v01);
+          fma4_bcast<O>(acc, W2, v10);
+          fma4_bcast<O>(acc, W3, v11);
         };
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
@@ -423,7 +515,7 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
           point(I2{});
           point(I3{});
         }
-        if (__builtin_amdgcn_ballot_w64(fb) != 0) {  // rare: a quad of the wave left its window
+        if (__builtin_amdgcn_ballot_w64(fb) != 0) {  // a quad of the wave left its window
           fixup(I0{});
           if (r < 2) {
             fixup(I1{});
@@ -454,69 +546,105 @@ __global__ void __launch_bounds__(512, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdPa
 
 namespace {
 
-constexpr int kTileH = 16, kTileW = 16, kHalo = 6;
-constexpr int kTileLdsLimit = 80 * 1024;  // two blocks per CU
+#ifndef DCN_TILE_HALO
+#define DCN_TILE_HALO 6
+#endif
+#ifndef DCN_PAIR_HALO
+#define DCN_PAIR_HALO 7
+#endif
+constexpr int kTileH = 16, kTileW = 16;
+// Halo and LDS budget per variant: one group per item runs two 512-thread
+// blocks per CU (80 KB each); two groups per item one 1024-thread block
+// (up to the 160 KB of a CU).
+template <int GP>
+constexpr int tile_halo() { return GP == 1 ? DCN_TILE_HALO : DCN_PAIR_HALO; }
+template <int GP>
+constexpr int tile_lds_limit() { return GP == 1 ? 80 * 1024 : 160 * 1024; }
 
 size_t tile_lds_bytes(const TileGeom &tg, int pixb) {
   return ((size_t)tg.span_h * tg.span_w + tg.span_w + 2) * pixb;  // window + zero block
 }
 
-template <int DT, bool SM, bool UNIT>
+template <int DT, bool SM, bool UNIT, int GP>
 hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, kHalo, UNIT>;
-  const size_t lds = tile_lds_bytes(tg, tile_pixel_stride<DT>());
+  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, tile_halo<GP>(), UNIT, GP>;
+  const size_t lds = tile_lds_bytes(tg, tile_pixel_stride<DT, GP>());
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kTileLdsLimit);
+      reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, tile_lds_limit<GP>());
   if (attr != hipSuccess) return attr;
-  // Persistent blocks: two per CU; each XCD walks one contiguous range of items.
+  // Persistent blocks, 1024 threads per CU; each XCD walks one contiguous
+  // range of items.
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const uint32_t blocks = std::min<uint32_t>(tg.items, 2u * (uint32_t)cus);
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(512), lds, s, p, tg);
+  const uint32_t blocks = std::min<uint32_t>(tg.items, (2u / GP) * (uint32_t)cus);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(512 * GP), lds, s, p, tg);
   return hipGetLastError();
+}
+
+template <int DT, int GP>
+hipError_t launch_tile_dt(int softmax, bool unit, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
+  if (unit) return softmax ? launch_tile<DT, true, true, GP>(p, tg, s) : launch_tile<DT, false, true, GP>(p, tg, s);
+  if constexpr (GP == 2) {
+    return hipErrorNotSupported;  // strided/dilated windows: one group per item
+  } else {
+    return softmax ? launch_tile<DT, true, false, GP>(p, tg, s) : launch_tile<DT, false, false, GP>(p, tg, s);
+  }
+}
+
+// Window geometry and work items for GP groups per item; false when the
+// problem does not fit this variant.
+template <int GP>
+bool tile_geometry(int dtype, const FwdParams &p, TileGeom &tg) {
+  if (p.G % GP != 0) return false;
+  const int halo = tile_halo<GP>();
+  tg = TileGeom{};
+  tg.span_h = (kTileH - 1) * p.SH + 2 * p.DH + 2 * halo + 2;
+  tg.span_w = (kTileW - 1) * p.SW + 2 * p.DW + 2 * halo + 2;
+  const int pixb = dtype == DCN_F32 ? tile_pixel_stride<DCN_F32, GP>() : tile_pixel_stride<DCN_F16, GP>();
+  if (tile_lds_bytes(tg, pixb) > (size_t)tile_lds_limit<GP>()) return false;
+  if (tg.span_h * tg.span_w > tile_max_span<GP>()) return false;
+  const int tiles_y = (p.Ho + kTileH - 1) / kTileH;
+  tg.tiles_x = (p.Wo + kTileW - 1) / kTileW;
+  tg.tiles_per_img = tiles_y * tg.tiles_x;
+  const int64_t imgs = p.pg_total / ((int64_t)p.Ho * p.Wo * p.G);
+  const int64_t items = imgs * tg.tiles_per_img * (p.G / GP);
+  if (items <= 0 || items >= (int64_t(1) << 31)) return false;
+  tg.div_g = make_fast_div((uint32_t)(p.G / GP));
+  tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
+  tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
+  tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
+  tg.items = (uint32_t)items;
+  return true;
+}
+
+template <int GP>
+hipError_t launch_tile_gp(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
+  TileGeom tg;
+  if (!tile_geometry<GP>(dtype, p, tg)) return hipErrorNotSupported;
+  const bool unit = p.SH == 1 && p.SW == 1 && p.DH == 1 && p.DW == 1;
+  switch (dtype) {
+    case DCN_F32: return launch_tile_dt<DCN_F32, GP>(softmax, unit, p, tg, s);
+    case DCN_F16: return launch_tile_dt<DCN_F16, GP>(softmax, unit, p, tg, s);
+    case DCN_BF16: return launch_tile_dt<DCN_BF16, GP>(softmax, unit, p, tg, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 // Returns hipErrorNotSupported (nothing launched) when the problem is not a
-// 3x3 one or its window does not fit the LDS budget.
-hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
+// 3x3 one or its window does not fit the LDS budget.  groups_per_item: 1 or
+// 2 forces that variant; 0 takes two groups per item where they fit.
+hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipStream_t s, int groups_per_item) {
   if (p.KH != 3 || p.KW != 3) return hipErrorNotSupported;
-  TileGeom tg{};
-  tg.span_h = (kTileH - 1) * p.SH + 2 * p.DH + 2 * kHalo + 2;
-  tg.span_w = (kTileW - 1) * p.SW + 2 * p.DW + 2 * kHalo + 2;
-  const int pixb = dtype == DCN_F32 ? tile_pixel_stride<DCN_F32>() : tile_pixel_stride<DCN_F16>();
-  if (tile_lds_bytes(tg, pixb) > (size_t)kTileLdsLimit) return hipErrorNotSupported;
-  if (tg.span_h * tg.span_w > kTileMaxSpan) return hipErrorNotSupported;
-  const int tiles_y = (p.Ho + kTileH - 1) / kTileH;
-  tg.tiles_x = (p.Wo + kTileW - 1) / kTileW;
-  tg.tiles_per_img = tiles_y * tg.tiles_x;
-  const int64_t imgs = p.pg_total / ((int64_t)p.Ho * p.Wo * p.G);
-  const int64_t blocks = imgs * tg.tiles_per_img * p.G;
-  if (blocks <= 0 || blocks >= (int64_t(1) << 31)) return hipErrorNotSupported;
-  tg.div_g = make_fast_div((uint32_t)p.G);
-  tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
-  tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
-  tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
-  tg.items = (uint32_t)blocks;
-  const bool unit = p.SH == 1 && p.SW == 1 && p.DH == 1 && p.DW == 1;
-  if (unit) {
-    switch (dtype) {
-      case DCN_F32: return softmax ? launch_tile<DCN_F32, true, true>(p, tg, s) : launch_tile<DCN_F32, false, true>(p, tg, s);
-      case DCN_F16: return softmax ? launch_tile<DCN_F16, true, true>(p, tg, s) : launch_tile<DCN_F16, false, true>(p, tg, s);
-      case DCN_BF16: return softmax ? launch_tile<DCN_BF16, true, true>(p, tg, s) : launch_tile<DCN_BF16, false, true>(p, tg, s);
-      default: return hipErrorInvalidValue;
-    }
+  if (groups_per_item != 1) {
+    const hipError_t e = launch_tile_gp<2>(dtype, softmax, p, s);
+    if (e != hipErrorNotSupported || groups_per_item == 2) return e;
   }
-  switch (dtype) {
-    case DCN_F32: return softmax ? launch_tile<DCN_F32, true, false>(p, tg, s) : launch_tile<DCN_F32, false, false>(p, tg, s);
-    case DCN_F16: return softmax ? launch_tile<DCN_F16, true, false>(p, tg, s) : launch_tile<DCN_F16, false, false>(p, tg, s);
-    case DCN_BF16: return softmax ? launch_tile<DCN_BF16, true, false>(p, tg, s) : launch_tile<DCN_BF16, false, false>(p, tg, s);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_tile_gp<1>(dtype, softmax, p, s);
 }
 
 }  // namespace dcn

@@ -48,7 +48,8 @@ struct TileGeom {
 };
 
 hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_t s);
-hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipStream_t s);
+hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipStream_t s,
+                                int groups_per_item);
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s);
 hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_tiled(int softmax, const BwdParams &p, hipStream_t s);

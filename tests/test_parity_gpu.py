@@ -94,10 +94,11 @@ PATH_CASES = [
     Workload("path_far", n=1, h=33, w=35, c=32, groups=2, offset_dist=uniform(5.0), seed=42),
     Workload("path_v4", n=2, h=20, w=17, c=32, groups=2, softmax=False, mask_dist=normal(0.5),
              seed=43),
+    Workload("path_pairs", n=2, h=37, w=29, c=96, groups=6, offset_dist=normal(2.5), seed=44),
 ]
 
 
-@pytest.mark.parametrize("path", ["generic", "tiled", "lane"])
+@pytest.mark.parametrize("path", ["generic", "tiled", "pair", "lane"])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("wl", PATH_CASES, ids=lambda w: w.name)
 def test_forward_each_kernel(wl, dtype, path, monkeypatch):
