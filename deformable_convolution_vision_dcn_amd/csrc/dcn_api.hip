@@ -43,7 +43,9 @@ int validate(const dcn_problem *p, int64_t *ho_out, int64_t *wo_out) {
   if ((int64_t)p->kernel_h * p->kernel_w > dcn::kMaxPoints) return DCN_ERR_UNSUPPORTED;
   const int64_t img_bytes = (int64_t)p->h * p->w * p->c * elem_bytes(p->dtype);
   const int64_t img_out_bytes = ho * wo * p->c * elem_bytes(p->dtype);
-  if (img_bytes > kMaxBytes31 || img_out_bytes > kMaxBytes31) return DCN_ERR_TOO_LARGE;
+  const int64_t img_off_bytes = ho * wo * p->groups * p->kernel_h * p->kernel_w * 2 * elem_bytes(p->dtype);
+  if (img_bytes > kMaxBytes31 || img_out_bytes > kMaxBytes31 || img_off_bytes > kMaxBytes31)
+    return DCN_ERR_TOO_LARGE;
   if (ho_out) *ho_out = ho;
   if (wo_out) *wo_out = wo;
   return DCN_OK;
@@ -80,15 +82,19 @@ dcn::FwdParams geometry(const dcn_problem *p, int64_t ho, int64_t wo) {
   return f;
 }
 
-// Images per launch: every chunk keeps its input and its output below 2^31
-// bytes, the reach of the kernels' 32-bit buffer offsets (pixel-group
-// indices then stay below 2^31 / 16 as well).
+// Images per launch: every chunk keeps its input, output and offset tensors
+// (the mask is half the offsets) below 2^31 bytes, the reach of the kernels'
+// 32-bit buffer offsets (pixel-group indices then stay below 2^31 / 16 as
+// well).
 int64_t images_per_chunk(const dcn_problem *p, int64_t ho, int64_t wo) {
   const int64_t img_bytes = (int64_t)p->h * p->w * p->c * elem_bytes(p->dtype);
   const int64_t img_out_bytes = ho * wo * p->c * elem_bytes(p->dtype);
+  const int64_t img_off_bytes = ho * wo * p->groups * p->kernel_h * p->kernel_w * 2 * elem_bytes(p->dtype);
   int64_t per = kMaxBytes31 / img_bytes;
   const int64_t per2 = kMaxBytes31 / img_out_bytes;
+  const int64_t per3 = kMaxBytes31 / img_off_bytes;
   if (per2 < per) per = per2;
+  if (per3 < per) per = per3;
   return per < 1 ? 1 : per;
 }
 
@@ -124,6 +130,9 @@ int dcn_forward(const dcn_problem *p, const void *input, const void *offset, con
     f.mask = static_cast<const char *>(mask) + n0 * img_pg * K * eb;
     f.output = static_cast<char *>(output) + n0 * img_pg * dcn::kGroupChannels * eb;
     f.in_bytes = (uint32_t)(nc * img_in);
+    f.off_bytes = (uint32_t)(nc * img_pg * K * 2 * eb);
+    f.mask_bytes = (uint32_t)(nc * img_pg * K * eb);
+    f.out_bytes = (uint32_t)(nc * img_pg * dcn::kGroupChannels * eb);
     f.pg_total = (uint32_t)(nc * img_pg);
     const hipError_t e = dcn::launch_forward(p->dtype, p->softmax, f, stream);
     if (e != hipSuccess) return hip_fail(e);
@@ -162,6 +171,9 @@ int dcn_backward(const dcn_problem *p, const void *input, const void *offset, co
     b.f.mask = static_cast<const float *>(mask) + n0 * img_pg * K;
     b.f.output = nullptr;
     b.f.in_bytes = (uint32_t)(nc * img_in);
+    b.f.off_bytes = (uint32_t)(nc * img_pg * K * 2 * 4);
+    b.f.mask_bytes = (uint32_t)(nc * img_pg * K * 4);
+    b.f.out_bytes = 0;
     b.f.pg_total = (uint32_t)(nc * img_pg);
     b.grad_out = static_cast<const float *>(grad_output) + n0 * img_pg * dcn::kGroupChannels;
     b.grad_in = static_cast<char *>(grad_input) + n0 * img_in;

@@ -219,6 +219,12 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   const uint32_t pix_bytes = (uint32_t)p.C * io::kBytes;
   const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
+  // Rows and outputs go through buffer instructions too: with 32-bit offsets
+  // the address unit handles them several times faster than 64-bit global
+  // addresses when a wave touches many cache lines.
+  const __amdgpu_buffer_rsrc_t roff = make_rsrc(p.offset, p.off_bytes);
+  const __amdgpu_buffer_rsrc_t rmask = make_rsrc(p.mask, p.mask_bytes);
+  const __amdgpu_buffer_rsrc_t rout = make_rsrc(p.output, p.out_bytes);
   constexpr int USPAN = TW + 2 * R + 3;  // window edge at stride 1, dilation 1
   const int span_w = UNIT ? USPAN : tg.span_w;
   const int span_h = UNIT ? (TH + 2 * R + 3) : tg.span_h;
@@ -321,14 +327,11 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   constexpr int NRW = DT == DCN_F32 ? 6 : 3;
   uint32_t rw[PASSES][NRW], rl[PASSES][3];
   auto load_rows = [&](uint32_t pg, uint32_t (&w)[NRW], uint32_t (&l)[3]) {
-    typedef uint32_t u4 __attribute__((ext_vector_type(4), aligned(4)));
-    typedef uint32_t u2 __attribute__((ext_vector_type(2), aligned(4)));
     if constexpr (DT == DCN_F32) {
-      const unsigned char *orow = static_cast<const unsigned char *>(p.offset) + (uint64_t)pg * (K * 8);
-      const unsigned char *mrow = static_cast<const unsigned char *>(p.mask) + (uint64_t)pg * (K * 4);
-      const u4 o = *reinterpret_cast<const u4 *>(orow + 16 * sub);
-      const u2 o8 = *reinterpret_cast<const u2 *>(orow + 64);
-      const u2 lg = *reinterpret_cast<const u2 *>(mrow + 8 * sub);
+      const uint32_t orow = pg * (K * 8), mrow = pg * (K * 4);
+      const auto o = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(orow + 16 * sub), 0, 0);
+      const auto o8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 64), 0, 0);
+      const auto lg = __builtin_amdgcn_raw_buffer_load_b64(rmask, (int)(mrow + 8 * sub), 0, 0);
       w[0] = o[0];
       w[1] = o[1];
       w[2] = o[2];
@@ -337,17 +340,16 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
       w[5] = o8[1];
       l[0] = lg[0];
       l[1] = lg[1];
-      l[2] = *reinterpret_cast<const uint32_t *>(mrow + 32);
+      l[2] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 32), 0, 0);
     } else {
-      const uint32_t *orow = static_cast<const uint32_t *>(p.offset) + (uint64_t)pg * K;
-      const uint16_t *mrow = static_cast<const uint16_t *>(p.mask) + (uint64_t)pg * K;
-      const u2 o = *reinterpret_cast<const u2 *>(orow + 2 * sub);
+      const uint32_t orow = pg * (K * 4), mrow = pg * (K * 2);
+      const auto o = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 8 * sub), 0, 0);
       w[0] = o[0];
       w[1] = o[1];
-      w[2] = orow[8];
-      l[0] = mrow[2 * sub];
-      l[1] = mrow[2 * sub + 1];
-      l[2] = mrow[8];
+      w[2] = __builtin_amdgcn_raw_buffer_load_b32(roff, (int)(orow + 32), 0, 0);
+      l[0] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub), 0, 0);
+      l[1] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub + 2), 0, 0);
+      l[2] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 16), 0, 0);
     }
   };
   auto issue_pgdata = [&](const Item &I, auto ps_tag) {
@@ -531,12 +533,18 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
 
       uint32_t outw[NW];
       pack_words<DT, CPL>(acc, outw);
-      store_words<NW>(static_cast<unsigned char *>(p.output) + ((uint64_t)pg * CG + sub * CPL) * io::kBytes,
-                      outw);
+      buffer_store_words<NW>(rout, (pg * CG + sub * CPL) * io::kBytes, outw);
     };
+    // Wave priority by progress: waves still in pass 0 issue ahead of waves
+    // in pass 1, and waves done with the item yield, so the block reaches
+    // its next barrier with less spread between its fastest and slowest
+    // waves (all of them wait there for the slowest).
+    __builtin_amdgcn_s_setprio(2);
     pass(P0{});
+    __builtin_amdgcn_s_setprio(1);
     issue_pgdata(nx, P0{});  // unconditional (see issue_window)
     pass(P1{});
+    __builtin_amdgcn_s_setprio(0);
     issue_pgdata(nx, P1{});
 
     item = next;

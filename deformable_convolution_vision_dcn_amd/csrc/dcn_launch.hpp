@@ -22,6 +22,9 @@ struct FwdParams {
   const void *mask;
   void *output;
   uint32_t in_bytes;   // bytes of the chunk's input (buffer num_records)
+  uint32_t off_bytes;  // bytes of the chunk's offset, mask and output tensors
+  uint32_t mask_bytes; // (each below 2^31, like the input)
+  uint32_t out_bytes;
   uint32_t pg_total;   // pixel-groups (n, ho, wo, g) in the chunk
   int32_t H, W, C, G, Ho, Wo;
   int32_t KH, KW, SH, SW, PH, PW, DH, DW;

@@ -71,8 +71,8 @@ typedef enum dcn_status {
     DCN_ERR_UNSUPPORTED = -3, /* dtype, channels-per-group or point count without a
                                  kernel, or a 16-bit backward                          */
     DCN_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                */
-    DCN_ERR_TOO_LARGE = -5,   /* one image's input exceeds 2^31-1 bytes, H or W exceeds
-                                 2^24, or one image's output exceeds 2^31-1 bytes      */
+    DCN_ERR_TOO_LARGE = -5,   /* one image's input, output or offset tensor exceeds
+                                 2^31-1 bytes, or H or W exceeds 2^24                  */
     DCN_ERR_HIP = -6,         /* the HIP runtime refused a launch; see dcn_status_string */
     DCN_ERR_ABI = -7,         /* problem->struct_size != sizeof(dcn_problem)            */
     DCN_ERR_ARG = -8          /* softmax not 0/1, or offset_scale not finite            */
