@@ -55,7 +55,10 @@ __device__ __forceinline__ void lds_read16(const unsigned char *src, uint32_t (&
 }  // namespace
 
 template <int DT, bool SOFTMAX>
-__global__ void __launch_bounds__(kLaneThreads, 2) dcn_fwd_lane_kernel(FwdParams p, TileGeom tg) {
+#ifndef DCN_LANE_WAVES
+#define DCN_LANE_WAVES 2  // waves per SIMD the register budget must allow
+#endif
+__global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_kernel(FwdParams p, TileGeom tg) {
   using io = Io<DT>;
   constexpr int TS = kLaneTile, R = kLaneHalo, SPAN_W = kLaneSpanUnit;
   constexpr int CG = kGroupChannels;
@@ -309,8 +312,14 @@ hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const uint32_t per_cu = DT == DCN_F32 ? 2u : 4u;  // LDS-limited persistent blocks
-  const uint32_t blocks = std::min<uint32_t>(tg.items, per_cu * (uint32_t)cus);
+  // Persistent blocks: as many per CU as are resident together (registers
+  // and LDS permitting), so no block waits for another to finish.
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern),
+                                                   kLaneThreads, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorNotSupported;
+  const uint32_t blocks = std::min<uint32_t>(tg.items, (uint32_t)per_cu * (uint32_t)cus);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kLaneThreads), lds, s, p, tg);
   return hipGetLastError();
 }
