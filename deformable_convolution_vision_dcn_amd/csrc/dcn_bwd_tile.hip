@@ -54,10 +54,22 @@ __device__ __forceinline__ void lds_read16(const unsigned char *src, float (&v)[
   v[3] = q.w;
 }
 
-// LDS integer add (ds_add_u32).  Float adds in LDS run at a small fraction of
-// the integer rate on this chip, so the scatter accumulates in fixed point.
-__device__ __forceinline__ void lds_iadd(unsigned char *dst, int v) {
-  __hip_atomic_fetch_add(reinterpret_cast<int *>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// Two neighbouring channels' fixed-point terms added by one 64-bit LDS
+// integer add (ds_add_u64).  Float adds in LDS run at a small fraction of the
+// integer rate on this chip, so the scatter accumulates in fixed point; a
+// 64-bit add moves two channels for about the cost of one 32-bit add.  The
+// pair is the 64-bit integer hi * 2^32 + lo (lo sign-extended into the high
+// word), so a sum of such terms is (sum hi) * 2^32 + sum lo exactly, and as
+// long as |sum lo| < 2^31 both sums are recovered from it (see unpack_pair).
+__device__ __forceinline__ void lds_iadd2(unsigned char *dst, int lo, int hi) {
+  const uint64_t v = ((uint64_t)(uint32_t)(hi + (lo >> 31)) << 32) | (uint32_t)lo;
+  __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// (sum lo, sum hi) of a pair accumulated by lds_iadd2.
+__device__ __forceinline__ int2 unpack_pair(uint64_t v) {
+  const int lo = (int)(uint32_t)v;
+  const int hi = (int)((int64_t)(v - (uint64_t)(int64_t)lo) >> 32);
+  return make_int2(lo, hi);
 }
 
 }  // namespace
@@ -145,9 +157,10 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
   for (int k = 0; k < K; ++k) gb[k] = gdx[k] = gdy[k] = 0.f;
 
   const uint32_t sq = lane / 2, sc = lane % 2;
-  int cro[CH];  // byte offset of channel (c + lane) mod 8 within a pixel slice
+  constexpr int NP = CH / 2;  // channel pairs per half
+  int cro[NP];  // byte offset of channel pair (q + lane) mod 4 within a pixel slice
 #pragma unroll
-  for (int c = 0; c < CH; ++c) cro[c] = (int)(((uint32_t)c + lane) % CH) * 4;
+  for (int q = 0; q < NP; ++q) cro[q] = (int)(((uint32_t)q + lane) % NP) * 8;
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {
     const uint32_t chan = (g * CG + h * CH + sc * 4) * 4u;  // this stager's 16 bytes
@@ -170,17 +183,18 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
         gyh[4 * q + 3] = v.w;
       }
     }
-    // The same 8 values rotated by this lane's position: gyr[c] = gyh[(c + lane) mod 8]
-    // (a 3-step barrel rotation), for the bank-spread scatter below.
+    // The same 8 values with their channel pairs rotated by this lane's
+    // position: (gyr[2q], gyr[2q + 1]) = pair (q + lane) mod 4 (a 2-step
+    // barrel rotation), for the bank-spread scatter below.
     float gyr[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) gyr[c] = gyh[c];
 #pragma unroll
-    for (int rs = 1; rs < CH; rs <<= 1) {
+    for (int rs = 1; rs < NP; rs <<= 1) {
       const bool on = (lane & (uint32_t)rs) != 0;
       float t[CH];
 #pragma unroll
-      for (int c = 0; c < CH; ++c) t[c] = on ? gyr[(c + rs) % CH] : gyr[c];
+      for (int c = 0; c < CH; ++c) t[c] = on ? gyr[(c + 2 * rs) % CH] : gyr[c];
 #pragma unroll
       for (int c = 0; c < CH; ++c) gyr[c] = t[c];
     }
@@ -189,10 +203,10 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
     // receives at most the sum over the tile's pixel-groups of
     // sum_k |m_k| * max_c |gy_c| (the four corner weights of a sample are
     // non-negative and add up to 1), call it B.  With S = 2^(30 - e), B <= 2^e,
-    // every partial sum of the scaled terms stays within 2^30, so 32-bit LDS
-    // integer atomics add them exactly; each term is rounded to the nearest
-    // multiple of 1/S.  A non-finite B (NaN or Inf in grad_out or the mask)
-    // switches the half to fp32 global atomics.
+    // every partial sum of the scaled terms stays within 2^30, so the LDS
+    // integer adds (two channels per 64-bit add) sum them exactly; each term
+    // is rounded to the nearest multiple of 1/S.  A non-finite B (NaN or Inf
+    // in grad_out or the mask) switches the half to fp32 global atomics.
     float gmax = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) gmax = fmaxf(gmax, fabsf(gyh[c]));
@@ -308,20 +322,20 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
       // window as scaled integers (a sample outside it adds into the sink
       // rows); the others, and every sample of a non-finite half, go to
       // grad_input with fp32 global atomics.
-      // At step c lane l adds channel (c + l) mod 8: with 32-byte pixel slices
-      // a common channel order would put every lane of an instruction in the
-      // same 8 of the 64 LDS banks.  Samples outside the window add nothing
+      // At step q lane l adds channel pair (q + l) mod 4: with 32-byte pixel
+      // slices a common order would put every lane of an instruction in the
+      // same few of the 64 LDS banks.  Samples outside the window add nothing
       // here (their lanes are masked off, so the sink rows see no traffic).
       if (fixed && inside) {
         const float s00 = w00 * S, s01 = w01 * S, s10 = w10 * S, s11 = w11 * S;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          const float gc = gyr[c];
-          unsigned char *d = gwin + A + cro[c];
-          lds_iadd(d, __float2int_rn(s00 * gc));
-          lds_iadd(d + PIXB, __float2int_rn(s01 * gc));
-          lds_iadd(d + ROW, __float2int_rn(s10 * gc));
-          lds_iadd(d + ROW + PIXB, __float2int_rn(s11 * gc));
+        for (int q = 0; q < NP; ++q) {
+          const float ga = gyr[2 * q], gb2 = gyr[2 * q + 1];
+          unsigned char *d = gwin + A + cro[q];
+          lds_iadd2(d, __float2int_rn(s00 * ga), __float2int_rn(s00 * gb2));
+          lds_iadd2(d + PIXB, __float2int_rn(s01 * ga), __float2int_rn(s01 * gb2));
+          lds_iadd2(d + ROW, __float2int_rn(s10 * ga), __float2int_rn(s10 * gb2));
+          lds_iadd2(d + ROW + PIXB, __float2int_rn(s11 * ga), __float2int_rn(s11 * gb2));
         }
       }
       const bool gscatter = fixed ? fb : (live && !nan_loc);
@@ -353,7 +367,8 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
         const int sy = idx / SPAN_W, sx = idx - sy * SPAN_W;
         const int gy_ = Y0 + sy, gx_ = X0 + sx;
         const bool ok = (uint32_t)gy_ < (uint32_t)p.H && (uint32_t)gx_ < (uint32_t)p.W;
-        const int q = *reinterpret_cast<const int *>(gwin + idx * PIXB + c8 * 4);
+        const int2 pr = unpack_pair(*reinterpret_cast<const uint64_t *>(gwin + idx * PIXB + (c8 / 2) * 8));
+        const int q = (c8 & 1) ? pr.y : pr.x;
         const uint32_t dst = img + (uint32_t)gy_ * row_bytes + (uint32_t)gx_ * pix_bytes + cbyte;
         __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32((float)q * invS, rgx, (int)((ok && q != 0) ? dst : kOutOfRange), 0, 0);
       }
