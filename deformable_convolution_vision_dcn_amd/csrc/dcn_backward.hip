@@ -212,9 +212,18 @@ hipError_t launch_one(const BwdParams &p, hipStream_t s) {
 
 }  // namespace
 
+// Backward path override for tests and measurements: DCN_MI355X_BWD_PATH =
+// "generic" (untiled kernel), "tiled" (the half-window tiled kernel) or
+// "quad" (the lane-quad tiled kernel, also the default where it applies).
 hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s) {
   const char *e = getenv("DCN_MI355X_BWD_PATH");
-  if (!(e && !strcmp(e, "generic"))) {
+  const bool generic = e && !strcmp(e, "generic");
+  const bool halves = e && !strcmp(e, "tiled");
+  if (!generic && !halves) {
+    const hipError_t q = launch_backward_quad(softmax, p, s);
+    if (q != hipErrorNotSupported) return q;
+  }
+  if (!generic) {
     const hipError_t t = launch_backward_tiled(softmax, p, s);
     if (t != hipErrorNotSupported) return t;
   }

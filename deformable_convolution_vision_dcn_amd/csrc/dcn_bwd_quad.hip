@@ -1,0 +1,542 @@
+// dcn_bwd_quad.hip -- LDS-tiled gfx950 backward kernel of the DCN core
+// (fp32), a lane quad per pixel-group, for 3x3 kernel points at stride 1 and
+// dilation 1 (the InternImage configuration; wmrh.cn/news/61976, section 二
+// steps 2-4 and section 三).
+//
+// The derivatives are those of the untiled backward kernel: every in-map
+// corner of a sample receives m_k * w_corner * gy_c; the offset gradient is
+// s * m_k * sum_c gy_c * dB_k[c]/d(px, py) (one-sided from the right at integer
+// coordinates); the mask gradient is gm_k = sum_c gy_c * B_k[c], through the
+// softmax Jacobian for DCNv3.
+//
+// Layout of the work: persistent 1024-thread blocks, one per CU, each walking
+// (image, 16x16 output tile, group) items.  A block stages the input window
+// its samples can reach (the tile's 3x3 footprint plus a halo of R pixels,
+// all 16 channels of the group, 64 bytes per pixel) in LDS, and accumulates
+// the grad_input scatter of the item in a second LDS window in fixed point;
+// both windows fit one CU's LDS together.  At the end of the item the grad
+// window is added to grad_input with global atomics, one 64-byte request per
+// window pixel, and cleared for the next item.  The next item's input window,
+// offset/mask rows and grad_output are requested into registers while the
+// current item computes.
+//
+// Per pixel-group one quad: lane `sub` owns channels [4 sub, 4 sub + 4) and
+// computes the location, bilinear weights (modulation folded in) and window
+// address of the points k = 2 sub, 2 sub + 1 (and k = 8 for sub 0), as in the
+// tiled forward.  For each point the quad reads its four corners (each lane
+// its 4 channels), forms the four per-corner dot products with grad_output
+// and sums them over the quad (DPP), which gives the owner the point's
+// gm, d/dx and d/dy; it scatters w_corner * gy_c for its 4 channels into the
+// grad window, two channels per 64-bit integer add.
+// Samples whose corners leave the window take the global path behind a wave
+// ballot: buffer loads for the corners and buffer atomics for the scatter.
+#include <algorithm>
+#include <type_traits>
+
+#include "dcn_device.hpp"
+#include "quad_ops.hpp"
+
+namespace dcn {
+
+#ifndef DCN_BQ_HALO
+#define DCN_BQ_HALO 7
+#endif
+constexpr int kBqTile = 16;
+constexpr int kBqHalo = DCN_BQ_HALO;
+constexpr int kBqSpan = kBqTile + 2 * kBqHalo + 3;        // window edge, pixels
+constexpr int kBqPixB = 64;                               // 16 fp32 channels
+constexpr int kBqRow = kBqSpan * kBqPixB;                 // LDS bytes per window row
+constexpr int kBqWin = kBqSpan * kBqSpan * kBqPixB;       // one window
+constexpr int kBqZero = kBqRow + 2 * kBqPixB;             // zero block after the input window
+constexpr int kBqThreads = 1024;
+constexpr int kBqWaves = kBqThreads / 64;
+constexpr size_t kBqLds = (size_t)kBqWin + kBqZero + kBqWin + 4 * kBqWaves;
+
+namespace {
+
+// v + v(quad lane swizzled by the DPP control), the swizzle a DPP operand.
+#define DCN_ADDF_DPP(QP)                                                              \
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 " QP " row_mask:0xf bank_mask:0xf"         \
+      : "=v"(r) : "v"(v))
+__device__ __forceinline__ float quad_sum_fused(float v) {
+  float r;
+  DCN_ADDF_DPP("quad_perm:[1,0,3,2]");
+  v = r;
+  DCN_ADDF_DPP("quad_perm:[2,3,0,1]");
+  return r;
+}
+#undef DCN_ADDF_DPP
+
+// Two neighbouring channels' fixed-point terms added by one 64-bit LDS
+// integer add (ds_add_u64) at LDS byte address `addr`.  The pair is the
+// 64-bit integer hi * 2^32 + lo (lo sign-extended into the high word), so a
+// sum of such terms is (sum hi) * 2^32 + sum lo exactly, and as long as
+// |sum lo| < 2^31 both sums come back from it (see pair_sums).
+__device__ __forceinline__ void lds_add_pair(uint32_t addr, int lo, int hi) {
+  typedef __attribute__((address_space(3))) uint64_t L;
+  const uint64_t v = ((uint64_t)(uint32_t)(hi + (lo >> 31)) << 32) | (uint32_t)lo;
+  __hip_atomic_fetch_add((L *)(size_t)addr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ int2 pair_sums(uint64_t v) {
+  const int lo = (int)(uint32_t)v;
+  const int hi = (int)((int64_t)(v - (uint64_t)(int64_t)lo) >> 32);
+  return make_int2(lo, hi);
+}
+
+}  // namespace
+
+template <bool SOFTMAX>
+__global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams bp, TileGeom tg) {
+  const FwdParams &p = bp.f;
+  constexpr int TS = kBqTile, R = kBqHalo, SPAN_W = kBqSpan;
+  constexpr int SPAN = SPAN_W * SPAN_W;
+  constexpr int PIXB = kBqPixB, ROW = kBqRow, LIM = SPAN_W - 2;
+  constexpr int CG = kGroupChannels, K = 9;
+  constexpr int WPIX = kBqThreads / 4;                   // window pixels per staging slice
+  constexpr int SLOTS = (SPAN + WPIX - 1) / WPIX;
+  constexpr uint32_t ZERO = kBqWin;                      // zero block (reads of outside samples)
+  constexpr uint32_t GWIN = kBqWin + kBqZero;            // fixed-point grad window
+  static_assert(CG == 16, "a quad covers 16 channels");
+
+  extern __shared__ __align__(16) unsigned char lds[];
+  typedef __attribute__((address_space(3))) unsigned char lds_byte;
+  const uint32_t lbase = (uint32_t)(size_t)(lds_byte *)lds;
+  float *wave_sums = reinterpret_cast<float *>(lds + GWIN + kBqWin);
+
+  const uint32_t quad = threadIdx.x >> 2, sub = threadIdx.x & 3;
+  const int oy = (int)quad / TS, ox = (int)quad % TS;  // output pixel within the tile
+  const uint32_t pix_bytes = (uint32_t)p.C * 4u;
+  const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
+  const __amdgpu_buffer_rsrc_t rgx = make_rsrc(bp.grad_in, p.in_bytes);
+  const __amdgpu_buffer_rsrc_t roff = make_rsrc(p.offset, p.off_bytes);
+  const __amdgpu_buffer_rsrc_t rmask = make_rsrc(p.mask, p.mask_bytes);
+  const __amdgpu_buffer_rsrc_t rgy = make_rsrc(bp.grad_out, p.pg_total * (uint32_t)(CG * 4));
+  const __amdgpu_buffer_rsrc_t rgoff = make_rsrc(bp.grad_offset, p.off_bytes);
+  const __amdgpu_buffer_rsrc_t rgm = make_rsrc(bp.grad_mask, p.mask_bytes);
+  const float s = p.scale;
+
+  // Window coordinates of each own slot's kernel point before its offset,
+  // packed as three 10-bit fields; slot r holds k = 2 sub + r (r < 2) or 8.
+  uint32_t bxp = 0, byp = 0;
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    const int k = r < 2 ? 2 * (int)sub + r : 8;
+    bxp |= (uint32_t)(ox + R + k % 3) << (10 * r);
+    byp |= (uint32_t)(oy + R + k / 3) << (10 * r);
+  }
+  const uint32_t win_chunk = lbase + sub * 16u;          // this lane's 4 channels of a window pixel
+  const uint32_t gwin_chunk = lbase + GWIN + sub * 16u;
+
+  // The grad window starts at zero; every item's flush clears it again.  The
+  // zero block after the input window is written once.  The first barrier of
+  // the item loop orders both.
+  for (uint32_t z = threadIdx.x * 16u; z < (uint32_t)kBqWin; z += kBqThreads * 16u)
+    *reinterpret_cast<uint4 *>(lds + GWIN + z) = make_uint4(0, 0, 0, 0);
+  for (uint32_t z = threadIdx.x * 16u; z < (uint32_t)kBqZero; z += kBqThreads * 16u)
+    *reinterpret_cast<uint4 *>(lds + ZERO + z) = make_uint4(0, 0, 0, 0);
+
+  struct Item {
+    uint32_t g, n, img, chan, pg;
+    int Y0, X0;
+    bool live;
+  };
+  auto decode = [&](uint32_t it) {
+    Item I;
+    const uint32_t t = fast_div(it, tg.div_g);
+    I.g = it - t * (uint32_t)p.G;
+    I.n = fast_div(t, tg.div_tiles);
+    const uint32_t tile_id = t - I.n * (uint32_t)tg.tiles_per_img;
+    const uint32_t tyi = fast_div(tile_id, tg.div_tiles_x);
+    const uint32_t txi = tile_id - tyi * (uint32_t)tg.tiles_x;
+    const int r0 = (int)tyi * TS, c0 = (int)txi * TS;
+    I.Y0 = r0 - p.PH - R;  // window origin in input coordinates
+    I.X0 = c0 - p.PW - R;
+    I.img = I.n * (uint32_t)p.H * row_bytes;
+    I.chan = I.g * (uint32_t)(CG * 4) + sub * 16u;
+    const int ho = r0 + oy, wo = c0 + ox;
+    I.live = ho < p.Ho && wo < p.Wo;
+    I.pg = I.live ? (((I.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + I.g : 0u;
+    return I;
+  };
+
+  // Next item's input window (4 lanes of 16 bytes per pixel), offset and mask
+  // rows and grad_output: requested into registers while the current item
+  // computes, on every path (a missing item loads nothing: its offsets are
+  // out of range), so the compiler's count of outstanding loads stays exact.
+  uint32_t win[SLOTS][4];
+  auto issue_window = [&](const Item &I, bool valid) {
+    // The slot geometry is recomputed per item from an opaque copy of the
+    // quad index: hoisted out of the item loop it would not fit the
+    // register budget.
+    uint32_t qd = quad;
+    asm volatile("" : "+v"(qd));
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u) {
+      const int idx = (int)qd + u * WPIX;
+      uint32_t offb = kOutOfRange;
+      if (valid && idx < SPAN) {
+        const int sy = idx / SPAN_W, sx = idx - sy * SPAN_W;
+        const int gy_ = I.Y0 + sy, gx_ = I.X0 + sx;
+        if ((uint32_t)gy_ < (uint32_t)p.H && (uint32_t)gx_ < (uint32_t)p.W)
+          offb = I.img + (uint32_t)gy_ * row_bytes + (uint32_t)gx_ * pix_bytes + I.chan;
+      }
+      buffer_load_words<4>(rin, offb, win[u]);
+    }
+  };
+  auto store_window = [&]() {
+    uint32_t qd = quad;
+    asm volatile("" : "+v"(qd));
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u) {
+      const int idx = (int)qd + u * WPIX;
+      if (idx < SPAN)
+        *reinterpret_cast<uint4 *>(lds + idx * PIXB + sub * 16u) = make_uint4(win[u][0], win[u][1], win[u][2], win[u][3]);
+    }
+  };
+  // Raw rows as loaded: rw = x, y of k = 2 sub; x, y of 2 sub + 1; x, y of 8;
+  // rl = logits of 2 sub, 2 sub + 1, 8; rg = grad_output of the lane's 4 channels.
+  uint32_t rw[6], rl[3], rg[4];
+  auto issue_rows = [&](const Item &I) {
+    const uint32_t orow = I.pg * (K * 8), mrow = I.pg * (K * 4);
+    const auto o = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(orow + 16 * sub), 0, 0);
+    const auto o8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 64), 0, 0);
+    const auto lg = __builtin_amdgcn_raw_buffer_load_b64(rmask, (int)(mrow + 8 * sub), 0, 0);
+    rl[2] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 32), 0, 0);
+    const auto gv = __builtin_amdgcn_raw_buffer_load_b128(rgy, (int)(I.pg * (CG * 4) + 16 * sub), 0, 0);
+    rw[0] = o[0];
+    rw[1] = o[1];
+    rw[2] = o[2];
+    rw[3] = o[3];
+    rw[4] = o8[0];
+    rw[5] = o8[1];
+    rl[0] = lg[0];
+    rl[1] = lg[1];
+    rg[0] = gv[0];
+    rg[1] = gv[1];
+    rg[2] = gv[2];
+    rg[3] = gv[3];
+  };
+
+  const XcdWalk walk = xcd_walk(blockIdx.x, gridDim.x, tg.items);
+  const uint32_t end = walk.end;
+  uint32_t item = walk.first;
+  Item cur = decode(item < end ? item : 0);
+  if (item < end) {
+    issue_window(cur, true);
+    issue_rows(cur);
+  }
+  const float qnan = __builtin_nanf("");
+
+  while (item < end) {
+    __syncthreads();  // the previous item's reads, scatters and flush are done
+    store_window();
+
+    // Own slots: offsets, modulation weights (softmax over the quad's nine
+    // logits for DCNv3, the raw mask for DCNv4) and grad_output.
+    float2 offs[3];
+    float m[3], gy[4];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) offs[r] = make_float2(__uint_as_float(rw[2 * r]), __uint_as_float(rw[2 * r + 1]));
+    float lgs[3] = {__uint_as_float(rl[0]), __uint_as_float(rl[1]), __uint_as_float(rl[2])};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) gy[c] = __uint_as_float(rg[c]);
+    if (sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 only
+    if constexpr (SOFTMAX) {
+      const float mx = quad_max(fmaxf(fmaxf(lgs[0], lgs[1]), lgs[2]));
+      float e[3], sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        e[r] = (r < 2 || sub == 0) ? __expf(lgs[r] - mx) : 0.f;
+        sum += e[r];
+      }
+      const float inv = __builtin_amdgcn_rcpf(quad_sum(sum));
+#pragma unroll
+      for (int r = 0; r < 3; ++r) m[r] = e[r] * inv;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 3; ++r) m[r] = lgs[r];
+    }
+
+    // Fixed-point scale of the item's grad window.  Every window
+    // pixel-channel receives at most the sum over the tile's pixel-groups of
+    // sum_k |m_k| * max_c |gy_c| (the four corner weights of a sample are
+    // non-negative and add up to 1), call it B.  With S = 2^(30 - e), B <= 2^e,
+    // every partial sum of the scaled terms stays within 2^30, so the LDS
+    // integer adds sum them exactly; each term is rounded to the nearest
+    // multiple of 1/S.  A non-finite B (NaN or Inf in grad_output or the mask)
+    // sends the whole item to fp32 global atomics instead.
+    {
+      float gmax = 0.f, nanflag = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        gmax = fmaxf(gmax, fabsf(gy[c]));
+        nanflag += 0.f * gy[c];  // fmaxf drops NaN: a NaN in gy must still reach the bound
+      }
+      const float msum = quad_sum(fabsf(m[0]) + fabsf(m[1]) + fabsf(m[2]));
+      float bound = quad_max(gmax) * msum + quad_sum(nanflag);
+      bound = (cur.live && sub == 0) ? bound : 0.f;
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) bound += __shfl_xor(bound, d, 64);
+      if ((threadIdx.x & 63) == 0) wave_sums[threadIdx.x >> 6] = bound;
+    }
+    __syncthreads();  // the window is in LDS, the wave bounds are ready
+
+    float B = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kBqWaves; ++wv) B += wave_sums[wv];
+    const bool fixed = B <= 3.0e38f;  // false for Inf and NaN (block-uniform)
+    int ex = 0;
+    frexpf(B, &ex);
+    ex = ex < -96 ? -96 : ex;
+    const float S = ldexpf(1.f, 30 - ex), invS = ldexpf(1.f, ex - 30);
+
+    const uint32_t next = item + walk.stride;
+    const bool more = next < end;  // block-uniform
+    const Item nx = decode(more ? next : item);
+    issue_window(nx, more);
+    issue_rows(nx);
+
+    // Per-slot results, shifted in round by round: after the three rounds
+    // res2 holds slot 0, res1 slot 1, res0 slot 2.  (gm, d/dx, d/dy)
+    float3 res0 = make_float3(0.f, 0.f, 0.f), res1 = res0, res2 = res0;
+    float2 o2 = offs[0], o2n = offs[1], o2nn = offs[2];
+    float mk = m[0], mkn = m[1], mknn = m[2];
+#pragma unroll 1
+    for (int r = 0; r < 3; ++r) {
+      const float dx = s * o2.x, dy = s * o2.y;
+      const bool nan_loc = (dx != dx) | (dy != dy);
+      const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
+      const float cy = __builtin_amdgcn_fmed3f(dy, -16777216.f, 16777216.f);
+      const float fx = floorf(cx), fy = floorf(cy);
+      const float lx = cx - fx, ly = cy - fy;
+      const float hx = 1.f - lx, hy = 1.f - ly;
+      const int tx = (int)((bxp >> (10 * r)) & 1023u) + (int)fx;  // window coordinates
+      const int ty = (int)((byp >> (10 * r)) & 1023u) + (int)fy;
+      const bool inside = cur.live && !nan_loc && (uint32_t)ty <= (uint32_t)LIM && (uint32_t)tx <= (uint32_t)LIM;
+      const uint32_t A = inside ? mad24((uint32_t)ty, (uint32_t)ROW, mul24((uint32_t)tx, PIXB)) : ZERO;
+      const float wy1 = ly * mk, wy0 = mk - wy1;
+      const float W1 = wy0 * lx, W0 = wy0 - W1;
+      const float W3 = wy1 * lx, W2 = wy1 - W3;
+      // scaled to the fixed-point grid for the LDS scatter
+      const float W0s = W0 * S, W1s = W1 * S, W2s = W2 * S, W3s = W3 * S;
+      // outside the window but touching the map: global gathers and atomics
+      const bool fb = cur.live && !inside && !nan_loc && (uint32_t)(cur.Y0 + 1 + ty) <= (uint32_t)p.H &&
+                      (uint32_t)(cur.X0 + 1 + tx) <= (uint32_t)p.W;
+      const bool scat = fixed && inside;           // LDS scatter
+      const bool gscat = fixed ? fb : (cur.live && !nan_loc);  // global scatter
+      float3 mine = make_float3(0.f, 0.f, 0.f);
+
+      auto point = [&](auto o_tag) {
+        constexpr int O = decltype(o_tag)::value;
+        // Gather this lane's 4 channels of the owner's four corners.
+        const uint32_t src = add_bcast<O>(A, win_chunk);
+        uint32_t q00[4], q01[4], q10[4], q11[4];
+        lds_load_at<4>(src, q00);
+        lds_load_at<4>(src + PIXB, q01);
+        lds_load_at<4>(src + ROW, q10);
+        lds_load_at<4>(src + ROW + PIXB, q11);
+        float P00 = 0.f, P01 = 0.f, P10 = 0.f, P11 = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          P00 = fmaf(gy[c], __uint_as_float(q00[c]), P00);
+          P01 = fmaf(gy[c], __uint_as_float(q01[c]), P01);
+          P10 = fmaf(gy[c], __uint_as_float(q10[c]), P10);
+          P11 = fmaf(gy[c], __uint_as_float(q11[c]), P11);
+        }
+        // Global byte offsets of the owner's four corners for this lane's
+        // channels (out of range where a corner is outside the map).
+        auto corners = [&](uint32_t (&ga)[4]) {
+          const int yb = qbcast<O>(ty) + cur.Y0, xb = qbcast<O>(tx) + cur.X0;
+          const bool vy0 = (uint32_t)yb < (uint32_t)p.H, vy1 = (uint32_t)(yb + 1) < (uint32_t)p.H;
+          const bool vx0 = (uint32_t)xb < (uint32_t)p.W, vx1 = (uint32_t)(xb + 1) < (uint32_t)p.W;
+          const uint32_t a00 = cur.img + (uint32_t)yb * row_bytes + (uint32_t)xb * pix_bytes + cur.chan;
+          ga[0] = (vy0 && vx0) ? a00 : kOutOfRange;
+          ga[1] = (vy0 && vx1) ? a00 + pix_bytes : kOutOfRange;
+          ga[2] = (vy1 && vx0) ? a00 + row_bytes : kOutOfRange;
+          ga[3] = (vy1 && vx1) ? a00 + row_bytes + pix_bytes : kOutOfRange;
+        };
+        const int ofb = qbcast<O>((int)fb);
+        if (__builtin_amdgcn_ballot_w64(ofb != 0) != 0) {  // a quad of the wave left its window
+          if (ofb) {
+            uint32_t ga[4];
+            corners(ga);
+            const uint32_t g00 = ga[0], g01 = ga[1], g10 = ga[2], g11 = ga[3];
+            buffer_load_words<4>(rin, g00, q00);
+            buffer_load_words<4>(rin, g01, q01);
+            buffer_load_words<4>(rin, g10, q10);
+            buffer_load_words<4>(rin, g11, q11);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              P00 = fmaf(gy[c], __uint_as_float(q00[c]), P00);
+              P01 = fmaf(gy[c], __uint_as_float(q01[c]), P01);
+              P10 = fmaf(gy[c], __uint_as_float(q10[c]), P10);
+              P11 = fmaf(gy[c], __uint_as_float(q11[c]), P11);
+            }
+          }
+        }
+        // Sums over the 16 channels: every lane of the quad gets them; the
+        // owner keeps gm, d/dx and d/dy of its point (one-sided derivatives
+        // of the bilinear form, linear in the corner sums).
+        const float G00 = quad_sum_fused(P00), G01 = quad_sum_fused(P01);
+        const float G10 = quad_sum_fused(P10), G11 = quad_sum_fused(P11);
+        if (sub == (uint32_t)O) {
+          const float T = hx * G00 + lx * G01, Bt = hx * G10 + lx * G11;
+          mine = nan_loc ? make_float3(qnan, qnan, qnan)
+                         : make_float3(hy * T + ly * Bt, hy * (G01 - G00) + ly * (G11 - G10), Bt - T);
+        }
+        // Scatter m_k * w_corner * gy_c of this lane's 4 channels.
+        if (qbcast<O>((int)scat)) {
+          const uint32_t d = add_bcast<O>(A, gwin_chunk);
+          auto corner = [&](float w, uint32_t at) {
+            const float t0 = mul_bcast<O>(w, gy[0]), t1 = mul_bcast<O>(w, gy[1]);
+            const float t2 = mul_bcast<O>(w, gy[2]), t3 = mul_bcast<O>(w, gy[3]);
+            lds_add_pair(at, cvt_rpi(t0), cvt_rpi(t1));
+            lds_add_pair(at + 8, cvt_rpi(t2), cvt_rpi(t3));
+          };
+          corner(W0s, d);
+          corner(W1s, d + PIXB);
+          corner(W2s, d + ROW);
+          corner(W3s, d + ROW + PIXB);
+        }
+        if (__builtin_amdgcn_ballot_w64(qbcast<O>((int)gscat) != 0) != 0) {
+          if (qbcast<O>((int)gscat)) {
+            uint32_t ga[4];
+            corners(ga);
+            const uint32_t g00 = ga[0], g01 = ga[1], g10 = ga[2], g11 = ga[3];
+            const float w00 = qbcast<O>(W0), w01 = qbcast<O>(W1);
+            const float w10 = qbcast<O>(W2), w11 = qbcast<O>(W3);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t cb = 4u * c;
+              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w00 * gy[c], rgx, (int)(g00 == kOutOfRange ? kOutOfRange : g00 + cb), 0, 0);
+              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w01 * gy[c], rgx, (int)(g01 == kOutOfRange ? kOutOfRange : g01 + cb), 0, 0);
+              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w10 * gy[c], rgx, (int)(g10 == kOutOfRange ? kOutOfRange : g10 + cb), 0, 0);
+              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w11 * gy[c], rgx, (int)(g11 == kOutOfRange ? kOutOfRange : g11 + cb), 0, 0);
+            }
+          }
+        }
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      point(I0{});
+      if (r < 2) {  // the last round holds only k = 8 (owner lane 0)
+        point(I1{});
+        point(I2{});
+        point(I3{});
+      }
+      res2 = res1;
+      res1 = res0;
+      res0 = mine;
+      o2 = o2n;
+      o2n = o2nn;
+      mk = mkn;
+      mkn = mknn;
+    }
+
+    // Offset and mask gradients of the own slots (a NaN sampling location
+    // makes its point's offset gradient and gm NaN).
+    if (cur.live) {
+      const float3 rs[3] = {res2, res1, res0};
+      float gm[3];
+#pragma unroll
+      for (int r = 0; r < 3; ++r) gm[r] = rs[r].x;
+      if constexpr (SOFTMAX) {
+        float dot = m[0] * gm[0] + m[1] * gm[1];
+        if (sub == 0) dot += m[2] * gm[2];
+        dot = quad_sum(dot);
+#pragma unroll
+        for (int r = 0; r < 3; ++r) gm[r] = m[r] * (gm[r] - dot);
+      }
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      const uint32_t orow = cur.pg * (K * 8), mrow = cur.pg * (K * 4);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(4))),
+                            f4{s * m[0] * rs[0].y, s * m[0] * rs[0].z, s * m[1] * rs[1].y, s * m[1] * rs[1].z}),
+          rgoff, (int)(orow + 16 * sub), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(
+          __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), f2{gm[0], gm[1]}), rgm,
+          (int)(mrow + 8 * sub), 0, 0);
+      if (sub == 0) {
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), f2{s * m[2] * rs[2].y, s * m[2] * rs[2].z}),
+            rgoff, (int)(orow + 64), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gm[2]), rgm, (int)(mrow + 32), 0, 0);
+      }
+    }
+
+    __syncthreads();  // every scatter into the grad window is done
+    // Add the grad window to grad_input, 16 lanes per window pixel (one
+    // 64-byte request), and clear it for the next item.  Pixels outside the
+    // map and zero sums are skipped.
+    {
+      const uint32_t ch = threadIdx.x & 15u;
+      const uint32_t cbyte = cur.g * (uint32_t)(CG * 4) + ch * 4u;
+#pragma unroll 2
+      for (int idx = (int)(threadIdx.x >> 4); idx < SPAN; idx += kBqThreads / 16) {
+        const int sy = idx / SPAN_W, sx = idx - sy * SPAN_W;
+        const int gy_ = cur.Y0 + sy, gx_ = cur.X0 + sx;
+        const bool ok = (uint32_t)gy_ < (uint32_t)p.H && (uint32_t)gx_ < (uint32_t)p.W;
+        uint64_t *slot = reinterpret_cast<uint64_t *>(lds + GWIN + idx * PIXB + (ch >> 1) * 8u);
+        const int2 pr = pair_sums(*slot);
+        if ((ch & 1u) == 0) *slot = 0;  // after both lanes of the pair have read it (same instruction)
+        const int q = (ch & 1u) ? pr.y : pr.x;
+        const uint32_t dst = cur.img + (uint32_t)gy_ * row_bytes + (uint32_t)gx_ * pix_bytes + cbyte;
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32((float)q * invS, rgx, (int)((ok && q != 0) ? dst : kOutOfRange), 0, 0);
+      }
+    }
+
+    item = next;
+    cur = nx;
+  }
+}
+
+namespace {
+
+template <bool SM>
+hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s) {
+  auto kern = dcn_bwd_quad_kernel<SM>;
+  // Set on every launch: the limit is per device and setting it is idempotent.
+  const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBqLds);
+  if (attr != hipSuccess) return attr;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), kBqThreads,
+                                                     kBqLds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorNotSupported;
+  const uint32_t blocks = std::min<uint32_t>(tg.items, (uint32_t)per_cu * (uint32_t)cus);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kBqThreads), kBqLds, s, p, tg);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// 3x3 points, stride 1, dilation 1 only; hipErrorNotSupported otherwise.
+hipError_t launch_backward_quad(int softmax, const BwdParams &b, hipStream_t s) {
+  const FwdParams &p = b.f;
+  if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
+    return hipErrorNotSupported;
+  TileGeom tg{};
+  tg.span_h = tg.span_w = kBqSpan;
+  const int tiles_y = (p.Ho + kBqTile - 1) / kBqTile;
+  tg.tiles_x = (p.Wo + kBqTile - 1) / kBqTile;
+  tg.tiles_per_img = tiles_y * tg.tiles_x;
+  const int64_t imgs = p.pg_total / ((int64_t)p.Ho * p.Wo * p.G);
+  const int64_t items = imgs * tg.tiles_per_img * p.G;
+  if (items <= 0 || items >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  tg.items = (uint32_t)items;
+  tg.div_g = make_fast_div((uint32_t)p.G);
+  tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
+  tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
+  tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
+  return softmax ? launch_bwd_quad<true>(b, tg, s) : launch_bwd_quad<false>(b, tg, s);
+}
+
+}  // namespace dcn

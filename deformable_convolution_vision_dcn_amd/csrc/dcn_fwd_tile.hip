@@ -28,132 +28,10 @@
 #include <type_traits>
 
 #include "dcn_device.hpp"
+#include "quad_ops.hpp"
 
 namespace dcn {
 
-namespace {
-
-template <int O>
-__device__ __forceinline__ int qbcast(int v) {
-  constexpr int ctrl = O | (O << 2) | (O << 4) | (O << 6);  // quad_perm [O,O,O,O]
-  return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, false);
-}
-template <int O>
-__device__ __forceinline__ float qbcast(float v) {
-  return __int_as_float(qbcast<O>(__float_as_int(v)));
-}
-
-// acc[c] += w(lane O of the quad) * v[c]: the broadcast rides on the FMA as a
-// DPP operand instead of a separate move.  The compiler does not look inside
-// asm for the DPP hazard (a VALU write of w then a DPP read of it needs two
-// wait states), hence the s_nop.
-#define DCN_FMA4_DPP(QP)                                                              \
-  asm("s_nop 1\n\t"                                                                  \
-      "v_fmac_f32_dpp %0, %4, %5 " QP " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %1, %4, %6 " QP " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %2, %4, %7 " QP " row_mask:0xf bank_mask:0xf\n\t"              \
-      "v_fmac_f32_dpp %3, %4, %8 " QP " row_mask:0xf bank_mask:0xf"                    \
-      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])                        \
-      : "v"(w), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]))
-template <int O>
-__device__ __forceinline__ void fma4_bcast(float (&acc)[4], float w, const float (&v)[4]) {
-  if constexpr (O == 0) DCN_FMA4_DPP("quad_perm:[0,0,0,0]");
-  if constexpr (O == 1) DCN_FMA4_DPP("quad_perm:[1,1,1,1]");
-  if constexpr (O == 2) DCN_FMA4_DPP("quad_perm:[2,2,2,2]");
-  if constexpr (O == 3) DCN_FMA4_DPP("quad_perm:[3,3,3,3]");
-}
-#undef DCN_FMA4_DPP
-
-// a(lane O of the quad) + b, the broadcast again a DPP operand.
-#define DCN_ADD_DPP(QP)                                                               \
-  asm("s_nop 1\n\tv_add_u32_dpp %0, %1, %2 " QP " row_mask:0xf bank_mask:0xf"         \
-      : "=v"(r) : "v"(a), "v"(b))
-template <int O>
-__device__ __forceinline__ uint32_t add_bcast(uint32_t a, uint32_t b) {
-  uint32_t r;
-  if constexpr (O == 0) DCN_ADD_DPP("quad_perm:[0,0,0,0]");
-  if constexpr (O == 1) DCN_ADD_DPP("quad_perm:[1,1,1,1]");
-  if constexpr (O == 2) DCN_ADD_DPP("quad_perm:[2,2,2,2]");
-  if constexpr (O == 3) DCN_ADD_DPP("quad_perm:[3,3,3,3]");
-  return r;
-}
-#undef DCN_ADD_DPP
-
-__device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  return v;
-}
-__device__ __forceinline__ float quad_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  return v;
-}
-
-template <int NW>
-__device__ __forceinline__ void lds_store(unsigned char *dst, const uint32_t (&w)[NW]) {
-  if constexpr (NW == 4) {
-    *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-    *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
-  }
-}
-// Read NW words at LDS byte address `addr` (an address, not an offset from a
-// generic pointer, so no base is added on the per-point path).
-template <int NW>
-__device__ __forceinline__ void lds_load_at(uint32_t addr, uint32_t (&w)[NW]) {
-  typedef uint32_t V __attribute__((ext_vector_type(NW)));
-  typedef __attribute__((address_space(3))) const V L;
-  const V v = *(L *)(size_t)addr;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) w[i] = v[i];
-}
-
-// a * b + c on the 24-bit multiplier (full rate; a, b < 2^24).
-__device__ __forceinline__ uint32_t mad24(uint32_t a, uint32_t b, uint32_t c) {
-  uint32_t r;
-  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ uint32_t mul24(uint32_t a, uint32_t b) {
-  uint32_t r;
-  asm("v_mul_u32_u24 %0, %2, %1" : "=v"(r) : "v"(a), "s"(b));
-  return r;
-}
-
-template <int NW>
-__device__ __forceinline__ void lds_load(const unsigned char *src, uint32_t (&w)[NW]) {
-  if constexpr (NW == 4) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(src);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2 *>(src);
-    w[0] = v.x; w[1] = v.y;
-  }
-}
-
-// (x, y) offset pair of element pair index e, widened to fp32.
-template <int DT>
-__device__ __forceinline__ float2 load_pair(const void *base, uint32_t e) {
-  if constexpr (DT == DCN_F32) {
-    return static_cast<const float2 *>(base)[e];
-  } else {
-    const uint32_t w = static_cast<const uint32_t *>(base)[e];
-    return make_float2(Io<DT>::lo(w), Io<DT>::hi(w));
-  }
-}
-template <int DT>
-__device__ __forceinline__ float load_one(const void *base, uint32_t e) {
-  if constexpr (DT == DCN_F32) {
-    return static_cast<const float *>(base)[e];
-  } else if constexpr (DT == DCN_F16) {
-    return (float)static_cast<const _Float16 *>(base)[e];
-  } else {
-    return __uint_as_float((uint32_t) static_cast<const uint16_t *>(base)[e] << 16);
-  }
-}
-
-}  // namespace
 
 #ifndef DCN_TILE_WAVES
 #define DCN_TILE_WAVES 4  // waves per SIMD the register budget must allow

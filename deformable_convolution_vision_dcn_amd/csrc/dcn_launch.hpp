@@ -56,6 +56,7 @@ hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipS
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s);
 hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_tiled(int softmax, const BwdParams &p, hipStream_t s);
+hipError_t launch_backward_quad(int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_zero(void *dst, uint64_t bytes, hipStream_t s);
 
 }  // namespace dcn

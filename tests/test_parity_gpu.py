@@ -215,15 +215,12 @@ BWD_PATH_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["generic", "tiled"])
+@pytest.mark.parametrize("path", ["generic", "tiled", "quad"])
 @pytest.mark.parametrize("wl", BWD_PATH_CASES, ids=lambda w: w.name)
 def test_backward_each_kernel(wl, path, monkeypatch):
-    """Both backward kernels, forced in turn, on multi-tile ragged shapes
+    """Every backward kernel, forced in turn, on multi-tile ragged shapes
     whose offsets also leave the tile windows (the global fix-up path)."""
-    if path == "generic":
-        monkeypatch.setenv("DCN_MI355X_BWD_PATH", "generic")
-    else:
-        monkeypatch.delenv("DCN_MI355X_BWD_PATH", raising=False)
+    monkeypatch.setenv("DCN_MI355X_BWD_PATH", path)
     print(f"backward {wl.name} path={path}", flush=True)
     t = synth.make_inputs(wl, with_grad=True)
     gx, goff, gm = run_backward(wl, t)
