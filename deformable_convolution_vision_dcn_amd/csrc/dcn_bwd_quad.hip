@@ -50,22 +50,10 @@ constexpr int kBqWin = kBqSpan * kBqSpan * kBqPixB;       // one window
 constexpr int kBqZero = kBqRow + 2 * kBqPixB;             // zero block after the input window
 constexpr int kBqThreads = 1024;
 constexpr int kBqWaves = kBqThreads / 64;
-constexpr size_t kBqLds = (size_t)kBqWin + kBqZero + kBqWin + 4 * kBqWaves;
+constexpr int kBqSink = kBqRow + 2 * kBqPixB;             // scatter sink after the grad window
+constexpr size_t kBqLds = (size_t)kBqWin + kBqZero + kBqWin + kBqSink + 4 * kBqWaves;
 
 namespace {
-
-// v + v(quad lane swizzled by the DPP control), the swizzle a DPP operand.
-#define DCN_ADDF_DPP(QP)                                                              \
-  asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 " QP " row_mask:0xf bank_mask:0xf"         \
-      : "=v"(r) : "v"(v))
-__device__ __forceinline__ float quad_sum_fused(float v) {
-  float r;
-  DCN_ADDF_DPP("quad_perm:[1,0,3,2]");
-  v = r;
-  DCN_ADDF_DPP("quad_perm:[2,3,0,1]");
-  return r;
-}
-#undef DCN_ADDF_DPP
 
 // Two neighbouring channels' fixed-point terms added by one 64-bit LDS
 // integer add (ds_add_u64) at LDS byte address `addr`.  The pair is the
@@ -96,12 +84,13 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
   constexpr int SLOTS = (SPAN + WPIX - 1) / WPIX;
   constexpr uint32_t ZERO = kBqWin;                      // zero block (reads of outside samples)
   constexpr uint32_t GWIN = kBqWin + kBqZero;            // fixed-point grad window
+  constexpr uint32_t SINK = GWIN + kBqWin;               // scatter target of samples not in the window
   static_assert(CG == 16, "a quad covers 16 channels");
 
   extern __shared__ __align__(16) unsigned char lds[];
   typedef __attribute__((address_space(3))) unsigned char lds_byte;
   const uint32_t lbase = (uint32_t)(size_t)(lds_byte *)lds;
-  float *wave_sums = reinterpret_cast<float *>(lds + GWIN + kBqWin);
+  float *wave_sums = reinterpret_cast<float *>(lds + SINK + kBqSink);
 
   const uint32_t quad = threadIdx.x >> 2, sub = threadIdx.x & 3;
   const int oy = (int)quad / TS, ox = (int)quad % TS;  // output pixel within the tile
@@ -323,8 +312,12 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
       // outside the window but touching the map: global gathers and atomics
       const bool fb = cur.live && !inside && !nan_loc && (uint32_t)(cur.Y0 + 1 + ty) <= (uint32_t)p.H &&
                       (uint32_t)(cur.X0 + 1 + tx) <= (uint32_t)p.W;
-      const bool scat = fixed && inside;           // LDS scatter
+      // LDS scatter target: the window, or the sink for samples it does not
+      // hold (outside it, NaN locations, dead lanes), which is never read.
+      const uint32_t AS = inside ? A : SINK - GWIN;
       const bool gscat = fixed ? fb : (cur.live && !nan_loc);  // global scatter
+      const bool fb_any = __builtin_amdgcn_ballot_w64(fb) != 0;      // wave-uniform
+      const bool gs_any = __builtin_amdgcn_ballot_w64(gscat) != 0;   // wave-uniform
       float3 mine = make_float3(0.f, 0.f, 0.f);
 
       auto point = [&](auto o_tag) {
@@ -336,13 +329,13 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
         lds_load_at<4>(src + PIXB, q01);
         lds_load_at<4>(src + ROW, q10);
         lds_load_at<4>(src + ROW + PIXB, q11);
-        float P00 = 0.f, P01 = 0.f, P10 = 0.f, P11 = 0.f;
+        float P[4] = {0.f, 0.f, 0.f, 0.f};  // corners 00, 01, 10, 11
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          P00 = fmaf(gy[c], __uint_as_float(q00[c]), P00);
-          P01 = fmaf(gy[c], __uint_as_float(q01[c]), P01);
-          P10 = fmaf(gy[c], __uint_as_float(q10[c]), P10);
-          P11 = fmaf(gy[c], __uint_as_float(q11[c]), P11);
+          P[0] = fmaf(gy[c], __uint_as_float(q00[c]), P[0]);
+          P[1] = fmaf(gy[c], __uint_as_float(q01[c]), P[1]);
+          P[2] = fmaf(gy[c], __uint_as_float(q10[c]), P[2]);
+          P[3] = fmaf(gy[c], __uint_as_float(q11[c]), P[3]);
         }
         // Global byte offsets of the owner's four corners for this lane's
         // channels (out of range where a corner is outside the map).
@@ -356,9 +349,8 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
           ga[2] = (vy1 && vx0) ? a00 + row_bytes : kOutOfRange;
           ga[3] = (vy1 && vx1) ? a00 + row_bytes + pix_bytes : kOutOfRange;
         };
-        const int ofb = qbcast<O>((int)fb);
-        if (__builtin_amdgcn_ballot_w64(ofb != 0) != 0) {  // a quad of the wave left its window
-          if (ofb) {
+        if (fb_any) {  // a quad of the wave left its window this round
+          if (qbcast<O>((int)fb)) {
             uint32_t ga[4];
             corners(ga);
             const uint32_t g00 = ga[0], g01 = ga[1], g10 = ga[2], g11 = ga[3];
@@ -368,38 +360,39 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
             buffer_load_words<4>(rin, g11, q11);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              P00 = fmaf(gy[c], __uint_as_float(q00[c]), P00);
-              P01 = fmaf(gy[c], __uint_as_float(q01[c]), P01);
-              P10 = fmaf(gy[c], __uint_as_float(q10[c]), P10);
-              P11 = fmaf(gy[c], __uint_as_float(q11[c]), P11);
+              P[0] = fmaf(gy[c], __uint_as_float(q00[c]), P[0]);
+              P[1] = fmaf(gy[c], __uint_as_float(q01[c]), P[1]);
+              P[2] = fmaf(gy[c], __uint_as_float(q10[c]), P[2]);
+              P[3] = fmaf(gy[c], __uint_as_float(q11[c]), P[3]);
             }
           }
         }
         // Sums over the 16 channels: every lane of the quad gets them; the
         // owner keeps gm, d/dx and d/dy of its point (one-sided derivatives
         // of the bilinear form, linear in the corner sums).
-        const float G00 = quad_sum_fused(P00), G01 = quad_sum_fused(P01);
-        const float G10 = quad_sum_fused(P10), G11 = quad_sum_fused(P11);
+        quad_sum4(P);
+        const float G00 = P[0], G01 = P[1], G10 = P[2], G11 = P[3];
         if (sub == (uint32_t)O) {
           const float T = hx * G00 + lx * G01, Bt = hx * G10 + lx * G11;
           mine = nan_loc ? make_float3(qnan, qnan, qnan)
                          : make_float3(hy * T + ly * Bt, hy * (G01 - G00) + ly * (G11 - G10), Bt - T);
         }
-        // Scatter m_k * w_corner * gy_c of this lane's 4 channels.
-        if (qbcast<O>((int)scat)) {
-          const uint32_t d = add_bcast<O>(A, gwin_chunk);
+        // Scatter m_k * w_corner * gy_c of this lane's 4 channels (no
+        // branch: samples the window does not hold add into the sink).
+        if (fixed) {  // block-uniform
+          const uint32_t d = add_bcast<O>(AS, gwin_chunk);
           auto corner = [&](float w, uint32_t at) {
-            const float t0 = mul_bcast<O>(w, gy[0]), t1 = mul_bcast<O>(w, gy[1]);
-            const float t2 = mul_bcast<O>(w, gy[2]), t3 = mul_bcast<O>(w, gy[3]);
-            lds_add_pair(at, cvt_rpi(t0), cvt_rpi(t1));
-            lds_add_pair(at + 8, cvt_rpi(t2), cvt_rpi(t3));
+            float t[4];
+            mul4_bcast<O>(t, w, gy);
+            lds_add_pair(at, cvt_rpi(t[0]), cvt_rpi(t[1]));
+            lds_add_pair(at + 8, cvt_rpi(t[2]), cvt_rpi(t[3]));
           };
           corner(W0s, d);
           corner(W1s, d + PIXB);
           corner(W2s, d + ROW);
           corner(W3s, d + ROW + PIXB);
         }
-        if (__builtin_amdgcn_ballot_w64(qbcast<O>((int)gscat) != 0) != 0) {
+        if (gs_any) {
           if (qbcast<O>((int)gscat)) {
             uint32_t ga[4];
             corners(ga);
@@ -473,19 +466,33 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
     // 64-byte request), and clear it for the next item.  Pixels outside the
     // map and zero sums are skipped.
     {
+      // Pixel idx = threadIdx.x / 16 + 64 j of the window, its row, column
+      // and grad_input offset walked incrementally.
+      constexpr int STEP = kBqThreads / 16;
+      constexpr int DY = STEP / SPAN_W, DX = STEP % SPAN_W;
       const uint32_t ch = threadIdx.x & 15u;
-      const uint32_t cbyte = cur.g * (uint32_t)(CG * 4) + ch * 4u;
+      int idx = (int)(threadIdx.x >> 4);
+      int sy = idx / SPAN_W, sx = idx - sy * SPAN_W;
+      uint32_t dst = cur.img + (uint32_t)(cur.Y0 + sy) * row_bytes + (uint32_t)(cur.X0 + sx) * pix_bytes +
+                     cur.g * (uint32_t)(CG * 4) + ch * 4u;
+      const uint32_t slot0 = lbase + GWIN + (ch >> 1) * 8u;
+      typedef __attribute__((address_space(3))) uint64_t L;
 #pragma unroll 2
-      for (int idx = (int)(threadIdx.x >> 4); idx < SPAN; idx += kBqThreads / 16) {
-        const int sy = idx / SPAN_W, sx = idx - sy * SPAN_W;
-        const int gy_ = cur.Y0 + sy, gx_ = cur.X0 + sx;
-        const bool ok = (uint32_t)gy_ < (uint32_t)p.H && (uint32_t)gx_ < (uint32_t)p.W;
-        uint64_t *slot = reinterpret_cast<uint64_t *>(lds + GWIN + idx * PIXB + (ch >> 1) * 8u);
+      for (; idx < SPAN; idx += STEP) {
+        const bool ok = (uint32_t)(cur.Y0 + sy) < (uint32_t)p.H && (uint32_t)(cur.X0 + sx) < (uint32_t)p.W;
+        L *slot = (L *)(size_t)(slot0 + (uint32_t)idx * PIXB);
         const int2 pr = pair_sums(*slot);
         if ((ch & 1u) == 0) *slot = 0;  // after both lanes of the pair have read it (same instruction)
         const int q = (ch & 1u) ? pr.y : pr.x;
-        const uint32_t dst = cur.img + (uint32_t)gy_ * row_bytes + (uint32_t)gx_ * pix_bytes + cbyte;
         __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32((float)q * invS, rgx, (int)((ok && q != 0) ? dst : kOutOfRange), 0, 0);
+        sx += DX;
+        sy += DY;
+        dst += (uint32_t)DY * row_bytes + (uint32_t)DX * pix_bytes;
+        if (sx >= SPAN_W) {
+          sx -= SPAN_W;
+          sy += 1;
+          dst += row_bytes - (uint32_t)SPAN_W * pix_bytes;
+        }
       }
     }
 

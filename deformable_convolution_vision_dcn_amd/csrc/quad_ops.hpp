@@ -114,6 +114,44 @@ __device__ __forceinline__ float mul_bcast(float w, float x) {
 }
 #undef DCN_MUL_DPP
 
+// r[i] = w(lane O of the quad) * x[i] for four x, one hazard wait for all.
+#define DCN_MUL4_DPP(QP)                                                              \
+  asm("s_nop 1\n\t"                                                                  \
+      "v_mul_f32_dpp %0, %4, %5 " QP " row_mask:0xf bank_mask:0xf\n\t"               \
+      "v_mul_f32_dpp %1, %4, %6 " QP " row_mask:0xf bank_mask:0xf\n\t"               \
+      "v_mul_f32_dpp %2, %4, %7 " QP " row_mask:0xf bank_mask:0xf\n\t"               \
+      "v_mul_f32_dpp %3, %4, %8 " QP " row_mask:0xf bank_mask:0xf"                     \
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])                            \
+      : "v"(w), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]))
+template <int O>
+__device__ __forceinline__ void mul4_bcast(float (&r)[4], float w, const float (&x)[4]) {
+  if constexpr (O == 0) DCN_MUL4_DPP("quad_perm:[0,0,0,0]");
+  if constexpr (O == 1) DCN_MUL4_DPP("quad_perm:[1,1,1,1]");
+  if constexpr (O == 2) DCN_MUL4_DPP("quad_perm:[2,2,2,2]");
+  if constexpr (O == 3) DCN_MUL4_DPP("quad_perm:[3,3,3,3]");
+}
+#undef DCN_MUL4_DPP
+
+// Quad sums of four values (every lane gets all four), the swizzles DPP
+// operands of the adds.  One hazard wait covers the inputs; the second step
+// reads results written at least three instructions earlier.
+__device__ __forceinline__ void quad_sum4(float (&v)[4]) {
+  float t0, t1, t2, t3;
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %4, %4 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %5, %5 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %2, %6, %6 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %3, %7, %7 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+  asm("v_add_f32_dpp %0, %4, %4 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %1, %5, %5 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %2, %6, %6 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %3, %7, %7 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(t0), "v"(t1), "v"(t2), "v"(t3));
+}
+
 // floor(x + 0.5) as an integer in one instruction (round half up).
 __device__ __forceinline__ int cvt_rpi(float x) {
   int r;
