@@ -293,6 +293,11 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
     float mk = m[0], mkn = m[1], mknn = m[2];
 #pragma unroll 1
     for (int r = 0; r < 3; ++r) {
+      // Wave priority falls round by round: the waves furthest behind issue
+      // first, so the block reaches its flush barrier with less spread.
+      if (r == 0) __builtin_amdgcn_s_setprio(3);
+      if (r == 1) __builtin_amdgcn_s_setprio(2);
+      if (r == 2) __builtin_amdgcn_s_setprio(1);
       const float dx = s * o2.x, dy = s * o2.y;
       const bool nan_loc = (dx != dx) | (dy != dy);
       const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
@@ -461,6 +466,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // every scatter into the grad window is done
     // Add the grad window to grad_input, 16 lanes per window pixel (one
     // 64-byte request), and clear it for the next item.  Pixels outside the

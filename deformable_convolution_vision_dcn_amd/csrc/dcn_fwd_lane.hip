@@ -209,6 +209,12 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
 
 #pragma unroll
       for (int k = 0; k < K; ++k) {
+        // Wave priority falls as the wave moves through the points, so the
+        // waves furthest behind issue first and the block reaches its next
+        // barrier with less spread.
+        if (k == 0) __builtin_amdgcn_s_setprio(3);
+        if (k == 3) __builtin_amdgcn_s_setprio(2);
+        if (k == 6) __builtin_amdgcn_s_setprio(1);
         const int i = k / 3, j = k % 3;
         const float dx = s * off[2 * k], dy = s * off[2 * k + 1];
         const bool nan_loc = (dx != dx) | (dy != dy);
@@ -290,6 +296,7 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
         buffer_store_words<4>(rout, obase + (uint32_t)rot[t], w);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     issue_pgdata(nx);
 
     item = next;
