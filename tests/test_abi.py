@@ -99,6 +99,11 @@ BASE = dict(n=2, h=9, w=7, c=32, groups=2, kernel_h=3, kernel_w=3, stride_h=1, s
     ({"kernel_h": 9, "kernel_w": 9, "pad_h": 4, "pad_w": 4}, "DCN_ERR_UNSUPPORTED"),  # 81 points
     ({"h": 1 << 25}, "DCN_ERR_TOO_LARGE"),
     ({"h": 8192, "w": 8192, "c": 32}, "DCN_ERR_TOO_LARGE"),   # 8 GiB per image
+    # 2048x2048x64 fp32: input and output 1 GiB per image; the offsets of a
+    # 3x3 window take 1.2 GiB, those of a 5x5 window 3.1 GiB.
+    ({"h": 2048, "w": 2048, "c": 64, "groups": 4}, "DCN_OK"),
+    ({"h": 2048, "w": 2048, "c": 64, "groups": 4, "kernel_h": 5, "kernel_w": 5,
+      "pad_h": 2, "pad_w": 2}, "DCN_ERR_TOO_LARGE"),
 ])
 def test_check_table(lib, change, code):
     p = _capi.make_problem(**{**BASE, **change})
