@@ -114,6 +114,34 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   const int DW = UNIT ? 1 : p.DW, DH = UNIT ? 1 : p.DH;
   const float s = p.scale;
 
+  // Window slots at unit stride.  A lane stages the same window pixels of
+  // every item: main slice u holds window rows [u RPS, u RPS + RPS) of
+  // columns [0, CW), the last slice the rows below and the columns right of
+  // that block.  So the per-item address work is one uniform base plus one
+  // column check per lane; rows outside the map fall out of the image's
+  // buffer range (negative or past its last byte) and read zero.
+  constexpr int CW = USPAN > 32 ? 32 : USPAN;
+  constexpr int RPS = WPIX / CW;
+  constexpr int NM = USPAN / RPS;
+  constexpr int REM_A = (USPAN - NM * RPS) * CW, REM_B = (USPAN - CW) * USPAN;
+  constexpr int WSL = UNIT ? NM + 1 : MAXPQ;  // register slices of a window
+  static_assert(!UNIT || (NM + 1 <= MAXPQ && REM_A + REM_B <= WPIX), "window slot mapping");
+  const uint32_t slot = threadIdx.x / LPP;
+  const uint32_t m_col = slot % CW;
+  const bool m_live = slot < (uint32_t)(RPS * CW);
+  uint32_t r_y = 0, r_x = 0;
+  if (slot < (uint32_t)REM_A) {
+    r_y = NM * RPS + slot / CW;
+    r_x = slot % CW;
+  } else if constexpr (USPAN > CW) {
+    r_y = (slot - REM_A) / (USPAN - CW);
+    r_x = CW + (slot - REM_A) % (USPAN - CW);
+  }
+  const bool r_live = slot < (uint32_t)(REM_A + REM_B);
+  const uint32_t m_lane = (slot / CW) * row_bytes + m_col * pix_bytes + wlane * LANE_BYTES;
+  const uint32_t r_lane = r_y * row_bytes + r_x * pix_bytes + wlane * LANE_BYTES;
+  const uint32_t img_bytes = (uint32_t)p.H * row_bytes;
+
   // Window coordinates of the kernel point of each own slot before its
   // offset, for pass 0 (pass 1 adds PIXPP / TW output rows), packed as three
   // 10-bit fields (every coordinate is below the span, at most 1023).  The
@@ -164,11 +192,21 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
 
   // Window slices of an item, LPP lanes per pixel: requested into registers
   // while the previous item computes, written to LDS when it is done.
-  uint32_t win[MAXPQ][NW];
+  uint32_t win[WSL][NW];
   // Issued on every path (an item that does not exist loads nothing: every
   // offset out of range), so that the compiler's count of outstanding loads
   // stays exact and no wait covers a prefetch before it is needed.
   auto issue_window = [&](const Item &I, bool valid) {
+    if constexpr (UNIT) {
+      const __amdgpu_buffer_rsrc_t rimg = make_rsrc(static_cast<const unsigned char *>(p.input) + I.img, img_bytes);
+      const uint32_t base = (uint32_t)I.Y0 * row_bytes + (uint32_t)I.X0 * pix_bytes + I.g * GBYTES;  // mod 2^32
+      const uint32_t m_off = valid && m_live && (uint32_t)(I.X0 + (int)m_col) < (uint32_t)p.W ? base + m_lane : kOutOfRange;
+#pragma unroll
+      for (int u = 0; u < NM; ++u) buffer_load_words<NW>(rimg, m_off + (uint32_t)(u * RPS) * row_bytes, win[u]);
+      const uint32_t r_off = valid && r_live && (uint32_t)(I.X0 + (int)r_x) < (uint32_t)p.W ? base + r_lane : kOutOfRange;
+      buffer_load_words<NW>(rimg, r_off, win[NM]);
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < MAXPQ; ++u) {
       const int idx = (int)(threadIdx.x / LPP) + u * WPIX;
@@ -184,6 +222,14 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
     }
   };
   auto store_window = [&]() {
+    if constexpr (UNIT) {
+      const uint32_t m_lds = (slot / CW) * row_lds + m_col * PIXB + wlane * LANE_BYTES;
+#pragma unroll
+      for (int u = 0; u < NM; ++u)
+        if (m_live) lds_store<NW>(tile + m_lds + u * RPS * row_lds, win[u]);
+      if (r_live) lds_store<NW>(tile + r_y * row_lds + r_x * PIXB + wlane * LANE_BYTES, win[NM]);
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < MAXPQ; ++u) {
       const int idx = (int)(threadIdx.x / LPP) + u * WPIX;
@@ -295,13 +341,10 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
       if (sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 only
       if constexpr (SOFTMAX) {
         const float mx = quad_max(fmaxf(fmaxf(lgs[0], lgs[1]), lgs[2]));
-        float e[3], sum = 0.f;
+        float e[3];
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-          e[r] = (r < 2 || sub == 0) ? __expf(lgs[r] - mx) : 0.f;
-          sum += e[r];
-        }
-        const float inv = __builtin_amdgcn_rcpf(quad_sum(sum));
+        for (int r = 0; r < 3; ++r) e[r] = (r < 2 || sub == 0) ? __expf(lgs[r] - mx) : 0.f;
+        const float inv = __builtin_amdgcn_rcpf(quad_sum(e[0] + e[1] + e[2]));
 #pragma unroll
         for (int r = 0; r < 3; ++r) m[r] = e[r] * inv;
       } else {
@@ -321,7 +364,7 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
       float2 o2 = offs[0], o2n = offs[1], o2nn = offs[2];
       float mk = m[0], mkn = m[1], mknn = m[2];
       const int by_pass = ps * (PIXPP / TW) * SH;
-#pragma unroll 1
+#pragma unroll
       for (int r = 0; r < 3; ++r) {
         const float dx = s * o2.x, dy = s * o2.y;
         const bool nan_loc = (dx != dx) | (dy != dy);
@@ -492,6 +535,13 @@ bool tile_geometry(int dtype, const FwdParams &p, TileGeom &tg) {
   const int pixb = dtype == DCN_F32 ? tile_pixel_stride<DCN_F32, GP>() : tile_pixel_stride<DCN_F16, GP>();
   if (tile_lds_bytes(tg, pixb) > (size_t)tile_lds_limit<GP>()) return false;
   if (tg.span_h * tg.span_w > tile_max_span<GP>()) return false;
+  // At unit stride the window rows above and below the map are rejected by
+  // the buffer range of their image, which needs the byte offset of every
+  // window row relative to the image (rows -pad - halo - 1 to
+  // H + pad + halo + 1) to fit int32.
+  const bool unit = p.SH == 1 && p.SW == 1 && p.DH == 1 && p.DW == 1;
+  const int64_t row_bytes = (int64_t)p.W * p.C * (dtype == DCN_F32 ? 4 : 2);
+  if (unit && ((int64_t)p.H + p.PH + tg.span_h + 1) * row_bytes >= (int64_t(1) << 31)) return false;
   const int tiles_y = (p.Ho + kTileH - 1) / kTileH;
   tg.tiles_x = (p.Wo + kTileW - 1) / kTileW;
   tg.tiles_per_img = tiles_y * tg.tiles_x;

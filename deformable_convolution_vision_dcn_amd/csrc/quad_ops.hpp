@@ -56,15 +56,23 @@ __device__ __forceinline__ uint32_t add_bcast(uint32_t a, uint32_t b) {
 }
 #undef DCN_ADD_DPP
 
+// Maximum and sum over the four lanes of a quad, one fused DPP instruction
+// per butterfly step.  The maximum drops a quiet NaN operand like fmaxf.
 __device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  return v;
+  float t, r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "=&v"(t) : "v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+      : "=&v"(r) : "v"(t));
+  return r;
 }
 __device__ __forceinline__ float quad_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  return v;
+  float t, r;
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "=&v"(t) : "v"(v));
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+      : "=&v"(r) : "v"(t));
+  return r;
 }
 
 template <int NW>
