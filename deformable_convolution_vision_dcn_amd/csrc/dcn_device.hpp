@@ -47,19 +47,27 @@ __device__ __forceinline__ void buffer_load_words(__amdgpu_buffer_rsrc_t r, uint
 
 // Store NW 32-bit words (NW in {1, 2, 4}) at byte offset voff; offsets beyond
 // num_records are dropped by the hardware.
-template <int NW>
-__device__ __forceinline__ void buffer_store_words(__amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                                   const uint32_t (&w)[NW]) {
+// AUX: the cache-policy operand of the buffer instruction (0 = default).
+constexpr int kNonTemporal = 2;  // the nt bit: streamed, evicted first
+template <int NW, int AUX>
+__device__ __forceinline__ void buffer_store_words_aux(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                       const uint32_t (&w)[NW]) {
   if constexpr (NW == 1) {
-    __builtin_amdgcn_raw_buffer_store_b32(w[0], r, (int)voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], r, (int)voff, 0, AUX);
   } else if constexpr (NW == 2) {
     typedef uint32_t v2 __attribute__((ext_vector_type(2)));
-    __builtin_amdgcn_raw_buffer_store_b64(v2{w[0], w[1]}, r, (int)voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v2{w[0], w[1]}, r, (int)voff, 0, AUX);
   } else {
     static_assert(NW == 4, "word count");
     typedef uint32_t v4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(v4{w[0], w[1], w[2], w[3]}, r, (int)voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v4{w[0], w[1], w[2], w[3]}, r, (int)voff, 0, AUX);
   }
+}
+
+template <int NW>
+__device__ __forceinline__ void buffer_store_words(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                   const uint32_t (&w)[NW]) {
+  buffer_store_words_aux<NW, 0>(r, voff, w);
 }
 
 // ---------------------------------------------------------------- I/O types

@@ -201,9 +201,9 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
       const __amdgpu_buffer_rsrc_t rimg = make_rsrc(static_cast<const unsigned char *>(p.input) + I.img, img_bytes);
       const uint32_t base = (uint32_t)I.Y0 * row_bytes + (uint32_t)I.X0 * pix_bytes + I.g * GBYTES;  // mod 2^32
       const uint32_t m_off = valid && m_live && (uint32_t)(I.X0 + (int)m_col) < (uint32_t)p.W ? base + m_lane : kOutOfRange;
+      const uint32_t r_off = valid && r_live && (uint32_t)(I.X0 + (int)r_x) < (uint32_t)p.W ? base + r_lane : kOutOfRange;
 #pragma unroll
       for (int u = 0; u < NM; ++u) buffer_load_words<NW>(rimg, m_off + (uint32_t)(u * RPS) * row_bytes, win[u]);
-      const uint32_t r_off = valid && r_live && (uint32_t)(I.X0 + (int)r_x) < (uint32_t)p.W ? base + r_lane : kOutOfRange;
       buffer_load_words<NW>(rimg, r_off, win[NM]);
       return;
     }
@@ -359,13 +359,12 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
       // Round r: every lane prepares its own point of slot r (location,
       // weights with the modulation folded in, window address), then the
       // quad consumes the round's points one owner at a time, the owner's
-      // address and weights reaching the other lanes as DPP operands.  The
-      // per-round inputs rotate through scalars (no run-time indexed arrays).
-      float2 o2 = offs[0], o2n = offs[1], o2nn = offs[2];
-      float mk = m[0], mkn = m[1], mknn = m[2];
+      // address and weights reaching the other lanes as DPP operands.
       const int by_pass = ps * (PIXPP / TW) * SH;
-#pragma unroll
-      for (int r = 0; r < 3; ++r) {
+      auto round = [&](auto r_tag) {
+        constexpr int r = decltype(r_tag)::value;
+        const float2 o2 = offs[r];
+        const float mk = m[r];
         const float dx = s * o2.x, dy = s * o2.y;
         const bool nan_loc = (dx != dx) | (dy != dy);
         const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
@@ -433,28 +432,28 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
         using I2 = std::integral_constant<int, 2>;
         using I3 = std::integral_constant<int, 3>;
         point(I0{});
-        if (r < 2) {  // the last round holds only k = 8 (owner lane 0)
+        if constexpr (r < 2) {  // the last round holds only k = 8 (owner lane 0)
           point(I1{});
           point(I2{});
           point(I3{});
         }
         if (__builtin_amdgcn_ballot_w64(fb) != 0) {  // a quad of the wave left its window
           fixup(I0{});
-          if (r < 2) {
+          if constexpr (r < 2) {
             fixup(I1{});
             fixup(I2{});
             fixup(I3{});
           }
         }
-        o2 = o2n;
-        o2n = o2nn;
-        mk = mkn;
-        mkn = mknn;
-      }
-
+      };
+      round(std::integral_constant<int, 0>{});
+      round(std::integral_constant<int, 1>{});
+      round(std::integral_constant<int, 2>{});
       uint32_t outw[NW];
       pack_words<DT, CPL>(acc, outw);
-      buffer_store_words<NW>(rout, (pg * CG + sub * CPL) * io::kBytes, outw);
+      // Outputs are not read again here: stored non-temporal, so they do not
+      // displace window and row lines from the L2.
+      buffer_store_words_aux<NW, kNonTemporal>(rout, (pg * CG + sub * CPL) * io::kBytes, outw);
     };
     // Wave priority by progress: waves still in pass 0 issue ahead of waves
     // in pass 1, and waves done with the item yield, so the block reaches
