@@ -17,7 +17,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 BUILD = PKG / "_build"
 LIB = PKG / "libdcn_mi355x.so"
-SOURCES = ["dcn_api.hip", "dcn_forward.hip", "dcn_fwd_tile.hip", "dcn_fwd_lane.hip", "dcn_backward.hip", "dcn_bwd_tile.hip", "dcn_bwd_quad.hip"]
+SOURCES = ["dcn_api.hip", "dcn_forward.hip", "dcn_fwd_tile.hip", "dcn_fwd_lane.hip", "dcn_fwd_map.hip", "dcn_backward.hip", "dcn_bwd_tile.hip", "dcn_bwd_quad.hip"]
 ARCH = "gfx950"
 
 

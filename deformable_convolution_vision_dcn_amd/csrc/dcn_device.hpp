@@ -47,6 +47,21 @@ __device__ __forceinline__ void buffer_load_words(__amdgpu_buffer_rsrc_t r, uint
 
 // Store NW 32-bit words (NW in {1, 2, 4}) at byte offset voff; offsets beyond
 // num_records are dropped by the hardware.
+// An empty asm that claims to modify its operands: the values must exist in
+// registers at this point of the program.  Used to keep a chain of FMAs next
+// to the loads that feed it: left alone, the compiler sinks pure arithmetic
+// to its last use and keeps every loaded operand live until then.
+template <int N>
+__device__ __forceinline__ void pin_values(float (&v)[N]) {
+  static_assert(N == 4 || N == 8, "four or eight values");
+  if constexpr (N == 4) {
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+  } else {
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                 "+v"(v[7]));
+  }
+}
+
 // AUX: the cache-policy operand of the buffer instruction (0 = default).
 constexpr int kNonTemporal = 2;  // the nt bit: streamed, evicted first
 template <int NW, int AUX>

@@ -208,9 +208,9 @@ hipError_t launch_dt(int softmax, const FwdParams &p, hipStream_t s) {
 
 // Forward path override for tests and measurements: DCN_MI355X_FWD_PATH =
 // "generic", "tiled" (one group per work item), "pair" (two groups per work
-// item) or "lane" tries that kernel first (and falls back to the generic
-// kernel where it does not apply).  Read at every call.
-enum class Path { kAuto, kGeneric, kTiled, kPair, kLane };
+// item), "lane" or "map" tries that kernel first (and falls back to the
+// generic kernel where it does not apply).  Read at every call.
+enum class Path { kAuto, kGeneric, kTiled, kPair, kLane, kMap };
 
 Path path_override() {
   const char *e = getenv("DCN_MI355X_FWD_PATH");
@@ -219,21 +219,35 @@ Path path_override() {
   if (!strcmp(e, "tiled")) return Path::kTiled;
   if (!strcmp(e, "pair")) return Path::kPair;
   if (!strcmp(e, "lane")) return Path::kLane;
+  if (!strcmp(e, "map")) return Path::kMap;
   return Path::kAuto;
 }
 
 }  // namespace
 
-// Kernel choice for 3x3 points that fit a tile window: fp32 runs the quad
-// tiled kernel (a quad of lanes per pixel-group; two groups per work item
-// where the group count is even), 16-bit I/O the
-// lane-per-pixel-group kernel, which needs a quarter of the address and
-// weight arithmetic and wins once a pixel's 16 channels are only 32 bytes.
-// Everything else runs the untiled kernel.
+// Kernel choice for 3x3 points: a map on which 16x16 output tiles would
+// leave more than a quarter of their pixel slots empty, and whose bordered
+// window (of one or more groups) fits in LDS, runs the whole-map kernel
+// (every lane busy, no halo re-reads, no global fix-ups).  Other maps that
+// fit a tile window: fp32 runs the quad tiled kernel (a quad of lanes per
+// pixel-group; two groups per work item where the group count is even),
+// 16-bit I/O the lane-per-pixel-group kernel, which needs a quarter of the
+// address and weight arithmetic and wins once a pixel's 16 channels are only
+// 32 bytes.  Everything else runs the untiled kernel.
+// Fraction of the pixel slots of 16x16 output tiles that fall on the map.
+static double tile_use(const FwdParams &p) {
+  const int64_t ty = (p.Ho + 15) / 16, tx = (p.Wo + 15) / 16;
+  return (double)p.Ho * p.Wo / (double)(ty * tx * 256);
+}
+
 hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
   const Path forced = path_override();
+  if (forced == Path::kMap || (forced == Path::kAuto && tile_use(p) < 0.75)) {
+    const hipError_t m = launch_forward_map(dtype, softmax, p, s);
+    if (m != hipErrorNotSupported) return m;
+  }
   const bool lane_first = forced == Path::kLane || (forced == Path::kAuto && dtype != DCN_F32);
-  if (forced != Path::kGeneric) {
+  if (forced != Path::kGeneric && forced != Path::kMap) {
     if (lane_first) {
       const hipError_t l = launch_forward_lane(dtype, softmax, p, s);
       if (l != hipErrorNotSupported) return l;

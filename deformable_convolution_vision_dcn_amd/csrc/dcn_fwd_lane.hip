@@ -251,6 +251,7 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
             acc[t][c] = fmaf(w10, f10[c], acc[t][c]);
             acc[t][c] = fmaf(w11, f11[c], acc[t][c]);
           }
+          pin_values(acc[t]);  // the chunk's FMAs happen here, not at the end
         }
         // Corners outside the window but touching the map: global gathers
         // (rare; the wave skips this when no lane needs it).

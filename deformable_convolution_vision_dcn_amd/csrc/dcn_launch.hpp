@@ -54,6 +54,7 @@ hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_
 hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipStream_t s,
                                 int groups_per_item);
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s);
+hipError_t launch_forward_map(int dtype, int softmax, const FwdParams &p, hipStream_t s);
 hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_tiled(int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_quad(int softmax, const BwdParams &p, hipStream_t s);

@@ -36,12 +36,12 @@
  * overwritten, never accumulated into, and must not alias any input.
  *
  * Kernel choice: the forward picks its kernel from the problem (dtype, point
- * count, stride, dilation, window size).  The environment variable
+ * count, stride, dilation, map and window size).  The environment variable
  * DCN_MI355X_FWD_PATH = "generic" | "tiled" (one group per work item) |
- * "pair" (two groups per work item) | "lane", read at every call, makes it
- * try that kernel first; DCN_MI355X_BWD_PATH = "generic" | "tiled" (half
- * windows) | "quad" does the same for the backward.  Results agree to
- * rounding either way.
+ * "pair" (two groups per work item) | "lane" | "map" (whole maps in LDS),
+ * read at every call, makes it try that kernel first; DCN_MI355X_BWD_PATH =
+ * "generic" | "tiled" (half windows) | "quad" does the same for the
+ * backward.  Results agree to rounding either way.
  *
  * Errors: every entry point returns DCN_OK (0) or a negative dcn_status.
  * Nothing is enqueued when a check fails.  N == 0 is valid and enqueues

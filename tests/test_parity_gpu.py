@@ -98,7 +98,7 @@ PATH_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["generic", "tiled", "pair", "lane"])
+@pytest.mark.parametrize("path", ["generic", "tiled", "pair", "lane", "map"])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("wl", PATH_CASES, ids=lambda w: w.name)
 def test_forward_each_kernel(wl, dtype, path, monkeypatch):
@@ -109,6 +109,30 @@ def test_forward_each_kernel(wl, dtype, path, monkeypatch):
     print(f"forward {wl.name} {dtype} path={path}", flush=True)
     t = synth.make_inputs(wl)
     gate(_np(run_forward(wl, t)), oracle_full(wl, t), dtype, f"{wl.name}/{dtype}/{path}")
+
+
+# Whole-map kernel: one group per item at the 24x24 stage-3 map (every lane
+# busy), four groups per item at 12x12 with a partial last group block (six
+# groups), strided and dilated sampling, a wide rectangle, far offsets.
+MAP_CASES = [
+    Workload("map_24x24", n=3, h=24, w=24, c=160, groups=10, offset_dist=uniform(3.0), seed=51),
+    Workload("map_12x12_g6", n=2, h=12, w=12, c=96, groups=6, offset_dist=normal(1.5), seed=52),
+    Workload("map_stride2_dil2", n=2, h=20, w=18, c=48, groups=3, stride=(2, 2), dilation=(2, 2),
+             pad=(2, 2), seed=53),
+    Workload("map_v4_rect", n=2, h=9, w=30, c=64, groups=4, softmax=False, mask_dist=normal(0.5),
+             seed=54),
+    Workload("map_far", n=1, h=14, w=16, c=32, groups=2, offset_dist=uniform(12.0), seed=55),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("wl", MAP_CASES, ids=lambda w: w.name)
+def test_forward_map_kernel(wl, dtype, monkeypatch):
+    monkeypatch.setenv("DCN_MI355X_FWD_PATH", "map")
+    wl = wl.replace(dtype=dtype)
+    print(f"forward {wl.name} {dtype} path=map", flush=True)
+    t = synth.make_inputs(wl)
+    gate(_np(run_forward(wl, t)), oracle_full(wl, t), dtype, f"{wl.name}/{dtype}/map")
 
 
 # --------------------------------------------------------------------------- forward, full size
