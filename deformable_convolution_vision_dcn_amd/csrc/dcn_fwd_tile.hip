@@ -47,7 +47,7 @@ namespace dcn {
 #define DCN_TILE_MAXSPAN 1024
 #endif
 #ifndef DCN_PAIR_MAXSPAN
-#define DCN_PAIR_MAXSPAN 1152
+#define DCN_PAIR_MAXSPAN 1280
 #endif
 
 // GP = groups per work item.  GP = 2 stages the two neighbouring groups of a
@@ -116,7 +116,7 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
 
   // Window slots at unit stride.  A lane stages the same window pixels of
   // every item: main slice u holds window rows [u RPS, u RPS + RPS) of
-  // columns [0, CW), the last slice the rows below and the columns right of
+  // columns [0, CW), the last slices the rows below and the columns right of
   // that block.  So the per-item address work is one uniform base plus one
   // column check per lane; rows outside the map fall out of the image's
   // buffer range (negative or past its last byte) and read zero.
@@ -124,22 +124,33 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   constexpr int RPS = WPIX / CW;
   constexpr int NM = USPAN / RPS;
   constexpr int REM_A = (USPAN - NM * RPS) * CW, REM_B = (USPAN - CW) * USPAN;
-  constexpr int WSL = UNIT ? NM + 1 : MAXPQ;  // register slices of a window
-  static_assert(!UNIT || (NM + 1 <= MAXPQ && REM_A + REM_B <= WPIX), "window slot mapping");
+  constexpr int NR = (REM_A + REM_B + WPIX - 1) / WPIX;  // remainder slices
+  constexpr int WSL = UNIT ? NM + NR : MAXPQ;            // register slices of a window
+  static_assert(!UNIT || (NR >= 1 && NM + NR <= MAXPQ), "window slot mapping");
   const uint32_t slot = threadIdx.x / LPP;
   const uint32_t m_col = slot % CW;
   const bool m_live = slot < (uint32_t)(RPS * CW);
-  uint32_t r_y = 0, r_x = 0;
-  if (slot < (uint32_t)REM_A) {
-    r_y = NM * RPS + slot / CW;
-    r_x = slot % CW;
-  } else if constexpr (USPAN > CW) {
-    r_y = (slot - REM_A) / (USPAN - CW);
-    r_x = CW + (slot - REM_A) % (USPAN - CW);
+  // remainder pixel rs = rho * WPIX + slot of remainder slice rho
+  uint32_t r_y[NR], r_x[NR];
+  bool r_live[NR];
+#pragma unroll
+  for (int rho = 0; rho < NR; ++rho) {
+    const uint32_t rs = (uint32_t)rho * WPIX + slot;
+    r_y[rho] = 0;
+    r_x[rho] = 0;
+    if (rs < (uint32_t)REM_A) {
+      r_y[rho] = NM * RPS + rs / CW;
+      r_x[rho] = rs % CW;
+    } else if constexpr (USPAN > CW) {
+      r_y[rho] = (rs - REM_A) / (USPAN - CW);
+      r_x[rho] = CW + (rs - REM_A) % (USPAN - CW);
+    }
+    r_live[rho] = rs < (uint32_t)(REM_A + REM_B);
   }
-  const bool r_live = slot < (uint32_t)(REM_A + REM_B);
   const uint32_t m_lane = (slot / CW) * row_bytes + m_col * pix_bytes + wlane * LANE_BYTES;
-  const uint32_t r_lane = r_y * row_bytes + r_x * pix_bytes + wlane * LANE_BYTES;
+  uint32_t r_lane[NR];
+#pragma unroll
+  for (int rho = 0; rho < NR; ++rho) r_lane[rho] = r_y[rho] * row_bytes + r_x[rho] * pix_bytes + wlane * LANE_BYTES;
   const uint32_t img_bytes = (uint32_t)p.H * row_bytes;
 
   // Window coordinates of the kernel point of each own slot before its
@@ -201,10 +212,14 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
       const __amdgpu_buffer_rsrc_t rimg = make_rsrc(static_cast<const unsigned char *>(p.input) + I.img, img_bytes);
       const uint32_t base = (uint32_t)I.Y0 * row_bytes + (uint32_t)I.X0 * pix_bytes + I.g * GBYTES;  // mod 2^32
       const uint32_t m_off = valid && m_live && (uint32_t)(I.X0 + (int)m_col) < (uint32_t)p.W ? base + m_lane : kOutOfRange;
-      const uint32_t r_off = valid && r_live && (uint32_t)(I.X0 + (int)r_x) < (uint32_t)p.W ? base + r_lane : kOutOfRange;
 #pragma unroll
       for (int u = 0; u < NM; ++u) buffer_load_words<NW>(rimg, m_off + (uint32_t)(u * RPS) * row_bytes, win[u]);
-      buffer_load_words<NW>(rimg, r_off, win[NM]);
+#pragma unroll
+      for (int rho = 0; rho < NR; ++rho) {
+        const uint32_t r_off = valid && r_live[rho] && (uint32_t)(I.X0 + (int)r_x[rho]) < (uint32_t)p.W
+                                   ? base + r_lane[rho] : kOutOfRange;
+        buffer_load_words<NW>(rimg, r_off, win[NM + rho]);
+      }
       return;
     }
 #pragma unroll
@@ -227,7 +242,9 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
 #pragma unroll
       for (int u = 0; u < NM; ++u)
         if (m_live) lds_store<NW>(tile + m_lds + u * RPS * row_lds, win[u]);
-      if (r_live) lds_store<NW>(tile + r_y * row_lds + r_x * PIXB + wlane * LANE_BYTES, win[NM]);
+#pragma unroll
+      for (int rho = 0; rho < NR; ++rho)
+        if (r_live[rho]) lds_store<NW>(tile + r_y[rho] * row_lds + r_x[rho] * PIXB + wlane * LANE_BYTES, win[NM + rho]);
       return;
     }
 #pragma unroll
@@ -380,9 +397,10 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
         const float W3 = wy1 * lx, W2 = wy1 - W3;
         const bool inside = !nan_loc && (uint32_t)ty <= (uint32_t)lim_y && (uint32_t)tx <= (uint32_t)lim_x;
         const uint32_t A = inside ? mad24((uint32_t)ty, (uint32_t)row_lds, mul24((uint32_t)tx, PIXB)) : (uint32_t)zero_base;
-        // outside the window but touching the map: needs the global fix-up
-        const bool fb = !inside && !nan_loc && (uint32_t)(cur.Y0 + 1 + ty) <= (uint32_t)p.H &&
-                        (uint32_t)(cur.X0 + 1 + tx) <= (uint32_t)p.W;
+        // outside the window: the global fix-up (whose buffer range check
+        // reads zeros for corners off the map, so a sample that misses the
+        // map entirely costs a rare gather instead of a test per round)
+        const bool fb = !inside && !nan_loc;
 
         // Main path, no branches: gather the round's corners from LDS.
         auto point = [&](auto o_tag) {
@@ -478,7 +496,7 @@ namespace {
 #define DCN_TILE_HALO 6
 #endif
 #ifndef DCN_PAIR_HALO
-#define DCN_PAIR_HALO 7
+#define DCN_PAIR_HALO 8
 #endif
 constexpr int kTileH = 16, kTileW = 16;
 // Halo and LDS budget per variant: one group per item runs two 512-thread
