@@ -68,13 +68,12 @@ def backward_bytes(wl) -> int:
 
 def forward_kernel_name(wl) -> str:
     """Kernel the library runs for this workload's forward (3x3 points,
-    stride and dilation 1): the whole-map kernel where 16x16 output tiles
-    would leave over a quarter of their slots empty (the small late-stage
-    maps), else the quad tiled kernel for fp32 and the lane-per-pixel-group
-    kernel for 16-bit I/O."""
+    stride and dilation 1): the whole-map kernel for output maps smaller than
+    a 16x16 tile or that tiles would leave over half empty (the 12x12 stage),
+    else the quad tiled kernel for fp32 and the lane-per-pixel-group kernel
+    for 16-bit I/O."""
     ho, wo = wl.out_hw
-    use = ho * wo / (((ho + 15) // 16) * ((wo + 15) // 16) * 256)
-    if use < 0.75:
+    if ho * wo < 256 or 2 * ho * wo < ((ho + 15) // 16) * ((wo + 15) // 16) * 256:
         return "dcn_fwd_map_kernel"
     return "dcn_fwd_tile_kernel" if wl.dtype == "f32" else "dcn_fwd_lane_kernel"
 

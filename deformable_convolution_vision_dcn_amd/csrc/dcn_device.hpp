@@ -246,4 +246,93 @@ __device__ __forceinline__ void load_mask(const void *base, uint32_t pg, float (
   }
 }
 
+// Offsets and mask values of one pixel-group of a 3x3 problem, kept as the
+// raw words the loads return (decoded where used, so that issuing the loads
+// does not wait for them).  fp32: 18 offset words (x, y per point) and 9
+// mask words.  16-bit: 9 offset words ((x, y) per point) and 5 words that
+// cover the 18-byte mask row.  Every load is a buffer load of at most 16
+// bytes at a 4-byte-aligned offset inside the tensor: the 16-bit mask row of
+// an odd pixel-group starts 2 bytes into a word, so its words are read from
+// 2 bytes before the row (the previous row's last value, ignored) to the row
+// end, and an even row's last value comes from a 2-byte load.
+template <int DT>
+struct RowWords {
+  static constexpr int kOff = DT == DCN_F32 ? 18 : 9;
+  static constexpr int kMask = DT == DCN_F32 ? 9 : 5;
+  uint32_t o[kOff], m[kMask];
+};
+
+template <int DT>
+__device__ __forceinline__ void load_row_words(__amdgpu_buffer_rsrc_t roff, __amdgpu_buffer_rsrc_t rmask,
+                                               uint32_t pg, RowWords<DT> &r) {
+  if constexpr (DT == DCN_F32) {
+    const uint32_t o = pg * 72u, m = pg * 36u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(o + 16 * q), 0, 0);
+      r.o[4 * q] = v[0];
+      r.o[4 * q + 1] = v[1];
+      r.o[4 * q + 2] = v[2];
+      r.o[4 * q + 3] = v[3];
+    }
+    const auto v8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(o + 64), 0, 0);
+    r.o[16] = v8[0];
+    r.o[17] = v8[1];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rmask, (int)(m + 16 * q), 0, 0);
+      r.m[4 * q] = v[0];
+      r.m[4 * q + 1] = v[1];
+      r.m[4 * q + 2] = v[2];
+      r.m[4 * q + 3] = v[3];
+    }
+    r.m[8] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(m + 32), 0, 0);
+  } else {
+    const uint32_t o = pg * 36u, m = pg * 18u, a = m & ~3u;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(o + 16 * q), 0, 0);
+      r.o[4 * q] = v[0];
+      r.o[4 * q + 1] = v[1];
+      r.o[4 * q + 2] = v[2];
+      r.o[4 * q + 3] = v[3];
+    }
+    r.o[8] = __builtin_amdgcn_raw_buffer_load_b32(roff, (int)(o + 32), 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rmask, (int)a, 0, 0);
+    r.m[0] = v[0];
+    r.m[1] = v[1];
+    r.m[2] = v[2];
+    r.m[3] = v[3];
+    const bool odd = (m & 2u) != 0;
+    const uint32_t w4a = __builtin_amdgcn_raw_buffer_load_b32(rmask, odd ? (int)(a + 16) : (int)kOutOfRange, 0, 0);
+    const uint32_t w4b = __builtin_amdgcn_raw_buffer_load_b16(rmask, odd ? (int)kOutOfRange : (int)(a + 16), 0, 0);
+    r.m[4] = w4a | w4b;
+  }
+}
+
+// The 18 offsets (x, y per point) and 9 mask values of load_row_words as fp32.
+template <int DT>
+__device__ __forceinline__ void decode_row_words(uint32_t pg, const RowWords<DT> &r, float (&off)[18],
+                                                 float (&msk)[9]) {
+  if constexpr (DT == DCN_F32) {
+#pragma unroll
+    for (int q = 0; q < 18; ++q) off[q] = __uint_as_float(r.o[q]);
+#pragma unroll
+    for (int q = 0; q < 9; ++q) msk[q] = __uint_as_float(r.m[q]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 9; ++q) {
+      off[2 * q] = Io<DT>::lo(r.o[q]);
+      off[2 * q + 1] = Io<DT>::hi(r.o[q]);
+    }
+    const uint32_t sh = (pg * 18u) & 2u ? 16u : 0u;  // odd pg: the row starts at a half word
+    uint32_t w[5];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_alignbit(r.m[q + 1], r.m[q], sh);
+    w[4] = r.m[4] >> sh;
+#pragma unroll
+    for (int q = 0; q < 9; ++q) msk[q] = (q & 1) ? Io<DT>::hi(w[q / 2]) : Io<DT>::lo(w[q / 2]);
+  }
+}
+
 }  // namespace dcn

@@ -225,24 +225,28 @@ Path path_override() {
 
 }  // namespace
 
-// Kernel choice for 3x3 points: a map on which 16x16 output tiles would
-// leave more than a quarter of their pixel slots empty, and whose bordered
-// window (of one or more groups) fits in LDS, runs the whole-map kernel
-// (every lane busy, no halo re-reads, no global fix-ups).  Other maps that
+// Kernel choice for 3x3 points: an output map smaller than one 16x16 tile
+// (or one that tiles would leave over half empty) whose bordered window, of
+// one or more groups, fits in LDS runs the whole-map kernel (every lane
+// busy, several groups per item, no halo re-reads, no global fix-ups).  Other maps that
 // fit a tile window: fp32 runs the quad tiled kernel (a quad of lanes per
 // pixel-group; two groups per work item where the group count is even),
 // 16-bit I/O the lane-per-pixel-group kernel, which needs a quarter of the
 // address and weight arithmetic and wins once a pixel's 16 channels are only
 // 32 bytes.  Everything else runs the untiled kernel.
-// Fraction of the pixel slots of 16x16 output tiles that fall on the map.
-static double tile_use(const FwdParams &p) {
+// Whether the whole-map kernel is the first choice: the output map is
+// smaller than one 16x16 tile, or tiles would leave over half of their
+// pixel slots empty.  (At 24x24, 56 % full, the tiled lane kernel is still
+// faster: with one group per item the whole-map kernel's rows are scattered.)
+static bool prefer_map(const FwdParams &p) {
   const int64_t ty = (p.Ho + 15) / 16, tx = (p.Wo + 15) / 16;
-  return (double)p.Ho * p.Wo / (double)(ty * tx * 256);
+  const int64_t area = (int64_t)p.Ho * p.Wo;
+  return area < 256 || 2 * area < ty * tx * 256;
 }
 
 hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
   const Path forced = path_override();
-  if (forced == Path::kMap || (forced == Path::kAuto && tile_use(p) < 0.75)) {
+  if (forced == Path::kMap || (forced == Path::kAuto && prefer_map(p))) {
     const hipError_t m = launch_forward_map(dtype, softmax, p, s);
     if (m != hipErrorNotSupported) return m;
   }

@@ -75,9 +75,6 @@ __global__ void __launch_bounds__(kMapThreads, map_waves<DT>()) dcn_fwd_map_kern
   constexpr int CPC = CHUNK / io::kBytes;  // channels per chunk: 4 or 8
   constexpr int GB = CG * io::kBytes;      // bytes of one group of one pixel
   constexpr int K = 9;
-  // raw row words: offsets (x, y) of the 9 points, then the 9 mask values
-  constexpr int NOW = DT == DCN_F32 ? 18 : 9;
-  constexpr int NMW = DT == DCN_F32 ? 9 : 5;
 
   extern __shared__ __align__(16) unsigned char lds[];
 
@@ -123,67 +120,7 @@ __global__ void __launch_bounds__(kMapThreads, map_waves<DT>()) dcn_fwd_map_kern
     return r;
   };
 
-  // Raw offset and mask words of a pixel-group (decoded where used).  The
-  // 16-bit mask row (18 bytes) starts 2 bytes into a word for odd pg: read
-  // the aligned words that cover it without leaving [row start - 2, row end).
-  auto load_rows = [&](uint32_t pg, uint32_t (&ow)[NOW], uint32_t (&mw)[NMW]) {
-    if constexpr (DT == DCN_F32) {
-      const uint32_t o = pg * 72u, m = pg * 36u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(o + 16 * q), 0, 0);
-        ow[4 * q] = v[0]; ow[4 * q + 1] = v[1]; ow[4 * q + 2] = v[2]; ow[4 * q + 3] = v[3];
-      }
-      const auto v8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(o + 64), 0, 0);
-      ow[16] = v8[0]; ow[17] = v8[1];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rmask, (int)(m + 16 * q), 0, 0);
-        mw[4 * q] = v[0]; mw[4 * q + 1] = v[1]; mw[4 * q + 2] = v[2]; mw[4 * q + 3] = v[3];
-      }
-      mw[8] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(m + 32), 0, 0);
-    } else {
-      const uint32_t o = pg * 36u, m = pg * 18u, a = m & ~3u;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(o + 16 * q), 0, 0);
-        ow[4 * q] = v[0]; ow[4 * q + 1] = v[1]; ow[4 * q + 2] = v[2]; ow[4 * q + 3] = v[3];
-      }
-      ow[8] = __builtin_amdgcn_raw_buffer_load_b32(roff, (int)(o + 32), 0, 0);
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rmask, (int)a, 0, 0);
-      mw[0] = v[0]; mw[1] = v[1]; mw[2] = v[2]; mw[3] = v[3];
-      const bool odd = (m & 2u) != 0;
-      // odd: one whole word ends the row; even: only its low half belongs to it
-      const uint32_t w4a = __builtin_amdgcn_raw_buffer_load_b32(rmask, odd ? (int)(a + 16) : (int)kOutOfRange, 0, 0);
-      const uint32_t w4b = __builtin_amdgcn_raw_buffer_load_b16(rmask, odd ? (int)kOutOfRange : (int)(a + 16), 0, 0);
-      mw[4] = w4a | w4b;
-    }
-  };
-  // Offsets (x, y) and mask values as fp32.
-  auto decode_rows = [&](uint32_t pg, const uint32_t (&ow)[NOW], const uint32_t (&mw)[NMW],
-                         float (&off)[18], float (&msk)[K]) {
-    if constexpr (DT == DCN_F32) {
-#pragma unroll
-      for (int q = 0; q < 18; ++q) off[q] = __uint_as_float(ow[q]);
-#pragma unroll
-      for (int q = 0; q < K; ++q) msk[q] = __uint_as_float(mw[q]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 9; ++q) {
-        off[2 * q] = io::lo(ow[q]);
-        off[2 * q + 1] = io::hi(ow[q]);
-      }
-      const uint32_t sh = (pg * 18u) & 2u ? 16u : 0u;  // odd pg: the row starts at a half word
-      uint32_t w[5];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_alignbit(mw[q + 1], mw[q], sh);
-      w[4] = mw[4] >> sh;
-#pragma unroll
-      for (int q = 0; q < K; ++q) msk[q] = (q & 1) ? io::hi(w[q / 2]) : io::lo(w[q / 2]);
-    }
-  };
-
-  uint32_t ow[2][NOW], mw[2][NMW];
+  RowWords<DT> rw[2];
 
   // One work item per block: nothing is carried from item to item, and the
   // hardware then starts each block as soon as a slot frees up, so the last
@@ -210,18 +147,18 @@ __global__ void __launch_bounds__(kMapThreads, map_waves<DT>()) dcn_fwd_map_kern
     }
     {
       const Pg q0 = pixel_group(n, g0, 0);
-      load_rows(q0.pg, ow[0], mw[0]);
+      load_row_words<DT>(roff, rmask, q0.pg, rw[0]);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's window loads have landed
     __syncthreads();                     // the windows are in LDS
 
     // One pass: decode this pass's rows from (cw, cm), request the next
     // pass's into (nw, nm), then the nine samples of every lane's pixel-group.
-    auto pass = [&](int q, uint32_t (&cw)[NOW], uint32_t (&cm)[NMW], uint32_t (&nw)[NOW], uint32_t (&nm)[NMW]) {
+    auto pass = [&](int q, const RowWords<DT> &cr, RowWords<DT> &nr) {
       const Pg cur = pixel_group(n, g0, q);
       float off[18], msk[K];
-      decode_rows(cur.pg, cw, cm, off, msk);
-      if (q + 1 < mg.passes) load_rows(pixel_group(n, g0, q + 1).pg, nw, nm);
+      decode_row_words<DT>(cur.pg, cr, off, msk);
+      if (q + 1 < mg.passes) load_row_words<DT>(roff, rmask, pixel_group(n, g0, q + 1).pg, nr);
       float m[K];
       if constexpr (SOFTMAX) {
         float mx = msk[0];
@@ -334,11 +271,8 @@ __global__ void __launch_bounds__(kMapThreads, map_waves<DT>()) dcn_fwd_map_kern
     };
 #pragma unroll 1
     for (int q = 0; q < mg.passes; ++q) {
-      pass(q, ow[0], mw[0], ow[1], mw[1]);
-#pragma unroll
-      for (int i = 0; i < NOW; ++i) ow[0][i] = ow[1][i];
-#pragma unroll
-      for (int i = 0; i < NMW; ++i) mw[0][i] = mw[1][i];
+      pass(q, rw[0], rw[1]);
+      rw[0] = rw[1];
     }
   }
 }
