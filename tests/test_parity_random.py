@@ -1,0 +1,77 @@
+"""Seeded random problems against the oracle.
+
+Each seed draws one problem -- batch, map size (1 to 40 on a side), groups,
+kernel size, stride, dilation, pad, offset scale, offset spread (from nearly
+integer-free small offsets to ones that leave any window), DCNv3 or DCNv4,
+dtype -- and runs the forward on every kernel in turn (forced through
+DCN_MI355X_FWD_PATH; a kernel that does not apply falls back to the generic
+one) and, for fp32, the backward on every backward kernel.  The bar is the
+same as the fixed cases: max-abs 1e-4 in fp32, |d| <= 2e-2 |ref| + 1e-3 for
+16-bit outputs.
+"""
+import numpy as np
+import pytest
+
+from deformable_convolution_vision_dcn_amd import synth
+from deformable_convolution_vision_dcn_amd.synth import Workload, normal, uniform
+from test_parity_gpu import _np, gate, oracle_backward, oracle_full, run_backward, run_forward
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = range(36)
+FWD_PATHS = ["auto", "generic", "tiled", "pair", "lane", "map"]
+BWD_PATHS = ["auto", "generic", "tiled", "quad"]
+
+
+def random_problem(seed: int) -> Workload:
+    r = np.random.default_rng(7000 + seed)
+    dtype = ("f32", "f16", "bf16")[seed % 3]
+    kernel = [(3, 3)] * 6 + [(1, 1), (3, 5), (5, 5)]
+    kh, kw = kernel[int(r.integers(0, len(kernel)))]
+    stride = (int(r.choice([1, 1, 1, 2])), int(r.choice([1, 1, 1, 2])))
+    dil = (int(r.choice([1, 1, 2])), int(r.choice([1, 1, 2])))
+    pad = (int(r.integers(0, 3)), int(r.integers(0, 3)))
+    h, w = int(r.integers(1, 41)), int(r.integers(1, 41))
+    # grow the map until the output has at least one pixel
+    h = max(h, dil[0] * (kh - 1) + 1 - 2 * pad[0])
+    w = max(w, dil[1] * (kw - 1) + 1 - 2 * pad[1])
+    groups = int(r.integers(1, 5))
+    spread = float(r.choice([0.3, 1.5, 4.0, 10.0]))
+    offset_dist = normal(spread) if r.integers(0, 2) else uniform(spread)
+    softmax = bool(r.integers(0, 2))
+    return Workload(f"rand{seed}", n=int(r.integers(1, 4)), h=h, w=w, c=16 * groups, groups=groups,
+                    dtype=dtype, softmax=softmax, kernel=(kh, kw), stride=stride, pad=pad,
+                    dilation=dil, offset_scale=float(r.choice([0.5, 1.0, 2.0])),
+                    offset_dist=offset_dist, mask_dist=normal(1.0 if softmax else 0.5), seed=seed)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_forward_every_kernel(seed, monkeypatch):
+    wl = random_problem(seed)
+    t = synth.make_inputs(wl)
+    ref = oracle_full(wl, t)
+    for path in FWD_PATHS:
+        if path == "auto":
+            monkeypatch.delenv("DCN_MI355X_FWD_PATH", raising=False)
+        else:
+            monkeypatch.setenv("DCN_MI355X_FWD_PATH", path)
+        print(f"forward {wl} path={path}", flush=True)
+        gate(_np(run_forward(wl, t)), ref, wl.dtype, f"{wl.name}/{wl.dtype}/{path}")
+
+
+@pytest.mark.parametrize("seed", [s for s in SEEDS if s % 3 == 0])  # the fp32 draws
+def test_random_backward_every_kernel(seed, monkeypatch):
+    wl = random_problem(seed)
+    assert wl.dtype == "f32"
+    t = synth.make_inputs(wl, with_grad=True)
+    rx, roff, rm = oracle_backward(wl, t)
+    for path in BWD_PATHS:
+        if path == "auto":
+            monkeypatch.delenv("DCN_MI355X_BWD_PATH", raising=False)
+        else:
+            monkeypatch.setenv("DCN_MI355X_BWD_PATH", path)
+        print(f"backward {wl} path={path}", flush=True)
+        gx, goff, gm = run_backward(wl, t)
+        gate(_np(gx), rx, "f32", f"{wl.name}/{path} grad_input")
+        gate(_np(goff), roff, "f32", f"{wl.name}/{path} grad_offset")
+        gate(_np(gm), rm, "f32", f"{wl.name}/{path} grad_mask")
