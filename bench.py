@@ -57,13 +57,15 @@ def forward_bytes(wl) -> int:
 
 def backward_bytes(wl) -> int:
     """Algorithmic bytes of one backward call: input, offsets, mask, grad_out
-    read; grad_input, grad_offset, grad_mask written (the grad_input clear is
-    counted separately)."""
+    read; grad_input, grad_offset, grad_mask written, all in the I/O dtype
+    (the grad_input clear, and for 16-bit I/O the fp32 accumulator, are the
+    implementation's own traffic and not counted)."""
     ho, wo = wl.out_hw
     pg = wl.n * ho * wo * wl.groups
     cg = wl.c // wl.groups
     in_elems = wl.n * wl.h * wl.w * wl.c
-    return (2 * in_elems + pg * (cg + 6 * wl.points)) * 4
+    eb = 4 if wl.dtype == "f32" else 2
+    return (2 * in_elems + pg * (cg + 6 * wl.points)) * eb
 
 
 def forward_kernel_name(wl) -> str:
@@ -312,18 +314,21 @@ def main() -> int:
             "note": "cold = 512 MB cache flush before each launch; median of per-launch HIP events"},
     }
 
-    if not args.no_backward and wl.dtype == "f32":
+    if not args.no_backward:
         print("bench: backward", file=sys.stderr, flush=True)
         gx = torch.empty_like(x)
         goff = torch.empty_like(off)
         gmk = torch.empty_like(m)
+        ws_bytes = dcn.backward_workspace_bytes(x, **kw)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
+        bkw = dict(grad_input=gx, grad_offset=goff, grad_mask=gmk, workspace=ws, **kw)
         nb = max(1, min(args.steps, 20))
         for _ in range(2):
-            dcn.dcn_backward(x, off, m, gy, grad_input=gx, grad_offset=goff, grad_mask=gmk, **kw)
+            dcn.dcn_backward(x, off, m, gy, **bkw)
         torch.cuda.synchronize()
         ev0.record(stream)
         for _ in range(nb):
-            dcn.dcn_backward(x, off, m, gy, grad_input=gx, grad_offset=goff, grad_mask=gmk, **kw)
+            dcn.dcn_backward(x, off, m, gy, **bkw)
         ev1.record(stream)
         torch.cuda.synchronize()
         bms = ev0.elapsed_time(ev1) / nb
@@ -332,7 +337,8 @@ def main() -> int:
                               "GSamples_per_s": round(wl.samples / (bms * 1e-3) / 1e9, 3),
                               "alg_GB_per_s": round(bbytes / (bms * 1e-3) / 1e9, 1),
                               "alg_bytes_per_call": bbytes,
-                              "note": "includes the grad_input clear"}
+                              "note": ("includes the grad_input clear" if wl.dtype == "f32" else
+                                       "includes the fp32 accumulator's clear and rounding")}
 
     if not args.no_cpu_baseline:
         images = min(wl.n, args.cpu_images or wl.n)

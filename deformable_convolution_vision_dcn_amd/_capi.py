@@ -13,7 +13,7 @@ import pathlib
 LIB_PATH = pathlib.Path(os.environ.get(
     "DCN_MI355X_LIB", pathlib.Path(__file__).resolve().parent / "libdcn_mi355x.so"))
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
 
@@ -27,6 +27,7 @@ STATUS = {
     -6: "DCN_ERR_HIP",
     -7: "DCN_ERR_ABI",
     -8: "DCN_ERR_ARG",
+    -9: "DCN_ERR_WORKSPACE",
 }
 CODES = {v: k for k, v in STATUS.items()}
 
@@ -87,7 +88,9 @@ def lib() -> ctypes.CDLL:
         L.dcn_forward.restype = ctypes.c_int
         L.dcn_forward.argtypes = [P, vp, vp, vp, vp, vp]
         L.dcn_backward.restype = ctypes.c_int
-        L.dcn_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.dcn_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+        L.dcn_backward_workspace_size.restype = ctypes.c_int
+        L.dcn_backward_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_uint64)]
         L.dcn_status_string.restype = ctypes.c_char_p
         L.dcn_status_string.argtypes = [ctypes.c_int]
         if L.dcn_abi_version() != ABI_VERSION:
@@ -116,10 +119,18 @@ def dcn_forward(p: dcn_problem, input_ptr, offset_ptr, mask_ptr, output_ptr, str
     return lib().dcn_forward(ctypes.byref(p), input_ptr, offset_ptr, mask_ptr, output_ptr, stream)
 
 
+def dcn_backward_workspace_size(p: dcn_problem):
+    """Returns (status, bytes)."""
+    n = ctypes.c_uint64(0)
+    st = lib().dcn_backward_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
 def dcn_backward(p: dcn_problem, input_ptr, offset_ptr, mask_ptr, grad_out_ptr, grad_in_ptr,
-                 grad_offset_ptr, grad_mask_ptr, stream) -> int:
+                 grad_offset_ptr, grad_mask_ptr, workspace_ptr, workspace_bytes, stream) -> int:
     return lib().dcn_backward(ctypes.byref(p), input_ptr, offset_ptr, mask_ptr, grad_out_ptr,
-                              grad_in_ptr, grad_offset_ptr, grad_mask_ptr, stream)
+                              grad_in_ptr, grad_offset_ptr, grad_mask_ptr, workspace_ptr,
+                              workspace_bytes, stream)
 
 
 def raise_on(status: int) -> None:

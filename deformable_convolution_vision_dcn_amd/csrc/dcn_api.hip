@@ -98,6 +98,38 @@ int64_t images_per_chunk(const dcn_problem *p, int64_t ho, int64_t wo) {
   return per < 1 ? 1 : per;
 }
 
+// The backward's extra checks: 16-bit I/O only for 3x3 points at stride and
+// dilation 1, and one image's fp32 grad_input accumulator below 2^31 bytes.
+int validate_backward(const dcn_problem *p, int64_t *ho, int64_t *wo) {
+  const int st = validate(p, ho, wo);
+  if (st != DCN_OK) return st;
+  if (p->dtype == DCN_F32) return DCN_OK;
+  const bool quad_shape = p->kernel_h == 3 && p->kernel_w == 3 && p->stride_h == 1 && p->stride_w == 1 &&
+                          p->dilation_h == 1 && p->dilation_w == 1;
+  if (!quad_shape) return DCN_ERR_UNSUPPORTED;
+  if ((int64_t)p->h * p->w * p->c * 4 > kMaxBytes31) return DCN_ERR_TOO_LARGE;
+  return DCN_OK;
+}
+
+// Images per backward launch: as for the forward, and for 16-bit I/O also
+// the fp32 accumulator of the chunk's grad_input below 2^31 bytes.
+int64_t images_per_chunk_bwd(const dcn_problem *p, int64_t ho, int64_t wo) {
+  int64_t per = images_per_chunk(p, ho, wo);
+  if (p->dtype != DCN_F32) {
+    const int64_t per32 = kMaxBytes31 / ((int64_t)p->h * p->w * p->c * 4);
+    if (per32 < per) per = per32;
+  }
+  return per < 1 ? 1 : per;
+}
+
+// fp32 accumulator bytes of the largest chunk (0 for fp32 I/O or N == 0).
+uint64_t workspace_bytes_bwd(const dcn_problem *p, int64_t ho, int64_t wo) {
+  if (p->dtype == DCN_F32 || p->n == 0) return 0;
+  int64_t per = images_per_chunk_bwd(p, ho, wo);
+  if (p->n < per) per = p->n;
+  return (uint64_t)(per * p->h * p->w * p->c * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,47 +172,76 @@ int dcn_forward(const dcn_problem *p, const void *input, const void *offset, con
   return DCN_OK;
 }
 
+int dcn_backward_workspace_size(const dcn_problem *p, uint64_t *bytes) {
+  int64_t ho = 0, wo = 0;
+  const int st = validate_backward(p, &ho, &wo);
+  if (st != DCN_OK) return st;
+  if (!bytes) return DCN_ERR_NULL;
+  *bytes = workspace_bytes_bwd(p, ho, wo);
+  return DCN_OK;
+}
+
 int dcn_backward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
                  const void *grad_output, void *grad_input, void *grad_offset, void *grad_mask,
-                 void *hip_stream) {
+                 void *workspace, uint64_t workspace_bytes, void *hip_stream) {
   int64_t ho = 0, wo = 0;
-  const int st = validate(p, &ho, &wo);
+  const int st = validate_backward(p, &ho, &wo);
   if (st != DCN_OK) return st;
-  if (p->dtype != DCN_F32) return DCN_ERR_UNSUPPORTED;
   if (p->n == 0) return DCN_OK;
-  if (!input || !offset || !mask || !grad_output || !grad_input || !grad_offset || !grad_mask)
+  const bool wide = p->dtype == DCN_F32;  // grad_input accumulates in place
+  if (!input || !offset || !mask || !grad_output || !grad_input || !grad_offset || !grad_mask ||
+      (!wide && !workspace))
     return DCN_ERR_NULL;
   if (!aligned16(input) || !aligned16(offset) || !aligned16(mask) || !aligned16(grad_output) ||
-      !aligned16(grad_input) || !aligned16(grad_offset) || !aligned16(grad_mask))
+      !aligned16(grad_input) || !aligned16(grad_offset) || !aligned16(grad_mask) ||
+      (!wide && !aligned16(workspace)))
     return DCN_ERR_ALIGN;
+  if (!wide && workspace_bytes < workspace_bytes_bwd(p, ho, wo)) return DCN_ERR_WORKSPACE;
 
   const int64_t K = (int64_t)p->kernel_h * p->kernel_w;
-  const int64_t img_in = (int64_t)p->h * p->w * p->c * 4;
+  const int64_t eb = elem_bytes(p->dtype);
+  const int64_t img_elems = (int64_t)p->h * p->w * p->c;
+  const int64_t img_in = img_elems * eb;
   const int64_t img_pg = ho * wo * p->groups;
-  const int64_t per = images_per_chunk(p, ho, wo);
+  const int64_t per = images_per_chunk_bwd(p, ho, wo);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
 
-  hipError_t e = dcn::launch_zero(grad_input, (uint64_t)(p->n * img_in), stream);
-  if (e != hipSuccess) return hip_fail(e);
+  hipError_t e = hipSuccess;
+  if (wide) {
+    e = dcn::launch_zero(grad_input, (uint64_t)(p->n * img_in), stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   dcn::BwdParams b{};
   b.f = geometry(p, ho, wo);
   for (int64_t n0 = 0; n0 < p->n; n0 += per) {
     const int64_t nc = (p->n - n0 < per) ? p->n - n0 : per;
     b.f.input = static_cast<const char *>(input) + n0 * img_in;
-    b.f.offset = static_cast<const float *>(offset) + n0 * img_pg * K * 2;
-    b.f.mask = static_cast<const float *>(mask) + n0 * img_pg * K;
+    b.f.offset = static_cast<const char *>(offset) + n0 * img_pg * K * 2 * eb;
+    b.f.mask = static_cast<const char *>(mask) + n0 * img_pg * K * eb;
     b.f.output = nullptr;
     b.f.in_bytes = (uint32_t)(nc * img_in);
-    b.f.off_bytes = (uint32_t)(nc * img_pg * K * 2 * 4);
-    b.f.mask_bytes = (uint32_t)(nc * img_pg * K * 4);
+    b.f.off_bytes = (uint32_t)(nc * img_pg * K * 2 * eb);
+    b.f.mask_bytes = (uint32_t)(nc * img_pg * K * eb);
     b.f.out_bytes = 0;
     b.f.pg_total = (uint32_t)(nc * img_pg);
-    b.grad_out = static_cast<const float *>(grad_output) + n0 * img_pg * dcn::kGroupChannels;
-    b.grad_in = static_cast<char *>(grad_input) + n0 * img_in;
-    b.grad_offset = static_cast<float *>(grad_offset) + n0 * img_pg * K * 2;
-    b.grad_mask = static_cast<float *>(grad_mask) + n0 * img_pg * K;
-    e = dcn::launch_backward(p->softmax, b, stream);
+    b.grad_out = static_cast<const char *>(grad_output) + n0 * img_pg * dcn::kGroupChannels * eb;
+    b.grad_offset = static_cast<char *>(grad_offset) + n0 * img_pg * K * 2 * eb;
+    b.grad_mask = static_cast<char *>(grad_mask) + n0 * img_pg * K * eb;
+    if (wide) {
+      b.grad_in = static_cast<char *>(grad_input) + n0 * img_in;
+    } else {  // each chunk reuses the workspace: zero it, accumulate, round out
+      b.grad_in = workspace;
+      e = dcn::launch_zero(workspace, (uint64_t)(nc * img_elems * 4), stream);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    e = dcn::launch_backward(p->dtype, p->softmax, b, stream);
+    if (e == hipErrorNotSupported && !wide) return DCN_ERR_UNSUPPORTED;
     if (e != hipSuccess) return hip_fail(e);
+    if (!wide) {
+      e = dcn::launch_narrow(p->dtype, workspace, static_cast<char *>(grad_input) + n0 * img_in,
+                             (uint64_t)(nc * img_elems), stream);
+      if (e != hipSuccess) return hip_fail(e);
+    }
   }
   return DCN_OK;
 }
@@ -196,6 +257,7 @@ const char *dcn_status_string(int status) {
     case DCN_ERR_HIP: return g_hip_message;
     case DCN_ERR_ABI: return "dcn_problem.struct_size does not match this library";
     case DCN_ERR_ARG: return "invalid argument value (softmax flag or offset_scale)";
+    case DCN_ERR_WORKSPACE: return "workspace smaller than dcn_backward_workspace_size reports";
     default: return "unknown status";
   }
 }

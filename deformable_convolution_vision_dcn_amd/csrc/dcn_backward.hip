@@ -1,5 +1,6 @@
 // dcn_backward.hip -- gfx950 backward kernel of the DCNv3/DCNv4 sampling core
-// (fp32), plus the fill kernel that clears grad_input before the scatter.
+// (fp32), plus the fill kernel that clears grad_input before the scatter and
+// the kernel that rounds an fp32 grad_input into a 16-bit one.
 //
 // Derivatives of the forward (wmrh.cn/news/61976, section 二 steps 2-4):
 //   out_c = sum_k m_k * B_k[c],  B_k[c] = sum over the 4 corners of
@@ -198,6 +199,17 @@ __global__ void __launch_bounds__(kBlock) dcn_zero_kernel(uint4 *dst, uint64_t n
     dst[i] = make_uint4(0, 0, 0, 0);
 }
 
+// dst[i] = round-to-nearest-even(src[i]) for 8 elements per lane and step.
+template <int DT>
+__global__ void __launch_bounds__(kBlock) dcn_narrow_kernel(const float4 *src, uint4 *dst, uint64_t n8) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const float4 a = src[2 * i], b = src[2 * i + 1];
+    dst[i] = make_uint4(Io<DT>::pack(a.x, a.y), Io<DT>::pack(a.z, a.w), Io<DT>::pack(b.x, b.y),
+                        Io<DT>::pack(b.z, b.w));
+  }
+}
+
 namespace {
 
 template <int KH, int KW, bool SM>
@@ -215,12 +227,14 @@ hipError_t launch_one(const BwdParams &p, hipStream_t s) {
 // Backward path override for tests and measurements: DCN_MI355X_BWD_PATH =
 // "generic" (untiled kernel), "tiled" (the half-window tiled kernel) or
 // "quad" (the lane-quad tiled kernel, also the default where it applies).
-hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s) {
+// 16-bit I/O has the quad kernel only (hipErrorNotSupported elsewhere).
+hipError_t launch_backward(int dtype, int softmax, const BwdParams &p, hipStream_t s) {
+  if (dtype != DCN_F32) return launch_backward_quad(dtype, softmax, p, s);
   const char *e = getenv("DCN_MI355X_BWD_PATH");
   const bool generic = e && !strcmp(e, "generic");
   const bool halves = e && !strcmp(e, "tiled");
   if (!generic && !halves) {
-    const hipError_t q = launch_backward_quad(softmax, p, s);
+    const hipError_t q = launch_backward_quad(DCN_F32, softmax, p, s);
     if (q != hipErrorNotSupported) return q;
   }
   if (!generic) {
@@ -239,6 +253,21 @@ hipError_t launch_zero(void *dst, uint64_t bytes, hipStream_t s) {
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(dcn_zero_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, s,
                      static_cast<uint4 *>(dst), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_narrow(int dtype, const void *src, void *dst, uint64_t count, hipStream_t s) {
+  const uint64_t n8 = count / 8;
+  if (n8 == 0) return hipSuccess;
+  uint64_t blocks = (n8 + kBlock - 1) / kBlock;
+  if (blocks > 8192) blocks = 8192;
+  const float4 *in = static_cast<const float4 *>(src);
+  uint4 *out = static_cast<uint4 *>(dst);
+  switch (dtype) {
+    case DCN_F16: hipLaunchKernelGGL(dcn_narrow_kernel<DCN_F16>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, in, out, n8); break;
+    case DCN_BF16: hipLaunchKernelGGL(dcn_narrow_kernel<DCN_BF16>, dim3((uint32_t)blocks), dim3(kBlock), 0, s, in, out, n8); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -73,9 +73,17 @@ __device__ __forceinline__ int2 pair_sums(uint64_t v) {
 
 }  // namespace
 
-template <bool SOFTMAX>
+template <int DT, bool SOFTMAX>
 __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams bp, TileGeom tg) {
   const FwdParams &p = bp.f;
+  using io = Io<DT>;
+  constexpr int EB = io::kBytes;         // bytes per element in memory
+  constexpr int LB = 4 * EB;             // a lane's 4 channels in memory
+  constexpr int NWL = LB / 4;            // words of them: 4 (fp32) or 2 (16-bit)
+  // grad_input is accumulated in fp32 for every I/O dtype (for 16-bit I/O in
+  // a caller's fp32 workspace of the input's shape): an input byte address
+  // times GX is the same element's address there.
+  constexpr uint32_t GX = 4 / EB;
   constexpr int TS = kBqTile, R = kBqHalo, SPAN_W = kBqSpan;
   constexpr int SPAN = SPAN_W * SPAN_W;
   constexpr int PIXB = kBqPixB, ROW = kBqRow, LIM = SPAN_W - 2;
@@ -94,13 +102,13 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
 
   const uint32_t quad = threadIdx.x >> 2, sub = threadIdx.x & 3;
   const int oy = (int)quad / TS, ox = (int)quad % TS;  // output pixel within the tile
-  const uint32_t pix_bytes = (uint32_t)p.C * 4u;
+  const uint32_t pix_bytes = (uint32_t)p.C * EB;
   const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
-  const __amdgpu_buffer_rsrc_t rgx = make_rsrc(bp.grad_in, p.in_bytes);
+  const __amdgpu_buffer_rsrc_t rgx = make_rsrc(bp.grad_in, p.in_bytes * GX);
   const __amdgpu_buffer_rsrc_t roff = make_rsrc(p.offset, p.off_bytes);
   const __amdgpu_buffer_rsrc_t rmask = make_rsrc(p.mask, p.mask_bytes);
-  const __amdgpu_buffer_rsrc_t rgy = make_rsrc(bp.grad_out, p.pg_total * (uint32_t)(CG * 4));
+  const __amdgpu_buffer_rsrc_t rgy = make_rsrc(bp.grad_out, p.pg_total * (uint32_t)(CG * EB));
   const __amdgpu_buffer_rsrc_t rgoff = make_rsrc(bp.grad_offset, p.off_bytes);
   const __amdgpu_buffer_rsrc_t rgm = make_rsrc(bp.grad_mask, p.mask_bytes);
   const float s = p.scale;
@@ -142,7 +150,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
     I.Y0 = r0 - p.PH - R;  // window origin in input coordinates
     I.X0 = c0 - p.PW - R;
     I.img = I.n * (uint32_t)p.H * row_bytes;
-    I.chan = I.g * (uint32_t)(CG * 4) + sub * 16u;
+    I.chan = I.g * (uint32_t)(CG * EB) + sub * (uint32_t)LB;
     const int ho = r0 + oy, wo = c0 + ox;
     I.live = ho < p.Ho && wo < p.Wo;
     I.pg = I.live ? (((I.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + I.g : 0u;
@@ -153,7 +161,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
   // rows and grad_output: requested into registers while the current item
   // computes, on every path (a missing item loads nothing: its offsets are
   // out of range), so the compiler's count of outstanding loads stays exact.
-  uint32_t win[SLOTS][4];
+  uint32_t win[SLOTS][NWL];
   auto issue_window = [&](const Item &I, bool valid) {
     // The slot geometry is recomputed per item from an opaque copy of the
     // quad index: hoisted out of the item loop it would not fit the
@@ -170,7 +178,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
         if ((uint32_t)gy_ < (uint32_t)p.H && (uint32_t)gx_ < (uint32_t)p.W)
           offb = I.img + (uint32_t)gy_ * row_bytes + (uint32_t)gx_ * pix_bytes + I.chan;
       }
-      buffer_load_words<4>(rin, offb, win[u]);
+      buffer_load_words<NWL>(rin, offb, win[u]);
     }
   };
   auto store_window = [&]() {
@@ -179,32 +187,46 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
 #pragma unroll
     for (int u = 0; u < SLOTS; ++u) {
       const int idx = (int)qd + u * WPIX;
-      if (idx < SPAN)
-        *reinterpret_cast<uint4 *>(lds + idx * PIXB + sub * 16u) = make_uint4(win[u][0], win[u][1], win[u][2], win[u][3]);
+      if (idx < SPAN) {  // staged as fp32 whatever the I/O dtype
+        float v[4];
+        unpack<DT, NWL>(win[u], v);
+        *reinterpret_cast<uint4 *>(lds + idx * PIXB + sub * 16u) =
+            make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+      }
     }
   };
-  // Raw rows as loaded: rw = x, y of k = 2 sub; x, y of 2 sub + 1; x, y of 8;
-  // rl = logits of 2 sub, 2 sub + 1, 8; rg = grad_output of the lane's 4 channels.
-  uint32_t rw[6], rl[3], rg[4];
+  // Raw rows as loaded (decoded where used).  fp32: rw = x, y of k = 2 sub;
+  // x, y of 2 sub + 1; x, y of 8; rl = logits of 2 sub, 2 sub + 1, 8; rg =
+  // grad_output of the lane's 4 channels.  16-bit: rw = (x, y) words of
+  // 2 sub, 2 sub + 1, 8; rl = the three logits (low halves); rg = two words.
+  constexpr int NRW = DT == DCN_F32 ? 6 : 3;
+  uint32_t rw[NRW], rl[3], rg[NWL];
   auto issue_rows = [&](const Item &I) {
-    const uint32_t orow = I.pg * (K * 8), mrow = I.pg * (K * 4);
-    const auto o = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(orow + 16 * sub), 0, 0);
-    const auto o8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 64), 0, 0);
-    const auto lg = __builtin_amdgcn_raw_buffer_load_b64(rmask, (int)(mrow + 8 * sub), 0, 0);
-    rl[2] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 32), 0, 0);
-    const auto gv = __builtin_amdgcn_raw_buffer_load_b128(rgy, (int)(I.pg * (CG * 4) + 16 * sub), 0, 0);
-    rw[0] = o[0];
-    rw[1] = o[1];
-    rw[2] = o[2];
-    rw[3] = o[3];
-    rw[4] = o8[0];
-    rw[5] = o8[1];
-    rl[0] = lg[0];
-    rl[1] = lg[1];
-    rg[0] = gv[0];
-    rg[1] = gv[1];
-    rg[2] = gv[2];
-    rg[3] = gv[3];
+    if constexpr (DT == DCN_F32) {
+      const uint32_t orow = I.pg * (K * 8), mrow = I.pg * (K * 4);
+      const auto o = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(orow + 16 * sub), 0, 0);
+      const auto o8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 64), 0, 0);
+      const auto lg = __builtin_amdgcn_raw_buffer_load_b64(rmask, (int)(mrow + 8 * sub), 0, 0);
+      rl[2] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 32), 0, 0);
+      rw[0] = o[0];
+      rw[1] = o[1];
+      rw[2] = o[2];
+      rw[3] = o[3];
+      rw[4] = o8[0];
+      rw[5] = o8[1];
+      rl[0] = lg[0];
+      rl[1] = lg[1];
+    } else {
+      const uint32_t orow = I.pg * (K * 4), mrow = I.pg * (K * 2);
+      const auto o = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 8 * sub), 0, 0);
+      rw[2] = __builtin_amdgcn_raw_buffer_load_b32(roff, (int)(orow + 32), 0, 0);
+      rw[0] = o[0];
+      rw[1] = o[1];
+      rl[0] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub), 0, 0);
+      rl[1] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub + 2), 0, 0);
+      rl[2] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 16), 0, 0);
+    }
+    buffer_load_words<NWL>(rgy, I.pg * (uint32_t)(CG * EB) + sub * (uint32_t)LB, rg);
   };
 
   const XcdWalk walk = xcd_walk(blockIdx.x, gridDim.x, tg.items);
@@ -225,11 +247,16 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
     // logits for DCNv3, the raw mask for DCNv4) and grad_output.
     float2 offs[3];
     float m[3], gy[4];
+    float lgs[3];
 #pragma unroll
-    for (int r = 0; r < 3; ++r) offs[r] = make_float2(__uint_as_float(rw[2 * r]), __uint_as_float(rw[2 * r + 1]));
-    float lgs[3] = {__uint_as_float(rl[0]), __uint_as_float(rl[1]), __uint_as_float(rl[2])};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) gy[c] = __uint_as_float(rg[c]);
+    for (int r = 0; r < 3; ++r) {
+      if constexpr (DT == DCN_F32)
+        offs[r] = make_float2(__uint_as_float(rw[2 * r]), __uint_as_float(rw[2 * r + 1]));
+      else
+        offs[r] = make_float2(io::lo(rw[r]), io::hi(rw[r]));
+      lgs[r] = io::lo(rl[r]);
+    }
+    unpack<DT, NWL>(rg, gy);
     if (sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 only
     if constexpr (SOFTMAX) {
       const float mx = quad_max(fmaxf(fmaxf(lgs[0], lgs[1]), lgs[2]));
@@ -358,17 +385,22 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
           if (qbcast<O>((int)fb)) {
             uint32_t ga[4];
             corners(ga);
-            const uint32_t g00 = ga[0], g01 = ga[1], g10 = ga[2], g11 = ga[3];
-            buffer_load_words<4>(rin, g00, q00);
-            buffer_load_words<4>(rin, g01, q01);
-            buffer_load_words<4>(rin, g10, q10);
-            buffer_load_words<4>(rin, g11, q11);
+            uint32_t r00[NWL], r01[NWL], r10[NWL], r11[NWL];
+            buffer_load_words<NWL>(rin, ga[0], r00);
+            buffer_load_words<NWL>(rin, ga[1], r01);
+            buffer_load_words<NWL>(rin, ga[2], r10);
+            buffer_load_words<NWL>(rin, ga[3], r11);
+            float v00[4], v01[4], v10[4], v11[4];
+            unpack<DT, NWL>(r00, v00);
+            unpack<DT, NWL>(r01, v01);
+            unpack<DT, NWL>(r10, v10);
+            unpack<DT, NWL>(r11, v11);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              P[0] = fmaf(gy[c], __uint_as_float(q00[c]), P[0]);
-              P[1] = fmaf(gy[c], __uint_as_float(q01[c]), P[1]);
-              P[2] = fmaf(gy[c], __uint_as_float(q10[c]), P[2]);
-              P[3] = fmaf(gy[c], __uint_as_float(q11[c]), P[3]);
+              P[0] = fmaf(gy[c], v00[c], P[0]);
+              P[1] = fmaf(gy[c], v01[c], P[1]);
+              P[2] = fmaf(gy[c], v10[c], P[2]);
+              P[3] = fmaf(gy[c], v11[c], P[3]);
             }
           }
         }
@@ -401,17 +433,13 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
           if (qbcast<O>((int)gscat)) {
             uint32_t ga[4];
             corners(ga);
-            const uint32_t g00 = ga[0], g01 = ga[1], g10 = ga[2], g11 = ga[3];
-            const float w00 = qbcast<O>(W0), w01 = qbcast<O>(W1);
-            const float w10 = qbcast<O>(W2), w11 = qbcast<O>(W3);
+            const float wc[4] = {qbcast<O>(W0), qbcast<O>(W1), qbcast<O>(W2), qbcast<O>(W3)};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const uint32_t cb = 4u * c;
-              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w00 * gy[c], rgx, (int)(g00 == kOutOfRange ? kOutOfRange : g00 + cb), 0, 0);
-              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w01 * gy[c], rgx, (int)(g01 == kOutOfRange ? kOutOfRange : g01 + cb), 0, 0);
-              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w10 * gy[c], rgx, (int)(g10 == kOutOfRange ? kOutOfRange : g10 + cb), 0, 0);
-              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w11 * gy[c], rgx, (int)(g11 == kOutOfRange ? kOutOfRange : g11 + cb), 0, 0);
-            }
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                    wc[q] * gy[c], rgx, (int)(ga[q] == kOutOfRange ? kOutOfRange : ga[q] * GX + 4u * c), 0, 0);
           }
         }
       };
@@ -448,21 +476,42 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
 #pragma unroll
         for (int r = 0; r < 3; ++r) gm[r] = m[r] * (gm[r] - dot);
       }
-      typedef float f4 __attribute__((ext_vector_type(4)));
-      typedef float f2 __attribute__((ext_vector_type(2)));
-      const uint32_t orow = cur.pg * (K * 8), mrow = cur.pg * (K * 4);
-      __builtin_amdgcn_raw_buffer_store_b128(
-          __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(4))),
-                            f4{s * m[0] * rs[0].y, s * m[0] * rs[0].z, s * m[1] * rs[1].y, s * m[1] * rs[1].z}),
-          rgoff, (int)(orow + 16 * sub), 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b64(
-          __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), f2{gm[0], gm[1]}), rgm,
-          (int)(mrow + 8 * sub), 0, 0);
-      if (sub == 0) {
+      // offset gradients (x, y) of the three slots
+      float go[3][2];
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        go[r][0] = s * m[r] * rs[r].y;
+        go[r][1] = s * m[r] * rs[r].z;
+      }
+      if constexpr (DT == DCN_F32) {
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const uint32_t orow = cur.pg * (K * 8), mrow = cur.pg * (K * 4);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(4))), f4{go[0][0], go[0][1], go[1][0], go[1][1]}),
+            rgoff, (int)(orow + 16 * sub), 0, 0);
         __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), f2{s * m[2] * rs[2].y, s * m[2] * rs[2].z}),
-            rgoff, (int)(orow + 64), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gm[2]), rgm, (int)(mrow + 32), 0, 0);
+            __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), f2{gm[0], gm[1]}), rgm,
+            (int)(mrow + 8 * sub), 0, 0);
+        if (sub == 0) {
+          __builtin_amdgcn_raw_buffer_store_b64(
+              __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), f2{go[2][0], go[2][1]}), rgoff,
+              (int)(orow + 64), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gm[2]), rgm, (int)(mrow + 32), 0, 0);
+        }
+      } else {  // rounded to the I/O dtype; the 18-byte mask rows take 2-byte stores
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        const uint32_t orow = cur.pg * (K * 4), mrow = cur.pg * (K * 2);
+        __builtin_amdgcn_raw_buffer_store_b64(u2{io::pack(go[0][0], go[0][1]), io::pack(go[1][0], go[1][1])}, rgoff,
+                                              (int)(orow + 8 * sub), 0, 0);
+        const uint32_t gmw = io::pack(gm[0], gm[1]);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(gmw & 0xffffu), rgm, (int)(mrow + 4 * sub), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(gmw >> 16), rgm, (int)(mrow + 4 * sub + 2), 0, 0);
+        if (sub == 0) {
+          __builtin_amdgcn_raw_buffer_store_b32(io::pack(go[2][0], go[2][1]), rgoff, (int)(orow + 32), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(io::pack(gm[2], 0.f) & 0xffffu), rgm,
+                                                (int)(mrow + 16), 0, 0);
+        }
       }
     }
 
@@ -480,7 +529,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
       int idx = (int)(threadIdx.x >> 4);
       int sy = idx / SPAN_W, sx = idx - sy * SPAN_W;
       uint32_t dst = cur.img + (uint32_t)(cur.Y0 + sy) * row_bytes + (uint32_t)(cur.X0 + sx) * pix_bytes +
-                     cur.g * (uint32_t)(CG * 4) + ch * 4u;
+                     cur.g * (uint32_t)(CG * EB) + ch * (uint32_t)EB;
       const uint32_t slot0 = lbase + GWIN + (ch >> 1) * 8u;
       typedef __attribute__((address_space(3))) uint64_t L;
 #pragma unroll 2
@@ -490,7 +539,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
         const int2 pr = pair_sums(*slot);
         if ((ch & 1u) == 0) *slot = 0;  // after both lanes of the pair have read it (same instruction)
         const int q = (ch & 1u) ? pr.y : pr.x;
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32((float)q * invS, rgx, (int)((ok && q != 0) ? dst : kOutOfRange), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32((float)q * invS, rgx, (int)((ok && q != 0) ? dst * GX : kOutOfRange), 0, 0);
         sx += DX;
         sy += DY;
         dst += (uint32_t)DY * row_bytes + (uint32_t)DX * pix_bytes;
@@ -509,9 +558,9 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
 
 namespace {
 
-template <bool SM>
+template <int DT, bool SM>
 hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_bwd_quad_kernel<SM>;
+  auto kern = dcn_bwd_quad_kernel<DT, SM>;
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBqLds);
@@ -532,7 +581,7 @@ hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s
 }  // namespace
 
 // 3x3 points, stride 1, dilation 1 only; hipErrorNotSupported otherwise.
-hipError_t launch_backward_quad(int softmax, const BwdParams &b, hipStream_t s) {
+hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipStream_t s) {
   const FwdParams &p = b.f;
   if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
     return hipErrorNotSupported;
@@ -549,7 +598,12 @@ hipError_t launch_backward_quad(int softmax, const BwdParams &b, hipStream_t s) 
   tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
-  return softmax ? launch_bwd_quad<true>(b, tg, s) : launch_bwd_quad<false>(b, tg, s);
+  switch (dtype) {
+    case DCN_F32: return softmax ? launch_bwd_quad<DCN_F32, true>(b, tg, s) : launch_bwd_quad<DCN_F32, false>(b, tg, s);
+    case DCN_F16: return softmax ? launch_bwd_quad<DCN_F16, true>(b, tg, s) : launch_bwd_quad<DCN_F16, false>(b, tg, s);
+    case DCN_BF16: return softmax ? launch_bwd_quad<DCN_BF16, true>(b, tg, s) : launch_bwd_quad<DCN_BF16, false>(b, tg, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace dcn

@@ -34,8 +34,8 @@ struct FwdParams {
 
 struct BwdParams {
   FwdParams f;             // input, offset, mask and geometry as in the forward
-  const void *grad_out;    // (chunk, Ho, Wo, C)
-  void *grad_in;           // (chunk, H, W, C), zeroed before the launch
+  const void *grad_out;    // (chunk, Ho, Wo, C), the I/O dtype like every tensor
+  void *grad_in;           // (chunk, H, W, C), fp32 for every I/O dtype, zeroed before the launch
   void *grad_offset;       // (chunk, Ho, Wo, G, K, 2)
   void *grad_mask;         // (chunk, Ho, Wo, G, K)
 };
@@ -55,9 +55,11 @@ hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipS
                                 int groups_per_item);
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s);
 hipError_t launch_forward_map(int dtype, int softmax, const FwdParams &p, hipStream_t s);
-hipError_t launch_backward(int softmax, const BwdParams &p, hipStream_t s);
+hipError_t launch_backward(int dtype, int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_tiled(int softmax, const BwdParams &p, hipStream_t s);
-hipError_t launch_backward_quad(int softmax, const BwdParams &p, hipStream_t s);
+hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_zero(void *dst, uint64_t bytes, hipStream_t s);
+// dst (16-bit dtype, count elements) = src (fp32) rounded; count % 8 == 0.
+hipError_t launch_narrow(int dtype, const void *src, void *dst, uint64_t count, hipStream_t s);
 
 }  // namespace dcn

@@ -120,8 +120,13 @@ def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
                  offset_scale: float = 2.0, softmax: bool = True,
                  grad_input: Optional[torch.Tensor] = None,
                  grad_offset: Optional[torch.Tensor] = None,
-                 grad_mask: Optional[torch.Tensor] = None):
-    """Backward of the DCN core; returns (grad_input, grad_offset, grad_mask)."""
+                 grad_mask: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
+    """Backward of the DCN core; returns (grad_input, grad_offset, grad_mask).
+
+    16-bit I/O accumulates grad_input in an fp32 device workspace
+    (``backward_workspace_bytes``); pass a ``workspace`` tensor on x's device
+    to reuse one, else a fresh one is taken from torch's allocator."""
     p, shp = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax)
     _expect(x, "input", x.shape, x.dtype, x.device)
     _expect(offset, "offset", shp["offset"], x.dtype, x.device)
@@ -140,12 +145,33 @@ def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
     _no_alias(outs, [("input", x), ("offset", offset), ("mask", mask), ("grad_out", grad_out)])
     for k, (a, ta) in enumerate(outs):
         _no_alias([(a, ta)], outs[k + 1:])
+    st, ws_bytes = _capi.dcn_backward_workspace_size(p)
+    _capi.raise_on(st)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    ws_ptr, ws_have = None, 0
+    if workspace is not None:
+        if workspace.device != x.device or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {x.device}")
+        _no_alias([("workspace", workspace)], outs + [("input", x), ("offset", offset), ("mask", mask),
+                                                       ("grad_out", grad_out)])
+        ws_ptr, ws_have = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with torch.cuda.device(x.device):
         st = _capi.dcn_backward(p, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
                                 grad_out.data_ptr(), grad_input.data_ptr(),
-                                grad_offset.data_ptr(), grad_mask.data_ptr(), _stream(x.device))
+                                grad_offset.data_ptr(), grad_mask.data_ptr(), ws_ptr, ws_have,
+                                _stream(x.device))
     _capi.raise_on(st)
     return grad_input, grad_offset, grad_mask
+
+
+def backward_workspace_bytes(x: torch.Tensor, *, groups: int, kernel=3, stride=1, pad=1, dilation=1,
+                             offset_scale: float = 2.0, softmax: bool = True) -> int:
+    """Device workspace bytes that dcn_backward needs for this problem (0 for fp32)."""
+    p, _ = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax)
+    st, n = _capi.dcn_backward_workspace_size(p)
+    _capi.raise_on(st)
+    return n
 
 
 class DCNCore(torch.autograd.Function):
@@ -168,6 +194,6 @@ class DCNCore(torch.autograd.Function):
 
 def dcn_core(x, offset, mask, *, groups, kernel=3, stride=1, pad=1, dilation=1,
              offset_scale=2.0, softmax=True):
-    """Differentiable DCN core (fp32 backward)."""
+    """Differentiable DCN core (backward in the HIP library: fp32, or 16-bit at 3x3, stride and dilation 1)."""
     return DCNCore.apply(x, offset, mask, groups, kernel, stride, pad, dilation, offset_scale,
                          softmax)

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DCN_ABI_VERSION 1
+#define DCN_ABI_VERSION 2
 
 /* Element type of every tensor of one call. */
 typedef enum dcn_dtype {
@@ -71,13 +71,17 @@ typedef enum dcn_status {
     DCN_ERR_SHAPE = -2,       /* a dim <= 0 (N may be 0), C % groups != 0, kernel,
                                  stride or dilation < 1, pad < 0, or Ho/Wo < 1         */
     DCN_ERR_UNSUPPORTED = -3, /* dtype, channels-per-group or point count without a
-                                 kernel, or a 16-bit backward                          */
+                                 kernel, or a 16-bit backward other than 3x3 points
+                                 at stride and dilation 1                              */
     DCN_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                */
     DCN_ERR_TOO_LARGE = -5,   /* one image's input, output or offset tensor exceeds
-                                 2^31-1 bytes, or H or W exceeds 2^24                  */
+                                 2^31-1 bytes, or H or W exceeds 2^24 (16-bit
+                                 backward: also H*W*C*4 bytes, its fp32 accumulator)   */
     DCN_ERR_HIP = -6,         /* the HIP runtime refused a launch; see dcn_status_string */
     DCN_ERR_ABI = -7,         /* problem->struct_size != sizeof(dcn_problem)            */
-    DCN_ERR_ARG = -8          /* softmax not 0/1, or offset_scale not finite            */
+    DCN_ERR_ARG = -8,         /* softmax not 0/1, or offset_scale not finite            */
+    DCN_ERR_WORKSPACE = -9    /* dcn_backward's workspace_bytes below what
+                                 dcn_backward_workspace_size reports                   */
 } dcn_status;
 
 /* One problem description.  Set struct_size = sizeof(dcn_problem). */
@@ -107,21 +111,37 @@ int dcn_check(const dcn_problem *p, int64_t *ho, int64_t *wo);
 int dcn_forward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
                 void *output, void *hip_stream);
 
+/* Bytes of device workspace that dcn_backward needs for this problem: 0 for
+ * fp32 (and for N == 0); for 16-bit I/O, one fp32 grad_input accumulator of
+ * the largest chunk of images (N*H*W*C*4 bytes unless the batch is split).
+ * Runs the backward's checks (the errors dcn_backward would return before
+ * touching a pointer); bytes must not be NULL. */
+int dcn_backward_workspace_size(const dcn_problem *p, uint64_t *bytes);
+
 /* Backward of the forward above for the gradient grad_output of output:
- *   grad_input  = adjoint bilinear scatter of m_k * weight * grad_output
- *                 (zeroed by the call itself, then accumulated with fp32
- *                 atomics, so its low bits can vary from run to run),
+ *   grad_input  = adjoint bilinear scatter of m_k * weight * grad_output,
  *   grad_offset = offset_scale * m_k * sum_c grad_output_c * d(bilinear)/d(px, py),
  *                 stored (x, y) like the offsets,
  *   grad_mask   = gradient with respect to the mask tensor as passed: through
  *                 the softmax Jacobian when softmax != 0.
  * At integer sampling coordinates the derivative is the one-sided one from the
- * right (the floor convention).  fp32 only (DCN_F32); other dtypes return
- * DCN_ERR_UNSUPPORTED.  Enqueues a fill kernel for grad_input and one
- * backward launch per chunk of images. */
+ * right (the floor convention).  fp32 for every shape.  16-bit I/O (all
+ * tensors of the call in that dtype) for 3x3 points at stride and dilation 1,
+ * else DCN_ERR_UNSUPPORTED.  The arithmetic is fp32 throughout and grad_input
+ * is accumulated in fp32: sums per output tile in fixed point, added with
+ * fp32 atomics (so its low bits can vary from run to run).  For fp32 the sums
+ * land in grad_input itself (the call zeroes it first) and workspace may be
+ * NULL.  For 16-bit I/O they land in `workspace`, a caller-owned device
+ * buffer of at least dcn_backward_workspace_size bytes, 16-byte aligned, whose
+ * contents on entry do not matter and are garbage on return; each chunk of
+ * images zeroes it, accumulates into it and is then rounded once to
+ * nearest-even into grad_input, like grad_offset and grad_mask.  Calls that
+ * share a workspace must be ordered on one stream.
+ * Enqueues per chunk of images a fill kernel, one backward launch and, for
+ * 16-bit I/O, one rounding kernel (fp32: one fill for the whole batch). */
 int dcn_backward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
                  const void *grad_output, void *grad_input, void *grad_offset, void *grad_mask,
-                 void *hip_stream);
+                 void *workspace, uint64_t workspace_bytes, void *hip_stream);
 
 /* Static description of a status code.  For DCN_ERR_HIP the string carries
  * the HIP runtime's message from the calling thread's most recent failure. */

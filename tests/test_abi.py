@@ -29,8 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["dcn_abi_version", "dcn_backward", "dcn_check",
-                                    "dcn_forward", "dcn_status_string"]
+    assert declared_functions() == ["dcn_abi_version", "dcn_backward", "dcn_backward_workspace_size",
+                                    "dcn_check", "dcn_forward", "dcn_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -140,14 +140,46 @@ def test_argument_checks_before_any_device_call(lib):
     assert F(p, a, a, a, None, None) == _capi.CODES["DCN_ERR_NULL"]
     assert F(p, a + 4, a, a, a, None) == _capi.CODES["DCN_ERR_ALIGN"]
     assert F(p, a, a, a, a + 8, None) == _capi.CODES["DCN_ERR_ALIGN"]
-    assert B(p, a, a, a, a, a, a, None, None) == _capi.CODES["DCN_ERR_NULL"]
-    assert B(p, a, a, a, a, a, a + 2, a, None) == _capi.CODES["DCN_ERR_ALIGN"]
+    assert B(p, a, a, a, a, a, a, None, None, 0, None) == _capi.CODES["DCN_ERR_NULL"]
+    assert B(p, a, a, a, a, a, a + 2, a, None, 0, None) == _capi.CODES["DCN_ERR_ALIGN"]
+    # 16-bit backward: 3x3 points at stride and dilation 1 only
+    for change in ({"stride_h": 2}, {"dilation_w": 2, "pad_w": 2},
+                   {"kernel_h": 5, "kernel_w": 5, "pad_h": 2, "pad_w": 2}):
+        for dt in (_capi.DCN_BF16, _capi.DCN_F16):
+            p16 = _capi.make_problem(**{**BASE, **change, "dtype": dt})
+            assert B(p16, a, a, a, a, a, a, a, a, 1 << 30, None) == _capi.CODES["DCN_ERR_UNSUPPORTED"], change
+            assert _capi.dcn_backward_workspace_size(p16)[0] == _capi.CODES["DCN_ERR_UNSUPPORTED"]
     p16 = _capi.make_problem(**{**BASE, "dtype": _capi.DCN_BF16})
-    assert B(p16, a, a, a, a, a, a, a, None) == _capi.CODES["DCN_ERR_UNSUPPORTED"]
+    st, need = _capi.dcn_backward_workspace_size(p16)
+    assert st == 0 and need == BASE["n"] * BASE["h"] * BASE["w"] * BASE["c"] * 4
+    assert B(p16, a, a, a, a, a, a, None, a, need, None) == _capi.CODES["DCN_ERR_NULL"]
+    assert B(p16, a, a, a, a, a, a, a, None, need, None) == _capi.CODES["DCN_ERR_NULL"]
+    assert B(p16, a, a, a, a, a, a, a, a + 8, need, None) == _capi.CODES["DCN_ERR_ALIGN"]
+    assert B(p16, a, a, a, a, a, a, a, a, need - 16, None) == _capi.CODES["DCN_ERR_WORKSPACE"]
+    assert lib.dcn_backward_workspace_size(ctypes.byref(p16), None) == _capi.CODES["DCN_ERR_NULL"]
+    # fp32 needs no workspace
+    assert _capi.dcn_backward_workspace_size(p) == (0, 0)
     # N = 0: valid, nothing enqueued, pointers may be NULL
     p0 = _capi.make_problem(**{**BASE, "n": 0})
     assert F(p0, None, None, None, None, None) == 0
-    assert B(p0, None, None, None, None, None, None, None, None) == 0
+    assert B(p0, None, None, None, None, None, None, None, None, 0, None) == 0
+    p0h = _capi.make_problem(**{**BASE, "n": 0, "dtype": _capi.DCN_F16})
+    assert _capi.dcn_backward_workspace_size(p0h) == (0, 0)
+    assert B(p0h, None, None, None, None, None, None, None, None, 0, None) == 0
     # an invalid problem is reported before the pointers are looked at
     pbad = _capi.make_problem(**{**BASE, "groups": 3})
     assert F(pbad, None, None, None, None, None) == _capi.CODES["DCN_ERR_SHAPE"]
+
+
+def test_backward_workspace_sizes(lib):
+    """The 16-bit backward's fp32 accumulator: one image must stay below 2^31
+    bytes, and the workspace covers the largest chunk of images."""
+    big = dict(BASE, h=4096, w=4096, c=48, groups=3, dtype=_capi.DCN_BF16, n=1)
+    assert _capi.dcn_check(_capi.make_problem(**big))[0] == 0  # the 16-bit tensors fit
+    assert _capi.dcn_backward_workspace_size(_capi.make_problem(**big))[0] == _capi.CODES["DCN_ERR_TOO_LARGE"]
+    assert _capi.dcn_backward_workspace_size(_capi.make_problem(**dict(big, dtype=_capi.DCN_F32)))[0] == \
+        _capi.CODES["DCN_ERR_TOO_LARGE"]  # fp32 input itself too large
+    # 2048x1024x64: 512 MiB of fp32 per image, so chunks of 3 images
+    chunked = dict(BASE, h=2048, w=1024, c=64, groups=4, dtype=_capi.DCN_F16, n=5)
+    assert _capi.dcn_backward_workspace_size(_capi.make_problem(**chunked)) == (0, 3 * 2048 * 1024 * 64 * 4)
+    assert _capi.dcn_backward_workspace_size(_capi.make_problem(**dict(chunked, n=2))) == (0, 2 * 2048 * 1024 * 64 * 4)

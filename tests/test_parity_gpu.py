@@ -254,6 +254,31 @@ def test_backward_each_kernel(wl, path, monkeypatch):
     gate(_np(gm), rm, "f32", f"{wl.name}/{path} grad_mask")
 
 
+BWD16 = [
+    Workload("bwd16_k3", n=2, h=13, w=11, c=48, groups=3, offset_dist=normal(2.0), seed=61),
+    Workload("bwd16_v4", n=2, h=12, w=10, c=32, groups=2, softmax=False, mask_dist=normal(0.5), seed=62),
+    Workload("bwd16_ragged_far", n=2, h=37, w=29, c=48, groups=3, offset_dist=uniform(5.0), seed=63),
+    Workload("bwd16_pad0", n=1, h=19, w=18, c=16, groups=1, pad=(0, 0), offset_dist=normal(3.0), seed=64),
+    Workload("bwd16_one_pixel", n=1, h=1, w=1, c=16, groups=1, seed=65),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("wl", BWD16, ids=lambda w: w.name)
+def test_backward_16bit(wl, dtype):
+    """16-bit backward (3x3, stride and dilation 1) against the oracle on the
+    same 16-bit inputs, with the 16-bit gate on all three gradients."""
+    wl = wl.replace(dtype=dtype)
+    print(f"backward {wl.name} {dtype}", flush=True)
+    t = synth.make_inputs(wl, with_grad=True)
+    gx, goff, gm = run_backward(wl, t)
+    assert gx.dtype == t["x"].dtype and goff.dtype == gx.dtype and gm.dtype == gx.dtype
+    rx, roff, rm = oracle_backward(wl, t)
+    gate(_np(gx), rx, dtype, f"{wl.name}/{dtype} grad_input")
+    gate(_np(goff), roff, dtype, f"{wl.name}/{dtype} grad_offset")
+    gate(_np(gm), rm, dtype, f"{wl.name}/{dtype} grad_mask")
+
+
 def test_backward_adjoint_at_stage1_size():
     """At the stage-1 size (too big for a quick full oracle backward) the
     grad_input is checked by the adjoint identity <F(x), g> = <x, F^T g>,
@@ -280,6 +305,56 @@ def test_backward_adjoint_at_stage1_size():
         gate(_np(gx[sl]), rx, "f32", f"stage1 grad_input image {n}")
         gate(_np(goff[sl]), roff, "f32", f"stage1 grad_offset image {n}")
         gate(_np(gm[sl]), rm, "f32", f"stage1 grad_mask image {n}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_backward_16bit_at_stage1_size(dtype):
+    """16-bit backward at the stage-1 size: grad_input by the adjoint identity
+    and all three gradients of the first and last image against the oracle.
+    The adjoint sides differ by the 16-bit rounding of y and grad_input (at
+    most half an ulp, 2^-9 relative for bf16, of each) plus fp32 sums, so the
+    bound is 2^-8 of the sum of both sides' absolute terms."""
+    wl = synth.WORKLOADS["stage1_dcnv3_f32"].replace(backward=True, dtype=dtype)
+    print(f"backward stage1 {dtype} (adjoint)", flush=True)
+    t = synth.make_inputs(wl, with_grad=True)
+    y = run_forward(wl, t)
+    gx, goff, gm = run_backward(wl, t)
+    x, gy = t["x"].to(DEV).double(), t["grad_out"].to(DEV).double()
+    lhs_t = y.double() * gy
+    rhs_t = x * gx.double()
+    bound = 2.0 ** -8 * float(lhs_t.abs().sum() + rhs_t.abs().sum())
+    assert abs(float(lhs_t.sum()) - float(rhs_t.sum())) <= bound
+    for n in (0, wl.n - 1):
+        sl = slice(n, n + 1)
+        sub = {k: v[sl] for k, v in t.items()}
+        rx, roff, rm = oracle_backward(wl.replace(n=1), sub)
+        gate(_np(gx[sl]), rx, dtype, f"stage1/{dtype} grad_input image {n}")
+        gate(_np(goff[sl]), roff, dtype, f"stage1/{dtype} grad_offset image {n}")
+        gate(_np(gm[sl]), rm, dtype, f"stage1/{dtype} grad_mask image {n}")
+
+
+def test_backward_16bit_reuses_a_workspace():
+    """Two 16-bit backward calls in a row through one caller workspace (left
+    dirty by the first) give the results of calls with fresh workspaces."""
+    wl = BWD16[2].replace(dtype="bf16")
+    t = synth.make_inputs(wl, with_grad=True)
+    x, off, m, gy = (t[k].to(DEV) for k in ("x", "offset", "mask", "grad_out"))
+    need = dcn.backward_workspace_bytes(x, **wl.op_kwargs())
+    assert need == x.numel() * 4
+    ws = torch.full((need + 64,), 0x7f, dtype=torch.uint8, device=DEV)
+    ref = [_np(g) for g in dcn.dcn_backward(x, off, m, gy, **wl.op_kwargs())]
+    small = wl.replace(n=1)
+    ref1 = [_np(g) for g in dcn.dcn_backward(x[:1], off[:1], m[:1], gy[:1], **small.op_kwargs())]
+    for _ in range(2):
+        got = [_np(g) for g in dcn.dcn_backward(x, off, m, gy, workspace=ws, **wl.op_kwargs())]
+        got1 = [_np(g) for g in dcn.dcn_backward(x[:1], off[:1], m[:1], gy[:1], workspace=ws,
+                                                  **small.op_kwargs())]
+        torch.cuda.synchronize()
+        for a, b in zip(got + got1, ref + ref1):
+            # fp32 atomics make grad_input's rounding order vary: 1 ulp of bf16 at most
+            np.testing.assert_allclose(a, b, rtol=2.0 ** -7, atol=1e-6)
+    with pytest.raises(dcn.DCNError, match="WORKSPACE"):
+        dcn.dcn_backward(x, off, m, gy, workspace=ws[: need - 16], **wl.op_kwargs())
 
 
 def test_autograd_function_matches_backward():

@@ -7,7 +7,8 @@ dtype -- and runs the forward on every kernel in turn (forced through
 DCN_MI355X_FWD_PATH; a kernel that does not apply falls back to the generic
 one) and, for fp32, the backward on every backward kernel.  The bar is the
 same as the fixed cases: max-abs 1e-4 in fp32, |d| <= 2e-2 |ref| + 1e-3 for
-16-bit outputs.
+16-bit outputs.  A second series of draws, held to 3x3 points at stride and
+dilation 1, runs the 16-bit backward.
 """
 import numpy as np
 import pytest
@@ -75,3 +76,26 @@ def test_random_backward_every_kernel(seed, monkeypatch):
         gate(_np(gx), rx, "f32", f"{wl.name}/{path} grad_input")
         gate(_np(goff), roff, "f32", f"{wl.name}/{path} grad_offset")
         gate(_np(gm), rm, "f32", f"{wl.name}/{path} grad_mask")
+
+
+
+def random_problem_16(seed: int) -> Workload:
+    """A draw of random_problem with the shape the 16-bit backward covers:
+    3x3 points at stride and dilation 1, f16 or bf16."""
+    wl = random_problem(100 + seed)
+    return wl.replace(name=f"rand16_{seed}", dtype=("f16", "bf16")[seed % 2], kernel=(3, 3),
+                      stride=(1, 1), dilation=(1, 1), h=max(wl.h, 3 - 2 * wl.pad[0]),
+                      w=max(wl.w, 3 - 2 * wl.pad[1]))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_backward_16bit(seed):
+    """16-bit backward on random 3x3, stride-1 problems, on the 16-bit gate."""
+    wl = random_problem_16(seed)
+    t = synth.make_inputs(wl, with_grad=True)
+    rx, roff, rm = oracle_backward(wl, t)
+    print(f"backward {wl}", flush=True)
+    gx, goff, gm = run_backward(wl, t)
+    gate(_np(gx), rx, wl.dtype, f"{wl.name}/{wl.dtype} grad_input")
+    gate(_np(goff), roff, wl.dtype, f"{wl.name}/{wl.dtype} grad_offset")
+    gate(_np(gm), rm, wl.dtype, f"{wl.name}/{wl.dtype} grad_mask")
