@@ -11,9 +11,11 @@ are converted exactly to float64 before the call.
 
 Layouts (the pages' NHWC convention, pnsm.cn/news/2029644.html section 2.3):
   x      (N, H, W, C)                  C = groups * Cg
-  offset (N, Ho, Wo, G, KH*KW, 2)      pair stored as (x, y)
-  mask   (N, Ho, Wo, G, KH*KW)         logits (softmax=True) or raw weights
+  offset (N, Ho, Wo, G, K, 2)          pair stored as (x, y)
+  mask   (N, Ho, Wo, G, K)             logits (softmax=True) or raw weights
   y      (N, Ho, Wo, C)
+K = KH*KW points, or KH*KW - 1 with remove_center=True (odd KH and KW; the
+centre point is dropped, pnsm.cn/news/2029644.html section 3.3).
 
 Every function here is pinned by ``tests/test_oracle_pins.py``; no function is
 parity-unpinned.
@@ -40,6 +42,7 @@ class _RefProblem(ctypes.Structure):
         ("dil_h", ctypes.c_int64), ("dil_w", ctypes.c_int64),
         ("offset_scale", ctypes.c_double),
         ("softmax", ctypes.c_int64),
+        ("remove_center", ctypes.c_int64),
     ]
 
 
@@ -84,19 +87,22 @@ class Oracle:
         """Output extent along one axis: floor((in + 2p - d(k-1) - 1)/s) + 1."""
         return int(self._lib.ref_out_size(in_size, kernel, stride, pad, dilation))
 
-    def _problem(self, x_shape, groups, kernel, stride, pad, dilation, offset_scale, softmax):
+    def _problem(self, x_shape, groups, kernel, stride, pad, dilation, offset_scale, softmax,
+                 remove_center=False):
         n, h, w, c = (int(v) for v in x_shape)
         kh, kw = _pair(kernel)
+        if remove_center and (kh % 2 == 0 or kw % 2 == 0 or kh * kw < 2):
+            raise ValueError("remove_center needs odd kernel sizes and at least 3 points")
         sh, sw = _pair(stride)
         ph, pw = _pair(pad)
         dh, dw = _pair(dilation)
         if groups <= 0 or c % groups:
             raise ValueError("C must be a multiple of groups")
         p = _RefProblem(n, h, w, c, groups, kh, kw, sh, sw, ph, pw, dh, dw,
-                        float(offset_scale), 1 if softmax else 0)
+                        float(offset_scale), 1 if softmax else 0, 1 if remove_center else 0)
         ho = self.out_size(h, kh, sh, ph, dh)
         wo = self.out_size(w, kw, sw, pw, dw)
-        return p, ho, wo, kh * kw
+        return p, ho, wo, kh * kw - (1 if remove_center else 0)
 
     @staticmethod
     def _check_shapes(x, offset, mask, groups, ho, wo, K):
@@ -107,25 +113,25 @@ class Oracle:
             raise ValueError(f"mask shape {mask.shape} != {(n, ho, wo, groups, K)}")
 
     def forward(self, x, offset, mask, *, groups, kernel=3, stride=1, pad=1, dilation=1,
-                offset_scale=2.0, softmax=True):
+                offset_scale=2.0, softmax=True, remove_center=False):
         """Full fp64 forward; returns y (N, Ho, Wo, C) as float64."""
         x, offset, mask = _f64(x), _f64(offset), _f64(mask)
         p, ho, wo, K = self._problem(x.shape, groups, kernel, stride, pad, dilation,
-                                     offset_scale, softmax)
+                                     offset_scale, softmax, remove_center)
         self._check_shapes(x, offset, mask, groups, ho, wo, K)
         y = np.zeros((x.shape[0], ho, wo, x.shape[3]), dtype=np.float64)
         self._lib.ref_forward(ctypes.byref(p), _dptr(x), _dptr(offset), _dptr(mask), _dptr(y))
         return y
 
     def forward_pixels(self, x, offset, mask, pixels, *, groups, kernel=3, stride=1, pad=1,
-                       dilation=1, offset_scale=2.0, softmax=True):
+                       dilation=1, offset_scale=2.0, softmax=True, remove_center=False):
         """fp64 forward at selected output pixels.
 
         ``pixels`` holds flat indices (n*Ho + ho)*Wo + wo; returns (len(pixels), C).
         """
         x, offset, mask = _f64(x), _f64(offset), _f64(mask)
         p, ho, wo, K = self._problem(x.shape, groups, kernel, stride, pad, dilation,
-                                     offset_scale, softmax)
+                                     offset_scale, softmax, remove_center)
         self._check_shapes(x, offset, mask, groups, ho, wo, K)
         pix = np.ascontiguousarray(pixels, dtype=np.int64).reshape(-1)
         if pix.size and (pix.min() < 0 or pix.max() >= x.shape[0] * ho * wo):
@@ -137,7 +143,7 @@ class Oracle:
         return y
 
     def backward(self, x, offset, mask, grad_out, *, groups, kernel=3, stride=1, pad=1,
-                 dilation=1, offset_scale=2.0, softmax=True):
+                 dilation=1, offset_scale=2.0, softmax=True, remove_center=False):
         """fp64 backward; returns (grad_input, grad_offset, grad_mask) as float64.
 
         grad_mask is taken with respect to the tensor passed as ``mask`` (the
@@ -145,7 +151,7 @@ class Oracle:
         """
         x, offset, mask, gy = _f64(x), _f64(offset), _f64(mask), _f64(grad_out)
         p, ho, wo, K = self._problem(x.shape, groups, kernel, stride, pad, dilation,
-                                     offset_scale, softmax)
+                                     offset_scale, softmax, remove_center)
         self._check_shapes(x, offset, mask, groups, ho, wo, K)
         if gy.shape != (x.shape[0], ho, wo, x.shape[3]):
             raise ValueError("grad_out shape mismatch")

@@ -13,6 +13,8 @@
  *        (NHWC output layout), section 3.3 (pad = kernel_size // 2).
  *   [P4] trdm.cn/news/584307, "DCNv3 operator compilation": section 2.3
  *        (stride-1 output keeps the input's spatial size).
+ *   [P2 §3.3] also lists DCNv4's remove_center argument: the kernel's centre
+ *        point is dropped from the sampling set.
  *
  * What is computed (the operation as the pages define it, written out):
  *   For every image n, output pixel (ho, wo), group g and kernel point
@@ -22,7 +24,7 @@
  *   [P5 §二 step 2: one (x, y) offset per point and group; §三: the offset is
  *   multiplied by offset_scale s before it moves the point off the regular
  *   3x3 grid].
- *     m_k = softmax over the KH*KW points of mask[n,ho,wo,g,:]   (DCNv3,
+ *     m_k = softmax over the K points of mask[n,ho,wo,g,:]       (DCNv3,
  *           [P5 §二 step 3]), or m_k = mask[n,ho,wo,g,k]           (DCNv4).
  *     y[n,ho,wo,g*Cg+c] = sum_k m_k * B(X[n,:,:,g*Cg+c], py, px)
  *   [P5 §二 step 4: per group, bilinear sampling then mask-weighted sum].
@@ -31,9 +33,13 @@
  *     B(X, py, px) = sum_{yc in {y0,y0+1}, xc in {x0,x0+1}}
  *                      (1-|py-yc|) * (1-|px-xc|) * Xz[yc, xc],
  *     y0 = floor(py), x0 = floor(px), Xz = X inside the map, 0 outside.
+ *   With remove_center (odd KH and KW) the centre point (i, j) = (KH/2, KW/2)
+ *   is left out: K = KH*KW - 1 points, numbered in the same row-major order
+ *   with the centre skipped (point k >= KH/2*KW + KW/2 sits at grid index
+ *   k + 1), and the DCNv3 softmax runs over those K points only.
  *   Layouts: x and y are NHWC with C = G*Cg [P2 §2.3]; offsets are
- *   (N,Ho,Wo,G,KH*KW,2) with the pair stored as (x, y); mask is
- *   (N,Ho,Wo,G,KH*KW).
+ *   (N,Ho,Wo,G,K,2) with the pair stored as (x, y); mask is (N,Ho,Wo,G,K),
+ *   K = KH*KW (KH*KW - 1 with remove_center).
  *   Ho = floor((H + 2*pad_h - dil_h*(KH-1) - 1)/stride_h) + 1 (same for Wo).
  *
  * Backward (the exact derivatives of the definition above, one-sided from the
@@ -65,7 +71,14 @@ typedef struct {
     int64_t dil_h, dil_w;
     double offset_scale;
     int64_t softmax; /* 1 = DCNv3 (softmax over the points), 0 = DCNv4 */
+    int64_t remove_center; /* 1 = the centre point is not sampled (odd KH, KW) */
 } ref_problem;
+
+/* Number of sampling points per (pixel, group). */
+static int64_t npoints(const ref_problem *p)
+{
+    return p->kh * p->kw - (p->remove_center ? 1 : 0);
+}
 
 int64_t ref_out_size(int64_t in, int64_t k, int64_t stride, int64_t pad, int64_t dil)
 {
@@ -87,7 +100,7 @@ static double feat(const ref_problem *p, const double *x, int64_t n, int64_t yy,
 /* Modulation scalars m_k of one (pixel, group): softmax or identity. */
 static void mask_weights(const ref_problem *p, const double *mrow, double *m)
 {
-    int64_t K = p->kh * p->kw;
+    int64_t K = npoints(p);
     if (!p->softmax) {
         for (int64_t k = 0; k < K; ++k)
             m[k] = mrow[k];
@@ -109,7 +122,10 @@ static void mask_weights(const ref_problem *p, const double *mrow, double *m)
 static void location(const ref_problem *p, int64_t ho, int64_t wo, int64_t k,
                      const double *offk, double *py, double *px)
 {
-    int64_t i = k / p->kw, j = k % p->kw;
+    int64_t q = k; /* position on the KH x KW grid */
+    if (p->remove_center && q >= (p->kh / 2) * p->kw + p->kw / 2)
+        ++q;
+    int64_t i = q / p->kw, j = q % p->kw;
     *py = (double)(ho * p->stride_h - p->pad_h + i * p->dil_h) + p->offset_scale * offk[1];
     *px = (double)(wo * p->stride_w - p->pad_w + j * p->dil_w) + p->offset_scale * offk[0];
 }
@@ -144,7 +160,7 @@ static void forward_pixel(const ref_problem *p, int64_t Ho, int64_t Wo, const do
                           const double *off, const double *mask, int64_t n, int64_t ho,
                           int64_t wo, double *yrow)
 {
-    int64_t G = p->groups, Cg = p->c / p->groups, K = p->kh * p->kw;
+    int64_t G = p->groups, Cg = p->c / p->groups, K = npoints(p);
     double *m = (double *)malloc(sizeof(double) * (size_t)K);
     for (int64_t g = 0; g < G; ++g) {
         int64_t pg = ((n * Ho + ho) * Wo + wo) * G + g;
@@ -213,7 +229,7 @@ void ref_backward(const ref_problem *p, const double *x, const double *off, cons
 {
     int64_t Ho = ref_out_size(p->h, p->kh, p->stride_h, p->pad_h, p->dil_h);
     int64_t Wo = ref_out_size(p->w, p->kw, p->stride_w, p->pad_w, p->dil_w);
-    int64_t G = p->groups, Cg = p->c / p->groups, K = p->kh * p->kw;
+    int64_t G = p->groups, Cg = p->c / p->groups, K = npoints(p);
     double s = p->offset_scale;
     memset(gx, 0, sizeof(double) * (size_t)(p->n * p->h * p->w * p->c));
     double *m = (double *)malloc(sizeof(double) * (size_t)K);

@@ -20,7 +20,8 @@ the oracle disagrees with:
     invariance of the DCNv3 logits, group independence, the adjoint identity
     <F(x), g> = <x, F^T g>, central finite differences, and the softmax
     gradient summing to zero over the points;
-  * hand-worked values in tests/golden/hand_bilinear.json.
+  * hand-worked values in tests/golden/hand_bilinear.json;
+  * a scalar loop per output element on tiny shapes (brute force).
 They are written so that a plausible slip anywhere in the oracle (a dropped
 term, a swapped (x, y) pair, a transposed point order, a wrong sign, a missing
 offset_scale or softmax Jacobian) fails at least one of them;
@@ -39,9 +40,22 @@ import torch.nn.functional as F
 GOLDEN = pathlib.Path(__file__).resolve().parent / "golden"
 
 
-def _kw(groups, kernel=(3, 3), stride=(1, 1), pad=(1, 1), dilation=(1, 1), s=2.0, softmax=True):
-    return dict(groups=groups, kernel=kernel, stride=stride, pad=pad, dilation=dilation,
-                offset_scale=s, softmax=softmax)
+def _kw(groups, kernel=(3, 3), stride=(1, 1), pad=(1, 1), dilation=(1, 1), s=2.0, softmax=True,
+        rc=False):
+    kw = dict(groups=groups, kernel=kernel, stride=stride, pad=pad, dilation=dilation,
+              offset_scale=s, softmax=softmax)
+    if rc:
+        kw["remove_center"] = True
+    return kw
+
+
+def _points(kernel, rc=False):
+    """Grid positions (i, j) of the sampling points in order: row-major over
+    the kernel, without the centre when it is removed."""
+    pts = [(i, j) for i in range(kernel[0]) for j in range(kernel[1])]
+    if rc:
+        pts.remove((kernel[0] // 2, kernel[1] // 2))
+    return pts
 
 
 def _out(h, k, st, p, d):
@@ -49,10 +63,10 @@ def _out(h, k, st, p, d):
 
 
 def _random_case(rng, n, h, w, c, g, kernel=(3, 3), stride=(1, 1), pad=(1, 1), dilation=(1, 1),
-                 off_std=1.5):
+                 off_std=1.5, rc=False):
     ho = _out(h, kernel[0], stride[0], pad[0], dilation[0])
     wo = _out(w, kernel[1], stride[1], pad[1], dilation[1])
-    K = kernel[0] * kernel[1]
+    K = len(_points(kernel, rc))
     x = rng.standard_normal((n, h, w, c))
     off = rng.standard_normal((n, ho, wo, g, K, 2)) * off_std
     m = rng.standard_normal((n, ho, wo, g, K))
@@ -253,7 +267,7 @@ def pin_out_size(orc):
 
 # --------------------------------------------------------------------------- library routines
 
-def _grid_sample_core(x, off, m, groups, kernel, stride, pad, dilation, s, softmax):
+def _grid_sample_core(x, off, m, groups, kernel, stride, pad, dilation, s, softmax, rc=False):
     """sum_k m_k * grid_sample(x_g, location_k) in torch (fp64, autograd-able).
 
     x (N,H,W,C), off (N,Ho,Wo,G,K,2), m (N,Ho,Wo,G,K) are torch tensors.
@@ -269,8 +283,7 @@ def _grid_sample_core(x, off, m, groups, kernel, stride, pad, dilation, s, softm
     for q in range(groups):
         xg = x[..., q * cg:(q + 1) * cg].permute(0, 3, 1, 2)          # (N, Cg, H, W)
         acc = 0.0
-        for k in range(K):
-            i, j = divmod(k, kernel[1])
+        for k, (i, j) in enumerate(_points(kernel, rc)):
             py = hh * stride[0] - pad[0] + i * dilation[0] + s * off[:, :, :, q, k, 1]
             px = ww * stride[1] - pad[1] + j * dilation[1] + s * off[:, :, :, q, k, 0]
             grid = torch.stack([(2 * px + 1) / w - 1, (2 * py + 1) / h - 1], dim=-1)
@@ -286,6 +299,11 @@ _LIB_CASES = [
     dict(n=1, h=9, w=11, c=6, g=3, kernel=(3, 3), stride=(2, 2), pad=(0, 0), dilation=(1, 1), s=2.0),
     dict(n=1, h=8, w=8, c=4, g=1, kernel=(3, 3), stride=(1, 1), pad=(2, 2), dilation=(2, 2), s=1.0),
     dict(n=1, h=6, w=9, c=10, g=2, kernel=(3, 5), stride=(1, 2), pad=(1, 2), dilation=(1, 1), s=0.5),
+    # the centre point removed (DCNv4's remove_center, pnsm.cn/news/2029644.html section 3.3)
+    dict(n=2, h=7, w=6, c=8, g=2, kernel=(3, 3), stride=(1, 1), pad=(1, 1), dilation=(1, 1), s=2.0,
+         rc=True),
+    dict(n=1, h=9, w=8, c=6, g=3, kernel=(3, 5), stride=(2, 1), pad=(1, 2), dilation=(1, 2), s=1.0,
+         rc=True),
 ]
 
 
@@ -294,13 +312,14 @@ def pin_grid_sample_forward(orc):
     rng = np.random.default_rng(108)
     for cs in _LIB_CASES:
         for softmax in (True, False):
+            rc = cs.get("rc", False)
             x, off, m = _random_case(rng, cs["n"], cs["h"], cs["w"], cs["c"], cs["g"], cs["kernel"],
-                                     cs["stride"], cs["pad"], cs["dilation"], off_std=2.0)
+                                     cs["stride"], cs["pad"], cs["dilation"], off_std=2.0, rc=rc)
             y = orc.forward(x, off, m, **_kw(cs["g"], cs["kernel"], cs["stride"], cs["pad"],
-                                             cs["dilation"], cs["s"], softmax))
+                                             cs["dilation"], cs["s"], softmax, rc))
             ref = _grid_sample_core(torch.from_numpy(x), torch.from_numpy(off), torch.from_numpy(m),
                                     cs["g"], cs["kernel"], cs["stride"], cs["pad"], cs["dilation"],
-                                    cs["s"], softmax)
+                                    cs["s"], softmax, rc)
             _close(y, ref.numpy(), 1e-12, f"grid_sample forward {cs} softmax={softmax}")
 
 
@@ -309,15 +328,16 @@ def pin_grid_sample_backward(orc):
     rng = np.random.default_rng(109)
     for cs in _LIB_CASES:
         for softmax in (True, False):
+            rc = cs.get("rc", False)
             x, off, m = _random_case(rng, cs["n"], cs["h"], cs["w"], cs["c"], cs["g"], cs["kernel"],
-                                     cs["stride"], cs["pad"], cs["dilation"], off_std=2.0)
-            kw = _kw(cs["g"], cs["kernel"], cs["stride"], cs["pad"], cs["dilation"], cs["s"], softmax)
+                                     cs["stride"], cs["pad"], cs["dilation"], off_std=2.0, rc=rc)
+            kw = _kw(cs["g"], cs["kernel"], cs["stride"], cs["pad"], cs["dilation"], cs["s"], softmax, rc)
             ho, wo = off.shape[1], off.shape[2]
             gy = rng.standard_normal((cs["n"], ho, wo, cs["c"]))
             gx, goff, gm = orc.backward(x, off, m, gy, **kw)
             xt, ot, mt = (torch.from_numpy(a).requires_grad_() for a in (x, off, m))
             out = _grid_sample_core(xt, ot, mt, cs["g"], cs["kernel"], cs["stride"], cs["pad"],
-                                    cs["dilation"], cs["s"], softmax)
+                                    cs["dilation"], cs["s"], softmax, rc)
             rx, ro, rm = torch.autograd.grad(out, (xt, ot, mt), grad_outputs=torch.from_numpy(gy))
             _close(gx, rx.numpy(), 1e-11, f"grad_input {cs} softmax={softmax}")
             _close(goff, ro.numpy(), 1e-10, f"grad_offset {cs} softmax={softmax}")
@@ -347,6 +367,103 @@ def pin_depthwise_conv(orc):
         ref = F.conv2d(torch.from_numpy(x).permute(0, 3, 1, 2), wt, stride=stride, padding=pad,
                        dilation=dil, groups=c).permute(0, 2, 3, 1).numpy()
         _close(y, ref, 1e-13, f"depthwise conv {kernel} {stride} {pad} {dil}")
+
+
+def pin_depthwise_conv_remove_center(orc):
+    """With the centre point removed, DCNv4 at zero offsets and a spatially
+    constant mask is the depthwise convolution whose centre tap is zero and
+    whose other taps take the K = KH*KW - 1 mask values in row-major order."""
+    rng = np.random.default_rng(114)
+    for (n, h, w, c, g, kernel, stride, pad, dil) in [
+            (2, 8, 7, 8, 2, (3, 3), (1, 1), (1, 1), (1, 1)),
+            (1, 11, 9, 6, 3, (5, 3), (2, 1), (2, 1), (1, 2)),
+            (1, 9, 12, 4, 1, (3, 5), (1, 2), (1, 2), (2, 1))]:
+        ho = _out(h, kernel[0], stride[0], pad[0], dil[0])
+        wo = _out(w, kernel[1], stride[1], pad[1], dil[1])
+        pts = _points(kernel, rc=True)
+        x = rng.standard_normal((n, h, w, c))
+        mg = rng.standard_normal((g, len(pts)))
+        m = np.broadcast_to(mg, (n, ho, wo, g, len(pts))).copy()
+        off = np.zeros((n, ho, wo, g, len(pts), 2))
+        y = orc.forward(x, off, m, **_kw(g, kernel, stride, pad, dil, 2.0, False, rc=True))
+        taps = np.zeros((g, kernel[0], kernel[1]))
+        for k, (i, j) in enumerate(pts):
+            taps[:, i, j] = mg[:, k]
+        cg = c // g
+        wt = torch.from_numpy(np.repeat(taps, cg, axis=0).reshape(c, 1, kernel[0], kernel[1]))
+        ref = F.conv2d(torch.from_numpy(x).permute(0, 3, 1, 2), wt, stride=stride, padding=pad,
+                       dilation=dil, groups=c).permute(0, 2, 3, 1).numpy()
+        _close(y, ref, 1e-13, f"depthwise conv without centre {kernel} {stride} {pad} {dil}")
+
+
+def _brute_forward(x, off, m, groups, kernel, stride, pad, dilation, s, softmax, rc):
+    """One output element at a time, in plain Python floats, straight from the
+    definition: for each point, its location on the regular grid moved by s
+    times its (x, y) offset, the four floor/floor+1 neighbours weighted by
+    (1 - |dy|)(1 - |dx|), zero off the map, weighted by the point's mask."""
+    import math
+    n_, h, w, c = x.shape
+    cg = c // groups
+    _, ho, wo, _, K, _ = off.shape
+    pts = _points(kernel, rc)
+    assert len(pts) == K
+    y = np.zeros((n_, ho, wo, c))
+    for n in range(n_):
+        for oy in range(ho):
+            for ox in range(wo):
+                for g in range(groups):
+                    logits = [float(m[n, oy, ox, g, k]) for k in range(K)]
+                    if softmax:
+                        top = max(logits)
+                        e = [math.exp(v - top) for v in logits]
+                        wts = [v / sum(e) for v in e]
+                    else:
+                        wts = logits
+                    for cc in range(cg):
+                        ch = g * cg + cc
+                        total = 0.0
+                        for k, (i, j) in enumerate(pts):
+                            py = oy * stride[0] - pad[0] + i * dilation[0] + s * float(off[n, oy, ox, g, k, 1])
+                            px = ox * stride[1] - pad[1] + j * dilation[1] + s * float(off[n, oy, ox, g, k, 0])
+                            val = 0.0
+                            for yy in (math.floor(py), math.floor(py) + 1):
+                                for xx in (math.floor(px), math.floor(px) + 1):
+                                    if 0 <= yy < h and 0 <= xx < w:
+                                        val += (1 - abs(py - yy)) * (1 - abs(px - xx)) * float(x[n, yy, xx, ch])
+                            total += wts[k] * val
+                        y[n, oy, ox, ch] = total
+    return y
+
+
+def pin_brute_force_tiny(orc):
+    """Tiny shapes against the scalar loop above: forward everywhere, and
+    grad_input column by column (the forward is linear in x, so the column
+    of input element e is the forward of the unit tensor at e)."""
+    rng = np.random.default_rng(115)
+    cases = [
+        dict(h=4, w=5, c=2, g=1, kernel=(3, 3), stride=(1, 1), pad=(1, 1), dilation=(1, 1), s=2.0),
+        dict(h=5, w=4, c=4, g=2, kernel=(3, 3), stride=(2, 1), pad=(0, 1), dilation=(1, 2), s=1.0),
+        dict(h=4, w=4, c=2, g=2, kernel=(3, 5), stride=(1, 1), pad=(1, 2), dilation=(1, 1), s=0.5),
+        dict(h=4, w=5, c=2, g=1, kernel=(3, 3), stride=(1, 1), pad=(1, 1), dilation=(1, 1), s=2.0, rc=True),
+        dict(h=5, w=5, c=2, g=1, kernel=(5, 3), stride=(1, 2), pad=(2, 1), dilation=(1, 1), s=1.0, rc=True),
+    ]
+    for cs in cases:
+        rc = cs.get("rc", False)
+        for softmax in (True, False):
+            x, off, m = _random_case(rng, 1, cs["h"], cs["w"], cs["c"], cs["g"], cs["kernel"], cs["stride"],
+                                     cs["pad"], cs["dilation"], off_std=1.5, rc=rc)
+            args = (cs["g"], cs["kernel"], cs["stride"], cs["pad"], cs["dilation"], cs["s"], softmax, rc)
+            kw = _kw(*args)
+            _close(orc.forward(x, off, m, **kw), _brute_forward(x, off, m, *args), 1e-13,
+                   f"brute force forward {cs} softmax={softmax}")
+            gy = rng.standard_normal((1, off.shape[1], off.shape[2], cs["c"]))
+            gx, _, _ = orc.backward(x, off, m, gy, **kw)
+            col = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                unit = np.zeros_like(x)
+                unit[idx] = 1.0
+                col[idx] = float(np.sum(_brute_forward(unit, off, m, *args) * gy))
+            _close(gx, col, 1e-13, f"brute force grad_input {cs} softmax={softmax}")
 
 
 # --------------------------------------------------------------------------- backward
@@ -418,5 +535,5 @@ ALL_PINS = [
     pin_box_average, pin_integer_offsets_exact_gather, pin_partition_of_unity,
     pin_out_of_range_is_zero, pin_hand_golden, pin_linearity, pin_group_independence,
     pin_forward_pixels, pin_out_size, pin_grid_sample_forward, pin_grid_sample_backward,
-    pin_depthwise_conv, pin_adjoint, pin_finite_differences, pin_softmax_grad_sums_to_zero,
+    pin_depthwise_conv, pin_depthwise_conv_remove_center, pin_brute_force_tiny, pin_adjoint, pin_finite_differences, pin_softmax_grad_sums_to_zero,
 ]

@@ -15,8 +15,8 @@ MUTANTS = [
     ("pad_sign", "ho * p->stride_h - p->pad_h", "ho * p->stride_h + p->pad_h"),
     ("dilation_dropped", "i * p->dil_h", "i"),
     ("stride_dropped", "wo * p->stride_w", "wo"),
-    ("point_order_transposed", "int64_t i = k / p->kw, j = k % p->kw;",
-     "int64_t i = k % p->kh, j = k / p->kh;"),
+    ("point_order_transposed", "int64_t i = q / p->kw, j = q % p->kw;",
+     "int64_t i = q % p->kh, j = q / p->kh;"),
     ("bilinear_weight_flipped", "wy[a] = 1.0 - fabs(py - (double)cy[a]);",
      "wy[a] = fabs(py - (double)cy[a]);"),
     ("second_corner_dropped", "cx[1] = cx[0] + 1;", "cx[1] = cx[0];"),
@@ -35,6 +35,10 @@ MUTANTS = [
     ("grad_mask_gy_dropped", "gm[k] += gyr[c] * b;", "gm[k] += b;"),
     ("grad_input_corner_weight", "m[k] * wy[a] * wx[e] * gyr[c];", "m[k] * wy[a] * gyr[c];"),
     ("out_size_off_by_one", "return span / stride + 1;", "return span / stride;"),
+    ("removed_point_is_the_first", "q >= (p->kh / 2) * p->kw + p->kw / 2", "q >= 0"),
+    ("removed_point_is_the_last", "q >= (p->kh / 2) * p->kw + p->kw / 2", "q >= p->kh * p->kw - 1"),
+    ("points_after_centre_not_shifted", "        ++q;", "        q += 0;"),
+    ("centre_still_counted", "- (p->remove_center ? 1 : 0)", "- 0"),
 ]
 
 
