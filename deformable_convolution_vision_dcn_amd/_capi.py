@@ -13,7 +13,7 @@ import pathlib
 LIB_PATH = pathlib.Path(os.environ.get(
     "DCN_MI355X_LIB", pathlib.Path(__file__).resolve().parent / "libdcn_mi355x.so"))
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
 
@@ -44,6 +44,7 @@ class dcn_problem(ctypes.Structure):
         ("offset_scale", ctypes.c_float),
         ("softmax", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("remove_center", ctypes.c_int32),
     ]
 
 

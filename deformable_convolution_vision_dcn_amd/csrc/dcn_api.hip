@@ -20,6 +20,10 @@ int64_t out_extent(int64_t in, int64_t k, int64_t stride, int64_t pad, int64_t d
 
 int elem_bytes(int32_t dtype) { return dtype == DCN_F32 ? 4 : 2; }
 
+// Sampling points per pixel-group: the kernel grid, less its centre with
+// remove_center.
+int64_t npoints(const dcn_problem *p) { return (int64_t)p->kernel_h * p->kernel_w - p->remove_center; }
+
 // Every check of dcn_check, in a fixed order; fills ho/wo on success.
 int validate(const dcn_problem *p, int64_t *ho_out, int64_t *wo_out) {
   if (!p) return DCN_ERR_NULL;
@@ -30,6 +34,9 @@ int validate(const dcn_problem *p, int64_t *ho_out, int64_t *wo_out) {
       p->dilation_h <= 0 || p->dilation_w <= 0 || p->pad_h < 0 || p->pad_w < 0)
     return DCN_ERR_SHAPE;
   if (p->softmax != 0 && p->softmax != 1) return DCN_ERR_ARG;
+  if (p->remove_center != 0 && p->remove_center != 1) return DCN_ERR_ARG;
+  if (p->remove_center && (p->kernel_h % 2 == 0 || p->kernel_w % 2 == 0)) return DCN_ERR_ARG;
+  if (npoints(p) < 1) return DCN_ERR_SHAPE;
   if (!isfinite(p->offset_scale)) return DCN_ERR_ARG;
   if (p->h > kMaxExtent || p->w > kMaxExtent || p->pad_h > kMaxExtent || p->pad_w > kMaxExtent ||
       (int64_t)p->dilation_h * p->kernel_h > kMaxExtent ||
@@ -40,10 +47,10 @@ int validate(const dcn_problem *p, int64_t *ho_out, int64_t *wo_out) {
   if (ho < 1 || wo < 1) return DCN_ERR_SHAPE;
   if (p->dtype != DCN_F32 && p->dtype != DCN_F16 && p->dtype != DCN_BF16) return DCN_ERR_UNSUPPORTED;
   if (p->c / p->groups != dcn::kGroupChannels) return DCN_ERR_UNSUPPORTED;
-  if ((int64_t)p->kernel_h * p->kernel_w > dcn::kMaxPoints) return DCN_ERR_UNSUPPORTED;
+  if (npoints(p) > dcn::kMaxPoints) return DCN_ERR_UNSUPPORTED;
   const int64_t img_bytes = (int64_t)p->h * p->w * p->c * elem_bytes(p->dtype);
   const int64_t img_out_bytes = ho * wo * p->c * elem_bytes(p->dtype);
-  const int64_t img_off_bytes = ho * wo * p->groups * p->kernel_h * p->kernel_w * 2 * elem_bytes(p->dtype);
+  const int64_t img_off_bytes = ho * wo * p->groups * npoints(p) * 2 * elem_bytes(p->dtype);
   if (img_bytes > kMaxBytes31 || img_out_bytes > kMaxBytes31 || img_off_bytes > kMaxBytes31)
     return DCN_ERR_TOO_LARGE;
   if (ho_out) *ho_out = ho;
@@ -75,6 +82,7 @@ dcn::FwdParams geometry(const dcn_problem *p, int64_t ho, int64_t wo) {
   f.PW = p->pad_w;
   f.DH = p->dilation_h;
   f.DW = p->dilation_w;
+  f.RC = p->remove_center;
   f.scale = p->offset_scale;
   f.div_g = dcn::make_fast_div((uint32_t)p->groups);
   f.div_wo = dcn::make_fast_div((uint32_t)wo);
@@ -89,7 +97,7 @@ dcn::FwdParams geometry(const dcn_problem *p, int64_t ho, int64_t wo) {
 int64_t images_per_chunk(const dcn_problem *p, int64_t ho, int64_t wo) {
   const int64_t img_bytes = (int64_t)p->h * p->w * p->c * elem_bytes(p->dtype);
   const int64_t img_out_bytes = ho * wo * p->c * elem_bytes(p->dtype);
-  const int64_t img_off_bytes = ho * wo * p->groups * p->kernel_h * p->kernel_w * 2 * elem_bytes(p->dtype);
+  const int64_t img_off_bytes = ho * wo * p->groups * npoints(p) * 2 * elem_bytes(p->dtype);
   int64_t per = kMaxBytes31 / img_bytes;
   const int64_t per2 = kMaxBytes31 / img_out_bytes;
   const int64_t per3 = kMaxBytes31 / img_off_bytes;
@@ -98,8 +106,9 @@ int64_t images_per_chunk(const dcn_problem *p, int64_t ho, int64_t wo) {
   return per < 1 ? 1 : per;
 }
 
-// The backward's extra checks: 16-bit I/O only for 3x3 points at stride and
-// dilation 1, and one image's fp32 grad_input accumulator below 2^31 bytes.
+// The backward's extra checks: 16-bit I/O only for 3x3 points (with or
+// without the centre) at stride and dilation 1, and one image's fp32
+// grad_input accumulator below 2^31 bytes.
 int validate_backward(const dcn_problem *p, int64_t *ho, int64_t *wo) {
   const int st = validate(p, ho, wo);
   if (st != DCN_OK) return st;
@@ -149,7 +158,7 @@ int dcn_forward(const dcn_problem *p, const void *input, const void *offset, con
     return DCN_ERR_ALIGN;
 
   const int eb = elem_bytes(p->dtype);
-  const int64_t K = (int64_t)p->kernel_h * p->kernel_w;
+  const int64_t K = npoints(p);
   const int64_t img_in = (int64_t)p->h * p->w * p->c * eb;
   const int64_t img_pg = ho * wo * p->groups;
   const int64_t per = images_per_chunk(p, ho, wo);
@@ -198,7 +207,7 @@ int dcn_backward(const dcn_problem *p, const void *input, const void *offset, co
     return DCN_ERR_ALIGN;
   if (!wide && workspace_bytes < workspace_bytes_bwd(p, ho, wo)) return DCN_ERR_WORKSPACE;
 
-  const int64_t K = (int64_t)p->kernel_h * p->kernel_w;
+  const int64_t K = npoints(p);
   const int64_t eb = elem_bytes(p->dtype);
   const int64_t img_elems = (int64_t)p->h * p->w * p->c;
   const int64_t img_in = img_elems * eb;
@@ -256,7 +265,7 @@ const char *dcn_status_string(int status) {
     case DCN_ERR_TOO_LARGE: return "a size exceeds the 32-bit index range of one image";
     case DCN_ERR_HIP: return g_hip_message;
     case DCN_ERR_ABI: return "dcn_problem.struct_size does not match this library";
-    case DCN_ERR_ARG: return "invalid argument value (softmax flag or offset_scale)";
+    case DCN_ERR_ARG: return "invalid argument value (softmax or remove_center flag, or offset_scale)";
     case DCN_ERR_WORKSPACE: return "workspace smaller than dcn_backward_workspace_size reports";
     default: return "unknown status";
   }

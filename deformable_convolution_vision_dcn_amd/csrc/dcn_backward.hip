@@ -47,7 +47,7 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
   constexpr bool FIXED = KH_ > 0;
   const int KH = FIXED ? KH_ : p.KH;
   const int KW = FIXED ? KW_ : p.KW;
-  const int K = KH * KW;
+  const int K = FIXED ? KH_ * KW_ : KH * KW - p.RC;  // fixed extents never drop the centre
 
   extern __shared__ __align__(16) unsigned char lds[];
   float *lds_off = reinterpret_cast<float *>(lds);
@@ -103,8 +103,8 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
   const float s = p.scale;
   float2 *goff = static_cast<float2 *>(bp.grad_offset) + (uint64_t)pg * K;
 
-  auto point = [&](const int ii, const int jj) {
-    const int k = ii * KW + jj;
+  // Point k at grid position (ii, jj).
+  auto point = [&](const int ii, const int jj, const int k) {
     const float dx = s * lds_off[(mrow + k) * 2];
     const float dy = s * lds_off[(mrow + k) * 2 + 1];
     const bool nan_loc = (dx != dx) | (dy != dy);
@@ -173,10 +173,16 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
 #pragma unroll
     for (int ii = 0; ii < KH_; ++ii)
 #pragma unroll
-      for (int jj = 0; jj < KW_; ++jj) point(ii, jj);
+      for (int jj = 0; jj < KW_; ++jj) point(ii, jj, ii * KW_ + jj);
   } else {
-    for (int ii = 0; ii < KH; ++ii)
-      for (int jj = 0; jj < KW; ++jj) point(ii, jj);
+    // Row-major over the grid; with RC the centre is skipped and the points
+    // after it take the next indices.
+    const int centre = p.RC ? (KH / 2) * KW + KW / 2 : -1;
+    for (int q = 0, k = 0; q < KH * KW; ++q) {
+      if (q == centre) continue;
+      const int ii = q / KW;
+      point(ii, q - ii * KW, k++);
+    }
   }
 
   // grad_mask: raw gm_k for DCNv4, through the softmax Jacobian for DCNv3.
@@ -215,7 +221,7 @@ namespace {
 template <int KH, int KW, bool SM>
 hipError_t launch_one(const BwdParams &p, hipStream_t s) {
   constexpr int BLOCK_PG = kBlock / kQuad;
-  const int K = p.f.KH * p.f.KW;
+  const int K = p.f.KH * p.f.KW - p.f.RC;
   const size_t lds = (size_t)BLOCK_PG * K * 4 * sizeof(float);
   const uint32_t blocks = (p.f.pg_total + BLOCK_PG - 1) / BLOCK_PG;
   hipLaunchKernelGGL((dcn_bwd_kernel<KH, KW, SM>), dim3(blocks), dim3(kBlock), lds, s, p);
@@ -241,7 +247,7 @@ hipError_t launch_backward(int dtype, int softmax, const BwdParams &p, hipStream
     const hipError_t t = launch_backward_tiled(softmax, p, s);
     if (t != hipErrorNotSupported) return t;
   }
-  if (p.f.KH == 3 && p.f.KW == 3)
+  if (p.f.KH == 3 && p.f.KW == 3 && !p.f.RC)
     return softmax ? launch_one<3, 3, true>(p, s) : launch_one<3, 3, false>(p, s);
   return softmax ? launch_one<0, 0, true>(p, s) : launch_one<0, 0, false>(p, s);
 }

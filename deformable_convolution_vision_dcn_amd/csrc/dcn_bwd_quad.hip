@@ -1,7 +1,8 @@
 // dcn_bwd_quad.hip -- LDS-tiled gfx950 backward kernel of the DCN core
-// (fp32), a lane quad per pixel-group, for 3x3 kernel points at stride 1 and
-// dilation 1 (the InternImage configuration; wmrh.cn/news/61976, section 二
-// steps 2-4 and section 三).
+// (fp32 arithmetic for fp32 and 16-bit I/O), a lane quad per pixel-group, for
+// 3x3 kernel points at stride 1 and dilation 1 (the InternImage configuration;
+// wmrh.cn/news/61976, section 二 steps 2-4 and section 三), all nine or the
+// eight left by DCNv4's remove_center (pnsm.cn/news/2029644.html section 3.3).
 //
 // The derivatives are those of the untiled backward kernel: every in-map
 // corner of a sample receives m_k * w_corner * gy_c; the offset gradient is
@@ -22,8 +23,8 @@
 //
 // Per pixel-group one quad: lane `sub` owns channels [4 sub, 4 sub + 4) and
 // computes the location, bilinear weights (modulation folded in) and window
-// address of the points k = 2 sub, 2 sub + 1 (and k = 8 for sub 0), as in the
-// tiled forward.  For each point the quad reads its four corners (each lane
+// address of the points k = 2 sub, 2 sub + 1 (and k = 8 for sub 0 when the
+// centre is kept), as in the tiled forward.  For each point the quad reads its four corners (each lane
 // its 4 channels), forms the four per-corner dot products with grad_output
 // and sums them over the quad (DPP), which gives the owner the point's
 // gm, d/dx and d/dy; it scatters w_corner * gy_c for its 4 channels into the
@@ -73,7 +74,10 @@ __device__ __forceinline__ int2 pair_sums(uint64_t v) {
 
 }  // namespace
 
-template <int DT, bool SOFTMAX>
+// RC: the centre point is removed (8 points, k -> grid index k + (k >= 4)):
+// each lane owns exactly two points, lane 0's third slot stays empty and the
+// item takes two rounds instead of three.
+template <int DT, bool SOFTMAX, bool RC>
 __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams bp, TileGeom tg) {
   const FwdParams &p = bp.f;
   using io = Io<DT>;
@@ -87,7 +91,8 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
   constexpr int TS = kBqTile, R = kBqHalo, SPAN_W = kBqSpan;
   constexpr int SPAN = SPAN_W * SPAN_W;
   constexpr int PIXB = kBqPixB, ROW = kBqRow, LIM = SPAN_W - 2;
-  constexpr int CG = kGroupChannels, K = 9;
+  constexpr int CG = kGroupChannels, K = RC ? 8 : 9;
+  constexpr int ROUNDS = RC ? 2 : 3;
   constexpr int WPIX = kBqThreads / 4;                   // window pixels per staging slice
   constexpr int SLOTS = (SPAN + WPIX - 1) / WPIX;
   constexpr uint32_t ZERO = kBqWin;                      // zero block (reads of outside samples)
@@ -114,13 +119,15 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
   const float s = p.scale;
 
   // Window coordinates of each own slot's kernel point before its offset,
-  // packed as three 10-bit fields; slot r holds k = 2 sub + r (r < 2) or 8.
+  // packed as three 10-bit fields; slot r holds k = 2 sub + r (r < 2) or 8
+  // (no point with RC), at grid index q.
   uint32_t bxp = 0, byp = 0;
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
     const int k = r < 2 ? 2 * (int)sub + r : 8;
-    bxp |= (uint32_t)(ox + R + k % 3) << (10 * r);
-    byp |= (uint32_t)(oy + R + k / 3) << (10 * r);
+    const int q = RC ? (r < 2 ? k + (k >= 4) : 4) : k;
+    bxp |= (uint32_t)(ox + R + q % 3) << (10 * r);
+    byp |= (uint32_t)(oy + R + q / 3) << (10 * r);
   }
   const uint32_t win_chunk = lbase + sub * 16u;          // this lane's 4 channels of a window pixel
   const uint32_t gwin_chunk = lbase + GWIN + sub * 16u;
@@ -205,26 +212,37 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
     if constexpr (DT == DCN_F32) {
       const uint32_t orow = I.pg * (K * 8), mrow = I.pg * (K * 4);
       const auto o = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(orow + 16 * sub), 0, 0);
-      const auto o8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 64), 0, 0);
       const auto lg = __builtin_amdgcn_raw_buffer_load_b64(rmask, (int)(mrow + 8 * sub), 0, 0);
-      rl[2] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 32), 0, 0);
+      if constexpr (RC) {
+        rw[4] = rw[5] = rl[2] = 0u;
+      } else {
+        const auto o8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 64), 0, 0);
+        rl[2] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 32), 0, 0);
+        rw[4] = o8[0];
+        rw[5] = o8[1];
+      }
       rw[0] = o[0];
       rw[1] = o[1];
       rw[2] = o[2];
       rw[3] = o[3];
-      rw[4] = o8[0];
-      rw[5] = o8[1];
       rl[0] = lg[0];
       rl[1] = lg[1];
     } else {
       const uint32_t orow = I.pg * (K * 4), mrow = I.pg * (K * 2);
       const auto o = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 8 * sub), 0, 0);
-      rw[2] = __builtin_amdgcn_raw_buffer_load_b32(roff, (int)(orow + 32), 0, 0);
       rw[0] = o[0];
       rw[1] = o[1];
-      rl[0] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub), 0, 0);
-      rl[1] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub + 2), 0, 0);
-      rl[2] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 16), 0, 0);
+      if constexpr (RC) {  // 16-byte mask rows: the lane's two logits in one word
+        const uint32_t lw = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 4 * sub), 0, 0);
+        rl[0] = lw & 0xffffu;
+        rl[1] = lw >> 16;
+        rw[2] = rl[2] = 0u;
+      } else {
+        rw[2] = __builtin_amdgcn_raw_buffer_load_b32(roff, (int)(orow + 32), 0, 0);
+        rl[0] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub), 0, 0);
+        rl[1] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub + 2), 0, 0);
+        rl[2] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 16), 0, 0);
+      }
     }
     buffer_load_words<NWL>(rgy, I.pg * (uint32_t)(CG * EB) + sub * (uint32_t)LB, rg);
   };
@@ -257,13 +275,13 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
       lgs[r] = io::lo(rl[r]);
     }
     unpack<DT, NWL>(rg, gy);
-    if (sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 only
+    if (RC || sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 only
     if constexpr (SOFTMAX) {
       const float mx = quad_max(fmaxf(fmaxf(lgs[0], lgs[1]), lgs[2]));
       float e[3], sum = 0.f;
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
-        e[r] = (r < 2 || sub == 0) ? __expf(lgs[r] - mx) : 0.f;
+        e[r] = (r < 2 || (!RC && sub == 0)) ? __expf(lgs[r] - mx) : 0.f;
         sum += e[r];
       }
       const float inv = __builtin_amdgcn_rcpf(quad_sum(sum));
@@ -314,12 +332,13 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
     issue_rows(nx);
 
     // Per-slot results, shifted in round by round: after the three rounds
-    // res2 holds slot 0, res1 slot 1, res0 slot 2.  (gm, d/dx, d/dy)
+    // (two with RC, then one empty shift) res2 holds slot 0, res1 slot 1,
+    // res0 slot 2.  (gm, d/dx, d/dy)
     float3 res0 = make_float3(0.f, 0.f, 0.f), res1 = res0, res2 = res0;
     float2 o2 = offs[0], o2n = offs[1], o2nn = offs[2];
     float mk = m[0], mkn = m[1], mknn = m[2];
 #pragma unroll 1
-    for (int r = 0; r < 3; ++r) {
+    for (int r = 0; r < ROUNDS; ++r) {
       // Wave priority falls round by round: the waves furthest behind issue
       // first, so the block reaches its flush barrier with less spread.
       if (r == 0) __builtin_amdgcn_s_setprio(3);
@@ -462,6 +481,12 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
       mkn = mknn;
     }
 
+    if constexpr (RC) {
+      res2 = res1;
+      res1 = res0;
+      res0 = make_float3(0.f, 0.f, 0.f);
+    }
+
     // Offset and mask gradients of the own slots (a NaN sampling location
     // makes its point's offset gradient and gm NaN).
     if (cur.live) {
@@ -471,7 +496,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
       for (int r = 0; r < 3; ++r) gm[r] = rs[r].x;
       if constexpr (SOFTMAX) {
         float dot = m[0] * gm[0] + m[1] * gm[1];
-        if (sub == 0) dot += m[2] * gm[2];
+        if (!RC && sub == 0) dot += m[2] * gm[2];
         dot = quad_sum(dot);
 #pragma unroll
         for (int r = 0; r < 3; ++r) gm[r] = m[r] * (gm[r] - dot);
@@ -493,7 +518,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
         __builtin_amdgcn_raw_buffer_store_b64(
             __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), f2{gm[0], gm[1]}), rgm,
             (int)(mrow + 8 * sub), 0, 0);
-        if (sub == 0) {
+        if (!RC && sub == 0) {
           __builtin_amdgcn_raw_buffer_store_b64(
               __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), f2{go[2][0], go[2][1]}), rgoff,
               (int)(orow + 64), 0, 0);
@@ -505,9 +530,13 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
         __builtin_amdgcn_raw_buffer_store_b64(u2{io::pack(go[0][0], go[0][1]), io::pack(go[1][0], go[1][1])}, rgoff,
                                               (int)(orow + 8 * sub), 0, 0);
         const uint32_t gmw = io::pack(gm[0], gm[1]);
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(gmw & 0xffffu), rgm, (int)(mrow + 4 * sub), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(gmw >> 16), rgm, (int)(mrow + 4 * sub + 2), 0, 0);
-        if (sub == 0) {
+        if constexpr (RC) {  // 16-byte mask rows: one aligned word per lane
+          __builtin_amdgcn_raw_buffer_store_b32(gmw, rgm, (int)(mrow + 4 * sub), 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(gmw & 0xffffu), rgm, (int)(mrow + 4 * sub), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(gmw >> 16), rgm, (int)(mrow + 4 * sub + 2), 0, 0);
+        }
+        if (!RC && sub == 0) {
           __builtin_amdgcn_raw_buffer_store_b32(io::pack(go[2][0], go[2][1]), rgoff, (int)(orow + 32), 0, 0);
           __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(io::pack(gm[2], 0.f) & 0xffffu), rgm,
                                                 (int)(mrow + 16), 0, 0);
@@ -558,9 +587,9 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
 
 namespace {
 
-template <int DT, bool SM>
+template <int DT, bool SM, bool RC>
 hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_bwd_quad_kernel<DT, SM>;
+  auto kern = dcn_bwd_quad_kernel<DT, SM, RC>;
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBqLds);
@@ -578,9 +607,20 @@ hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s
   return hipGetLastError();
 }
 
+template <bool RC>
+hipError_t launch_dt(int dtype, int softmax, const BwdParams &b, const TileGeom &tg, hipStream_t s) {
+  switch (dtype) {
+    case DCN_F32: return softmax ? launch_bwd_quad<DCN_F32, true, RC>(b, tg, s) : launch_bwd_quad<DCN_F32, false, RC>(b, tg, s);
+    case DCN_F16: return softmax ? launch_bwd_quad<DCN_F16, true, RC>(b, tg, s) : launch_bwd_quad<DCN_F16, false, RC>(b, tg, s);
+    case DCN_BF16: return softmax ? launch_bwd_quad<DCN_BF16, true, RC>(b, tg, s) : launch_bwd_quad<DCN_BF16, false, RC>(b, tg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
-// 3x3 points, stride 1, dilation 1 only; hipErrorNotSupported otherwise.
+// 3x3 points (all nine, or eight without the centre), stride 1, dilation 1
+// only; hipErrorNotSupported otherwise.
 hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipStream_t s) {
   const FwdParams &p = b.f;
   if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
@@ -598,12 +638,7 @@ hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipS
   tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
-  switch (dtype) {
-    case DCN_F32: return softmax ? launch_bwd_quad<DCN_F32, true>(b, tg, s) : launch_bwd_quad<DCN_F32, false>(b, tg, s);
-    case DCN_F16: return softmax ? launch_bwd_quad<DCN_F16, true>(b, tg, s) : launch_bwd_quad<DCN_F16, false>(b, tg, s);
-    case DCN_BF16: return softmax ? launch_bwd_quad<DCN_BF16, true>(b, tg, s) : launch_bwd_quad<DCN_BF16, false>(b, tg, s);
-    default: return hipErrorInvalidValue;
-  }
+  return p.RC ? launch_dt<true>(dtype, softmax, b, tg, s) : launch_dt<false>(dtype, softmax, b, tg, s);
 }
 
 }  // namespace dcn

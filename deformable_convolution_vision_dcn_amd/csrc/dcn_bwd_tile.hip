@@ -419,7 +419,7 @@ hipError_t launch_bwd_tile(const BwdParams &p, const TileGeom &tg, hipStream_t s
 // 3x3 points, stride 1, dilation 1 only; hipErrorNotSupported otherwise.
 hipError_t launch_backward_tiled(int softmax, const BwdParams &b, hipStream_t s) {
   const FwdParams &p = b.f;
-  if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
+  if (p.RC || p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
     return hipErrorNotSupported;
   TileGeom tg{};
   tg.span_h = tg.span_w = kBwdSpan;

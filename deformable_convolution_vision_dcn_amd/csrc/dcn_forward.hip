@@ -52,7 +52,7 @@ __global__ void __launch_bounds__(kBlock) dcn_fwd_kernel(FwdParams p) {
   constexpr bool FIXED = KH_ > 0;
   const int KH = FIXED ? KH_ : p.KH;
   const int KW = FIXED ? KW_ : p.KW;
-  const int K = KH * KW;
+  const int K = FIXED ? KH_ * KW_ : KH * KW - p.RC;  // fixed extents never drop the centre
 
   extern __shared__ __align__(16) unsigned char lds[];
   unsigned char *lds_off = lds;
@@ -109,9 +109,9 @@ __global__ void __launch_bounds__(kBlock) dcn_fwd_kernel(FwdParams p) {
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
   bool nan_loc = false;
 
-  // One kernel point (ii, jj): location, weights, four corner gathers, FMAs.
-  auto point = [&](const int ii, const int jj) {
-    const int k = ii * KW + jj;
+  // Point k at grid position (ii, jj): location, weights, four corner
+  // gathers, FMAs.
+  auto point = [&](const int ii, const int jj, const int k) {
     const uint32_t o = (mrow + k) * 2;
     const float dx = s * lds_get<DT>(lds_off, o);
     const float dy = s * lds_get<DT>(lds_off, o + 1);
@@ -165,10 +165,16 @@ __global__ void __launch_bounds__(kBlock) dcn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int ii = 0; ii < KH_; ++ii)
 #pragma unroll
-      for (int jj = 0; jj < KW_; ++jj) point(ii, jj);
+      for (int jj = 0; jj < KW_; ++jj) point(ii, jj, ii * KW_ + jj);
   } else {
-    for (int ii = 0; ii < KH; ++ii)
-      for (int jj = 0; jj < KW; ++jj) point(ii, jj);
+    // Row-major over the grid; with RC the centre is skipped and the points
+    // after it take the next indices.
+    const int centre = p.RC ? (KH / 2) * KW + KW / 2 : -1;
+    for (int q = 0, k = 0; q < KH * KW; ++q) {
+      if (q == centre) continue;
+      const int ii = q / KW;
+      point(ii, q - ii * KW, k++);
+    }
   }
 
   if (nan_loc) {
@@ -187,7 +193,7 @@ namespace {
 template <int DT, int LANES, int KH, int KW, bool SM>
 hipError_t launch_one(const FwdParams &p, hipStream_t s) {
   constexpr int BLOCK_PG = kBlock / LANES;
-  const int K = p.KH * p.KW;
+  const int K = p.KH * p.KW - p.RC;
   const size_t lds = (size_t)BLOCK_PG * K * 3 * Io<DT>::kBytes;
   const uint32_t blocks = (p.pg_total + BLOCK_PG - 1) / BLOCK_PG;
   hipLaunchKernelGGL((dcn_fwd_kernel<DT, LANES, KH, KW, SM>), dim3(blocks), dim3(kBlock), lds, s, p);
@@ -199,7 +205,7 @@ hipError_t launch_one(const FwdParams &p, hipStream_t s) {
 template <int DT>
 hipError_t launch_dt(int softmax, const FwdParams &p, hipStream_t s) {
   constexpr int LANES = DT == DCN_F32 ? 4 : 2;
-  const bool k33 = p.KH == 3 && p.KW == 3;
+  const bool k33 = p.KH == 3 && p.KW == 3 && !p.RC;
   if (k33) {
     return softmax ? launch_one<DT, LANES, 3, 3, true>(p, s) : launch_one<DT, LANES, 3, 3, false>(p, s);
   }

@@ -336,7 +336,7 @@ hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
 
 // Stride 1, dilation 1, 3x3 points only; hipErrorNotSupported otherwise.
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
-  if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
+  if (p.RC || p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
     return hipErrorNotSupported;
   TileGeom tg{};
   tg.span_h = tg.span_w = kLaneSpanUnit;

@@ -296,7 +296,7 @@ hipError_t launch_map(const FwdParams &p, const MapGeom &mg, size_t lds, hipStre
 // per item: the smallest power of two that keeps the passes' lanes at least
 // 90 % busy, within the budget (else the best one found).
 hipError_t launch_forward_map(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
-  if (p.KH != 3 || p.KW != 3) return hipErrorNotSupported;
+  if (p.RC || p.KH != 3 || p.KW != 3) return hipErrorNotSupported;
   const int pixb = dtype == DCN_F32 ? 64 : 32;
   const int64_t cell_bytes = (int64_t)(p.H + 2) * (p.W + 2) * pixb;
   const int64_t howo = (int64_t)p.Ho * p.Wo;

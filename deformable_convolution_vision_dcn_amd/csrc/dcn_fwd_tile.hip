@@ -592,7 +592,7 @@ hipError_t launch_tile_gp(int dtype, int softmax, const FwdParams &p, hipStream_
 // 3x3 one or its window does not fit the LDS budget.  groups_per_item: 1 or
 // 2 forces that variant; 0 takes two groups per item where they fit.
 hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipStream_t s, int groups_per_item) {
-  if (p.KH != 3 || p.KW != 3) return hipErrorNotSupported;
+  if (p.RC || p.KH != 3 || p.KW != 3) return hipErrorNotSupported;
   if (groups_per_item != 1) {
     const hipError_t e = launch_tile_gp<2>(dtype, softmax, p, s);
     if (e != hipErrorNotSupported || groups_per_item == 2) return e;

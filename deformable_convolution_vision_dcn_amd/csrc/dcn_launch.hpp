@@ -11,7 +11,7 @@
 namespace dcn {
 
 constexpr int kGroupChannels = 16;  // channels per group with a kernel
-constexpr int kMaxPoints = 64;      // kernel_h * kernel_w upper bound
+constexpr int kMaxPoints = 64;      // sampling points per pixel-group, upper bound
 constexpr int kBlock = 256;         // threads per block of every kernel
 
 // One launch covers a chunk of whole images whose input stays below 2^31
@@ -28,6 +28,7 @@ struct FwdParams {
   uint32_t pg_total;   // pixel-groups (n, ho, wo, g) in the chunk
   int32_t H, W, C, G, Ho, Wo;
   int32_t KH, KW, SH, SW, PH, PW, DH, DW;
+  int32_t RC;          // 1: the centre point is not sampled (K = KH*KW - 1)
   float scale;
   FastDiv div_g, div_wo, div_ho;
 };

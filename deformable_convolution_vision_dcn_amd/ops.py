@@ -27,7 +27,7 @@ def _pair(v) -> Tuple[int, int]:
 
 
 def make_problem(x_shape, *, groups, kernel=3, stride=1, pad=1, dilation=1, offset_scale=2.0,
-                 softmax=True, dtype=torch.float32) -> _capi.dcn_problem:
+                 softmax=True, dtype=torch.float32, remove_center=False) -> _capi.dcn_problem:
     """The dcn_problem of an (N, H, W, C) input and the operator's arguments."""
     n, h, w, c = (int(v) for v in x_shape)
     kh, kw = _pair(kernel)
@@ -39,7 +39,8 @@ def make_problem(x_shape, *, groups, kernel=3, stride=1, pad=1, dilation=1, offs
     return _capi.make_problem(n=n, h=h, w=w, c=c, groups=int(groups), kernel_h=kh, kernel_w=kw,
                               stride_h=sh, stride_w=sw, pad_h=ph, pad_w=pw, dilation_h=dh,
                               dilation_w=dw, offset_scale=float(offset_scale),
-                              softmax=1 if softmax else 0, dtype=_DTYPES[dtype])
+                              softmax=1 if softmax else 0, dtype=_DTYPES[dtype],
+                              remove_center=1 if remove_center else 0)
 
 
 def dcn_check(x_shape, **kw) -> Tuple[int, int]:
@@ -77,16 +78,18 @@ def _no_alias(outputs, inputs):
                 raise ValueError(f"{oname} overlaps {iname}: outputs must not alias other tensors")
 
 
-def _shapes(x: torch.Tensor, groups, kernel, stride, pad, dilation, offset_scale, softmax):
+def _shapes(x: torch.Tensor, groups, kernel, stride, pad, dilation, offset_scale, softmax,
+            remove_center=False):
     if not isinstance(x, torch.Tensor) or x.dim() != 4:
         raise ValueError("input must be a 4-D (N, H, W, C) tensor")
     if x.device.type != "cuda":
         raise ValueError("the DCN core runs on the GPU only: input must be a cuda tensor")
     p = make_problem(x.shape, groups=groups, kernel=kernel, stride=stride, pad=pad,
-                     dilation=dilation, offset_scale=offset_scale, softmax=softmax, dtype=x.dtype)
+                     dilation=dilation, offset_scale=offset_scale, softmax=softmax, dtype=x.dtype,
+                     remove_center=remove_center)
     st, ho, wo = _capi.dcn_check(p)
     _capi.raise_on(st)
-    K = p.kernel_h * p.kernel_w
+    K = p.kernel_h * p.kernel_w - p.remove_center
     n = x.shape[0]
     return p, {"offset": (n, ho, wo, groups, K, 2), "mask": (n, ho, wo, groups, K),
                "out": (n, ho, wo, x.shape[3])}
@@ -98,9 +101,10 @@ def _stream(device) -> int:
 
 def dcn_forward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor, *, groups: int,
                 kernel=3, stride=1, pad=1, dilation=1, offset_scale: float = 2.0,
-                softmax: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                softmax: bool = True, remove_center: bool = False,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Forward of the DCN core; returns (N, Ho, Wo, C) in x's dtype."""
-    p, shp = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax)
+    p, shp = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax, remove_center)
     _expect(x, "input", x.shape, x.dtype, x.device)
     _expect(offset, "offset", shp["offset"], x.dtype, x.device)
     _expect(mask, "mask", shp["mask"], x.dtype, x.device)
@@ -117,7 +121,7 @@ def dcn_forward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor, *, gr
 
 def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
                  grad_out: torch.Tensor, *, groups: int, kernel=3, stride=1, pad=1, dilation=1,
-                 offset_scale: float = 2.0, softmax: bool = True,
+                 offset_scale: float = 2.0, softmax: bool = True, remove_center: bool = False,
                  grad_input: Optional[torch.Tensor] = None,
                  grad_offset: Optional[torch.Tensor] = None,
                  grad_mask: Optional[torch.Tensor] = None,
@@ -127,7 +131,7 @@ def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
     16-bit I/O accumulates grad_input in an fp32 device workspace
     (``backward_workspace_bytes``); pass a ``workspace`` tensor on x's device
     to reuse one, else a fresh one is taken from torch's allocator."""
-    p, shp = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax)
+    p, shp = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax, remove_center)
     _expect(x, "input", x.shape, x.dtype, x.device)
     _expect(offset, "offset", shp["offset"], x.dtype, x.device)
     _expect(mask, "mask", shp["mask"], x.dtype, x.device)
@@ -166,9 +170,10 @@ def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
 
 
 def backward_workspace_bytes(x: torch.Tensor, *, groups: int, kernel=3, stride=1, pad=1, dilation=1,
-                             offset_scale: float = 2.0, softmax: bool = True) -> int:
+                             offset_scale: float = 2.0, softmax: bool = True,
+                             remove_center: bool = False) -> int:
     """Device workspace bytes that dcn_backward needs for this problem (0 for fp32)."""
-    p, _ = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax)
+    p, _ = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax, remove_center)
     st, n = _capi.dcn_backward_workspace_size(p)
     _capi.raise_on(st)
     return n
@@ -178,22 +183,24 @@ class DCNCore(torch.autograd.Function):
     """Autograd wrapper: forward and backward both run in the HIP library."""
 
     @staticmethod
-    def forward(ctx, x, offset, mask, groups, kernel, stride, pad, dilation, offset_scale, softmax):
+    def forward(ctx, x, offset, mask, groups, kernel, stride, pad, dilation, offset_scale, softmax,
+                remove_center):
         x, offset, mask = x.contiguous(), offset.contiguous(), mask.contiguous()
         ctx.save_for_backward(x, offset, mask)
         ctx.args = dict(groups=groups, kernel=kernel, stride=stride, pad=pad, dilation=dilation,
-                        offset_scale=offset_scale, softmax=softmax)
+                        offset_scale=offset_scale, softmax=softmax, remove_center=remove_center)
         return dcn_forward(x, offset, mask, **ctx.args)
 
     @staticmethod
     def backward(ctx, grad_out):
         x, offset, mask = ctx.saved_tensors
         gx, goff, gm = dcn_backward(x, offset, mask, grad_out.contiguous(), **ctx.args)
-        return gx, goff, gm, None, None, None, None, None, None, None
+        return gx, goff, gm, None, None, None, None, None, None, None, None
 
 
 def dcn_core(x, offset, mask, *, groups, kernel=3, stride=1, pad=1, dilation=1,
-             offset_scale=2.0, softmax=True):
-    """Differentiable DCN core (backward in the HIP library: fp32, or 16-bit at 3x3, stride and dilation 1)."""
+             offset_scale=2.0, softmax=True, remove_center=False):
+    """Differentiable DCN core (backward in the HIP library: fp32, or 16-bit for
+    3x3 points at stride and dilation 1)."""
     return DCNCore.apply(x, offset, mask, groups, kernel, stride, pad, dilation, offset_scale,
-                         softmax)
+                         softmax, remove_center)

@@ -83,6 +83,7 @@ class Workload:
     seed: int = 0
     draw: int = 0
     backward: bool = False
+    remove_center: bool = False
 
     @property
     def out_hw(self) -> Tuple[int, int]:
@@ -93,7 +94,7 @@ class Workload:
 
     @property
     def points(self) -> int:
-        return self.kernel[0] * self.kernel[1]
+        return self.kernel[0] * self.kernel[1] - (1 if self.remove_center else 0)
 
     @property
     def samples(self) -> int:
@@ -113,9 +114,11 @@ class Workload:
 
     def op_kwargs(self) -> dict:
         """Keyword arguments describing the operator (shared spelling of both sides)."""
-        return dict(groups=self.groups, kernel=self.kernel, stride=self.stride, pad=self.pad,
-                    dilation=self.dilation, offset_scale=self.offset_scale,
-                    softmax=self.softmax)
+        kw = dict(groups=self.groups, kernel=self.kernel, stride=self.stride, pad=self.pad,
+                  dilation=self.dilation, offset_scale=self.offset_scale, softmax=self.softmax)
+        if self.remove_center:
+            kw["remove_center"] = True
+        return kw
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)

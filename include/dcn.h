@@ -7,7 +7,7 @@
  * sections 2.2-2.3 and 3.3):
  *
  *   for every image n, output pixel (ho, wo), group g and kernel point
- *   k = i*kernel_w + j (i along H, j along W):
+ *   k = i*kernel_w + j (i along H, j along W), K = kernel_h*kernel_w points:
  *     py  = ho*stride_h - pad_h + i*dilation_h + offset_scale * offset[n,ho,wo,g,k,1]
  *     px  = wo*stride_w - pad_w + j*dilation_w + offset_scale * offset[n,ho,wo,g,k,0]
  *     m_k = softmax_k(mask[n,ho,wo,g,:])   if softmax != 0   (DCNv3)
@@ -15,13 +15,19 @@
  *     out[n,ho,wo,g*Cg+c] = sum_k m_k * bilinear(input[n,:,:,g*Cg+c], py, px)
  *
  *   bilinear() puts pixel centres at integer coordinates and reads zero outside
- *   [0,H) x [0,W).  Ho = (H + 2*pad_h - dilation_h*(kernel_h-1) - 1)/stride_h + 1
+ *   [0,H) x [0,W).
+ *
+ *   remove_center (DCNv4's option of that name, pnsm.cn/news/2029644.html
+ *   section 3.3; odd kernel sizes only) drops the centre point (i, j) =
+ *   (kernel_h/2, kernel_w/2): K = kernel_h*kernel_w - 1, the points keep the
+ *   row-major order with the centre skipped (point k at or past the centre's
+ *   index sits at grid index k + 1) and the softmax runs over those K.  Ho = (H + 2*pad_h - dilation_h*(kernel_h-1) - 1)/stride_h + 1
  *   (integer division; the same form gives Wo).  Cg = C / groups.
  *
  * Layouts (all tensors dense and contiguous, row-major, one dtype per call):
  *   input        (N, H, W, C)                              NHWC
- *   offset       (N, Ho, Wo, groups, kernel_h*kernel_w, 2) pair stored (x, y)
- *   mask         (N, Ho, Wo, groups, kernel_h*kernel_w)    logits or weights
+ *   offset       (N, Ho, Wo, groups, K, 2)                 pair stored (x, y)
+ *   mask         (N, Ho, Wo, groups, K)                    logits or weights
  *   output       (N, Ho, Wo, C)                            NHWC
  *   grad_*       the shape of the tensor it is the gradient of.
  *
@@ -36,7 +42,8 @@
  * overwritten, never accumulated into, and must not alias any input.
  *
  * Kernel choice: the forward picks its kernel from the problem (dtype, point
- * count, stride, dilation, map and window size).  The environment variable
+ * count, stride, dilation, map and window size; the forward with
+ * remove_center runs the untiled kernel).  The environment variable
  * DCN_MI355X_FWD_PATH = "generic" | "tiled" (one group per work item) |
  * "pair" (two groups per work item) | "lane" | "map" (whole maps in LDS),
  * read at every call, makes it try that kernel first; DCN_MI355X_BWD_PATH =
@@ -56,7 +63,7 @@
 extern "C" {
 #endif
 
-#define DCN_ABI_VERSION 2
+#define DCN_ABI_VERSION 3
 
 /* Element type of every tensor of one call. */
 typedef enum dcn_dtype {
@@ -69,17 +76,19 @@ typedef enum dcn_status {
     DCN_OK = 0,
     DCN_ERR_NULL = -1,        /* NULL problem, or NULL pointer for a non-empty tensor   */
     DCN_ERR_SHAPE = -2,       /* a dim <= 0 (N may be 0), C % groups != 0, kernel,
-                                 stride or dilation < 1, pad < 0, or Ho/Wo < 1         */
-    DCN_ERR_UNSUPPORTED = -3, /* dtype, channels-per-group or point count without a
-                                 kernel, or a 16-bit backward other than 3x3 points
-                                 at stride and dilation 1                              */
+                                 stride or dilation < 1, pad < 0, Ho/Wo < 1, or no
+                                 point left (1x1 with remove_center)                   */
+    DCN_ERR_UNSUPPORTED = -3, /* dtype, channels-per-group or point count (K > 64)
+                                 without a kernel, or a 16-bit backward other than
+                                 3x3 points at stride and dilation 1                   */
     DCN_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                */
     DCN_ERR_TOO_LARGE = -5,   /* one image's input, output or offset tensor exceeds
                                  2^31-1 bytes, or H or W exceeds 2^24 (16-bit
                                  backward: also H*W*C*4 bytes, its fp32 accumulator)   */
     DCN_ERR_HIP = -6,         /* the HIP runtime refused a launch; see dcn_status_string */
     DCN_ERR_ABI = -7,         /* problem->struct_size != sizeof(dcn_problem)            */
-    DCN_ERR_ARG = -8,         /* softmax not 0/1, or offset_scale not finite            */
+    DCN_ERR_ARG = -8,         /* softmax or remove_center not 0/1, remove_center with
+                                 an even kernel size, or offset_scale not finite       */
     DCN_ERR_WORKSPACE = -9    /* dcn_backward's workspace_bytes below what
                                  dcn_backward_workspace_size reports                   */
 } dcn_status;
@@ -95,6 +104,7 @@ typedef struct dcn_problem {
     float offset_scale;   /* multiplies the learned offset only, not the grid   */
     int32_t softmax;      /* 1 = DCNv3 (softmax over the points), 0 = DCNv4     */
     int32_t dtype;        /* dcn_dtype                                          */
+    int32_t remove_center;/* 1 = the kernel's centre point is not sampled       */
 } dcn_problem;
 
 /* Version of this ABI (DCN_ABI_VERSION of the built library). */
@@ -126,8 +136,8 @@ int dcn_backward_workspace_size(const dcn_problem *p, uint64_t *bytes);
  *                 the softmax Jacobian when softmax != 0.
  * At integer sampling coordinates the derivative is the one-sided one from the
  * right (the floor convention).  fp32 for every shape.  16-bit I/O (all
- * tensors of the call in that dtype) for 3x3 points at stride and dilation 1,
- * else DCN_ERR_UNSUPPORTED.  The arithmetic is fp32 throughout and grad_input
+ * tensors of the call in that dtype) for 3x3 points (remove_center or not)
+ * at stride and dilation 1, else DCN_ERR_UNSUPPORTED.  The arithmetic is fp32 throughout and grad_input
  * is accumulated in fp32: sums per output tile in fixed point, added with
  * fp32 atomics (so its low bits can vary from run to run).  For fp32 the sums
  * land in grad_input itself (the call zeroes it first) and workspace may be

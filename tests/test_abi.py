@@ -55,13 +55,13 @@ def test_status_codes_match_header():
 
 
 def test_problem_struct_layout_is_guarded(lib):
-    # 17 four-byte fields, no padding
-    assert ctypes.sizeof(_capi.dcn_problem) == 68
+    # 18 four-byte fields, no padding
+    assert ctypes.sizeof(_capi.dcn_problem) == 72
     p = _capi.make_problem(n=1, h=8, w=8, c=16, groups=1, kernel_h=3, kernel_w=3, stride_h=1,
                            stride_w=1, pad_h=1, pad_w=1, dilation_h=1, dilation_w=1,
                            offset_scale=2.0, softmax=1, dtype=0)
     assert _capi.dcn_check(p)[0] == 0
-    p.struct_size = 64
+    p.struct_size = 68  # the layout before remove_center
     assert _capi.dcn_check(p)[0] == _capi.CODES["DCN_ERR_ABI"]
 
 
@@ -104,6 +104,16 @@ BASE = dict(n=2, h=9, w=7, c=32, groups=2, kernel_h=3, kernel_w=3, stride_h=1, s
     ({"h": 2048, "w": 2048, "c": 64, "groups": 4}, "DCN_OK"),
     ({"h": 2048, "w": 2048, "c": 64, "groups": 4, "kernel_h": 5, "kernel_w": 5,
       "pad_h": 2, "pad_w": 2}, "DCN_ERR_TOO_LARGE"),
+    # remove_center: a 0/1 flag, odd kernel sizes only, at least one point left
+    ({"remove_center": 1}, "DCN_OK"),
+    ({"remove_center": 1, "kernel_h": 5, "kernel_w": 3, "pad_h": 2}, "DCN_OK"),
+    ({"remove_center": 2}, "DCN_ERR_ARG"),
+    ({"remove_center": -1}, "DCN_ERR_ARG"),
+    ({"remove_center": 1, "kernel_h": 4, "pad_h": 2}, "DCN_ERR_ARG"),
+    ({"remove_center": 1, "kernel_h": 1, "kernel_w": 1, "pad_h": 0, "pad_w": 0}, "DCN_ERR_SHAPE"),
+    # 65 grid points less the centre is 64: within the limit
+    ({"remove_center": 1, "kernel_h": 5, "kernel_w": 13, "pad_h": 2, "pad_w": 6, "w": 13}, "DCN_OK"),
+    ({"kernel_h": 5, "kernel_w": 13, "pad_h": 2, "pad_w": 6, "w": 13}, "DCN_ERR_UNSUPPORTED"),
 ])
 def test_check_table(lib, change, code):
     p = _capi.make_problem(**{**BASE, **change})
@@ -159,6 +169,13 @@ def test_argument_checks_before_any_device_call(lib):
     assert lib.dcn_backward_workspace_size(ctypes.byref(p16), None) == _capi.CODES["DCN_ERR_NULL"]
     # fp32 needs no workspace
     assert _capi.dcn_backward_workspace_size(p) == (0, 0)
+    # remove_center: the same workspace rule
+    prc = _capi.make_problem(**{**BASE, "remove_center": 1})
+    assert _capi.dcn_backward_workspace_size(prc) == (0, 0)
+    prc16 = _capi.make_problem(**{**BASE, "remove_center": 1, "dtype": _capi.DCN_F16})
+    assert _capi.dcn_backward_workspace_size(prc16) == (0, need)
+    prc16s = _capi.make_problem(**{**BASE, "remove_center": 1, "dtype": _capi.DCN_F16, "stride_w": 2})
+    assert _capi.dcn_backward_workspace_size(prc16s)[0] == _capi.CODES["DCN_ERR_UNSUPPORTED"]
     # N = 0: valid, nothing enqueued, pointers may be NULL
     p0 = _capi.make_problem(**{**BASE, "n": 0})
     assert F(p0, None, None, None, None, None) == 0

@@ -28,6 +28,9 @@ def test_dcn_check_reports_shape_and_errors():
         dcn.dcn_check((1, 8, 8, 30), groups=4)
     with pytest.raises(dcn.DCNError, match="DCN_ERR_UNSUPPORTED"):
         dcn.dcn_check((1, 8, 8, 64), groups=2)
+    assert dcn.dcn_check((1, 8, 8, 16), groups=1, remove_center=True) == (8, 8)
+    with pytest.raises(dcn.DCNError, match="DCN_ERR_ARG"):
+        dcn.dcn_check((1, 8, 8, 16), groups=1, kernel=(3, 4), pad=(1, 2), remove_center=True)
 
 
 def test_missing_library_fails_loudly(tmp_path):

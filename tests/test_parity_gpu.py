@@ -77,6 +77,13 @@ SMALL = [
              offset_scale=1.3, seed=20),
     Workload("one_pixel", n=1, h=1, w=1, c=16, groups=1, seed=21),
     Workload("wide_many_groups", n=1, h=5, w=37, c=16 * 21, groups=21, seed=22),
+    # the centre point removed (8 of the 3x3 points; 14 of a 5x3 grid)
+    Workload("rc_k3_v4", n=2, h=13, w=11, c=48, groups=3, softmax=False, mask_dist=normal(0.5),
+             remove_center=True, seed=24),
+    Workload("rc_k3_v3", n=2, h=12, w=14, c=32, groups=2, offset_dist=uniform(3.0),
+             remove_center=True, seed=25),
+    Workload("rc_k5x3_stride2", n=1, h=15, w=12, c=32, groups=2, kernel=(5, 3), pad=(2, 1),
+             stride=(2, 1), dilation=(1, 2), remove_center=True, seed=26),
 ]
 
 
@@ -109,6 +116,23 @@ def test_forward_each_kernel(wl, dtype, path, monkeypatch):
     print(f"forward {wl.name} {dtype} path={path}", flush=True)
     t = synth.make_inputs(wl)
     gate(_np(run_forward(wl, t)), oracle_full(wl, t), dtype, f"{wl.name}/{dtype}/{path}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_remove_center_every_path(dtype, monkeypatch):
+    """With remove_center every forced kernel choice ends in a kernel that
+    handles it (the tiled kernels refuse the 8-point rows)."""
+    wl = Workload("rc_paths", n=2, h=37, w=29, c=48, groups=3, offset_dist=normal(2.0),
+                  remove_center=True, dtype=dtype, seed=27)
+    t = synth.make_inputs(wl)
+    ref = oracle_full(wl, t)
+    for path in ["auto", "generic", "tiled", "pair", "lane", "map"]:
+        if path == "auto":
+            monkeypatch.delenv("DCN_MI355X_FWD_PATH", raising=False)
+        else:
+            monkeypatch.setenv("DCN_MI355X_FWD_PATH", path)
+        print(f"forward rc_paths {dtype} path={path}", flush=True)
+        gate(_np(run_forward(wl, t)), ref, dtype, f"rc_paths/{dtype}/{path}")
 
 
 # Whole-map kernel: one group per item at the 24x24 stage-3 map (every lane
@@ -202,6 +226,12 @@ BWD = [
     Workload("bwd_k3x5_generic_v4", n=1, h=8, w=11, c=16, groups=1, kernel=(3, 5), pad=(1, 2),
              softmax=False, seed=36),
     Workload("bwd_one_pixel", n=1, h=1, w=1, c=16, groups=1, seed=37),
+    Workload("bwd_rc_k3_v4", n=2, h=12, w=10, c=32, groups=2, softmax=False, mask_dist=normal(0.5),
+             remove_center=True, seed=38),
+    Workload("bwd_rc_k3_v3", n=1, h=21, w=19, c=48, groups=3, offset_dist=uniform(3.0),
+             remove_center=True, seed=39),
+    Workload("bwd_rc_k3x5", n=1, h=9, w=11, c=16, groups=1, kernel=(3, 5), pad=(1, 2),
+             remove_center=True, seed=40),
 ]
 
 
@@ -240,7 +270,8 @@ BWD_PATH_CASES = [
 
 
 @pytest.mark.parametrize("path", ["generic", "tiled", "quad"])
-@pytest.mark.parametrize("wl", BWD_PATH_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", BWD_PATH_CASES + [BWD_PATH_CASES[0].replace(name="bwdp_rc", remove_center=True)],
+                         ids=lambda w: w.name)
 def test_backward_each_kernel(wl, path, monkeypatch):
     """Every backward kernel, forced in turn, on multi-tile ragged shapes
     whose offsets also leave the tile windows (the global fix-up path)."""
@@ -260,14 +291,19 @@ BWD16 = [
     Workload("bwd16_ragged_far", n=2, h=37, w=29, c=48, groups=3, offset_dist=uniform(5.0), seed=63),
     Workload("bwd16_pad0", n=1, h=19, w=18, c=16, groups=1, pad=(0, 0), offset_dist=normal(3.0), seed=64),
     Workload("bwd16_one_pixel", n=1, h=1, w=1, c=16, groups=1, seed=65),
+    Workload("bwd16_rc_v4", n=2, h=20, w=17, c=32, groups=2, softmax=False, mask_dist=normal(0.5),
+             remove_center=True, seed=66),
+    Workload("bwd16_rc_far", n=1, h=37, w=29, c=48, groups=3, offset_dist=uniform(5.0),
+             remove_center=True, seed=67),
 ]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("wl", BWD16, ids=lambda w: w.name)
 def test_backward_16bit(wl, dtype):
-    """16-bit backward (3x3, stride and dilation 1) against the oracle on the
-    same 16-bit inputs, with the 16-bit gate on all three gradients."""
+    """16-bit backward (3x3 with or without the centre, stride and dilation 1)
+    against the oracle on the same 16-bit inputs, with the 16-bit gate on all
+    three gradients."""
     wl = wl.replace(dtype=dtype)
     print(f"backward {wl.name} {dtype}", flush=True)
     t = synth.make_inputs(wl, with_grad=True)
