@@ -189,11 +189,13 @@ __device__ __forceinline__ void stage_to_lds(void *lds, const void *src, uint32_
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 
-// The 9 (x, y) offset pairs of pixel-group pg as 18 fp32 values.
-template <int DT>
-__device__ __forceinline__ void load_offsets(const void *base, uint32_t pg, float (&o)[18]) {
+// The K (x, y) offset pairs of pixel-group pg as 2K fp32 values, for the 9
+// points of a 3x3 kernel or the 8 left without its centre.
+template <int DT, int K>
+__device__ __forceinline__ void load_offsets(const void *base, uint32_t pg, float (&o)[2 * K]) {
+  static_assert(K == 9 || K == 8, "3x3 rows");
   if constexpr (DT == DCN_F32) {
-    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * 18;
+    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * (2 * K);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src + 4 * q);
@@ -202,12 +204,14 @@ __device__ __forceinline__ void load_offsets(const void *base, uint32_t pg, floa
       o[4 * q + 2] = __uint_as_float(v[2]);
       o[4 * q + 3] = __uint_as_float(v[3]);
     }
-    const u32x2_a4 v = *reinterpret_cast<const u32x2_a4 *>(src + 16);
-    o[16] = __uint_as_float(v[0]);
-    o[17] = __uint_as_float(v[1]);
+    if constexpr (K == 9) {
+      const u32x2_a4 v = *reinterpret_cast<const u32x2_a4 *>(src + 16);
+      o[16] = __uint_as_float(v[0]);
+      o[17] = __uint_as_float(v[1]);
+    }
   } else {
-    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * 9;
-    uint32_t w[9];
+    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * K;
+    uint32_t w[K];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src + 4 * q);
@@ -216,20 +220,21 @@ __device__ __forceinline__ void load_offsets(const void *base, uint32_t pg, floa
       w[4 * q + 2] = v[2];
       w[4 * q + 3] = v[3];
     }
-    w[8] = src[8];
+    if constexpr (K == 9) w[8] = src[8];
 #pragma unroll
-    for (int q = 0; q < 9; ++q) {
+    for (int q = 0; q < K; ++q) {
       o[2 * q] = Io<DT>::lo(w[q]);
       o[2 * q + 1] = Io<DT>::hi(w[q]);
     }
   }
 }
 
-// The 9 mask values of pixel-group pg as fp32.
-template <int DT>
-__device__ __forceinline__ void load_mask(const void *base, uint32_t pg, float (&m)[9]) {
+// The K mask values of pixel-group pg as fp32 (K = 9 or 8 as above).
+template <int DT, int K>
+__device__ __forceinline__ void load_mask(const void *base, uint32_t pg, float (&m)[K]) {
+  static_assert(K == 9 || K == 8, "3x3 rows");
   if constexpr (DT == DCN_F32) {
-    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * 9;
+    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * K;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src + 4 * q);
@@ -238,11 +243,19 @@ __device__ __forceinline__ void load_mask(const void *base, uint32_t pg, float (
       m[4 * q + 2] = __uint_as_float(v[2]);
       m[4 * q + 3] = __uint_as_float(v[3]);
     }
-    m[8] = __uint_as_float(src[8]);
-  } else {
-    const uint16_t *src = static_cast<const uint16_t *>(base) + (uint64_t)pg * 9;
+    if constexpr (K == 9) m[8] = __uint_as_float(src[8]);
+  } else if constexpr (K == 8) {  // 16-byte rows: one aligned 16-byte load
+    const uint32_t *src = static_cast<const uint32_t *>(base) + (uint64_t)pg * 4;
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4 *>(src);
 #pragma unroll
-    for (int q = 0; q < 9; ++q) m[q] = Io<DT>::lo((uint32_t)src[q]);
+    for (int q = 0; q < 4; ++q) {
+      m[2 * q] = Io<DT>::lo(v[q]);
+      m[2 * q + 1] = Io<DT>::hi(v[q]);
+    }
+  } else {
+    const uint16_t *src = static_cast<const uint16_t *>(base) + (uint64_t)pg * K;
+#pragma unroll
+    for (int q = 0; q < K; ++q) m[q] = Io<DT>::lo((uint32_t)src[q]);
   }
 }
 

@@ -239,7 +239,8 @@ Path path_override() {
 // pixel-group; two groups per work item where the group count is even),
 // 16-bit I/O the lane-per-pixel-group kernel, which needs a quarter of the
 // address and weight arithmetic and wins once a pixel's 16 channels are only
-// 32 bytes.  Everything else runs the untiled kernel.
+// 32 bytes.  Without the kernel's centre (8 points) the lane kernel serves
+// every dtype.  Everything else runs the untiled kernel.
 // Whether the whole-map kernel is the first choice: the output map is
 // smaller than one 16x16 tile, or tiles would leave over half of their
 // pixel slots empty.  (At 24x24, 56 % full, the tiled lane kernel is still
@@ -266,6 +267,10 @@ hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_
       const int gpi = forced == Path::kTiled ? 1 : (forced == Path::kPair ? 2 : 0);
       const hipError_t t = launch_forward_tiled(dtype, softmax, p, s, gpi);
       if (t != hipErrorNotSupported) return t;
+    }
+    if (!lane_first && forced == Path::kAuto) {  // fp32 rows the tiled kernels refuse (remove_center)
+      const hipError_t l = launch_forward_lane(dtype, softmax, p, s);
+      if (l != hipErrorNotSupported) return l;
     }
   }
   switch (dtype) {

@@ -1,6 +1,7 @@
 // dcn_fwd_lane.hip -- LDS-tiled gfx950 forward kernel of the DCN core for
 // 3x3 kernel points, one lane per pixel-group (wmrh.cn/news/61976, section 二
-// steps 2-4 and section 三).
+// steps 2-4 and section 三); also for the 8 points DCNv4's remove_center
+// leaves (pnsm.cn/news/2029644.html section 3.3).
 //
 // The forward is a gather-reduce: per bilinear sample 64 fp32 FMAs (16
 // channels x 4 corners) against a few dozen instructions of location and
@@ -54,7 +55,9 @@ __device__ __forceinline__ void lds_read16(const unsigned char *src, uint32_t (&
 
 }  // namespace
 
-template <int DT, bool SOFTMAX>
+// RC: the centre point is removed (8 points; point k sits at grid index
+// k + (k >= 4)).
+template <int DT, bool SOFTMAX, bool RC>
 #ifndef DCN_LANE_WAVES
 #define DCN_LANE_WAVES 2  // waves per SIMD the register budget must allow
 #endif
@@ -72,7 +75,7 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
   constexpr int SLOTS = (SPAN + QUADS - 1) / QUADS;
   constexpr int LIM = SPAN_W - 2;
   constexpr int ZERO = SPAN * PIXB;
-  constexpr int K = 9;
+  constexpr int K = RC ? 8 : 9;
 
   extern __shared__ __align__(16) unsigned char tile[];
 
@@ -138,15 +141,15 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
     }
   };
 
-  float off[18], msk[9];
+  float off[2 * K], msk[K];
   // Unconditional (a dead lane reads pixel-group 0 and ignores it): every
   // memory instruction of the item loop is issued on every path, so the
   // compiler's wait counting stays exact and the window prefetch is only
   // waited for where the LDS store needs it.
   auto issue_pgdata = [&](const Item &I) {
     const uint32_t pg = I.live ? I.pg : 0u;
-    load_offsets<DT>(p.offset, pg, off);
-    load_mask<DT>(p.mask, pg, msk);
+    load_offsets<DT, K>(p.offset, pg, off);
+    load_mask<DT, K>(p.mask, pg, msk);
   };
 
   // Per-lane chunk rotation (bank spreading) and its byte offsets.
@@ -215,7 +218,8 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
         if (k == 0) __builtin_amdgcn_s_setprio(3);
         if (k == 3) __builtin_amdgcn_s_setprio(2);
         if (k == 6) __builtin_amdgcn_s_setprio(1);
-        const int i = k / 3, j = k % 3;
+        const int q = RC ? k + (k >= 4) : k;  // grid index
+        const int i = q / 3, j = q % 3;
         const float dx = s * off[2 * k], dy = s * off[2 * k + 1];
         const bool nan_loc = (dx != dx) | (dy != dy);
         const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
@@ -307,9 +311,9 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
 
 namespace {
 
-template <int DT, bool SM>
+template <int DT, bool SM, bool RC>
 hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_fwd_lane_kernel<DT, SM>;
+  auto kern = dcn_fwd_lane_kernel<DT, SM, RC>;
   constexpr int PIXB = lane_pixel_stride<DT>();
   const size_t lds = ((size_t)kLaneSpanUnit * kLaneSpanUnit + kLaneSpanUnit + 2) * PIXB;
   // Set on every launch: the limit is per device and setting it is idempotent.
@@ -332,11 +336,21 @@ hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool RC>
+hipError_t launch_lane_dt(int dtype, int softmax, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
+  switch (dtype) {
+    case DCN_F32: return softmax ? launch_lane<DCN_F32, true, RC>(p, tg, s) : launch_lane<DCN_F32, false, RC>(p, tg, s);
+    case DCN_F16: return softmax ? launch_lane<DCN_F16, true, RC>(p, tg, s) : launch_lane<DCN_F16, false, RC>(p, tg, s);
+    case DCN_BF16: return softmax ? launch_lane<DCN_BF16, true, RC>(p, tg, s) : launch_lane<DCN_BF16, false, RC>(p, tg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 // Stride 1, dilation 1, 3x3 points only; hipErrorNotSupported otherwise.
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
-  if (p.RC || p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
+  if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
     return hipErrorNotSupported;
   TileGeom tg{};
   tg.span_h = tg.span_w = kLaneSpanUnit;
@@ -351,12 +365,7 @@ hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipSt
   tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
-  switch (dtype) {
-    case DCN_F32: return softmax ? launch_lane<DCN_F32, true>(p, tg, s) : launch_lane<DCN_F32, false>(p, tg, s);
-    case DCN_F16: return softmax ? launch_lane<DCN_F16, true>(p, tg, s) : launch_lane<DCN_F16, false>(p, tg, s);
-    case DCN_BF16: return softmax ? launch_lane<DCN_BF16, true>(p, tg, s) : launch_lane<DCN_BF16, false>(p, tg, s);
-    default: return hipErrorInvalidValue;
-  }
+  return p.RC ? launch_lane_dt<true>(dtype, softmax, p, tg, s) : launch_lane_dt<false>(dtype, softmax, p, tg, s);
 }
 
 }  // namespace dcn

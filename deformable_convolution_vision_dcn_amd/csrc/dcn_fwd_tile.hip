@@ -1,6 +1,7 @@
 // dcn_fwd_tile.hip -- LDS-tiled gfx950 forward kernel of the DCN core for
 // 3x3 kernel points (the InternImage configuration; wmrh.cn/news/61976,
-// section 二 steps 2-4 and section 三).
+// section 二 steps 2-4 and section 三), in fp32 also for the 8 points that
+// DCNv4's remove_center leaves (pnsm.cn/news/2029644.html section 3.3).
 //
 // Why tiles: every bilinear sample reads four 16-channel corner slices at
 // offset-driven addresses, 256 bytes per sample in fp32 against 59*4/9 bytes
@@ -63,8 +64,11 @@ constexpr int tile_pixel_stride() {
 }
 
 // UNIT: stride 1 and dilation 1, so the window geometry is a compile-time
-// constant (no run-time multiplies on the per-point path).
-template <int DT, bool SOFTMAX, int TH, int TW, int R, bool UNIT, int GP>
+// constant (no run-time multiplies on the per-point path).  RC: the centre
+// point is removed (8 points, point k at grid index k + (k >= 4)): each lane
+// owns two points, lane 0's third slot stays empty, two rounds instead of
+// three.
+template <int DT, bool SOFTMAX, int TH, int TW, int R, bool UNIT, int GP, bool RC>
 __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdParams p, TileGeom tg) {
   using io = Io<DT>;
   constexpr int CG = kGroupChannels;
@@ -80,7 +84,7 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   constexpr int LPP = 4 * GP;                      // lanes per staged window pixel
   constexpr int WPIX = THREADS / LPP;              // window pixels per slice
   constexpr int MAXPQ = (tile_max_span<GP>() + WPIX - 1) / WPIX;  // slices per lane
-  constexpr int K = 9;
+  constexpr int K = RC ? 8 : 9;
   static_assert(PASSES == 2, "the pass sequence below assumes two passes");
   static_assert(PIXB % LANE_BYTES == 0 && PIXB % 8 == 0 && PIXB >= GP * 4 * LANE_BYTES, "pixel stride");
   static_assert(GP == 1 || GP == 2, "one or two groups per item");
@@ -157,12 +161,13 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   // offset, for pass 0 (pass 1 adds PIXPP / TW output rows), packed as three
   // 10-bit fields (every coordinate is below the span, at most 1023).  The
   // output pixel of the quad is (pix / TW, pix % TW) within its pass; slot r
-  // holds k = 2 sub + r (r < 2) or k = 8.
+  // holds k = 2 sub + r (r < 2) or k = 8 (no point with RC), at grid index q.
   uint32_t bxp = 0, byp = 0;
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
     const int k = r < 2 ? 2 * (int)sub + r : 8;
-    const int i = k / 3, j = k - 3 * (k / 3);
+    const int q = RC ? (r < 2 ? k + (k >= 4) : 4) : k;
+    const int i = q / 3, j = q - 3 * (q / 3);
     bxp |= (uint32_t)((int)(pix % TW) * SW + R + j * DW) << (10 * r);
     byp |= (uint32_t)((int)(pix / TW) * SH + R + i * DH) << (10 * r);
   }
@@ -271,26 +276,37 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
     if constexpr (DT == DCN_F32) {
       const uint32_t orow = pg * (K * 8), mrow = pg * (K * 4);
       const auto o = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(orow + 16 * sub), 0, 0);
-      const auto o8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 64), 0, 0);
       const auto lg = __builtin_amdgcn_raw_buffer_load_b64(rmask, (int)(mrow + 8 * sub), 0, 0);
       w[0] = o[0];
       w[1] = o[1];
       w[2] = o[2];
       w[3] = o[3];
-      w[4] = o8[0];
-      w[5] = o8[1];
       l[0] = lg[0];
       l[1] = lg[1];
-      l[2] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 32), 0, 0);
+      if constexpr (RC) {
+        w[4] = w[5] = l[2] = 0u;
+      } else {
+        const auto o8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 64), 0, 0);
+        w[4] = o8[0];
+        w[5] = o8[1];
+        l[2] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 32), 0, 0);
+      }
     } else {
       const uint32_t orow = pg * (K * 4), mrow = pg * (K * 2);
       const auto o = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 8 * sub), 0, 0);
       w[0] = o[0];
       w[1] = o[1];
-      w[2] = __builtin_amdgcn_raw_buffer_load_b32(roff, (int)(orow + 32), 0, 0);
-      l[0] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub), 0, 0);
-      l[1] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub + 2), 0, 0);
-      l[2] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 16), 0, 0);
+      if constexpr (RC) {  // 16-byte mask rows: the lane's two logits in one word
+        const uint32_t lw = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 4 * sub), 0, 0);
+        l[0] = lw & 0xffffu;
+        l[1] = lw >> 16;
+        w[2] = l[2] = 0u;
+      } else {
+        w[2] = __builtin_amdgcn_raw_buffer_load_b32(roff, (int)(orow + 32), 0, 0);
+        l[0] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub), 0, 0);
+        l[1] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 4 * sub + 2), 0, 0);
+        l[2] = __builtin_amdgcn_raw_buffer_load_b16(rmask, (int)(mrow + 16), 0, 0);
+      }
     }
   };
   auto issue_pgdata = [&](const Item &I, auto ps_tag) {
@@ -355,12 +371,12 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
       float2 offs[3];
       float lgs[3], m[3];
       decode_rows(rw[ps], rl[ps], offs, lgs);
-      if (sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 only
+      if (RC || sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 only
       if constexpr (SOFTMAX) {
         const float mx = quad_max(fmaxf(fmaxf(lgs[0], lgs[1]), lgs[2]));
         float e[3];
 #pragma unroll
-        for (int r = 0; r < 3; ++r) e[r] = (r < 2 || sub == 0) ? __expf(lgs[r] - mx) : 0.f;
+        for (int r = 0; r < 3; ++r) e[r] = (r < 2 || (!RC && sub == 0)) ? __expf(lgs[r] - mx) : 0.f;
         const float inv = __builtin_amdgcn_rcpf(quad_sum(e[0] + e[1] + e[2]));
 #pragma unroll
         for (int r = 0; r < 3; ++r) m[r] = e[r] * inv;
@@ -466,7 +482,7 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
       };
       round(std::integral_constant<int, 0>{});
       round(std::integral_constant<int, 1>{});
-      round(std::integral_constant<int, 2>{});
+      if constexpr (!RC) round(std::integral_constant<int, 2>{});
       uint32_t outw[NW];
       pack_words<DT, CPL>(acc, outw);
       // Outputs are not read again here: stored non-temporal, so they do not
@@ -511,9 +527,9 @@ size_t tile_lds_bytes(const TileGeom &tg, int pixb) {
   return ((size_t)tg.span_h * tg.span_w + tg.span_w + 2) * pixb;  // window + zero block
 }
 
-template <int DT, bool SM, bool UNIT, int GP>
+template <int DT, bool SM, bool UNIT, int GP, bool RC>
 hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, tile_halo<GP>(), UNIT, GP>;
+  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, tile_halo<GP>(), UNIT, GP, RC>;
   const size_t lds = tile_lds_bytes(tg, tile_pixel_stride<DT, GP>());
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
@@ -530,13 +546,14 @@ hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT, int GP>
+template <int DT, int GP, bool RC>
 hipError_t launch_tile_dt(int softmax, bool unit, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  if (unit) return softmax ? launch_tile<DT, true, true, GP>(p, tg, s) : launch_tile<DT, false, true, GP>(p, tg, s);
+  if (unit)
+    return softmax ? launch_tile<DT, true, true, GP, RC>(p, tg, s) : launch_tile<DT, false, true, GP, RC>(p, tg, s);
   if constexpr (GP == 2) {
     return hipErrorNotSupported;  // strided/dilated windows: one group per item
   } else {
-    return softmax ? launch_tile<DT, true, false, GP>(p, tg, s) : launch_tile<DT, false, false, GP>(p, tg, s);
+    return softmax ? launch_tile<DT, true, false, GP, RC>(p, tg, s) : launch_tile<DT, false, false, GP, RC>(p, tg, s);
   }
 }
 
@@ -578,10 +595,13 @@ hipError_t launch_tile_gp(int dtype, int softmax, const FwdParams &p, hipStream_
   TileGeom tg;
   if (!tile_geometry<GP>(dtype, p, tg)) return hipErrorNotSupported;
   const bool unit = p.SH == 1 && p.SW == 1 && p.DH == 1 && p.DW == 1;
+  if (p.RC) {  // fp32 only: 16-bit rows without the centre go to the lane kernel
+    return dtype == DCN_F32 ? launch_tile_dt<DCN_F32, GP, true>(softmax, unit, p, tg, s) : hipErrorNotSupported;
+  }
   switch (dtype) {
-    case DCN_F32: return launch_tile_dt<DCN_F32, GP>(softmax, unit, p, tg, s);
-    case DCN_F16: return launch_tile_dt<DCN_F16, GP>(softmax, unit, p, tg, s);
-    case DCN_BF16: return launch_tile_dt<DCN_BF16, GP>(softmax, unit, p, tg, s);
+    case DCN_F32: return launch_tile_dt<DCN_F32, GP, false>(softmax, unit, p, tg, s);
+    case DCN_F16: return launch_tile_dt<DCN_F16, GP, false>(softmax, unit, p, tg, s);
+    case DCN_BF16: return launch_tile_dt<DCN_BF16, GP, false>(softmax, unit, p, tg, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -589,10 +609,11 @@ hipError_t launch_tile_gp(int dtype, int softmax, const FwdParams &p, hipStream_
 }  // namespace
 
 // Returns hipErrorNotSupported (nothing launched) when the problem is not a
-// 3x3 one or its window does not fit the LDS budget.  groups_per_item: 1 or
+// 3x3 one (all nine points, or eight without the centre in fp32) or its
+// window does not fit the LDS budget.  groups_per_item: 1 or
 // 2 forces that variant; 0 takes two groups per item where they fit.
 hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipStream_t s, int groups_per_item) {
-  if (p.RC || p.KH != 3 || p.KW != 3) return hipErrorNotSupported;
+  if (p.KH != 3 || p.KW != 3) return hipErrorNotSupported;
   if (groups_per_item != 1) {
     const hipError_t e = launch_tile_gp<2>(dtype, softmax, p, s);
     if (e != hipErrorNotSupported || groups_per_item == 2) return e;
