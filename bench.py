@@ -71,24 +71,29 @@ def backward_bytes(wl) -> int:
 def forward_kernel_name(wl) -> str:
     """Kernel the library runs for this workload's forward (3x3 points,
     stride and dilation 1): the whole-map kernel for output maps smaller than
-    a 16x16 tile or that tiles would leave over half empty (the 12x12 stage),
-    else the quad tiled kernel for fp32 and the lane-per-pixel-group kernel
-    for 16-bit I/O."""
+    a 16x16 tile or that tiles would leave over half empty (the 12x12 stage;
+    not without the centre point), else the quad tiled kernel for fp32 and
+    the lane-per-pixel-group kernel for 16-bit I/O."""
     ho, wo = wl.out_hw
-    if ho * wo < 256 or 2 * ho * wo < ((ho + 15) // 16) * ((wo + 15) // 16) * 256:
+    small = ho * wo < 256 or 2 * ho * wo < ((ho + 15) // 16) * ((wo + 15) // 16) * 256
+    if small and not wl.remove_center:
         return "dcn_fwd_map_kernel"
     return "dcn_fwd_tile_kernel" if wl.dtype == "f32" else "dcn_fwd_lane_kernel"
 
 
-def traffic_from_profile():
+def traffic_from_profile(workload: str):
     """HBM bytes per launch measured by rocprofv3 counters, if the committed
-    counter summary was taken on the current kernel sources."""
+    counter summary was taken on this workload and the current kernel
+    sources."""
     if not COUNTERS.exists():
         return None
     text = COUNTERS.read_text()
+    m_wl = re.search(r"HBM traffic of the forward kernel, workload (\S+)", text)
     m_hash = re.search(r"kernel_source_sha256:\s*(\w+)", text)
     m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_hash and m_val) or m_hash.group(1) != kernel_source_hash():
+    if not (m_wl and m_hash and m_val) or m_wl.group(1) != workload:
+        return None
+    if m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_val.group(1))
 
@@ -211,6 +216,8 @@ def main() -> int:
                     help="images of the batch the CPU oracle runs (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--remove-center", action="store_true",
+                    help="the workload without the kernel's centre point (DCNv4's remove_center)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--cold-iters", type=int, default=50,
@@ -247,6 +254,8 @@ def main() -> int:
     from deformable_convolution_vision_dcn_amd import synth
 
     wl = synth.WORKLOADS[args.workload or synth.HEADLINE]
+    if args.remove_center:
+        wl = wl.replace(name=wl.name + "_remove_center", remove_center=True)
     dev = torch.device("cuda:0")
     print(f"bench: generating {wl.name}", file=sys.stderr, flush=True)
     t = synth.make_inputs(wl, with_grad=True)
@@ -282,7 +291,7 @@ def main() -> int:
     value = wl.samples / (ms_per_step * 1e-3) / 1e9
     fwd_bytes = forward_bytes(wl)
     achieved = fwd_bytes / (launch_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile(wl.name)
 
     result = {
         "metric": METRIC,
@@ -301,7 +310,7 @@ def main() -> int:
                    "groups": wl.groups, "kernel": list(wl.kernel), "stride": list(wl.stride),
                    "pad": list(wl.pad), "dilation": list(wl.dilation),
                    "offset_scale": wl.offset_scale, "softmax": wl.softmax,
-                   "samples_per_step": wl.samples},
+                   "remove_center": wl.remove_center, "samples_per_step": wl.samples},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": forward_kernel_name(wl),
