@@ -393,6 +393,43 @@ def test_backward_16bit_reuses_a_workspace():
         dcn.dcn_backward(x, off, m, gy, workspace=ws[: need - 16], **wl.op_kwargs())
 
 
+def test_backward_16bit_multi_chunk():
+    """A bf16 batch whose fp32 grad_input accumulator exceeds 2 GiB runs as
+    chunks of two images through one workspace; an image of the first and of
+    the second chunk gets the gradients of a one-image call (grad_offset and
+    grad_mask bit for bit, grad_input within one bf16 ulp and the fp32
+    rounding of its partial sums: the order of its fp32 atomics may
+    differ)."""
+    wl = Workload("chunked_bwd16", n=3, h=384, w=384, c=1280, groups=80, dtype="bf16",
+                  offset_dist=normal(1.5), seed=28)
+    img32 = wl.h * wl.w * wl.c * 4
+    assert wl.n * img32 > 2 ** 31 and 2 * img32 < 2 ** 31
+    print("backward chunked bf16 (3 x 384x384x1280)", flush=True)
+    t = synth.make_inputs(wl, with_grad=True)
+    x, off, m, gy = (t[k].to(DEV) for k in ("x", "offset", "mask", "grad_out"))
+    del t
+    kw = wl.op_kwargs()
+    assert dcn.backward_workspace_bytes(x, **kw) == 2 * img32
+    batch = dcn.dcn_backward(x, off, m, gy, **kw)
+    for n in (1, 2):
+        sl = slice(n, n + 1)
+        one = dcn.dcn_backward(x[sl], off[sl], m[sl], gy[sl], **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(batch[1][sl], one[1]), f"grad_offset of image {n}"
+        assert torch.equal(batch[2][sl], one[2]), f"grad_mask of image {n}"
+        a, b = batch[0][sl].float(), one[0].float()
+        # one bf16 ulp of the value, plus the fp32 rounding of partial sums of
+        # magnitude O(10) where the total nearly cancels
+        d = (a - b).abs()
+        bad = d > 2.0 ** -7 * b.abs() + 1e-5
+        assert not bool(bad.any()), (f"grad_input of image {n}: {int(bad.sum())} elements, max diff "
+                                     f"{float(d.max()):.3e}, max |ref| {float(b.abs().max()):.3e}, "
+                                     f"differing {int((d > 0).sum())} of {d.numel()}")
+        del one
+    del batch, x, off, m, gy
+    torch.cuda.empty_cache()
+
+
 def test_autograd_function_matches_backward():
     wl = BWD[0]
     t = synth.make_inputs(wl, with_grad=True)
