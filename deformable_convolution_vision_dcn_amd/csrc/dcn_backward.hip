@@ -13,11 +13,13 @@
 //   grad_mask   : gm_k = sum_c gy_c * B_k[c], then through the softmax
 //                 Jacobian, gl_k = m_k * (gm_k - sum_j m_j gm_j), for DCNv3.
 //
-// Mapping: a quad of lanes per pixel-group, 4 contiguous channels per lane
-// (16-byte corner loads and grad_out loads).  The three per-point channel sums
-// are reduced across the quad with two DPP quad permutes.  The grad_input
-// scatter uses raw buffer atomics: a corner outside the map carries a byte
-// offset beyond the buffer, and the hardware drops that atomic.
+// Mapping of the untiled kernel: 16 lanes per pixel-group, one channel per
+// lane, so a corner gather and a corner scatter are each one 64-byte request
+// per pixel-group (fp32 atomics add one value per lane: with a quad of lanes
+// per pixel-group a corner took four atomic requests).  The three per-point
+// channel sums are reduced over the 16 lanes with four DPP steps.  The
+// grad_input scatter uses raw buffer atomics: a corner outside the map carries
+// a byte offset beyond the buffer, and the hardware drops that atomic.
 #include <stdlib.h>
 #include <string.h>
 
@@ -27,10 +29,11 @@ namespace dcn {
 
 namespace {
 
-constexpr int kQuad = 4;
-
-// Sum of v over the 4 lanes of a quad (DPP quad_perm [1,0,3,2] then [2,3,0,1]).
-__device__ __forceinline__ float quad_sum(float v) {
+// Sum of v over the 16 lanes of a DPP row (rotations by 8 and 4 within the
+// row, then the two quad permutes); every lane of the row gets the total.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
   return v;
@@ -38,12 +41,15 @@ __device__ __forceinline__ float quad_sum(float v) {
 
 }  // namespace
 
+// Untiled backward for any point set, stride and dilation: 16 lanes per
+// pixel-group, one channel per lane (one DPP row), so each corner's gather is
+// one 64-byte request and its grad_input scatter one 64-byte atomic request
+// of the row (a lane per channel: the hardware adds one fp32 per lane).
 template <int KH_, int KW_, bool SOFTMAX>
 __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
   const FwdParams &p = bp.f;
   constexpr int CG = kGroupChannels;
-  constexpr int CPL = CG / kQuad;
-  constexpr int BLOCK_PG = kBlock / kQuad;
+  constexpr int BLOCK_PG = kBlock / CG;
   constexpr bool FIXED = KH_ > 0;
   const int KH = FIXED ? KH_ : p.KH;
   const int KW = FIXED ? KW_ : p.KW;
@@ -61,9 +67,10 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
   stage_to_lds(lds_mask, static_cast<const float *>(p.mask) + (uint64_t)pg0 * K, npg * K * 4);
   __syncthreads();
 
-  const uint32_t lp = threadIdx.x / kQuad;
-  const uint32_t sub = threadIdx.x % kQuad;
-  // Whole quads leave together, so the DPP partners of a live lane are live.
+  const uint32_t lp = threadIdx.x / CG;
+  const uint32_t ch = threadIdx.x % CG;
+  // The 16 lanes of a pixel-group (one DPP row) leave together, so the DPP
+  // partners of a live lane are live.
   if (lp >= npg) return;
   const uint32_t pg = pg0 + lp;
 
@@ -88,14 +95,12 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
     else return lds_mask[mrow + k];
   };
 
-  const float4 gy4 = *reinterpret_cast<const float4 *>(static_cast<const float *>(bp.grad_out) +
-                                                       (uint64_t)pg * CG + sub * CPL);
-  const float gy[CPL] = {gy4.x, gy4.y, gy4.z, gy4.w};
+  const float gy = static_cast<const float *>(bp.grad_out)[(uint64_t)pg * CG + ch];
 
   constexpr uint32_t kBytes = 4;
   const uint32_t pix_bytes = (uint32_t)p.C * kBytes;
   const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
-  const uint32_t base = n * (uint32_t)p.H * row_bytes + (g * CG + sub * CPL) * kBytes;
+  const uint32_t base = n * (uint32_t)p.H * row_bytes + (g * CG + ch) * kBytes;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
   const __amdgpu_buffer_rsrc_t rgx = make_rsrc(bp.grad_in, p.in_bytes);
   const int by = (int)ho * p.SH - p.PH;
@@ -130,44 +135,30 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
     const uint32_t a10 = (vy1 && vx0) ? a00r + row_bytes : kOutOfRange;
     const uint32_t a11 = (vy1 && vx1) ? a00r + row_bytes + pix_bytes : kOutOfRange;
 
-    uint32_t q00[CPL], q01[CPL], q10[CPL], q11[CPL];
-    buffer_load_words<CPL>(rin, a00, q00);
-    buffer_load_words<CPL>(rin, a01, q01);
-    buffer_load_words<CPL>(rin, a10, q10);
-    buffer_load_words<CPL>(rin, a11, q11);
-
-    float gb = 0.f, gdy = 0.f, gdx = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const float v00 = __uint_as_float(q00[c]), v01 = __uint_as_float(q01[c]);
-      const float v10 = __uint_as_float(q10[c]), v11 = __uint_as_float(q11[c]);
-      const float top = hx * v00 + lx * v01;   // row y0 along x
-      const float bot = hx * v10 + lx * v11;   // row y0+1 along x
-      gb = fmaf(gy[c], hy * top + ly * bot, gb);
-      gdy = fmaf(gy[c], bot - top, gdy);
-      gdx = fmaf(gy[c], hy * (v01 - v00) + ly * (v11 - v10), gdx);
-    }
-    gb = quad_sum(gb);
-    gdy = quad_sum(gdy);
-    gdx = quad_sum(gdx);
-    // After the quad sums every lane of the quad holds the same totals; each
-    // lane keeps gm_k in its pixel-group's LDS row (the same value from all
-    // four lanes), lane 0 writes the offset gradient.
-    lds_gm[mrow + k] = nan_loc ? __builtin_nanf("") : gb;
-    if (sub == 0) {
+    const float v00 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (int)a00, 0, 0));
+    const float v01 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (int)a01, 0, 0));
+    const float v10 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (int)a10, 0, 0));
+    const float v11 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (int)a11, 0, 0));
+    const float top = hx * v00 + lx * v01;  // row y0 along x
+    const float bot = hx * v10 + lx * v11;  // row y0+1 along x
+    const float gb = row16_sum(gy * (hy * top + ly * bot));
+    const float gdy = row16_sum(gy * (bot - top));
+    const float gdx = row16_sum(gy * (hy * (v01 - v00) + ly * (v11 - v10)));
+    // Every lane of the row holds the totals: lane 0 keeps gm_k in the
+    // pixel-group's LDS row and writes the offset gradient.
+    if (ch == 0) {
+      lds_gm[mrow + k] = nan_loc ? __builtin_nanf("") : gb;
       goff[k] = nan_loc ? make_float2(__builtin_nanf(""), __builtin_nanf(""))
                         : make_float2(s * mk * gdx, s * mk * gdy);
     }
 
-    // Scatter m_k * w_corner * gy_c into grad_input.
-    const float w00 = mk * hy * hx, w01 = mk * hy * lx, w10 = mk * ly * hx, w11 = mk * ly * lx;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w00 * gy[c], rgx, (int)(a00 + 4u * c), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w01 * gy[c], rgx, (int)(a01 + 4u * c), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w10 * gy[c], rgx, (int)(a10 + 4u * c), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(w11 * gy[c], rgx, (int)(a11 + 4u * c), 0, 0);
-    }
+    // Scatter m_k * w_corner * gy into grad_input (out-of-map corners carry
+    // an offset beyond the buffer, and the hardware drops those atomics).
+    const float g = mk * gy;
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * hy * hx, rgx, (int)a00, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * hy * lx, rgx, (int)a01, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * ly * hx, rgx, (int)a10, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * ly * lx, rgx, (int)a11, 0, 0);
   };
   if constexpr (FIXED) {
 #pragma unroll
@@ -186,19 +177,19 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
   }
 
   // grad_mask: raw gm_k for DCNv4, through the softmax Jacobian for DCNv3.
-  // Lane `sub` of the quad writes the points k = sub, sub+4, ...
+  // Lane ch of the row writes the points k = ch, ch + 16, ... (lane 0's LDS
+  // writes above precede these reads in the wave's program order).
   float dot = 0.f;
   if constexpr (SOFTMAX) {
     for (int k = 0; k < K; ++k) dot = fmaf(weight(k), lds_gm[mrow + k], dot);
   }
   float *gmask = static_cast<float *>(bp.grad_mask) + (uint64_t)pg * K;
-  for (int k = sub; k < K; k += kQuad) {
+  for (int k = (int)ch; k < K; k += CG) {
     const float gmk = lds_gm[mrow + k];
     gmask[k] = SOFTMAX ? weight(k) * (gmk - dot) : gmk;
   }
 }
 
-// Fill nbytes (a multiple of 16) at a 16-byte-aligned address with zeros.
 __global__ void __launch_bounds__(kBlock) dcn_zero_kernel(uint4 *dst, uint64_t n16) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
@@ -220,7 +211,7 @@ namespace {
 
 template <int KH, int KW, bool SM>
 hipError_t launch_one(const BwdParams &p, hipStream_t s) {
-  constexpr int BLOCK_PG = kBlock / kQuad;
+  constexpr int BLOCK_PG = kBlock / kGroupChannels;
   const int K = p.f.KH * p.f.KW - p.f.RC;
   const size_t lds = (size_t)BLOCK_PG * K * 4 * sizeof(float);
   const uint32_t blocks = (p.f.pg_total + BLOCK_PG - 1) / BLOCK_PG;
