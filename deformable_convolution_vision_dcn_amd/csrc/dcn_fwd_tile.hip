@@ -522,14 +522,17 @@ template <int GP>
 constexpr int tile_halo() { return GP == 1 ? DCN_TILE_HALO : DCN_PAIR_HALO; }
 template <int GP>
 constexpr int tile_lds_limit() { return GP == 1 ? 80 * 1024 : 160 * 1024; }
+// One group per item at stride or dilation above 1: the halo taken when the
+// default one overflows the window budget (dilation 2: a 31x31 window).
+constexpr int kTileHaloSmall = 5;
 
 size_t tile_lds_bytes(const TileGeom &tg, int pixb) {
   return ((size_t)tg.span_h * tg.span_w + tg.span_w + 2) * pixb;  // window + zero block
 }
 
-template <int DT, bool SM, bool UNIT, int GP, bool RC>
+template <int DT, bool SM, bool UNIT, int GP, bool RC, int HALO = tile_halo<GP>()>
 hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, tile_halo<GP>(), UNIT, GP, RC>;
+  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, HALO, UNIT, GP, RC>;
   const size_t lds = tile_lds_bytes(tg, tile_pixel_stride<DT, GP>());
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
@@ -547,12 +550,15 @@ hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
 }
 
 template <int DT, int GP, bool RC>
-hipError_t launch_tile_dt(int softmax, bool unit, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
+hipError_t launch_tile_dt(int softmax, bool unit, int halo, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   if (unit)
     return softmax ? launch_tile<DT, true, true, GP, RC>(p, tg, s) : launch_tile<DT, false, true, GP, RC>(p, tg, s);
   if constexpr (GP == 2) {
     return hipErrorNotSupported;  // strided/dilated windows: one group per item
   } else {
+    if (halo == kTileHaloSmall)
+      return softmax ? launch_tile<DT, true, false, GP, RC, kTileHaloSmall>(p, tg, s)
+                     : launch_tile<DT, false, false, GP, RC, kTileHaloSmall>(p, tg, s);
     return softmax ? launch_tile<DT, true, false, GP, RC>(p, tg, s) : launch_tile<DT, false, false, GP, RC>(p, tg, s);
   }
 }
@@ -560,9 +566,8 @@ hipError_t launch_tile_dt(int softmax, bool unit, const FwdParams &p, const Tile
 // Window geometry and work items for GP groups per item; false when the
 // problem does not fit this variant.
 template <int GP>
-bool tile_geometry(int dtype, const FwdParams &p, TileGeom &tg) {
+bool tile_geometry(int dtype, const FwdParams &p, TileGeom &tg, int halo) {
   if (p.G % GP != 0) return false;
-  const int halo = tile_halo<GP>();
   tg = TileGeom{};
   tg.span_h = (kTileH - 1) * p.SH + 2 * p.DH + 2 * halo + 2;
   tg.span_w = (kTileW - 1) * p.SW + 2 * p.DW + 2 * halo + 2;
@@ -593,15 +598,20 @@ bool tile_geometry(int dtype, const FwdParams &p, TileGeom &tg) {
 template <int GP>
 hipError_t launch_tile_gp(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
   TileGeom tg;
-  if (!tile_geometry<GP>(dtype, p, tg)) return hipErrorNotSupported;
   const bool unit = p.SH == 1 && p.SW == 1 && p.DH == 1 && p.DW == 1;
+  int halo = tile_halo<GP>();
+  if (!tile_geometry<GP>(dtype, p, tg, halo)) {
+    if (GP != 1 || unit) return hipErrorNotSupported;
+    halo = kTileHaloSmall;
+    if (!tile_geometry<GP>(dtype, p, tg, halo)) return hipErrorNotSupported;
+  }
   if (p.RC) {  // fp32 only: 16-bit rows without the centre go to the lane kernel
-    return dtype == DCN_F32 ? launch_tile_dt<DCN_F32, GP, true>(softmax, unit, p, tg, s) : hipErrorNotSupported;
+    return dtype == DCN_F32 ? launch_tile_dt<DCN_F32, GP, true>(softmax, unit, halo, p, tg, s) : hipErrorNotSupported;
   }
   switch (dtype) {
-    case DCN_F32: return launch_tile_dt<DCN_F32, GP, false>(softmax, unit, p, tg, s);
-    case DCN_F16: return launch_tile_dt<DCN_F16, GP, false>(softmax, unit, p, tg, s);
-    case DCN_BF16: return launch_tile_dt<DCN_BF16, GP, false>(softmax, unit, p, tg, s);
+    case DCN_F32: return launch_tile_dt<DCN_F32, GP, false>(softmax, unit, halo, p, tg, s);
+    case DCN_F16: return launch_tile_dt<DCN_F16, GP, false>(softmax, unit, halo, p, tg, s);
+    case DCN_BF16: return launch_tile_dt<DCN_BF16, GP, false>(softmax, unit, halo, p, tg, s);
     default: return hipErrorInvalidValue;
   }
 }

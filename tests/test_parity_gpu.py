@@ -102,6 +102,9 @@ PATH_CASES = [
     Workload("path_v4", n=2, h=20, w=17, c=32, groups=2, softmax=False, mask_dist=normal(0.5),
              seed=43),
     Workload("path_pairs", n=2, h=37, w=29, c=96, groups=6, offset_dist=normal(2.5), seed=44),
+    # dilation 2: the one-group tiled kernel with its smaller halo (31x31 window)
+    Workload("path_dil2", n=2, h=37, w=29, c=48, groups=3, dilation=(2, 2), pad=(2, 2),
+             offset_dist=normal(2.0), seed=45),
 ]
 
 
