@@ -107,14 +107,14 @@ int64_t images_per_chunk(const dcn_problem *p, int64_t ho, int64_t wo) {
 }
 
 // The backward's extra checks: 16-bit I/O only for 3x3 points (with or
-// without the centre) at stride and dilation 1, and one image's fp32
+// without the centre) at stride 1 and dilation 1 or 2, and one image's fp32
 // grad_input accumulator below 2^31 bytes.
 int validate_backward(const dcn_problem *p, int64_t *ho, int64_t *wo) {
   const int st = validate(p, ho, wo);
   if (st != DCN_OK) return st;
   if (p->dtype == DCN_F32) return DCN_OK;
   const bool quad_shape = p->kernel_h == 3 && p->kernel_w == 3 && p->stride_h == 1 && p->stride_w == 1 &&
-                          p->dilation_h == 1 && p->dilation_w == 1;
+                          p->dilation_h == p->dilation_w && (p->dilation_h == 1 || p->dilation_h == 2);
   if (!quad_shape) return DCN_ERR_UNSUPPORTED;
   if ((int64_t)p->h * p->w * p->c * 4 > kMaxBytes31) return DCN_ERR_TOO_LARGE;
   return DCN_OK;

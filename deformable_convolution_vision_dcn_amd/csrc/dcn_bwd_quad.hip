@@ -1,8 +1,9 @@
 // dcn_bwd_quad.hip -- LDS-tiled gfx950 backward kernel of the DCN core
 // (fp32 arithmetic for fp32 and 16-bit I/O), a lane quad per pixel-group, for
-// 3x3 kernel points at stride 1 and dilation 1 (the InternImage configuration;
-// wmrh.cn/news/61976, section 二 steps 2-4 and section 三), all nine or the
-// eight left by DCNv4's remove_center (pnsm.cn/news/2029644.html section 3.3).
+// 3x3 kernel points at stride 1 and dilation 1 (the InternImage
+// configuration; wmrh.cn/news/61976, section 二 steps 2-4 and section 三) or
+// 2, all nine or the eight left by DCNv4's remove_center
+// (pnsm.cn/news/2029644.html section 3.3).
 //
 // The derivatives are those of the untiled backward kernel: every in-map
 // corner of a sample receives m_k * w_corner * gy_c; the offset gradient is
@@ -77,7 +78,9 @@ __device__ __forceinline__ int2 pair_sums(uint64_t v) {
 // RC: the centre point is removed (8 points, k -> grid index k + (k >= 4)):
 // each lane owns exactly two points, lane 0's third slot stays empty and the
 // item takes two rounds instead of three.
-template <int DT, bool SOFTMAX, bool RC>
+// DIL: the dilation (1 or 2, both axes).  The window keeps its size: the
+// halo shrinks by one pixel per side at dilation 2.
+template <int DT, bool SOFTMAX, bool RC, int DIL>
 __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams bp, TileGeom tg) {
   const FwdParams &p = bp.f;
   using io = Io<DT>;
@@ -88,7 +91,8 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
   // a caller's fp32 workspace of the input's shape): an input byte address
   // times GX is the same element's address there.
   constexpr uint32_t GX = 4 / EB;
-  constexpr int TS = kBqTile, R = kBqHalo, SPAN_W = kBqSpan;
+  constexpr int TS = kBqTile, R = kBqHalo - (DIL - 1), SPAN_W = kBqSpan;
+  static_assert(DIL == 1 || DIL == 2, "dilation 1 or 2");
   constexpr int SPAN = SPAN_W * SPAN_W;
   constexpr int PIXB = kBqPixB, ROW = kBqRow, LIM = SPAN_W - 2;
   constexpr int CG = kGroupChannels, K = RC ? 8 : 9;
@@ -126,8 +130,8 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
   for (int r = 0; r < 3; ++r) {
     const int k = r < 2 ? 2 * (int)sub + r : 8;
     const int q = RC ? (r < 2 ? k + (k >= 4) : 4) : k;
-    bxp |= (uint32_t)(ox + R + q % 3) << (10 * r);
-    byp |= (uint32_t)(oy + R + q / 3) << (10 * r);
+    bxp |= (uint32_t)(ox + R + (q % 3) * DIL) << (10 * r);
+    byp |= (uint32_t)(oy + R + (q / 3) * DIL) << (10 * r);
   }
   const uint32_t win_chunk = lbase + sub * 16u;          // this lane's 4 channels of a window pixel
   const uint32_t gwin_chunk = lbase + GWIN + sub * 16u;
@@ -587,9 +591,9 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
 
 namespace {
 
-template <int DT, bool SM, bool RC>
+template <int DT, bool SM, bool RC, int DIL>
 hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_bwd_quad_kernel<DT, SM, RC>;
+  auto kern = dcn_bwd_quad_kernel<DT, SM, RC, DIL>;
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBqLds);
@@ -607,12 +611,15 @@ hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s
   return hipGetLastError();
 }
 
-template <bool RC>
+template <bool RC, int DIL>
 hipError_t launch_dt(int dtype, int softmax, const BwdParams &b, const TileGeom &tg, hipStream_t s) {
   switch (dtype) {
-    case DCN_F32: return softmax ? launch_bwd_quad<DCN_F32, true, RC>(b, tg, s) : launch_bwd_quad<DCN_F32, false, RC>(b, tg, s);
-    case DCN_F16: return softmax ? launch_bwd_quad<DCN_F16, true, RC>(b, tg, s) : launch_bwd_quad<DCN_F16, false, RC>(b, tg, s);
-    case DCN_BF16: return softmax ? launch_bwd_quad<DCN_BF16, true, RC>(b, tg, s) : launch_bwd_quad<DCN_BF16, false, RC>(b, tg, s);
+    case DCN_F32:
+      return softmax ? launch_bwd_quad<DCN_F32, true, RC, DIL>(b, tg, s) : launch_bwd_quad<DCN_F32, false, RC, DIL>(b, tg, s);
+    case DCN_F16:
+      return softmax ? launch_bwd_quad<DCN_F16, true, RC, DIL>(b, tg, s) : launch_bwd_quad<DCN_F16, false, RC, DIL>(b, tg, s);
+    case DCN_BF16:
+      return softmax ? launch_bwd_quad<DCN_BF16, true, RC, DIL>(b, tg, s) : launch_bwd_quad<DCN_BF16, false, RC, DIL>(b, tg, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -620,10 +627,10 @@ hipError_t launch_dt(int dtype, int softmax, const BwdParams &b, const TileGeom 
 }  // namespace
 
 // 3x3 points (all nine, or eight without the centre), stride 1, dilation 1
-// only; hipErrorNotSupported otherwise.
+// or 2 (the same on both axes) only; hipErrorNotSupported otherwise.
 hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipStream_t s) {
   const FwdParams &p = b.f;
-  if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
+  if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != p.DW || (p.DH != 1 && p.DH != 2))
     return hipErrorNotSupported;
   TileGeom tg{};
   tg.span_h = tg.span_w = kBqSpan;
@@ -638,7 +645,9 @@ hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipS
   tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
-  return p.RC ? launch_dt<true>(dtype, softmax, b, tg, s) : launch_dt<false>(dtype, softmax, b, tg, s);
+  if (p.DH == 2)
+    return p.RC ? launch_dt<true, 2>(dtype, softmax, b, tg, s) : launch_dt<false, 2>(dtype, softmax, b, tg, s);
+  return p.RC ? launch_dt<true, 1>(dtype, softmax, b, tg, s) : launch_dt<false, 1>(dtype, softmax, b, tg, s);
 }
 
 }  // namespace dcn

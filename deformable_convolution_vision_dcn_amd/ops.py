@@ -201,6 +201,6 @@ class DCNCore(torch.autograd.Function):
 def dcn_core(x, offset, mask, *, groups, kernel=3, stride=1, pad=1, dilation=1,
              offset_scale=2.0, softmax=True, remove_center=False):
     """Differentiable DCN core (backward in the HIP library: fp32, or 16-bit for
-    3x3 points at stride and dilation 1)."""
+    3x3 points at stride 1 and dilation 1 or 2)."""
     return DCNCore.apply(x, offset, mask, groups, kernel, stride, pad, dilation, offset_scale,
                          softmax, remove_center)

@@ -80,7 +80,7 @@ typedef enum dcn_status {
                                  point left (1x1 with remove_center)                   */
     DCN_ERR_UNSUPPORTED = -3, /* dtype, channels-per-group or point count (K > 64)
                                  without a kernel, or a 16-bit backward other than
-                                 3x3 points at stride and dilation 1                   */
+                                 3x3 points at stride 1, dilation 1 or 2               */
     DCN_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                */
     DCN_ERR_TOO_LARGE = -5,   /* one image's input, output or offset tensor exceeds
                                  2^31-1 bytes, or H or W exceeds 2^24 (16-bit
@@ -137,7 +137,8 @@ int dcn_backward_workspace_size(const dcn_problem *p, uint64_t *bytes);
  * At integer sampling coordinates the derivative is the one-sided one from the
  * right (the floor convention).  fp32 for every shape.  16-bit I/O (all
  * tensors of the call in that dtype) for 3x3 points (remove_center or not)
- * at stride and dilation 1, else DCN_ERR_UNSUPPORTED.  The arithmetic is fp32 throughout and grad_input
+ * at stride 1 and dilation 1 or 2 (equal on both axes), else
+ * DCN_ERR_UNSUPPORTED.  The arithmetic is fp32 throughout and grad_input
  * is accumulated in fp32: sums per output tile in fixed point, added with
  * fp32 atomics (so its low bits can vary from run to run).  For fp32 the sums
  * land in grad_input itself (the call zeroes it first) and workspace may be

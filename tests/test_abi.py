@@ -176,6 +176,10 @@ def test_argument_checks_before_any_device_call(lib):
     assert _capi.dcn_backward_workspace_size(prc16) == (0, need)
     prc16s = _capi.make_problem(**{**BASE, "remove_center": 1, "dtype": _capi.DCN_F16, "stride_w": 2})
     assert _capi.dcn_backward_workspace_size(prc16s)[0] == _capi.CODES["DCN_ERR_UNSUPPORTED"]
+    # dilation 2 on both axes: supported in 16-bit
+    pd16 = _capi.make_problem(**{**BASE, "dtype": _capi.DCN_BF16, "dilation_h": 2, "dilation_w": 2,
+                                 "pad_h": 2, "pad_w": 2})
+    assert _capi.dcn_backward_workspace_size(pd16) == (0, need)
     # N = 0: valid, nothing enqueued, pointers may be NULL
     p0 = _capi.make_problem(**{**BASE, "n": 0})
     assert F(p0, None, None, None, None, None) == 0

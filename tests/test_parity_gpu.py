@@ -235,6 +235,8 @@ BWD = [
              remove_center=True, seed=39),
     Workload("bwd_rc_k3x5", n=1, h=9, w=11, c=16, groups=1, kernel=(3, 5), pad=(1, 2),
              remove_center=True, seed=40),
+    Workload("bwd_dil2", n=2, h=37, w=29, c=48, groups=3, dilation=(2, 2), pad=(2, 2),
+             offset_dist=normal(2.0), seed=41),
 ]
 
 
@@ -273,7 +275,8 @@ BWD_PATH_CASES = [
 
 
 @pytest.mark.parametrize("path", ["generic", "tiled", "quad"])
-@pytest.mark.parametrize("wl", BWD_PATH_CASES + [BWD_PATH_CASES[0].replace(name="bwdp_rc", remove_center=True)],
+@pytest.mark.parametrize("wl", BWD_PATH_CASES + [BWD_PATH_CASES[0].replace(name="bwdp_rc", remove_center=True),
+                                BWD_PATH_CASES[1].replace(name="bwdp_dil2_far", dilation=(2, 2), pad=(2, 2))],
                          ids=lambda w: w.name)
 def test_backward_each_kernel(wl, path, monkeypatch):
     """Every backward kernel, forced in turn, on multi-tile ragged shapes
@@ -298,15 +301,17 @@ BWD16 = [
              remove_center=True, seed=66),
     Workload("bwd16_rc_far", n=1, h=37, w=29, c=48, groups=3, offset_dist=uniform(5.0),
              remove_center=True, seed=67),
+    Workload("bwd16_dil2", n=2, h=30, w=35, c=32, groups=2, dilation=(2, 2), pad=(2, 2),
+             offset_dist=normal(2.0), seed=68),
 ]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("wl", BWD16, ids=lambda w: w.name)
 def test_backward_16bit(wl, dtype):
-    """16-bit backward (3x3 with or without the centre, stride and dilation 1)
-    against the oracle on the same 16-bit inputs, with the 16-bit gate on all
-    three gradients."""
+    """16-bit backward (3x3 with or without the centre, stride 1, dilation 1
+    or 2) against the oracle on the same 16-bit inputs, with the 16-bit gate
+    on all three gradients."""
     wl = wl.replace(dtype=dtype)
     print(f"backward {wl.name} {dtype}", flush=True)
     t = synth.make_inputs(wl, with_grad=True)

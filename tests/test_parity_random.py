@@ -84,13 +84,14 @@ def test_random_backward_every_kernel(seed, monkeypatch):
 
 def random_problem_16(seed: int) -> Workload:
     """A draw of random_problem with the shape the 16-bit backward covers:
-    3x3 points at stride and dilation 1 (every third without the centre),
-    f16 or bf16."""
+    3x3 points at stride 1 (every third without the centre, every fourth at
+    dilation 2), f16 or bf16."""
     wl = random_problem(100 + seed)
+    dil = 2 if seed % 4 == 1 else 1
     return wl.replace(name=f"rand16_{seed}", dtype=("f16", "bf16")[seed % 2], kernel=(3, 3),
-                      remove_center=seed % 3 == 2,
-                      stride=(1, 1), dilation=(1, 1), h=max(wl.h, 3 - 2 * wl.pad[0]),
-                      w=max(wl.w, 3 - 2 * wl.pad[1]))
+                      remove_center=seed % 3 == 2, dilation=(dil, dil),
+                      stride=(1, 1), h=max(wl.h, 2 * dil + 1 - 2 * wl.pad[0]),
+                      w=max(wl.w, 2 * dil + 1 - 2 * wl.pad[1]))
 
 
 @pytest.mark.parametrize("seed", range(16))
