@@ -34,11 +34,13 @@ namespace dcn {
 #define DCN_LANE_HALO 6
 #endif
 
-constexpr int kLaneTile = 16;                 // output tile edge
 constexpr int kLaneHalo = DCN_LANE_HALO;      // window halo for the offsets
-constexpr int kLaneSpanUnit = kLaneTile + 2 * kLaneHalo + 3;
-constexpr int kLaneThreads = kLaneTile * kLaneTile;
-constexpr int kLaneMaxSpan = 1024;
+// Output tiles: 16x16 (256 lanes), or 24x8 (192 lanes, three waves) for
+// maps 24 pixels wide, which 16x16 tiles would leave 44 % empty.
+template <int TW, int TH>
+constexpr int lane_lds_bytes(int pixb) {
+  return ((TW + 2 * kLaneHalo + 3) * (TH + 2 * kLaneHalo + 3) + (TW + 2 * kLaneHalo + 3) + 2) * pixb;
+}
 
 template <int DT>
 constexpr int lane_pixel_stride() { return DT == DCN_F32 ? 64 : 32; }
@@ -56,31 +58,32 @@ __device__ __forceinline__ void lds_read16(const unsigned char *src, uint32_t (&
 }  // namespace
 
 // RC: the centre point is removed (8 points; point k sits at grid index
-// k + (k >= 4)).
-template <int DT, bool SOFTMAX, bool RC>
+// k + (k >= 4)).  TW x TH: the output tile, one lane per pixel.
+template <int DT, bool SOFTMAX, bool RC, int TW, int TH>
 #ifndef DCN_LANE_WAVES
 #define DCN_LANE_WAVES 2  // waves per SIMD the register budget must allow
 #endif
-__global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_kernel(FwdParams p, TileGeom tg) {
+__global__ void __launch_bounds__(TW * TH, DCN_LANE_WAVES) dcn_fwd_lane_kernel(FwdParams p, TileGeom tg) {
   using io = Io<DT>;
-  constexpr int TS = kLaneTile, R = kLaneHalo, SPAN_W = kLaneSpanUnit;
+  constexpr int THREADS = TW * TH, R = kLaneHalo;
+  constexpr int SPAN_W = TW + 2 * R + 3, SPAN_H = TH + 2 * R + 3;
   constexpr int CG = kGroupChannels;
   constexpr int PIXB = lane_pixel_stride<DT>();   // one pixel's 16-channel slice
   constexpr int CHUNK = 16;                        // bytes per ds_read_b128
   constexpr int NCH = PIXB / CHUNK;                // chunks per slice: 4 (fp32) or 2
   constexpr int CPC = CHUNK / io::kBytes;          // channels per chunk: 4 or 8
   constexpr int ROW = SPAN_W * PIXB;               // LDS bytes per window row
-  constexpr int SPAN = SPAN_W * SPAN_W;
-  constexpr int QUADS = kLaneThreads / NCH;        // lanes groups staging one pixel each
+  constexpr int SPAN = SPAN_W * SPAN_H;
+  constexpr int QUADS = THREADS / NCH;             // lanes groups staging one pixel each
   constexpr int SLOTS = (SPAN + QUADS - 1) / QUADS;
-  constexpr int LIM = SPAN_W - 2;
+  constexpr int LIM_X = SPAN_W - 2, LIM_Y = SPAN_H - 2;
   constexpr int ZERO = SPAN * PIXB;
   constexpr int K = RC ? 8 : 9;
 
   extern __shared__ __align__(16) unsigned char tile[];
 
   const uint32_t lane = threadIdx.x;
-  const int oy = (int)lane / TS, ox = (int)lane % TS;
+  const int oy = (int)lane / TW, ox = (int)lane % TW;
   const uint32_t pix_bytes = (uint32_t)p.C * io::kBytes;
   const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
@@ -88,7 +91,7 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
   const float s = p.scale;
 
   // Zero block after the window (written once; ordered by the first barrier).
-  for (int z = (int)lane * 16; z < ROW + 2 * PIXB; z += kLaneThreads * 16)
+  for (int z = (int)lane * 16; z < ROW + 2 * PIXB; z += THREADS * 16)
     *reinterpret_cast<uint4 *>(tile + ZERO + z) = make_uint4(0, 0, 0, 0);
 
   // Staging: NCH lanes per pixel, SLOTS pixels per lane group.
@@ -108,7 +111,7 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
     const uint32_t tile_id = t - I.n * (uint32_t)tg.tiles_per_img;
     const uint32_t tyi = fast_div(tile_id, tg.div_tiles_x);
     const uint32_t txi = tile_id - tyi * (uint32_t)tg.tiles_x;
-    const int r0 = (int)tyi * TS, c0 = (int)txi * TS;
+    const int r0 = (int)tyi * TH, c0 = (int)txi * TW;
     I.Y0 = r0 - p.PH - R;  // window origin (stride and dilation 1)
     I.X0 = c0 - p.PW - R;
     I.ho = r0 + oy;
@@ -232,7 +235,7 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
         const float wy0 = (1.f - ly) * mk, wy1 = ly * mk;
         const float w00 = wy0 * (1.f - lx), w01 = wy0 * lx;
         const float w10 = wy1 * (1.f - lx), w11 = wy1 * lx;
-        const bool inside = !nan_loc && (uint32_t)ty <= (uint32_t)LIM && (uint32_t)tx <= (uint32_t)LIM;
+        const bool inside = !nan_loc && (uint32_t)ty <= (uint32_t)LIM_Y && (uint32_t)tx <= (uint32_t)LIM_X;
         const int A = inside ? ty * ROW + tx * PIXB : ZERO;
         const unsigned char *src = tile + A;
 #pragma unroll
@@ -311,11 +314,11 @@ __global__ void __launch_bounds__(kLaneThreads, DCN_LANE_WAVES) dcn_fwd_lane_ker
 
 namespace {
 
-template <int DT, bool SM, bool RC>
+template <int DT, bool SM, bool RC, int TW, int TH>
 hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_fwd_lane_kernel<DT, SM, RC>;
-  constexpr int PIXB = lane_pixel_stride<DT>();
-  const size_t lds = ((size_t)kLaneSpanUnit * kLaneSpanUnit + kLaneSpanUnit + 2) * PIXB;
+  auto kern = dcn_fwd_lane_kernel<DT, SM, RC, TW, TH>;
+  constexpr int THREADS = TW * TH;
+  const size_t lds = lane_lds_bytes<TW, TH>(lane_pixel_stride<DT>());
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -328,22 +331,35 @@ hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   // and LDS permitting), so no block waits for another to finish.
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern),
-                                                   kLaneThreads, lds);
+                                                   THREADS, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorNotSupported;
   const uint32_t blocks = std::min<uint32_t>(tg.items, (uint32_t)per_cu * (uint32_t)cus);
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kLaneThreads), lds, s, p, tg);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(THREADS), lds, s, p, tg);
   return hipGetLastError();
 }
 
-template <bool RC>
+template <bool RC, int TW, int TH>
 hipError_t launch_lane_dt(int dtype, int softmax, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   switch (dtype) {
-    case DCN_F32: return softmax ? launch_lane<DCN_F32, true, RC>(p, tg, s) : launch_lane<DCN_F32, false, RC>(p, tg, s);
-    case DCN_F16: return softmax ? launch_lane<DCN_F16, true, RC>(p, tg, s) : launch_lane<DCN_F16, false, RC>(p, tg, s);
-    case DCN_BF16: return softmax ? launch_lane<DCN_BF16, true, RC>(p, tg, s) : launch_lane<DCN_BF16, false, RC>(p, tg, s);
+    case DCN_F32:
+      if constexpr (TW == 16) {  // the 24x8 tile is 16-bit only (fp32 would need 19 window slots per lane)
+        return softmax ? launch_lane<DCN_F32, true, RC, TW, TH>(p, tg, s) : launch_lane<DCN_F32, false, RC, TW, TH>(p, tg, s);
+      } else {
+        return hipErrorNotSupported;
+      }
+    case DCN_F16:
+      return softmax ? launch_lane<DCN_F16, true, RC, TW, TH>(p, tg, s) : launch_lane<DCN_F16, false, RC, TW, TH>(p, tg, s);
+    case DCN_BF16:
+      return softmax ? launch_lane<DCN_BF16, true, RC, TW, TH>(p, tg, s) : launch_lane<DCN_BF16, false, RC, TW, TH>(p, tg, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Share of the tiles' lanes that hold an output pixel.
+double lane_use(const FwdParams &p, int tw, int th) {
+  const double tiled = (double)((p.Ho + th - 1) / th) * th * (double)((p.Wo + tw - 1) / tw) * tw;
+  return (double)p.Ho * p.Wo / tiled;
 }
 
 }  // namespace
@@ -352,10 +368,14 @@ hipError_t launch_lane_dt(int dtype, int softmax, const FwdParams &p, const Tile
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
   if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
     return hipErrorNotSupported;
+  // 24x8 tiles (16-bit) where they leave clearly fewer lanes idle than 16x16
+  const bool wide = dtype != DCN_F32 && lane_use(p, 24, 8) > lane_use(p, 16, 16) + 0.1;
+  const int tw = wide ? 24 : 16, th = wide ? 8 : 16;
   TileGeom tg{};
-  tg.span_h = tg.span_w = kLaneSpanUnit;
-  const int tiles_y = (p.Ho + kLaneTile - 1) / kLaneTile;
-  tg.tiles_x = (p.Wo + kLaneTile - 1) / kLaneTile;
+  tg.span_w = tw + 2 * kLaneHalo + 3;
+  tg.span_h = th + 2 * kLaneHalo + 3;
+  const int tiles_y = (p.Ho + th - 1) / th;
+  tg.tiles_x = (p.Wo + tw - 1) / tw;
   tg.tiles_per_img = tiles_y * tg.tiles_x;
   const int64_t imgs = p.pg_total / ((int64_t)p.Ho * p.Wo * p.G);
   const int64_t items = imgs * tg.tiles_per_img * p.G;
@@ -365,7 +385,9 @@ hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipSt
   tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
-  return p.RC ? launch_lane_dt<true>(dtype, softmax, p, tg, s) : launch_lane_dt<false>(dtype, softmax, p, tg, s);
+  if (wide)
+    return p.RC ? launch_lane_dt<true, 24, 8>(dtype, softmax, p, tg, s) : launch_lane_dt<false, 24, 8>(dtype, softmax, p, tg, s);
+  return p.RC ? launch_lane_dt<true, 16, 16>(dtype, softmax, p, tg, s) : launch_lane_dt<false, 16, 16>(dtype, softmax, p, tg, s);
 }
 
 }  // namespace dcn

@@ -105,6 +105,8 @@ PATH_CASES = [
     # dilation 2: the one-group tiled kernel with its smaller halo (31x31 window)
     Workload("path_dil2", n=2, h=37, w=29, c=48, groups=3, dilation=(2, 2), pad=(2, 2),
              offset_dist=normal(2.0), seed=45),
+    # 24 wide, 41 high: 16-bit lane kernel with 24x8 tiles (the last tile row holds one row)
+    Workload("path_24wide", n=2, h=41, w=24, c=48, groups=3, offset_dist=uniform(4.0), seed=46),
 ]
 
 
