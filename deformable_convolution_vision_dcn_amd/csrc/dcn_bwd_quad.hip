@@ -43,17 +43,24 @@ namespace dcn {
 #ifndef DCN_BQ_HALO
 #define DCN_BQ_HALO 7
 #endif
-constexpr int kBqTile = 16;
 constexpr int kBqHalo = DCN_BQ_HALO;
-constexpr int kBqSpan = kBqTile + 2 * kBqHalo + 3;        // window edge, pixels
 constexpr int kBqPixB = 64;                               // 16 fp32 channels
-constexpr int kBqRow = kBqSpan * kBqPixB;                 // LDS bytes per window row
-constexpr int kBqWin = kBqSpan * kBqSpan * kBqPixB;       // one window
-constexpr int kBqZero = kBqRow + 2 * kBqPixB;             // zero block after the input window
-constexpr int kBqThreads = 1024;
-constexpr int kBqWaves = kBqThreads / 64;
-constexpr int kBqSink = kBqRow + 2 * kBqPixB;             // scatter sink after the grad window
-constexpr size_t kBqLds = (size_t)kBqWin + kBqZero + kBqWin + kBqSink + 4 * kBqWaves;
+
+// Block geometry for TW x TH output tiles (a quad per pixel): 16x16 (1024
+// threads), or 24x8 (768 threads) for maps 24 pixels wide, which 16x16 tiles
+// would leave 44 % empty.
+template <int TW, int TH>
+struct BqGeom {
+  static constexpr int kThreads = 4 * TW * TH;
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kSpanW = TW + 2 * kBqHalo + 3;     // window edges, pixels
+  static constexpr int kSpanH = TH + 2 * kBqHalo + 3;
+  static constexpr int kRow = kSpanW * kBqPixB;           // LDS bytes per window row
+  static constexpr int kWin = kSpanW * kSpanH * kBqPixB;  // one window
+  static constexpr int kZero = kRow + 2 * kBqPixB;        // zero block after the input window
+  static constexpr int kSink = kRow + 2 * kBqPixB;        // scatter sink after the grad window
+  static constexpr size_t kLds = (size_t)kWin + kZero + kWin + kSink + 4 * kWaves;
+};
 
 namespace {
 
@@ -80,8 +87,9 @@ __device__ __forceinline__ int2 pair_sums(uint64_t v) {
 // item takes two rounds instead of three.
 // DIL: the dilation (1 or 2, both axes).  The window keeps its size: the
 // halo shrinks by one pixel per side at dilation 2.
-template <int DT, bool SOFTMAX, bool RC, int DIL>
-__global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams bp, TileGeom tg) {
+template <int DT, bool SOFTMAX, bool RC, int DIL, int TW, int TH>
+__global__ void __launch_bounds__(4 * TW * TH, TW * TH / 64) dcn_bwd_quad_kernel(BwdParams bp, TileGeom tg) {
+  using G = BqGeom<TW, TH>;
   const FwdParams &p = bp.f;
   using io = Io<DT>;
   constexpr int EB = io::kBytes;         // bytes per element in memory
@@ -91,26 +99,26 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
   // a caller's fp32 workspace of the input's shape): an input byte address
   // times GX is the same element's address there.
   constexpr uint32_t GX = 4 / EB;
-  constexpr int TS = kBqTile, R = kBqHalo - (DIL - 1), SPAN_W = kBqSpan;
+  constexpr int R = kBqHalo - (DIL - 1), SPAN_W = G::kSpanW, SPAN_H = G::kSpanH;
   static_assert(DIL == 1 || DIL == 2, "dilation 1 or 2");
-  constexpr int SPAN = SPAN_W * SPAN_W;
-  constexpr int PIXB = kBqPixB, ROW = kBqRow, LIM = SPAN_W - 2;
+  constexpr int SPAN = SPAN_W * SPAN_H;
+  constexpr int PIXB = kBqPixB, ROW = G::kRow, LIM_X = SPAN_W - 2, LIM_Y = SPAN_H - 2;
   constexpr int CG = kGroupChannels, K = RC ? 8 : 9;
   constexpr int ROUNDS = RC ? 2 : 3;
-  constexpr int WPIX = kBqThreads / 4;                   // window pixels per staging slice
+  constexpr int WPIX = G::kThreads / 4;                  // window pixels per staging slice
   constexpr int SLOTS = (SPAN + WPIX - 1) / WPIX;
-  constexpr uint32_t ZERO = kBqWin;                      // zero block (reads of outside samples)
-  constexpr uint32_t GWIN = kBqWin + kBqZero;            // fixed-point grad window
-  constexpr uint32_t SINK = GWIN + kBqWin;               // scatter target of samples not in the window
+  constexpr uint32_t ZERO = G::kWin;                     // zero block (reads of outside samples)
+  constexpr uint32_t GWIN = G::kWin + G::kZero;          // fixed-point grad window
+  constexpr uint32_t SINK = GWIN + G::kWin;              // scatter target of samples not in the window
   static_assert(CG == 16, "a quad covers 16 channels");
 
   extern __shared__ __align__(16) unsigned char lds[];
   typedef __attribute__((address_space(3))) unsigned char lds_byte;
   const uint32_t lbase = (uint32_t)(size_t)(lds_byte *)lds;
-  float *wave_sums = reinterpret_cast<float *>(lds + SINK + kBqSink);
+  float *wave_sums = reinterpret_cast<float *>(lds + SINK + G::kSink);
 
   const uint32_t quad = threadIdx.x >> 2, sub = threadIdx.x & 3;
-  const int oy = (int)quad / TS, ox = (int)quad % TS;  // output pixel within the tile
+  const int oy = (int)quad / TW, ox = (int)quad % TW;  // output pixel within the tile
   const uint32_t pix_bytes = (uint32_t)p.C * EB;
   const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
@@ -139,9 +147,9 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
   // The grad window starts at zero; every item's flush clears it again.  The
   // zero block after the input window is written once.  The first barrier of
   // the item loop orders both.
-  for (uint32_t z = threadIdx.x * 16u; z < (uint32_t)kBqWin; z += kBqThreads * 16u)
+  for (uint32_t z = threadIdx.x * 16u; z < (uint32_t)G::kWin; z += G::kThreads * 16u)
     *reinterpret_cast<uint4 *>(lds + GWIN + z) = make_uint4(0, 0, 0, 0);
-  for (uint32_t z = threadIdx.x * 16u; z < (uint32_t)kBqZero; z += kBqThreads * 16u)
+  for (uint32_t z = threadIdx.x * 16u; z < (uint32_t)G::kZero; z += G::kThreads * 16u)
     *reinterpret_cast<uint4 *>(lds + ZERO + z) = make_uint4(0, 0, 0, 0);
 
   struct Item {
@@ -157,7 +165,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
     const uint32_t tile_id = t - I.n * (uint32_t)tg.tiles_per_img;
     const uint32_t tyi = fast_div(tile_id, tg.div_tiles_x);
     const uint32_t txi = tile_id - tyi * (uint32_t)tg.tiles_x;
-    const int r0 = (int)tyi * TS, c0 = (int)txi * TS;
+    const int r0 = (int)tyi * TH, c0 = (int)txi * TW;
     I.Y0 = r0 - p.PH - R;  // window origin in input coordinates
     I.X0 = c0 - p.PW - R;
     I.img = I.n * (uint32_t)p.H * row_bytes;
@@ -322,7 +330,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
 
     float B = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < kBqWaves; ++wv) B += wave_sums[wv];
+    for (int wv = 0; wv < G::kWaves; ++wv) B += wave_sums[wv];
     const bool fixed = B <= 3.0e38f;  // false for Inf and NaN (block-uniform)
     int ex = 0;
     frexpf(B, &ex);
@@ -357,7 +365,7 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
       const float hx = 1.f - lx, hy = 1.f - ly;
       const int tx = (int)((bxp >> (10 * r)) & 1023u) + (int)fx;  // window coordinates
       const int ty = (int)((byp >> (10 * r)) & 1023u) + (int)fy;
-      const bool inside = cur.live && !nan_loc && (uint32_t)ty <= (uint32_t)LIM && (uint32_t)tx <= (uint32_t)LIM;
+      const bool inside = cur.live && !nan_loc && (uint32_t)ty <= (uint32_t)LIM_Y && (uint32_t)tx <= (uint32_t)LIM_X;
       const uint32_t A = inside ? mad24((uint32_t)ty, (uint32_t)ROW, mul24((uint32_t)tx, PIXB)) : ZERO;
       const float wy1 = ly * mk, wy0 = mk - wy1;
       const float W1 = wy0 * lx, W0 = wy0 - W1;
@@ -554,9 +562,9 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
     // 64-byte request), and clear it for the next item.  Pixels outside the
     // map and zero sums are skipped.
     {
-      // Pixel idx = threadIdx.x / 16 + 64 j of the window, its row, column
+      // Pixel idx = threadIdx.x / 16 + STEP j of the window, its row, column
       // and grad_input offset walked incrementally.
-      constexpr int STEP = kBqThreads / 16;
+      constexpr int STEP = G::kThreads / 16;
       constexpr int DY = STEP / SPAN_W, DX = STEP % SPAN_W;
       const uint32_t ch = threadIdx.x & 15u;
       int idx = (int)(threadIdx.x >> 4);
@@ -591,37 +599,47 @@ __global__ void __launch_bounds__(kBqThreads, 4) dcn_bwd_quad_kernel(BwdParams b
 
 namespace {
 
-template <int DT, bool SM, bool RC, int DIL>
+template <int DT, bool SM, bool RC, int DIL, int TW, int TH>
 hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_bwd_quad_kernel<DT, SM, RC, DIL>;
+  using G = BqGeom<TW, TH>;
+  auto kern = dcn_bwd_quad_kernel<DT, SM, RC, DIL, TW, TH>;
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBqLds);
+      reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
   if (attr != hipSuccess) return attr;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), kBqThreads,
-                                                     kBqLds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), G::kThreads,
+                                                     G::kLds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorNotSupported;
   const uint32_t blocks = std::min<uint32_t>(tg.items, (uint32_t)per_cu * (uint32_t)cus);
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kBqThreads), kBqLds, s, p, tg);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(G::kThreads), G::kLds, s, p, tg);
   return hipGetLastError();
 }
 
-template <bool RC, int DIL>
+template <bool RC, int DIL, int TW, int TH>
 hipError_t launch_dt(int dtype, int softmax, const BwdParams &b, const TileGeom &tg, hipStream_t s) {
   switch (dtype) {
     case DCN_F32:
-      return softmax ? launch_bwd_quad<DCN_F32, true, RC, DIL>(b, tg, s) : launch_bwd_quad<DCN_F32, false, RC, DIL>(b, tg, s);
+      return softmax ? launch_bwd_quad<DCN_F32, true, RC, DIL, TW, TH>(b, tg, s)
+                     : launch_bwd_quad<DCN_F32, false, RC, DIL, TW, TH>(b, tg, s);
     case DCN_F16:
-      return softmax ? launch_bwd_quad<DCN_F16, true, RC, DIL>(b, tg, s) : launch_bwd_quad<DCN_F16, false, RC, DIL>(b, tg, s);
+      return softmax ? launch_bwd_quad<DCN_F16, true, RC, DIL, TW, TH>(b, tg, s)
+                     : launch_bwd_quad<DCN_F16, false, RC, DIL, TW, TH>(b, tg, s);
     case DCN_BF16:
-      return softmax ? launch_bwd_quad<DCN_BF16, true, RC, DIL>(b, tg, s) : launch_bwd_quad<DCN_BF16, false, RC, DIL>(b, tg, s);
+      return softmax ? launch_bwd_quad<DCN_BF16, true, RC, DIL, TW, TH>(b, tg, s)
+                     : launch_bwd_quad<DCN_BF16, false, RC, DIL, TW, TH>(b, tg, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Share of the tiles' pixels that are output pixels.
+double quad_tile_use(const FwdParams &p, int tw, int th) {
+  const double tiled = (double)((p.Ho + th - 1) / th) * th * (double)((p.Wo + tw - 1) / tw) * tw;
+  return (double)p.Ho * p.Wo / tiled;
 }
 
 }  // namespace
@@ -632,10 +650,14 @@ hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipS
   const FwdParams &p = b.f;
   if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != p.DW || (p.DH != 1 && p.DH != 2))
     return hipErrorNotSupported;
+  // 24x8 tiles (dilation 1) where they leave clearly fewer quads idle
+  const bool wide = p.DH == 1 && quad_tile_use(p, 24, 8) > quad_tile_use(p, 16, 16) + 0.1;
+  const int tw = wide ? 24 : 16, th = wide ? 8 : 16;
   TileGeom tg{};
-  tg.span_h = tg.span_w = kBqSpan;
-  const int tiles_y = (p.Ho + kBqTile - 1) / kBqTile;
-  tg.tiles_x = (p.Wo + kBqTile - 1) / kBqTile;
+  tg.span_w = tw + 2 * kBqHalo + 3;
+  tg.span_h = th + 2 * kBqHalo + 3;
+  const int tiles_y = (p.Ho + th - 1) / th;
+  tg.tiles_x = (p.Wo + tw - 1) / tw;
   tg.tiles_per_img = tiles_y * tg.tiles_x;
   const int64_t imgs = p.pg_total / ((int64_t)p.Ho * p.Wo * p.G);
   const int64_t items = imgs * tg.tiles_per_img * p.G;
@@ -646,8 +668,10 @@ hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipS
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
   if (p.DH == 2)
-    return p.RC ? launch_dt<true, 2>(dtype, softmax, b, tg, s) : launch_dt<false, 2>(dtype, softmax, b, tg, s);
-  return p.RC ? launch_dt<true, 1>(dtype, softmax, b, tg, s) : launch_dt<false, 1>(dtype, softmax, b, tg, s);
+    return p.RC ? launch_dt<true, 2, 16, 16>(dtype, softmax, b, tg, s) : launch_dt<false, 2, 16, 16>(dtype, softmax, b, tg, s);
+  if (wide)
+    return p.RC ? launch_dt<true, 1, 24, 8>(dtype, softmax, b, tg, s) : launch_dt<false, 1, 24, 8>(dtype, softmax, b, tg, s);
+  return p.RC ? launch_dt<true, 1, 16, 16>(dtype, softmax, b, tg, s) : launch_dt<false, 1, 16, 16>(dtype, softmax, b, tg, s);
 }
 
 }  // namespace dcn
