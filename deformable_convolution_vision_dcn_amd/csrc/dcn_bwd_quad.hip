@@ -47,8 +47,8 @@ constexpr int kBqHalo = DCN_BQ_HALO;
 constexpr int kBqPixB = 64;                               // 16 fp32 channels
 
 // Block geometry for TW x TH output tiles (a quad per pixel): 16x16 (1024
-// threads), or 24x8 (768 threads) for maps 24 pixels wide, which 16x16 tiles
-// would leave 44 % empty.
+// threads), 24x8 (768 threads) for maps 24 pixels wide or 12x12 (576
+// threads) for 12x12 maps, both of which 16x16 tiles would leave 44 % empty.
 template <int TW, int TH>
 struct BqGeom {
   static constexpr int kThreads = 4 * TW * TH;
@@ -88,7 +88,7 @@ __device__ __forceinline__ int2 pair_sums(uint64_t v) {
 // DIL: the dilation (1 or 2, both axes).  The window keeps its size: the
 // halo shrinks by one pixel per side at dilation 2.
 template <int DT, bool SOFTMAX, bool RC, int DIL, int TW, int TH>
-__global__ void __launch_bounds__(4 * TW * TH, TW * TH / 64) dcn_bwd_quad_kernel(BwdParams bp, TileGeom tg) {
+__global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kernel(BwdParams bp, TileGeom tg) {
   using G = BqGeom<TW, TH>;
   const FwdParams &p = bp.f;
   using io = Io<DT>;
@@ -650,9 +650,12 @@ hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipS
   const FwdParams &p = b.f;
   if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != p.DW || (p.DH != 1 && p.DH != 2))
     return hipErrorNotSupported;
-  // 24x8 tiles (dilation 1) where they leave clearly fewer quads idle
-  const bool wide = p.DH == 1 && quad_tile_use(p, 24, 8) > quad_tile_use(p, 16, 16) + 0.1;
-  const int tw = wide ? 24 : 16, th = wide ? 8 : 16;
+  // 24x8 or 12x12 tiles (dilation 1) where they leave clearly fewer quads
+  // idle than 16x16 ones (24x8 on a tie between the two)
+  const double u16 = quad_tile_use(p, 16, 16), u24 = quad_tile_use(p, 24, 8), u12 = quad_tile_use(p, 12, 12);
+  const bool wide = p.DH == 1 && u24 > u16 + 0.1 && u24 >= u12;
+  const bool small = p.DH == 1 && !wide && u12 > u16 + 0.1;
+  const int tw = wide ? 24 : (small ? 12 : 16), th = wide ? 8 : (small ? 12 : 16);
   TileGeom tg{};
   tg.span_w = tw + 2 * kBqHalo + 3;
   tg.span_h = th + 2 * kBqHalo + 3;
@@ -671,6 +674,8 @@ hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipS
     return p.RC ? launch_dt<true, 2, 16, 16>(dtype, softmax, b, tg, s) : launch_dt<false, 2, 16, 16>(dtype, softmax, b, tg, s);
   if (wide)
     return p.RC ? launch_dt<true, 1, 24, 8>(dtype, softmax, b, tg, s) : launch_dt<false, 1, 24, 8>(dtype, softmax, b, tg, s);
+  if (small)
+    return p.RC ? launch_dt<true, 1, 12, 12>(dtype, softmax, b, tg, s) : launch_dt<false, 1, 12, 12>(dtype, softmax, b, tg, s);
   return p.RC ? launch_dt<true, 1, 16, 16>(dtype, softmax, b, tg, s) : launch_dt<false, 1, 16, 16>(dtype, softmax, b, tg, s);
 }
 

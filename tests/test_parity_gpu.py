@@ -280,7 +280,9 @@ BWD_PATH_CASES = [
 @pytest.mark.parametrize("wl", BWD_PATH_CASES + [BWD_PATH_CASES[0].replace(name="bwdp_rc", remove_center=True),
                                 BWD_PATH_CASES[1].replace(name="bwdp_dil2_far", dilation=(2, 2), pad=(2, 2)),
                                 Workload("bwdp_24wide", n=2, h=41, w=24, c=48, groups=3,
-                                         offset_dist=uniform(4.0), seed=55)],
+                                         offset_dist=uniform(4.0), seed=55),
+                                Workload("bwdp_12x12", n=3, h=12, w=12, c=64, groups=4,
+                                         offset_dist=uniform(4.0), seed=56)],
                          ids=lambda w: w.name)
 def test_backward_each_kernel(wl, path, monkeypatch):
     """Every backward kernel, forced in turn, on multi-tile ragged shapes
@@ -308,6 +310,8 @@ BWD16 = [
     Workload("bwd16_dil2", n=2, h=30, w=35, c=32, groups=2, dilation=(2, 2), pad=(2, 2),
              offset_dist=normal(2.0), seed=68),
     Workload("bwd16_24wide", n=2, h=24, w=24, c=48, groups=3, offset_dist=uniform(3.0), seed=69),
+    Workload("bwd16_12x12", n=3, h=12, w=12, c=64, groups=4, softmax=False, mask_dist=normal(0.5),
+             seed=70),
 ]
 
 
