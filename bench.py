@@ -252,7 +252,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
+        print("bench.py: the DCN core benchmark runs on one GPU; multi-GPU runs are not supported "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         return 2
 
