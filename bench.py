@@ -71,12 +71,12 @@ def backward_bytes(wl) -> int:
 def forward_kernel_name(wl) -> str:
     """Kernel the library runs for this workload's forward (3x3 points,
     stride and dilation 1): the whole-map kernel for output maps smaller than
-    a 16x16 tile or that tiles would leave over half empty (the 12x12 stage;
-    not without the centre point), else the quad tiled kernel for fp32 and
-    the lane-per-pixel-group kernel for 16-bit I/O."""
+    a 16x16 tile or that tiles would leave over half empty (the 12x12 stage),
+    else the quad tiled kernel for fp32 and the lane-per-pixel-group kernel
+    for 16-bit I/O."""
     ho, wo = wl.out_hw
     small = ho * wo < 256 or 2 * ho * wo < ((ho + 15) // 16) * ((wo + 15) // 16) * 256
-    if small and not wl.remove_center:
+    if small:
         return "dcn_fwd_map_kernel"
     return "dcn_fwd_tile_kernel" if wl.dtype == "f32" else "dcn_fwd_lane_kernel"
 

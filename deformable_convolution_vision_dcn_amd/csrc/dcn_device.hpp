@@ -268,17 +268,38 @@ __device__ __forceinline__ void load_mask(const void *base, uint32_t pg, float (
 // an odd pixel-group starts 2 bytes into a word, so its words are read from
 // 2 bytes before the row (the previous row's last value, ignored) to the row
 // end, and an even row's last value comes from a 2-byte load.
-template <int DT>
+template <int DT, int K = 9>
 struct RowWords {
-  static constexpr int kOff = DT == DCN_F32 ? 18 : 9;
-  static constexpr int kMask = DT == DCN_F32 ? 9 : 5;
+  static_assert(K == 9 || K == 8, "3x3 rows");
+  static constexpr int kOff = DT == DCN_F32 ? 2 * K : K;
+  static constexpr int kMask = DT == DCN_F32 ? K : (K == 9 ? 5 : 4);
   uint32_t o[kOff], m[kMask];
 };
 
-template <int DT>
+template <int DT, int K = 9>
 __device__ __forceinline__ void load_row_words(__amdgpu_buffer_rsrc_t roff, __amdgpu_buffer_rsrc_t rmask,
-                                               uint32_t pg, RowWords<DT> &r) {
-  if constexpr (DT == DCN_F32) {
+                                               uint32_t pg, RowWords<DT, K> &r) {
+  if constexpr (K == 8) {
+    // Rows of 8 points are 16-byte aligned in every dtype: whole b128 loads.
+    constexpr int NO = RowWords<DT, K>::kOff / 4, NM = RowWords<DT, K>::kMask / 4;
+    const uint32_t o = pg * (uint32_t)(16 * NO), m = pg * (uint32_t)(16 * NM);
+#pragma unroll
+    for (int q = 0; q < NO; ++q) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(o + 16 * q), 0, 0);
+      r.o[4 * q] = v[0];
+      r.o[4 * q + 1] = v[1];
+      r.o[4 * q + 2] = v[2];
+      r.o[4 * q + 3] = v[3];
+    }
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rmask, (int)(m + 16 * q), 0, 0);
+      r.m[4 * q] = v[0];
+      r.m[4 * q + 1] = v[1];
+      r.m[4 * q + 2] = v[2];
+      r.m[4 * q + 3] = v[3];
+    }
+  } else if constexpr (DT == DCN_F32) {
     const uint32_t o = pg * 72u, m = pg * 36u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -323,28 +344,33 @@ __device__ __forceinline__ void load_row_words(__amdgpu_buffer_rsrc_t roff, __am
   }
 }
 
-// The 18 offsets (x, y per point) and 9 mask values of load_row_words as fp32.
-template <int DT>
-__device__ __forceinline__ void decode_row_words(uint32_t pg, const RowWords<DT> &r, float (&off)[18],
-                                                 float (&msk)[9]) {
+// The 2K offsets (x, y per point) and K mask values of load_row_words as fp32.
+template <int DT, int K = 9>
+__device__ __forceinline__ void decode_row_words(uint32_t pg, const RowWords<DT, K> &r, float (&off)[2 * K],
+                                                 float (&msk)[K]) {
   if constexpr (DT == DCN_F32) {
 #pragma unroll
-    for (int q = 0; q < 18; ++q) off[q] = __uint_as_float(r.o[q]);
+    for (int q = 0; q < 2 * K; ++q) off[q] = __uint_as_float(r.o[q]);
 #pragma unroll
-    for (int q = 0; q < 9; ++q) msk[q] = __uint_as_float(r.m[q]);
+    for (int q = 0; q < K; ++q) msk[q] = __uint_as_float(r.m[q]);
   } else {
 #pragma unroll
-    for (int q = 0; q < 9; ++q) {
+    for (int q = 0; q < K; ++q) {
       off[2 * q] = Io<DT>::lo(r.o[q]);
       off[2 * q + 1] = Io<DT>::hi(r.o[q]);
     }
-    const uint32_t sh = (pg * 18u) & 2u ? 16u : 0u;  // odd pg: the row starts at a half word
-    uint32_t w[5];
+    if constexpr (K == 8) {  // aligned rows: two values per word
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_alignbit(r.m[q + 1], r.m[q], sh);
-    w[4] = r.m[4] >> sh;
+      for (int q = 0; q < 8; ++q) msk[q] = (q & 1) ? Io<DT>::hi(r.m[q / 2]) : Io<DT>::lo(r.m[q / 2]);
+    } else {
+      const uint32_t sh = (pg * 18u) & 2u ? 16u : 0u;  // odd pg: the row starts at a half word
+      uint32_t w[5];
 #pragma unroll
-    for (int q = 0; q < 9; ++q) msk[q] = (q & 1) ? Io<DT>::hi(w[q / 2]) : Io<DT>::lo(w[q / 2]);
+      for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_alignbit(r.m[q + 1], r.m[q], sh);
+      w[4] = r.m[4] >> sh;
+#pragma unroll
+      for (int q = 0; q < 9; ++q) msk[q] = (q & 1) ? Io<DT>::hi(w[q / 2]) : Io<DT>::lo(w[q / 2]);
+    }
   }
 }
 

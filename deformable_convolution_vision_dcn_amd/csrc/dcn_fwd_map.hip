@@ -1,6 +1,8 @@
 // dcn_fwd_map.hip -- whole-map gfx950 forward kernel of the DCN core for 3x3
 // kernel points on small feature maps (wmrh.cn/news/61976, section 二 steps
-// 2-4 and section 三; the late InternImage stages run at 24x24 and 12x12).
+// 2-4 and section 三; the late InternImage stages run at 24x24 and 12x12),
+// all nine or the eight left by DCNv4's remove_center
+// (pnsm.cn/news/2029644.html section 3.3).
 //
 // Why a second layout: a 16x16 output tile on a 24x24 or 12x12 map leaves up
 // to 44 % of the lanes of the tiled kernels without a pixel, and its window
@@ -65,7 +67,9 @@ __device__ __forceinline__ void map_dma16(__amdgpu_buffer_rsrc_t r, unsigned cha
 
 }  // namespace
 
-template <int DT, bool SOFTMAX>
+// RC: the centre point is removed (8 points; point k sits at grid index
+// k + (k >= 4)).
+template <int DT, bool SOFTMAX, bool RC>
 __global__ void __launch_bounds__(kMapThreads, map_waves<DT>()) dcn_fwd_map_kernel(FwdParams p, MapGeom mg) {
   using io = Io<DT>;
   constexpr int CG = kGroupChannels;
@@ -74,7 +78,7 @@ __global__ void __launch_bounds__(kMapThreads, map_waves<DT>()) dcn_fwd_map_kern
   constexpr int NCH = PIXB / CHUNK;        // 16-byte chunks per pixel slice: 4 or 2
   constexpr int CPC = CHUNK / io::kBytes;  // channels per chunk: 4 or 8
   constexpr int GB = CG * io::kBytes;      // bytes of one group of one pixel
-  constexpr int K = 9;
+  constexpr int K = RC ? 8 : 9;
 
   extern __shared__ __align__(16) unsigned char lds[];
 
@@ -120,7 +124,7 @@ __global__ void __launch_bounds__(kMapThreads, map_waves<DT>()) dcn_fwd_map_kern
     return r;
   };
 
-  RowWords<DT> rw[2];
+  RowWords<DT, K> rw[2];
 
   // One work item per block: nothing is carried from item to item, and the
   // hardware then starts each block as soon as a slot frees up, so the last
@@ -147,18 +151,18 @@ __global__ void __launch_bounds__(kMapThreads, map_waves<DT>()) dcn_fwd_map_kern
     }
     {
       const Pg q0 = pixel_group(n, g0, 0);
-      load_row_words<DT>(roff, rmask, q0.pg, rw[0]);
+      load_row_words<DT, K>(roff, rmask, q0.pg, rw[0]);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's window loads have landed
     __syncthreads();                     // the windows are in LDS
 
     // One pass: decode this pass's rows from (cw, cm), request the next
     // pass's into (nw, nm), then the nine samples of every lane's pixel-group.
-    auto pass = [&](int q, const RowWords<DT> &cr, RowWords<DT> &nr) {
+    auto pass = [&](int q, const RowWords<DT, K> &cr, RowWords<DT, K> &nr) {
       const Pg cur = pixel_group(n, g0, q);
-      float off[18], msk[K];
-      decode_row_words<DT>(cur.pg, cr, off, msk);
-      if (q + 1 < mg.passes) load_row_words<DT>(roff, rmask, pixel_group(n, g0, q + 1).pg, nr);
+      float off[2 * K], msk[K];
+      decode_row_words<DT, K>(cur.pg, cr, off, msk);
+      if (q + 1 < mg.passes) load_row_words<DT, K>(roff, rmask, pixel_group(n, g0, q + 1).pg, nr);
       float m[K];
       if constexpr (SOFTMAX) {
         float mx = msk[0];
@@ -191,7 +195,8 @@ __global__ void __launch_bounds__(kMapThreads, map_waves<DT>()) dcn_fwd_map_kern
         uint32_t A;
       };
       auto locate = [&](int k, Pt &P) {
-        const int i = k / 3, j = k % 3;
+        const int g3 = RC ? k + (k >= 4) : k;  // grid index
+        const int i = g3 / 3, j = g3 % 3;
         const float dx = s * off[2 * k], dy = s * off[2 * k + 1];
         const bool nan_loc = (dx != dx) | (dy != dy);
         const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
@@ -279,9 +284,9 @@ __global__ void __launch_bounds__(kMapThreads, map_waves<DT>()) dcn_fwd_map_kern
 
 namespace {
 
-template <int DT, bool SM>
+template <int DT, bool SM, bool RC>
 hipError_t launch_map(const FwdParams &p, const MapGeom &mg, size_t lds, hipStream_t s) {
-  auto kern = dcn_fwd_map_kernel<DT, SM>;
+  auto kern = dcn_fwd_map_kernel<DT, SM, RC>;
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
@@ -289,14 +294,24 @@ hipError_t launch_map(const FwdParams &p, const MapGeom &mg, size_t lds, hipStre
   return hipGetLastError();
 }
 
+template <bool RC>
+hipError_t launch_map_dt(int dtype, int softmax, const FwdParams &p, const MapGeom &mg, size_t lds, hipStream_t s) {
+  switch (dtype) {
+    case DCN_F32: return softmax ? launch_map<DCN_F32, true, RC>(p, mg, lds, s) : launch_map<DCN_F32, false, RC>(p, mg, lds, s);
+    case DCN_F16: return softmax ? launch_map<DCN_F16, true, RC>(p, mg, lds, s) : launch_map<DCN_F16, false, RC>(p, mg, lds, s);
+    case DCN_BF16: return softmax ? launch_map<DCN_BF16, true, RC>(p, mg, lds, s) : launch_map<DCN_BF16, false, RC>(p, mg, lds, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
-// 3x3 points on a map whose bordered window (of at least one group) fits
-// the LDS budget; hipErrorNotSupported (nothing launched) otherwise.  Groups
+// 3x3 points (nine, or eight without the centre) on a map whose bordered
+// window (of at least one group) fits the LDS budget; hipErrorNotSupported (nothing launched) otherwise.  Groups
 // per item: the smallest power of two that keeps the passes' lanes at least
 // 90 % busy, within the budget (else the best one found).
 hipError_t launch_forward_map(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
-  if (p.RC || p.KH != 3 || p.KW != 3) return hipErrorNotSupported;
+  if (p.KH != 3 || p.KW != 3) return hipErrorNotSupported;
   const int pixb = dtype == DCN_F32 ? 64 : 32;
   const int64_t cell_bytes = (int64_t)(p.H + 2) * (p.W + 2) * pixb;
   const int64_t howo = (int64_t)p.Ho * p.Wo;
@@ -335,12 +350,7 @@ hipError_t launch_forward_map(int dtype, int softmax, const FwdParams &p, hipStr
   mg.div_ww = make_fast_div((uint32_t)(p.W + 2));
   mg.div_cell = make_fast_div((uint32_t)((p.H + 2) * (p.W + 2)));
   const size_t lds = (size_t)mg.zero + mg.wrow + 2 * pixb;
-  switch (dtype) {
-    case DCN_F32: return softmax ? launch_map<DCN_F32, true>(p, mg, lds, s) : launch_map<DCN_F32, false>(p, mg, lds, s);
-    case DCN_F16: return softmax ? launch_map<DCN_F16, true>(p, mg, lds, s) : launch_map<DCN_F16, false>(p, mg, lds, s);
-    case DCN_BF16: return softmax ? launch_map<DCN_BF16, true>(p, mg, lds, s) : launch_map<DCN_BF16, false>(p, mg, lds, s);
-    default: return hipErrorInvalidValue;
-  }
+  return p.RC ? launch_map_dt<true>(dtype, softmax, p, mg, lds, s) : launch_map_dt<false>(dtype, softmax, p, mg, lds, s);
 }
 
 }  // namespace dcn

@@ -42,4 +42,4 @@ def test_forward_kernel_names_follow_the_dispatch():
     assert bench.forward_kernel_name(synth.WORKLOADS["stage2_dcnv4_f16"]) == "dcn_fwd_lane_kernel"
     assert bench.forward_kernel_name(synth.WORKLOADS["stage4_dcnv4_f16"]) == "dcn_fwd_map_kernel"
     assert bench.forward_kernel_name(synth.WORKLOADS["stage4_dcnv4_f16"].replace(remove_center=True)) == \
-        "dcn_fwd_lane_kernel"
+        "dcn_fwd_map_kernel"

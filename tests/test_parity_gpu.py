@@ -151,6 +151,10 @@ MAP_CASES = [
     Workload("map_v4_rect", n=2, h=9, w=30, c=64, groups=4, softmax=False, mask_dist=normal(0.5),
              seed=54),
     Workload("map_far", n=1, h=14, w=16, c=32, groups=2, offset_dist=uniform(12.0), seed=55),
+    Workload("map_rc_12x12", n=2, h=12, w=12, c=96, groups=6, softmax=False, mask_dist=normal(0.5),
+             remove_center=True, seed=56),
+    Workload("map_rc_v3_24x24", n=2, h=24, w=24, c=64, groups=4, offset_dist=uniform(3.0),
+             remove_center=True, seed=57),
 ]
 
 
