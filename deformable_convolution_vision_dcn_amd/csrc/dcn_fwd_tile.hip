@@ -63,12 +63,13 @@ constexpr int tile_pixel_stride() {
   return GP == 2 ? 2 * kGroupChannels * Io<DT>::kBytes : (DT == DCN_F32 ? DCN_PIXB_F32 : DCN_PIXB_16);
 }
 
-// UNIT: stride 1 and dilation 1, so the window geometry is a compile-time
-// constant (no run-time multiplies on the per-point path).  RC: the centre
+// UDIL > 0: stride 1 and dilation UDIL (1 or 2) on both axes, so the window
+// geometry is a compile-time constant (no run-time multiplies on the
+// per-point path); UDIL = 0: any stride and dilation.  RC: the centre
 // point is removed (8 points, point k at grid index k + (k >= 4)): each lane
 // owns two points, lane 0's third slot stays empty, two rounds instead of
 // three.
-template <int DT, bool SOFTMAX, int TH, int TW, int R, bool UNIT, int GP, bool RC>
+template <int DT, bool SOFTMAX, int TH, int TW, int R, int UDIL, int GP, bool RC>
 __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(FwdParams p, TileGeom tg) {
   using io = Io<DT>;
   constexpr int CG = kGroupChannels;
@@ -107,15 +108,16 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   const __amdgpu_buffer_rsrc_t roff = make_rsrc(p.offset, p.off_bytes);
   const __amdgpu_buffer_rsrc_t rmask = make_rsrc(p.mask, p.mask_bytes);
   const __amdgpu_buffer_rsrc_t rout = make_rsrc(p.output, p.out_bytes);
-  constexpr int USPAN = TW + 2 * R + 3;  // window edge at stride 1, dilation 1
+  constexpr bool UNIT = UDIL > 0;
+  constexpr int USPAN = TW + 2 * R + 1 + 2 * UDIL;  // window edge at stride 1, dilation UDIL
   const int span_w = UNIT ? USPAN : tg.span_w;
-  const int span_h = UNIT ? (TH + 2 * R + 3) : tg.span_h;
+  const int span_h = UNIT ? (TH + 2 * R + 1 + 2 * UDIL) : tg.span_h;
   const int span = span_h * span_w;
   const int row_lds = span_w * PIXB;
   const int zero_base = span * PIXB;
   const int lim_y = span_h - 2, lim_x = span_w - 2;
   const int SW = UNIT ? 1 : p.SW, SH = UNIT ? 1 : p.SH;
-  const int DW = UNIT ? 1 : p.DW, DH = UNIT ? 1 : p.DH;
+  const int DW = UNIT ? UDIL : p.DW, DH = UNIT ? UDIL : p.DH;
   const float s = p.scale;
 
   // Window slots at unit stride.  A lane stages the same window pixels of
@@ -530,9 +532,9 @@ size_t tile_lds_bytes(const TileGeom &tg, int pixb) {
   return ((size_t)tg.span_h * tg.span_w + tg.span_w + 2) * pixb;  // window + zero block
 }
 
-template <int DT, bool SM, bool UNIT, int GP, bool RC, int HALO = tile_halo<GP>()>
+template <int DT, bool SM, int UDIL, int GP, bool RC, int HALO = tile_halo<GP>()>
 hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, HALO, UNIT, GP, RC>;
+  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, HALO, UDIL, GP, RC>;
   const size_t lds = tile_lds_bytes(tg, tile_pixel_stride<DT, GP>());
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
@@ -549,17 +551,22 @@ hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   return hipGetLastError();
 }
 
+// udil: the compile-time geometry's dilation (1 or 2 at stride 1), 0 for
+// any other stride/dilation (one group per item only).
 template <int DT, int GP, bool RC>
-hipError_t launch_tile_dt(int softmax, bool unit, int halo, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  if (unit)
-    return softmax ? launch_tile<DT, true, true, GP, RC>(p, tg, s) : launch_tile<DT, false, true, GP, RC>(p, tg, s);
+hipError_t launch_tile_dt(int softmax, int udil, int halo, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
+  constexpr int H2 = tile_halo<GP>() - 1;  // dilation 2: the same window edge as dilation 1
+  if (udil == 1)
+    return softmax ? launch_tile<DT, true, 1, GP, RC>(p, tg, s) : launch_tile<DT, false, 1, GP, RC>(p, tg, s);
+  if (udil == 2)
+    return softmax ? launch_tile<DT, true, 2, GP, RC, H2>(p, tg, s) : launch_tile<DT, false, 2, GP, RC, H2>(p, tg, s);
   if constexpr (GP == 2) {
-    return hipErrorNotSupported;  // strided/dilated windows: one group per item
+    return hipErrorNotSupported;  // strided windows: one group per item
   } else {
     if (halo == kTileHaloSmall)
-      return softmax ? launch_tile<DT, true, false, GP, RC, kTileHaloSmall>(p, tg, s)
-                     : launch_tile<DT, false, false, GP, RC, kTileHaloSmall>(p, tg, s);
-    return softmax ? launch_tile<DT, true, false, GP, RC>(p, tg, s) : launch_tile<DT, false, false, GP, RC>(p, tg, s);
+      return softmax ? launch_tile<DT, true, 0, GP, RC, kTileHaloSmall>(p, tg, s)
+                     : launch_tile<DT, false, 0, GP, RC, kTileHaloSmall>(p, tg, s);
+    return softmax ? launch_tile<DT, true, 0, GP, RC>(p, tg, s) : launch_tile<DT, false, 0, GP, RC>(p, tg, s);
   }
 }
 
@@ -578,7 +585,7 @@ bool tile_geometry(int dtype, const FwdParams &p, TileGeom &tg, int halo) {
   // the buffer range of their image, which needs the byte offset of every
   // window row relative to the image (rows -pad - halo - 1 to
   // H + pad + halo + 1) to fit int32.
-  const bool unit = p.SH == 1 && p.SW == 1 && p.DH == 1 && p.DW == 1;
+  const bool unit = p.SH == 1 && p.SW == 1 && p.DH == p.DW && (p.DH == 1 || p.DH == 2);
   const int64_t row_bytes = (int64_t)p.W * p.C * (dtype == DCN_F32 ? 4 : 2);
   if (unit && ((int64_t)p.H + p.PH + tg.span_h + 1) * row_bytes >= (int64_t(1) << 31)) return false;
   const int tiles_y = (p.Ho + kTileH - 1) / kTileH;
@@ -598,20 +605,23 @@ bool tile_geometry(int dtype, const FwdParams &p, TileGeom &tg, int halo) {
 template <int GP>
 hipError_t launch_tile_gp(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
   TileGeom tg;
-  const bool unit = p.SH == 1 && p.SW == 1 && p.DH == 1 && p.DW == 1;
-  int halo = tile_halo<GP>();
+  // Stride 1 at dilation 1 or 2 (equal on both axes) runs the compile-time
+  // geometry; dilation 2 takes a halo one smaller, so the window keeps its
+  // edge.  Other strides and dilations run the general one-group variant.
+  const int udil = (p.SH == 1 && p.SW == 1 && p.DH == p.DW && (p.DH == 1 || p.DH == 2)) ? p.DH : 0;
+  int halo = tile_halo<GP>() - (udil == 2 ? 1 : 0);
   if (!tile_geometry<GP>(dtype, p, tg, halo)) {
-    if (GP != 1 || unit) return hipErrorNotSupported;
+    if (GP != 1 || udil != 0) return hipErrorNotSupported;
     halo = kTileHaloSmall;
     if (!tile_geometry<GP>(dtype, p, tg, halo)) return hipErrorNotSupported;
   }
   if (p.RC) {  // fp32 only: 16-bit rows without the centre go to the lane kernel
-    return dtype == DCN_F32 ? launch_tile_dt<DCN_F32, GP, true>(softmax, unit, halo, p, tg, s) : hipErrorNotSupported;
+    return dtype == DCN_F32 ? launch_tile_dt<DCN_F32, GP, true>(softmax, udil, halo, p, tg, s) : hipErrorNotSupported;
   }
   switch (dtype) {
-    case DCN_F32: return launch_tile_dt<DCN_F32, GP, false>(softmax, unit, halo, p, tg, s);
-    case DCN_F16: return launch_tile_dt<DCN_F16, GP, false>(softmax, unit, halo, p, tg, s);
-    case DCN_BF16: return launch_tile_dt<DCN_BF16, GP, false>(softmax, unit, halo, p, tg, s);
+    case DCN_F32: return launch_tile_dt<DCN_F32, GP, false>(softmax, udil, halo, p, tg, s);
+    case DCN_F16: return launch_tile_dt<DCN_F16, GP, false>(softmax, udil, halo, p, tg, s);
+    case DCN_BF16: return launch_tile_dt<DCN_BF16, GP, false>(softmax, udil, halo, p, tg, s);
     default: return hipErrorInvalidValue;
   }
 }
