@@ -560,3 +560,51 @@ def test_runs_on_a_side_stream():
         y = dcn.dcn_forward(x, off, m, **wl.op_kwargs())
     s.synchronize()
     gate(_np(y), oracle_full(wl, t), "f32", "side stream")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_graph_capture_replays_match_eager(dtype):
+    """Forward and backward captured in a HIP graph (the library clears with a
+    fill kernel, never hipMemsetAsync): every replay, on new inputs copied into
+    the captured buffers with eager work and a synchronisation between
+    replays, equals an eager call on the same inputs."""
+    wl = PATH_CASES[0].replace(dtype=dtype)
+    kw = wl.op_kwargs()
+    print(f"graph capture {dtype}", flush=True)
+    draws = [synth.make_inputs(wl.replace(seed=wl.seed + 100 * r), with_grad=True) for r in range(4)]
+    x, off, m, gy = (draws[0][k].to(DEV) for k in ("x", "offset", "mask", "grad_out"))
+    y = torch.empty((wl.n, *wl.out_hw, wl.c), dtype=x.dtype, device=DEV)
+    gx, goff, gm = torch.empty_like(x), torch.empty_like(off), torch.empty_like(m)
+    nb = dcn.backward_workspace_bytes(x, **kw)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    outs = dict(grad_input=gx, grad_offset=goff, grad_mask=gm, workspace=ws if nb else None)
+
+    def step():
+        dcn.dcn_forward(x, off, m, out=y, **kw)
+        dcn.dcn_backward(x, off, m, gy, **outs, **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(1, 4):
+        for k, dst in (("x", x), ("offset", off), ("mask", m), ("grad_out", gy)):
+            dst.copy_(draws[r][k].to(DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [_np(t) for t in (y, gx, goff, gm)]
+        ey = dcn.dcn_forward(x, off, m, **kw)
+        eg = dcn.dcn_backward(x, off, m, gy, **kw)
+        torch.cuda.synchronize()
+        ref = [_np(ey)] + [_np(t) for t in eg]
+        # the forward is deterministic; grad_input's fp32 atomics may add in another order
+        assert np.array_equal(got[0], ref[0]), f"replay {r}: output"
+        assert np.array_equal(got[2], ref[2]) and np.array_equal(got[3], ref[3]), f"replay {r}: grad_offset/mask"
+        tol = 1e-5 if dtype == "f32" else 2.0 ** -7
+        np.testing.assert_allclose(got[1], ref[1], rtol=tol, atol=1e-5, err_msg=f"replay {r}: grad_input")
