@@ -463,6 +463,23 @@ def test_autograd_function_matches_backward():
     gate(_np(gm), rm, "f32", "autograd grad_mask")
 
 
+@pytest.mark.parametrize("rc", [False, True], ids=["k9", "remove_center"])
+def test_autograd_function_bf16(rc):
+    """dcn_core in bf16 through torch autograd (the 16-bit backward with a
+    workspace from torch's allocator), against the oracle on the 16-bit gate."""
+    wl = BWD16[2].replace(dtype="bf16", remove_center=rc)
+    t = synth.make_inputs(wl, with_grad=True)
+    x, off, m, gy = (t[k].to(DEV).requires_grad_(k != "grad_out") for k in ("x", "offset", "mask", "grad_out"))
+    y = dcn.dcn_core(x, off, m, **wl.op_kwargs())
+    gx, goff, gm = torch.autograd.grad(y, (x, off, m), grad_outputs=gy)
+    assert gx.dtype == torch.bfloat16
+    rx, roff, rm = oracle_backward(wl, t)
+    gate(_np(y.detach()), oracle_full(wl, t), "bf16", f"autograd bf16 rc={rc} output")
+    gate(_np(gx), rx, "bf16", f"autograd bf16 rc={rc} grad_input")
+    gate(_np(goff), roff, "bf16", f"autograd bf16 rc={rc} grad_offset")
+    gate(_np(gm), rm, "bf16", f"autograd bf16 rc={rc} grad_mask")
+
+
 # --------------------------------------------------------------------------- edge cases
 
 def test_empty_batch():
