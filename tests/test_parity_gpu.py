@@ -625,3 +625,36 @@ def test_graph_capture_replays_match_eager(dtype):
         assert np.array_equal(got[2], ref[2]) and np.array_equal(got[3], ref[3]), f"replay {r}: grad_offset/mask"
         tol = 1e-5 if dtype == "f32" else 2.0 ** -7
         np.testing.assert_allclose(got[1], ref[1], rtol=tol, atol=1e-5, err_msg=f"replay {r}: grad_input")
+
+
+def test_concurrent_calls_from_two_threads():
+    """The library keeps no mutable state: two host threads, each on its own
+    stream, run forwards of different problems at once and get the results
+    of serial calls."""
+    import threading
+    cases = [PATH_CASES[0], PATH_CASES[3].replace(dtype="bf16")]
+    ins = [{k: v.to(DEV) for k, v in synth.make_inputs(wl).items()} for wl in cases]
+    ref = [_np(dcn.dcn_forward(t["x"], t["offset"], t["mask"], **wl.op_kwargs())) for wl, t in zip(cases, ins)]
+    torch.cuda.synchronize()
+    got = [None, None]
+    errors = []
+
+    def run(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    y = dcn.dcn_forward(ins[i]["x"], ins[i]["offset"], ins[i]["mask"], **cases[i].op_kwargs())
+            s.synchronize()
+            got[i] = _np(y)
+        except Exception as e:  # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert not errors, errors
+    for i in range(2):
+        assert np.array_equal(got[i], ref[i]), f"thread {i}"
