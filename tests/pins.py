@@ -531,9 +531,107 @@ def pin_softmax_grad_sums_to_zero(orc):
     assert np.max(np.abs(gm)) > 1e-3
 
 
+def pin_backward_far_away_is_zero(orc):
+    """Zero padding in the backward (wmrh.cn/news/61976 section 二 step 4: the
+    sample reads zeros off the map).  A sample off the map has B = 0 and
+    dB = 0, so it scatters nothing into grad_input, its offset gradient
+    s * m_k * 0 is 0, its gm_k is 0, and through the DCNv3 softmax Jacobian
+    m_k * (0 - sum_j m_j * 0) = 0 as well.  Offsets of +-1e4 (far, through the
+    ordinary corner path), +-1e300 and +-Inf (beyond any representable map),
+    on both axes or only one of them."""
+    rng = np.random.default_rng(114)
+    n, h, w, c, g = 1, 6, 5, 8, 2
+    x = rng.standard_normal((n, h, w, c))
+    m = rng.standard_normal((n, h, w, g, 9))
+    gy = rng.standard_normal((n, h, w, c))
+    for big in (1e4, -1e4, 1e300, -1e300, np.inf, -np.inf):
+        for axes in ((0, 1), (0,), (1,)):
+            off = rng.standard_normal((n, h, w, g, 9, 2))
+            for a in axes:
+                off[..., a] = big
+            for softmax in (True, False):
+                kw = _kw(g, softmax=softmax)
+                what = f"offset {big} on axes {axes}, softmax={softmax}"
+                y = orc.forward(x, off, m, **kw)
+                assert np.all(y == 0.0), f"forward, {what}: not exactly zero"
+                gx, goff, gm = orc.backward(x, off, m, gy, **kw)
+                assert np.all(gx == 0.0), f"grad_input, {what}: not exactly zero"
+                assert np.all(goff == 0.0), f"grad_offset, {what}: not exactly zero"
+                assert np.all(gm == 0.0), f"grad_mask, {what}: not exactly zero"
+    # one far point in an otherwise ordinary problem: its rows are zero and the
+    # rest equals the problem with that point's weight set to zero (DCNv4: the
+    # raw mask; DCNv3: the softmax weights computed here by scipy and passed
+    # as raw weights, the far point's zeroed)
+    x, off, m = _random_case(rng, 1, 6, 5, 8, 2, off_std=1.5)
+    gy = rng.standard_normal((1, 6, 5, 8))
+    at = (0, 2, 3, 1, 5)
+    off[at + (1,)] = np.inf
+    for softmax in (True, False):
+        gx, goff, gm = orc.backward(x, off, m, gy, **_kw(2, softmax=softmax))
+        assert np.all(goff[at] == 0.0), f"far point's grad_offset (softmax={softmax})"
+        wts = scipy.special.softmax(m, axis=-1) if softmax else m.copy()
+        wts[at] = 0.0
+        off0 = off.copy()
+        off0[at] = 0.0
+        rx, roff, rgm = orc.backward(x, off0, wts, gy, **_kw(2, softmax=False))
+        _close(gx, rx, 1e-12, f"grad_input with one far point (softmax={softmax})")
+        keep = np.ones(off.shape[:-1], dtype=bool)
+        keep[at] = False
+        _close(goff[keep], roff[keep], 1e-12, f"grad_offset of the other points (softmax={softmax})")
+        if softmax:  # gm of the far point is 0; the Jacobian of the scipy softmax
+            sm = scipy.special.softmax(m, axis=-1)
+            raw = rgm.copy()
+            raw[at] = 0.0
+            ref = sm * (raw - np.sum(sm * raw, axis=-1, keepdims=True))
+            _close(gm, ref, 1e-12, "grad_mask with one far point (softmax)")
+        else:
+            assert gm[at] == 0.0, "far point's gm (DCNv4)"
+            _close(gm[keep], rgm[keep], 1e-12, "grad_mask of the other points (DCNv4)")
+
+
+def pin_backward_nan_offset_is_local(orc):
+    """A NaN offset makes its sampling location NaN.  Reading taken: the
+    sample's gradients are NaN (its grad_offset pair and gm_k, and for DCNv3
+    every logit gradient of its (pixel, group), through the softmax Jacobian's
+    sum over the points) and it scatters nothing into grad_input.  Every other
+    gradient is that of the same problem with the point's weight set to zero:
+    checked against the oracle run on raw weights (the DCNv3 softmax computed
+    here by scipy), the Jacobian applied here for DCNv3."""
+    rng = np.random.default_rng(115)
+    x, off, m = _random_case(rng, 1, 6, 5, 8, 2, off_std=1.5)
+    gy = rng.standard_normal((1, 6, 5, 8))
+    at = (0, 2, 3, 1, 4)
+    off[at + (0,)] = np.nan
+    for softmax in (True, False):
+        gx, goff, gm = orc.backward(x, off, m, gy, **_kw(2, softmax=softmax))
+        assert np.all(np.isnan(goff[at])), f"NaN point's grad_offset (softmax={softmax})"
+        wts = scipy.special.softmax(m, axis=-1) if softmax else m.copy()
+        wts[at] = 0.0
+        off0 = off.copy()
+        off0[at] = 0.0
+        rx, roff, rgm = orc.backward(x, off0, wts, gy, **_kw(2, softmax=False))
+        assert np.all(np.isfinite(gx)), f"NaN reached grad_input (softmax={softmax})"
+        _close(gx, rx, 1e-12, f"grad_input beside a NaN point (softmax={softmax})")
+        keep = np.ones(off.shape[:-1], dtype=bool)
+        keep[at] = False
+        _close(goff[keep], roff[keep], 1e-12, f"grad_offset beside a NaN point (softmax={softmax})")
+        if softmax:
+            assert np.all(np.isnan(gm[at[:4]])), "the NaN point's group: every logit gradient NaN"
+            other = np.ones(m.shape[:-1], dtype=bool)
+            other[at[:4]] = False
+            sm = scipy.special.softmax(m, axis=-1)
+            ref = sm * (rgm - np.sum(sm * rgm, axis=-1, keepdims=True))
+            _close(gm[other], ref[other], 1e-12, "grad_mask of the other (pixel, group)s (softmax)")
+        else:
+            assert np.isnan(gm[at]), "the NaN point's gm (DCNv4)"
+            assert np.sum(np.isnan(gm)) == 1, "NaN leaked into other mask gradients (DCNv4)"
+            _close(gm[keep], rgm[keep], 1e-12, "grad_mask beside a NaN point (DCNv4)")
+
+
 ALL_PINS = [
     pin_box_average, pin_integer_offsets_exact_gather, pin_partition_of_unity,
-    pin_out_of_range_is_zero, pin_hand_golden, pin_linearity, pin_group_independence,
+    pin_out_of_range_is_zero, pin_backward_far_away_is_zero, pin_backward_nan_offset_is_local,
+    pin_hand_golden, pin_linearity, pin_group_independence,
     pin_forward_pixels, pin_out_size, pin_grid_sample_forward, pin_grid_sample_backward,
     pin_depthwise_conv, pin_depthwise_conv_remove_center, pin_brute_force_tiny, pin_adjoint, pin_finite_differences, pin_softmax_grad_sums_to_zero,
 ]

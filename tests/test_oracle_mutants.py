@@ -39,6 +39,14 @@ MUTANTS = [
     ("removed_point_is_the_last", "q >= (p->kh / 2) * p->kw + p->kw / 2", "q >= p->kh * p->kw - 1"),
     ("points_after_centre_not_shifted", "        ++q;", "        q += 0;"),
     ("centre_still_counted", "- (p->remove_center ? 1 : 0)", "- 0"),
+    # the backward's branches for samples infinitely far away and NaN locations
+    ("far_grad_offset_not_zero", "go[0] = s * m[k] * 0.0;", "go[0] = s * m[k];"),
+    ("far_needs_both_axes", "if (!(fabs(py) < 1e15 && fabs(px) < 1e15))",
+     "if (!(fabs(py) < 1e15 || fabs(px) < 1e15))"),
+    ("nan_grad_mask_not_poisoned", "gm[k] = go[0] = go[1] = NAN;", "go[0] = go[1] = NAN;"),
+    ("nan_grad_offset_zero", "gm[k] = go[0] = go[1] = NAN;", "gm[k] = NAN; go[0] = go[1] = 0.0;"),
+    ("nan_location_taken_as_far", "if (isnan(py) || isnan(px))\n        return -1;",
+     "if (isnan(py) || isnan(px))\n        return 0;"),
 ]
 
 
