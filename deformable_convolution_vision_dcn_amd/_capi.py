@@ -13,7 +13,7 @@ import pathlib
 LIB_PATH = pathlib.Path(os.environ.get(
     "DCN_MI355X_LIB", pathlib.Path(__file__).resolve().parent / "libdcn_mi355x.so"))
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
 

@@ -106,16 +106,12 @@ int64_t images_per_chunk(const dcn_problem *p, int64_t ho, int64_t wo) {
   return per < 1 ? 1 : per;
 }
 
-// The backward's extra checks: 16-bit I/O only for 3x3 points (with or
-// without the centre) at stride 1 and dilation 1 or 2, and one image's fp32
-// grad_input accumulator below 2^31 bytes.
+// The backward's extra check: for 16-bit I/O, one image's fp32 grad_input
+// accumulator below 2^31 bytes.
 int validate_backward(const dcn_problem *p, int64_t *ho, int64_t *wo) {
   const int st = validate(p, ho, wo);
   if (st != DCN_OK) return st;
   if (p->dtype == DCN_F32) return DCN_OK;
-  const bool quad_shape = p->kernel_h == 3 && p->kernel_w == 3 && p->stride_h == 1 && p->stride_w == 1 &&
-                          p->dilation_h == p->dilation_w && (p->dilation_h == 1 || p->dilation_h == 2);
-  if (!quad_shape) return DCN_ERR_UNSUPPORTED;
   if ((int64_t)p->h * p->w * p->c * 4 > kMaxBytes31) return DCN_ERR_TOO_LARGE;
   return DCN_OK;
 }
@@ -137,6 +133,65 @@ uint64_t workspace_bytes_bwd(const dcn_problem *p, int64_t ho, int64_t wo) {
   int64_t per = images_per_chunk_bwd(p, ho, wo);
   if (p->n < per) per = p->n;
   return (uint64_t)(per * p->h * p->w * p->c * 4);
+}
+
+// The enqueue stage of both backward entry points, after their checks:
+// pointers are checked here, then the chunks of `per` images are launched.
+// For 16-bit I/O `ws` is the fp32 accumulator of one chunk (per*H*W*C*4
+// bytes at least).
+int run_backward(const dcn_problem *p, int64_t ho, int64_t wo, const void *input, const void *offset,
+                 const void *mask, const void *grad_output, void *grad_input, void *grad_offset, void *grad_mask,
+                 void *ws, int64_t per, void *hip_stream) {
+  const bool wide = p->dtype == DCN_F32;  // grad_input accumulates in place
+  if (!input || !offset || !mask || !grad_output || !grad_input || !grad_offset || !grad_mask) return DCN_ERR_NULL;
+  if (!aligned16(input) || !aligned16(offset) || !aligned16(mask) || !aligned16(grad_output) ||
+      !aligned16(grad_input) || !aligned16(grad_offset) || !aligned16(grad_mask))
+    return DCN_ERR_ALIGN;
+
+  const int64_t K = npoints(p);
+  const int64_t eb = elem_bytes(p->dtype);
+  const int64_t img_elems = (int64_t)p->h * p->w * p->c;
+  const int64_t img_in = img_elems * eb;
+  const int64_t img_pg = ho * wo * p->groups;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+
+  hipError_t e = hipSuccess;
+  if (wide) {
+    e = dcn::launch_zero(grad_input, (uint64_t)(p->n * img_in), stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  dcn::BwdParams b{};
+  b.f = geometry(p, ho, wo);
+  for (int64_t n0 = 0; n0 < p->n; n0 += per) {
+    const int64_t nc = (p->n - n0 < per) ? p->n - n0 : per;
+    b.f.input = static_cast<const char *>(input) + n0 * img_in;
+    b.f.offset = static_cast<const char *>(offset) + n0 * img_pg * K * 2 * eb;
+    b.f.mask = static_cast<const char *>(mask) + n0 * img_pg * K * eb;
+    b.f.output = nullptr;
+    b.f.in_bytes = (uint32_t)(nc * img_in);
+    b.f.off_bytes = (uint32_t)(nc * img_pg * K * 2 * eb);
+    b.f.mask_bytes = (uint32_t)(nc * img_pg * K * eb);
+    b.f.out_bytes = 0;
+    b.f.pg_total = (uint32_t)(nc * img_pg);
+    b.grad_out = static_cast<const char *>(grad_output) + n0 * img_pg * dcn::kGroupChannels * eb;
+    b.grad_offset = static_cast<char *>(grad_offset) + n0 * img_pg * K * 2 * eb;
+    b.grad_mask = static_cast<char *>(grad_mask) + n0 * img_pg * K * eb;
+    if (wide) {
+      b.grad_in = static_cast<char *>(grad_input) + n0 * img_in;
+    } else {  // each chunk reuses the accumulator: zero it, accumulate, round out
+      b.grad_in = ws;
+      e = dcn::launch_zero(ws, (uint64_t)(nc * img_elems * 4), stream);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    e = dcn::launch_backward(p->dtype, p->softmax, b, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (!wide) {
+      e = dcn::launch_narrow(p->dtype, ws, static_cast<char *>(grad_input) + n0 * img_in,
+                             (uint64_t)(nc * img_elems), stream);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+  }
+  return DCN_OK;
 }
 
 }  // namespace
@@ -198,61 +253,11 @@ int dcn_backward(const dcn_problem *p, const void *input, const void *offset, co
   if (st != DCN_OK) return st;
   if (p->n == 0) return DCN_OK;
   const bool wide = p->dtype == DCN_F32;  // grad_input accumulates in place
-  if (!input || !offset || !mask || !grad_output || !grad_input || !grad_offset || !grad_mask ||
-      (!wide && !workspace))
-    return DCN_ERR_NULL;
-  if (!aligned16(input) || !aligned16(offset) || !aligned16(mask) || !aligned16(grad_output) ||
-      !aligned16(grad_input) || !aligned16(grad_offset) || !aligned16(grad_mask) ||
-      (!wide && !aligned16(workspace)))
-    return DCN_ERR_ALIGN;
+  if (!wide && !workspace) return DCN_ERR_NULL;
+  if (!wide && !aligned16(workspace)) return DCN_ERR_ALIGN;
   if (!wide && workspace_bytes < workspace_bytes_bwd(p, ho, wo)) return DCN_ERR_WORKSPACE;
-
-  const int64_t K = npoints(p);
-  const int64_t eb = elem_bytes(p->dtype);
-  const int64_t img_elems = (int64_t)p->h * p->w * p->c;
-  const int64_t img_in = img_elems * eb;
-  const int64_t img_pg = ho * wo * p->groups;
-  const int64_t per = images_per_chunk_bwd(p, ho, wo);
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-
-  hipError_t e = hipSuccess;
-  if (wide) {
-    e = dcn::launch_zero(grad_input, (uint64_t)(p->n * img_in), stream);
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  dcn::BwdParams b{};
-  b.f = geometry(p, ho, wo);
-  for (int64_t n0 = 0; n0 < p->n; n0 += per) {
-    const int64_t nc = (p->n - n0 < per) ? p->n - n0 : per;
-    b.f.input = static_cast<const char *>(input) + n0 * img_in;
-    b.f.offset = static_cast<const char *>(offset) + n0 * img_pg * K * 2 * eb;
-    b.f.mask = static_cast<const char *>(mask) + n0 * img_pg * K * eb;
-    b.f.output = nullptr;
-    b.f.in_bytes = (uint32_t)(nc * img_in);
-    b.f.off_bytes = (uint32_t)(nc * img_pg * K * 2 * eb);
-    b.f.mask_bytes = (uint32_t)(nc * img_pg * K * eb);
-    b.f.out_bytes = 0;
-    b.f.pg_total = (uint32_t)(nc * img_pg);
-    b.grad_out = static_cast<const char *>(grad_output) + n0 * img_pg * dcn::kGroupChannels * eb;
-    b.grad_offset = static_cast<char *>(grad_offset) + n0 * img_pg * K * 2 * eb;
-    b.grad_mask = static_cast<char *>(grad_mask) + n0 * img_pg * K * eb;
-    if (wide) {
-      b.grad_in = static_cast<char *>(grad_input) + n0 * img_in;
-    } else {  // each chunk reuses the workspace: zero it, accumulate, round out
-      b.grad_in = workspace;
-      e = dcn::launch_zero(workspace, (uint64_t)(nc * img_elems * 4), stream);
-      if (e != hipSuccess) return hip_fail(e);
-    }
-    e = dcn::launch_backward(p->dtype, p->softmax, b, stream);
-    if (e == hipErrorNotSupported && !wide) return DCN_ERR_UNSUPPORTED;
-    if (e != hipSuccess) return hip_fail(e);
-    if (!wide) {
-      e = dcn::launch_narrow(p->dtype, workspace, static_cast<char *>(grad_input) + n0 * img_in,
-                             (uint64_t)(nc * img_elems), stream);
-      if (e != hipSuccess) return hip_fail(e);
-    }
-  }
-  return DCN_OK;
+  return run_backward(p, ho, wo, input, offset, mask, grad_output, grad_input, grad_offset, grad_mask,
+                      workspace, images_per_chunk_bwd(p, ho, wo), hip_stream);
 }
 
 const char *dcn_status_string(int status) {
@@ -260,7 +265,7 @@ const char *dcn_status_string(int status) {
     case DCN_OK: return "ok";
     case DCN_ERR_NULL: return "null pointer for a problem or a non-empty tensor";
     case DCN_ERR_SHAPE: return "invalid shape (dims, C % groups, kernel/stride/dilation/pad, or empty output)";
-    case DCN_ERR_UNSUPPORTED: return "unsupported dtype, channels per group, point count, or 16-bit backward";
+    case DCN_ERR_UNSUPPORTED: return "unsupported dtype, channels per group or point count";
     case DCN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case DCN_ERR_TOO_LARGE: return "a size exceeds the 32-bit index range of one image";
     case DCN_ERR_HIP: return g_hip_message;

@@ -41,30 +41,48 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 }  // namespace
 
+// Offset or mask value i of a block's rows staged in LDS in the I/O dtype.
+template <int DT>
+__device__ __forceinline__ float staged(const unsigned char *lds, uint32_t i) {
+  if constexpr (DT == DCN_F32) {
+    return reinterpret_cast<const float *>(lds)[i];
+  } else {
+    return Io<DT>::lo((uint32_t) reinterpret_cast<const uint16_t *>(lds)[i]);
+  }
+}
+
 // Untiled backward for any point set, stride and dilation: 16 lanes per
 // pixel-group, one channel per lane (one DPP row), so each corner's gather is
-// one 64-byte request and its grad_input scatter one 64-byte atomic request
-// of the row (a lane per channel: the hardware adds one fp32 per lane).
-template <int KH_, int KW_, bool SOFTMAX>
+// one request per pixel-group and its grad_input scatter one 64-byte atomic
+// request of the row (a lane per channel: the hardware adds one fp32 per
+// lane).  16-bit I/O (DT) reads its tensors as they are, computes in fp32,
+// accumulates grad_input in an fp32 buffer of the input's shape and rounds
+// grad_offset and grad_mask once to the I/O dtype.
+template <int DT, int KH_, int KW_, bool SOFTMAX>
 __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
+  using io = Io<DT>;
   const FwdParams &p = bp.f;
   constexpr int CG = kGroupChannels;
   constexpr int BLOCK_PG = kBlock / CG;
+  constexpr uint32_t EB = io::kBytes;
+  constexpr uint32_t GX = 4 / EB;  // input byte offset -> fp32 grad_input byte offset
   constexpr bool FIXED = KH_ > 0;
   const int KH = FIXED ? KH_ : p.KH;
   const int KW = FIXED ? KW_ : p.KW;
   const int K = FIXED ? KH_ * KW_ : KH * KW - p.RC;  // fixed extents never drop the centre
 
+  // LDS: the block's offset rows and mask rows (I/O dtype), then gm (fp32).
   extern __shared__ __align__(16) unsigned char lds[];
-  float *lds_off = reinterpret_cast<float *>(lds);
-  float *lds_mask = lds_off + BLOCK_PG * K * 2;
-  float *lds_gm = lds_mask + BLOCK_PG * K;
+  const unsigned char *lds_off = lds;
+  const unsigned char *lds_mask = lds + (uint32_t)BLOCK_PG * K * 2 * EB;
+  float *lds_gm = reinterpret_cast<float *>(lds + (uint32_t)BLOCK_PG * K * 3 * EB);
 
   const uint32_t blk = xcd_block(blockIdx.x, gridDim.x);
   const uint32_t pg0 = blk * BLOCK_PG;
   const uint32_t npg = min((uint32_t)BLOCK_PG, p.pg_total - pg0);
-  stage_to_lds(lds_off, static_cast<const float *>(p.offset) + (uint64_t)pg0 * K * 2, npg * K * 8);
-  stage_to_lds(lds_mask, static_cast<const float *>(p.mask) + (uint64_t)pg0 * K, npg * K * 4);
+  stage_to_lds(lds, static_cast<const unsigned char *>(p.offset) + (uint64_t)pg0 * K * 2 * EB, npg * K * 2 * EB);
+  stage_to_lds(lds + (uint32_t)BLOCK_PG * K * 2 * EB,
+               static_cast<const unsigned char *>(p.mask) + (uint64_t)pg0 * K * EB, npg * K * EB);
   __syncthreads();
 
   const uint32_t lp = threadIdx.x / CG;
@@ -85,33 +103,43 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
   float mx = 0.f, inv = 1.f;
   if constexpr (SOFTMAX) {
     mx = -INFINITY;
-    for (int k = 0; k < K; ++k) mx = fmaxf(mx, lds_mask[mrow + k]);
+    for (int k = 0; k < K; ++k) mx = fmaxf(mx, staged<DT>(lds_mask, mrow + k));
     float sum = 0.f;
-    for (int k = 0; k < K; ++k) sum += __expf(lds_mask[mrow + k] - mx);
+    for (int k = 0; k < K; ++k) sum += __expf(staged<DT>(lds_mask, mrow + k) - mx);
     inv = __builtin_amdgcn_rcpf(sum);
   }
   auto weight = [&](int k) -> float {
-    if constexpr (SOFTMAX) return __expf(lds_mask[mrow + k] - mx) * inv;
-    else return lds_mask[mrow + k];
+    if constexpr (SOFTMAX) return __expf(staged<DT>(lds_mask, mrow + k) - mx) * inv;
+    else return staged<DT>(lds_mask, mrow + k);
   };
 
-  const float gy = static_cast<const float *>(bp.grad_out)[(uint64_t)pg * CG + ch];
+  const float gy = io::one(bp.grad_out, (int64_t)pg * CG + ch);
 
-  constexpr uint32_t kBytes = 4;
-  const uint32_t pix_bytes = (uint32_t)p.C * kBytes;
+  const uint32_t pix_bytes = (uint32_t)p.C * EB;
   const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
-  const uint32_t base = n * (uint32_t)p.H * row_bytes + (g * CG + ch) * kBytes;
+  const uint32_t base = n * (uint32_t)p.H * row_bytes + (g * CG + ch) * EB;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
-  const __amdgpu_buffer_rsrc_t rgx = make_rsrc(bp.grad_in, p.in_bytes);
+  const __amdgpu_buffer_rsrc_t rgx = make_rsrc(bp.grad_in, p.in_bytes * GX);
   const int by = (int)ho * p.SH - p.PH;
   const int bx = (int)wo * p.SW - p.PW;
   const float s = p.scale;
-  float2 *goff = static_cast<float2 *>(bp.grad_offset) + (uint64_t)pg * K;
+  unsigned char *goff = static_cast<unsigned char *>(bp.grad_offset) + (uint64_t)pg * K * 2 * EB;
+
+  // One corner value of this lane's channel (0 at kOutOfRange).
+  auto corner = [&](uint32_t a) -> float {
+    if constexpr (DT == DCN_F32) {
+      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (int)a, 0, 0));
+    } else {
+      return io::lo((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rin, (int)a, 0, 0));
+    }
+  };
+  // grad_input offset of an input offset (fp32 elements; out of range stays so)
+  auto gxo = [&](uint32_t a) -> int { return (int)(a == kOutOfRange ? kOutOfRange : a * GX); };
 
   // Point k at grid position (ii, jj).
   auto point = [&](const int ii, const int jj, const int k) {
-    const float dx = s * lds_off[(mrow + k) * 2];
-    const float dy = s * lds_off[(mrow + k) * 2 + 1];
+    const float dx = s * staged<DT>(lds_off, (mrow + k) * 2);
+    const float dy = s * staged<DT>(lds_off, (mrow + k) * 2 + 1);
     const bool nan_loc = (dx != dx) | (dy != dy);
     // Clamp first (|s*offset| >= 2^24 is far outside any map, and an infinite
     // offset must not turn the fraction into Inf - Inf), then split into an
@@ -135,10 +163,7 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
     const uint32_t a10 = (vy1 && vx0) ? a00r + row_bytes : kOutOfRange;
     const uint32_t a11 = (vy1 && vx1) ? a00r + row_bytes + pix_bytes : kOutOfRange;
 
-    const float v00 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (int)a00, 0, 0));
-    const float v01 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (int)a01, 0, 0));
-    const float v10 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (int)a10, 0, 0));
-    const float v11 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (int)a11, 0, 0));
+    const float v00 = corner(a00), v01 = corner(a01), v10 = corner(a10), v11 = corner(a11);
     const float top = hx * v00 + lx * v01;  // row y0 along x
     const float bot = hx * v10 + lx * v11;  // row y0+1 along x
     const float gb = row16_sum(gy * (hy * top + ly * bot));
@@ -148,17 +173,22 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
     // pixel-group's LDS row and writes the offset gradient.
     if (ch == 0) {
       lds_gm[mrow + k] = nan_loc ? __builtin_nanf("") : gb;
-      goff[k] = nan_loc ? make_float2(__builtin_nanf(""), __builtin_nanf(""))
-                        : make_float2(s * mk * gdx, s * mk * gdy);
+      const float gox = nan_loc ? __builtin_nanf("") : s * mk * gdx;
+      const float goy = nan_loc ? __builtin_nanf("") : s * mk * gdy;
+      if constexpr (DT == DCN_F32) {
+        reinterpret_cast<float2 *>(goff)[k] = make_float2(gox, goy);
+      } else {
+        reinterpret_cast<uint32_t *>(goff)[k] = io::pack(gox, goy);
+      }
     }
 
     // Scatter m_k * w_corner * gy into grad_input (out-of-map corners carry
     // an offset beyond the buffer, and the hardware drops those atomics).
     const float g = mk * gy;
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * hy * hx, rgx, (int)a00, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * hy * lx, rgx, (int)a01, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * ly * hx, rgx, (int)a10, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * ly * lx, rgx, (int)a11, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * hy * hx, rgx, gxo(a00), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * hy * lx, rgx, gxo(a01), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * ly * hx, rgx, gxo(a10), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(g * ly * lx, rgx, gxo(a11), 0, 0);
   };
   if constexpr (FIXED) {
 #pragma unroll
@@ -183,10 +213,15 @@ __global__ void __launch_bounds__(kBlock) dcn_bwd_kernel(BwdParams bp) {
   if constexpr (SOFTMAX) {
     for (int k = 0; k < K; ++k) dot = fmaf(weight(k), lds_gm[mrow + k], dot);
   }
-  float *gmask = static_cast<float *>(bp.grad_mask) + (uint64_t)pg * K;
+  unsigned char *gmask = static_cast<unsigned char *>(bp.grad_mask) + (uint64_t)pg * K * EB;
   for (int k = (int)ch; k < K; k += CG) {
     const float gmk = lds_gm[mrow + k];
-    gmask[k] = SOFTMAX ? weight(k) * (gmk - dot) : gmk;
+    const float v = SOFTMAX ? weight(k) * (gmk - dot) : gmk;
+    if constexpr (DT == DCN_F32) {
+      reinterpret_cast<float *>(gmask)[k] = v;
+    } else {
+      reinterpret_cast<uint16_t *>(gmask)[k] = (uint16_t)(io::pack(v, 0.f) & 0xffffu);
+    }
   }
 }
 
@@ -209,38 +244,47 @@ __global__ void __launch_bounds__(kBlock) dcn_narrow_kernel(const float4 *src, u
 
 namespace {
 
-template <int KH, int KW, bool SM>
+template <int DT, int KH, int KW, bool SM>
 hipError_t launch_one(const BwdParams &p, hipStream_t s) {
   constexpr int BLOCK_PG = kBlock / kGroupChannels;
   const int K = p.f.KH * p.f.KW - p.f.RC;
-  const size_t lds = (size_t)BLOCK_PG * K * 4 * sizeof(float);
+  const size_t lds = (size_t)BLOCK_PG * K * (3 * Io<DT>::kBytes + 4);
   const uint32_t blocks = (p.f.pg_total + BLOCK_PG - 1) / BLOCK_PG;
-  hipLaunchKernelGGL((dcn_bwd_kernel<KH, KW, SM>), dim3(blocks), dim3(kBlock), lds, s, p);
+  hipLaunchKernelGGL((dcn_bwd_kernel<DT, KH, KW, SM>), dim3(blocks), dim3(kBlock), lds, s, p);
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_untiled(int softmax, const BwdParams &p, hipStream_t s) {
+  if (p.f.KH == 3 && p.f.KW == 3 && !p.f.RC)
+    return softmax ? launch_one<DT, 3, 3, true>(p, s) : launch_one<DT, 3, 3, false>(p, s);
+  return softmax ? launch_one<DT, 0, 0, true>(p, s) : launch_one<DT, 0, 0, false>(p, s);
 }
 
 }  // namespace
 
 // Backward path override for tests and measurements: DCN_MI355X_BWD_PATH =
-// "generic" (untiled kernel), "tiled" (the half-window tiled kernel) or
-// "quad" (the lane-quad tiled kernel, also the default where it applies).
-// 16-bit I/O has the quad kernel only (hipErrorNotSupported elsewhere).
+// "generic" (untiled kernel), "tiled" (the half-window tiled kernel, fp32
+// only) or "quad" (the lane-quad tiled kernel, also the default where it
+// applies).  Read at every call.
 hipError_t launch_backward(int dtype, int softmax, const BwdParams &p, hipStream_t s) {
-  if (dtype != DCN_F32) return launch_backward_quad(dtype, softmax, p, s);
   const char *e = getenv("DCN_MI355X_BWD_PATH");
   const bool generic = e && !strcmp(e, "generic");
   const bool halves = e && !strcmp(e, "tiled");
   if (!generic && !halves) {
-    const hipError_t q = launch_backward_quad(DCN_F32, softmax, p, s);
+    const hipError_t q = launch_backward_quad(dtype, softmax, p, s);
     if (q != hipErrorNotSupported) return q;
   }
-  if (!generic) {
+  if (!generic && dtype == DCN_F32) {
     const hipError_t t = launch_backward_tiled(softmax, p, s);
     if (t != hipErrorNotSupported) return t;
   }
-  if (p.f.KH == 3 && p.f.KW == 3 && !p.f.RC)
-    return softmax ? launch_one<3, 3, true>(p, s) : launch_one<3, 3, false>(p, s);
-  return softmax ? launch_one<0, 0, true>(p, s) : launch_one<0, 0, false>(p, s);
+  switch (dtype) {
+    case DCN_F32: return launch_untiled<DCN_F32>(softmax, p, s);
+    case DCN_F16: return launch_untiled<DCN_F16>(softmax, p, s);
+    case DCN_BF16: return launch_untiled<DCN_BF16>(softmax, p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_zero(void *dst, uint64_t bytes, hipStream_t s) {

@@ -59,7 +59,7 @@ struct BqGeom {
   static constexpr int kWin = kSpanW * kSpanH * kBqPixB;  // one window
   static constexpr int kZero = kRow + 2 * kBqPixB;        // zero block after the input window
   static constexpr int kSink = kRow + 2 * kBqPixB;        // scatter sink after the grad window
-  static constexpr size_t kLds = (size_t)kWin + kZero + kWin + kSink + 4 * kWaves;
+  static constexpr size_t kLds = (size_t)kWin + kZero + kWin + kSink + 8 * kWaves;
 };
 
 namespace {
@@ -116,6 +116,7 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
   typedef __attribute__((address_space(3))) unsigned char lds_byte;
   const uint32_t lbase = (uint32_t)(size_t)(lds_byte *)lds;
   float *wave_sums = reinterpret_cast<float *>(lds + SINK + G::kSink);
+  float *wave_mins = wave_sums + G::kWaves;
 
   const uint32_t quad = threadIdx.x >> 2, sub = threadIdx.x & 3;
   const int oy = (int)quad / TW, ox = (int)quad % TW;  // output pixel within the tile
@@ -304,14 +305,20 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
       for (int r = 0; r < 3; ++r) m[r] = lgs[r];
     }
 
-    // Fixed-point scale of the item's grad window.  Every window
-    // pixel-channel receives at most the sum over the tile's pixel-groups of
-    // sum_k |m_k| * max_c |gy_c| (the four corner weights of a sample are
-    // non-negative and add up to 1), call it B.  With S = 2^(30 - e), B <= 2^e,
-    // every partial sum of the scaled terms stays within 2^30, so the LDS
-    // integer adds sum them exactly; each term is rounded to the nearest
-    // multiple of 1/S.  A non-finite B (NaN or Inf in grad_output or the mask)
-    // sends the whole item to fp32 global atomics instead.
+    // Fixed-point scale of the item's grad window.  A pixel-group adds at
+    // most b = sum_k |m_k| * max_c |gy_c| to any window pixel-channel (the
+    // four corner weights of a sample are non-negative and add up to 1), so
+    // every partial sum there is at most B = the sum of b over the tile.
+    // With S = 2^(30 - e), B <= 2^e, the scaled partial sums stay within
+    // 2^30 and the LDS integer adds sum them exactly; each term is rounded to
+    // the nearest multiple of 1/S, so an element that receives n terms is off
+    // by at most n * 2^(e - 31) <= n * B * 2^-30.  That bound is set by the
+    // whole tile, so the item takes fixed point only where it is small
+    // against every contributor: B <= 2^12 * (the smallest nonzero b of the
+    // tile), which keeps the error within n * 2^-18 of the bound b of each
+    // pixel-group whose samples reach the element.  Tiles with a wider spread
+    // (an outlier in grad_output or the mask) and a non-finite B (NaN or Inf
+    // there) send the whole item to fp32 global atomics instead.
     {
       float gmax = 0.f, nanflag = 0.f;
 #pragma unroll
@@ -322,16 +329,27 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
       const float msum = quad_sum(fabsf(m[0]) + fabsf(m[1]) + fabsf(m[2]));
       float bound = quad_max(gmax) * msum + quad_sum(nanflag);
       bound = (cur.live && sub == 0) ? bound : 0.f;
+      float bmin = bound > 0.f ? bound : INFINITY;
 #pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) bound += __shfl_xor(bound, d, 64);
-      if ((threadIdx.x & 63) == 0) wave_sums[threadIdx.x >> 6] = bound;
+      for (int d = 32; d >= 1; d >>= 1) {
+        bound += __shfl_xor(bound, d, 64);
+        bmin = fminf(bmin, __shfl_xor(bmin, d, 64));
+      }
+      if ((threadIdx.x & 63) == 0) {
+        wave_sums[threadIdx.x >> 6] = bound;
+        wave_mins[threadIdx.x >> 6] = bmin;
+      }
     }
     __syncthreads();  // the window is in LDS, the wave bounds are ready
 
-    float B = 0.f;
+    float B = 0.f, bmin = INFINITY;
 #pragma unroll
-    for (int wv = 0; wv < G::kWaves; ++wv) B += wave_sums[wv];
-    const bool fixed = B <= 3.0e38f;  // false for Inf and NaN (block-uniform)
+    for (int wv = 0; wv < G::kWaves; ++wv) {
+      B += wave_sums[wv];
+      bmin = fminf(bmin, wave_mins[wv]);
+    }
+    // false for Inf and NaN, and for a spread above 2^12 (block-uniform)
+    const bool fixed = B <= 3.0e38f && B <= kFixedSpread * bmin;
     int ex = 0;
     frexpf(B, &ex);
     ex = ex < -96 ? -96 : ex;

@@ -206,7 +206,10 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
     // every partial sum of the scaled terms stays within 2^30, so the LDS
     // integer adds (two channels per 64-bit add) sum them exactly; each term
     // is rounded to the nearest multiple of 1/S.  A non-finite B (NaN or Inf
-    // in grad_out or the mask) switches the half to fp32 global atomics.
+    // in grad_out or the mask), or a spread above 2^12 between B and the
+    // smallest nonzero per-pixel-group bound (so that rounding to the tile's
+    // grid stays small against every contributor), switches the half to fp32
+    // global atomics.
     float gmax = 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) gmax = fmaxf(gmax, fabsf(gyh[c]));
@@ -214,11 +217,18 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
     float bound = live ? msum * gmax : 0.f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) bound += live ? 0.f * gyh[c] : 0.f;
+    float lmin = bound > 0.f ? bound : INFINITY;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) bound += __shfl_xor(bound, d, 64);
+    for (int d = 32; d >= 1; d >>= 1) {
+      bound += __shfl_xor(bound, d, 64);
+      lmin = fminf(lmin, __shfl_xor(lmin, d, 64));
+    }
 
     __syncthreads();  // the previous half's flush has read gwin, every read of win is done
-    if ((lane & 63) == 0) wave_sums[lane / 64] = bound;
+    if ((lane & 63) == 0) {
+      wave_sums[lane / 64] = bound;
+      wave_sums[WAVES + lane / 64] = lmin;
+    }
 #pragma unroll
     for (int u = 0; u < SLOTS; ++u) {
       const int idx = (int)sq + u * STAGERS;
@@ -234,10 +244,14 @@ __global__ void __launch_bounds__(kBwdThreads, 2) dcn_bwd_tile_kernel(BwdParams 
     }
     __syncthreads();  // both half-windows and the wave bounds are ready
 
-    float B = 0.f;
+    float B = 0.f, bmin = INFINITY;
 #pragma unroll
-    for (int wv = 0; wv < WAVES; ++wv) B += wave_sums[wv];
-    const bool fixed = B <= 3.0e38f;  // false for Inf and NaN (block-uniform)
+    for (int wv = 0; wv < WAVES; ++wv) {
+      B += wave_sums[wv];
+      bmin = fminf(bmin, wave_sums[WAVES + wv]);
+    }
+    // false for Inf and NaN, and for a spread above 2^12 (block-uniform)
+    const bool fixed = B <= 3.0e38f && B <= kFixedSpread * bmin;
     int e = 0;
     frexpf(B, &e);
     e = e < -96 ? -96 : e;
@@ -405,7 +419,7 @@ namespace {
 template <bool SM>
 hipError_t launch_bwd_tile(const BwdParams &p, const TileGeom &tg, hipStream_t s) {
   auto kern = dcn_bwd_tile_kernel<SM>;
-  const size_t lds = 2 * (size_t)kBwdWinBytes + 16;  // two windows + the wave bounds
+  const size_t lds = 2 * (size_t)kBwdWinBytes + 32;  // two windows + the wave bounds
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -9,6 +9,12 @@
 
 namespace dcn {
 
+// Largest ratio between a tile's fixed-point bound B (the sum over its
+// pixel-groups of sum_k |m_k| * max_c |gy_c|) and its smallest nonzero
+// per-pixel-group term for which the tiled backward kernels accumulate
+// grad_input in fixed point; a wider spread takes fp32 atomics.
+constexpr float kFixedSpread = 4096.f;
+
 // ---------------------------------------------------------------- raw buffers
 // A raw buffer resource (stride 0, num_records in bytes).  Loads whose byte
 // offset lies beyond num_records return 0 and stores/atomics there are

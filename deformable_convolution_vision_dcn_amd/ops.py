@@ -119,18 +119,10 @@ def dcn_forward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor, *, gr
     return out
 
 
-def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
-                 grad_out: torch.Tensor, *, groups: int, kernel=3, stride=1, pad=1, dilation=1,
-                 offset_scale: float = 2.0, softmax: bool = True, remove_center: bool = False,
-                 grad_input: Optional[torch.Tensor] = None,
-                 grad_offset: Optional[torch.Tensor] = None,
-                 grad_mask: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None):
-    """Backward of the DCN core; returns (grad_input, grad_offset, grad_mask).
-
-    16-bit I/O accumulates grad_input in an fp32 device workspace
-    (``backward_workspace_bytes``); pass a ``workspace`` tensor on x's device
-    to reuse one, else a fresh one is taken from torch's allocator."""
+def _backward_args(x, offset, mask, grad_out, groups, kernel, stride, pad, dilation, offset_scale, softmax,
+                   remove_center, grad_input, grad_offset, grad_mask):
+    """Checked problem and gradient tensors of a backward call (allocated
+    here when not given)."""
     p, shp = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax, remove_center)
     _expect(x, "input", x.shape, x.dtype, x.device)
     _expect(offset, "offset", shp["offset"], x.dtype, x.device)
@@ -149,6 +141,24 @@ def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
     _no_alias(outs, [("input", x), ("offset", offset), ("mask", mask), ("grad_out", grad_out)])
     for k, (a, ta) in enumerate(outs):
         _no_alias([(a, ta)], outs[k + 1:])
+    return p, outs
+
+
+def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
+                 grad_out: torch.Tensor, *, groups: int, kernel=3, stride=1, pad=1, dilation=1,
+                 offset_scale: float = 2.0, softmax: bool = True, remove_center: bool = False,
+                 grad_input: Optional[torch.Tensor] = None,
+                 grad_offset: Optional[torch.Tensor] = None,
+                 grad_mask: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
+    """Backward of the DCN core; returns (grad_input, grad_offset, grad_mask).
+
+    16-bit I/O accumulates grad_input in an fp32 device workspace
+    (``backward_workspace_bytes``); pass a ``workspace`` tensor on x's device
+    to reuse one, else a fresh one is taken from torch's allocator."""
+    p, outs = _backward_args(x, offset, mask, grad_out, groups, kernel, stride, pad, dilation, offset_scale,
+                             softmax, remove_center, grad_input, grad_offset, grad_mask)
+    grad_input, grad_offset, grad_mask = (t for _, t in outs)
     st, ws_bytes = _capi.dcn_backward_workspace_size(p)
     _capi.raise_on(st)
     if workspace is None and ws_bytes:
@@ -200,7 +210,7 @@ class DCNCore(torch.autograd.Function):
 
 def dcn_core(x, offset, mask, *, groups, kernel=3, stride=1, pad=1, dilation=1,
              offset_scale=2.0, softmax=True, remove_center=False):
-    """Differentiable DCN core (backward in the HIP library: fp32, or 16-bit for
-    3x3 points at stride 1 and dilation 1 or 2)."""
+    """Differentiable DCN core (forward and backward in the HIP library, fp32
+    or 16-bit I/O)."""
     return DCNCore.apply(x, offset, mask, groups, kernel, stride, pad, dilation, offset_scale,
                          softmax, remove_center)

@@ -21,7 +21,13 @@
  *   section 3.3; odd kernel sizes only) drops the centre point (i, j) =
  *   (kernel_h/2, kernel_w/2): K = kernel_h*kernel_w - 1, the points keep the
  *   row-major order with the centre skipped (point k at or past the centre's
- *   index sits at grid index k + 1) and the softmax runs over those K.  Ho = (H + 2*pad_h - dilation_h*(kernel_h-1) - 1)/stride_h + 1
+ *   index sits at grid index k + 1) and the softmax runs over those K.
+ *
+ *   Output extent (the convolution arithmetic behind the pages' statements
+ *   that pad = kernel_size // 2 keeps a stride-1 output at the input's size,
+ *   pnsm.cn/news/2029644.html section 3.3 and trdm.cn/news/584307, "DCNv3
+ *   operator compilation", section 2.3):
+ *     Ho = (H + 2*pad_h - dilation_h*(kernel_h-1) - 1) / stride_h + 1
  *   (integer division; the same form gives Wo).  Cg = C / groups.
  *
  * Layouts (all tensors dense and contiguous, row-major, one dtype per call):
@@ -37,22 +43,32 @@
  * Ownership and execution: every tensor pointer is a DEVICE pointer owned by
  * the caller.  The library allocates nothing, keeps no pointer after it
  * returns and has no mutable global state, so calls are reentrant.  Work is
- * enqueued on the caller's hipStream_t (NULL = the null stream) and the call
- * returns without waiting: DCN_OK means "validated and enqueued".  Outputs are
- * overwritten, never accumulated into, and must not alias any input.
+ * enqueued on the caller's hipStream_t (NULL = the null
+ * stream) and the call returns without waiting: DCN_OK means "validated and
+ * enqueued".  Outputs are overwritten, never accumulated into, and must not
+ * alias any input.
  *
- * Kernel choice: the forward picks its kernel from the problem (dtype, point
- * count, stride, dilation, map and window size; the forward with
- * remove_center runs the untiled kernel).  The environment variable
+ * Kernel choice (3x3 points unless noted): output maps smaller than one
+ * 16x16 tile, or that such tiles would leave over half empty, run the
+ * whole-map kernel; other maps whose tile window fits the LDS run a tiled
+ * kernel (fp32: the quad kernel, two groups per work item where the group
+ * count is even; 16-bit I/O and fp32 without the centre: the lane kernel);
+ * everything else (other point sets, strides whose windows do not fit) runs
+ * the untiled kernel.  The backward runs the tiled quad kernel at stride 1
+ * and dilation 1 or 2, else the untiled kernel.  The environment variable
  * DCN_MI355X_FWD_PATH = "generic" | "tiled" (one group per work item) |
  * "pair" (two groups per work item) | "lane" | "map" (whole maps in LDS),
- * read at every call, makes it try that kernel first; DCN_MI355X_BWD_PATH =
- * "generic" | "tiled" (half windows) | "quad" does the same for the
- * backward.  Results agree to rounding either way.
+ * read at every call, makes the forward try that kernel first;
+ * DCN_MI355X_BWD_PATH = "generic" | "tiled" (half windows, fp32) | "quad"
+ * does the same for the backward.  Results agree to rounding either way.
  *
  * Errors: every entry point returns DCN_OK (0) or a negative dcn_status.
- * Nothing is enqueued when a check fails.  N == 0 is valid and enqueues
- * nothing.  There is no fallback path: an unsupported problem is an error.
+ * Nothing is enqueued when a check fails (every check of the problem, the
+ * pointers and the workspace runs before the first launch).  A DCN_ERR_HIP
+ * from a launch can come after earlier launches of the same call (a chunk,
+ * or the grad_input clear) were enqueued: the outputs are then partly
+ * written and must be discarded.  N == 0 is valid and enqueues nothing.
+ * There is no fallback path: an unsupported problem is an error.
  */
 #ifndef DCN_MI355X_H
 #define DCN_MI355X_H
@@ -63,7 +79,7 @@
 extern "C" {
 #endif
 
-#define DCN_ABI_VERSION 3
+#define DCN_ABI_VERSION 4
 
 /* Element type of every tensor of one call. */
 typedef enum dcn_dtype {
@@ -79,8 +95,7 @@ typedef enum dcn_status {
                                  stride or dilation < 1, pad < 0, Ho/Wo < 1, or no
                                  point left (1x1 with remove_center)                   */
     DCN_ERR_UNSUPPORTED = -3, /* dtype, channels-per-group or point count (K > 64)
-                                 without a kernel, or a 16-bit backward other than
-                                 3x3 points at stride 1, dilation 1 or 2               */
+                                 without a kernel                                      */
     DCN_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned                */
     DCN_ERR_TOO_LARGE = -5,   /* one image's input, output or offset tensor exceeds
                                  2^31-1 bytes, or H or W exceeds 2^24 (16-bit
@@ -135,12 +150,19 @@ int dcn_backward_workspace_size(const dcn_problem *p, uint64_t *bytes);
  *   grad_mask   = gradient with respect to the mask tensor as passed: through
  *                 the softmax Jacobian when softmax != 0.
  * At integer sampling coordinates the derivative is the one-sided one from the
- * right (the floor convention).  fp32 for every shape.  16-bit I/O (all
- * tensors of the call in that dtype) for 3x3 points (remove_center or not)
- * at stride 1 and dilation 1 or 2 (equal on both axes), else
- * DCN_ERR_UNSUPPORTED.  The arithmetic is fp32 throughout and grad_input
- * is accumulated in fp32: sums per output tile in fixed point, added with
- * fp32 atomics (so its low bits can vary from run to run).  For fp32 the sums
+ * right (the floor convention).  Every shape, in fp32 and in 16-bit I/O (all
+ * tensors of the call in that dtype).  The arithmetic is fp32 throughout and
+ * grad_input is accumulated in fp32 atomics, so its low bits can vary from
+ * run to run.  The tiled kernel (3x3 points, stride 1, dilation 1 or 2) first
+ * sums each output tile's scatter in fixed point on the tile's own grid: a
+ * term is rounded to a multiple of 2^(e-30), where 2^e bounds the tile's sum
+ * B of sum_k |m_k| * max_c |grad_output_c| over its pixel-groups, so an
+ * element reached by n terms is off by at most n * 2^(e-31) <= n * B * 2^-30.
+ * A tile whose B exceeds 2^12 times its smallest nonzero per-pixel-group term
+ * (an outlier in grad_output or the mask), or is not finite, adds its terms
+ * with fp32 atomics instead; so the fixed-point error of an element stays
+ * within n * 2^-18 of the term bound of every pixel-group that reaches it.
+ * For fp32 the sums
  * land in grad_input itself (the call zeroes it first) and workspace may be
  * NULL.  For 16-bit I/O they land in `workspace`, a caller-owned device
  * buffer of at least dcn_backward_workspace_size bytes, 16-byte aligned, whose

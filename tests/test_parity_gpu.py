@@ -197,17 +197,40 @@ def check_sampled(wl, t, y, pixels):
         gate(got, ref, wl.dtype, f"{wl.name} image {n}")
 
 
+def check_every_image(wl, t, y):
+    """Compare every output element of y (GPU, full batch) with the oracle,
+    one image per oracle call (an image's output depends on that image only),
+    the calls spread over a thread pool (the oracle keeps no state and ctypes
+    releases the GIL)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    kw = wl.op_kwargs()
+    x, off, m = t["x"], t["offset"], t["mask"]
+    yh = y.cpu()  # one copy to the host; the pool threads touch host memory only
+
+    def one(n):
+        sl = slice(n, n + 1)
+        ref = oracle.forward(_np(x[sl]), _np(off[sl]), _np(m[sl]), **kw)
+        gate(_np(yh[sl]), ref, wl.dtype, f"{wl.name} image {n}")
+        return n
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), wl.n))
+    with ThreadPoolExecutor(workers) as pool:
+        done = list(pool.map(one, range(wl.n)))
+    assert done == list(range(wl.n))
+
+
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_named_workload_forward(name):
+    """Every named workload at full size, every output element against the
+    oracle."""
     wl = synth.WORKLOADS[name]
-    print(f"forward {name} (full size)", flush=True)
+    print(f"forward {name} (full size, every pixel)", flush=True)
     t = synth.make_inputs(wl, with_grad=False)
     y = run_forward(wl, t)
     assert torch.isfinite(y).all()
-    if wl.samples <= 5_000_000:
-        gate(_np(y), oracle_full(wl, t), wl.dtype, name)
-    else:
-        check_sampled(wl, t, y, sampled_pixels(wl, 3000))
+    check_every_image(wl, t, y)
 
 
 def test_forward_multi_chunk():
@@ -317,6 +340,56 @@ BWD16 = [
     Workload("bwd16_12x12", n=3, h=12, w=12, c=64, groups=4, softmax=False, mask_dist=normal(0.5),
              seed=70),
 ]
+
+
+# Shapes the tiled backward does not take (other strides, dilations and
+# point sets): the untiled kernel, with 16-bit I/O accumulating in fp32.
+BWD16_UNTILED = [
+    Workload("bwd16_stride2", n=2, h=15, w=17, c=32, groups=2, stride=(2, 2), offset_dist=normal(2.0), seed=71),
+    Workload("bwd16_stride2_dil2", n=2, h=15, w=17, c=32, groups=2, stride=(2, 2), dilation=(2, 2),
+             pad=(2, 2), seed=72),
+    Workload("bwd16_k5", n=1, h=9, w=8, c=32, groups=2, kernel=(5, 5), pad=(2, 2), seed=73),
+    Workload("bwd16_k3x5_v4", n=1, h=8, w=11, c=48, groups=3, kernel=(3, 5), pad=(1, 2), softmax=False,
+             mask_dist=normal(0.5), seed=74),
+    Workload("bwd16_rc_k5x3_s2", n=1, h=15, w=12, c=32, groups=2, kernel=(5, 3), pad=(2, 1), stride=(2, 1),
+             dilation=(1, 2), remove_center=True, seed=75),
+    Workload("bwd16_k1", n=2, h=6, w=7, c=32, groups=2, kernel=(1, 1), pad=(0, 0), offset_dist=uniform(3.0),
+             seed=76),
+    Workload("bwd16_dil_1x2", n=1, h=19, w=23, c=16, groups=1, dilation=(1, 2), pad=(1, 2),
+             offset_dist=uniform(5.0), seed=77),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("wl", BWD16_UNTILED, ids=lambda w: w.name)
+def test_backward_16bit_untiled_shapes(wl, dtype):
+    """16-bit backward on shapes outside the tiled kernel's (stride 2, 5x5,
+    3x5, 1x1, dilation on one axis, remove_center on a 5x3 grid), against the
+    oracle on the 16-bit gate."""
+    wl = wl.replace(dtype=dtype)
+    print(f"backward {wl.name} {dtype}", flush=True)
+    t = synth.make_inputs(wl, with_grad=True)
+    gx, goff, gm = run_backward(wl, t)
+    rx, roff, rm = oracle_backward(wl, t)
+    gate(_np(gx), rx, dtype, f"{wl.name}/{dtype} grad_input")
+    gate(_np(goff), roff, dtype, f"{wl.name}/{dtype} grad_offset")
+    gate(_np(gm), rm, dtype, f"{wl.name}/{dtype} grad_mask")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("wl", [BWD16[2], BWD16[5], BWD16[7]], ids=lambda w: w.name)
+def test_backward_16bit_forced_untiled(wl, dtype, monkeypatch):
+    """The untiled 16-bit backward forced on shapes the tiled kernel takes by
+    default (ragged far offsets, remove_center, dilation 2)."""
+    monkeypatch.setenv("DCN_MI355X_BWD_PATH", "generic")
+    wl = wl.replace(dtype=dtype)
+    print(f"backward {wl.name} {dtype} path=generic", flush=True)
+    t = synth.make_inputs(wl, with_grad=True)
+    gx, goff, gm = run_backward(wl, t)
+    rx, roff, rm = oracle_backward(wl, t)
+    gate(_np(gx), rx, dtype, f"{wl.name}/{dtype}/generic grad_input")
+    gate(_np(goff), roff, dtype, f"{wl.name}/{dtype}/generic grad_offset")
+    gate(_np(gm), rm, dtype, f"{wl.name}/{dtype}/generic grad_mask")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -500,6 +573,148 @@ def test_far_offsets_give_exact_zeros(dtype):
         t["offset"] = torch.full_like(t["offset"], big)
         y = run_forward(wl, t)
         assert torch.all(y == 0), big
+
+
+@pytest.mark.parametrize("path", ["auto", "generic", "tiled"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_far_offsets_backward_exact_zeros(dtype, path, monkeypatch):
+    """Offsets that put every sample off the map (+-1e4, +-Inf, 3e38, on both
+    axes or on one): every gradient is exactly zero, as the oracle's pinned
+    far-away branch gives (zero padding: B = 0 and dB = 0 off the map)."""
+    if path != "auto":
+        if dtype != "f32" and path == "tiled":
+            pytest.skip("the half-window tiled backward is fp32 only")
+        monkeypatch.setenv("DCN_MI355X_BWD_PATH", path)
+    wl = Workload("far_bwd", n=2, h=19, w=21, c=32, groups=2, dtype=dtype, seed=46)
+    t = synth.make_inputs(wl, with_grad=True)
+    rng = np.random.default_rng(9)
+    for big in (1e4, -1e4, float("inf"), -float("inf"), 3e38):
+        for axes in ((0, 1), (0,), (1,)):
+            off = torch.from_numpy(rng.standard_normal(t["offset"].shape).astype(np.float32))
+            for a in axes:
+                off[..., a] = big
+            t["offset"] = off.to(t["x"].dtype)
+            print(f"backward far offsets {big} axes {axes} {dtype} path={path}", flush=True)
+            gx, goff, gm = run_backward(wl, t)
+            rx, roff, rm = oracle_backward(wl, t)
+            assert np.all(rx == 0) and np.all(roff == 0) and np.all(rm == 0)
+            assert torch.all(gx == 0), (big, axes, "grad_input")
+            assert torch.all(goff == 0), (big, axes, "grad_offset")
+            assert torch.all(gm == 0), (big, axes, "grad_mask")
+
+
+GUARD = 256  # elements of canary on each side of every output buffer
+
+
+def _guarded(shape, dtype, fill):
+    """A tensor of `shape` inside a buffer with GUARD canary elements on each
+    side; returns (view, buffer)."""
+    numel = int(np.prod(shape))
+    buf = torch.full((numel + 2 * GUARD,), fill, dtype=dtype, device=DEV)
+    return buf[GUARD:GUARD + numel].view(shape), buf
+
+
+def _canaries_intact(buf, fill, what):
+    head, tail = buf[:GUARD], buf[-GUARD:]
+    assert torch.all(head == fill) and torch.all(tail == fill), f"{what}: a guard band was written"
+
+
+@pytest.mark.parametrize("path", ["auto", "generic", "tiled"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_guard_bands_untouched(dtype, path, monkeypatch):
+    """grad_input, grad_offset, grad_mask and the 16-bit fp32 workspace each
+    sit between two guard bands of canary values; a multi-tile problem whose
+    offsets reach far outside the tile windows and the map (the global
+    fix-up and atomic paths) must leave every band as it was, call after
+    call, and give the oracle's gradients."""
+    if path != "auto":
+        if dtype != "f32" and path == "tiled":
+            pytest.skip("the half-window tiled backward is fp32 only")
+        monkeypatch.setenv("DCN_MI355X_BWD_PATH", path)
+    wl = Workload("guard_bwd", n=2, h=37, w=29, c=48, groups=3, dtype=dtype, offset_dist=uniform(8.0), seed=47)
+    t = synth.make_inputs(wl, with_grad=True)
+    x, off, m, gy = (t[k].to(DEV) for k in ("x", "offset", "mask", "grad_out"))
+    fill = 12345.0 if dtype == "f32" else 1234.0
+    gx, bx = _guarded(x.shape, x.dtype, fill)
+    goff, boff = _guarded(off.shape, x.dtype, fill)
+    gm, bm = _guarded(m.shape, x.dtype, fill)
+    need = dcn.backward_workspace_bytes(x, **wl.op_kwargs())
+    ws = bws = None
+    if need:
+        ws, bws = _guarded((need // 4,), torch.float32, -777.0)
+    rx, roff, rm = oracle_backward(wl, t)
+    for call in range(2):
+        print(f"backward guard bands {dtype} path={path} call {call}", flush=True)
+        dcn.dcn_backward(x, off, m, gy, grad_input=gx, grad_offset=goff, grad_mask=gm,
+                         workspace=None if ws is None else ws.view(torch.uint8), **wl.op_kwargs())
+        torch.cuda.synchronize()
+        _canaries_intact(bx, fill, "grad_input")
+        _canaries_intact(boff, fill, "grad_offset")
+        _canaries_intact(bm, fill, "grad_mask")
+        if bws is not None:
+            _canaries_intact(bws, -777.0, "workspace")
+        gate(_np(gx), rx, dtype, f"guarded grad_input call {call}")
+        gate(_np(goff), roff, dtype, f"guarded grad_offset call {call}")
+        gate(_np(gm), rm, dtype, f"guarded grad_mask call {call}")
+
+
+@pytest.mark.parametrize("path", ["auto", "tiled"])
+@pytest.mark.parametrize("softmax", [True, False], ids=["dcnv3_gy_outlier", "dcnv4_mask_outlier"])
+def test_backward_outlier_per_tile(softmax, path, monkeypatch):
+    """Heavy-tailed gradients: in every other 16x16 output tile one
+    pixel-group carries terms 1e4 times the others (DCNv3: its grad_output
+    row scaled by 1e4; DCNv4: its unnormalised mask row).  grad_input
+    elements that none of those pixel-groups' samples reach keep the fp32
+    bar of 1e-4 against the oracle; elements they reach are held to 1e-4 of
+    their sum of absolute terms (the oracle's grad_input with |grad_output|
+    and |mask|); the outliers' own offset and mask rows to 1e-4 of their
+    largest value, and every other offset and mask gradient to 1e-4."""
+    monkeypatch.setenv("DCN_MI355X_BWD_PATH", path)
+    wl = Workload("outlier", n=2, h=48, w=40, c=32, groups=2, softmax=softmax,
+                  mask_dist=normal(1.0 if softmax else 0.5), offset_dist=normal(1.5), seed=48)
+    t = synth.make_inputs(wl, with_grad=True)
+    rng = np.random.default_rng(10)
+    ho, wo = wl.out_hw
+    hot = []  # (n, ho, wo, g) of the outliers
+    for n in range(wl.n):
+        for g in range(wl.groups):
+            for ty in range(0, ho, 16):
+                for tx in range(0, wo, 16):
+                    if (ty // 16 + tx // 16 + g) % 2 == 0:
+                        hot.append((n, int(rng.integers(ty, min(ty + 16, ho))),
+                                    int(rng.integers(tx, min(tx + 16, wo))), g))
+    for (n, y, xx, g) in hot:
+        if softmax:
+            t["grad_out"][n, y, xx, 16 * g:16 * g + 16] *= 1e4
+        else:
+            t["mask"][n, y, xx, g] *= 1e4
+    print(f"backward outliers softmax={softmax} path={path} ({len(hot)} outliers)", flush=True)
+    gx, goff, gm = (_np(a) for a in run_backward(wl, t))
+    rx, roff, rm = oracle_backward(wl, t)
+    # the outliers' scatter alone (grad_output zero elsewhere) marks the
+    # grad_input elements they reach
+    keep = torch.zeros(t["grad_out"].shape, dtype=torch.bool)
+    for (n, y, xx, g) in hot:
+        keep[n, y, xx, 16 * g:16 * g + 16] = True
+    only = dict(t, grad_out=torch.where(keep, t["grad_out"], torch.zeros_like(t["grad_out"])))
+    reach = np.abs(oracle_backward(wl, only)[0]) > 0
+    assert reach.any() and not reach.all()
+    # sum of the absolute scatter terms of every element
+    absd = dict(t, grad_out=t["grad_out"].abs(), mask=t["mask"] if softmax else t["mask"].abs())
+    scale = oracle_backward(wl, absd)[0]
+    err = np.abs(gx - rx)
+    assert err[~reach].max() <= ATOL_F32, f"grad_input away from the outliers: {err[~reach].max():.3e}"
+    worst = float(np.max(err[reach] / np.maximum(1.0, scale[reach])))
+    assert worst <= 1e-4, f"grad_input near the outliers: {worst:.3e} of the absolute terms"
+    rows = np.zeros(rm.shape[:4], dtype=bool)
+    for h_ in hot:
+        rows[h_] = True
+    for got, ref, name in ((goff, roff, "grad_offset"), (gm, rm, "grad_mask")):
+        e = np.abs(got - ref).reshape(rows.shape + (-1,))
+        r = np.abs(ref).reshape(rows.shape + (-1,))
+        assert e[~rows].max() <= ATOL_F32, f"{name} of ordinary pixel-groups: {e[~rows].max():.3e}"
+        rowmax = np.maximum(1.0, r[rows].max(axis=-1, keepdims=True))
+        assert np.all(e[rows] <= 1e-4 * rowmax), f"{name} of the outliers"
 
 
 def test_nan_offset_poisons_only_its_group():

@@ -7,8 +7,10 @@ dtype -- and runs the forward on every kernel in turn (forced through
 DCN_MI355X_FWD_PATH; a kernel that does not apply falls back to the generic
 one) and, for fp32, the backward on every backward kernel.  The bar is the
 same as the fixed cases: max-abs 1e-4 in fp32, |d| <= 2e-2 |ref| + 1e-3 for
-16-bit outputs.  A second series of draws, held to 3x3 points at stride and
-dilation 1, runs the 16-bit backward.
+16-bit outputs.  The 16-bit draws also run the 16-bit backward on every
+backward kernel that takes them (default and untiled), and a second series
+of draws, held to the tiled backward's shape (3x3 points at stride 1), runs
+it on the tiled kernel.
 """
 import numpy as np
 import pytest
@@ -80,6 +82,24 @@ def test_random_backward_every_kernel(seed, monkeypatch):
         gate(_np(goff), roff, "f32", f"{wl.name}/{path} grad_offset")
         gate(_np(gm), rm, "f32", f"{wl.name}/{path} grad_mask")
 
+
+
+@pytest.mark.parametrize("seed", [s for s in SEEDS if s % 3 != 0])  # the 16-bit draws
+def test_random_backward_16bit_any_shape(seed, monkeypatch):
+    wl = random_problem(seed)
+    assert wl.dtype in ("f16", "bf16")
+    t = synth.make_inputs(wl, with_grad=True)
+    rx, roff, rm = oracle_backward(wl, t)
+    for path in ["auto", "generic"]:
+        if path == "auto":
+            monkeypatch.delenv("DCN_MI355X_BWD_PATH", raising=False)
+        else:
+            monkeypatch.setenv("DCN_MI355X_BWD_PATH", path)
+        print(f"backward {wl} path={path}", flush=True)
+        gx, goff, gm = run_backward(wl, t)
+        gate(_np(gx), rx, wl.dtype, f"{wl.name}/{wl.dtype}/{path} grad_input")
+        gate(_np(goff), roff, wl.dtype, f"{wl.name}/{wl.dtype}/{path} grad_offset")
+        gate(_np(gm), rm, wl.dtype, f"{wl.name}/{wl.dtype}/{path} grad_mask")
 
 
 def random_problem_16(seed: int) -> Workload:
