@@ -37,9 +37,15 @@ def test_algorithmic_bytes():
     assert rc.samples == pg * 8
 
 
-def test_forward_kernel_names_follow_the_dispatch():
-    assert bench.forward_kernel_name(synth.WORKLOADS["stage1_dcnv3_f32"]) == "dcn_fwd_tile_kernel"
-    assert bench.forward_kernel_name(synth.WORKLOADS["stage2_dcnv4_f16"]) == "dcn_fwd_lane_kernel"
-    assert bench.forward_kernel_name(synth.WORKLOADS["stage4_dcnv4_f16"]) == "dcn_fwd_map_kernel"
-    assert bench.forward_kernel_name(synth.WORKLOADS["stage4_dcnv4_f16"].replace(remove_center=True)) == \
-        "dcn_fwd_map_kernel"
+def test_kernel_names_are_shortened_from_the_trace():
+    name = ("void dcn::dcn_fwd_tile_kernel<0, true, 16, 16, 8, 1, 2, false>(dcn::FwdParams, "
+            "dcn::TileGeom)")
+    assert bench.short_kernel_name(name) == "dcn_fwd_tile_kernel"
+    assert bench.short_kernel_name("dcn::dcn_bwd_quad_kernel<0, true>") == "dcn_bwd_quad_kernel"
+    assert bench.short_kernel_name("elementwise_kernel") == "elementwise_kernel"
+
+
+def test_host_cpu_report():
+    h = bench.host_cpu()
+    assert h["cores_available"] >= 1 and 1 <= h["cores_usable"] <= bench.GPU_HOST_SHARE
+    assert isinstance(h["model"], str) and h["model"]
