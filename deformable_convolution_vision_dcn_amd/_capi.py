@@ -13,7 +13,10 @@ import pathlib
 LIB_PATH = pathlib.Path(os.environ.get(
     "DCN_MI355X_LIB", pathlib.Path(__file__).resolve().parent / "libdcn_mi355x.so"))
 
-ABI_VERSION = 4
+ABI_VERSION = 5
+
+# bytes of the library's fixed scratch behind dcn_backward_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 DCN_F32, DCN_F16, DCN_BF16 = 0, 1, 2
 
@@ -28,6 +31,7 @@ STATUS = {
     -7: "DCN_ERR_ABI",
     -8: "DCN_ERR_ARG",
     -9: "DCN_ERR_WORKSPACE",
+    -10: "DCN_ERR_SCRATCH",
 }
 CODES = {v: k for k, v in STATUS.items()}
 
@@ -90,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.dcn_forward.argtypes = [P, vp, vp, vp, vp, vp]
         L.dcn_backward.restype = ctypes.c_int
         L.dcn_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+        L.dcn_backward_noalloc.restype = ctypes.c_int
+        L.dcn_backward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.dcn_backward_workspace_size.restype = ctypes.c_int
         L.dcn_backward_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_uint64)]
         L.dcn_status_string.restype = ctypes.c_char_p
@@ -132,6 +138,12 @@ def dcn_backward(p: dcn_problem, input_ptr, offset_ptr, mask_ptr, grad_out_ptr, 
     return lib().dcn_backward(ctypes.byref(p), input_ptr, offset_ptr, mask_ptr, grad_out_ptr,
                               grad_in_ptr, grad_offset_ptr, grad_mask_ptr, workspace_ptr,
                               workspace_bytes, stream)
+
+
+def dcn_backward_noalloc(p: dcn_problem, input_ptr, offset_ptr, mask_ptr, grad_out_ptr, grad_in_ptr,
+                         grad_offset_ptr, grad_mask_ptr, stream) -> int:
+    return lib().dcn_backward_noalloc(ctypes.byref(p), input_ptr, offset_ptr, mask_ptr, grad_out_ptr,
+                                      grad_in_ptr, grad_offset_ptr, grad_mask_ptr, stream)
 
 
 def raise_on(status: int) -> None:

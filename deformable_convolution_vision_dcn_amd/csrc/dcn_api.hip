@@ -4,7 +4,18 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "dcn_launch.hpp"
+
+// The fp32 grad_input accumulator of dcn_backward_noalloc's 16-bit chunks:
+// device memory the library owns, one copy per GPU, held until the process
+// ends.  Host code never passes this name to a kernel (on the host it is a
+// stand-in, not a device address): it uses the address that
+// hipGetSymbolAddress reports for the current device.
+constexpr uint64_t kScratchBytes = uint64_t(DCN_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -194,6 +205,32 @@ int run_backward(const dcn_problem *p, int64_t ho, int64_t wo, const void *input
   return DCN_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_lock;
+
+int scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return DCN_ERR_UNSUPPORTED;
+  void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> hold(g_scratch_lock);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e);
+      if (!ptr) return hip_fail(hipErrorInvalidSymbol);
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return DCN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -260,6 +297,26 @@ int dcn_backward(const dcn_problem *p, const void *input, const void *offset, co
                       workspace, images_per_chunk_bwd(p, ho, wo), hip_stream);
 }
 
+int dcn_backward_noalloc(const dcn_problem *p, const void *input, const void *offset, const void *mask,
+                         const void *grad_output, void *grad_input, void *grad_offset, void *grad_mask,
+                         void *hip_stream) {
+  int64_t ho = 0, wo = 0;
+  const int st = validate_backward(p, &ho, &wo);
+  if (st != DCN_OK) return st;
+  if (p->n == 0) return DCN_OK;
+  int64_t per = images_per_chunk_bwd(p, ho, wo);
+  void *ws = nullptr;
+  if (p->dtype != DCN_F32) {
+    const int64_t img32 = (int64_t)p->h * p->w * p->c * 4;
+    if (img32 > (int64_t)kScratchBytes) return DCN_ERR_SCRATCH;
+    if ((int64_t)kScratchBytes / img32 < per) per = (int64_t)kScratchBytes / img32;
+    const int sst = scratch_address(&ws);
+    if (sst != DCN_OK) return sst;
+  }
+  return run_backward(p, ho, wo, input, offset, mask, grad_output, grad_input, grad_offset, grad_mask, ws,
+                      per, hip_stream);
+}
+
 const char *dcn_status_string(int status) {
   switch (status) {
     case DCN_OK: return "ok";
@@ -272,6 +329,7 @@ const char *dcn_status_string(int status) {
     case DCN_ERR_ABI: return "dcn_problem.struct_size does not match this library";
     case DCN_ERR_ARG: return "invalid argument value (softmax or remove_center flag, or offset_scale)";
     case DCN_ERR_WORKSPACE: return "workspace smaller than dcn_backward_workspace_size reports";
+    case DCN_ERR_SCRATCH: return "dcn_backward_noalloc: one image's fp32 grad_input accumulator exceeds the library's fixed scratch";
     default: return "unknown status";
   }
 }

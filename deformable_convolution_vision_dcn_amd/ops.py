@@ -179,6 +179,27 @@ def dcn_backward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
     return grad_input, grad_offset, grad_mask
 
 
+def dcn_backward_noalloc(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor,
+                         grad_out: torch.Tensor, *, groups: int, kernel=3, stride=1, pad=1, dilation=1,
+                         offset_scale: float = 2.0, softmax: bool = True, remove_center: bool = False,
+                         grad_input: Optional[torch.Tensor] = None,
+                         grad_offset: Optional[torch.Tensor] = None,
+                         grad_mask: Optional[torch.Tensor] = None):
+    """dcn_backward through the library's allocation-free entry point: 16-bit
+    I/O accumulates in the library's fixed per-GPU scratch instead of a
+    workspace.  With the gradient tensors passed in, the call allocates no
+    device memory; 16-bit calls on one GPU must not overlap."""
+    p, outs = _backward_args(x, offset, mask, grad_out, groups, kernel, stride, pad, dilation, offset_scale,
+                             softmax, remove_center, grad_input, grad_offset, grad_mask)
+    grad_input, grad_offset, grad_mask = (t for _, t in outs)
+    with torch.cuda.device(x.device):
+        st = _capi.dcn_backward_noalloc(p, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
+                                        grad_out.data_ptr(), grad_input.data_ptr(),
+                                        grad_offset.data_ptr(), grad_mask.data_ptr(), _stream(x.device))
+    _capi.raise_on(st)
+    return grad_input, grad_offset, grad_mask
+
+
 def backward_workspace_bytes(x: torch.Tensor, *, groups: int, kernel=3, stride=1, pad=1, dilation=1,
                              offset_scale: float = 2.0, softmax: bool = True,
                              remove_center: bool = False) -> int:

@@ -41,9 +41,10 @@
  * are fp32 for every I/O dtype; 16-bit results are rounded to nearest-even.
  *
  * Ownership and execution: every tensor pointer is a DEVICE pointer owned by
- * the caller.  The library allocates nothing, keeps no pointer after it
- * returns and has no mutable global state, so calls are reentrant.  Work is
- * enqueued on the caller's hipStream_t (NULL = the null
+ * the caller.  dcn_forward and dcn_backward allocate nothing, keep no
+ * pointer after they return and touch no mutable global state, so calls are
+ * reentrant (dcn_backward_noalloc's fixed scratch is the one exception; see
+ * there).  Work is enqueued on the caller's hipStream_t (NULL = the null
  * stream) and the call returns without waiting: DCN_OK means "validated and
  * enqueued".  Outputs are overwritten, never accumulated into, and must not
  * alias any input.
@@ -79,7 +80,11 @@
 extern "C" {
 #endif
 
-#define DCN_ABI_VERSION 4
+#define DCN_ABI_VERSION 5
+
+/* Bytes of the fixed device scratch behind dcn_backward_noalloc (one copy
+ * per GPU the library runs on, held until the process ends). */
+#define DCN_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* Element type of every tensor of one call. */
 typedef enum dcn_dtype {
@@ -104,8 +109,11 @@ typedef enum dcn_status {
     DCN_ERR_ABI = -7,         /* problem->struct_size != sizeof(dcn_problem)            */
     DCN_ERR_ARG = -8,         /* softmax or remove_center not 0/1, remove_center with
                                  an even kernel size, or offset_scale not finite       */
-    DCN_ERR_WORKSPACE = -9    /* dcn_backward's workspace_bytes below what
+    DCN_ERR_WORKSPACE = -9,   /* dcn_backward's workspace_bytes below what
                                  dcn_backward_workspace_size reports                   */
+    DCN_ERR_SCRATCH = -10     /* dcn_backward_noalloc, 16-bit I/O: one image's fp32
+                                 grad_input accumulator (H*W*C*4 bytes) exceeds
+                                 DCN_NOALLOC_SCRATCH_BYTES                             */
 } dcn_status;
 
 /* One problem description.  Set struct_size = sizeof(dcn_problem). */
@@ -175,6 +183,27 @@ int dcn_backward_workspace_size(const dcn_problem *p, uint64_t *bytes);
 int dcn_backward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
                  const void *grad_output, void *grad_input, void *grad_offset, void *grad_mask,
                  void *workspace, uint64_t workspace_bytes, void *hip_stream);
+
+/* dcn_backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same checks, kernels and results as dcn_backward, with the 16-bit fp32
+ * grad_input accumulator in a fixed device scratch the library owns
+ * (DCN_NOALLOC_SCRATCH_BYTES on each GPU, part of the library's device code,
+ * so the HIP runtime reserves it when it loads that code) instead of a caller
+ * workspace.  The batch runs in chunks of images whose accumulator fits the
+ * scratch (so possibly more chunks than dcn_backward); each chunk clears it with a fill
+ * kernel, so whatever a previous call left there does not matter.  16-bit
+ * I/O with one image's accumulator (H*W*C*4 bytes) above the scratch returns
+ * DCN_ERR_SCRATCH before enqueueing anything.  fp32 needs no scratch and
+ * behaves exactly like dcn_backward without a workspace.  The call allocates
+ * nothing: the scratch's device address is looked up once per device, on the
+ * first call made with that device current, and kept.
+ * Every call on one GPU shares that GPU's scratch: 16-bit calls that may
+ * overlap on the device (other streams, other host threads) race and must be
+ * ordered by the caller, for instance on one stream. */
+int dcn_backward_noalloc(const dcn_problem *p, const void *input, const void *offset, const void *mask,
+                         const void *grad_output, void *grad_input, void *grad_offset, void *grad_mask,
+                         void *hip_stream);
 
 /* Static description of a status code.  For DCN_ERR_HIP the string carries
  * the HIP runtime's message from the calling thread's most recent failure. */

@@ -29,8 +29,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["dcn_abi_version", "dcn_backward", "dcn_backward_workspace_size",
-                                    "dcn_check", "dcn_forward", "dcn_status_string"]
+    assert declared_functions() == ["dcn_abi_version", "dcn_backward", "dcn_backward_noalloc",
+                                    "dcn_backward_workspace_size", "dcn_check", "dcn_forward",
+                                    "dcn_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -190,6 +191,28 @@ def test_argument_checks_before_any_device_call(lib):
     # an invalid problem is reported before the pointers are looked at
     pbad = _capi.make_problem(**{**BASE, "groups": 3})
     assert F(pbad, None, None, None, None, None) == _capi.CODES["DCN_ERR_SHAPE"]
+
+
+def test_noalloc_backward_checks_before_any_device_call(lib):
+    """dcn_backward_noalloc runs dcn_backward's checks on the host; a 16-bit
+    image whose fp32 accumulator exceeds the fixed scratch is refused before
+    anything is enqueued (the fake pointers are never dereferenced)."""
+    m = re.search(r"#define DCN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", HEADER.read_text())
+    assert int(m.group(1)) << int(m.group(2)) == _capi.NOALLOC_SCRATCH_BYTES
+    NB = _capi.dcn_backward_noalloc
+    a = 0x10000
+    p = _capi.make_problem(**BASE)
+    assert NB(p, a, a, a, a, a, a, None, None) == _capi.CODES["DCN_ERR_NULL"]
+    assert NB(p, a, a, a, a, a + 4, a, a, None) == _capi.CODES["DCN_ERR_ALIGN"]
+    assert NB(_capi.make_problem(**{**BASE, "groups": 3}), a, a, a, a, a, a, a, None) == _capi.CODES["DCN_ERR_SHAPE"]
+    p0 = _capi.make_problem(**{**BASE, "n": 0, "dtype": _capi.DCN_BF16})
+    assert NB(p0, None, None, None, None, None, None, None, None) == 0
+    # 2048 x 2048 x 16 bf16: a 256 MiB fp32 accumulator per image, above the scratch
+    big = _capi.make_problem(**{**BASE, "n": 1, "h": 2048, "w": 2048, "c": 16, "groups": 1,
+                                "dtype": _capi.DCN_BF16})
+    assert 2048 * 2048 * 16 * 4 > _capi.NOALLOC_SCRATCH_BYTES
+    assert NB(big, a, a, a, a, a, a, a, None) == _capi.CODES["DCN_ERR_SCRATCH"]
+    assert "scratch" in _capi.dcn_status_string(_capi.CODES["DCN_ERR_SCRATCH"])
 
 
 def test_backward_workspace_sizes(lib):
