@@ -422,7 +422,7 @@ def main() -> int:
     for _ in range(max(args.flush_iters, 1)):
         scratch.fill_(1.0)
         ftimes += timed_launches(lambda i: fwd(0), stream, 1)[1]
-        torch.sum(scratch, out=sink)
+        torch.sum(scratch, dim=0, out=sink)
         rtimes += timed_launches(lambda i: fwd(0), stream, 1)[1]
     del scratch, sink
     ftimes.sort()
