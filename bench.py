@@ -346,6 +346,12 @@ def main() -> int:
     ap.add_argument("--command", default="", help="command recorded in --summarize-counters")
     args = ap.parse_args()
 
+    import deformable_convolution_vision_dcn_amd as dcn
+    from deformable_convolution_vision_dcn_amd import synth
+
+    # output extents of the workloads from the library's own host-side check
+    synth.set_out_hw(lambda wl: dcn.dcn_check((wl.n, wl.h, wl.w, wl.c), **wl.op_kwargs()))
+
     if args.summarize_counters:
         text = summarize_counters(pathlib.Path(args.summarize_counters),
                                   args.workload or "stage1_dcnv3_f32", args.kernel or "dcn_fwd_tile_kernel",
@@ -370,9 +376,6 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes_read": a.numel() * 4,
                           "copy_calibration_bytes_written": b.numel() * 4, "launches": 5}))
         return 0
-
-    import deformable_convolution_vision_dcn_amd as dcn
-    from deformable_convolution_vision_dcn_amd import synth
 
     wl = synth.WORKLOADS[args.workload or synth.HEADLINE]
     if args.remove_center:

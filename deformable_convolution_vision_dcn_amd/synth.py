@@ -60,6 +60,17 @@ def uniform(half_width: float) -> Dist:
 
 ZERO = Dist("zero", 0.0)
 
+# The output extent of a problem is part of the operator's arithmetic, which
+# this module does not hold: the process drawing inputs installs a function
+# workload -> (Ho, Wo) for it (the test suite and the smoke check use the
+# oracle's, the benchmark the library's own host-side check).
+_out_hw_fn = None
+
+
+def set_out_hw(fn) -> None:
+    global _out_hw_fn
+    _out_hw_fn = fn
+
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
@@ -87,10 +98,11 @@ class Workload:
 
     @property
     def out_hw(self) -> Tuple[int, int]:
-        (kh, kw), (sh, sw), (ph, pw), (dh, dw) = self.kernel, self.stride, self.pad, self.dilation
-        ho = (self.h + 2 * ph - dh * (kh - 1) - 1) // sh + 1
-        wo = (self.w + 2 * pw - dw * (kw - 1) - 1) // sw + 1
-        return ho, wo
+        """Output extent (Ho, Wo), from the function installed by set_out_hw."""
+        if _out_hw_fn is None:
+            raise RuntimeError("synth.set_out_hw() must install the output-extent function first")
+        ho, wo = _out_hw_fn(self)
+        return int(ho), int(wo)
 
     @property
     def points(self) -> int:

@@ -178,6 +178,12 @@ def out_size(in_size, kernel, stride, pad, dilation):
     return default().out_size(in_size, kernel, stride, pad, dilation)
 
 
+def out_hw(wl):
+    """(Ho, Wo) of a synth.Workload from the oracle's own output-size rule."""
+    return (out_size(wl.h, wl.kernel[0], wl.stride[0], wl.pad[0], wl.dilation[0]),
+            out_size(wl.w, wl.kernel[1], wl.stride[1], wl.pad[1], wl.dilation[1]))
+
+
 def forward(*args, **kwargs):
     return default().forward(*args, **kwargs)
 
