@@ -17,6 +17,11 @@ Layouts (the pages' NHWC convention, pnsm.cn/news/2029644.html section 2.3):
 K = KH*KW points, or KH*KW - 1 with remove_center=True (odd KH and KW; the
 centre point is dropped, pnsm.cn/news/2029644.html section 3.3).
 
+Beside the core: ``linear`` (a linear layer), ``forward_om`` (the core with
+its offsets and mask generated from a guide feature by two linear branches,
+wmrh.cn/news/61976 section 二 steps 2-3) and ``forward_proj`` (the core
+followed by the output_proj linear layer, step 4).
+
 Every function here is pinned by ``tests/test_oracle_pins.py``; no function is
 parity-unpinned.
 """
@@ -81,6 +86,13 @@ class Oracle:
         lib.ref_forward_pixels.argtypes = [P, D, D, D, I, ctypes.c_int64, D]
         lib.ref_backward.restype = None
         lib.ref_backward.argtypes = [P, D, D, D, D, D, D, D]
+        i64 = ctypes.c_int64
+        lib.ref_linear.restype = None
+        lib.ref_linear.argtypes = [i64, i64, i64, D, D, D, D]
+        lib.ref_forward_om.restype = None
+        lib.ref_forward_om.argtypes = [P, D, D, i64, D, D, D, D, D]
+        lib.ref_forward_proj.restype = None
+        lib.ref_forward_proj.argtypes = [P, D, D, D, D, D, D]
         self._lib = lib
 
     def out_size(self, in_size, kernel, stride, pad, dilation):
@@ -163,6 +175,65 @@ class Oracle:
         return gx, goff, gmask
 
 
+    def linear(self, x, w, b=None):
+        """fp64 linear layer over the last axis: x (..., nin), w (nout, nin),
+        b (nout) or None; returns (..., nout)."""
+        x, w = _f64(x), _f64(w)
+        nin = x.shape[-1]
+        if w.ndim != 2 or w.shape[1] != nin:
+            raise ValueError(f"weight shape {w.shape} does not match {nin} input features")
+        nout = w.shape[0]
+        bb = None if b is None else _f64(b)
+        if bb is not None and bb.shape != (nout,):
+            raise ValueError("bias shape mismatch")
+        rows = x.size // nin if nin else 0
+        out = np.zeros(x.shape[:-1] + (nout,), dtype=np.float64)
+        self._lib.ref_linear(rows, nin, nout, _dptr(x), _dptr(w), None if bb is None else _dptr(bb), _dptr(out))
+        return out
+
+    def forward_om(self, x, guide, w_offset, b_offset, w_mask, b_mask, *, groups, kernel=3, stride=1,
+                   pad=1, dilation=1, offset_scale=2.0, softmax=True, remove_center=False):
+        """fp64 forward with the offsets and mask generated from ``guide``
+        (N, Ho, Wo, Cgd) by the linear branches w_offset (G*K*2, Cgd),
+        b_offset and w_mask (G*K, Cgd), b_mask (biases may be None)."""
+        x, guide, wo_, wm = _f64(x), _f64(guide), _f64(w_offset), _f64(w_mask)
+        p, ho, wo, K = self._problem(x.shape, groups, kernel, stride, pad, dilation,
+                                     offset_scale, softmax, remove_center)
+        n, cgd = x.shape[0], guide.shape[-1]
+        if guide.shape != (n, ho, wo, cgd):
+            raise ValueError(f"guide shape {guide.shape} != {(n, ho, wo, cgd)}")
+        if wo_.shape != (groups * K * 2, cgd) or wm.shape != (groups * K, cgd):
+            raise ValueError("generation weight shapes do not match")
+        bo = None if b_offset is None else _f64(b_offset)
+        bm = None if b_mask is None else _f64(b_mask)
+        if (bo is not None and bo.shape != (groups * K * 2,)) or (bm is not None and bm.shape != (groups * K,)):
+            raise ValueError("generation bias shapes do not match")
+        y = np.zeros((n, ho, wo, x.shape[3]), dtype=np.float64)
+        self._lib.ref_forward_om(ctypes.byref(p), _dptr(x), _dptr(guide), cgd, _dptr(wo_),
+                                 None if bo is None else _dptr(bo), _dptr(wm),
+                                 None if bm is None else _dptr(bm), _dptr(y))
+        return y
+
+    def forward_proj(self, x, offset, mask, w_out, b_out, *, groups, kernel=3, stride=1, pad=1,
+                     dilation=1, offset_scale=2.0, softmax=True, remove_center=False):
+        """fp64 forward followed by the output projection w_out (C, C), b_out
+        (C) or None."""
+        x, offset, mask, w = _f64(x), _f64(offset), _f64(mask), _f64(w_out)
+        p, ho, wo, K = self._problem(x.shape, groups, kernel, stride, pad, dilation,
+                                     offset_scale, softmax, remove_center)
+        self._check_shapes(x, offset, mask, groups, ho, wo, K)
+        c = x.shape[3]
+        if w.shape != (c, c):
+            raise ValueError(f"w_out shape {w.shape} != {(c, c)}")
+        b = None if b_out is None else _f64(b_out)
+        if b is not None and b.shape != (c,):
+            raise ValueError("b_out shape mismatch")
+        out = np.zeros((x.shape[0], ho, wo, c), dtype=np.float64)
+        self._lib.ref_forward_proj(ctypes.byref(p), _dptr(x), _dptr(offset), _dptr(mask), _dptr(w),
+                                   None if b is None else _dptr(b), _dptr(out))
+        return out
+
+
 _default = None
 
 
@@ -194,3 +265,15 @@ def forward_pixels(*args, **kwargs):
 
 def backward(*args, **kwargs):
     return default().backward(*args, **kwargs)
+
+
+def linear(*args, **kwargs):
+    return default().linear(*args, **kwargs)
+
+
+def forward_om(*args, **kwargs):
+    return default().forward_om(*args, **kwargs)
+
+
+def forward_proj(*args, **kwargs):
+    return default().forward_proj(*args, **kwargs)

@@ -49,6 +49,17 @@
  *   dL/dmask  : gm_k = sum_c gy_c * B_k[c]; for DCNv3 through the softmax
  *               Jacobian, gl_k = m_k * (gm_k - sum_j m_j gm_j).
  *
+ * The steps before and after the core [P5 §二 steps 2-4]: a linear layer of
+ * the guide feature gives, per output pixel, the 2K offset components and
+ * the K mask values of every group (two branches of the same linear
+ * structure, step 2 for the offsets and step 3 for the scores); after the
+ * weighted sum, the output_proj linear layer maps the C channels of each
+ * pixel to C channels (step 4).  A linear layer here is
+ *   out[q, o] = sum_c in[q, c] * W[o, c] + b[o]
+ * for every row q (W row-major, out_features x in_features; b optional).
+ * The offset rows of W are ordered (g, k, e): row g*K*2 + k*2 + e gives
+ * component e (0 = x, 1 = y) of point k of group g; the mask rows (g, k).
+ *
  * Non-finite values: a NaN offset makes that sample NaN; an infinite offset
  * puts the sample outside the map, where B = 0, so it contributes m_k * 0
  * (0 for a finite m_k, NaN for a NaN or infinite one, as IEEE arithmetic
@@ -297,4 +308,51 @@ void ref_backward(const ref_problem *p, const double *x, const double *off, cons
                 }
     free(m);
     free(gm);
+}
+
+/* A linear layer over `rows` rows: out (rows, nout) = in (rows, nin) times
+ * the transpose of w (nout, nin), plus b (nout) when b is not NULL. */
+void ref_linear(int64_t rows, int64_t nin, int64_t nout, const double *in, const double *w,
+                const double *b, double *out)
+{
+    for (int64_t q = 0; q < rows; ++q)
+        for (int64_t o = 0; o < nout; ++o) {
+            double acc = b ? b[o] : 0.0;
+            for (int64_t c = 0; c < nin; ++c)
+                acc += in[q * nin + c] * w[o * nin + c];
+            out[q * nout + o] = acc;
+        }
+}
+
+/* The core with its offsets and mask generated from a guide feature
+ * (N, Ho, Wo, cgd) by the two linear branches w_off (G*K*2, cgd), b_off and
+ * w_mask (G*K, cgd), b_mask (biases may be NULL): y is (N, Ho, Wo, C). */
+void ref_forward_om(const ref_problem *p, const double *x, const double *guide, int64_t cgd,
+                    const double *w_off, const double *b_off, const double *w_mask,
+                    const double *b_mask, double *y)
+{
+    int64_t Ho = ref_out_size(p->h, p->kh, p->stride_h, p->pad_h, p->dil_h);
+    int64_t Wo = ref_out_size(p->w, p->kw, p->stride_w, p->pad_w, p->dil_w);
+    int64_t npix = p->n * Ho * Wo, K = npoints(p);
+    double *off = (double *)malloc(sizeof(double) * (size_t)(npix * p->groups * K * 2));
+    double *mask = (double *)malloc(sizeof(double) * (size_t)(npix * p->groups * K));
+    ref_linear(npix, cgd, p->groups * K * 2, guide, w_off, b_off, off);
+    ref_linear(npix, cgd, p->groups * K, guide, w_mask, b_mask, mask);
+    ref_forward(p, x, off, mask, y);
+    free(off);
+    free(mask);
+}
+
+/* The core followed by the output_proj linear layer w_out (C, C), b_out (C)
+ * (b_out may be NULL): out is (N, Ho, Wo, C). */
+void ref_forward_proj(const ref_problem *p, const double *x, const double *off, const double *mask,
+                      const double *w_out, const double *b_out, double *out)
+{
+    int64_t Ho = ref_out_size(p->h, p->kh, p->stride_h, p->pad_h, p->dil_h);
+    int64_t Wo = ref_out_size(p->w, p->kw, p->stride_w, p->pad_w, p->dil_w);
+    int64_t npix = p->n * Ho * Wo;
+    double *y = (double *)malloc(sizeof(double) * (size_t)(npix * p->c));
+    ref_forward(p, x, off, mask, y);
+    ref_linear(npix, p->c, p->c, y, w_out, b_out, out);
+    free(y);
 }

@@ -628,10 +628,138 @@ def pin_backward_nan_offset_is_local(orc):
             _close(gm[keep], rgm[keep], 1e-12, "grad_mask beside a NaN point (DCNv4)")
 
 
+# --------------------------------------------------------------------------- the steps before and after
+
+def pin_linear_is_matmul(orc):
+    """The oracle's linear layer equals a library matrix product, x w^T + b,
+    over any leading shape, with and without a bias."""
+    rng = np.random.default_rng(120)
+    for shape, nin, nout in [((5,), 7, 3), ((2, 3, 4), 16, 54), ((1,), 1, 1)]:
+        x = rng.standard_normal(shape + (nin,))
+        w = rng.standard_normal((nout, nin))
+        b = rng.standard_normal(nout)
+        _close(orc.linear(x, w, b), np.matmul(x, w.T) + b, 1e-12, f"linear {shape} {nin}->{nout}")
+        _close(orc.linear(x, w, None), np.matmul(x, w.T), 1e-12, f"linear without bias {shape}")
+
+
+def _om_case(rng, n, h, w, c, g, cgd, kernel=(3, 3), stride=(1, 1), pad=(1, 1), dilation=(1, 1), rc=False,
+             wscale=0.3):
+    ho = _out(h, kernel[0], stride[0], pad[0], dilation[0])
+    wo = _out(w, kernel[1], stride[1], pad[1], dilation[1])
+    K = len(_points(kernel, rc))
+    x = rng.standard_normal((n, h, w, c))
+    guide = rng.standard_normal((n, ho, wo, cgd))
+    w_off = rng.standard_normal((g * K * 2, cgd)) * wscale
+    b_off = rng.standard_normal(g * K * 2)
+    w_mask = rng.standard_normal((g * K, cgd)) * wscale
+    b_mask = rng.standard_normal(g * K)
+    return x, guide, w_off, b_off, w_mask, b_mask
+
+
+def pin_generation_zero_weights_is_box_average(orc):
+    """With the generation weights and biases all zero (the initialisation
+    the pages describe, wmrh.cn/news/61976 section 二, the "细节亮点" note:
+    offsets and mask start at zero, so the operator starts as a plain 3x3
+    convolution) the offsets are 0 and the logits 0: DCNv3 is then the
+    zero-padded 3x3 box average of x, whatever the guide."""
+    rng = np.random.default_rng(121)
+    n, h, w, c, g, cgd = 2, 7, 6, 32, 2, 24
+    x, guide, w_off, b_off, w_mask, b_mask = _om_case(rng, n, h, w, c, g, cgd)
+    z = lambda a: np.zeros_like(a)
+    y = orc.forward_om(x, guide, z(w_off), z(b_off), z(w_mask), z(b_mask), **_kw(g))
+    xt = torch.from_numpy(x).permute(0, 3, 1, 2)
+    ref = F.avg_pool2d(xt, 3, stride=1, padding=1, count_include_pad=True).permute(0, 2, 3, 1).numpy()
+    _close(y, ref, 1e-14, "generation with zero weights")
+    y0 = orc.forward_om(x, guide, z(w_off), None, z(w_mask), None, **_kw(g))
+    _close(y0, ref, 1e-14, "generation with zero weights and no biases")
+
+
+def pin_generation_is_linear_then_core(orc):
+    """forward_om equals torch's F.linear for the two branches, reshaped to
+    (N, Ho, Wo, G, K, 2) and (N, Ho, Wo, G, K), fed to the grid_sample
+    composition of the core (fp64 torch), over several geometries, both mask
+    kinds and without the centre."""
+    rng = np.random.default_rng(122)
+    for cs in _LIB_CASES:
+        rc = cs.get("rc", False)
+        for softmax in (True, False):
+            cgd = 12
+            x, guide, w_off, b_off, w_mask, b_mask = _om_case(
+                rng, cs["n"], cs["h"], cs["w"], cs["c"], cs["g"], cgd, cs["kernel"], cs["stride"], cs["pad"],
+                cs["dilation"], rc)
+            kw = _kw(cs["g"], cs["kernel"], cs["stride"], cs["pad"], cs["dilation"], cs["s"], softmax, rc)
+            y = orc.forward_om(x, guide, w_off, b_off, w_mask, b_mask, **kw)
+            gt = torch.from_numpy(guide)
+            n, ho, wo, _ = guide.shape
+            K = len(_points(cs["kernel"], rc))
+            off = F.linear(gt, torch.from_numpy(w_off), torch.from_numpy(b_off)).reshape(n, ho, wo, cs["g"], K, 2)
+            m = F.linear(gt, torch.from_numpy(w_mask), torch.from_numpy(b_mask)).reshape(n, ho, wo, cs["g"], K)
+            ref = _grid_sample_core(torch.from_numpy(x), off, m, cs["g"], cs["kernel"], cs["stride"], cs["pad"],
+                                    cs["dilation"], cs["s"], softmax, rc)
+            _close(y, ref.numpy(), 1e-12, f"generation then core {cs} softmax={softmax}")
+
+
+def pin_generation_brute_force_tiny(orc):
+    """Tiny shapes: each offset component and mask value summed term by term
+    in plain Python floats from the weights' (out, in) layout, then the
+    scalar forward loop."""
+    rng = np.random.default_rng(123)
+    for cs in [dict(h=4, w=5, c=2, g=1, cgd=3, kernel=(3, 3), rc=False),
+               dict(h=3, w=4, c=4, g=2, cgd=5, kernel=(3, 3), rc=True)]:
+        for softmax in (True, False):
+            x, guide, w_off, b_off, w_mask, b_mask = _om_case(rng, 1, cs["h"], cs["w"], cs["c"], cs["g"], cs["cgd"],
+                                                               cs["kernel"], rc=cs["rc"])
+            n, ho, wo, cgd = guide.shape
+            K = len(_points(cs["kernel"], cs["rc"]))
+            off = np.zeros((n, ho, wo, cs["g"], K, 2))
+            m = np.zeros((n, ho, wo, cs["g"], K))
+            for oy in range(ho):
+                for ox in range(wo):
+                    for g in range(cs["g"]):
+                        for k in range(K):
+                            for e in range(2):
+                                row = (g * K + k) * 2 + e
+                                off[0, oy, ox, g, k, e] = float(b_off[row]) + sum(
+                                    float(guide[0, oy, ox, q]) * float(w_off[row, q]) for q in range(cgd))
+                            row = g * K + k
+                            m[0, oy, ox, g, k] = float(b_mask[row]) + sum(
+                                float(guide[0, oy, ox, q]) * float(w_mask[row, q]) for q in range(cgd))
+            args = (cs["g"], cs["kernel"], (1, 1), (1, 1), (1, 1), 2.0, softmax, cs["rc"])
+            ref = _brute_forward(x, off, m, *args)
+            _close(orc.forward_om(x, guide, w_off, b_off, w_mask, b_mask, **_kw(*args)), ref, 1e-12,
+                   f"generation brute force {cs} softmax={softmax}")
+
+
+def pin_output_projection(orc):
+    """forward_proj equals torch's F.linear applied to the grid_sample
+    composition of the core; the identity projection returns the core's
+    output, a channel permutation permutes it."""
+    rng = np.random.default_rng(124)
+    for cs in _LIB_CASES[:3] + _LIB_CASES[4:5]:
+        rc = cs.get("rc", False)
+        for softmax in (True, False):
+            x, off, m = _random_case(rng, cs["n"], cs["h"], cs["w"], cs["c"], cs["g"], cs["kernel"], cs["stride"],
+                                     cs["pad"], cs["dilation"], off_std=2.0, rc=rc)
+            c = cs["c"]
+            w_out = rng.standard_normal((c, c))
+            b_out = rng.standard_normal(c)
+            kw = _kw(cs["g"], cs["kernel"], cs["stride"], cs["pad"], cs["dilation"], cs["s"], softmax, rc)
+            core = _grid_sample_core(torch.from_numpy(x), torch.from_numpy(off), torch.from_numpy(m), cs["g"],
+                                     cs["kernel"], cs["stride"], cs["pad"], cs["dilation"], cs["s"], softmax, rc)
+            ref = F.linear(core, torch.from_numpy(w_out), torch.from_numpy(b_out)).numpy()
+            _close(orc.forward_proj(x, off, m, w_out, b_out, **kw), ref, 1e-12, f"projection {cs} softmax={softmax}")
+            _close(orc.forward_proj(x, off, m, np.eye(c), None, **kw), core.numpy(), 1e-13, "identity projection")
+            perm = rng.permutation(c)
+            _close(orc.forward_proj(x, off, m, np.eye(c)[perm], None, **kw), core.numpy()[..., perm], 1e-13,
+                   "permutation projection")
+
+
 ALL_PINS = [
     pin_box_average, pin_integer_offsets_exact_gather, pin_partition_of_unity,
     pin_out_of_range_is_zero, pin_backward_far_away_is_zero, pin_backward_nan_offset_is_local,
     pin_hand_golden, pin_linearity, pin_group_independence,
     pin_forward_pixels, pin_out_size, pin_grid_sample_forward, pin_grid_sample_backward,
     pin_depthwise_conv, pin_depthwise_conv_remove_center, pin_brute_force_tiny, pin_adjoint, pin_finite_differences, pin_softmax_grad_sums_to_zero,
+    pin_linear_is_matmul, pin_generation_zero_weights_is_box_average, pin_generation_is_linear_then_core,
+    pin_generation_brute_force_tiny, pin_output_projection,
 ]

@@ -45,6 +45,16 @@ MUTANTS = [
      "if (!(fabs(py) < 1e15 || fabs(px) < 1e15))"),
     ("nan_grad_mask_not_poisoned", "gm[k] = go[0] = go[1] = NAN;", "go[0] = go[1] = NAN;"),
     ("nan_grad_offset_zero", "gm[k] = go[0] = go[1] = NAN;", "gm[k] = NAN; go[0] = go[1] = 0.0;"),
+    # the linear layer and the steps before and after the core
+    ("linear_weight_transposed", "in[q * nin + c] * w[o * nin + c]", "in[q * nin + c] * w[c * nout + o]"),
+    ("linear_bias_dropped", "double acc = b ? b[o] : 0.0;", "double acc = 0.0;"),
+    ("linear_last_input_dropped", "for (int64_t c = 0; c < nin; ++c)\n                acc +=",
+     "for (int64_t c = 0; c + 1 < nin; ++c)\n                acc +="),
+    ("generation_branches_swapped", "ref_linear(npix, cgd, p->groups * K, guide, w_mask, b_mask, mask);",
+     "ref_linear(npix, cgd, p->groups * K, guide, w_off, b_off, mask);"),
+    ("generation_offset_bias_dropped", "guide, w_off, b_off, off);", "guide, w_off, NULL, off);"),
+    ("projection_skipped", "ref_linear(npix, p->c, p->c, y, w_out, b_out, out);",
+     "memcpy(out, y, sizeof(double) * (size_t)(npix * p->c));"),
     ("nan_location_taken_as_far", "if (isnan(py) || isnan(px))\n        return -1;",
      "if (isnan(py) || isnan(px))\n        return 0;"),
 ]
