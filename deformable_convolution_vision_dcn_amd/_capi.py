@@ -13,7 +13,7 @@ import pathlib
 LIB_PATH = pathlib.Path(os.environ.get(
     "DCN_MI355X_LIB", pathlib.Path(__file__).resolve().parent / "libdcn_mi355x.so"))
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 # bytes of the library's fixed scratch behind dcn_backward_noalloc
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -94,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.dcn_forward.argtypes = [P, vp, vp, vp, vp, vp]
         L.dcn_backward.restype = ctypes.c_int
         L.dcn_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+        L.dcn_forward_generated.restype = ctypes.c_int
+        L.dcn_forward_generated.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.dcn_forward_projected.restype = ctypes.c_int
+        L.dcn_forward_projected.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.dcn_backward_noalloc.restype = ctypes.c_int
         L.dcn_backward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.dcn_backward_workspace_size.restype = ctypes.c_int
@@ -124,6 +128,18 @@ def dcn_check(p: dcn_problem):
 
 def dcn_forward(p: dcn_problem, input_ptr, offset_ptr, mask_ptr, output_ptr, stream) -> int:
     return lib().dcn_forward(ctypes.byref(p), input_ptr, offset_ptr, mask_ptr, output_ptr, stream)
+
+
+def dcn_forward_generated(p: dcn_problem, guide_channels, input_ptr, guide_ptr, w_offset_ptr, b_offset_ptr,
+                          w_mask_ptr, b_mask_ptr, output_ptr, stream) -> int:
+    return lib().dcn_forward_generated(ctypes.byref(p), guide_channels, input_ptr, guide_ptr, w_offset_ptr,
+                                       b_offset_ptr, w_mask_ptr, b_mask_ptr, output_ptr, stream)
+
+
+def dcn_forward_projected(p: dcn_problem, input_ptr, offset_ptr, mask_ptr, w_out_ptr, b_out_ptr, output_ptr,
+                          stream) -> int:
+    return lib().dcn_forward_projected(ctypes.byref(p), input_ptr, offset_ptr, mask_ptr, w_out_ptr, b_out_ptr,
+                                       output_ptr, stream)
 
 
 def dcn_backward_workspace_size(p: dcn_problem):

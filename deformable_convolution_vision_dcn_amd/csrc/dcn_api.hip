@@ -70,6 +70,8 @@ int validate(const dcn_problem *p, int64_t *ho_out, int64_t *wo_out) {
 }
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+// NULL or aligned to one element of `eb` bytes
+bool aligned_elem(const void *ptr, int eb) { return (reinterpret_cast<uintptr_t>(ptr) & (uintptr_t)(eb - 1)) == 0; }
 
 int hip_fail(hipError_t e) {
   snprintf(g_hip_message, sizeof(g_hip_message), "HIP error %d: %s", (int)e, hipGetErrorString(e));
@@ -268,6 +270,99 @@ int dcn_forward(const dcn_problem *p, const void *input, const void *offset, con
     f.out_bytes = (uint32_t)(nc * img_pg * dcn::kGroupChannels * eb);
     f.pg_total = (uint32_t)(nc * img_pg);
     const hipError_t e = dcn::launch_forward(p->dtype, p->softmax, f, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return DCN_OK;
+}
+
+int dcn_forward_generated(const dcn_problem *p, int32_t guide_channels, const void *input, const void *guide,
+                          const void *w_offset, const void *b_offset, const void *w_mask, const void *b_mask,
+                          void *output, void *hip_stream) {
+  int64_t ho = 0, wo = 0;
+  const int st = validate(p, &ho, &wo);
+  if (st != DCN_OK) return st;
+  if (guide_channels <= 0 || guide_channels % 8 != 0) return DCN_ERR_SHAPE;
+  const int eb = elem_bytes(p->dtype);
+  const int64_t K = npoints(p);
+  const int64_t img_guide = ho * wo * guide_channels * eb;
+  const int64_t w_off_bytes = p->groups * K * 2 * guide_channels * eb;
+  if (img_guide > kMaxBytes31 || w_off_bytes > kMaxBytes31) return DCN_ERR_TOO_LARGE;
+  if (!dcn::fused_fits(p->groups, (int)K, p->c, false)) return DCN_ERR_UNSUPPORTED;
+  if (p->n == 0) return DCN_OK;
+  if (!input || !guide || !w_offset || !w_mask || !output) return DCN_ERR_NULL;
+  if (!aligned16(input) || !aligned16(guide) || !aligned16(w_offset) || !aligned16(w_mask) || !aligned16(output) ||
+      !aligned_elem(b_offset, eb) || !aligned_elem(b_mask, eb))
+    return DCN_ERR_ALIGN;
+
+  dcn::FusedParams fp{};
+  fp.f = geometry(p, ho, wo);
+  fp.cgd = guide_channels;
+  fp.w_off = w_offset;
+  fp.b_off = b_offset;
+  fp.w_mask = w_mask;
+  fp.b_mask = b_mask;
+  fp.w_off_bytes = (uint32_t)w_off_bytes;
+  fp.w_mask_bytes = (uint32_t)(w_off_bytes / 2);
+  const int64_t img_in = (int64_t)p->h * p->w * p->c * eb;
+  const int64_t img_pix = ho * wo;
+  int64_t per = images_per_chunk(p, ho, wo);
+  if (kMaxBytes31 / img_guide < per) per = kMaxBytes31 / img_guide;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  for (int64_t n0 = 0; n0 < p->n; n0 += per) {
+    const int64_t nc = (p->n - n0 < per) ? p->n - n0 : per;
+    fp.f.input = static_cast<const char *>(input) + n0 * img_in;
+    fp.f.output = static_cast<char *>(output) + n0 * img_pix * p->c * eb;
+    fp.f.in_bytes = (uint32_t)(nc * img_in);
+    fp.f.out_bytes = (uint32_t)(nc * img_pix * p->c * eb);
+    fp.f.pg_total = (uint32_t)(nc * img_pix * p->groups);
+    fp.guide = static_cast<const char *>(guide) + n0 * img_guide;
+    fp.guide_bytes = (uint32_t)(nc * img_guide);
+    fp.npix = (uint32_t)(nc * img_pix);
+    const hipError_t e = dcn::launch_forward_generated(p->dtype, p->softmax, fp, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return DCN_OK;
+}
+
+int dcn_forward_projected(const dcn_problem *p, const void *input, const void *offset, const void *mask,
+                          const void *w_out, const void *b_out, void *output, void *hip_stream) {
+  int64_t ho = 0, wo = 0;
+  const int st = validate(p, &ho, &wo);
+  if (st != DCN_OK) return st;
+  const int eb = elem_bytes(p->dtype);
+  const int64_t K = npoints(p);
+  const int64_t w_out_bytes = (int64_t)p->c * p->c * eb;
+  if (w_out_bytes > kMaxBytes31) return DCN_ERR_TOO_LARGE;
+  if (!dcn::fused_fits(p->groups, (int)K, p->c, true)) return DCN_ERR_UNSUPPORTED;
+  if (p->n == 0) return DCN_OK;
+  if (!input || !offset || !mask || !w_out || !output) return DCN_ERR_NULL;
+  if (!aligned16(input) || !aligned16(offset) || !aligned16(mask) || !aligned16(w_out) || !aligned16(output) ||
+      !aligned_elem(b_out, eb))
+    return DCN_ERR_ALIGN;
+
+  dcn::FusedParams fp{};
+  fp.f = geometry(p, ho, wo);
+  fp.w_out = w_out;
+  fp.b_out = b_out;
+  fp.w_out_bytes = (uint32_t)w_out_bytes;
+  const int64_t img_in = (int64_t)p->h * p->w * p->c * eb;
+  const int64_t img_pix = ho * wo;
+  const int64_t img_pg = img_pix * p->groups;
+  const int64_t per = images_per_chunk(p, ho, wo);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  for (int64_t n0 = 0; n0 < p->n; n0 += per) {
+    const int64_t nc = (p->n - n0 < per) ? p->n - n0 : per;
+    fp.f.input = static_cast<const char *>(input) + n0 * img_in;
+    fp.f.offset = static_cast<const char *>(offset) + n0 * img_pg * K * 2 * eb;
+    fp.f.mask = static_cast<const char *>(mask) + n0 * img_pg * K * eb;
+    fp.f.output = static_cast<char *>(output) + n0 * img_pix * p->c * eb;
+    fp.f.in_bytes = (uint32_t)(nc * img_in);
+    fp.f.off_bytes = (uint32_t)(nc * img_pg * K * 2 * eb);
+    fp.f.mask_bytes = (uint32_t)(nc * img_pg * K * eb);
+    fp.f.out_bytes = (uint32_t)(nc * img_pix * p->c * eb);
+    fp.f.pg_total = (uint32_t)(nc * img_pg);
+    fp.npix = (uint32_t)(nc * img_pix);
+    const hipError_t e = dcn::launch_forward_projected(p->dtype, p->softmax, fp, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   return DCN_OK;

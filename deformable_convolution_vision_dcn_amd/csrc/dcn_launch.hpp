@@ -41,6 +41,25 @@ struct BwdParams {
   void *grad_mask;         // (chunk, Ho, Wo, G, K)
 };
 
+// The forward fused with the linear steps around the core: offsets and mask
+// generated from a guide feature, or an output projection after it.
+struct FusedParams {
+  FwdParams f;             // geometry, input, output; offset and mask when not generated
+  uint32_t npix;           // output pixels of the chunk (N * Ho * Wo)
+  int32_t gc;              // groups per chunk (set by the launcher)
+  const void *guide;       // (chunk, Ho, Wo, cgd)
+  uint32_t guide_bytes;
+  int32_t cgd;             // guide channels, a multiple of 8
+  const void *w_off;       // (G*K*2, cgd)
+  const void *b_off;       // (G*K*2) or NULL
+  const void *w_mask;      // (G*K, cgd)
+  const void *b_mask;      // (G*K) or NULL
+  uint32_t w_off_bytes, w_mask_bytes;
+  const void *w_out;       // (C, C)
+  const void *b_out;       // (C) or NULL
+  uint32_t w_out_bytes;
+};
+
 // Geometry of the LDS-tiled forward: one block per (image, output tile,
 // group); the input window of the tile (plus a halo of R pixels on every
 // side for the learned offsets) is staged into LDS.
@@ -59,6 +78,10 @@ hipError_t launch_forward_map(int dtype, int softmax, const FwdParams &p, hipStr
 hipError_t launch_backward(int dtype, int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_tiled(int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &p, hipStream_t s);
+hipError_t launch_forward_generated(int dtype, int softmax, const FusedParams &p, hipStream_t s);
+hipError_t launch_forward_projected(int dtype, int softmax, const FusedParams &p, hipStream_t s);
+// Whether the fused kernel's LDS holds this problem (G groups of K points, C channels).
+bool fused_fits(int G, int K, int C, bool proj);
 hipError_t launch_zero(void *dst, uint64_t bytes, hipStream_t s);
 // dst (16-bit dtype, count elements) = src (fp32) rounded; count % 8 == 0.
 hipError_t launch_narrow(int dtype, const void *src, void *dst, uint64_t count, hipStream_t s);

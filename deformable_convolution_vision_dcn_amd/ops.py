@@ -119,6 +119,73 @@ def dcn_forward(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor, *, gr
     return out
 
 
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def dcn_forward_generated(x: torch.Tensor, guide: torch.Tensor, w_offset: torch.Tensor,
+                          b_offset: Optional[torch.Tensor], w_mask: torch.Tensor, b_mask: Optional[torch.Tensor],
+                          *, groups: int, kernel=3, stride=1, pad=1, dilation=1, offset_scale: float = 2.0,
+                          softmax: bool = True, remove_center: bool = False,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Forward with the offsets and mask generated in the kernel from
+    ``guide`` (N, Ho, Wo, Cgd) by the linear branches w_offset (G*K*2, Cgd),
+    b_offset and w_mask (G*K, Cgd), b_mask (biases may be None)."""
+    p, shp = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax, remove_center)
+    n, ho, wo, G, K, _ = shp["offset"]
+    if guide.dim() != 4:
+        raise ValueError("guide must be a 4-D (N, Ho, Wo, Cgd) tensor")
+    cgd = guide.shape[3]
+    _expect(x, "input", x.shape, x.dtype, x.device)
+    _expect(guide, "guide", (n, ho, wo, cgd), x.dtype, x.device)
+    _expect(w_offset, "w_offset", (G * K * 2, cgd), x.dtype, x.device)
+    _expect(w_mask, "w_mask", (G * K, cgd), x.dtype, x.device)
+    if b_offset is not None:
+        _expect(b_offset, "b_offset", (G * K * 2,), x.dtype, x.device)
+    if b_mask is not None:
+        _expect(b_mask, "b_mask", (G * K,), x.dtype, x.device)
+    if out is None:
+        out = torch.empty(shp["out"], dtype=x.dtype, device=x.device)
+    _expect(out, "out", shp["out"], x.dtype, x.device)
+    ins = [("input", x), ("guide", guide), ("w_offset", w_offset), ("w_mask", w_mask)]
+    ins += [(k, t) for k, t in (("b_offset", b_offset), ("b_mask", b_mask)) if t is not None]
+    _no_alias([("out", out)], ins)
+    with torch.cuda.device(x.device):
+        st = _capi.dcn_forward_generated(p, cgd, x.data_ptr(), guide.data_ptr(), w_offset.data_ptr(),
+                                         _ptr(b_offset), w_mask.data_ptr(), _ptr(b_mask), out.data_ptr(),
+                                         _stream(x.device))
+    _capi.raise_on(st)
+    return out
+
+
+def dcn_forward_projected(x: torch.Tensor, offset: torch.Tensor, mask: torch.Tensor, w_out: torch.Tensor,
+                          b_out: Optional[torch.Tensor], *, groups: int, kernel=3, stride=1, pad=1, dilation=1,
+                          offset_scale: float = 2.0, softmax: bool = True, remove_center: bool = False,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Forward followed in the kernel by the output projection w_out (C, C),
+    b_out (C) or None."""
+    p, shp = _shapes(x, groups, kernel, stride, pad, dilation, offset_scale, softmax, remove_center)
+    c = x.shape[3]
+    _expect(x, "input", x.shape, x.dtype, x.device)
+    _expect(offset, "offset", shp["offset"], x.dtype, x.device)
+    _expect(mask, "mask", shp["mask"], x.dtype, x.device)
+    _expect(w_out, "w_out", (c, c), x.dtype, x.device)
+    if b_out is not None:
+        _expect(b_out, "b_out", (c,), x.dtype, x.device)
+    if out is None:
+        out = torch.empty(shp["out"], dtype=x.dtype, device=x.device)
+    _expect(out, "out", shp["out"], x.dtype, x.device)
+    ins = [("input", x), ("offset", offset), ("mask", mask), ("w_out", w_out)]
+    if b_out is not None:
+        ins.append(("b_out", b_out))
+    _no_alias([("out", out)], ins)
+    with torch.cuda.device(x.device):
+        st = _capi.dcn_forward_projected(p, x.data_ptr(), offset.data_ptr(), mask.data_ptr(), w_out.data_ptr(),
+                                         _ptr(b_out), out.data_ptr(), _stream(x.device))
+    _capi.raise_on(st)
+    return out
+
+
 def _backward_args(x, offset, mask, grad_out, groups, kernel, stride, pad, dilation, offset_scale, softmax,
                    remove_center, grad_input, grad_offset, grad_mask):
     """Checked problem and gradient tensors of a backward call (allocated

@@ -181,3 +181,44 @@ def make_inputs(wl: Workload, with_grad: Optional[bool] = None) -> Dict[str, tor
         with_grad = wl.backward
     names = ["x", "offset", "mask"] + (["grad_out"] if with_grad else [])
     return {k: draw_tensor(wl, k) for k in names}
+
+
+# --------------------------------------------------------------------------- the fused forwards
+_EXTRA_IDS = {"guide": 4, "w_offset": 5, "b_offset": 6, "w_mask": 7, "b_mask": 8, "w_out": 9, "b_out": 10}
+
+
+def _std(d: Dist) -> float:
+    return d.scale if d.kind == "normal" else d.scale / 3 ** 0.5
+
+
+def _extra(wl: Workload, name: str, shape, std: float) -> torch.Tensor:
+    rng = np.random.default_rng([wl.seed, wl.draw, _EXTRA_IDS[name]])
+    a = normal(std).draw(rng, shape)
+    t = torch.from_numpy(a)
+    return t if wl.dtype == "f32" else t.to(DTYPES[wl.dtype])
+
+
+def make_generation_inputs(wl: Workload, guide_channels: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """The guide feature (N, Ho, Wo, Cgd) ~ N(0, 1) and the two linear
+    branches that turn it into offsets and mask values (CPU tensors, I/O
+    dtype).  The weights are N(0, sd / sqrt(Cgd)) and the biases
+    N(0, sd / 10), sd the spread of the workload's own offset and mask draws,
+    so the generated values have about that spread."""
+    cgd = guide_channels or wl.c
+    ho, wo = wl.out_hw
+    K = wl.points
+    so, sm = _std(wl.offset_dist), _std(wl.mask_dist)
+    return {
+        "guide": _extra(wl, "guide", (wl.n, ho, wo, cgd), 1.0),
+        "w_offset": _extra(wl, "w_offset", (wl.groups * K * 2, cgd), so / cgd ** 0.5),
+        "b_offset": _extra(wl, "b_offset", (wl.groups * K * 2,), so / 10),
+        "w_mask": _extra(wl, "w_mask", (wl.groups * K, cgd), sm / cgd ** 0.5),
+        "b_mask": _extra(wl, "b_mask", (wl.groups * K,), sm / 10),
+    }
+
+
+def make_projection_inputs(wl: Workload) -> Dict[str, torch.Tensor]:
+    """The output_proj weights (C, C) ~ N(0, 1 / sqrt(C)) and bias
+    ~ N(0, 0.1) (CPU tensors, I/O dtype)."""
+    return {"w_out": _extra(wl, "w_out", (wl.c, wl.c), 1.0 / wl.c ** 0.5),
+            "b_out": _extra(wl, "b_out", (wl.c,), 0.1)}

@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define DCN_ABI_VERSION 5
+#define DCN_ABI_VERSION 6
 
 /* Bytes of the fixed device scratch behind dcn_backward_noalloc (one copy
  * per GPU the library runs on, held until the process ends). */
@@ -143,6 +143,42 @@ int dcn_check(const dcn_problem *p, int64_t *ho, int64_t *wo);
  * chunk of images (one chunk unless an image batch exceeds 2 GiB of input). */
 int dcn_forward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
                 void *output, void *hip_stream);
+
+/* The forward with the step before the core fused in (wmrh.cn/news/61976,
+ * section 二 steps 2 and 3: a linear layer of the guide feature gives every
+ * point's (x, y) offset per group, the other branch of the same linear
+ * structure its score): for every output pixel q and group g,
+ *   offset[q, g, k, e] = sum_c guide[q, c] * w_offset[(g*K + k)*2 + e, c] + b_offset[(g*K + k)*2 + e]
+ *   mask[q, g, k]      = sum_c guide[q, c] * w_mask[g*K + k, c]          + b_mask[g*K + k]
+ * and then output = DCN(input, offset, mask) as dcn_forward computes it
+ * (softmax over the K mask values when p->softmax).  The offsets and mask
+ * values are formed on the matrix cores with fp32 accumulation, kept in
+ * fp32 and never stored.
+ *   guide     (N, Ho, Wo, guide_channels), guide_channels a positive multiple of 8
+ *   w_offset  (groups*K*2, guide_channels), row-major (out, in)
+ *   b_offset  (groups*K*2) or NULL (no bias)
+ *   w_mask    (groups*K, guide_channels), b_mask (groups*K) or NULL
+ * Every tensor is in p->dtype; input, guide, the weights and output 16-byte
+ * aligned.  Errors as dcn_forward, plus DCN_ERR_SHAPE for guide_channels and
+ * DCN_ERR_UNSUPPORTED when one group's generated values do not fit the
+ * kernel's LDS.  Enqueues one launch per chunk of images. */
+int dcn_forward_generated(const dcn_problem *p, int32_t guide_channels, const void *input, const void *guide,
+                          const void *w_offset, const void *b_offset, const void *w_mask, const void *b_mask,
+                          void *output, void *hip_stream);
+
+/* The forward with the step after the core fused in (wmrh.cn/news/61976,
+ * section 二 step 4: the weighted sum passes through the output_proj linear
+ * layer): output[q, o] = sum_c y[q, c] * w_out[o, c] + b_out[o], where y is
+ * what dcn_forward computes, kept in fp32 on chip; the product runs on the
+ * matrix cores with fp32 accumulation (for 16-bit I/O y enters them as two
+ * parts in p->dtype, its rounding and the rounding of the remainder, which
+ * keeps about twice the dtype's significant bits of y).
+ *   w_out (C, C), row-major (out, in); b_out (C) or NULL.
+ * Layouts, errors and chunking otherwise as dcn_forward
+ * (DCN_ERR_UNSUPPORTED when the kernel's LDS cannot hold 16 pixels of C
+ * channels). */
+int dcn_forward_projected(const dcn_problem *p, const void *input, const void *offset, const void *mask,
+                          const void *w_out, const void *b_out, void *output, void *hip_stream);
 
 /* Bytes of device workspace that dcn_backward needs for this problem: 0 for
  * fp32 (and for N == 0); for 16-bit I/O, one fp32 grad_input accumulator of

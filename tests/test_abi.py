@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["dcn_abi_version", "dcn_backward", "dcn_backward_noalloc",
                                     "dcn_backward_workspace_size", "dcn_check", "dcn_forward",
-                                    "dcn_status_string"]
+                                    "dcn_forward_generated", "dcn_forward_projected", "dcn_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -213,6 +213,30 @@ def test_noalloc_backward_checks_before_any_device_call(lib):
     assert 2048 * 2048 * 16 * 4 > _capi.NOALLOC_SCRATCH_BYTES
     assert NB(big, a, a, a, a, a, a, a, None) == _capi.CODES["DCN_ERR_SCRATCH"]
     assert "scratch" in _capi.dcn_status_string(_capi.CODES["DCN_ERR_SCRATCH"])
+
+
+def test_fused_forward_checks_before_any_device_call(lib):
+    """The fused forwards run dcn_forward's checks plus their own on the host
+    (the fake pointers are never dereferenced)."""
+    a = 0x10000
+    p = _capi.make_problem(**BASE)
+    FG, FP = _capi.dcn_forward_generated, _capi.dcn_forward_projected
+    for bad_cgd in (0, -8, 12):
+        assert FG(p, bad_cgd, a, a, a, None, a, None, a, None) == _capi.CODES["DCN_ERR_SHAPE"], bad_cgd
+    assert FG(p, 16, None, a, a, None, a, None, a, None) == _capi.CODES["DCN_ERR_NULL"]
+    assert FG(p, 16, a, a, None, None, a, None, a, None) == _capi.CODES["DCN_ERR_NULL"]
+    assert FG(p, 16, a, a + 4, a, None, a, None, a, None) == _capi.CODES["DCN_ERR_ALIGN"]
+    assert FG(p, 16, a, a, a, a + 2, a, None, a, None) == _capi.CODES["DCN_ERR_ALIGN"]  # fp32 bias
+    assert FG(_capi.make_problem(**{**BASE, "groups": 3}), 16, a, a, a, None, a, None, a, None) == \
+        _capi.CODES["DCN_ERR_SHAPE"]
+    assert FP(p, a, a, a, None, None, a, None) == _capi.CODES["DCN_ERR_NULL"]
+    assert FP(p, a, a, a, a + 8, None, a, None) == _capi.CODES["DCN_ERR_ALIGN"]
+    p0 = _capi.make_problem(**{**BASE, "n": 0})
+    assert FG(p0, 16, None, None, None, None, None, None, None, None) == 0
+    assert FP(p0, None, None, None, None, None, None, None) == 0
+    # 2560 channels: 16 pixels of fp32 core output (160 KB) leave no room in LDS
+    big = _capi.make_problem(**{**BASE, "c": 2560, "groups": 160})
+    assert FP(big, a, a, a, a, None, a, None) == _capi.CODES["DCN_ERR_UNSUPPORTED"]
 
 
 def test_backward_workspace_sizes(lib):
