@@ -10,7 +10,7 @@
 //           before it is stored.
 //
 // Layout of the work: a block of 256 threads (four waves) owns PIX = 16 MT
-// consecutive output pixels and walks the groups in chunks of GC.  A chunk's
+// (16 or 32) consecutive output pixels and walks the groups in chunks of GC.  A chunk's
 // LDS row holds its 2 K GC offset values, padded to a multiple of 16, then
 // its K GC mask values, so that no 16-column tile mixes the two.
 //   1. Generation (GEN): the chunk's offset and mask columns for the PIX
@@ -18,7 +18,9 @@
 //      (v_mfma_f32_16x16x4f32 for fp32, ..._16x16x32_bf16 / _f16 for 16-bit
 //      I/O, fp32 accumulation).  Wave w takes the 16-column tiles w, w+4, ...
 //      and all MT row tiles, so each weight fragment is loaded once per block
-//      and used MT times; the results (plus bias) land in LDS.  Without GEN
+//      and used MT times; the k loop fetches the next step's fragments before
+//      it issues this step's matrix instructions; the results (plus bias) land
+//      in LDS.  Without GEN
 //      the chunk's offset and mask rows are copied into the same LDS layout.
 //   2. Sampling: four lanes per pixel-group (four channels each) read the
 //      pixel-group's offsets and logits from LDS, form the softmax (DCNv3),
@@ -49,6 +51,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Largest block, in 16-pixel row tiles: the generation GEMM is fastest with
+// 32 pixels (64 need 253 VGPRs and one wave per SIMD), the projection with
+// 16 (measured at the InternImage-L stage shapes).
+#ifndef DCN_FUSED_MAX_MT_GEN
+#define DCN_FUSED_MAX_MT_GEN 2
+#endif
+#ifndef DCN_FUSED_MAX_MT_PROJ
+#define DCN_FUSED_MAX_MT_PROJ 1
+#endif
 
 constexpr int kFusedThreads = 256;
 constexpr int kFusedTilesPerWave = 4;  // 16-column tiles per wave in one generation chunk
@@ -133,23 +145,38 @@ __global__ void __launch_bounds__(kFusedThreads) dcn_fused_kernel(FusedParams fp
         live[j] = in_off[j] ? col < n_off : col - m0 < n_msk;
         wrow[j] = in_off[j] ? (uint32_t)(g0 * K * 2 + col) : (uint32_t)(g0 * K + (col - m0));
       }
-      for (int k0 = 0; k0 < cgd; k0 += mma::kStep) {
+      // The k loop is software-pipelined: the fragments of step k0 + kStep
+      // are requested before the matrix instructions of step k0 issue.
+      u32x4 a[MT], b[kFusedTilesPerWave];
+      auto fetch = [&](int k0, u32x4 (&fa)[MT], u32x4 (&fb)[kFusedTilesPerWave]) {
         const int kk = k0 + mma::kPerLane * lq;
         const bool kok = kk < cgd;
-        u32x4 a[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const uint32_t q = pix0 + 16 * m + lr;
-          a[m] = load16(rg, kok && q < fp.npix ? (q * (uint32_t)cgd + kk) * EB : kOutOfRange);
+          fa[m] = load16(rg, kok && q < fp.npix ? (q * (uint32_t)cgd + kk) * EB : kOutOfRange);
         }
 #pragma unroll
         for (int j = 0; j < kFusedTilesPerWave; ++j) {
-          if (wave + 4 * j >= ntiles) break;  // wave-uniform
-          const uint32_t voff = kok && live[j] ? (wrow[j] * (uint32_t)cgd + kk) * EB : kOutOfRange;
-          const u32x4 b = in_off[j] ? load16(rwo, voff) : load16(rwm, voff);
-#pragma unroll
-          for (int m = 0; m < MT; ++m) acc[j][m] = mma::mac(a[m], b, acc[j][m]);
+          const uint32_t voff =
+              kok && live[j] && wave + 4 * j < ntiles ? (wrow[j] * (uint32_t)cgd + kk) * EB : kOutOfRange;
+          fb[j] = in_off[j] ? load16(rwo, voff) : load16(rwm, voff);
         }
+      };
+      fetch(0, a, b);
+      for (int k0 = 0; k0 < cgd; k0 += mma::kStep) {
+        u32x4 an[MT], bn[kFusedTilesPerWave];
+        fetch(k0 + mma::kStep, an, bn);  // past the last step: every offset out of range, nothing read
+#pragma unroll
+        for (int j = 0; j < kFusedTilesPerWave; ++j) {
+          if (wave + 4 * j >= ntiles) break;  // wave-uniform
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[j][m] = mma::mac(a[m], b[j], acc[j][m]);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) a[m] = an[m];
+#pragma unroll
+        for (int j = 0; j < kFusedTilesPerWave; ++j) b[j] = bn[j];
       }
 #pragma unroll
       for (int j = 0; j < kFusedTilesPerWave; ++j) {
@@ -273,10 +300,17 @@ __global__ void __launch_bounds__(kFusedThreads) dcn_fused_kernel(FusedParams fp
       f32x4 acc[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // B fragments one step ahead (software-pipelined), A from LDS
+      auto fetch_b = [&](int k0) {
+        const int kk = k0 + mma::kPerLane * lq;
+        return load16(rw, kk < C ? ((uint32_t)col * (uint32_t)C + kk) * EB : kOutOfRange);
+      };
+      u32x4 bnext = fetch_b(0);
       for (int k0 = 0; k0 < C; k0 += mma::kStep) {
         const int kk = k0 + mma::kPerLane * lq;
         const bool kok = kk < C;  // C is a multiple of 16, the 16-bit step 32
-        const u32x4 b = load16(rw, kok ? ((uint32_t)col * (uint32_t)C + kk) * EB : kOutOfRange);
+        const u32x4 b = bnext;
+        bnext = fetch_b(k0 + mma::kStep);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const float *src = ys + (16 * m + lr) * C + (kok ? kk : 0);
@@ -354,7 +388,7 @@ hipError_t launch_fused_dt(FusedParams fp, hipStream_t s) {
   // the most pixels per block (weights reused the most) whose LDS fits
   for (int mt : {4, 2, 1}) {
     const size_t lds = fused_lds_bytes(mt, fp.gc, K, fp.f.C, PROJ);
-    if (lds > kFusedLdsLimit) continue;
+    if (mt > (PROJ ? DCN_FUSED_MAX_MT_PROJ : DCN_FUSED_MAX_MT_GEN) || lds > kFusedLdsLimit) continue;
     if (mt == 4) return launch_fused_mt<DT, SM, GEN, PROJ, 4>(fp, lds, s);
     if (mt == 2) return launch_fused_mt<DT, SM, GEN, PROJ, 2>(fp, lds, s);
     return launch_fused_mt<DT, SM, GEN, PROJ, 1>(fp, lds, s);
