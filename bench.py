@@ -59,6 +59,49 @@ def forward_bytes(wl) -> int:
     return (in_elems + pg * (cg + 3 * wl.points)) * b
 
 
+# Dense matrix-core peaks of MI355X (TFLOP/s) by operand type.
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0, "bf16": 2500.0}
+
+
+def generated_cost(wl, cgd: int):
+    """(algorithmic bytes, GEMM flops) of one dcn_forward_generated call:
+    input once, the guide, the output, the two branches' weights and biases;
+    2 flops per multiply-add of the offset and mask GEMM."""
+    ho, wo = wl.out_hw
+    npix = wl.n * ho * wo
+    b = 4 if wl.dtype == "f32" else 2
+    cols = wl.groups * wl.points * 3
+    nbytes = (wl.n * wl.h * wl.w * wl.c + npix * cgd + npix * wl.c + cols * (cgd + 1)) * b
+    return nbytes, 2 * npix * cols * cgd
+
+
+def projected_cost(wl):
+    """(algorithmic bytes, GEMM flops) of one dcn_forward_projected call:
+    the core's bytes plus the C x C weight and the bias; 2 flops per
+    multiply-add of the projection."""
+    ho, wo = wl.out_hw
+    npix = wl.n * ho * wo
+    b = 4 if wl.dtype == "f32" else 2
+    return forward_bytes(wl) + (wl.c * wl.c + wl.c) * b, 2 * npix * wl.c * wl.c
+
+
+def roofline_of(nbytes: int, flops: int, dtype: str, ms: float) -> dict:
+    """The bound (HBM or matrix cores, whichever needs longer at its peak)
+    and the achieved rate against it, with both fractions."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[dtype] * 1e12)
+    hbm = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    both = {"hbm_frac": round(hbm / HBM_PEAK_GBS, 4), "mfma_frac": round(tf / MFMA_PEAK_TFLOPS[dtype], 4),
+            "hbm_GB_per_s": round(hbm, 1), "mfma_TFLOP_per_s": round(tf, 2),
+            "alg_bytes_per_launch": nbytes, "gemm_flops_per_launch": flops}
+    if t_mfma > t_hbm:
+        return {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
+                "frac": round(tf / MFMA_PEAK_TFLOPS[dtype], 4), **both}
+    return {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(hbm / HBM_PEAK_GBS, 4), **both}
+
+
 def backward_bytes(wl) -> int:
     """Algorithmic bytes of one backward call: input, offsets, mask, grad_out
     read; grad_input, grad_offset, grad_mask written, all in the I/O dtype
@@ -205,7 +248,7 @@ def host_cpu() -> dict:
             "cores_usable": max(1, min(avail, GPU_HOST_SHARE))}
 
 
-def cpu_baseline(wl, t, images: int):
+def cpu_baseline(wl, t, images: int, mode: str = "core", extra=None, guide=None):
     """The fp64 C oracle as it stands, on the first `images` images of the
     same inputs: on all host cores (one image per call, calls spread over a
     thread pool; ctypes releases the GIL, and the oracle keeps no state), and
@@ -223,7 +266,15 @@ def cpu_baseline(wl, t, images: int):
     host = host_cpu()
     cores = max(1, min(host["cores_usable"], images))
 
+    ex = {k: v.double().numpy() for k, v in (extra or {}).items()}
+    gd = guide.cpu()[:images].double().numpy() if guide is not None else None
+
     def one(i):
+        if mode == "generated":
+            return oracle.forward_om(x[i:i + 1], gd[i:i + 1], ex["w_offset"], ex["b_offset"], ex["w_mask"],
+                                     ex["b_mask"], **kw)
+        if mode == "projected":
+            return oracle.forward_proj(x[i:i + 1], off[i:i + 1], m[i:i + 1], ex["w_out"], ex["b_out"], **kw)
         return oracle.forward(x[i:i + 1], off[i:i + 1], m[i:i + 1], **kw)
 
     t0 = time.perf_counter()
@@ -231,7 +282,8 @@ def cpu_baseline(wl, t, images: int):
         list(pool.map(one, range(images)))
     dt_all = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.forward(x, off, m, **kw)
+    for i in range(images):
+        one(i)
     dt_one = time.perf_counter() - t0
     return {"value": round(samples / dt_all / 1e9, 6), "unit": "GSamples/s", "cores": cores,
             "kind": "oracle",
@@ -324,6 +376,10 @@ def main() -> int:
     ap.add_argument("--clock-warmup", type=float, default=2.0,
                     help="seconds of untimed steps before the timed region (clocks settle)")
     ap.add_argument("--workload", default=None, help="named workload (default: stage-1 fp32)")
+    ap.add_argument("--mode", choices=["core", "generated", "projected"], default="core",
+                    help="core: dcn_forward; generated: offsets and mask generated in the kernel from a guide "
+                         "feature (dcn_forward_generated); projected: output_proj fused after the core "
+                         "(dcn_forward_projected)")
     ap.add_argument("--sets", type=int, default=None,
                     help="input sets rotated over the steps (default: at least 3 and 1 GiB in all)")
     ap.add_argument("--cpu-images", type=int, default=None,
@@ -334,6 +390,10 @@ def main() -> int:
                     help="skip the torch-profiler trace that names the kernels (for runs under rocprofv3)")
     ap.add_argument("--remove-center", action="store_true",
                     help="the workload without the kernel's centre point (DCNv4's remove_center)")
+    ap.add_argument("--stride", type=int, default=None, help="the workload at this stride (both axes)")
+    ap.add_argument("--kernel-size", type=int, default=None,
+                    help="the workload with this odd kernel size (pad = dilation * (K - 1) / 2)")
+    ap.add_argument("--dilation", type=int, default=None, help="the workload at this dilation (both axes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--warm-iters", type=int, default=30,
@@ -380,22 +440,75 @@ def main() -> int:
     wl = synth.WORKLOADS[args.workload or synth.HEADLINE]
     if args.remove_center:
         wl = wl.replace(name=wl.name + "_remove_center", remove_center=True)
+    if args.stride or args.kernel_size or args.dilation:
+        k = args.kernel_size or wl.kernel[0]
+        d = args.dilation or wl.dilation[0]
+        st = args.stride or wl.stride[0]
+        tag = "".join(f"_{n}{v}" for n, v in (("s", args.stride), ("k", args.kernel_size), ("d", args.dilation)) if v)
+        wl = wl.replace(name=wl.name + tag, stride=(st, st), kernel=(k, k), dilation=(d, d),
+                        pad=(d * (k - 1) // 2, d * (k - 1) // 2))
     dev = torch.device("cuda:0")
     print(f"bench: generating {wl.name}", file=sys.stderr, flush=True)
+    mode = args.mode
+    if mode != "core":
+        args.no_backward = True
     t = synth.make_inputs(wl, with_grad=True)
     base = {k: t[k].to(dev) for k in ("x", "offset", "mask", "grad_out")}
+    extra_cpu = {}
+    if mode == "generated":
+        extra_cpu = synth.make_generation_inputs(wl)
+    elif mode == "projected":
+        extra_cpu = synth.make_projection_inputs(wl)
+    extra = {k: v.to(dev) for k, v in extra_cpu.items()}
+    if mode == "generated":
+        base = {"x": base["x"], "guide": extra.pop("guide")}
     set_bytes = sum(v.numel() * v.element_size() for k, v in base.items() if k != "grad_out")
     nsets = args.sets or max(3, -(-(1 << 30) // set_bytes))
     sets = rotated_sets(base, nsets)
     kw = wl.op_kwargs()
     y = torch.empty((wl.n, *wl.out_hw, wl.c), dtype=base["x"].dtype, device=dev)
     stream = torch.cuda.current_stream(dev)
+    ho_, wo_ = wl.out_hw
+    K_ = wl.points
 
-    def fwd(i):
-        s_ = sets[i % nsets]
-        dcn.dcn_forward(s_["x"], s_["offset"], s_["mask"], out=y, **kw)
+    if mode == "core":
+        def fwd(i):
+            s_ = sets[i % nsets]
+            dcn.dcn_forward(s_["x"], s_["offset"], s_["mask"], out=y, **kw)
 
-    fwd_bytes = forward_bytes(wl)
+        unfused = None
+        fwd_bytes, fwd_flops = forward_bytes(wl), 0
+    elif mode == "generated":
+        def fwd(i):
+            s_ = sets[i % nsets]
+            dcn.dcn_forward_generated(s_["x"], s_["guide"], extra["w_offset"], extra["b_offset"], extra["w_mask"],
+                                      extra["b_mask"], out=y, **kw)
+
+        uoff = torch.empty((wl.n, ho_, wo_, wl.groups, K_, 2), dtype=y.dtype, device=dev)
+        umsk = torch.empty((wl.n, ho_, wo_, wl.groups, K_), dtype=y.dtype, device=dev)
+
+        def unfused(i):  # the same step unfused: torch's linear layers, then dcn_forward
+            s_ = sets[i % nsets]
+            g2 = s_["guide"].view(-1, s_["guide"].shape[3])
+            torch.addmm(extra["b_offset"], g2, extra["w_offset"].t(), out=uoff.view(g2.shape[0], -1))
+            torch.addmm(extra["b_mask"], g2, extra["w_mask"].t(), out=umsk.view(g2.shape[0], -1))
+            dcn.dcn_forward(s_["x"], uoff, umsk, out=y, **kw)
+
+        fwd_bytes, fwd_flops = generated_cost(wl, base["guide"].shape[3])
+    else:
+        yc = torch.empty_like(y)
+
+        def fwd(i):
+            s_ = sets[i % nsets]
+            dcn.dcn_forward_projected(s_["x"], s_["offset"], s_["mask"], extra["w_out"], extra["b_out"], out=y,
+                                      **kw)
+
+        def unfused(i):  # dcn_forward, then torch's linear layer
+            s_ = sets[i % nsets]
+            dcn.dcn_forward(s_["x"], s_["offset"], s_["mask"], out=yc, **kw)
+            torch.addmm(extra["b_out"], yc.view(-1, wl.c), extra["w_out"].t(), out=y.view(-1, wl.c))
+
+        fwd_bytes, fwd_flops = projected_cost(wl)
     kernels = None
     if not args.no_trace:
         try:
@@ -411,7 +524,7 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     cold = dist(times)
     value = wl.samples / (ms_per_step * 1e-3) / 1e9
-    achieved = fwd_bytes / (cold["median_ms"] * 1e-3) / 1e9
+    roof = roofline_of(fwd_bytes, fwd_flops, wl.dtype, cold["median_ms"])
 
     # Beside the graded figure: the same launches on one input set back to
     # back (warm: part of the working set can stay in the 256 MB last-level
@@ -430,8 +543,14 @@ def main() -> int:
     del scratch, sink
     ftimes.sort()
     rtimes.sort()
-    fwd_kernel = next((k for k in (kernels or []) if k.startswith("dcn_fwd")), None)
-    traffic = traffic_from_profile(fwd_kernel, wl.name) if fwd_kernel else None
+    fwd_kernel = next((k for k in (kernels or []) if k.startswith("dcn_fwd") or k.startswith("dcn_fused")), None)
+    wl_label = wl.name if mode == "core" else f"{wl.name}_{mode}"
+    traffic = traffic_from_profile(fwd_kernel, wl_label) if fwd_kernel else None
+    unfused_stats = None
+    if unfused is not None:
+        clock_warmup(unfused, 0.5, 5)
+        _, utimes = timed_launches(unfused, stream, max(20, min(args.steps, 100)))
+        unfused_stats = dist(utimes)
 
     result = {
         "metric": METRIC,
@@ -446,25 +565,25 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded, InternImage-L stage-shaped; no dataset or trained weights)",
-        "config": {"workload": wl.name, "n": wl.n, "h": wl.h, "w": wl.w, "c": wl.c,
+        "config": {"workload": wl_label, "n": wl.n, "h": wl.h, "w": wl.w, "c": wl.c,
                    "groups": wl.groups, "kernel": list(wl.kernel), "stride": list(wl.stride),
                    "pad": list(wl.pad), "dilation": list(wl.dilation),
                    "offset_scale": wl.offset_scale, "softmax": wl.softmax,
                    "remove_center": wl.remove_center, "samples_per_step": wl.samples},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": fwd_kernel,
-                     "alg_bytes_per_launch": fwd_bytes,
+        "roofline": {**roof, "traffic": traffic, "kernel": fwd_kernel,
                      "launch_ms": cold["median_ms"],
-                     "note": "achieved = algorithmic bytes / median per-launch HIP-event time of the "
-                             "timed steps (cold: rotated input sets)"},
+                     "note": "achieved = algorithmic bytes (or GEMM flops, when the matrix cores bound the "
+                             "step) / median per-launch HIP-event time of the timed steps (cold: rotated "
+                             "input sets)"},
         "forward_launch": {
             "cold_rotated": cold, "warm_same_set": dist(wtimes), "cold_after_write_flush": dist(ftimes),
             "cold_after_read_flush": dist(rtimes),
             "input_sets": nsets, "input_set_bytes": set_bytes,
             "clock_warmup": {"seconds": args.clock_warmup, "calls": warm_calls},
             "kernels_traced": kernels,
+            "unfused_same_step": unfused_stats,
             "note": "cold_rotated: the timed steps, each on another copy of the batch; "
+                    "unfused_same_step: the same step as torch linear layers plus dcn_forward; "
                     "warm_same_set: one set back to back; cold_after_write_flush / cold_after_read_flush: "
                     "512 MB written / read before each launch"},
     }
@@ -510,7 +629,9 @@ def main() -> int:
     if not args.no_cpu_baseline:
         images = min(wl.n, args.cpu_images or wl.n)
         print(f"bench: CPU oracle on {images} images", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, t, images)
+        result["cpu_baseline"] = cpu_baseline(wl, t, images, mode,
+                                              {k: v for k, v in extra_cpu.items() if k != "guide"},
+                                              extra_cpu.get("guide"))
 
     result["device"] = torch.cuda.get_device_name(dev)
     print(json.dumps(result), flush=True)
