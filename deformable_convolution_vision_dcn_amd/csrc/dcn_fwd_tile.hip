@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   constexpr int WPIX = THREADS / LPP;              // window pixels per slice
   constexpr int MAXPQ = (tile_max_span<GP>() + WPIX - 1) / WPIX;  // slices per lane
   constexpr int K = RC ? 8 : 9;
-  static_assert(PASSES == 2, "the pass sequence below assumes two passes");
+  static_assert(PASSES == 1 || PASSES == 2, "one or two passes per item");
   static_assert(PIXB % LANE_BYTES == 0 && PIXB % 8 == 0 && PIXB >= GP * 4 * LANE_BYTES, "pixel stride");
   static_assert(GP == 1 || GP == 2, "one or two groups per item");
 
@@ -136,9 +136,11 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   const uint32_t slot = threadIdx.x / LPP;
   const uint32_t m_col = slot % CW;
   const bool m_live = slot < (uint32_t)(RPS * CW);
-  // remainder pixel rs = rho * WPIX + slot of remainder slice rho
-  uint32_t r_y[NR], r_x[NR];
-  bool r_live[NR];
+  // remainder pixel rs = rho * WPIX + slot of remainder slice rho (the
+  // arrays keep one element where the run-time geometry has no remainder)
+  constexpr int NRA = NR > 0 ? NR : 1;
+  uint32_t r_y[NRA], r_x[NRA];
+  bool r_live[NRA];
 #pragma unroll
   for (int rho = 0; rho < NR; ++rho) {
     const uint32_t rs = (uint32_t)rho * WPIX + slot;
@@ -154,7 +156,7 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
     r_live[rho] = rs < (uint32_t)(REM_A + REM_B);
   }
   const uint32_t m_lane = (slot / CW) * row_bytes + m_col * pix_bytes + wlane * LANE_BYTES;
-  uint32_t r_lane[NR];
+  uint32_t r_lane[NRA];
 #pragma unroll
   for (int rho = 0; rho < NR; ++rho) r_lane[rho] = r_y[rho] * row_bytes + r_x[rho] * pix_bytes + wlane * LANE_BYTES;
   const uint32_t img_bytes = (uint32_t)p.H * row_bytes;
@@ -345,7 +347,7 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   if (item < end) {
     issue_window(cur, true);
     issue_pgdata(cur, P0{});
-    issue_pgdata(cur, P1{});
+    if constexpr (PASSES == 2) issue_pgdata(cur, P1{});
   }
 
   while (item < end) {
@@ -499,9 +501,13 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
     pass(P0{});
     __builtin_amdgcn_s_setprio(1);
     issue_pgdata(nx, P0{});  // unconditional (see issue_window)
-    pass(P1{});
-    __builtin_amdgcn_s_setprio(0);
-    issue_pgdata(nx, P1{});
+    if constexpr (PASSES == 2) {
+      pass(P1{});
+      __builtin_amdgcn_s_setprio(0);
+      issue_pgdata(nx, P1{});
+    } else {
+      __builtin_amdgcn_s_setprio(0);
+    }
 
     item = next;
     cur = nx;
@@ -527,14 +533,19 @@ constexpr int tile_lds_limit() { return GP == 1 ? 80 * 1024 : 160 * 1024; }
 // One group per item at stride or dilation above 1: the halo taken when the
 // default one overflows the window budget (dilation 2: a 31x31 window).
 constexpr int kTileHaloSmall = 5;
+// Two groups per item at other strides and dilations: 8-row output tiles and
+// a halo of 4 (3 where 4 overflows; stride 2 at dilation 1 takes a 26 x 42
+// window, 145 KB).
+constexpr int kPairStridedTH = 8;
+constexpr int kPairHaloStrided = 4;
 
 size_t tile_lds_bytes(const TileGeom &tg, int pixb) {
   return ((size_t)tg.span_h * tg.span_w + tg.span_w + 2) * pixb;  // window + zero block
 }
 
-template <int DT, bool SM, int UDIL, int GP, bool RC, int HALO = tile_halo<GP>()>
+template <int DT, bool SM, int UDIL, int GP, bool RC, int HALO = tile_halo<GP>(), int TH = kTileH>
 hipError_t launch_tile(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_fwd_tile_kernel<DT, SM, kTileH, kTileW, HALO, UDIL, GP, RC>;
+  auto kern = dcn_fwd_tile_kernel<DT, SM, TH, kTileW, HALO, UDIL, GP, RC>;
   const size_t lds = tile_lds_bytes(tg, tile_pixel_stride<DT, GP>());
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
@@ -561,7 +572,15 @@ hipError_t launch_tile_dt(int softmax, int udil, int halo, const FwdParams &p, c
   if (udil == 2)
     return softmax ? launch_tile<DT, true, 2, GP, RC, H2>(p, tg, s) : launch_tile<DT, false, 2, GP, RC, H2>(p, tg, s);
   if constexpr (GP == 2) {
-    return hipErrorNotSupported;  // strided windows: one group per item
+    // other strides and dilations: 8 x 16 output tiles (one pass of 128
+    // pixels x 2 groups), so that the strided window fits
+    if (halo == kPairHaloStrided)
+      return softmax ? launch_tile<DT, true, 0, GP, RC, kPairHaloStrided, kPairStridedTH>(p, tg, s)
+                     : launch_tile<DT, false, 0, GP, RC, kPairHaloStrided, kPairStridedTH>(p, tg, s);
+    if (halo == kPairHaloStrided - 1)
+      return softmax ? launch_tile<DT, true, 0, GP, RC, kPairHaloStrided - 1, kPairStridedTH>(p, tg, s)
+                     : launch_tile<DT, false, 0, GP, RC, kPairHaloStrided - 1, kPairStridedTH>(p, tg, s);
+    return hipErrorNotSupported;
   } else {
     if (halo == kTileHaloSmall)
       return softmax ? launch_tile<DT, true, 0, GP, RC, kTileHaloSmall>(p, tg, s)
@@ -573,10 +592,10 @@ hipError_t launch_tile_dt(int softmax, int udil, int halo, const FwdParams &p, c
 // Window geometry and work items for GP groups per item; false when the
 // problem does not fit this variant.
 template <int GP>
-bool tile_geometry(int dtype, const FwdParams &p, TileGeom &tg, int halo) {
+bool tile_geometry(int dtype, const FwdParams &p, TileGeom &tg, int halo, int th = kTileH) {
   if (p.G % GP != 0) return false;
   tg = TileGeom{};
-  tg.span_h = (kTileH - 1) * p.SH + 2 * p.DH + 2 * halo + 2;
+  tg.span_h = (th - 1) * p.SH + 2 * p.DH + 2 * halo + 2;
   tg.span_w = (kTileW - 1) * p.SW + 2 * p.DW + 2 * halo + 2;
   const int pixb = dtype == DCN_F32 ? tile_pixel_stride<DCN_F32, GP>() : tile_pixel_stride<DCN_F16, GP>();
   if (tile_lds_bytes(tg, pixb) > (size_t)tile_lds_limit<GP>()) return false;
@@ -588,7 +607,7 @@ bool tile_geometry(int dtype, const FwdParams &p, TileGeom &tg, int halo) {
   const bool unit = p.SH == 1 && p.SW == 1 && p.DH == p.DW && (p.DH == 1 || p.DH == 2);
   const int64_t row_bytes = (int64_t)p.W * p.C * (dtype == DCN_F32 ? 4 : 2);
   if (unit && ((int64_t)p.H + p.PH + tg.span_h + 1) * row_bytes >= (int64_t(1) << 31)) return false;
-  const int tiles_y = (p.Ho + kTileH - 1) / kTileH;
+  const int tiles_y = (p.Ho + th - 1) / th;
   tg.tiles_x = (p.Wo + kTileW - 1) / kTileW;
   tg.tiles_per_img = tiles_y * tg.tiles_x;
   const int64_t imgs = p.pg_total / ((int64_t)p.Ho * p.Wo * p.G);
@@ -610,7 +629,13 @@ hipError_t launch_tile_gp(int dtype, int softmax, const FwdParams &p, hipStream_
   // edge.  Other strides and dilations run the general one-group variant.
   const int udil = (p.SH == 1 && p.SW == 1 && p.DH == p.DW && (p.DH == 1 || p.DH == 2)) ? p.DH : 0;
   int halo = tile_halo<GP>() - (udil == 2 ? 1 : 0);
-  if (!tile_geometry<GP>(dtype, p, tg, halo)) {
+  if (GP == 2 && udil == 0) {  // strided or unevenly dilated windows: 8-row tiles
+    halo = kPairHaloStrided;
+    if (!tile_geometry<GP>(dtype, p, tg, halo, kPairStridedTH)) {
+      halo = kPairHaloStrided - 1;
+      if (!tile_geometry<GP>(dtype, p, tg, halo, kPairStridedTH)) return hipErrorNotSupported;
+    }
+  } else if (!tile_geometry<GP>(dtype, p, tg, halo)) {
     if (GP != 1 || udil != 0) return hipErrorNotSupported;
     halo = kTileHaloSmall;
     if (!tile_geometry<GP>(dtype, p, tg, halo)) return hipErrorNotSupported;
