@@ -2,8 +2,9 @@
 // (fp32 arithmetic for fp32 and 16-bit I/O), a lane quad per pixel-group, for
 // 3x3 kernel points at stride 1 and dilation 1 (the InternImage
 // configuration; wmrh.cn/news/61976, section 二 steps 2-4 and section 三) or
-// 2, all nine or the eight left by DCNv4's remove_center
-// (pnsm.cn/news/2029644.html section 3.3).
+// 2, also at stride 2 (the DCNv4 signature carries stride and dilation), all
+// nine or the eight left by DCNv4's remove_center (pnsm.cn/news/2029644.html
+// section 3.3).
 //
 // The derivatives are those of the untiled backward kernel: every in-map
 // corner of a sample receives m_k * w_corner * gy_c; the offset gradient is
@@ -46,15 +47,24 @@ namespace dcn {
 constexpr int kBqHalo = DCN_BQ_HALO;
 constexpr int kBqPixB = 64;                               // 16 fp32 channels
 
-// Block geometry for TW x TH output tiles (a quad per pixel): 16x16 (1024
-// threads), 24x8 (768 threads) for maps 24 pixels wide or 12x12 (576
-// threads) for 12x12 maps, both of which 16x16 tiles would leave 44 % empty.
-template <int TW, int TH>
+// Halo at stride 2 (dilation 1; one less at dilation 2, so the window keeps
+// its size).
+constexpr int kBqHaloS2 = 4;
+
+// Block geometry for TW x TH output tiles (a quad per pixel) at stride ST:
+// 16x16 (1024 threads), 24x8 (768 threads) for maps 24 pixels wide or 12x12
+// (576 threads) for 12x12 maps, both of which 16x16 tiles would leave 44 %
+// empty; at stride 2, 16x8 tiles (512 threads) whose 42 x 26 windows (the
+// footprint plus a halo of 4) fit beside their grad windows.
+template <int TW, int TH, int ST = 1>
 struct BqGeom {
+  static_assert(ST == 1 || ST == 2, "stride 1 or 2");
   static constexpr int kThreads = 4 * TW * TH;
   static constexpr int kWaves = kThreads / 64;
-  static constexpr int kSpanW = TW + 2 * kBqHalo + 3;     // window edges, pixels
-  static constexpr int kSpanH = TH + 2 * kBqHalo + 3;
+  // window edges, pixels: (T - 1) * ST + 2 * DIL + 2 * R + 2 with the halo R
+  // one smaller at dilation 2, so independent of the dilation
+  static constexpr int kSpanW = ST == 1 ? TW + 2 * kBqHalo + 3 : 2 * TW + 2 * kBqHaloS2 + 2;
+  static constexpr int kSpanH = ST == 1 ? TH + 2 * kBqHalo + 3 : 2 * TH + 2 * kBqHaloS2 + 2;
   static constexpr int kRow = kSpanW * kBqPixB;           // LDS bytes per window row
   static constexpr int kWin = kSpanW * kSpanH * kBqPixB;  // one window
   static constexpr int kZero = kRow + 2 * kBqPixB;        // zero block after the input window
@@ -87,9 +97,9 @@ __device__ __forceinline__ int2 pair_sums(uint64_t v) {
 // item takes two rounds instead of three.
 // DIL: the dilation (1 or 2, both axes).  The window keeps its size: the
 // halo shrinks by one pixel per side at dilation 2.
-template <int DT, bool SOFTMAX, bool RC, int DIL, int TW, int TH>
+template <int DT, bool SOFTMAX, bool RC, int DIL, int TW, int TH, int ST>
 __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kernel(BwdParams bp, TileGeom tg) {
-  using G = BqGeom<TW, TH>;
+  using G = BqGeom<TW, TH, ST>;
   const FwdParams &p = bp.f;
   using io = Io<DT>;
   constexpr int EB = io::kBytes;         // bytes per element in memory
@@ -99,7 +109,7 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
   // a caller's fp32 workspace of the input's shape): an input byte address
   // times GX is the same element's address there.
   constexpr uint32_t GX = 4 / EB;
-  constexpr int R = kBqHalo - (DIL - 1), SPAN_W = G::kSpanW, SPAN_H = G::kSpanH;
+  constexpr int R = (ST == 1 ? kBqHalo : kBqHaloS2) - (DIL - 1), SPAN_W = G::kSpanW, SPAN_H = G::kSpanH;
   static_assert(DIL == 1 || DIL == 2, "dilation 1 or 2");
   constexpr int SPAN = SPAN_W * SPAN_H;
   constexpr int PIXB = kBqPixB, ROW = G::kRow, LIM_X = SPAN_W - 2, LIM_Y = SPAN_H - 2;
@@ -139,8 +149,8 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
   for (int r = 0; r < 3; ++r) {
     const int k = r < 2 ? 2 * (int)sub + r : 8;
     const int q = RC ? (r < 2 ? k + (k >= 4) : 4) : k;
-    bxp |= (uint32_t)(ox + R + (q % 3) * DIL) << (10 * r);
-    byp |= (uint32_t)(oy + R + (q / 3) * DIL) << (10 * r);
+    bxp |= (uint32_t)(ox * ST + R + (q % 3) * DIL) << (10 * r);
+    byp |= (uint32_t)(oy * ST + R + (q / 3) * DIL) << (10 * r);
   }
   const uint32_t win_chunk = lbase + sub * 16u;          // this lane's 4 channels of a window pixel
   const uint32_t gwin_chunk = lbase + GWIN + sub * 16u;
@@ -167,8 +177,8 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
     const uint32_t tyi = fast_div(tile_id, tg.div_tiles_x);
     const uint32_t txi = tile_id - tyi * (uint32_t)tg.tiles_x;
     const int r0 = (int)tyi * TH, c0 = (int)txi * TW;
-    I.Y0 = r0 - p.PH - R;  // window origin in input coordinates
-    I.X0 = c0 - p.PW - R;
+    I.Y0 = r0 * ST - p.PH - R;  // window origin in input coordinates
+    I.X0 = c0 * ST - p.PW - R;
     I.img = I.n * (uint32_t)p.H * row_bytes;
     I.chan = I.g * (uint32_t)(CG * EB) + sub * (uint32_t)LB;
     const int ho = r0 + oy, wo = c0 + ox;
@@ -617,10 +627,10 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
 
 namespace {
 
-template <int DT, bool SM, bool RC, int DIL, int TW, int TH>
+template <int DT, bool SM, bool RC, int DIL, int TW, int TH, int ST>
 hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s) {
-  using G = BqGeom<TW, TH>;
-  auto kern = dcn_bwd_quad_kernel<DT, SM, RC, DIL, TW, TH>;
+  using G = BqGeom<TW, TH, ST>;
+  auto kern = dcn_bwd_quad_kernel<DT, SM, RC, DIL, TW, TH, ST>;
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
@@ -638,18 +648,18 @@ hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s
   return hipGetLastError();
 }
 
-template <bool RC, int DIL, int TW, int TH>
+template <bool RC, int DIL, int TW, int TH, int ST = 1>
 hipError_t launch_dt(int dtype, int softmax, const BwdParams &b, const TileGeom &tg, hipStream_t s) {
   switch (dtype) {
     case DCN_F32:
-      return softmax ? launch_bwd_quad<DCN_F32, true, RC, DIL, TW, TH>(b, tg, s)
-                     : launch_bwd_quad<DCN_F32, false, RC, DIL, TW, TH>(b, tg, s);
+      return softmax ? launch_bwd_quad<DCN_F32, true, RC, DIL, TW, TH, ST>(b, tg, s)
+                     : launch_bwd_quad<DCN_F32, false, RC, DIL, TW, TH, ST>(b, tg, s);
     case DCN_F16:
-      return softmax ? launch_bwd_quad<DCN_F16, true, RC, DIL, TW, TH>(b, tg, s)
-                     : launch_bwd_quad<DCN_F16, false, RC, DIL, TW, TH>(b, tg, s);
+      return softmax ? launch_bwd_quad<DCN_F16, true, RC, DIL, TW, TH, ST>(b, tg, s)
+                     : launch_bwd_quad<DCN_F16, false, RC, DIL, TW, TH, ST>(b, tg, s);
     case DCN_BF16:
-      return softmax ? launch_bwd_quad<DCN_BF16, true, RC, DIL, TW, TH>(b, tg, s)
-                     : launch_bwd_quad<DCN_BF16, false, RC, DIL, TW, TH>(b, tg, s);
+      return softmax ? launch_bwd_quad<DCN_BF16, true, RC, DIL, TW, TH, ST>(b, tg, s)
+                     : launch_bwd_quad<DCN_BF16, false, RC, DIL, TW, TH, ST>(b, tg, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -662,21 +672,24 @@ double quad_tile_use(const FwdParams &p, int tw, int th) {
 
 }  // namespace
 
-// 3x3 points (all nine, or eight without the centre), stride 1, dilation 1
-// or 2 (the same on both axes) only; hipErrorNotSupported otherwise.
+// 3x3 points (all nine, or eight without the centre), stride 1 or 2 and
+// dilation 1 or 2 (each the same on both axes) only; hipErrorNotSupported
+// otherwise.
 hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipStream_t s) {
   const FwdParams &p = b.f;
-  if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != p.DW || (p.DH != 1 && p.DH != 2))
+  if (p.KH != 3 || p.KW != 3 || p.SH != p.SW || (p.SH != 1 && p.SH != 2) || p.DH != p.DW ||
+      (p.DH != 1 && p.DH != 2))
     return hipErrorNotSupported;
-  // 24x8 or 12x12 tiles (dilation 1) where they leave clearly fewer quads
-  // idle than 16x16 ones (24x8 on a tie between the two)
+  const bool s2 = p.SH == 2;
+  // 24x8 or 12x12 tiles (stride and dilation 1) where they leave clearly
+  // fewer quads idle than 16x16 ones (24x8 on a tie between the two)
   const double u16 = quad_tile_use(p, 16, 16), u24 = quad_tile_use(p, 24, 8), u12 = quad_tile_use(p, 12, 12);
-  const bool wide = p.DH == 1 && u24 > u16 + 0.1 && u24 >= u12;
-  const bool small = p.DH == 1 && !wide && u12 > u16 + 0.1;
-  const int tw = wide ? 24 : (small ? 12 : 16), th = wide ? 8 : (small ? 12 : 16);
+  const bool wide = !s2 && p.DH == 1 && u24 > u16 + 0.1 && u24 >= u12;
+  const bool small = !s2 && p.DH == 1 && !wide && u12 > u16 + 0.1;
+  const int tw = wide ? 24 : (small ? 12 : 16), th = s2 || wide ? 8 : (small ? 12 : 16);
   TileGeom tg{};
-  tg.span_w = tw + 2 * kBqHalo + 3;
-  tg.span_h = th + 2 * kBqHalo + 3;
+  tg.span_w = s2 ? BqGeom<16, 8, 2>::kSpanW : tw + 2 * kBqHalo + 3;
+  tg.span_h = s2 ? BqGeom<16, 8, 2>::kSpanH : th + 2 * kBqHalo + 3;
   const int tiles_y = (p.Ho + th - 1) / th;
   tg.tiles_x = (p.Wo + tw - 1) / tw;
   tg.tiles_per_img = tiles_y * tg.tiles_x;
@@ -688,6 +701,10 @@ hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipS
   tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
+  if (s2 && p.DH == 2)
+    return p.RC ? launch_dt<true, 2, 16, 8, 2>(dtype, softmax, b, tg, s) : launch_dt<false, 2, 16, 8, 2>(dtype, softmax, b, tg, s);
+  if (s2)
+    return p.RC ? launch_dt<true, 1, 16, 8, 2>(dtype, softmax, b, tg, s) : launch_dt<false, 1, 16, 8, 2>(dtype, softmax, b, tg, s);
   if (p.DH == 2)
     return p.RC ? launch_dt<true, 2, 16, 16>(dtype, softmax, b, tg, s) : launch_dt<false, 2, 16, 16>(dtype, softmax, b, tg, s);
   if (wide)
