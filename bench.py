@@ -193,8 +193,15 @@ def summarize_counters(root: pathlib.Path, workload: str, kernel: str, command: 
     w_bytes = sum(write) / len(write) * kib * w_scale
     from deformable_convolution_vision_dcn_amd import synth
 
-    wl = synth.WORKLOADS[workload]
-    alg = backward_bytes(wl) if "bwd" in kernel else forward_bytes(wl)
+    base, _, mode = workload.partition("_generated") if workload.endswith("_generated") else \
+        workload.partition("_projected")
+    wl = synth.WORKLOADS[base]
+    if workload.endswith("_generated"):
+        alg = generated_cost(wl, wl.c)[0]
+    elif workload.endswith("_projected"):
+        alg = projected_cost(wl)[0]
+    else:
+        alg = backward_bytes(wl) if "bwd" in kernel else forward_bytes(wl)
     lines = [
         f"# HBM traffic and counters of {kernel}, workload {workload}",
         f"command: {command}",
@@ -212,7 +219,7 @@ def summarize_counters(root: pathlib.Path, workload: str, kernel: str, command: 
         f"algorithmic_bytes_per_launch: {alg}",
         f"traffic_over_algorithmic: {(f_bytes + w_bytes) / alg:.3f}",
     ]
-    for run in ("l2", "sq", "busy"):
+    for run in ("l2", "sq", "busy", "mfma"):
         names = set()
         for f in root.glob(f"{run}/**/*counter_collection.csv"):
             for row in csv.DictReader(open(f)):
