@@ -163,8 +163,10 @@ def summarize_counters(root: pathlib.Path, workload: str, kernel: str, command: 
     summary of one kernel: runs "fetch" (FETCH_SIZE) and "write" (WRITE_SIZE)
     of the benchmark, "copy_fetch" and "copy_write" of its --copy-calibration
     mode (each counter scaled by what it reads for a plain device copy of
-    known size), and optional runs "l2" (L2 hits and misses) and "sq"
-    (instruction and busy counters), averaged per dispatch of `kernel`."""
+    known size), and optional runs "l2" (L2 hits and misses), "sq"
+    (instruction counts), "wait" (wave-cycles issuing and waiting), "busy"
+    (address-unit and L1 busy counters) and "mfma" (matrix-core counters),
+    averaged per dispatch of `kernel`."""
     import csv
 
     def per_dispatch(run: str, counter: str, match):
@@ -219,7 +221,7 @@ def summarize_counters(root: pathlib.Path, workload: str, kernel: str, command: 
         f"algorithmic_bytes_per_launch: {alg}",
         f"traffic_over_algorithmic: {(f_bytes + w_bytes) / alg:.3f}",
     ]
-    for run in ("l2", "sq", "busy", "mfma"):
+    for run in ("l2", "sq", "wait", "busy", "mfma"):
         names = set()
         for f in root.glob(f"{run}/**/*counter_collection.csv"):
             for row in csv.DictReader(open(f)):

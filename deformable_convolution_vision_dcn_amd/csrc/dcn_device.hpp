@@ -350,6 +350,38 @@ __device__ __forceinline__ void load_row_words(__amdgpu_buffer_rsrc_t roff, __am
   }
 }
 
+// The K mask values of load_row_words as fp32.
+template <int DT, int K = 9>
+__device__ __forceinline__ void decode_mask_words(uint32_t pg, const RowWords<DT, K> &r, float (&msk)[K]) {
+  if constexpr (DT == DCN_F32) {
+#pragma unroll
+    for (int q = 0; q < K; ++q) msk[q] = __uint_as_float(r.m[q]);
+  } else if constexpr (K == 8) {  // aligned rows: two values per word
+#pragma unroll
+    for (int q = 0; q < 8; ++q) msk[q] = (q & 1) ? Io<DT>::hi(r.m[q / 2]) : Io<DT>::lo(r.m[q / 2]);
+  } else {
+    const uint32_t sh = (pg * 18u) & 2u ? 16u : 0u;  // odd pg: the row starts at a half word
+    uint32_t w[5];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_alignbit(r.m[q + 1], r.m[q], sh);
+    w[4] = r.m[4] >> sh;
+#pragma unroll
+    for (int q = 0; q < 9; ++q) msk[q] = (q & 1) ? Io<DT>::hi(w[q / 2]) : Io<DT>::lo(w[q / 2]);
+  }
+}
+
+// Offset (x, y) of point k of load_row_words as fp32.
+template <int DT, int K = 9>
+__device__ __forceinline__ void offset_words_xy(const RowWords<DT, K> &r, int k, float &x, float &y) {
+  if constexpr (DT == DCN_F32) {
+    x = __uint_as_float(r.o[2 * k]);
+    y = __uint_as_float(r.o[2 * k + 1]);
+  } else {
+    x = Io<DT>::lo(r.o[k]);
+    y = Io<DT>::hi(r.o[k]);
+  }
+}
+
 // The 2K offsets (x, y per point) and K mask values of load_row_words as fp32.
 template <int DT, int K = 9>
 __device__ __forceinline__ void decode_row_words(uint32_t pg, const RowWords<DT, K> &r, float (&off)[2 * K],

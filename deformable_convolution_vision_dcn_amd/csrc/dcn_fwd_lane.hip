@@ -6,24 +6,30 @@
 // The forward is a gather-reduce: per bilinear sample 64 fp32 FMAs (16
 // channels x 4 corners) against a few dozen instructions of location and
 // weight math.  With one lane per pixel-group that math is done exactly once
-// per sample and needs no cross-lane broadcast, so the instruction stream is
-// dominated by the FMAs themselves (vector fp32 issue is the binding limit on
-// this chip once the corners come from LDS).
+// per sample and needs no cross-lane broadcast; for 16-bit I/O each FMA takes
+// its 16-bit operand directly (v_fma_mix), so no unpacking either.
 //
-// Block = 256 threads = one (image, 16x16 output tile, group) work item at a
-// time; blocks are persistent and each XCD walks one contiguous range of items.
-// The input window of an item (its regular 3x3 footprint plus a halo of R
-// pixels for the learned offsets, zero outside the map) is staged in LDS; the
-// next item's window, offsets and logits are requested into registers while
-// the current item computes.  A sample whose corners leave the window is
-// served from global memory behind a wave ballot (the buffer range check
-// supplying the zeros); the main path has no branches.
+// Block = one (image, output tile, block of GP groups) work item at a time,
+// one lane per (pixel, group): 16x16 tiles, 16x8 or 24x8 with four groups
+// (512 or 768 threads); blocks are persistent and each XCD walks one
+// contiguous range of items.  The input window of an item (its regular 3x3
+// footprint plus a halo of R pixels for the learned offsets, zero outside the
+// map) is staged in LDS, the GP group slices of a window pixel side by side
+// as they lie in memory: with four 16-bit groups a window pixel is one whole
+// 128-byte line, which took the stage-2 launch from 1.74x to 1.00x of its
+// algorithmic HBM bytes.  Each lane stages the same window pixels of every
+// item (lane-constant slices of rows and columns), so the per-item address
+// work is one add per slice.  The next item's window, offsets and logits are
+// requested into registers while the current item computes.  A sample whose
+// corners leave the window is served from global memory behind a wave
+// ballot (the buffer range check supplying the zeros); the main path has no
+// branches.
 //
 // LDS banking: a wave64 ds_read_b128 is served 16 lanes at a time from 64
-// banks.  Lane l reads the 16-byte chunks of a corner in the rotated order
-// (t + l) mod 4, so the four lanes that share a chunk position come from four
-// different pixels; the remaining conflicts are the random coincidences of
-// those pixels' bank quarters.
+// banks.  Lanes read the 16-byte chunks of a corner in a rotated order, so
+// that pixels which share a bank row at unit offsets start on different
+// chunks; the remaining conflicts are the random coincidences of the
+// sampled pixels' bank quarters.
 #include <algorithm>
 
 #include "dcn_device.hpp"
@@ -35,15 +41,16 @@ namespace dcn {
 #endif
 
 constexpr int kLaneHalo = DCN_LANE_HALO;      // window halo for the offsets
-// Output tiles: 16x16 (256 lanes), or 24x8 (192 lanes, three waves) for
-// maps 24 pixels wide, which 16x16 tiles would leave 44 % empty.
+// LDS bytes of a TW x TH tile's window (and its zero block) at pixb bytes
+// per staged window pixel.
 template <int TW, int TH>
 constexpr int lane_lds_bytes(int pixb) {
   return ((TW + 2 * kLaneHalo + 3) * (TH + 2 * kLaneHalo + 3) + (TW + 2 * kLaneHalo + 3) + 2) * pixb;
 }
 
+// Bytes of one pixel-group (16 channels) in the I/O dtype.
 template <int DT>
-constexpr int lane_pixel_stride() { return DT == DCN_F32 ? 64 : 32; }
+constexpr int lane_slice_bytes() { return kGroupChannels * Io<DT>::kBytes; }
 
 namespace {
 
@@ -58,55 +65,107 @@ __device__ __forceinline__ void lds_read16(const unsigned char *src, uint32_t (&
 }  // namespace
 
 // RC: the centre point is removed (8 points; point k sits at grid index
-// k + (k >= 4)).  TW x TH: the output tile, one lane per pixel.
-template <int DT, bool SOFTMAX, bool RC, int TW, int TH>
+// k + (k >= 4)).  TW x TH: the output tile.  GP: groups per work item (1, 2
+// or 4), one lane per (pixel, group), the GP lanes of a pixel adjacent.
+// A staged window pixel holds the item's GP neighbouring group slices, which
+// are contiguous in memory: with four 16-bit groups it is one whole 128-byte
+// line, so the window costs a quarter of the line requests of one group per
+// item, and the GP lanes of a pixel read one contiguous stretch of the
+// offset and mask rows.
+template <int DT, bool SOFTMAX, bool RC, int TW, int TH, int GP>
 #ifndef DCN_LANE_WAVES
 #define DCN_LANE_WAVES 2  // waves per SIMD the register budget must allow
 #endif
-__global__ void __launch_bounds__(TW * TH, DCN_LANE_WAVES) dcn_fwd_lane_kernel(FwdParams p, TileGeom tg) {
+__global__ void __launch_bounds__(TW * TH * GP, DCN_LANE_WAVES) dcn_fwd_lane_kernel(FwdParams p, TileGeom tg) {
   using io = Io<DT>;
-  constexpr int THREADS = TW * TH, R = kLaneHalo;
+  constexpr int THREADS = TW * TH * GP, R = kLaneHalo;
   constexpr int SPAN_W = TW + 2 * R + 3, SPAN_H = TH + 2 * R + 3;
-  constexpr int CG = kGroupChannels;
-  constexpr int PIXB = lane_pixel_stride<DT>();   // one pixel's 16-channel slice
+  constexpr int GS = lane_slice_bytes<DT>();       // one pixel-group slice
+  constexpr int PIXB = GS * GP;                    // one staged window pixel
   constexpr int CHUNK = 16;                        // bytes per ds_read_b128
-  constexpr int NCH = PIXB / CHUNK;                // chunks per slice: 4 (fp32) or 2
+  constexpr int NCH = GS / CHUNK;                  // chunks per slice: 4 (fp32) or 2
   constexpr int CPC = CHUNK / io::kBytes;          // channels per chunk: 4 or 8
   constexpr int ROW = SPAN_W * PIXB;               // LDS bytes per window row
   constexpr int SPAN = SPAN_W * SPAN_H;
-  constexpr int QUADS = THREADS / NCH;             // lanes groups staging one pixel each
-  constexpr int SLOTS = (SPAN + QUADS - 1) / QUADS;
+  constexpr int LPP = PIXB / CHUNK;                // lanes staging one window pixel
+  constexpr int WPIX = THREADS / LPP;              // window pixels per staging slice
   constexpr int LIM_X = SPAN_W - 2, LIM_Y = SPAN_H - 2;
   constexpr int ZERO = SPAN * PIXB;
   constexpr int K = RC ? 8 : 9;
+  constexpr int BANK_PIX = 256 / PIXB;             // window pixels per 256-byte bank row
+  static_assert(GP == 1 || GP == 2 || GP == 4, "one, two or four groups per item");
+  static_assert(PIXB <= 128 && (PIXB & (PIXB - 1)) == 0 && THREADS % LPP == 0, "a window pixel is at most one line");
+
+  // Window slices, the same window pixels for a lane in every item: main
+  // slice u holds rows [u RPS, u RPS + RPS) of columns [0, CW), remainder
+  // slices the rows below and the columns right of that block.  Per item a
+  // slice costs one add; rows outside the map fall out of the image's buffer
+  // range (negative or past its last byte) and read zero, and one column
+  // check per slice rejects columns left or right of the map.
+  constexpr int CW = SPAN_W > 32 ? 32 : SPAN_W;
+  constexpr int RPS = WPIX / CW;
+  constexpr int NM = SPAN_H / RPS;
+  constexpr int REM_A = (SPAN_H - NM * RPS) * CW, REM_B = (SPAN_W - CW) * SPAN_H;
+  constexpr int NR = (REM_A + REM_B + WPIX - 1) / WPIX;
+  constexpr int NRA = NR > 0 ? NR : 1;
+  constexpr int SLOTS = NM + NR;
+  static_assert(RPS >= 1 && NM >= 1, "window slice mapping");
 
   extern __shared__ __align__(16) unsigned char tile[];
 
   const uint32_t lane = threadIdx.x;
-  const int oy = (int)lane / TW, ox = (int)lane % TW;
+  const uint32_t gsel = lane % GP, px = lane / GP;
+  const int oy = (int)px / TW, ox = (int)px % TW;
   const uint32_t pix_bytes = (uint32_t)p.C * io::kBytes;
   const uint32_t row_bytes = (uint32_t)p.W * pix_bytes;
+  const uint32_t img_bytes = (uint32_t)p.H * row_bytes;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.input, p.in_bytes);
-  const __amdgpu_buffer_rsrc_t rout = make_rsrc(p.output, p.pg_total * (uint32_t)(CG * io::kBytes));
+  const __amdgpu_buffer_rsrc_t roff = make_rsrc(p.offset, p.off_bytes);
+  const __amdgpu_buffer_rsrc_t rmask = make_rsrc(p.mask, p.mask_bytes);
+  const __amdgpu_buffer_rsrc_t rout = make_rsrc(p.output, p.out_bytes);
   const float s = p.scale;
+  const uint32_t gblocks = (uint32_t)p.G / GP;     // the launcher checks G % GP == 0
 
   // Zero block after the window (written once; ordered by the first barrier).
   for (int z = (int)lane * 16; z < ROW + 2 * PIXB; z += THREADS * 16)
     *reinterpret_cast<uint4 *>(tile + ZERO + z) = make_uint4(0, 0, 0, 0);
 
-  // Staging: NCH lanes per pixel, SLOTS pixels per lane group.
-  const uint32_t sq = lane / NCH, sc = lane % NCH;
+  // This lane's window slices: LPP lanes per window pixel, one 16-byte chunk each.
+  const uint32_t slot = lane / LPP, sc = lane % LPP;
+  const uint32_t m_col = slot % CW, m_row = slot / CW;
+  const bool m_live = slot < (uint32_t)(RPS * CW);
+  const uint32_t m_lane = m_row * row_bytes + m_col * pix_bytes + sc * CHUNK;
+  const uint32_t m_lds = (m_row * SPAN_W + m_col) * PIXB + sc * CHUNK;
+  uint32_t r_x[NRA], r_lane[NRA], r_lds[NRA];
+  bool r_live[NRA];
+#pragma unroll
+  for (int rho = 0; rho < NR; ++rho) {
+    const uint32_t rs = (uint32_t)rho * WPIX + slot;
+    uint32_t y = 0, x = 0;
+    if (rs < (uint32_t)REM_A) {
+      y = NM * RPS + rs / CW;
+      x = rs % CW;
+    } else if constexpr (SPAN_W > CW) {
+      y = (rs - REM_A) / (SPAN_W - CW);
+      x = CW + (rs - REM_A) % (SPAN_W - CW);
+    }
+    r_live[rho] = rs < (uint32_t)(REM_A + REM_B);
+    r_x[rho] = x;
+    r_lane[rho] = y * row_bytes + x * pix_bytes + sc * CHUNK;
+    r_lds[rho] = (y * SPAN_W + x) * PIXB + sc * CHUNK;
+  }
 
   struct Item {
-    uint32_t g, n;
-    int Y0, X0, ho, wo;
+    uint32_t g0, g, n;
+    int Y0, X0;
     bool live;
-    uint32_t pg;
+    uint32_t pg, rpg;  // rpg: the row the loads read (row 0 for a dead lane)
   };
   auto decode = [&](uint32_t it) {
     Item I;
-    const uint32_t t = fast_div(it, tg.div_g);
-    I.g = it - t * (uint32_t)p.G;
+    const uint32_t t = fast_div(it, tg.div_g);  // divides by the G / GP group blocks
+    I.g0 = (it - t * gblocks) * GP;
+    I.g = I.g0 + gsel;
     I.n = fast_div(t, tg.div_tiles);
     const uint32_t tile_id = t - I.n * (uint32_t)tg.tiles_per_img;
     const uint32_t tyi = fast_div(tile_id, tg.div_tiles_x);
@@ -114,51 +173,52 @@ __global__ void __launch_bounds__(TW * TH, DCN_LANE_WAVES) dcn_fwd_lane_kernel(F
     const int r0 = (int)tyi * TH, c0 = (int)txi * TW;
     I.Y0 = r0 - p.PH - R;  // window origin (stride and dilation 1)
     I.X0 = c0 - p.PW - R;
-    I.ho = r0 + oy;
-    I.wo = c0 + ox;
-    I.live = I.ho < p.Ho && I.wo < p.Wo;
-    I.pg = (((I.n * (uint32_t)p.Ho + I.ho) * (uint32_t)p.Wo + I.wo) * (uint32_t)p.G) + I.g;
+    const int ho = r0 + oy, wo = c0 + ox;
+    I.live = ho < p.Ho && wo < p.Wo;
+    I.pg = (((I.n * (uint32_t)p.Ho + ho) * (uint32_t)p.Wo + wo) * (uint32_t)p.G) + I.g;
+    I.rpg = I.live ? I.pg : 0u;
     return I;
   };
 
   uint32_t win[SLOTS][4];
   auto issue_window = [&](const Item &I) {
-    const uint32_t base = I.n * (uint32_t)p.H * row_bytes + (I.g * CG) * io::kBytes + sc * CHUNK;
+    const __amdgpu_buffer_rsrc_t rimg =
+        make_rsrc(static_cast<const unsigned char *>(p.input) + (size_t)I.n * img_bytes, img_bytes);
+    const uint32_t base = (uint32_t)I.Y0 * row_bytes + (uint32_t)I.X0 * pix_bytes + I.g0 * GS;  // mod 2^32
+    const uint32_t m_off = m_live && (uint32_t)(I.X0 + (int)m_col) < (uint32_t)p.W ? base + m_lane : kOutOfRange;
 #pragma unroll
-    for (int u = 0; u < SLOTS; ++u) {
-      const int idx = (int)sq + u * QUADS;
-      const int sy = idx / SPAN_W, sx = idx - sy * SPAN_W;  // constant divisor
-      const int gy = I.Y0 + sy, gx = I.X0 + sx;
-      const bool ok = idx < SPAN && (uint32_t)gy < (uint32_t)p.H && (uint32_t)gx < (uint32_t)p.W;
-      const uint32_t offb = ok ? base + (uint32_t)gy * row_bytes + (uint32_t)gx * pix_bytes : kOutOfRange;
-      buffer_load_words<4>(rin, offb, win[u]);
+    for (int u = 0; u < NM; ++u) buffer_load_words<4>(rimg, m_off + (uint32_t)(u * RPS) * row_bytes, win[u]);
+#pragma unroll
+    for (int rho = 0; rho < NR; ++rho) {
+      const uint32_t r_off = r_live[rho] && (uint32_t)(I.X0 + (int)r_x[rho]) < (uint32_t)p.W
+                                 ? base + r_lane[rho] : kOutOfRange;
+      buffer_load_words<4>(rimg, r_off, win[NM + rho]);
     }
   };
   auto store_window = [&]() {
+    if (m_live) {
 #pragma unroll
-    for (int u = 0; u < SLOTS; ++u) {
-      const int idx = (int)sq + u * QUADS;
-      if (idx < SPAN)
-        *reinterpret_cast<uint4 *>(tile + idx * PIXB + sc * CHUNK) =
-            make_uint4(win[u][0], win[u][1], win[u][2], win[u][3]);
+      for (int u = 0; u < NM; ++u)
+        *reinterpret_cast<uint4 *>(tile + m_lds + u * RPS * ROW) = make_uint4(win[u][0], win[u][1], win[u][2], win[u][3]);
     }
+#pragma unroll
+    for (int rho = 0; rho < NR; ++rho)
+      if (r_live[rho])
+        *reinterpret_cast<uint4 *>(tile + r_lds[rho]) =
+            make_uint4(win[NM + rho][0], win[NM + rho][1], win[NM + rho][2], win[NM + rho][3]);
   };
 
-  float off[2 * K], msk[K];
-  // Unconditional (a dead lane reads pixel-group 0 and ignores it): every
-  // memory instruction of the item loop is issued on every path, so the
-  // compiler's wait counting stays exact and the window prefetch is only
-  // waited for where the LDS store needs it.
-  auto issue_pgdata = [&](const Item &I) {
-    const uint32_t pg = I.live ? I.pg : 0u;
-    load_offsets<DT, K>(p.offset, pg, off);
-    load_mask<DT, K>(p.mask, pg, msk);
-  };
+  // Offsets and logits of the next item, as the raw words the buffer loads
+  // return: decoded after the next window is in LDS, so the loads overlap a
+  // whole item of compute.  Issued on every path (a dead lane reads row 0),
+  // so the compiler's wait counting stays exact.
+  RowWords<DT, K> rw;
 
-  // Per-lane chunk rotation (bank spreading) and its byte offsets.
+  // Per-lane chunk order (bank spreading): the pixels that share a bank row
+  // at unit offsets start on different chunks.
   int rot[NCH];
 #pragma unroll
-  for (int t = 0; t < NCH; ++t) rot[t] = ((t + (int)lane) % NCH) * CHUNK;
+  for (int t = 0; t < NCH; ++t) rot[t] = ((t + (int)px / BANK_PIX) % NCH) * CHUNK;
 
   const XcdWalk walk = xcd_walk(blockIdx.x, gridDim.x, tg.items);
   const uint32_t end = walk.end;
@@ -166,7 +226,7 @@ __global__ void __launch_bounds__(TW * TH, DCN_LANE_WAVES) dcn_fwd_lane_kernel(F
   Item cur = decode(item < end ? item : 0);
   if (item < end) {
     issue_window(cur);
-    issue_pgdata(cur);
+    load_row_words<DT, K>(roff, rmask, cur.rpg, rw);
   }
 
   while (item < end) {
@@ -174,138 +234,143 @@ __global__ void __launch_bounds__(TW * TH, DCN_LANE_WAVES) dcn_fwd_lane_kernel(F
     store_window();
     __syncthreads();  // the window is in LDS
 
-    // The next item's window lands in registers during this item's compute;
-    // its offsets and logits are requested once this item's are consumed.
-    // (Issued on the last item too, re-reading its own data, so that no
-    // branch changes the count of outstanding loads.)
+    // This item's rows (the offsets are decoded point by point).
+    const RowWords<DT, K> cw = rw;
+
+    // The next item's window and rows land in registers during this item's
+    // compute.  (Issued on the last item too, re-reading its own data, so
+    // that no branch changes the count of outstanding loads.)
     const uint32_t next = item + walk.stride;
     const bool more = next < end;  // block-uniform
     const Item nx = decode(more ? next : item);
     issue_window(nx);
+    load_row_words<DT, K>(roff, rmask, nx.rpg, rw);
 
-    {
-      // modulation scalars
-      float m[K];
-      if constexpr (SOFTMAX) {
-        float mx = msk[0];
+    // modulation scalars
+    float msk[K], m[K];
+    decode_mask_words<DT, K>(cur.rpg, cw, msk);
+    if constexpr (SOFTMAX) {
+      float mx = msk[0];
 #pragma unroll
-        for (int k = 1; k < K; ++k) mx = fmaxf(mx, msk[k]);
-        float sum = 0.f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          m[k] = __expf(msk[k] - mx);
-          sum += m[k];
-        }
-        const float inv = __builtin_amdgcn_rcpf(sum);
-#pragma unroll
-        for (int k = 0; k < K; ++k) m[k] *= inv;
-      } else {
-#pragma unroll
-        for (int k = 0; k < K; ++k) m[k] = msk[k];
-      }
-
-      float acc[NCH][CPC];
-#pragma unroll
-      for (int t = 0; t < NCH; ++t)
-#pragma unroll
-        for (int c = 0; c < CPC; ++c) acc[t][c] = 0.f;
-
-      const uint32_t img = cur.n * (uint32_t)p.H * row_bytes;
-      const uint32_t chan = (cur.g * CG) * io::kBytes;
-
+      for (int k = 1; k < K; ++k) mx = fmaxf(mx, msk[k]);
+      float sum = 0.f;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        // Wave priority falls as the wave moves through the points, so the
-        // waves furthest behind issue first and the block reaches its next
-        // barrier with less spread.
-        if (k == 0) __builtin_amdgcn_s_setprio(3);
-        if (k == 3) __builtin_amdgcn_s_setprio(2);
-        if (k == 6) __builtin_amdgcn_s_setprio(1);
-        const int q = RC ? k + (k >= 4) : k;  // grid index
-        const int i = q / 3, j = q % 3;
-        const float dx = s * off[2 * k], dy = s * off[2 * k + 1];
-        const bool nan_loc = (dx != dx) | (dy != dy);
-        const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
-        const float cy = __builtin_amdgcn_fmed3f(dy, -16777216.f, 16777216.f);
-        const float fx = floorf(cx), fy = floorf(cy);
-        const float lx = cx - fx, ly = cy - fy;
-        // window coordinates: regular position oy + i + R (stride/dilation 1)
-        const int ty = oy + i + R + (int)fy, tx = ox + j + R + (int)fx;
-        const float mk = nan_loc ? __builtin_nanf("") : m[k];
-        const float wy0 = (1.f - ly) * mk, wy1 = ly * mk;
-        const float w00 = wy0 * (1.f - lx), w01 = wy0 * lx;
-        const float w10 = wy1 * (1.f - lx), w11 = wy1 * lx;
-        const bool inside = !nan_loc && (uint32_t)ty <= (uint32_t)LIM_Y && (uint32_t)tx <= (uint32_t)LIM_X;
-        const int A = inside ? ty * ROW + tx * PIXB : ZERO;
-        const unsigned char *src = tile + A;
+        m[k] = __expf(msk[k] - mx);
+        sum += m[k];
+      }
+      const float inv = __builtin_amdgcn_rcpf(sum);
 #pragma unroll
-        for (int t = 0; t < NCH; ++t) {
-          const unsigned char *q = src + rot[t];
-          uint32_t v00[4], v01[4], v10[4], v11[4];
-          lds_read16(q, v00);
-          lds_read16(q + PIXB, v01);
-          lds_read16(q + ROW, v10);
-          lds_read16(q + ROW + PIXB, v11);
-          float f00[CPC], f01[CPC], f10[CPC], f11[CPC];
-          unpack<DT, 4>(v00, f00);
-          unpack<DT, 4>(v01, f01);
-          unpack<DT, 4>(v10, f10);
-          unpack<DT, 4>(v11, f11);
+      for (int k = 0; k < K; ++k) m[k] *= inv;
+    } else {
 #pragma unroll
-          for (int c = 0; c < CPC; ++c) {
-            acc[t][c] = fmaf(w00, f00[c], acc[t][c]);
-            acc[t][c] = fmaf(w01, f01[c], acc[t][c]);
-            acc[t][c] = fmaf(w10, f10[c], acc[t][c]);
-            acc[t][c] = fmaf(w11, f11[c], acc[t][c]);
-          }
-          pin_values(acc[t]);  // the chunk's FMAs happen here, not at the end
+      for (int k = 0; k < K; ++k) m[k] = msk[k];
+    }
+
+    float acc[NCH][CPC];
+#pragma unroll
+    for (int t = 0; t < NCH; ++t)
+#pragma unroll
+      for (int c = 0; c < CPC; ++c) acc[t][c] = 0.f;
+
+    const uint32_t img = cur.n * img_bytes;
+    const uint32_t chan = cur.g * GS;
+    const unsigned char *slice = tile + gsel * GS;  // this lane's group in a window pixel
+
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      // Wave priority falls as the wave moves through the points, so the
+      // waves furthest behind issue first and the block reaches its next
+      // barrier with less spread.
+      if (k == 0) __builtin_amdgcn_s_setprio(3);
+      if (k == 3) __builtin_amdgcn_s_setprio(2);
+      if (k == 6) __builtin_amdgcn_s_setprio(1);
+      const int q = RC ? k + (k >= 4) : k;  // grid index
+      const int i = q / 3, j = q % 3;
+      float ox_k, oy_k;
+      offset_words_xy<DT, K>(cw, k, ox_k, oy_k);
+      const float dx = s * ox_k, dy = s * oy_k;
+      const bool nan_loc = (dx != dx) | (dy != dy);
+      const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
+      const float cy = __builtin_amdgcn_fmed3f(dy, -16777216.f, 16777216.f);
+      const float fx = floorf(cx), fy = floorf(cy);
+      const float lx = cx - fx, ly = cy - fy;
+      // window coordinates: regular position oy + i + R (stride/dilation 1)
+      const int ty = oy + i + R + (int)fy, tx = ox + j + R + (int)fx;
+      const float mk = nan_loc ? __builtin_nanf("") : m[k];
+      const float wy0 = (1.f - ly) * mk, wy1 = ly * mk;
+      const float w00 = wy0 * (1.f - lx), w01 = wy0 * lx;
+      const float w10 = wy1 * (1.f - lx), w11 = wy1 * lx;
+      const bool inside = !nan_loc && (uint32_t)ty <= (uint32_t)LIM_Y && (uint32_t)tx <= (uint32_t)LIM_X;
+      // (24-bit multiply: an inside ty is below the span)
+      const uint32_t A = inside ? (uint32_t)__umul24((uint32_t)ty, (uint32_t)ROW) + (uint32_t)tx * PIXB : (uint32_t)ZERO;
+      const unsigned char *src = slice + A;
+#pragma unroll
+      for (int t = 0; t < NCH; ++t) {
+        const unsigned char *q = src + rot[t];
+        uint32_t v00[4], v01[4], v10[4], v11[4];
+        lds_read16(q, v00);
+        lds_read16(q + PIXB, v01);
+        lds_read16(q + ROW, v10);
+        lds_read16(q + ROW + PIXB, v11);
+        float f00[CPC], f01[CPC], f10[CPC], f11[CPC];
+        unpack<DT, 4>(v00, f00);
+        unpack<DT, 4>(v01, f01);
+        unpack<DT, 4>(v10, f10);
+        unpack<DT, 4>(v11, f11);
+#pragma unroll
+        for (int c = 0; c < CPC; ++c) {
+          acc[t][c] = fmaf(w00, f00[c], acc[t][c]);
+          acc[t][c] = fmaf(w01, f01[c], acc[t][c]);
+          acc[t][c] = fmaf(w10, f10[c], acc[t][c]);
+          acc[t][c] = fmaf(w11, f11[c], acc[t][c]);
         }
-        // Corners outside the window but touching the map: global gathers
-        // (rare; the wave skips this when no lane needs it).
-        const bool fb = !inside && !nan_loc;
-        if (__builtin_amdgcn_ballot_w64(fb) != 0) {
-          if (fb) {
-            const int y0 = cur.Y0 + ty, x0 = cur.X0 + tx;
-            const bool vy0 = (uint32_t)y0 < (uint32_t)p.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)p.H;
-            const bool vx0 = (uint32_t)x0 < (uint32_t)p.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)p.W;
-            const uint32_t a00 = img + (uint32_t)y0 * row_bytes + (uint32_t)x0 * pix_bytes + chan;
+        pin_values(acc[t]);  // the chunk's FMAs happen here, not at the end
+      }
+      // Corners outside the window but touching the map: global gathers
+      // (rare; the wave skips this when no lane needs it).
+      const bool fb = !inside && !nan_loc;
+      if (__builtin_amdgcn_ballot_w64(fb) != 0) {
+        if (fb) {
+          const int y0 = cur.Y0 + ty, x0 = cur.X0 + tx;
+          const bool vy0 = (uint32_t)y0 < (uint32_t)p.H, vy1 = (uint32_t)(y0 + 1) < (uint32_t)p.H;
+          const bool vx0 = (uint32_t)x0 < (uint32_t)p.W, vx1 = (uint32_t)(x0 + 1) < (uint32_t)p.W;
+          const uint32_t a00 = img + (uint32_t)y0 * row_bytes + (uint32_t)x0 * pix_bytes + chan;
 #pragma unroll
-            for (int t = 0; t < NCH; ++t) {
-              uint32_t v00[4], v01[4], v10[4], v11[4];
-              const uint32_t ct = (uint32_t)rot[t];
-              buffer_load_words<4>(rin, (vy0 && vx0) ? a00 + ct : kOutOfRange, v00);
-              buffer_load_words<4>(rin, (vy0 && vx1) ? a00 + pix_bytes + ct : kOutOfRange, v01);
-              buffer_load_words<4>(rin, (vy1 && vx0) ? a00 + row_bytes + ct : kOutOfRange, v10);
-              buffer_load_words<4>(rin, (vy1 && vx1) ? a00 + row_bytes + pix_bytes + ct : kOutOfRange, v11);
-              float f00[CPC], f01[CPC], f10[CPC], f11[CPC];
-              unpack<DT, 4>(v00, f00);
-              unpack<DT, 4>(v01, f01);
-              unpack<DT, 4>(v10, f10);
-              unpack<DT, 4>(v11, f11);
+          for (int t = 0; t < NCH; ++t) {
+            uint32_t v00[4], v01[4], v10[4], v11[4];
+            const uint32_t ct = (uint32_t)rot[t];
+            buffer_load_words<4>(rin, (vy0 && vx0) ? a00 + ct : kOutOfRange, v00);
+            buffer_load_words<4>(rin, (vy0 && vx1) ? a00 + pix_bytes + ct : kOutOfRange, v01);
+            buffer_load_words<4>(rin, (vy1 && vx0) ? a00 + row_bytes + ct : kOutOfRange, v10);
+            buffer_load_words<4>(rin, (vy1 && vx1) ? a00 + row_bytes + pix_bytes + ct : kOutOfRange, v11);
+            float f00[CPC], f01[CPC], f10[CPC], f11[CPC];
+            unpack<DT, 4>(v00, f00);
+            unpack<DT, 4>(v01, f01);
+            unpack<DT, 4>(v10, f10);
+            unpack<DT, 4>(v11, f11);
 #pragma unroll
-              for (int c = 0; c < CPC; ++c) {
-                acc[t][c] = fmaf(w00, f00[c], acc[t][c]);
-                acc[t][c] = fmaf(w01, f01[c], acc[t][c]);
-                acc[t][c] = fmaf(w10, f10[c], acc[t][c]);
-                acc[t][c] = fmaf(w11, f11[c], acc[t][c]);
-              }
+            for (int c = 0; c < CPC; ++c) {
+              acc[t][c] = fmaf(w00, f00[c], acc[t][c]);
+              acc[t][c] = fmaf(w01, f01[c], acc[t][c]);
+              acc[t][c] = fmaf(w10, f10[c], acc[t][c]);
+              acc[t][c] = fmaf(w11, f11[c], acc[t][c]);
             }
           }
         }
       }
+    }
 
-      // acc[t] holds the chunk at byte offset rot[t] of the 16-channel slice;
-      // a dead lane's store carries an out-of-range offset and is dropped.
-      const uint32_t obase = cur.live ? cur.pg * (uint32_t)(CG * io::kBytes) : kOutOfRange;
+    // acc[t] holds the chunk at byte offset rot[t] of the 16-channel slice;
+    // a dead lane's store carries an out-of-range offset and is dropped.
+    const uint32_t obase = cur.live ? cur.pg * (uint32_t)GS : kOutOfRange;
 #pragma unroll
-      for (int t = 0; t < NCH; ++t) {
-        uint32_t w[4];
-        pack_words<DT, CPC>(acc[t], w);
-        buffer_store_words<4>(rout, obase + (uint32_t)rot[t], w);
-      }
+    for (int t = 0; t < NCH; ++t) {
+      uint32_t w[4];
+      pack_words<DT, CPC>(acc[t], w);
+      buffer_store_words<4>(rout, obase + (uint32_t)rot[t], w);
     }
     __builtin_amdgcn_s_setprio(0);
-    issue_pgdata(nx);
 
     item = next;
     cur = nx;
@@ -314,11 +379,18 @@ __global__ void __launch_bounds__(TW * TH, DCN_LANE_WAVES) dcn_fwd_lane_kernel(F
 
 namespace {
 
-template <int DT, bool SM, bool RC, int TW, int TH>
+#ifndef DCN_LANE_GP_MAX
+#define DCN_LANE_GP_MAX 4
+#endif
+#ifndef DCN_LANE_TH4
+#define DCN_LANE_TH4 8  // height of the 16-wide tiles with four groups per item
+#endif
+
+template <int DT, bool SM, bool RC, int TW, int TH, int GP>
 hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_fwd_lane_kernel<DT, SM, RC, TW, TH>;
-  constexpr int THREADS = TW * TH;
-  const size_t lds = lane_lds_bytes<TW, TH>(lane_pixel_stride<DT>());
+  auto kern = dcn_fwd_lane_kernel<DT, SM, RC, TW, TH, GP>;
+  constexpr int THREADS = TW * TH * GP;
+  const size_t lds = lane_lds_bytes<TW, TH>(lane_slice_bytes<DT>() * GP);
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -339,21 +411,39 @@ hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool RC, int TW, int TH>
-hipError_t launch_lane_dt(int dtype, int softmax, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  switch (dtype) {
-    case DCN_F32:
-      if constexpr (TW == 16) {  // the 24x8 tile is 16-bit only (fp32 would need 19 window slots per lane)
-        return softmax ? launch_lane<DCN_F32, true, RC, TW, TH>(p, tg, s) : launch_lane<DCN_F32, false, RC, TW, TH>(p, tg, s);
-      } else {
-        return hipErrorNotSupported;
-      }
-    case DCN_F16:
-      return softmax ? launch_lane<DCN_F16, true, RC, TW, TH>(p, tg, s) : launch_lane<DCN_F16, false, RC, TW, TH>(p, tg, s);
-    case DCN_BF16:
-      return softmax ? launch_lane<DCN_BF16, true, RC, TW, TH>(p, tg, s) : launch_lane<DCN_BF16, false, RC, TW, TH>(p, tg, s);
-    default: return hipErrorInvalidValue;
+// Tile shape of each kind of work item: 16 x 16, or 16 x 8 with four
+// groups (a 1024-thread block would have half the registers per lane), or
+// 24 x 8 (16-bit).
+struct LaneShape {
+  int tw, th;
+};
+
+LaneShape lane_shape(bool wide, int gp) {
+  if (wide) return LaneShape{24, 8};
+  return gp == 4 ? LaneShape{16, DCN_LANE_TH4} : LaneShape{16, 16};
+}
+
+template <int DT, bool SM, bool RC>
+hipError_t launch_lane_shape(bool wide, int gp, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
+  if constexpr (DT == DCN_F32) {  // one group per item, 16x16 tiles (the 24x8 window would need 19 slots per lane)
+    if (wide || gp != 1) return hipErrorNotSupported;
+    return launch_lane<DT, SM, RC, 16, 16, 1>(p, tg, s);
+  } else {
+    if (gp == 4)
+      return wide ? launch_lane<DT, SM, RC, 24, 8, 4>(p, tg, s) : launch_lane<DT, SM, RC, 16, DCN_LANE_TH4, 4>(p, tg, s);
+    if (gp == 2)
+      return wide ? launch_lane<DT, SM, RC, 24, 8, 2>(p, tg, s) : launch_lane<DT, SM, RC, 16, 16, 2>(p, tg, s);
+    return wide ? launch_lane<DT, SM, RC, 24, 8, 1>(p, tg, s) : launch_lane<DT, SM, RC, 16, 16, 1>(p, tg, s);
   }
+}
+
+template <int DT>
+hipError_t launch_lane_dt(bool wide, int gp, int softmax, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
+  if (p.RC)
+    return softmax ? launch_lane_shape<DT, true, true>(wide, gp, p, tg, s)
+                   : launch_lane_shape<DT, false, true>(wide, gp, p, tg, s);
+  return softmax ? launch_lane_shape<DT, true, false>(wide, gp, p, tg, s)
+                 : launch_lane_shape<DT, false, false>(wide, gp, p, tg, s);
 }
 
 // Share of the tiles' lanes that hold an output pixel.
@@ -365,29 +455,48 @@ double lane_use(const FwdParams &p, int tw, int th) {
 }  // namespace
 
 // Stride 1, dilation 1, 3x3 points only; hipErrorNotSupported otherwise.
+// 16-bit I/O takes four groups per work item where the group count allows
+// (two, else one), fp32 one.
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
   if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
     return hipErrorNotSupported;
-  // 24x8 tiles (16-bit) where they leave clearly fewer lanes idle than 16x16
-  const bool wide = dtype != DCN_F32 && lane_use(p, 24, 8) > lane_use(p, 16, 16) + 0.1;
-  const int tw = wide ? 24 : 16, th = wide ? 8 : 16;
+  if (dtype != DCN_F32 && dtype != DCN_F16 && dtype != DCN_BF16) return hipErrorInvalidValue;
+  int gp = 1;
+  if (dtype != DCN_F32) {
+    if (p.G % 4 == 0 && DCN_LANE_GP_MAX >= 4) gp = 4;
+    else if (p.G % 2 == 0 && DCN_LANE_GP_MAX >= 2) gp = 2;
+  }
+  const LaneShape sq = lane_shape(false, gp), sw = lane_shape(true, gp);
+  // 24x8 tiles where they leave clearly fewer lanes idle; with four groups
+  // also where they leave as few (768 threads, twelve waves, against 512 on
+  // 16x8 tiles, and fewer halo pixels per output pixel: 4.7 against 5.6)
+  const double use_w = lane_use(p, sw.tw, sw.th), use_q = lane_use(p, sq.tw, sq.th);
+  const bool wide = dtype != DCN_F32 && (use_w > use_q + 0.1 || (gp == 4 && use_w >= use_q));
+  const LaneShape sh = wide ? sw : sq;
   TileGeom tg{};
-  tg.span_w = tw + 2 * kLaneHalo + 3;
-  tg.span_h = th + 2 * kLaneHalo + 3;
-  const int tiles_y = (p.Ho + th - 1) / th;
-  tg.tiles_x = (p.Wo + tw - 1) / tw;
+  tg.span_w = sh.tw + 2 * kLaneHalo + 3;
+  tg.span_h = sh.th + 2 * kLaneHalo + 3;
+  // The window rows above and below the map are rejected by the buffer range
+  // of their image, which needs the byte offset of every window row relative
+  // to the image to fit int32.
+  const int64_t row_bytes = (int64_t)p.W * p.C * (dtype == DCN_F32 ? 4 : 2);
+  if (((int64_t)p.H + p.PH + tg.span_h + 1) * row_bytes >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  const int tiles_y = (p.Ho + sh.th - 1) / sh.th;
+  tg.tiles_x = (p.Wo + sh.tw - 1) / sh.tw;
   tg.tiles_per_img = tiles_y * tg.tiles_x;
   const int64_t imgs = p.pg_total / ((int64_t)p.Ho * p.Wo * p.G);
-  const int64_t items = imgs * tg.tiles_per_img * p.G;
+  const int64_t items = imgs * tg.tiles_per_img * (p.G / gp);
   if (items <= 0 || items >= (int64_t(1) << 31)) return hipErrorNotSupported;
   tg.items = (uint32_t)items;
-  tg.div_g = make_fast_div((uint32_t)p.G);
+  tg.div_g = make_fast_div((uint32_t)(p.G / gp));  // group blocks per tile
   tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
-  if (wide)
-    return p.RC ? launch_lane_dt<true, 24, 8>(dtype, softmax, p, tg, s) : launch_lane_dt<false, 24, 8>(dtype, softmax, p, tg, s);
-  return p.RC ? launch_lane_dt<true, 16, 16>(dtype, softmax, p, tg, s) : launch_lane_dt<false, 16, 16>(dtype, softmax, p, tg, s);
+  switch (dtype) {
+    case DCN_F32: return launch_lane_dt<DCN_F32>(wide, gp, softmax, p, tg, s);
+    case DCN_F16: return launch_lane_dt<DCN_F16>(wide, gp, softmax, p, tg, s);
+    default: return launch_lane_dt<DCN_BF16>(wide, gp, softmax, p, tg, s);
+  }
 }
 
 }  // namespace dcn

@@ -107,6 +107,13 @@ PATH_CASES = [
              offset_dist=normal(2.0), seed=45),
     # 24 wide, 41 high: 16-bit lane kernel with 24x8 tiles (the last tile row holds one row)
     Workload("path_24wide", n=2, h=41, w=24, c=48, groups=3, offset_dist=uniform(4.0), seed=46),
+    # group counts divisible by four (the 16-bit lane kernel's four-group
+    # items): ragged 16x16 tiles, the 24-wide tiles with far offsets, and the
+    # stage-2 count of 20 groups
+    Workload("path_quads", n=2, h=37, w=29, c=128, groups=8, offset_dist=normal(2.5), seed=47),
+    Workload("path_quads_v4_24wide", n=2, h=33, w=24, c=64, groups=4, softmax=False,
+             mask_dist=normal(0.5), offset_dist=uniform(4.0), seed=48),
+    Workload("path_groups20", n=1, h=20, w=18, c=320, groups=20, seed=49),
 ]
 
 
@@ -123,11 +130,12 @@ def test_forward_each_kernel(wl, dtype, path, monkeypatch):
     gate(_np(run_forward(wl, t)), oracle_full(wl, t), dtype, f"{wl.name}/{dtype}/{path}")
 
 
+@pytest.mark.parametrize("groups", [3, 4])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_forward_remove_center_every_path(dtype, monkeypatch):
+def test_forward_remove_center_every_path(dtype, groups, monkeypatch):
     """With remove_center every forced kernel choice ends in a kernel that
     handles it (the tiled kernels refuse the 8-point rows)."""
-    wl = Workload("rc_paths", n=2, h=37, w=29, c=48, groups=3, offset_dist=normal(2.0),
+    wl = Workload("rc_paths", n=2, h=37, w=29, c=16 * groups, groups=groups, offset_dist=normal(2.0),
                   remove_center=True, dtype=dtype, seed=27)
     t = synth.make_inputs(wl)
     ref = oracle_full(wl, t)
