@@ -38,10 +38,24 @@ HBM_PEAK_GBS = 8000.0
 CSRC = ROOT / "deformable_convolution_vision_dcn_amd" / "csrc"
 
 
-def kernel_source_hash() -> str:
+# The source file of each kernel whose counters the bench reads.
+KERNEL_SOURCES = {
+    "dcn_fwd_tile_kernel": "dcn_fwd_tile.hip", "dcn_fwd_lane_kernel": "dcn_fwd_lane.hip",
+    "dcn_fwd_map_kernel": "dcn_fwd_map.hip", "dcn_fwd_kernel": "dcn_forward.hip",
+    "dcn_fused_kernel": "dcn_fused.hip", "dcn_bwd_quad_kernel": "dcn_bwd_quad.hip",
+    "dcn_bwd_tile_kernel": "dcn_bwd_tile.hip", "dcn_bwd_kernel": "dcn_backward.hip",
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of what decides `kernel`'s code and launch: its own source file,
+    the shared device headers, the host entry points and the public header
+    (every library source for a kernel not listed)."""
     h = hashlib.sha256()
+    own = KERNEL_SOURCES.get(kernel)
     for f in sorted(CSRC.glob("*")):
-        if f.suffix in (".hip", ".hpp", ".h"):
+        shared = f.suffix in (".hpp", ".h") or f.name == "dcn_api.hip"
+        if f.suffix in (".hip", ".hpp", ".h") and (own is None or shared or f.name == own):
             h.update(f.name.encode())
             h.update(f.read_bytes())
     h.update((ROOT / "include" / "dcn.h").read_bytes())
@@ -153,7 +167,7 @@ def traffic_from_profile(kernel: str, workload: str):
     text = path.read_text()
     m_hash = re.search(r"kernel_source_sha256:\s*(\w+)", text)
     m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_hash and m_val) or m_hash.group(1) != kernel_source_hash():
+    if not (m_hash and m_val) or m_hash.group(1) != kernel_source_hash(kernel):
         return None
     return float(m_val.group(1))
 
@@ -207,7 +221,7 @@ def summarize_counters(root: pathlib.Path, workload: str, kernel: str, command: 
     lines = [
         f"# HBM traffic and counters of {kernel}, workload {workload}",
         f"command: {command}",
-        f"kernel_source_sha256: {kernel_source_hash()}",
+        f"kernel_source_sha256: {kernel_source_hash(kernel)}",
         f"dispatches_fetch: {len(fetch)}  write: {len(write)}",
         f"FETCH_SIZE_KiB_per_dispatch_raw: {sum(fetch) / len(fetch):.1f}",
         f"WRITE_SIZE_KiB_per_dispatch_raw: {sum(write) / len(write):.1f}",

@@ -49,3 +49,24 @@ def test_host_cpu_report():
     h = bench.host_cpu()
     assert h["cores_available"] >= 1 and 1 <= h["cores_usable"] <= bench.GPU_HOST_SHARE
     assert isinstance(h["model"], str) and h["model"]
+
+
+def test_counter_hash_follows_the_kernels_own_sources(tmp_path, monkeypatch):
+    """A counter summary goes stale when its kernel's file, a shared header or
+    the entry points change, and not when another kernel's file does."""
+    for f in bench.CSRC.glob("*"):
+        if f.suffix in (".hip", ".hpp", ".h"):
+            (tmp_path / f.name).write_bytes(f.read_bytes())
+    monkeypatch.setattr(bench, "CSRC", tmp_path)
+    before = {k: bench.kernel_source_hash(k) for k in ("dcn_fwd_tile_kernel", "dcn_bwd_quad_kernel")}
+
+    def touched(name):
+        p = tmp_path / name
+        p.write_bytes(p.read_bytes() + b"\n// edit\n")
+        return {k: bench.kernel_source_hash(k) for k in before}
+
+    after = touched("dcn_bwd_quad.hip")
+    assert after["dcn_fwd_tile_kernel"] == before["dcn_fwd_tile_kernel"]
+    assert after["dcn_bwd_quad_kernel"] != before["dcn_bwd_quad_kernel"]
+    shared = touched("dcn_device.hpp")
+    assert all(shared[k] != after[k] for k in before)
