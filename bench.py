@@ -47,18 +47,27 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> bytes:
+    """C/C++ source without its comments and blank space (so that editing a
+    comment does not change the hash)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split()).encode()
+
+
 def kernel_source_hash(kernel: str) -> str:
-    """Hash of what decides `kernel`'s code and launch: its own source file,
-    the shared device headers, the host entry points and the public header
-    (every library source for a kernel not listed)."""
+    """Hash of the code that decides `kernel`'s instructions and launch: its
+    own source file, the shared device headers, the host entry points and the
+    public header (every library source for a kernel not listed), comments
+    left out."""
     h = hashlib.sha256()
     own = KERNEL_SOURCES.get(kernel)
     for f in sorted(CSRC.glob("*")):
         shared = f.suffix in (".hpp", ".h") or f.name == "dcn_api.hip"
         if f.suffix in (".hip", ".hpp", ".h") and (own is None or shared or f.name == own):
             h.update(f.name.encode())
-            h.update(f.read_bytes())
-    h.update((ROOT / "include" / "dcn.h").read_bytes())
+            h.update(_code_only(f.read_text()))
+    h.update(_code_only((ROOT / "include" / "dcn.h").read_text()))
     return h.hexdigest()[:16]
 
 

@@ -161,7 +161,13 @@ int dcn_forward(const dcn_problem *p, const void *input, const void *offset, con
  * Every tensor is in p->dtype; input, guide, the weights and output 16-byte
  * aligned.  Errors as dcn_forward, plus DCN_ERR_SHAPE for guide_channels and
  * DCN_ERR_UNSUPPORTED when one group's generated values do not fit the
- * kernel's LDS.  Enqueues one launch per chunk of images. */
+ * kernel's LDS.  Enqueues one launch per chunk of images.
+ * Throughput: the fused kernel gathers its corners from global memory (its
+ * blocks own a few pixels with all their groups, where the sampling kernels
+ * stage one tile's window of one or a few groups), so on MI355X at the
+ * InternImage stage shapes this call takes about twice as long as a
+ * library GEMM for the two branches followed by dcn_forward.  It is for
+ * callers that must not hold the offset and mask tensors. */
 int dcn_forward_generated(const dcn_problem *p, int32_t guide_channels, const void *input, const void *guide,
                           const void *w_offset, const void *b_offset, const void *w_mask, const void *b_mask,
                           void *output, void *hip_stream);
@@ -176,7 +182,12 @@ int dcn_forward_generated(const dcn_problem *p, int32_t guide_channels, const vo
  *   w_out (C, C), row-major (out, in); b_out (C) or NULL.
  * Layouts, errors and chunking otherwise as dcn_forward
  * (DCN_ERR_UNSUPPORTED when the kernel's LDS cannot hold 16 pixels of C
- * channels). */
+ * channels).
+ * Throughput: each block of 16 pixels reads all of w_out for its one
+ * matrix-core row tile and gathers its corners from global memory, so this
+ * call is 2.5x (C = 160) to 16x (C = 1280) slower on MI355X than
+ * dcn_forward followed by a library GEMM; it is for callers that must not
+ * hold the core's output before the projection. */
 int dcn_forward_projected(const dcn_problem *p, const void *input, const void *offset, const void *mask,
                           const void *w_out, const void *b_out, void *output, void *hip_stream);
 

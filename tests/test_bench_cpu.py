@@ -62,7 +62,7 @@ def test_counter_hash_follows_the_kernels_own_sources(tmp_path, monkeypatch):
 
     def touched(name):
         p = tmp_path / name
-        p.write_bytes(p.read_bytes() + b"\n// edit\n")
+        p.write_bytes(p.read_bytes() + b"\nnamespace dcn {}\n")
         return {k: bench.kernel_source_hash(k) for k in before}
 
     after = touched("dcn_bwd_quad.hip")
@@ -70,3 +70,16 @@ def test_counter_hash_follows_the_kernels_own_sources(tmp_path, monkeypatch):
     assert after["dcn_bwd_quad_kernel"] != before["dcn_bwd_quad_kernel"]
     shared = touched("dcn_device.hpp")
     assert all(shared[k] != after[k] for k in before)
+
+
+def test_counter_hash_ignores_comments(tmp_path, monkeypatch):
+    for f in bench.CSRC.glob("*"):
+        if f.suffix in (".hip", ".hpp", ".h"):
+            (tmp_path / f.name).write_bytes(f.read_bytes())
+    monkeypatch.setattr(bench, "CSRC", tmp_path)
+    before = bench.kernel_source_hash("dcn_fwd_tile_kernel")
+    p = tmp_path / "dcn_fwd_tile.hip"
+    p.write_text(p.read_text() + "\n// a remark\n/* another\n   remark */\n")
+    assert bench.kernel_source_hash("dcn_fwd_tile_kernel") == before
+    p.write_text(p.read_text() + "\nnamespace dcn {}\n")
+    assert bench.kernel_source_hash("dcn_fwd_tile_kernel") != before
