@@ -236,11 +236,13 @@ Path path_override() {
 // one or more groups, fits in LDS runs the whole-map kernel (every lane
 // busy, several groups per item, no halo re-reads, no global fix-ups).  Other maps that
 // fit a tile window: fp32 runs the quad tiled kernel (a quad of lanes per
-// pixel-group; two groups per work item where the group count is even),
-// 16-bit I/O the lane-per-pixel-group kernel, which needs a quarter of the
-// address and weight arithmetic and wins once a pixel's 16 channels are only
-// 32 bytes.  Without the kernel's centre (8 points) the lane kernel serves
-// every dtype.  Everything else runs the untiled kernel.
+// pixel-group; two groups per work item where the group count is even; also
+// at stride 2 and dilation 2, and without the kernel's centre), 16-bit I/O
+// the lane-per-pixel-group kernel at stride and dilation 1 (one, two or four
+// groups per work item), which needs a quarter of the address and weight
+// arithmetic and wins once a pixel's 16 channels are only 32 bytes, and the
+// quad tiled kernel at other strides and dilations.  Everything else runs
+// the untiled kernel.
 // Whether the whole-map kernel is the first choice: the output map is
 // smaller than one 16x16 tile, or tiles would leave over half of their
 // pixel slots empty.  (At 24x24, 56 % full, the tiled lane kernel is still
@@ -268,7 +270,7 @@ hipError_t launch_forward(int dtype, int softmax, const FwdParams &p, hipStream_
       const hipError_t t = launch_forward_tiled(dtype, softmax, p, s, gpi);
       if (t != hipErrorNotSupported) return t;
     }
-    if (!lane_first && forced == Path::kAuto) {  // fp32 rows the tiled kernels refuse (remove_center)
+    if (!lane_first && forced == Path::kAuto) {  // fp32 problems whose window the tiled kernels refuse
       const hipError_t l = launch_forward_lane(dtype, softmax, p, s);
       if (l != hipErrorNotSupported) return l;
     }

@@ -38,7 +38,9 @@
  *   grad_*       the shape of the tensor it is the gradient of.
  *
  * Arithmetic: sampling locations, weights, the softmax and every accumulation
- * are fp32 for every I/O dtype; 16-bit results are rounded to nearest-even.
+ * are fp32 for every I/O dtype (the tiled backward sums grad_input in exact
+ * integer arithmetic on a per-tile fixed-point grid instead, with the error
+ * bound stated at dcn_backward); 16-bit results are rounded to nearest-even.
  *
  * Ownership and execution: every tensor pointer is a DEVICE pointer owned by
  * the caller.  dcn_forward and dcn_backward allocate nothing, keep no
@@ -53,10 +55,12 @@
  * 16x16 tile, or that such tiles would leave over half empty, run the
  * whole-map kernel; other maps whose tile window fits the LDS run a tiled
  * kernel (fp32: the quad kernel, two groups per work item where the group
- * count is even; 16-bit I/O and fp32 without the centre: the lane kernel);
- * everything else (other point sets, strides whose windows do not fit) runs
- * the untiled kernel.  The backward runs the tiled quad kernel at stride 1
- * and dilation 1 or 2, else the untiled kernel.  The environment variable
+ * count is even, at stride 1 or 2 and dilation 1 or 2, with or without the
+ * centre; 16-bit I/O: the lane kernel, up to four groups per work item, at
+ * stride and dilation 1, else the quad kernel); everything else (other
+ * point sets, windows that do not fit) runs the untiled kernel.  The
+ * backward runs the tiled quad kernel at stride 1 or 2 and dilation 1 or 2,
+ * else the untiled kernel.  The environment variable
  * DCN_MI355X_FWD_PATH = "generic" | "tiled" (one group per work item) |
  * "pair" (two groups per work item) | "lane" | "map" (whole maps in LDS),
  * read at every call, makes the forward try that kernel first;
