@@ -90,6 +90,47 @@ __device__ __forceinline__ int2 pair_sums(uint64_t v) {
   return make_int2(lo, hi);
 }
 
+// Lane-constant slices of a SW x SH window for WP lane groups: main slice u
+// holds rows [u RPS, u RPS + RPS) of columns [0, CW) (CW divides WP, so
+// every group has a pixel in every main slice), remainder slice rho the
+// pixels rho WP + group of the rows below (columns [0, CW)) and then of the
+// columns right of that block.  A group keeps its column in every main
+// slice, so per item a main slice costs one add.
+constexpr int slice_width(int sw, int wp) {
+  int c = sw < 32 ? sw : 32;
+  while (c > 1 && wp % c != 0) --c;
+  return c;
+}
+template <int SW, int SH, int WP>
+struct Slices {
+  static constexpr int CW = slice_width(SW, WP);
+  static constexpr int RPS = WP / CW;
+  static constexpr int NM = SH / RPS;
+  static constexpr int REM_A = (SH - NM * RPS) * CW, REM_B = (SW - CW) * SH;
+  static constexpr int NR = (REM_A + REM_B + WP - 1) / WP;
+  static constexpr int N = NM + NR;
+  static_assert(RPS >= 1 && NM >= 1, "slice geometry");
+  // Window pixel (y, x) of remainder slice rho for lane group g; false if
+  // the slice has no pixel for it.  (rho is a constant once the slice loop
+  // is unrolled, so the divisions are by constants.)
+  __device__ static __forceinline__ bool rem(int rho, uint32_t g, uint32_t &y, uint32_t &x) {
+    const uint32_t rs = (uint32_t)(rho * WP) + g;
+    if (rs < (uint32_t)REM_A) {
+      y = (uint32_t)(NM * RPS) + rs / (uint32_t)CW;
+      x = rs % (uint32_t)CW;
+      return true;
+    }
+    if constexpr (SW > CW) {
+      const uint32_t r = rs - (uint32_t)REM_A;
+      y = r / (uint32_t)(SW - CW);
+      x = (uint32_t)CW + r % (uint32_t)(SW - CW);
+      return rs < (uint32_t)(REM_A + REM_B);
+    }
+    y = x = 0;
+    return false;
+  }
+};
+
 }  // namespace
 
 // RC: the centre point is removed (8 points, k -> grid index k + (k >= 4)):
@@ -111,12 +152,13 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
   constexpr uint32_t GX = 4 / EB;
   constexpr int R = (ST == 1 ? kBqHalo : kBqHaloS2) - (DIL - 1), SPAN_W = G::kSpanW, SPAN_H = G::kSpanH;
   static_assert(DIL == 1 || DIL == 2, "dilation 1 or 2");
-  constexpr int SPAN = SPAN_W * SPAN_H;
   constexpr int PIXB = kBqPixB, ROW = G::kRow, LIM_X = SPAN_W - 2, LIM_Y = SPAN_H - 2;
   constexpr int CG = kGroupChannels, K = RC ? 8 : 9;
   constexpr int ROUNDS = RC ? 2 : 3;
   constexpr int WPIX = G::kThreads / 4;                  // window pixels per staging slice
-  constexpr int SLOTS = (SPAN + WPIX - 1) / WPIX;
+  using WS = Slices<SPAN_W, SPAN_H, WPIX>;               // input window: a quad per pixel
+  using FS = Slices<SPAN_W, SPAN_H, G::kThreads / 16>;   // flush: 16 lanes per pixel
+  constexpr int SLOTS = WS::N;
   constexpr uint32_t ZERO = G::kWin;                     // zero block (reads of outside samples)
   constexpr uint32_t GWIN = G::kWin + G::kZero;          // fixed-point grad window
   constexpr uint32_t SINK = GWIN + G::kWin;              // scatter target of samples not in the window
@@ -140,6 +182,12 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
   const __amdgpu_buffer_rsrc_t rgoff = make_rsrc(bp.grad_offset, p.off_bytes);
   const __amdgpu_buffer_rsrc_t rgm = make_rsrc(bp.grad_mask, p.mask_bytes);
   const float s = p.scale;
+  const uint32_t img_bytes = (uint32_t)p.H * row_bytes;
+
+  // This quad's input-window slices (main: row w_row + u RPS, column w_col).
+  const uint32_t w_col = quad % (uint32_t)WS::CW, w_row = quad / (uint32_t)WS::CW;
+  const uint32_t w_lane = w_row * row_bytes + w_col * pix_bytes;
+  const uint32_t w_lds = (w_row * SPAN_W + w_col) * PIXB + sub * 16u;
 
   // Window coordinates of each own slot's kernel point before its offset,
   // packed as three 10-bit fields; slot r holds k = 2 sub + r (r < 2) or 8
@@ -192,37 +240,40 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
   // computes, on every path (a missing item loads nothing: its offsets are
   // out of range), so the compiler's count of outstanding loads stays exact.
   uint32_t win[SLOTS][NWL];
+  // Rows above and below the map fall out of the image's buffer range
+  // (offsets relative to the image, negative ones wrapping past it); one
+  // column check per slice rejects the columns beside it.
   auto issue_window = [&](const Item &I, bool valid) {
-    // The slot geometry is recomputed per item from an opaque copy of the
-    // quad index: hoisted out of the item loop it would not fit the
-    // register budget.
-    uint32_t qd = quad;
-    asm volatile("" : "+v"(qd));
+    const __amdgpu_buffer_rsrc_t rimg =
+        make_rsrc(static_cast<const unsigned char *>(p.input) + I.img, img_bytes);
+    const uint32_t base = (uint32_t)I.Y0 * row_bytes + (uint32_t)I.X0 * pix_bytes + I.chan;  // mod 2^32
+    const uint32_t m_off = valid && (uint32_t)(I.X0 + (int)w_col) < (uint32_t)p.W ? base + w_lane : kOutOfRange;
 #pragma unroll
-    for (int u = 0; u < SLOTS; ++u) {
-      const int idx = (int)qd + u * WPIX;
-      uint32_t offb = kOutOfRange;
-      if (valid && idx < SPAN) {
-        const int sy = idx / SPAN_W, sx = idx - sy * SPAN_W;
-        const int gy_ = I.Y0 + sy, gx_ = I.X0 + sx;
-        if ((uint32_t)gy_ < (uint32_t)p.H && (uint32_t)gx_ < (uint32_t)p.W)
-          offb = I.img + (uint32_t)gy_ * row_bytes + (uint32_t)gx_ * pix_bytes + I.chan;
-      }
-      buffer_load_words<NWL>(rin, offb, win[u]);
+    for (int u = 0; u < WS::NM; ++u)
+      buffer_load_words<NWL>(rimg, m_off + (uint32_t)(u * WS::RPS) * row_bytes, win[u]);
+#pragma unroll
+    for (int rho = 0; rho < WS::NR; ++rho) {
+      uint32_t y, x;
+      const bool live = WS::rem(rho, quad, y, x);
+      const uint32_t off = valid && live && (uint32_t)(I.X0 + (int)x) < (uint32_t)p.W
+                               ? base + y * row_bytes + x * pix_bytes : kOutOfRange;
+      buffer_load_words<NWL>(rimg, off, win[WS::NM + rho]);
     }
   };
+  // (staged as fp32 whatever the I/O dtype)
+  auto store_one = [&](uint32_t at, const uint32_t (&w)[NWL]) {
+    float v[4];
+    unpack<DT, NWL>(w, v);
+    *reinterpret_cast<uint4 *>(lds + at) =
+        make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+  };
   auto store_window = [&]() {
-    uint32_t qd = quad;
-    asm volatile("" : "+v"(qd));
 #pragma unroll
-    for (int u = 0; u < SLOTS; ++u) {
-      const int idx = (int)qd + u * WPIX;
-      if (idx < SPAN) {  // staged as fp32 whatever the I/O dtype
-        float v[4];
-        unpack<DT, NWL>(win[u], v);
-        *reinterpret_cast<uint4 *>(lds + idx * PIXB + sub * 16u) =
-            make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
-      }
+    for (int u = 0; u < WS::NM; ++u) store_one(w_lds + (uint32_t)(u * WS::RPS * ROW), win[u]);
+#pragma unroll
+    for (int rho = 0; rho < WS::NR; ++rho) {
+      uint32_t y, x;
+      if (WS::rem(rho, quad, y, x)) store_one((y * SPAN_W + x) * PIXB + sub * 16u, win[WS::NM + rho]);
     }
   };
   // Raw rows as loaded (decoded where used).  fp32: rw = x, y of k = 2 sub;
@@ -587,36 +638,40 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // every scatter into the grad window is done
     // Add the grad window to grad_input, 16 lanes per window pixel (one
-    // 64-byte request), and clear it for the next item.  Pixels outside the
-    // map and zero sums are skipped.
+    // 64-byte request), and clear it for the next item.  Zero sums are
+    // skipped; rows outside the map fall out of the image's buffer range,
+    // columns beside it are rejected per slice.
     {
-      // Pixel idx = threadIdx.x / 16 + STEP j of the window, its row, column
-      // and grad_input offset walked incrementally.
-      constexpr int STEP = G::kThreads / 16;
-      constexpr int DY = STEP / SPAN_W, DX = STEP % SPAN_W;
-      const uint32_t ch = threadIdx.x & 15u;
-      int idx = (int)(threadIdx.x >> 4);
-      int sy = idx / SPAN_W, sx = idx - sy * SPAN_W;
-      uint32_t dst = cur.img + (uint32_t)(cur.Y0 + sy) * row_bytes + (uint32_t)(cur.X0 + sx) * pix_bytes +
-                     cur.g * (uint32_t)(CG * EB) + ch * (uint32_t)EB;
-      const uint32_t slot0 = lbase + GWIN + (ch >> 1) * 8u;
+      const uint32_t ch = threadIdx.x & 15u, fg = threadIdx.x >> 4;  // channel, lane group
+      const __amdgpu_buffer_rsrc_t rgimg =
+          make_rsrc(static_cast<unsigned char *>(bp.grad_in) + (size_t)cur.img * GX, img_bytes * GX);
+      // grad_input offset (in input bytes, relative to the image, mod 2^32)
+      // of window pixel (0, 0), channel ch of the group
+      const uint32_t base = (uint32_t)cur.Y0 * row_bytes + (uint32_t)cur.X0 * pix_bytes +
+                            cur.g * (uint32_t)(CG * EB) + ch * (uint32_t)EB;
+      const uint32_t pair = GWIN + (ch >> 1) * 8u;
       typedef __attribute__((address_space(3))) uint64_t L;
-#pragma unroll 2
-      for (; idx < SPAN; idx += STEP) {
-        const bool ok = (uint32_t)(cur.Y0 + sy) < (uint32_t)p.H && (uint32_t)(cur.X0 + sx) < (uint32_t)p.W;
-        L *slot = (L *)(size_t)(slot0 + (uint32_t)idx * PIXB);
+      auto flush_one = [&](uint32_t lds_at, uint32_t dst, bool ok) {
+        L *slot = (L *)(size_t)(lbase + lds_at);
         const int2 pr = pair_sums(*slot);
-        if ((ch & 1u) == 0) *slot = 0;  // after both lanes of the pair have read it (same instruction)
+        *slot = 0;  // both lanes of the pair, after both have read it (the read is the earlier instruction)
         const int q = (ch & 1u) ? pr.y : pr.x;
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32((float)q * invS, rgx, (int)((ok && q != 0) ? dst * GX : kOutOfRange), 0, 0);
-        sx += DX;
-        sy += DY;
-        dst += (uint32_t)DY * row_bytes + (uint32_t)DX * pix_bytes;
-        if (sx >= SPAN_W) {
-          sx -= SPAN_W;
-          sy += 1;
-          dst += row_bytes - (uint32_t)SPAN_W * pix_bytes;
-        }
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32((float)q * invS, rgimg,
+                                                        (int)((ok && q != 0) ? dst * GX : kOutOfRange), 0, 0);
+      };
+      const uint32_t f_col = fg % (uint32_t)FS::CW, f_row = fg / (uint32_t)FS::CW;
+      const bool f_ok = (uint32_t)(cur.X0 + (int)f_col) < (uint32_t)p.W;
+      const uint32_t f_dst = base + f_row * row_bytes + f_col * pix_bytes;
+      const uint32_t f_lds = pair + (f_row * SPAN_W + f_col) * PIXB;
+#pragma unroll 4
+      for (int u = 0; u < FS::NM; ++u)
+        flush_one(f_lds + (uint32_t)(u * FS::RPS * ROW), f_dst + (uint32_t)(u * FS::RPS) * row_bytes, f_ok);
+#pragma unroll
+      for (int rho = 0; rho < FS::NR; ++rho) {
+        uint32_t y, x;
+        if (FS::rem(rho, fg, y, x))
+          flush_one(pair + (y * SPAN_W + x) * PIXB, base + y * row_bytes + x * pix_bytes,
+                    (uint32_t)(cur.X0 + (int)x) < (uint32_t)p.W);
       }
     }
 
@@ -690,6 +745,12 @@ hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipS
   TileGeom tg{};
   tg.span_w = s2 ? BqGeom<16, 8, 2>::kSpanW : tw + 2 * kBqHalo + 3;
   tg.span_h = s2 ? BqGeom<16, 8, 2>::kSpanH : th + 2 * kBqHalo + 3;
+  // Window rows outside the map are rejected by the buffer range of their
+  // image (input, and grad_input at GX bytes per input byte), which needs
+  // every window row's offset relative to the image to fit int32.
+  const int64_t row_bytes = (int64_t)p.W * p.C * (dtype == DCN_F32 ? 4 : 2);
+  const int64_t gx = dtype == DCN_F32 ? 1 : 2;
+  if (((int64_t)p.H + p.PH + tg.span_h + 1) * row_bytes * gx >= (int64_t(1) << 31)) return hipErrorNotSupported;
   const int tiles_y = (p.Ho + th - 1) / th;
   tg.tiles_x = (p.Wo + tw - 1) / tw;
   tg.tiles_per_img = tiles_y * tg.tiles_x;
