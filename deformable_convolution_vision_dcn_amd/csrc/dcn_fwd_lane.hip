@@ -31,6 +31,7 @@
 // chunks; the remaining conflicts are the random coincidences of the
 // sampled pixels' bank quarters.
 #include <algorithm>
+#include <type_traits>
 
 #include "dcn_device.hpp"
 
@@ -41,11 +42,11 @@ namespace dcn {
 #endif
 
 constexpr int kLaneHalo = DCN_LANE_HALO;      // window halo for the offsets
-// LDS bytes of a TW x TH tile's window (and its zero block) at pixb bytes
-// per staged window pixel.
-template <int TW, int TH>
+// LDS bytes of a TW x TH tile's window for KS x KS points (and its zero
+// block) at pixb bytes per staged window pixel.
+template <int TW, int TH, int KS = 3>
 constexpr int lane_lds_bytes(int pixb) {
-  return ((TW + 2 * kLaneHalo + 3) * (TH + 2 * kLaneHalo + 3) + (TW + 2 * kLaneHalo + 3) + 2) * pixb;
+  return ((TW + 2 * kLaneHalo + KS) * (TH + 2 * kLaneHalo + KS) + (TW + 2 * kLaneHalo + KS) + 2) * pixb;
 }
 
 // Bytes of one pixel-group (16 channels) in the I/O dtype.
@@ -62,24 +63,130 @@ __device__ __forceinline__ void lds_read16(const unsigned char *src, uint32_t (&
   w[3] = v.w;
 }
 
+// Words [0, N) of w from N consecutive words at byte offset `off` (4-byte
+// aligned), in loads of at most 16 bytes.
+template <int N, int M>
+__device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[M]) {
+  static_assert(N <= M, "run length");
+#pragma unroll
+  for (int q = 0; q + 4 <= N; q += 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 4 * q), 0, 0);
+    w[q] = v[0];
+    w[q + 1] = v[1];
+    w[q + 2] = v[2];
+    w[q + 3] = v[3];
+  }
+  constexpr int B = N & ~3;
+  if constexpr (N - B >= 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(off + 4 * B), 0, 0);
+    w[B] = v[0];
+    w[B + 1] = v[1];
+  }
+  if constexpr (N - B == 1 || N - B == 3)
+    w[N - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 4 * (N - 1)), 0, 0);
+}
+
+// Offset and mask rows of one pixel-group for any number K of points, as
+// raw words: fp32 2K offset words and K mask words; 16-bit K offset words
+// (x, y per word) and the mask row's words from the 4-byte boundary at or
+// below its start.  With K odd, 16-bit mask rows alternate between starting
+// on a word and two bytes into one: a row that starts on a word takes its
+// last value by a 2-byte load, so no load reaches past the row.
+template <int DT, int K>
+struct PointRows {
+  static constexpr bool kF32 = DT == DCN_F32;
+  static constexpr int kOff = kF32 ? 2 * K : K;
+  static constexpr int kMask = kF32 ? K : (K % 2 == 0 ? K / 2 : (2 * K + 2) / 4);
+  uint32_t o[kOff], m[kMask];
+};
+
+// The row words of a KS x KS problem: RowWords for 3x3 (nine or eight
+// points), PointRows otherwise.
+template <int DT, int K, int KS>
+struct RowsOf {
+  using type = PointRows<DT, K>;
+};
+template <int DT, int K>
+struct RowsOf<DT, K, 3> {
+  using type = RowWords<DT, K>;
+};
+
+template <int DT, int K, int KS>
+__device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t roff, __amdgpu_buffer_rsrc_t rmask, uint32_t pg,
+                                          typename RowsOf<DT, K, KS>::type &r) {
+  if constexpr (KS == 3) {
+    load_row_words<DT, K>(roff, rmask, pg, r);
+  } else {
+    using R = PointRows<DT, K>;
+    load_run<R::kOff>(roff, pg * (uint32_t)(4 * R::kOff), r.o);
+    if constexpr (R::kF32 || K % 2 == 0) {
+      load_run<R::kMask>(rmask, pg * (uint32_t)(4 * R::kMask), r.m);
+    } else {
+      const uint32_t mb = pg * (uint32_t)(2 * K), a = mb & ~3u;
+      const bool odd = (mb & 2u) != 0;
+      load_run<R::kMask - 1>(rmask, a, r.m);
+      const uint32_t last = a + 4u * (R::kMask - 1);
+      const uint32_t wa = __builtin_amdgcn_raw_buffer_load_b32(rmask, odd ? (int)last : (int)kOutOfRange, 0, 0);
+      const uint32_t wb = __builtin_amdgcn_raw_buffer_load_b16(rmask, odd ? (int)kOutOfRange : (int)last, 0, 0);
+      r.m[R::kMask - 1] = wa | wb;
+    }
+  }
+}
+
+template <int DT, int K, int KS>
+__device__ __forceinline__ void decode_mask(uint32_t pg, const typename RowsOf<DT, K, KS>::type &r,
+                                            float (&msk)[K]) {
+  if constexpr (KS == 3) {
+    decode_mask_words<DT, K>(pg, r, msk);
+  } else {
+    using R = PointRows<DT, K>;
+    if constexpr (R::kF32) {
+#pragma unroll
+      for (int q = 0; q < K; ++q) msk[q] = __uint_as_float(r.m[q]);
+    } else {
+      const uint32_t sh = (K % 2 != 0 && ((pg * (uint32_t)(2 * K)) & 2u)) ? 16u : 0u;  // row starts at a half word
+      uint32_t w[R::kMask];
+#pragma unroll
+      for (int q = 0; q + 1 < R::kMask; ++q) w[q] = __builtin_amdgcn_alignbit(r.m[q + 1], r.m[q], sh);
+      w[R::kMask - 1] = r.m[R::kMask - 1] >> sh;
+#pragma unroll
+      for (int q = 0; q < K; ++q) msk[q] = (q & 1) ? Io<DT>::hi(w[q / 2]) : Io<DT>::lo(w[q / 2]);
+    }
+  }
+}
+
+template <int DT, int K, int KS>
+__device__ __forceinline__ void offset_xy(const typename RowsOf<DT, K, KS>::type &r, int k, float &x, float &y) {
+  if constexpr (KS == 3) {
+    offset_words_xy<DT, K>(r, k, x, y);
+  } else if constexpr (DT == DCN_F32) {
+    x = __uint_as_float(r.o[2 * k]);
+    y = __uint_as_float(r.o[2 * k + 1]);
+  } else {
+    x = Io<DT>::lo(r.o[k]);
+    y = Io<DT>::hi(r.o[k]);
+  }
+}
+
 }  // namespace
 
-// RC: the centre point is removed (8 points; point k sits at grid index
-// k + (k >= 4)).  TW x TH: the output tile.  GP: groups per work item (1, 2
+// KS: the kernel's side (3 or 5).  RC: the centre point is removed (K =
+// KS^2 - 1 points; point k sits at grid index k + (k >= KS^2 / 2)).  TW x
+// TH: the output tile.  GP: groups per work item (1, 2
 // or 4), one lane per (pixel, group), the GP lanes of a pixel adjacent.
 // A staged window pixel holds the item's GP neighbouring group slices, which
 // are contiguous in memory: with four 16-bit groups it is one whole 128-byte
 // line, so the window costs a quarter of the line requests of one group per
 // item, and the GP lanes of a pixel read one contiguous stretch of the
 // offset and mask rows.
-template <int DT, bool SOFTMAX, bool RC, int TW, int TH, int GP>
+template <int DT, bool SOFTMAX, bool RC, int TW, int TH, int GP, int KS>
 #ifndef DCN_LANE_WAVES
 #define DCN_LANE_WAVES 2  // waves per SIMD the register budget must allow
 #endif
 __global__ void __launch_bounds__(TW * TH * GP, DCN_LANE_WAVES) dcn_fwd_lane_kernel(FwdParams p, TileGeom tg) {
   using io = Io<DT>;
   constexpr int THREADS = TW * TH * GP, R = kLaneHalo;
-  constexpr int SPAN_W = TW + 2 * R + 3, SPAN_H = TH + 2 * R + 3;
+  constexpr int SPAN_W = TW + 2 * R + KS, SPAN_H = TH + 2 * R + KS;
   constexpr int GS = lane_slice_bytes<DT>();       // one pixel-group slice
   constexpr int PIXB = GS * GP;                    // one staged window pixel
   constexpr int CHUNK = 16;                        // bytes per ds_read_b128
@@ -91,7 +198,14 @@ __global__ void __launch_bounds__(TW * TH * GP, DCN_LANE_WAVES) dcn_fwd_lane_ker
   constexpr int WPIX = THREADS / LPP;              // window pixels per staging slice
   constexpr int LIM_X = SPAN_W - 2, LIM_Y = SPAN_H - 2;
   constexpr int ZERO = SPAN * PIXB;
-  constexpr int K = RC ? 8 : 9;
+  constexpr int K = KS * KS - (RC ? 1 : 0);
+  constexpr int KC = KS * KS / 2;                  // the centre's grid index
+  // 3x3 rows as RowWords (nine or eight points), others as PointRows.  The
+  // next item's rows are requested before this item's compute, except for
+  // 5x5 fp32 rows (75 words), which would not fit twice beside the window
+  // prefetch: those are requested after it.
+  using Rows = typename RowsOf<DT, K, KS>::type;
+  constexpr bool EARLY_ROWS = KS == 3 || DT != DCN_F32;
   constexpr int BANK_PIX = 256 / PIXB;             // window pixels per 256-byte bank row
   static_assert(GP == 1 || GP == 2 || GP == 4, "one, two or four groups per item");
   static_assert(PIXB <= 128 && (PIXB & (PIXB - 1)) == 0 && THREADS % LPP == 0, "a window pixel is at most one line");
@@ -212,7 +326,7 @@ __global__ void __launch_bounds__(TW * TH * GP, DCN_LANE_WAVES) dcn_fwd_lane_ker
   // return: decoded after the next window is in LDS, so the loads overlap a
   // whole item of compute.  Issued on every path (a dead lane reads row 0),
   // so the compiler's wait counting stays exact.
-  RowWords<DT, K> rw;
+  Rows rw;
 
   // Per-lane chunk order (bank spreading): the pixels that share a bank row
   // at unit offsets start on different chunks.
@@ -226,7 +340,7 @@ __global__ void __launch_bounds__(TW * TH * GP, DCN_LANE_WAVES) dcn_fwd_lane_ker
   Item cur = decode(item < end ? item : 0);
   if (item < end) {
     issue_window(cur);
-    load_row_words<DT, K>(roff, rmask, cur.rpg, rw);
+    load_rows<DT, K, KS>(roff, rmask, cur.rpg, rw);
   }
 
   while (item < end) {
@@ -235,7 +349,7 @@ __global__ void __launch_bounds__(TW * TH * GP, DCN_LANE_WAVES) dcn_fwd_lane_ker
     __syncthreads();  // the window is in LDS
 
     // This item's rows (the offsets are decoded point by point).
-    const RowWords<DT, K> cw = rw;
+    const Rows cw = rw;
 
     // The next item's window and rows land in registers during this item's
     // compute.  (Issued on the last item too, re-reading its own data, so
@@ -244,11 +358,11 @@ __global__ void __launch_bounds__(TW * TH * GP, DCN_LANE_WAVES) dcn_fwd_lane_ker
     const bool more = next < end;  // block-uniform
     const Item nx = decode(more ? next : item);
     issue_window(nx);
-    load_row_words<DT, K>(roff, rmask, nx.rpg, rw);
+    if constexpr (EARLY_ROWS) load_rows<DT, K, KS>(roff, rmask, nx.rpg, rw);
 
     // modulation scalars
     float msk[K], m[K];
-    decode_mask_words<DT, K>(cur.rpg, cw, msk);
+    decode_mask<DT, K, KS>(cur.rpg, cw, msk);
     if constexpr (SOFTMAX) {
       float mx = msk[0];
 #pragma unroll
@@ -283,12 +397,12 @@ __global__ void __launch_bounds__(TW * TH * GP, DCN_LANE_WAVES) dcn_fwd_lane_ker
       // waves furthest behind issue first and the block reaches its next
       // barrier with less spread.
       if (k == 0) __builtin_amdgcn_s_setprio(3);
-      if (k == 3) __builtin_amdgcn_s_setprio(2);
-      if (k == 6) __builtin_amdgcn_s_setprio(1);
-      const int q = RC ? k + (k >= 4) : k;  // grid index
-      const int i = q / 3, j = q % 3;
+      if (k == (KS == 3 ? 3 : K / 3)) __builtin_amdgcn_s_setprio(2);
+      if (k == (KS == 3 ? 6 : 2 * K / 3)) __builtin_amdgcn_s_setprio(1);
+      const int q = RC ? k + (k >= KC) : k;  // grid index
+      const int i = q / KS, j = q % KS;
       float ox_k, oy_k;
-      offset_words_xy<DT, K>(cw, k, ox_k, oy_k);
+      offset_xy<DT, K, KS>(cw, k, ox_k, oy_k);
       const float dx = s * ox_k, dy = s * oy_k;
       const bool nan_loc = (dx != dx) | (dy != dy);
       const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
@@ -371,6 +485,7 @@ __global__ void __launch_bounds__(TW * TH * GP, DCN_LANE_WAVES) dcn_fwd_lane_ker
       buffer_store_words<4>(rout, obase + (uint32_t)rot[t], w);
     }
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (!EARLY_ROWS) load_rows<DT, K, KS>(roff, rmask, nx.rpg, rw);
 
     item = next;
     cur = nx;
@@ -386,11 +501,11 @@ namespace {
 #define DCN_LANE_TH4 8  // height of the 16-wide tiles with four groups per item
 #endif
 
-template <int DT, bool SM, bool RC, int TW, int TH, int GP>
+template <int DT, bool SM, bool RC, int TW, int TH, int GP, int KS>
 hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
-  auto kern = dcn_fwd_lane_kernel<DT, SM, RC, TW, TH, GP>;
+  auto kern = dcn_fwd_lane_kernel<DT, SM, RC, TW, TH, GP, KS>;
   constexpr int THREADS = TW * TH * GP;
-  const size_t lds = lane_lds_bytes<TW, TH>(lane_slice_bytes<DT>() * GP);
+  const size_t lds = lane_lds_bytes<TW, TH, KS>(lane_slice_bytes<DT>() * GP);
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -413,7 +528,7 @@ hipError_t launch_lane(const FwdParams &p, const TileGeom &tg, hipStream_t s) {
 
 // Tile shape of each kind of work item: 16 x 16, or 16 x 8 with four
 // groups (a 1024-thread block would have half the registers per lane), or
-// 24 x 8 (16-bit).
+// 24 x 8 (16-bit, 3x3 points).
 struct LaneShape {
   int tw, th;
 };
@@ -423,27 +538,31 @@ LaneShape lane_shape(bool wide, int gp) {
   return gp == 4 ? LaneShape{16, DCN_LANE_TH4} : LaneShape{16, 16};
 }
 
-template <int DT, bool SM, bool RC>
+template <int DT, bool SM, bool RC, int KS>
 hipError_t launch_lane_shape(bool wide, int gp, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   if constexpr (DT == DCN_F32) {  // one group per item, 16x16 tiles (the 24x8 window would need 19 slots per lane)
     if (wide || gp != 1) return hipErrorNotSupported;
-    return launch_lane<DT, SM, RC, 16, 16, 1>(p, tg, s);
+    return launch_lane<DT, SM, RC, 16, 16, 1, KS>(p, tg, s);
+  } else if constexpr (KS == 5) {  // 16-wide tiles only
+    if (wide) return hipErrorNotSupported;
+    if (gp == 4) return launch_lane<DT, SM, RC, 16, DCN_LANE_TH4, 4, KS>(p, tg, s);
+    return launch_lane<DT, SM, RC, 16, 16, 1, KS>(p, tg, s);
   } else {
     if (gp == 4)
-      return wide ? launch_lane<DT, SM, RC, 24, 8, 4>(p, tg, s) : launch_lane<DT, SM, RC, 16, DCN_LANE_TH4, 4>(p, tg, s);
+      return wide ? launch_lane<DT, SM, RC, 24, 8, 4, KS>(p, tg, s) : launch_lane<DT, SM, RC, 16, DCN_LANE_TH4, 4, KS>(p, tg, s);
     if (gp == 2)
-      return wide ? launch_lane<DT, SM, RC, 24, 8, 2>(p, tg, s) : launch_lane<DT, SM, RC, 16, 16, 2>(p, tg, s);
-    return wide ? launch_lane<DT, SM, RC, 24, 8, 1>(p, tg, s) : launch_lane<DT, SM, RC, 16, 16, 1>(p, tg, s);
+      return wide ? launch_lane<DT, SM, RC, 24, 8, 2, KS>(p, tg, s) : launch_lane<DT, SM, RC, 16, 16, 2, KS>(p, tg, s);
+    return wide ? launch_lane<DT, SM, RC, 24, 8, 1, KS>(p, tg, s) : launch_lane<DT, SM, RC, 16, 16, 1, KS>(p, tg, s);
   }
 }
 
-template <int DT>
+template <int DT, int KS>
 hipError_t launch_lane_dt(bool wide, int gp, int softmax, const FwdParams &p, const TileGeom &tg, hipStream_t s) {
   if (p.RC)
-    return softmax ? launch_lane_shape<DT, true, true>(wide, gp, p, tg, s)
-                   : launch_lane_shape<DT, false, true>(wide, gp, p, tg, s);
-  return softmax ? launch_lane_shape<DT, true, false>(wide, gp, p, tg, s)
-                 : launch_lane_shape<DT, false, false>(wide, gp, p, tg, s);
+    return softmax ? launch_lane_shape<DT, true, true, KS>(wide, gp, p, tg, s)
+                   : launch_lane_shape<DT, false, true, KS>(wide, gp, p, tg, s);
+  return softmax ? launch_lane_shape<DT, true, false, KS>(wide, gp, p, tg, s)
+                 : launch_lane_shape<DT, false, false, KS>(wide, gp, p, tg, s);
 }
 
 // Share of the tiles' lanes that hold an output pixel.
@@ -454,28 +573,36 @@ double lane_use(const FwdParams &p, int tw, int th) {
 
 }  // namespace
 
-// Stride 1, dilation 1, 3x3 points only; hipErrorNotSupported otherwise.
+// 3x3 or 5x5 points, stride 1, dilation 1; hipErrorNotSupported otherwise.
 // 16-bit I/O takes four groups per work item where the group count allows
-// (two, else one), fp32 one.
+// (3x3: two, else one; 5x5: see below), fp32 one.
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s) {
-  if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
+  if (p.KH != p.KW || (p.KH != 3 && p.KH != 5) || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1)
     return hipErrorNotSupported;
   if (dtype != DCN_F32 && dtype != DCN_F16 && dtype != DCN_BF16) return hipErrorInvalidValue;
+  const int ks = p.KH;
   int gp = 1;
   if (dtype != DCN_F32) {
     if (p.G % 4 == 0 && DCN_LANE_GP_MAX >= 4) gp = 4;
     else if (p.G % 2 == 0 && DCN_LANE_GP_MAX >= 2) gp = 2;
   }
+  // 5x5 (16-bit): one group per item on 16x16 tiles (a third more blocks
+  // per CU than four groups on 16x8 tiles: 0.46 against 0.54 ms at stage-2
+  // size), unless those tiles leave clearly more lanes idle (the 24x24
+  // stage: 56 % full against 75 %; 0.53 against 0.43 ms)
+  if (ks == 5 && gp != 1)
+    gp = (p.G % 4 == 0 && DCN_LANE_GP_MAX >= 4 && lane_use(p, 16, DCN_LANE_TH4) > lane_use(p, 16, 16) + 0.1) ? 4 : 1;
   const LaneShape sq = lane_shape(false, gp), sw = lane_shape(true, gp);
-  // 24x8 tiles where they leave clearly fewer lanes idle; with four groups
-  // also where they leave as few (768 threads, twelve waves, against 512 on
-  // 16x8 tiles, and fewer halo pixels per output pixel: 4.7 against 5.6)
+  // 24x8 tiles (16-bit, 3x3) where they leave clearly fewer lanes idle; with
+  // four groups also where they leave as few (768 threads, twelve waves,
+  // against 512 on 16x8 tiles, and fewer halo pixels per output pixel: 4.7
+  // against 5.6)
   const double use_w = lane_use(p, sw.tw, sw.th), use_q = lane_use(p, sq.tw, sq.th);
-  const bool wide = dtype != DCN_F32 && (use_w > use_q + 0.1 || (gp == 4 && use_w >= use_q));
+  const bool wide = dtype != DCN_F32 && ks == 3 && (use_w > use_q + 0.1 || (gp == 4 && use_w >= use_q));
   const LaneShape sh = wide ? sw : sq;
   TileGeom tg{};
-  tg.span_w = sh.tw + 2 * kLaneHalo + 3;
-  tg.span_h = sh.th + 2 * kLaneHalo + 3;
+  tg.span_w = sh.tw + 2 * kLaneHalo + ks;
+  tg.span_h = sh.th + 2 * kLaneHalo + ks;
   // The window rows above and below the map are rejected by the buffer range
   // of their image, which needs the byte offset of every window row relative
   // to the image to fit int32.
@@ -492,10 +619,17 @@ hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipSt
   tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
+  if (ks == 5) {
+    switch (dtype) {
+      case DCN_F32: return launch_lane_dt<DCN_F32, 5>(wide, gp, softmax, p, tg, s);
+      case DCN_F16: return launch_lane_dt<DCN_F16, 5>(wide, gp, softmax, p, tg, s);
+      default: return launch_lane_dt<DCN_BF16, 5>(wide, gp, softmax, p, tg, s);
+    }
+  }
   switch (dtype) {
-    case DCN_F32: return launch_lane_dt<DCN_F32>(wide, gp, softmax, p, tg, s);
-    case DCN_F16: return launch_lane_dt<DCN_F16>(wide, gp, softmax, p, tg, s);
-    default: return launch_lane_dt<DCN_BF16>(wide, gp, softmax, p, tg, s);
+    case DCN_F32: return launch_lane_dt<DCN_F32, 3>(wide, gp, softmax, p, tg, s);
+    case DCN_F16: return launch_lane_dt<DCN_F16, 3>(wide, gp, softmax, p, tg, s);
+    default: return launch_lane_dt<DCN_BF16, 3>(wide, gp, softmax, p, tg, s);
   }
 }
 

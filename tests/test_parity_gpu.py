@@ -114,6 +114,12 @@ PATH_CASES = [
     Workload("path_quads_v4_24wide", n=2, h=33, w=24, c=64, groups=4, softmax=False,
              mask_dist=normal(0.5), offset_dist=uniform(4.0), seed=48),
     Workload("path_groups20", n=1, h=20, w=18, c=320, groups=20, seed=49),
+    # 5x5 points (the lane kernel's 33-pixel-wide windows): four groups, and
+    # three with offsets that leave the windows
+    Workload("path_k5", n=2, h=37, w=29, c=64, groups=4, kernel=(5, 5), pad=(2, 2), offset_dist=normal(2.0),
+             seed=50),
+    Workload("path_k5_v4_far", n=1, h=21, w=35, c=48, groups=3, kernel=(5, 5), pad=(2, 2), softmax=False,
+             mask_dist=normal(0.5), offset_dist=uniform(8.0), seed=53),
 ]
 
 
@@ -146,6 +152,24 @@ def test_forward_remove_center_every_path(dtype, groups, monkeypatch):
             monkeypatch.setenv("DCN_MI355X_FWD_PATH", path)
         print(f"forward rc_paths {dtype} path={path}", flush=True)
         gate(_np(run_forward(wl, t)), ref, dtype, f"rc_paths/{dtype}/{path}")
+
+
+@pytest.mark.parametrize("groups", [2, 4])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_forward_5x5_remove_center_every_path(dtype, groups, monkeypatch):
+    """5x5 points without the centre (24 points, even-length 16-bit mask
+    rows) through every forced kernel choice."""
+    wl = Workload("rc_k5_paths", n=2, h=24, w=33, c=16 * groups, groups=groups, kernel=(5, 5), pad=(2, 2),
+                  offset_dist=normal(2.0), remove_center=True, dtype=dtype, seed=57)
+    t = synth.make_inputs(wl)
+    ref = oracle_full(wl, t)
+    for path in ["auto", "generic", "lane"]:
+        if path == "auto":
+            monkeypatch.delenv("DCN_MI355X_FWD_PATH", raising=False)
+        else:
+            monkeypatch.setenv("DCN_MI355X_FWD_PATH", path)
+        print(f"forward rc_k5_paths {dtype} G={groups} path={path}", flush=True)
+        gate(_np(run_forward(wl, t)), ref, dtype, f"rc_k5_paths/{dtype}/{path}")
 
 
 # Whole-map kernel: one group per item at the 24x24 stage-3 map (every lane
