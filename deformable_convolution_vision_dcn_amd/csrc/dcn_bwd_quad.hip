@@ -50,21 +50,27 @@ constexpr int kBqPixB = 64;                               // 16 fp32 channels
 // Halo at stride 2 (dilation 1; one less at dilation 2, so the window keeps
 // its size).
 constexpr int kBqHaloS2 = 4;
+// Halo of 5x5 points (stride and dilation 1): a 16x16 tile's window is then
+// 33 pixels on a side, as with 3x3 points and halo 7.
+constexpr int kBqHalo5 = 6;
 
 // Block geometry for TW x TH output tiles (a quad per pixel) at stride ST:
 // 16x16 (1024 threads), 24x8 (768 threads) for maps 24 pixels wide or 12x12
 // (576 threads) for 12x12 maps, both of which 16x16 tiles would leave 44 %
 // empty; at stride 2, 16x8 tiles (512 threads) whose 42 x 26 windows (the
-// footprint plus a halo of 4) fit beside their grad windows.
-template <int TW, int TH, int ST = 1>
+// footprint plus a halo of 4) fit beside their grad windows; with 5x5 points,
+// 16x16 or 16x8 tiles with a halo of 6 (33 x 33 or 33 x 25 windows).
+template <int TW, int TH, int ST = 1, int KS = 3>
 struct BqGeom {
   static_assert(ST == 1 || ST == 2, "stride 1 or 2");
+  static_assert(KS == 3 || (KS == 5 && ST == 1), "3x3 points, or 5x5 at stride 1");
+  static constexpr int kHalo1 = KS == 5 ? kBqHalo5 : kBqHalo;  // stride 1, dilation 1
   static constexpr int kThreads = 4 * TW * TH;
   static constexpr int kWaves = kThreads / 64;
   // window edges, pixels: (T - 1) * ST + 2 * DIL + 2 * R + 2 with the halo R
   // one smaller at dilation 2, so independent of the dilation
-  static constexpr int kSpanW = ST == 1 ? TW + 2 * kBqHalo + 3 : 2 * TW + 2 * kBqHaloS2 + 2;
-  static constexpr int kSpanH = ST == 1 ? TH + 2 * kBqHalo + 3 : 2 * TH + 2 * kBqHaloS2 + 2;
+  static constexpr int kSpanW = ST == 1 ? TW + 2 * kHalo1 + KS : 2 * TW + 2 * kBqHaloS2 + 2;
+  static constexpr int kSpanH = ST == 1 ? TH + 2 * kHalo1 + KS : 2 * TH + 2 * kBqHaloS2 + 2;
   static constexpr int kRow = kSpanW * kBqPixB;           // LDS bytes per window row
   static constexpr int kWin = kSpanW * kSpanH * kBqPixB;  // one window
   static constexpr int kZero = kRow + 2 * kBqPixB;        // zero block after the input window
@@ -138,9 +144,9 @@ struct Slices {
 // item takes two rounds instead of three.
 // DIL: the dilation (1 or 2, both axes).  The window keeps its size: the
 // halo shrinks by one pixel per side at dilation 2.
-template <int DT, bool SOFTMAX, bool RC, int DIL, int TW, int TH, int ST>
+template <int DT, bool SOFTMAX, bool RC, int DIL, int TW, int TH, int ST, int KS>
 __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kernel(BwdParams bp, TileGeom tg) {
-  using G = BqGeom<TW, TH, ST>;
+  using G = BqGeom<TW, TH, ST, KS>;
   const FwdParams &p = bp.f;
   using io = Io<DT>;
   constexpr int EB = io::kBytes;         // bytes per element in memory
@@ -150,11 +156,15 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
   // a caller's fp32 workspace of the input's shape): an input byte address
   // times GX is the same element's address there.
   constexpr uint32_t GX = 4 / EB;
-  constexpr int R = (ST == 1 ? kBqHalo : kBqHaloS2) - (DIL - 1), SPAN_W = G::kSpanW, SPAN_H = G::kSpanH;
+  constexpr int R = (ST == 1 ? G::kHalo1 : kBqHaloS2) - (DIL - 1), SPAN_W = G::kSpanW, SPAN_H = G::kSpanH;
   static_assert(DIL == 1 || DIL == 2, "dilation 1 or 2");
   constexpr int PIXB = kBqPixB, ROW = G::kRow, LIM_X = SPAN_W - 2, LIM_Y = SPAN_H - 2;
-  constexpr int CG = kGroupChannels, K = RC ? 8 : 9;
-  constexpr int ROUNDS = RC ? 2 : 3;
+  constexpr int CG = kGroupChannels, K = KS * KS - (RC ? 1 : 0);
+  // Points per lane.  3x3: lane sub owns k = 2 sub, 2 sub + 1 and (lane 0)
+  // k = 8; 5x5: lane sub owns k = P sub + r, r < P, where below K.
+  constexpr int P = KS == 3 ? 3 : (K + 3) / 4;
+  constexpr int ROUNDS = KS == 3 ? (RC ? 2 : 3) : P;
+  static_assert(KS == 3 || (DIL == 1 && ST == 1), "5x5 points at stride and dilation 1");
   constexpr int WPIX = G::kThreads / 4;                  // window pixels per staging slice
   using WS = Slices<SPAN_W, SPAN_H, WPIX>;               // input window: a quad per pixel
   using FS = Slices<SPAN_W, SPAN_H, G::kThreads / 16>;   // flush: 16 lanes per pixel
@@ -193,12 +203,14 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
   // packed as three 10-bit fields; slot r holds k = 2 sub + r (r < 2) or 8
   // (no point with RC), at grid index q.
   uint32_t bxp = 0, byp = 0;
+  if constexpr (KS == 3) {
 #pragma unroll
-  for (int r = 0; r < 3; ++r) {
-    const int k = r < 2 ? 2 * (int)sub + r : 8;
-    const int q = RC ? (r < 2 ? k + (k >= 4) : 4) : k;
-    bxp |= (uint32_t)(ox * ST + R + (q % 3) * DIL) << (10 * r);
-    byp |= (uint32_t)(oy * ST + R + (q / 3) * DIL) << (10 * r);
+    for (int r = 0; r < 3; ++r) {
+      const int k = r < 2 ? 2 * (int)sub + r : 8;
+      const int q = RC ? (r < 2 ? k + (k >= 4) : 4) : k;
+      bxp |= (uint32_t)(ox * ST + R + (q % 3) * DIL) << (10 * r);
+      byp |= (uint32_t)(oy * ST + R + (q / 3) * DIL) << (10 * r);
+    }
   }
   const uint32_t win_chunk = lbase + sub * 16u;          // this lane's 4 channels of a window pixel
   const uint32_t gwin_chunk = lbase + GWIN + sub * 16u;
@@ -280,9 +292,31 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
   // x, y of 2 sub + 1; x, y of 8; rl = logits of 2 sub, 2 sub + 1, 8; rg =
   // grad_output of the lane's 4 channels.  16-bit: rw = (x, y) words of
   // 2 sub, 2 sub + 1, 8; rl = the three logits (low halves); rg = two words.
-  constexpr int NRW = DT == DCN_F32 ? 6 : 3;
-  uint32_t rw[NRW], rl[3], rg[NWL];
+  constexpr int NRW = DT == DCN_F32 ? 2 * P : P;
+  uint32_t rw[NRW], rl[P], rg[NWL];
   auto issue_rows = [&](const Item &I) {
+    if constexpr (KS == 5) {  // one point at a time: the lane's P points, k = P sub + r (none past K)
+#pragma unroll
+      for (int r = 0; r < P; ++r) {
+        const bool has = P * (int)sub + r < K;
+        const uint32_t k = (uint32_t)(P * (int)sub + r);
+        if constexpr (DT == DCN_F32) {
+          const auto o = __builtin_amdgcn_raw_buffer_load_b64(
+              roff, has ? (int)(I.pg * (uint32_t)(K * 8) + 8u * k) : (int)kOutOfRange, 0, 0);
+          rw[2 * r] = o[0];
+          rw[2 * r + 1] = o[1];
+          rl[r] = __builtin_amdgcn_raw_buffer_load_b32(
+              rmask, has ? (int)(I.pg * (uint32_t)(K * 4) + 4u * k) : (int)kOutOfRange, 0, 0);
+        } else {
+          rw[r] = __builtin_amdgcn_raw_buffer_load_b32(
+              roff, has ? (int)(I.pg * (uint32_t)(K * 4) + 4u * k) : (int)kOutOfRange, 0, 0);
+          rl[r] = __builtin_amdgcn_raw_buffer_load_b16(
+              rmask, has ? (int)(I.pg * (uint32_t)(K * 2) + 2u * k) : (int)kOutOfRange, 0, 0);
+        }
+      }
+      buffer_load_words<NWL>(rgy, I.pg * (uint32_t)(CG * EB) + sub * (uint32_t)LB, rg);
+      return;
+    }
     if constexpr (DT == DCN_F32) {
       const uint32_t orow = I.pg * (K * 8), mrow = I.pg * (K * 4);
       const auto o = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(orow + 16 * sub), 0, 0);
@@ -335,35 +369,44 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
     __syncthreads();  // the previous item's reads, scatters and flush are done
     store_window();
 
-    // Own slots: offsets, modulation weights (softmax over the quad's nine
+    // Own slots: offsets, modulation weights (softmax over the quad's K
     // logits for DCNv3, the raw mask for DCNv4) and grad_output.
-    float2 offs[3];
-    float m[3], gy[4];
-    float lgs[3];
-#pragma unroll
-    for (int r = 0; r < 3; ++r) {
+    float2 offs[P];
+    float m[P], gy[4];
+    float lgs[P];
+    // whether slot r of this lane holds a point (3x3: slot 2 is lane 0's k = 8)
+    auto has_slot = [&](int r) -> bool { return KS == 3 ? (r < 2 || (!RC && sub == 0)) : (P * (int)sub + r < K); };
+    // offset of slot r from the raw row words (5x5: decoded where used, so
+    // the words stay the only copy)
+    auto slot_offset = [&](int r) -> float2 {
       if constexpr (DT == DCN_F32)
-        offs[r] = make_float2(__uint_as_float(rw[2 * r]), __uint_as_float(rw[2 * r + 1]));
+        return make_float2(__uint_as_float(rw[2 * r]), __uint_as_float(rw[2 * r + 1]));
       else
-        offs[r] = make_float2(io::lo(rw[r]), io::hi(rw[r]));
-      lgs[r] = io::lo(rl[r]);
+        return make_float2(io::lo(rw[r]), io::hi(rw[r]));
+    };
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+      if constexpr (KS == 3) offs[r] = slot_offset(r);
+      lgs[r] = has_slot(r) ? io::lo(rl[r]) : (SOFTMAX ? -INFINITY : 0.f);
     }
     unpack<DT, NWL>(rg, gy);
-    if (RC || sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 only
     if constexpr (SOFTMAX) {
-      const float mx = quad_max(fmaxf(fmaxf(lgs[0], lgs[1]), lgs[2]));
-      float e[3], sum = 0.f;
+      float mx = lgs[0];
 #pragma unroll
-      for (int r = 0; r < 3; ++r) {
-        e[r] = (r < 2 || (!RC && sub == 0)) ? __expf(lgs[r] - mx) : 0.f;
+      for (int r = 1; r < P; ++r) mx = fmaxf(mx, lgs[r]);
+      mx = quad_max(mx);
+      float e[P], sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < P; ++r) {
+        e[r] = has_slot(r) ? __expf(lgs[r] - mx) : 0.f;
         sum += e[r];
       }
       const float inv = __builtin_amdgcn_rcpf(quad_sum(sum));
 #pragma unroll
-      for (int r = 0; r < 3; ++r) m[r] = e[r] * inv;
+      for (int r = 0; r < P; ++r) m[r] = e[r] * inv;
     } else {
 #pragma unroll
-      for (int r = 0; r < 3; ++r) m[r] = lgs[r];
+      for (int r = 0; r < P; ++r) m[r] = lgs[r];
     }
 
     // Fixed-point scale of the item's grad window.  A pixel-group adds at
@@ -387,7 +430,10 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
         gmax = fmaxf(gmax, fabsf(gy[c]));
         nanflag += 0.f * gy[c];  // fmaxf drops NaN: a NaN in gy must still reach the bound
       }
-      const float msum = quad_sum(fabsf(m[0]) + fabsf(m[1]) + fabsf(m[2]));
+      float mabs = 0.f;
+#pragma unroll
+      for (int r = 0; r < P; ++r) mabs += fabsf(m[r]);
+      const float msum = quad_sum(mabs);
       float bound = quad_max(gmax) * msum + quad_sum(nanflag);
       bound = (cur.live && sub == 0) ? bound : 0.f;
       float bmin = bound > 0.f ? bound : INFINITY;
@@ -420,21 +466,18 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
     const bool more = next < end;  // block-uniform
     const Item nx = decode(more ? next : item);
     issue_window(nx, more);
-    issue_rows(nx);
+    if constexpr (KS == 3) issue_rows(nx);  // 5x5: after the rounds, which read the current rows
 
-    // Per-slot results, shifted in round by round: after the three rounds
-    // (two with RC, then one empty shift) res2 holds slot 0, res1 slot 1,
-    // res0 slot 2.  (gm, d/dx, d/dy)
-    float3 res0 = make_float3(0.f, 0.f, 0.f), res1 = res0, res2 = res0;
-    float2 o2 = offs[0], o2n = offs[1], o2nn = offs[2];
-    float mk = m[0], mkn = m[1], mknn = m[2];
-#pragma unroll 1
-    for (int r = 0; r < ROUNDS; ++r) {
+    // One round: every lane's point of slot r (its offset o2 and weight mk,
+    // its window position (bx, by) before the offset), processed by the
+    // whole quad; `owners` of the quad's lanes hold a point this round.
+    // Returns the owner's (gm, d/dx, d/dy).
+    auto round = [&](int r, float2 o2, float mk, int bx, int by, int owners) -> float3 {
       // Wave priority falls round by round: the waves furthest behind issue
       // first, so the block reaches its flush barrier with less spread.
       if (r == 0) __builtin_amdgcn_s_setprio(3);
-      if (r == 1) __builtin_amdgcn_s_setprio(2);
-      if (r == 2) __builtin_amdgcn_s_setprio(1);
+      if (r == (KS == 3 ? 1 : P / 3)) __builtin_amdgcn_s_setprio(2);
+      if (r == (KS == 3 ? 2 : 2 * P / 3)) __builtin_amdgcn_s_setprio(1);
       const float dx = s * o2.x, dy = s * o2.y;
       const bool nan_loc = (dx != dx) | (dy != dy);
       const float cx = __builtin_amdgcn_fmed3f(dx, -16777216.f, 16777216.f);
@@ -442,8 +485,8 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
       const float fx = floorf(cx), fy = floorf(cy);
       const float lx = cx - fx, ly = cy - fy;
       const float hx = 1.f - lx, hy = 1.f - ly;
-      const int tx = (int)((bxp >> (10 * r)) & 1023u) + (int)fx;  // window coordinates
-      const int ty = (int)((byp >> (10 * r)) & 1023u) + (int)fy;
+      const int tx = bx + (int)fx;  // window coordinates
+      const int ty = by + (int)fy;
       const bool inside = cur.live && !nan_loc && (uint32_t)ty <= (uint32_t)LIM_Y && (uint32_t)tx <= (uint32_t)LIM_X;
       const uint32_t A = inside ? mad24((uint32_t)ty, (uint32_t)ROW, mul24((uint32_t)tx, PIXB)) : ZERO;
       const float wy1 = ly * mk, wy0 = mk - wy1;
@@ -558,48 +601,102 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
       using I2 = std::integral_constant<int, 2>;
       using I3 = std::integral_constant<int, 3>;
       point(I0{});
-      if (r < 2) {  // the last round holds only k = 8 (owner lane 0)
-        point(I1{});
-        point(I2{});
-        point(I3{});
-      }
-      res2 = res1;
-      res1 = res0;
-      res0 = mine;
-      o2 = o2n;
-      o2n = o2nn;
-      mk = mkn;
-      mkn = mknn;
-    }
+      if (owners > 1) point(I1{});
+      if (owners > 2) point(I2{});
+      if (owners > 3) point(I3{});
+      return mine;
+    };
 
-    if constexpr (RC) {
-      res2 = res1;
-      res1 = res0;
-      res0 = make_float3(0.f, 0.f, 0.f);
+    // (gm, d/dx, d/dy) of the own slots
+    float3 res[P];
+    if constexpr (KS == 3) {
+      // Slot inputs shifted in round by round; after the three rounds (two
+      // with RC, then one empty shift) res2 holds slot 0, res1 slot 1, res0
+      // slot 2.  The last round holds only k = 8 (owner lane 0).
+      float3 res0 = make_float3(0.f, 0.f, 0.f), res1 = res0, res2 = res0;
+      float2 o2 = offs[0], o2n = offs[1], o2nn = offs[2];
+      float mk = m[0], mkn = m[1], mknn = m[2];
+#pragma unroll 1
+      for (int r = 0; r < ROUNDS; ++r) {
+        const float3 mine = round(r, o2, mk, (int)((bxp >> (10 * r)) & 1023u), (int)((byp >> (10 * r)) & 1023u),
+                                  r < 2 ? 4 : 1);
+        res2 = res1;
+        res1 = res0;
+        res0 = mine;
+        o2 = o2n;
+        o2n = o2nn;
+        mk = mkn;
+        mkn = mknn;
+      }
+      if constexpr (RC) {
+        res2 = res1;
+        res1 = res0;
+        res0 = make_float3(0.f, 0.f, 0.f);
+      }
+      res[0] = res2;
+      res[1] = res1;
+      res[2] = res0;
+    } else {
+      // The offset gradients of each slot are stored as its round ends (they
+      // need no other slot); gm waits for the softmax Jacobian.
+#pragma unroll
+      for (int r = 0; r < P; ++r) {
+        const int k = P * (int)sub + r;
+        const int q = RC ? k + (k >= KS * KS / 2) : k;  // grid index
+        const int owners = (K - 1 - r) / P + 1 < 4 ? (K - 1 - r) / P + 1 : 4;
+        const float3 mine = round(r, slot_offset(r), m[r], ox + R + q % KS, oy + R + q / KS, owners);
+        res[r] = make_float3(mine.x, 0.f, 0.f);
+        const bool put = cur.live && has_slot(r);
+        const float gx_ = s * m[r] * mine.y, gy_ = s * m[r] * mine.z;
+        if constexpr (DT == DCN_F32) {
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          __builtin_amdgcn_raw_buffer_store_b64(
+              __builtin_bit_cast(uint32_t __attribute__((ext_vector_type(2))), f2{gx_, gy_}), rgoff,
+              put ? (int)(cur.pg * (uint32_t)(K * 8) + 8u * (uint32_t)k) : (int)kOutOfRange, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(
+              io::pack(gx_, gy_), rgoff, put ? (int)(cur.pg * (uint32_t)(K * 4) + 4u * (uint32_t)k) : (int)kOutOfRange,
+              0, 0);
+        }
+      }
+      issue_rows(nx);
     }
 
     // Offset and mask gradients of the own slots (a NaN sampling location
     // makes its point's offset gradient and gm NaN).
     if (cur.live) {
-      const float3 rs[3] = {res2, res1, res0};
-      float gm[3];
+      float gm[P];
 #pragma unroll
-      for (int r = 0; r < 3; ++r) gm[r] = rs[r].x;
+      for (int r = 0; r < P; ++r) gm[r] = res[r].x;
       if constexpr (SOFTMAX) {
-        float dot = m[0] * gm[0] + m[1] * gm[1];
-        if (!RC && sub == 0) dot += m[2] * gm[2];
+        float dot = 0.f;
+#pragma unroll
+        for (int r = 0; r < P; ++r)
+          if (has_slot(r)) dot += m[r] * gm[r];
         dot = quad_sum(dot);
 #pragma unroll
-        for (int r = 0; r < 3; ++r) gm[r] = m[r] * (gm[r] - dot);
+        for (int r = 0; r < P; ++r) gm[r] = m[r] * (gm[r] - dot);
       }
-      // offset gradients (x, y) of the three slots
-      float go[3][2];
+      // offset gradients (x, y) of the slots
+      float go[P][2];
 #pragma unroll
-      for (int r = 0; r < 3; ++r) {
-        go[r][0] = s * m[r] * rs[r].y;
-        go[r][1] = s * m[r] * rs[r].z;
+      for (int r = 0; r < P; ++r) {
+        go[r][0] = s * m[r] * res[r].y;
+        go[r][1] = s * m[r] * res[r].z;
       }
-      if constexpr (DT == DCN_F32) {
+      if constexpr (KS == 5) {  // gm, one point at a time (k = P sub + r), none past K
+#pragma unroll
+        for (int r = 0; r < P; ++r) {
+          const bool has = has_slot(r);
+          const uint32_t k = (uint32_t)(P * (int)sub + r);
+          if constexpr (DT == DCN_F32)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gm[r]), rgm,
+                                                  has ? (int)(cur.pg * (uint32_t)(K * 4) + 4u * k) : (int)kOutOfRange, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(io::pack(gm[r], 0.f) & 0xffffu), rgm,
+                                                  has ? (int)(cur.pg * (uint32_t)(K * 2) + 2u * k) : (int)kOutOfRange, 0, 0);
+        }
+      } else if constexpr (DT == DCN_F32) {
         typedef float f4 __attribute__((ext_vector_type(4)));
         typedef float f2 __attribute__((ext_vector_type(2)));
         const uint32_t orow = cur.pg * (K * 8), mrow = cur.pg * (K * 4);
@@ -682,10 +779,10 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
 
 namespace {
 
-template <int DT, bool SM, bool RC, int DIL, int TW, int TH, int ST>
+template <int DT, bool SM, bool RC, int DIL, int TW, int TH, int ST, int KS>
 hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s) {
-  using G = BqGeom<TW, TH, ST>;
-  auto kern = dcn_bwd_quad_kernel<DT, SM, RC, DIL, TW, TH, ST>;
+  using G = BqGeom<TW, TH, ST, KS>;
+  auto kern = dcn_bwd_quad_kernel<DT, SM, RC, DIL, TW, TH, ST, KS>;
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
@@ -703,18 +800,32 @@ hipError_t launch_bwd_quad(const BwdParams &p, const TileGeom &tg, hipStream_t s
   return hipGetLastError();
 }
 
-template <bool RC, int DIL, int TW, int TH, int ST = 1>
+template <bool RC, int DIL, int TW, int TH, int ST = 1, int KS = 3>
 hipError_t launch_dt(int dtype, int softmax, const BwdParams &b, const TileGeom &tg, hipStream_t s) {
   switch (dtype) {
     case DCN_F32:
-      return softmax ? launch_bwd_quad<DCN_F32, true, RC, DIL, TW, TH, ST>(b, tg, s)
-                     : launch_bwd_quad<DCN_F32, false, RC, DIL, TW, TH, ST>(b, tg, s);
+      return softmax ? launch_bwd_quad<DCN_F32, true, RC, DIL, TW, TH, ST, KS>(b, tg, s)
+                     : launch_bwd_quad<DCN_F32, false, RC, DIL, TW, TH, ST, KS>(b, tg, s);
     case DCN_F16:
-      return softmax ? launch_bwd_quad<DCN_F16, true, RC, DIL, TW, TH, ST>(b, tg, s)
-                     : launch_bwd_quad<DCN_F16, false, RC, DIL, TW, TH, ST>(b, tg, s);
+      return softmax ? launch_bwd_quad<DCN_F16, true, RC, DIL, TW, TH, ST, KS>(b, tg, s)
+                     : launch_bwd_quad<DCN_F16, false, RC, DIL, TW, TH, ST, KS>(b, tg, s);
     case DCN_BF16:
-      return softmax ? launch_bwd_quad<DCN_BF16, true, RC, DIL, TW, TH, ST>(b, tg, s)
-                     : launch_bwd_quad<DCN_BF16, false, RC, DIL, TW, TH, ST>(b, tg, s);
+      return softmax ? launch_bwd_quad<DCN_BF16, true, RC, DIL, TW, TH, ST, KS>(b, tg, s)
+                     : launch_bwd_quad<DCN_BF16, false, RC, DIL, TW, TH, ST, KS>(b, tg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The same for shapes only taken with 16-bit I/O.
+template <bool RC, int DIL, int TW, int TH, int ST, int KS>
+hipError_t launch_16bit(int dtype, int softmax, const BwdParams &b, const TileGeom &tg, hipStream_t s) {
+  switch (dtype) {
+    case DCN_F16:
+      return softmax ? launch_bwd_quad<DCN_F16, true, RC, DIL, TW, TH, ST, KS>(b, tg, s)
+                     : launch_bwd_quad<DCN_F16, false, RC, DIL, TW, TH, ST, KS>(b, tg, s);
+    case DCN_BF16:
+      return softmax ? launch_bwd_quad<DCN_BF16, true, RC, DIL, TW, TH, ST, KS>(b, tg, s)
+                     : launch_bwd_quad<DCN_BF16, false, RC, DIL, TW, TH, ST, KS>(b, tg, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -727,24 +838,34 @@ double quad_tile_use(const FwdParams &p, int tw, int th) {
 
 }  // namespace
 
-// 3x3 points (all nine, or eight without the centre), stride 1 or 2 and
-// dilation 1 or 2 (each the same on both axes) only; hipErrorNotSupported
+// 3x3 points (all nine, or eight without the centre) at stride 1 or 2 and
+// dilation 1 or 2 (each the same on both axes), and 5x5 points (25 or 24)
+// at stride and dilation 1, on tiles of 8 to 16 rows; hipErrorNotSupported
 // otherwise.
 hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipStream_t s) {
   const FwdParams &p = b.f;
-  if (p.KH != 3 || p.KW != 3 || p.SH != p.SW || (p.SH != 1 && p.SH != 2) || p.DH != p.DW ||
-      (p.DH != 1 && p.DH != 2))
+  const bool k5 = p.KH == 5 && p.KW == 5 && p.SH == 1 && p.SW == 1 && p.DH == 1 && p.DW == 1;
+  if (!k5 && (p.KH != 3 || p.KW != 3 || p.SH != p.SW || (p.SH != 1 && p.SH != 2) || p.DH != p.DW ||
+              (p.DH != 1 && p.DH != 2)))
     return hipErrorNotSupported;
   const bool s2 = p.SH == 2;
   // 24x8 or 12x12 tiles (stride and dilation 1) where they leave clearly
   // fewer quads idle than 16x16 ones (24x8 on a tie between the two)
   const double u16 = quad_tile_use(p, 16, 16), u24 = quad_tile_use(p, 24, 8), u12 = quad_tile_use(p, 12, 12);
-  const bool wide = !s2 && p.DH == 1 && u24 > u16 + 0.1 && u24 >= u12;
-  const bool small = !s2 && p.DH == 1 && !wide && u12 > u16 + 0.1;
-  const int tw = wide ? 24 : (small ? 12 : 16), th = s2 || wide ? 8 : (small ? 12 : 16);
+  const bool wide = !k5 && !s2 && p.DH == 1 && u24 > u16 + 0.1 && u24 >= u12;
+  const bool small = !k5 && !s2 && p.DH == 1 && !wide && u12 > u16 + 0.1;
+  // 5x5 points: 16x8 tiles in fp32 (16x16 ones spill at 1024 threads) and
+  // where they leave clearly fewer quads idle, 16x16 tiles otherwise
+  const bool k5_tall = k5 && dtype != DCN_F32 && quad_tile_use(p, 16, 8) <= u16 + 0.1;
+  const int tw = wide ? 24 : (small ? 12 : 16),
+            th = k5 ? (k5_tall ? 16 : 8) : (s2 || wide ? 8 : (small ? 12 : 16));
   TileGeom tg{};
-  tg.span_w = s2 ? BqGeom<16, 8, 2>::kSpanW : tw + 2 * kBqHalo + 3;
-  tg.span_h = s2 ? BqGeom<16, 8, 2>::kSpanH : th + 2 * kBqHalo + 3;
+  tg.span_w = s2 ? BqGeom<16, 8, 2>::kSpanW
+                 : (k5 ? (k5_tall ? BqGeom<16, 16, 1, 5>::kSpanW : BqGeom<16, 8, 1, 5>::kSpanW)
+                       : tw + 2 * kBqHalo + 3);
+  tg.span_h = s2 ? BqGeom<16, 8, 2>::kSpanH
+                 : (k5 ? (k5_tall ? BqGeom<16, 16, 1, 5>::kSpanH : BqGeom<16, 8, 1, 5>::kSpanH)
+                       : th + 2 * kBqHalo + 3);
   // Window rows outside the map are rejected by the buffer range of their
   // image (input, and grad_input at GX bytes per input byte), which needs
   // every window row's offset relative to the image to fit int32.
@@ -762,6 +883,12 @@ hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &b, hipS
   tg.div_tiles = make_fast_div((uint32_t)tg.tiles_per_img);
   tg.div_tiles_x = make_fast_div((uint32_t)tg.tiles_x);
   tg.div_span_w = make_fast_div((uint32_t)tg.span_w);
+  if (k5_tall)
+    return p.RC ? launch_16bit<true, 1, 16, 16, 1, 5>(dtype, softmax, b, tg, s)
+                : launch_16bit<false, 1, 16, 16, 1, 5>(dtype, softmax, b, tg, s);
+  if (k5)
+    return p.RC ? launch_dt<true, 1, 16, 8, 1, 5>(dtype, softmax, b, tg, s)
+                : launch_dt<false, 1, 16, 8, 1, 5>(dtype, softmax, b, tg, s);
   if (s2 && p.DH == 2)
     return p.RC ? launch_dt<true, 2, 16, 8, 2>(dtype, softmax, b, tg, s) : launch_dt<false, 2, 16, 8, 2>(dtype, softmax, b, tg, s);
   if (s2)

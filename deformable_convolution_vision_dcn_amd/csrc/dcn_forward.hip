@@ -241,7 +241,8 @@ Path path_override() {
 // the lane-per-pixel-group kernel at stride and dilation 1 (one, two or four
 // groups per work item), which needs a quarter of the address and weight
 // arithmetic and wins once a pixel's 16 channels are only 32 bytes, and the
-// quad tiled kernel at other strides and dilations.  Everything else runs
+// quad tiled kernel at other strides and dilations.  5x5 points at stride
+// and dilation 1 run the lane kernel in every dtype.  Everything else runs
 // the untiled kernel.
 // Whether the whole-map kernel is the first choice: the output map is
 // smaller than one 16x16 tile, or tiles would leave over half of their

@@ -57,10 +57,12 @@
  * kernel (fp32: the quad kernel, two groups per work item where the group
  * count is even, at stride 1 or 2 and dilation 1 or 2, with or without the
  * centre; 16-bit I/O: the lane kernel, up to four groups per work item, at
- * stride and dilation 1, else the quad kernel); everything else (other
+ * stride and dilation 1, else the quad kernel); 5x5 points at stride and
+ * dilation 1 run the lane kernel in every dtype; everything else (other
  * point sets, windows that do not fit) runs the untiled kernel.  The
- * backward runs the tiled quad kernel at stride 1 or 2 and dilation 1 or 2,
- * else the untiled kernel.  The environment variable
+ * backward runs the tiled quad kernel for 3x3 points at stride 1 or 2 and
+ * dilation 1 or 2 and for 5x5 points at stride and dilation 1, else the
+ * untiled kernel.  The environment variable
  * DCN_MI355X_FWD_PATH = "generic" | "tiled" (one group per work item) |
  * "pair" (two groups per work item) | "lane" | "map" (whole maps in LDS),
  * read at every call, makes the forward try that kernel first;
@@ -212,8 +214,8 @@ int dcn_backward_workspace_size(const dcn_problem *p, uint64_t *bytes);
  * right (the floor convention).  Every shape, in fp32 and in 16-bit I/O (all
  * tensors of the call in that dtype).  The arithmetic is fp32 throughout and
  * grad_input is accumulated in fp32 atomics, so its low bits can vary from
- * run to run.  The tiled kernel (3x3 points, stride 1, dilation 1 or 2) first
- * sums each output tile's scatter in fixed point on the tile's own grid: a
+ * run to run.  The tiled quad kernel (the shapes under kernel choice above)
+ * first sums each output tile's scatter in fixed point on the tile's own grid: a
  * term is rounded to a multiple of 2^(e-30), where 2^e bounds the tile's sum
  * B of sum_k |m_k| * max_c |grad_output_c| over its pixel-groups, so an
  * element reached by n terms is off by at most n * 2^(e-31) <= n * B * 2^-30.

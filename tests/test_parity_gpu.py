@@ -341,7 +341,12 @@ BWD_PATH_CASES = [
                                 Workload("bwdp_24wide", n=2, h=41, w=24, c=48, groups=3,
                                          offset_dist=uniform(4.0), seed=55),
                                 Workload("bwdp_12x12", n=3, h=12, w=12, c=64, groups=4,
-                                         offset_dist=uniform(4.0), seed=56)],
+                                         offset_dist=uniform(4.0), seed=56),
+                                Workload("bwdp_k5", n=2, h=37, w=29, c=48, groups=3, kernel=(5, 5), pad=(2, 2),
+                                         offset_dist=normal(2.0), seed=57),
+                                Workload("bwdp_k5_rc_v4_far", n=1, h=33, w=35, c=32, groups=2, kernel=(5, 5),
+                                         pad=(2, 2), softmax=False, mask_dist=normal(0.5), remove_center=True,
+                                         offset_dist=uniform(6.0), seed=58)],
                          ids=lambda w: w.name)
 def test_backward_each_kernel(wl, path, monkeypatch):
     """Every backward kernel, forced in turn, on multi-tile ragged shapes
@@ -371,11 +376,16 @@ BWD16 = [
     Workload("bwd16_24wide", n=2, h=24, w=24, c=48, groups=3, offset_dist=uniform(3.0), seed=69),
     Workload("bwd16_12x12", n=3, h=12, w=12, c=64, groups=4, softmax=False, mask_dist=normal(0.5),
              seed=70),
+    Workload("bwd16_k5_tiles", n=2, h=37, w=29, c=64, groups=4, kernel=(5, 5), pad=(2, 2),
+             offset_dist=normal(2.0), seed=78),
+    Workload("bwd16_k5_rc_far", n=1, h=26, w=33, c=48, groups=3, kernel=(5, 5), pad=(2, 2), softmax=False,
+             mask_dist=normal(0.5), remove_center=True, offset_dist=uniform(6.0), seed=79),
 ]
 
 
-# Shapes the tiled backward does not take (other strides, dilations and
-# point sets): the untiled kernel, with 16-bit I/O accumulating in fp32.
+# Shapes beyond 3x3 at stride 1: stride 2 and 5x5 (the tiled quad kernel at
+# small sizes) and the untiled kernel's (other strides, dilations and point
+# sets), with 16-bit I/O accumulating in fp32.
 BWD16_UNTILED = [
     Workload("bwd16_stride2", n=2, h=15, w=17, c=32, groups=2, stride=(2, 2), offset_dist=normal(2.0), seed=71),
     Workload("bwd16_stride2_dil2", n=2, h=15, w=17, c=32, groups=2, stride=(2, 2), dilation=(2, 2),
@@ -690,9 +700,10 @@ def test_backward_guard_bands_untouched(dtype, path, monkeypatch):
         gate(_np(gm), rm, dtype, f"guarded grad_mask call {call}")
 
 
+@pytest.mark.parametrize("ks", [3, 5], ids=["k3", "k5"])
 @pytest.mark.parametrize("path", ["auto", "tiled"])
 @pytest.mark.parametrize("softmax", [True, False], ids=["dcnv3_gy_outlier", "dcnv4_mask_outlier"])
-def test_backward_outlier_per_tile(softmax, path, monkeypatch):
+def test_backward_outlier_per_tile(softmax, path, ks, monkeypatch):
     """Heavy-tailed gradients: in every other 16x16 output tile one
     pixel-group carries terms 1e4 times the others (DCNv3: its grad_output
     row scaled by 1e4; DCNv4: its unnormalised mask row).  grad_input
@@ -702,8 +713,9 @@ def test_backward_outlier_per_tile(softmax, path, monkeypatch):
     and |mask|); the outliers' own offset and mask rows to 1e-4 of their
     largest value, and every other offset and mask gradient to 1e-4."""
     monkeypatch.setenv("DCN_MI355X_BWD_PATH", path)
-    wl = Workload("outlier", n=2, h=48, w=40, c=32, groups=2, softmax=softmax,
-                  mask_dist=normal(1.0 if softmax else 0.5), offset_dist=normal(1.5), seed=48)
+    wl = Workload("outlier", n=2, h=48, w=40, c=32, groups=2, softmax=softmax, kernel=(ks, ks),
+                  pad=(ks // 2, ks // 2), mask_dist=normal(1.0 if softmax else 0.5), offset_dist=normal(1.5),
+                  seed=48)
     t = synth.make_inputs(wl, with_grad=True)
     rng = np.random.default_rng(10)
     ho, wo = wl.out_hw
@@ -720,7 +732,7 @@ def test_backward_outlier_per_tile(softmax, path, monkeypatch):
             t["grad_out"][n, y, xx, 16 * g:16 * g + 16] *= 1e4
         else:
             t["mask"][n, y, xx, g] *= 1e4
-    print(f"backward outliers softmax={softmax} path={path} ({len(hot)} outliers)", flush=True)
+    print(f"backward outliers softmax={softmax} path={path} {ks}x{ks} ({len(hot)} outliers)", flush=True)
     gx, goff, gm = (_np(a) for a in run_backward(wl, t))
     rx, roff, rm = oracle_backward(wl, t)
     # the outliers' scatter alone (grad_output zero elsewhere) marks the
