@@ -503,7 +503,19 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
       const bool gscat = fixed ? fb : (cur.live && !nan_loc);  // global scatter
       const bool fb_any = __builtin_amdgcn_ballot_w64(fb) != 0;      // wave-uniform
       const bool gs_any = __builtin_amdgcn_ballot_w64(gscat) != 0;   // wave-uniform
+      // 3x3: the quad's corner sums of this lane's own point, turned into
+      // its results once per round; 5x5 (whose tiles leave fewer registers):
+      // the owner's results directly.
+      float Gown[4] = {0.f, 0.f, 0.f, 0.f};
       float3 mine = make_float3(0.f, 0.f, 0.f);
+
+      // gm, d/dx and d/dy of the own point from the quad's corner sums G (00,
+      // 01, 10, 11): one-sided derivatives of the bilinear form, linear in G.
+      auto own_results = [&](const float (&G)[4]) -> float3 {
+        const float T = hx * G[0] + lx * G[1], Bt = hx * G[2] + lx * G[3];
+        return nan_loc ? make_float3(qnan, qnan, qnan)
+                       : make_float3(hy * T + ly * Bt, hy * (G[1] - G[0]) + ly * (G[3] - G[2]), Bt - T);
+      };
 
       auto point = [&](auto o_tag) {
         constexpr int O = decltype(o_tag)::value;
@@ -558,14 +570,14 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
           }
         }
         // Sums over the 16 channels: every lane of the quad gets them; the
-        // owner keeps gm, d/dx and d/dy of its point (one-sided derivatives
-        // of the bilinear form, linear in the corner sums).
+        // owner keeps them (3x3: selects, no branch) or its results.
         quad_sum4(P);
-        const float G00 = P[0], G01 = P[1], G10 = P[2], G11 = P[3];
-        if (sub == (uint32_t)O) {
-          const float T = hx * G00 + lx * G01, Bt = hx * G10 + lx * G11;
-          mine = nan_loc ? make_float3(qnan, qnan, qnan)
-                         : make_float3(hy * T + ly * Bt, hy * (G01 - G00) + ly * (G11 - G10), Bt - T);
+        if constexpr (KS == 3) {
+          const bool owner = sub == (uint32_t)O;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) Gown[q] = owner ? P[q] : Gown[q];
+        } else if (sub == (uint32_t)O) {
+          mine = own_results(P);
         }
         // Scatter m_k * w_corner * gy_c of this lane's 4 channels (no
         // branch: samples the window does not hold add into the sink).
@@ -604,6 +616,9 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
       if (owners > 1) point(I1{});
       if (owners > 2) point(I2{});
       if (owners > 3) point(I3{});
+      // 3x3: once per round in every lane (a lane without a point this round
+      // returns values nobody stores)
+      if constexpr (KS == 3) mine = own_results(Gown);
       return mine;
     };
 
