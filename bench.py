@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "dcn_fwd_map_kernel": "dcn_fwd_map.hip", "dcn_fwd_kernel": "dcn_forward.hip",
     "dcn_fused_kernel": "dcn_fused.hip", "dcn_bwd_quad_kernel": "dcn_bwd_quad.hip",
     "dcn_bwd_tile_kernel": "dcn_bwd_tile.hip", "dcn_bwd_kernel": "dcn_backward.hip",
+    "dcn_bwd_map_kernel": "dcn_bwd_map.hip",
 }
 
 

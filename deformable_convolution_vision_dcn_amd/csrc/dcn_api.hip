@@ -169,12 +169,16 @@ int run_backward(const dcn_problem *p, int64_t ho, int64_t wo, const void *input
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
 
   hipError_t e = hipSuccess;
-  if (wide) {
+  dcn::BwdParams b{};
+  b.f = geometry(p, ho, wo);
+  // The whole-map kernel writes every grad_input element itself, in the I/O
+  // dtype: no clear, no rounding pass (16-bit: the workspace only takes the
+  // items that fall back to fp32 atomics).  Decided once, before any launch.
+  const bool whole_map = dcn::backward_takes_map(b.f);
+  if (wide && !whole_map) {
     e = dcn::launch_zero(grad_input, (uint64_t)(p->n * img_in), stream);
     if (e != hipSuccess) return hip_fail(e);
   }
-  dcn::BwdParams b{};
-  b.f = geometry(p, ho, wo);
   for (int64_t n0 = 0; n0 < p->n; n0 += per) {
     const int64_t nc = (p->n - n0 < per) ? p->n - n0 : per;
     b.f.input = static_cast<const char *>(input) + n0 * img_in;
@@ -189,16 +193,19 @@ int run_backward(const dcn_problem *p, int64_t ho, int64_t wo, const void *input
     b.grad_out = static_cast<const char *>(grad_output) + n0 * img_pg * dcn::kGroupChannels * eb;
     b.grad_offset = static_cast<char *>(grad_offset) + n0 * img_pg * K * 2 * eb;
     b.grad_mask = static_cast<char *>(grad_mask) + n0 * img_pg * K * eb;
-    if (wide) {
+    if (whole_map) {
+      b.grad_in = static_cast<char *>(grad_input) + n0 * img_in;
+      b.acc = wide ? b.grad_in : ws;
+    } else if (wide) {
       b.grad_in = static_cast<char *>(grad_input) + n0 * img_in;
     } else {  // each chunk reuses the accumulator: zero it, accumulate, round out
       b.grad_in = ws;
       e = dcn::launch_zero(ws, (uint64_t)(nc * img_elems * 4), stream);
       if (e != hipSuccess) return hip_fail(e);
     }
-    e = dcn::launch_backward(p->dtype, p->softmax, b, stream);
+    e = dcn::launch_backward(p->dtype, p->softmax, b, whole_map, stream);
     if (e != hipSuccess) return hip_fail(e);
-    if (!wide) {
+    if (!wide && !whole_map) {
       e = dcn::launch_narrow(p->dtype, ws, static_cast<char *>(grad_input) + n0 * img_in,
                              (uint64_t)(nc * img_elems), stream);
       if (e != hipSuccess) return hip_fail(e);

@@ -265,9 +265,17 @@ hipError_t launch_untiled(int softmax, const BwdParams &p, hipStream_t s) {
 
 // Backward path override for tests and measurements: DCN_MI355X_BWD_PATH =
 // "generic" (untiled kernel), "tiled" (the half-window tiled kernel, fp32
-// only) or "quad" (the lane-quad tiled kernel, also the default where it
-// applies).  Read at every call.
-hipError_t launch_backward(int dtype, int softmax, const BwdParams &p, hipStream_t s) {
+// only), "quad" (the lane-quad tiled kernel, the default where it applies
+// and the whole-map kernel does not) or "map" (the whole-map kernel, the
+// default where it applies).  Read at every call.
+bool backward_takes_map(const FwdParams &p) {
+  const char *e = getenv("DCN_MI355X_BWD_PATH");
+  if (e && (!strcmp(e, "generic") || !strcmp(e, "tiled") || !strcmp(e, "quad"))) return false;
+  return backward_map_applies(p);
+}
+
+hipError_t launch_backward(int dtype, int softmax, const BwdParams &p, bool whole_map, hipStream_t s) {
+  if (whole_map) return launch_backward_map(dtype, softmax, p, s);
   const char *e = getenv("DCN_MI355X_BWD_PATH");
   const bool generic = e && !strcmp(e, "generic");
   const bool halves = e && !strcmp(e, "tiled");

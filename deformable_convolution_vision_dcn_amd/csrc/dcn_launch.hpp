@@ -36,7 +36,11 @@ struct FwdParams {
 struct BwdParams {
   FwdParams f;             // input, offset, mask and geometry as in the forward
   const void *grad_out;    // (chunk, Ho, Wo, C), the I/O dtype like every tensor
-  void *grad_in;           // (chunk, H, W, C), fp32 for every I/O dtype, zeroed before the launch
+  void *grad_in;           // (chunk, H, W, C): the whole-map kernel writes it in the I/O dtype;
+                           // the others add into it in fp32 (for 16-bit I/O the fp32
+                           // accumulator), zeroed before the launch
+  void *acc;               // whole-map kernel: fp32 (chunk, H, W, C) accumulator of items on
+                           // fp32 atomics (grad_in itself for fp32 I/O); contents on entry unused
   void *grad_offset;       // (chunk, Ho, Wo, G, K, 2)
   void *grad_mask;         // (chunk, Ho, Wo, G, K)
 };
@@ -75,7 +79,14 @@ hipError_t launch_forward_tiled(int dtype, int softmax, const FwdParams &p, hipS
                                 int groups_per_item);
 hipError_t launch_forward_lane(int dtype, int softmax, const FwdParams &p, hipStream_t s);
 hipError_t launch_forward_map(int dtype, int softmax, const FwdParams &p, hipStream_t s);
-hipError_t launch_backward(int dtype, int softmax, const BwdParams &p, hipStream_t s);
+// The backward; `whole_map` (from backward_takes_map) selects the whole-map
+// kernel, which writes grad_in in the I/O dtype without a prior clear.
+hipError_t launch_backward(int dtype, int softmax, const BwdParams &p, bool whole_map, hipStream_t s);
+// Whether the backward of this problem runs the whole-map kernel (read at
+// every call: the DCN_MI355X_BWD_PATH override can turn it off).
+bool backward_takes_map(const FwdParams &p);
+bool backward_map_applies(const FwdParams &p);
+hipError_t launch_backward_map(int dtype, int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_tiled(int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_backward_quad(int dtype, int softmax, const BwdParams &p, hipStream_t s);
 hipError_t launch_forward_generated(int dtype, int softmax, const FusedParams &p, hipStream_t s);

@@ -38,9 +38,10 @@
  *   grad_*       the shape of the tensor it is the gradient of.
  *
  * Arithmetic: sampling locations, weights, the softmax and every accumulation
- * are fp32 for every I/O dtype (the tiled backward sums grad_input in exact
- * integer arithmetic on a per-tile fixed-point grid instead, with the error
- * bound stated at dcn_backward); 16-bit results are rounded to nearest-even.
+ * are fp32 for every I/O dtype (the tiled and whole-map backward kernels sum
+ * grad_input in exact integer arithmetic on a per-item fixed-point grid
+ * instead, with the error bound stated at dcn_backward); 16-bit results are
+ * rounded to nearest-even.
  *
  * Ownership and execution: every tensor pointer is a DEVICE pointer owned by
  * the caller.  dcn_forward and dcn_backward allocate nothing, keep no
@@ -60,14 +61,17 @@
  * stride and dilation 1, else the quad kernel); 5x5 points at stride and
  * dilation 1 run the lane kernel in every dtype; everything else (other
  * point sets, windows that do not fit) runs the untiled kernel.  The
- * backward runs the tiled quad kernel for 3x3 points at stride 1 or 2 and
- * dilation 1 or 2 and for 5x5 points at stride and dilation 1, else the
- * untiled kernel.  The environment variable
+ * backward runs the whole-map kernel for 3x3 points at stride and dilation 1
+ * where the input and output maps both fit 12x12, 16x16 or 24x24 (one work
+ * item per image and group), the tiled quad kernel for other 3x3 problems at
+ * stride 1 or 2 and dilation 1 or 2 and for 5x5 points at stride and
+ * dilation 1, else the untiled kernel.  The environment variable
  * DCN_MI355X_FWD_PATH = "generic" | "tiled" (one group per work item) |
  * "pair" (two groups per work item) | "lane" | "map" (whole maps in LDS),
  * read at every call, makes the forward try that kernel first;
- * DCN_MI355X_BWD_PATH = "generic" | "tiled" (half windows, fp32) | "quad"
- * does the same for the backward.  Results agree to rounding either way.
+ * DCN_MI355X_BWD_PATH = "generic" | "tiled" (half windows, fp32) | "quad" |
+ * "map" does the same for the backward.  Results agree to rounding either
+ * way.
  *
  * Errors: every entry point returns DCN_OK (0) or a negative dcn_status.
  * Nothing is enqueued when a check fails (every check of the problem, the
@@ -231,8 +235,16 @@ int dcn_backward_workspace_size(const dcn_problem *p, uint64_t *bytes);
  * images zeroes it, accumulates into it and is then rounded once to
  * nearest-even into grad_input, like grad_offset and grad_mask.  Calls that
  * share a workspace must be ordered on one stream.
+ * The whole-map kernel applies the same fixed point with one grid per
+ * (image, group), whose whole grad_input slice it owns: it writes that slice
+ * once, rounded to the I/O dtype, so grad_input is not zeroed first and an
+ * item on fixed point gives the same bits from run to run; the workspace
+ * (still required for 16-bit I/O) only takes the items that fall back to
+ * fp32 atomics, each clearing its own slice of it first (fp32: grad_input
+ * itself).
  * Enqueues per chunk of images a fill kernel, one backward launch and, for
- * 16-bit I/O, one rounding kernel (fp32: one fill for the whole batch). */
+ * 16-bit I/O, one rounding kernel (fp32: one fill for the whole batch);
+ * for the whole-map kernel's shapes only the backward launch. */
 int dcn_backward(const dcn_problem *p, const void *input, const void *offset, const void *mask,
                  const void *grad_output, void *grad_input, void *grad_offset, void *grad_mask,
                  void *workspace, uint64_t workspace_bytes, void *hip_stream);

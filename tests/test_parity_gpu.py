@@ -335,8 +335,22 @@ BWD_PATH_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["generic", "tiled", "quad"])
-@pytest.mark.parametrize("wl", BWD_PATH_CASES + [BWD_PATH_CASES[0].replace(name="bwdp_rc", remove_center=True),
+# Maps the whole-map backward takes (a 24x24, 16x16 or 12x12 window with its
+# border): ragged maps smaller than the window, padding 0 and 2 (output map
+# smaller or larger than the input), remove_center, DCNv4 masks and offsets
+# that leave the map.
+BWD_MAP_CASES = [
+    Workload("bwdp_map_ragged", n=2, h=20, w=17, c=48, groups=3, offset_dist=uniform(4.0), seed=59),
+    Workload("bwdp_map_pad2_v4", n=2, h=10, w=9, c=32, groups=2, pad=(2, 2), softmax=False,
+             mask_dist=normal(0.5), offset_dist=normal(2.0), seed=60),
+    Workload("bwdp_map16_rc_far", n=1, h=15, w=16, c=32, groups=2, remove_center=True,
+             offset_dist=uniform(9.0), seed=61),
+    Workload("bwdp_map_pad0", n=2, h=24, w=24, c=16, groups=1, pad=(0, 0), offset_dist=normal(3.0), seed=62),
+]
+
+
+@pytest.mark.parametrize("path", ["generic", "tiled", "quad", "map"])
+@pytest.mark.parametrize("wl", BWD_PATH_CASES + BWD_MAP_CASES + [BWD_PATH_CASES[0].replace(name="bwdp_rc", remove_center=True),
                                 BWD_PATH_CASES[1].replace(name="bwdp_dil2_far", dilation=(2, 2), pad=(2, 2)),
                                 Workload("bwdp_24wide", n=2, h=41, w=24, c=48, groups=3,
                                          offset_dist=uniform(4.0), seed=55),
@@ -350,7 +364,9 @@ BWD_PATH_CASES = [
                          ids=lambda w: w.name)
 def test_backward_each_kernel(wl, path, monkeypatch):
     """Every backward kernel, forced in turn, on multi-tile ragged shapes
-    whose offsets also leave the tile windows (the global fix-up path)."""
+    whose offsets also leave the tile windows (the global fix-up path), and
+    on small maps (the whole-map kernel; a forced kernel that does not take a
+    shape falls back to the next)."""
     monkeypatch.setenv("DCN_MI355X_BWD_PATH", path)
     print(f"backward {wl.name} path={path}", flush=True)
     t = synth.make_inputs(wl, with_grad=True)
@@ -661,9 +677,10 @@ def _canaries_intact(buf, fill, what):
     assert torch.all(head == fill) and torch.all(tail == fill), f"{what}: a guard band was written"
 
 
+@pytest.mark.parametrize("small", [False, True], ids=["tiles", "whole_map"])
 @pytest.mark.parametrize("path", ["auto", "generic", "tiled"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_guard_bands_untouched(dtype, path, monkeypatch):
+def test_backward_guard_bands_untouched(dtype, path, small, monkeypatch):
     """grad_input, grad_offset, grad_mask and the 16-bit fp32 workspace each
     sit between two guard bands of canary values; a multi-tile problem whose
     offsets reach far outside the tile windows and the map (the global
@@ -674,6 +691,8 @@ def test_backward_guard_bands_untouched(dtype, path, monkeypatch):
             pytest.skip("the half-window tiled backward is fp32 only")
         monkeypatch.setenv("DCN_MI355X_BWD_PATH", path)
     wl = Workload("guard_bwd", n=2, h=37, w=29, c=48, groups=3, dtype=dtype, offset_dist=uniform(8.0), seed=47)
+    if small:  # the whole-map kernel's shapes
+        wl = wl.replace(h=21, w=19)
     t = synth.make_inputs(wl, with_grad=True)
     x, off, m, gy = (t[k].to(DEV) for k in ("x", "offset", "mask", "grad_out"))
     fill = 12345.0 if dtype == "f32" else 1234.0
@@ -686,7 +705,7 @@ def test_backward_guard_bands_untouched(dtype, path, monkeypatch):
         ws, bws = _guarded((need // 4,), torch.float32, -777.0)
     rx, roff, rm = oracle_backward(wl, t)
     for call in range(2):
-        print(f"backward guard bands {dtype} path={path} call {call}", flush=True)
+        print(f"backward guard bands {dtype} path={path} small={small} call {call}", flush=True)
         dcn.dcn_backward(x, off, m, gy, grad_input=gx, grad_offset=goff, grad_mask=gm,
                          workspace=None if ws is None else ws.view(torch.uint8), **wl.op_kwargs())
         torch.cuda.synchronize()
@@ -700,7 +719,7 @@ def test_backward_guard_bands_untouched(dtype, path, monkeypatch):
         gate(_np(gm), rm, dtype, f"guarded grad_mask call {call}")
 
 
-@pytest.mark.parametrize("ks", [3, 5], ids=["k3", "k5"])
+@pytest.mark.parametrize("ks", [3, 5, "map"], ids=["k3", "k5", "k3_whole_map"])
 @pytest.mark.parametrize("path", ["auto", "tiled"])
 @pytest.mark.parametrize("softmax", [True, False], ids=["dcnv3_gy_outlier", "dcnv4_mask_outlier"])
 def test_backward_outlier_per_tile(softmax, path, ks, monkeypatch):
@@ -713,7 +732,9 @@ def test_backward_outlier_per_tile(softmax, path, ks, monkeypatch):
     and |mask|); the outliers' own offset and mask rows to 1e-4 of their
     largest value, and every other offset and mask gradient to 1e-4."""
     monkeypatch.setenv("DCN_MI355X_BWD_PATH", path)
-    wl = Workload("outlier", n=2, h=48, w=40, c=32, groups=2, softmax=softmax, kernel=(ks, ks),
+    hw = (24, 24) if ks == "map" else (48, 40)  # 24x24: the whole-map kernel, its items on atomics
+    ks = 3 if ks == "map" else ks
+    wl = Workload("outlier", n=2, h=hw[0], w=hw[1], c=32, groups=2, softmax=softmax, kernel=(ks, ks),
                   pad=(ks // 2, ks // 2), mask_dist=normal(1.0 if softmax else 0.5), offset_dist=normal(1.5),
                   seed=48)
     t = synth.make_inputs(wl, with_grad=True)
@@ -759,6 +780,26 @@ def test_backward_outlier_per_tile(softmax, path, ks, monkeypatch):
         assert e[~rows].max() <= ATOL_F32, f"{name} of ordinary pixel-groups: {e[~rows].max():.3e}"
         rowmax = np.maximum(1.0, r[rows].max(axis=-1, keepdims=True))
         assert np.all(e[rows] <= 1e-4 * rowmax), f"{name} of the outliers"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_backward_whole_map_atomic_items_16bit(dtype):
+    """16-bit I/O on the whole-map backward with a few grad_output rows
+    scaled by 1000: those items' terms are too spread for fixed point, so
+    they clear their slice of the caller's fp32 workspace, add there with
+    fp32 atomics and round the slice into grad_input; every gradient within
+    the 16-bit bar of the oracle."""
+    wl = Workload("map_atomics", n=2, h=20, w=17, c=48, groups=3, dtype=dtype, offset_dist=normal(2.0), seed=63)
+    t = synth.make_inputs(wl, with_grad=True)
+    ho, wo = wl.out_hw
+    for (n, y, x, g) in ((0, 3, 4, 0), (0, 15, 11, 1), (1, 8, 2, 2), (1, 19, 16, 0)):
+        t["grad_out"][n, y, x, 16 * g:16 * g + 16] *= 1000
+    print(f"backward whole-map atomic items {dtype}", flush=True)
+    gx, goff, gm = run_backward(wl, t)
+    rx, roff, rm = oracle_backward(wl, t)
+    gate(_np(gx), rx, dtype, f"map atomics {dtype} grad_input")
+    gate(_np(goff), roff, dtype, f"map atomics {dtype} grad_offset")
+    gate(_np(gm), rm, dtype, f"map atomics {dtype} grad_mask")
 
 
 def test_nan_offset_poisons_only_its_group():
