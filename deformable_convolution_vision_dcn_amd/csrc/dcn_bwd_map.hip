@@ -112,7 +112,12 @@ __global__ void __launch_bounds__(4 * TW * TH, 1) dcn_bwd_map_kernel(BwdParams b
     by[r] = oy - p.PH + q / 3 + 1;
   }
   const uint32_t win_chunk = lbase + sub * 16u;  // this lane's 4 channels of a window pixel
-  const uint32_t gwin_chunk = lbase + GWIN + sub * 16u;
+  // The scatter's first 64-bit add of a corner takes the lane's first channel
+  // pair in even quads and its second pair in odd ones, so the four quads of
+  // a 16-lane group spread over twice as many LDS banks (the layout is the
+  // same: pair 0 at +0, pair 1 at +8 of the lane's 16 bytes).
+  const uint32_t podd = quad & 1u;
+  const uint32_t gwin_chunk = lbase + GWIN + sub * 16u + 8u * podd;
 
   // The grad window starts at zero; every item's flush clears it again.  The
   // zero block after the input window is written once.
@@ -368,6 +373,8 @@ __global__ void __launch_bounds__(4 * TW * TH, 1) dcn_bwd_map_kernel(BwdParams b
       float2 offs[P];
       weights(std::integral_constant<int, 0>{}, m);
       unpack<DT, NWL>(rg[0], gy);
+      // grad_output in the scatter's pair order
+      const float gys[4] = {podd ? gy[2] : gy[0], podd ? gy[3] : gy[1], podd ? gy[0] : gy[2], podd ? gy[1] : gy[3]};
 #pragma unroll
       for (int r = 0; r < P; ++r) {
         if constexpr (DT == DCN_F32)
@@ -429,17 +436,17 @@ __global__ void __launch_bounds__(4 * TW * TH, 1) dcn_bwd_map_kernel(BwdParams b
           // Scatter m_k * w_corner * gy_c of this lane's 4 channels (no
           // branch: samples off the map add into the sink).
           if (fixed) {  // block-uniform
-            const uint32_t d = add_bcast<O>(AS, gwin_chunk);
-            auto corner = [&](float w, uint32_t at) {
+            const uint32_t d = add_bcast<O>(AS, gwin_chunk), d2 = d ^ 8u;  // the lane's first and second pair
+            auto corner = [&](float w, uint32_t off) {
               float t[4];
-              mul4_bcast<O>(t, w, gy);
-              lds_add_pair(at, cvt_rpi(t[0]), cvt_rpi(t[1]));
-              lds_add_pair(at + 8, cvt_rpi(t[2]), cvt_rpi(t[3]));
+              mul4_bcast<O>(t, w, gys);
+              lds_add_pair(d + off, cvt_rpi(t[0]), cvt_rpi(t[1]));
+              lds_add_pair(d2 + off, cvt_rpi(t[2]), cvt_rpi(t[3]));
             };
-            corner(W0s, d);
-            corner(W1s, d + PIXB);
-            corner(W2s, d + ROW);
-            corner(W3s, d + ROW + PIXB);
+            corner(W0s, 0u);
+            corner(W1s, PIXB);
+            corner(W2s, ROW);
+            corner(W3s, ROW + PIXB);
           }
           if (gs_any) {
             if (qbcast<O>((int)gscat)) {  // the whole quad follows its owner
