@@ -153,7 +153,14 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
     }
   }
   const uint32_t win_chunk = lbase + sub * 16u;          // this lane's 4 channels of a window pixel
-  const uint32_t gwin_chunk = lbase + GWIN + sub * 16u;
+  // The scatter's first 64-bit add of a corner takes the lane's first channel
+  // pair in even quads and its second pair in odd ones, so the four quads of
+  // a 16-lane group spread over twice as many LDS banks (the layout is the
+  // same: pair 0 at +0, pair 1 at +8 of the lane's 16 bytes).  Not for fp32
+  // 3x3 points, whose 1024-thread tiles have no registers to spare for it.
+  constexpr bool ALT = DT != DCN_F32 || KS == 5;
+  const uint32_t podd = ALT ? (quad & 1u) : 0u;
+  const uint32_t gwin_chunk = lbase + GWIN + sub * 16u + 8u * podd;
 
   // The grad window starts at zero; every item's flush clears it again.  The
   // zero block after the input window is written once.  The first barrier of
@@ -330,6 +337,8 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
       lgs[r] = has_slot(r) ? io::lo(rl[r]) : (SOFTMAX ? -INFINITY : 0.f);
     }
     unpack<DT, NWL>(rg, gy);
+    // grad_output in the scatter's pair order
+    const float gys[4] = {podd ? gy[2] : gy[0], podd ? gy[3] : gy[1], podd ? gy[0] : gy[2], podd ? gy[1] : gy[3]};
     if constexpr (SOFTMAX) {
       float mx = lgs[0];
 #pragma unroll
@@ -522,17 +531,18 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
         // Scatter m_k * w_corner * gy_c of this lane's 4 channels (no
         // branch: samples the window does not hold add into the sink).
         if (fixed) {  // block-uniform
-          const uint32_t d = add_bcast<O>(AS, gwin_chunk);
-          auto corner = [&](float w, uint32_t at) {
+          const uint32_t d = add_bcast<O>(AS, gwin_chunk);  // the lane's first pair
+          const uint32_t d2 = ALT ? (d ^ 8u) : d + 8u;              // and its second
+          auto corner = [&](float w, uint32_t off) {
             float t[4];
-            mul4_bcast<O>(t, w, gy);
-            lds_add_pair(at, cvt_rpi(t[0]), cvt_rpi(t[1]));
-            lds_add_pair(at + 8, cvt_rpi(t[2]), cvt_rpi(t[3]));
+            mul4_bcast<O>(t, w, gys);
+            lds_add_pair(d + off, cvt_rpi(t[0]), cvt_rpi(t[1]));
+            lds_add_pair(d2 + off, cvt_rpi(t[2]), cvt_rpi(t[3]));
           };
-          corner(W0s, d);
-          corner(W1s, d + PIXB);
-          corner(W2s, d + ROW);
-          corner(W3s, d + ROW + PIXB);
+          corner(W0s, 0u);
+          corner(W1s, PIXB);
+          corner(W2s, ROW);
+          corner(W3s, ROW + PIXB);
         }
         if (gs_any) {
           if (qbcast<O>((int)gscat)) {
