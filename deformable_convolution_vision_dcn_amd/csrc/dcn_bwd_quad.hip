@@ -157,8 +157,8 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
   // pair in even quads and its second pair in odd ones, so the four quads of
   // a 16-lane group spread over twice as many LDS banks (the layout is the
   // same: pair 0 at +0, pair 1 at +8 of the lane's 16 bytes).  Not for fp32
-  // 3x3 points, whose 1024-thread tiles have no registers to spare for it.
-  constexpr bool ALT = DT != DCN_F32 || KS == 5;
+  // at stride 2, where it measured slower.
+  constexpr bool ALT = !(DT == DCN_F32 && ST == 2);
   const uint32_t podd = ALT ? (quad & 1u) : 0u;
   const uint32_t gwin_chunk = lbase + GWIN + sub * 16u + 8u * podd;
 
@@ -409,7 +409,8 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
     int ex = 0;
     frexpf(B, &ex);
     ex = ex < -96 ? -96 : ex;
-    const float S = ldexpf(1.f, 30 - ex), invS = ldexpf(1.f, ex - 30);
+    // (an item off fixed point keeps its weights unscaled: S = 1)
+    const float S = fixed ? ldexpf(1.f, 30 - ex) : 1.f, invS = fixed ? ldexpf(1.f, ex - 30) : 1.f;
 
     const uint32_t next = item + walk.stride;
     const bool more = next < end;  // block-uniform
@@ -441,7 +442,8 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
       const float wy1 = ly * mk, wy0 = mk - wy1;
       const float W1 = wy0 * lx, W0 = wy0 - W1;
       const float W3 = wy1 * lx, W2 = wy1 - W3;
-      // scaled to the fixed-point grid for the LDS scatter
+      // scaled to the fixed-point grid for the LDS scatter (the global path
+      // scales them back: powers of two, so exactly)
       const float W0s = W0 * S, W1s = W1 * S, W2s = W2 * S, W3s = W3 * S;
       // outside the window but touching the map: global gathers and atomics
       const bool fb = cur.live && !inside && !nan_loc && (uint32_t)(cur.Y0 + 1 + ty) <= (uint32_t)p.H &&
@@ -548,7 +550,8 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
           if (qbcast<O>((int)gscat)) {
             uint32_t ga[4];
             corners(ga);
-            const float wc[4] = {qbcast<O>(W0), qbcast<O>(W1), qbcast<O>(W2), qbcast<O>(W3)};
+            const float wc[4] = {qbcast<O>(W0s) * invS, qbcast<O>(W1s) * invS, qbcast<O>(W2s) * invS,
+                                 qbcast<O>(W3s) * invS};
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
