@@ -1,9 +1,9 @@
 // dcn_bwd_map.hip -- whole-map gfx950 backward kernel of the DCN core for
 // small feature maps (fp32 arithmetic for fp32 and 16-bit I/O): 3x3 kernel
-// points at stride and dilation 1 (the InternImage configuration;
-// wmrh.cn/news/61976, section 二 steps 2-4 and section 三), all nine or the
-// eight left by DCNv4's remove_center (pnsm.cn/news/2029644.html section
-// 3.3).
+// points at dilation 1 and stride 1 (the InternImage configuration;
+// wmrh.cn/news/61976, section 二 steps 2-4 and section 三) or 2 (the DCNv4
+// signature carries the stride), all nine points or the eight left by
+// DCNv4's remove_center (pnsm.cn/news/2029644.html section 3.3).
 //
 // The derivatives are those of the tiled kernels: every in-map corner of a
 // sample receives m_k * w_corner * gy_c; the offset gradient is
@@ -36,13 +36,15 @@ namespace dcn {
 
 constexpr int kBmPixB = 64;  // 16 fp32 channels of a window pixel
 
-// TW x TH output pixels per pass (a quad per pixel), NP passes; the window
-// holds an input map of up to TW x NP*TH pixels and its border.
-template <int TW, int TH, int NP>
+// TW x TH output pixels per pass (a quad per pixel), NP passes, at stride
+// ST; the window holds an input map of up to ST*TW x ST*NP*TH pixels and its
+// border.
+template <int TW, int TH, int NP, int ST>
 struct BmGeom {
+  static_assert(ST == 1 || ST == 2, "stride 1 or 2");
   static constexpr int kThreads = 4 * TW * TH;
   static constexpr int kWaves = kThreads / 64;
-  static constexpr int kSpanW = TW + 2, kSpanH = NP * TH + 2;
+  static constexpr int kSpanW = ST * TW + 2, kSpanH = ST * NP * TH + 2;
   static constexpr int kRow = kSpanW * kBmPixB;
   static constexpr int kWin = kSpanW * kSpanH * kBmPixB;
   static constexpr int kZero = kRow + 2 * kBmPixB;  // zero block after the input window
@@ -54,9 +56,9 @@ struct BmGeom {
 // RC: the centre point is removed (8 points, k -> grid index k + (k >= 4)):
 // each lane owns exactly two points and a pass takes two rounds instead of
 // three.
-template <int DT, bool SOFTMAX, bool RC, int TW, int TH, int NP>
+template <int DT, bool SOFTMAX, bool RC, int TW, int TH, int NP, int ST>
 __global__ void __launch_bounds__(4 * TW * TH, 1) dcn_bwd_map_kernel(BwdParams bp, TileGeom tg) {
-  using G = BmGeom<TW, TH, NP>;
+  using G = BmGeom<TW, TH, NP, ST>;
   const FwdParams &p = bp.f;
   using io = Io<DT>;
   constexpr int EB = io::kBytes;         // bytes per element in memory
@@ -102,14 +104,14 @@ __global__ void __launch_bounds__(4 * TW * TH, 1) dcn_bwd_map_kernel(BwdParams b
 
   // Window position of each own slot's kernel point before its offset in
   // pass 0 (window pixel (y, x) is input pixel (y - 1, x - 1)); a pass moves
-  // it down by TH rows.
+  // it down by ST * TH rows.
   int bx[P], by[P];
 #pragma unroll
   for (int r = 0; r < P; ++r) {
     const int k = r < 2 ? 2 * (int)sub + r : 8;
     const int q = RC ? (r < 2 ? k + (k >= 4) : 4) : k;
-    bx[r] = ox - p.PW + q % 3 + 1;
-    by[r] = oy - p.PH + q / 3 + 1;
+    bx[r] = ox * ST - p.PW + q % 3 + 1;
+    by[r] = oy * ST - p.PH + q / 3 + 1;
   }
   const uint32_t win_chunk = lbase + sub * 16u;  // this lane's 4 channels of a window pixel
   // The scatter's first 64-bit add of a corner takes the lane's first channel
@@ -489,7 +491,7 @@ __global__ void __launch_bounds__(4 * TW * TH, 1) dcn_bwd_map_kernel(BwdParams b
       res[2] = make_float3(0.f, 0.f, 0.f);
 #pragma unroll
       for (int r = 0; r < ROUNDS; ++r)
-        res[r] = round(offs[r], m[r], bx[r], by[r] + pp * TH, r < 2 ? 4 : 1);
+        res[r] = round(offs[r], m[r], bx[r], by[r] + pp * (ST * TH), r < 2 ? 4 : 1);
 
       // Offset and mask gradients of the own slots (a NaN sampling location
       // makes its point's offset gradient and gm NaN).
@@ -603,10 +605,10 @@ __global__ void __launch_bounds__(4 * TW * TH, 1) dcn_bwd_map_kernel(BwdParams b
 
 namespace {
 
-template <int DT, bool SM, bool RC, int TW, int TH, int NP>
+template <int DT, bool SM, bool RC, int TW, int TH, int NP, int ST>
 hipError_t launch_bwd_map(const BwdParams &p, const TileGeom &tg, hipStream_t s) {
-  using G = BmGeom<TW, TH, NP>;
-  auto kern = dcn_bwd_map_kernel<DT, SM, RC, TW, TH, NP>;
+  using G = BmGeom<TW, TH, NP, ST>;
+  auto kern = dcn_bwd_map_kernel<DT, SM, RC, TW, TH, NP, ST>;
   // Set on every launch: the limit is per device and setting it is idempotent.
   const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
@@ -624,13 +626,13 @@ hipError_t launch_bwd_map(const BwdParams &p, const TileGeom &tg, hipStream_t s)
   return hipGetLastError();
 }
 
-template <int TW, int TH, int NP>
+template <int TW, int TH, int NP, int ST>
 hipError_t launch_map_dt(int dtype, int softmax, bool rc, const BwdParams &b, const TileGeom &tg, hipStream_t s) {
 #define DCN_BM_LAUNCH(DT)                                                                      \
-  return softmax ? (rc ? launch_bwd_map<DT, true, true, TW, TH, NP>(b, tg, s)                  \
-                       : launch_bwd_map<DT, true, false, TW, TH, NP>(b, tg, s))                \
-                 : (rc ? launch_bwd_map<DT, false, true, TW, TH, NP>(b, tg, s)                 \
-                       : launch_bwd_map<DT, false, false, TW, TH, NP>(b, tg, s))
+  return softmax ? (rc ? launch_bwd_map<DT, true, true, TW, TH, NP, ST>(b, tg, s)              \
+                       : launch_bwd_map<DT, true, false, TW, TH, NP, ST>(b, tg, s))            \
+                 : (rc ? launch_bwd_map<DT, false, true, TW, TH, NP, ST>(b, tg, s)             \
+                       : launch_bwd_map<DT, false, false, TW, TH, NP, ST>(b, tg, s))
   switch (dtype) {
     case DCN_F32: DCN_BM_LAUNCH(DCN_F32);
     case DCN_F16: DCN_BM_LAUNCH(DCN_F16);
@@ -640,18 +642,20 @@ hipError_t launch_map_dt(int dtype, int softmax, bool rc, const BwdParams &b, co
 #undef DCN_BM_LAUNCH
 }
 
-// Whole-map shapes: (TW, TH, NP) with the input and output maps both within
-// TW x NP*TH; the first that holds the map is taken.
+// Whole-map shapes: (TW, TH, NP, ST) with the output map within TW x NP*TH
+// and the input map within ST*TW x ST*NP*TH; the first that holds the map at
+// its stride is taken.
 struct MapShape {
-  int tw, th, np;
+  int tw, th, np, st;
 };
-constexpr MapShape kMapShapes[] = {{12, 12, 1}, {16, 16, 1}, {24, 8, 3}};
+constexpr MapShape kMapShapes[] = {{12, 12, 1, 1}, {16, 16, 1, 1}, {24, 8, 3, 1}, {12, 12, 1, 2}};
 
 int map_shape(const FwdParams &p) {
-  if (p.KH != 3 || p.KW != 3 || p.SH != 1 || p.SW != 1 || p.DH != 1 || p.DW != 1) return -1;
+  if (p.KH != 3 || p.KW != 3 || p.SH != p.SW || p.DH != 1 || p.DW != 1) return -1;
   for (int i = 0; i < (int)(sizeof(kMapShapes) / sizeof(kMapShapes[0])); ++i) {
     const MapShape m = kMapShapes[i];
-    if (p.W <= m.tw && p.Wo <= m.tw && p.H <= m.th * m.np && p.Ho <= m.th * m.np) return i;
+    if (p.SH == m.st && p.Wo <= m.tw && p.Ho <= m.th * m.np && p.W <= m.st * m.tw && p.H <= m.st * m.th * m.np)
+      return i;
   }
   return -1;
 }
@@ -677,9 +681,10 @@ hipError_t launch_backward_map(int dtype, int softmax, const BwdParams &b, hipSt
   tg.items = (uint32_t)items;
   tg.div_g = make_fast_div((uint32_t)p.G);
   switch (map_shape(p)) {
-    case 0: return launch_map_dt<12, 12, 1>(dtype, softmax, p.RC != 0, b, tg, s);
-    case 1: return launch_map_dt<16, 16, 1>(dtype, softmax, p.RC != 0, b, tg, s);
-    case 2: return launch_map_dt<24, 8, 3>(dtype, softmax, p.RC != 0, b, tg, s);
+    case 0: return launch_map_dt<12, 12, 1, 1>(dtype, softmax, p.RC != 0, b, tg, s);
+    case 1: return launch_map_dt<16, 16, 1, 1>(dtype, softmax, p.RC != 0, b, tg, s);
+    case 2: return launch_map_dt<24, 8, 3, 1>(dtype, softmax, p.RC != 0, b, tg, s);
+    case 3: return launch_map_dt<12, 12, 1, 2>(dtype, softmax, p.RC != 0, b, tg, s);
     default: return hipErrorNotSupported;
   }
 }

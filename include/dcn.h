@@ -61,9 +61,10 @@
  * stride and dilation 1, else the quad kernel); 5x5 points at stride and
  * dilation 1 run the lane kernel in every dtype; everything else (other
  * point sets, windows that do not fit) runs the untiled kernel.  The
- * backward runs the whole-map kernel for 3x3 points at stride and dilation 1
- * where the input and output maps both fit 12x12, 16x16 or 24x24 (one work
- * item per image and group), the tiled quad kernel for other 3x3 problems at
+ * backward runs the whole-map kernel for 3x3 points at dilation 1 where the
+ * input and output maps both fit 12x12, 16x16 or 24x24 at stride 1, or the
+ * input fits 24x24 at stride 2 (one work item per image and group), the
+ * tiled quad kernel for other 3x3 problems at
  * stride 1 or 2 and dilation 1 or 2 and for 5x5 points at stride and
  * dilation 1, else the untiled kernel.  The environment variable
  * DCN_MI355X_FWD_PATH = "generic" | "tiled" (one group per work item) |

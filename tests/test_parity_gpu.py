@@ -336,9 +336,9 @@ BWD_PATH_CASES = [
 
 
 # Maps the whole-map backward takes (a 24x24, 16x16 or 12x12 window with its
-# border): ragged maps smaller than the window, padding 0 and 2 (output map
-# smaller or larger than the input), remove_center, DCNv4 masks and offsets
-# that leave the map.
+# border, or a 24x24 one at stride 2): ragged maps smaller than the window,
+# padding 0 and 2 (output map smaller or larger than the input), remove_center,
+# DCNv4 masks and offsets that leave the map.
 BWD_MAP_CASES = [
     Workload("bwdp_map_ragged", n=2, h=20, w=17, c=48, groups=3, offset_dist=uniform(4.0), seed=59),
     Workload("bwdp_map_pad2_v4", n=2, h=10, w=9, c=32, groups=2, pad=(2, 2), softmax=False,
@@ -346,6 +346,9 @@ BWD_MAP_CASES = [
     Workload("bwdp_map16_rc_far", n=1, h=15, w=16, c=32, groups=2, remove_center=True,
              offset_dist=uniform(9.0), seed=61),
     Workload("bwdp_map_pad0", n=2, h=24, w=24, c=16, groups=1, pad=(0, 0), offset_dist=normal(3.0), seed=62),
+    Workload("bwdp_map_s2", n=2, h=23, w=21, c=32, groups=2, stride=(2, 2), offset_dist=uniform(4.0), seed=64),
+    Workload("bwdp_map_s2_rc_v4", n=1, h=24, w=24, c=48, groups=3, stride=(2, 2), softmax=False,
+             mask_dist=normal(0.5), remove_center=True, offset_dist=normal(2.0), seed=65),
 ]
 
 
