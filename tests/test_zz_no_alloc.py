@@ -76,6 +76,33 @@ def test_noalloc_matches_backward_on_two_calls(first, second):
                 gate(_np(g), r, wl.dtype, f"{wl.name} noalloc {name}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_noalloc_whole_map_items_on_atomics(dtype):
+    """Small maps run the whole-map backward, whose items off fixed point add
+    their terms into the fixed scratch (each first clearing its own slice):
+    a few grad_output rows scaled by 2000 send items there, on two calls in a
+    row, the second smaller and of another shape; each call against
+    dcn_backward and the oracle."""
+    wls = (Workload("na_map_24", n=4, h=24, w=24, c=64, groups=4, dtype=dtype, offset_dist=uniform(3.0), seed=85),
+           Workload("na_map_12", n=2, h=12, w=11, c=32, groups=2, dtype=dtype, softmax=False,
+                    mask_dist=normal(0.5), offset_dist=normal(2.0), seed=86))
+    for wl in wls:
+        print(f"noalloc whole-map backward {wl.name} {dtype}", flush=True)
+        t = synth.make_inputs(wl, with_grad=True)
+        for n in range(wl.n):
+            t["grad_out"][n, 3 + n, 4, :16] *= 2000  # group 0 of image n off fixed point
+        ins = {k: v.to(DEV) for k, v in t.items()}
+        outs = (torch.full_like(ins["x"], 7.0), torch.full_like(ins["offset"], 7.0),
+                torch.full_like(ins["mask"], 7.0))
+        _call_noalloc(wl, ins, outs)
+        ref = dcn.dcn_backward(ins["x"], ins["offset"], ins["mask"], ins["grad_out"], **wl.op_kwargs())
+        torch.cuda.synchronize()
+        _check_pair(wl, ins, outs, ref)
+        rx, roff, rm = oracle_backward(wl, t)
+        for g, r, name in zip(outs, (rx, roff, rm), ("grad_input", "grad_offset", "grad_mask")):
+            gate(_np(g), r, wl.dtype, f"{wl.name} noalloc {name}")
+
+
 def test_noalloc_python_entry_point_and_scratch_limit():
     """The binding's dcn_backward_noalloc gives the same gradients, and a
     16-bit image whose fp32 accumulator exceeds the scratch is refused with
