@@ -412,22 +412,36 @@ __global__ void __launch_bounds__(4 * TW * TH, 1) dcn_bwd_map_kernel(BwdParams b
         const bool gs_any = __builtin_amdgcn_ballot_w64(gscat) != 0;  // wave-uniform
         float Gown[4] = {0.f, 0.f, 0.f, 0.f};  // the quad's corner sums of this lane's own point
 
-        auto point = [&](auto o_tag) {
+        // Gather this lane's 4 channels of the four corners of the point of
+        // lane O (input window; the corners 00, 01, 10, 11 in q[0..3],
+        // q[4..7], ...).  A point's gather is issued before the previous
+        // point's scatter: the two touch different windows, and the compiler
+        // would not move reads across the LDS atomics by itself.
+        auto gather = [&](auto o_tag, uint32_t (&q)[16]) {
           constexpr int O = decltype(o_tag)::value;
-          // Gather this lane's 4 channels of the owner's four corners.
           const uint32_t src = add_bcast<O>(A, win_chunk);
           uint32_t q00[4], q01[4], q10[4], q11[4];
           lds_load_at<4>(src, q00);
           lds_load_at<4>(src + PIXB, q01);
           lds_load_at<4>(src + ROW, q10);
           lds_load_at<4>(src + ROW + PIXB, q11);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            q[c] = q00[c];
+            q[4 + c] = q01[c];
+            q[8 + c] = q10[c];
+            q[12 + c] = q11[c];
+          }
+        };
+        auto point = [&](auto o_tag, const uint32_t (&q)[16]) {
+          constexpr int O = decltype(o_tag)::value;
           float Pc[4] = {0.f, 0.f, 0.f, 0.f};  // corners 00, 01, 10, 11
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            Pc[0] = fmaf(gy[c], __uint_as_float(q00[c]), Pc[0]);
-            Pc[1] = fmaf(gy[c], __uint_as_float(q01[c]), Pc[1]);
-            Pc[2] = fmaf(gy[c], __uint_as_float(q10[c]), Pc[2]);
-            Pc[3] = fmaf(gy[c], __uint_as_float(q11[c]), Pc[3]);
+            Pc[0] = fmaf(gy[c], __uint_as_float(q[c]), Pc[0]);
+            Pc[1] = fmaf(gy[c], __uint_as_float(q[4 + c]), Pc[1]);
+            Pc[2] = fmaf(gy[c], __uint_as_float(q[8 + c]), Pc[2]);
+            Pc[3] = fmaf(gy[c], __uint_as_float(q[12 + c]), Pc[3]);
           }
           // Sums over the 16 channels: every lane of the quad gets them; the
           // owner keeps them (selects, no branch) for after the round.
@@ -475,10 +489,15 @@ __global__ void __launch_bounds__(4 * TW * TH, 1) dcn_bwd_map_kernel(BwdParams b
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, 2>;
         using I3 = std::integral_constant<int, 3>;
-        point(I0{});
-        if (owners > 1) point(I1{});
-        if (owners > 2) point(I2{});
-        if (owners > 3) point(I3{});
+        uint32_t qa[16], qb[16];
+        gather(I0{}, qa);
+        if (owners > 1) gather(I1{}, qb);
+        point(I0{}, qa);
+        if (owners > 2) gather(I2{}, qa);
+        if (owners > 1) point(I1{}, qb);
+        if (owners > 3) gather(I3{}, qb);
+        if (owners > 2) point(I2{}, qa);
+        if (owners > 3) point(I3{}, qb);
         // gm, d/dx and d/dy of the own point (one-sided derivatives of the
         // bilinear form, linear in the corner sums); a lane without a point
         // this round returns values nobody stores.
