@@ -103,6 +103,34 @@ def test_noalloc_whole_map_items_on_atomics(dtype):
             gate(_np(g), r, wl.dtype, f"{wl.name} noalloc {name}")
 
 
+def test_noalloc_whole_map_in_chunks():
+    """A stage-3-shaped bf16 batch of 100 images (24x24, C = 640) runs the
+    whole-map backward in three chunks through the fixed scratch (45 images
+    of fp32 accumulator a chunk), dcn_backward in one: the gradients are
+    equal bit for bit (integer sums, plain stores), and two images of each
+    chunk match the oracle."""
+    wl = Workload("na_map_chunks", n=100, h=24, w=24, c=640, groups=40, dtype="bf16", offset_dist=uniform(3.0),
+                  seed=87)
+    t = synth.make_inputs(wl, with_grad=True)
+    ins = {k: v.to(DEV) for k, v in t.items()}
+    per_chunk = _capi.NOALLOC_SCRATCH_BYTES // (wl.h * wl.w * wl.c * 4)
+    assert per_chunk < wl.n < 3 * per_chunk, per_chunk
+    print(f"noalloc whole-map backward in chunks of {per_chunk} images", flush=True)
+    outs = (torch.full_like(ins["x"], 7.0), torch.full_like(ins["offset"], 7.0),
+            torch.full_like(ins["mask"], 7.0))
+    _call_noalloc(wl, ins, outs)
+    ref = dcn.dcn_backward(ins["x"], ins["offset"], ins["mask"], ins["grad_out"], **wl.op_kwargs())
+    torch.cuda.synchronize()
+    for g, r, name in zip(outs, ref, ("grad_input", "grad_offset", "grad_mask")):
+        assert torch.equal(g, r), f"{name} differs between the chunked and the single call"
+    for n in (0, per_chunk - 1, per_chunk, 2 * per_chunk, wl.n - 1):
+        one = wl.replace(n=1)
+        tn = {k: v[n:n + 1] for k, v in t.items()}
+        rx, roff, rm = oracle_backward(one, tn)
+        for g, r, name in zip(outs, (rx, roff, rm), ("grad_input", "grad_offset", "grad_mask")):
+            gate(_np(g[n:n + 1]), r, wl.dtype, f"image {n} {name}")
+
+
 def test_noalloc_python_entry_point_and_scratch_limit():
     """The binding's dcn_backward_noalloc gives the same gradients, and a
     16-bit image whose fp32 accumulator exceeds the scratch is refused with
