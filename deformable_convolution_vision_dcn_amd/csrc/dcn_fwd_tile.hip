@@ -20,7 +20,9 @@
 //
 // Per pixel-group one quad: lane `sub` owns channels [4*sub, 4*sub+4) and
 // computes the location, bilinear weights (modulation folded in) and LDS
-// address of the kernel points k = 2 sub, 2 sub + 1 (and k = 8 for sub 0);
+// address of the kernel points k = 2 sub, 2 sub + 1 (and k = 8 for sub 0;
+// in fp32 group pairs the second group's quad owns 2 sub + 1, 2 sub + 2 and,
+// in lane 0, k = 0, see the row loads);
 // DPP quad broadcasts hand them to the other three lanes, so no lane repeats
 // another's address math.  Each lane then reads its 16-byte chunk of the four corners and does
 // 4 FMAs per channel per point.  The softmax over the nine logits is a quad
@@ -86,6 +88,9 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   constexpr int WPIX = THREADS / LPP;              // window pixels per slice
   constexpr int MAXPQ = (tile_max_span<GP>() + WPIX - 1) / WPIX;  // slices per lane
   constexpr int K = RC ? 8 : 9;
+  // fp32 group pairs of nine points: the quads of the pair's two groups split
+  // its 144-byte offset row at the middle chunk (see the row loads).
+  constexpr bool SPLIT = DT == DCN_F32 && GP == 2 && !RC;
   static_assert(PASSES == 1 || PASSES == 2, "one or two passes per item");
   static_assert(PIXB % LANE_BYTES == 0 && PIXB % 8 == 0 && PIXB >= GP * 4 * LANE_BYTES, "pixel stride");
   static_assert(GP == 1 || GP == 2, "one or two groups per item");
@@ -165,11 +170,13 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   // offset, for pass 0 (pass 1 adds PIXPP / TW output rows), packed as three
   // 10-bit fields (every coordinate is below the span, at most 1023).  The
   // output pixel of the quad is (pix / TW, pix % TW) within its pass; slot r
-  // holds k = 2 sub + r (r < 2) or k = 8 (no point with RC), at grid index q.
+  // holds k = 2 sub + r (r < 2) or k = 8 (no point with RC), at grid index q;
+  // with SPLIT the second group's quad holds k = 2 sub + r + 1 and k = 0.
+  const int kshift = SPLIT ? (int)gsel : 0;
   uint32_t bxp = 0, byp = 0;
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
-    const int k = r < 2 ? 2 * (int)sub + r : 8;
+    const int k = r < 2 ? 2 * (int)sub + r + kshift : (kshift ? 0 : 8);
     const int q = RC ? (r < 2 ? k + (k >= 4) : 4) : k;
     const int i = q / 3, j = q - 3 * (q / 3);
     bxp |= (uint32_t)((int)(pix % TW) * SW + R + j * DW) << (10 * r);
@@ -265,8 +272,9 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
 
   // Own points' offsets and logits of both passes: the quad owns output
   // pixel pp = ps*PIXPP + pix of the tile, group g + gsel; lane `sub` owns the
-  // points k = 2 sub, 2 sub + 1 (slots 0, 1) and lane 0 also k = 8 (slot 2),
-  // so a quad reads its pixel-group's offset and mask rows contiguously.
+  // points k = 2 sub, 2 sub + 1 (slots 0, 1) and lane 0 also k = 8 (slot 2)
+  // (SPLIT below shifts the second group's by one), so a quad reads its
+  // pixel-group's offset and mask rows contiguously.
   // The rows are kept as loaded (raw words) and decoded where they are used:
   // any arithmetic on them here would make the wave wait for the load at
   // once.  Every lane loads every slot (a dead quad reads row 0), so the
@@ -274,10 +282,35 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   //   fp32:   rw = x, y of k = 2 sub; x, y of 2 sub + 1; x, y of k = 8;
   //           rl = logits of 2 sub, 2 sub + 1, 8.
   //   16-bit: rw = (x, y) words of 2 sub, 2 sub + 1, 8; rl = logit halves.
+  //   SPLIT:  rw = x, y of the quad's points 2 sub + gsel, 2 sub + gsel + 1
+  //           and of its slot-2 point (8 or 0); rl = the group's logits
+  //           2 sub, 2 sub + 1, 2 sub + 2.
+  // SPLIT: a pixel's pair of offset rows is 144 contiguous bytes, nine
+  // 16-byte chunks.  The first group's quad reads chunks 0-3 (its points
+  // 0-7), the second group's quad chunks 5-8 (its points 1-8), and chunk 4
+  // holds the first group's point 8 and the second's point 0, one line for
+  // every pixel; the logits take one 12-byte load per lane.  Per wave that
+  // is three row loads touching about 4.6 lines per pixel instead of four
+  // touching about 6.5, and the address unit's time goes with its line
+  // count.  Lane 0 of the first group takes its ninth logit from lane 3.
   constexpr int NRW = DT == DCN_F32 ? 6 : 3;
   uint32_t rw[PASSES][NRW], rl[PASSES][3];
   auto load_rows = [&](uint32_t pg, uint32_t (&w)[NRW], uint32_t (&l)[3]) {
-    if constexpr (DT == DCN_F32) {
+    if constexpr (SPLIT) {
+      const uint32_t orow = pg * 72u, mrow = pg * 36u;
+      const auto o = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(orow + 16 * sub + 8 * gsel), 0, 0);
+      const auto o8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(gsel ? orow : orow + 64), 0, 0);
+      const auto lg = __builtin_amdgcn_raw_buffer_load_b96(rmask, (int)(mrow + 8 * sub), 0, 0);
+      w[0] = o[0];
+      w[1] = o[1];
+      w[2] = o[2];
+      w[3] = o[3];
+      w[4] = o8[0];
+      w[5] = o8[1];
+      l[0] = lg[0];
+      l[1] = lg[1];
+      l[2] = lg[2];
+    } else if constexpr (DT == DCN_F32) {
       const uint32_t orow = pg * (K * 8), mrow = pg * (K * 4);
       const auto o = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(orow + 16 * sub), 0, 0);
       const auto lg = __builtin_amdgcn_raw_buffer_load_b64(rmask, (int)(mrow + 8 * sub), 0, 0);
@@ -323,7 +356,14 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
   };
   // Decoded offsets (x, y) and logits of three slots.
   auto decode_rows = [&](const uint32_t (&w)[NRW], const uint32_t (&l)[3], float2 (&o)[3], float (&lg)[3]) {
-    if constexpr (DT == DCN_F32) {
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int r = 0; r < 3; ++r) o[r] = make_float2(__uint_as_float(w[2 * r]), __uint_as_float(w[2 * r + 1]));
+      const uint32_t l8 = (uint32_t)qbcast<3>((int)l[2]);  // the first group's logit 8 (all four lanes live)
+      lg[0] = __uint_as_float(gsel ? l[1] : l[0]);
+      lg[1] = __uint_as_float(gsel ? l[2] : l[1]);
+      lg[2] = __uint_as_float(gsel ? l[0] : l8);
+    } else if constexpr (DT == DCN_F32) {
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
         o[r] = make_float2(__uint_as_float(w[2 * r]), __uint_as_float(w[2 * r + 1]));
@@ -375,7 +415,7 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
       float2 offs[3];
       float lgs[3], m[3];
       decode_rows(rw[ps], rl[ps], offs, lgs);
-      if (RC || sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 only
+      if (RC || sub != 0) lgs[2] = SOFTMAX ? -INFINITY : 0.f;  // slot 2 is lane 0's point 8 (or 0) only
       if constexpr (SOFTMAX) {
         const float mx = quad_max(fmaxf(fmaxf(lgs[0], lgs[1]), lgs[2]));
         float e[3];
@@ -470,7 +510,7 @@ __global__ void __launch_bounds__(512 * GP, DCN_TILE_WAVES) dcn_fwd_tile_kernel(
         using I2 = std::integral_constant<int, 2>;
         using I3 = std::integral_constant<int, 3>;
         point(I0{});
-        if constexpr (r < 2) {  // the last round holds only k = 8 (owner lane 0)
+        if constexpr (r < 2) {  // the last round holds only lane 0's slot-2 point
           point(I1{});
           point(I2{});
           point(I3{});
