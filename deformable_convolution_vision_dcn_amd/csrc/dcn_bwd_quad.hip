@@ -236,7 +236,8 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
     }
   };
   // Raw rows as loaded (decoded where used).  fp32: rw = x, y of k = 2 sub;
-  // x, y of 2 sub + 1; x, y of 8; rl = logits of 2 sub, 2 sub + 1, 8; rg =
+  // x, y of 2 sub + 1; x, y of 8; rl = logits of 2 sub, 2 sub + 1, 2 sub + 2
+  // (lane 3: logit 8; with RC logits 2 sub, 2 sub + 1 and 0); rg =
   // grad_output of the lane's 4 channels.  16-bit: rw = (x, y) words of
   // 2 sub, 2 sub + 1, 8; rl = the three logits (low halves); rg = two words.
   constexpr int NRW = DT == DCN_F32 ? 2 * P : P;
@@ -267,21 +268,27 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
     if constexpr (DT == DCN_F32) {
       const uint32_t orow = I.pg * (K * 8), mrow = I.pg * (K * 4);
       const auto o = __builtin_amdgcn_raw_buffer_load_b128(roff, (int)(orow + 16 * sub), 0, 0);
-      const auto lg = __builtin_amdgcn_raw_buffer_load_b64(rmask, (int)(mrow + 8 * sub), 0, 0);
       if constexpr (RC) {
+        const auto lg = __builtin_amdgcn_raw_buffer_load_b64(rmask, (int)(mrow + 8 * sub), 0, 0);
         rw[4] = rw[5] = rl[2] = 0u;
+        rl[0] = lg[0];
+        rl[1] = lg[1];
       } else {
+        // logits 2 sub, 2 sub + 1, 2 sub + 2 in one load: lane 3's third is
+        // logit 8, which lane 0 takes from it by DPP when the rows are decoded
+        // (one row load fewer per lane than a separate load of logit 8)
+        const auto lg = __builtin_amdgcn_raw_buffer_load_b96(rmask, (int)(mrow + 8 * sub), 0, 0);
         const auto o8 = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 64), 0, 0);
-        rl[2] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (int)(mrow + 32), 0, 0);
         rw[4] = o8[0];
         rw[5] = o8[1];
+        rl[0] = lg[0];
+        rl[1] = lg[1];
+        rl[2] = lg[2];
       }
       rw[0] = o[0];
       rw[1] = o[1];
       rw[2] = o[2];
       rw[3] = o[3];
-      rl[0] = lg[0];
-      rl[1] = lg[1];
     } else {
       const uint32_t orow = I.pg * (K * 4), mrow = I.pg * (K * 2);
       const auto o = __builtin_amdgcn_raw_buffer_load_b64(roff, (int)(orow + 8 * sub), 0, 0);
@@ -331,6 +338,7 @@ __global__ void __launch_bounds__(4 * TW * TH, (TW * TH) / 64) dcn_bwd_quad_kern
       else
         return make_float2(io::lo(rw[r]), io::hi(rw[r]));
     };
+    if constexpr (KS == 3 && DT == DCN_F32 && !RC) rl[2] = (uint32_t)qbcast<3>((int)rl[2]);  // logit 8 from lane 3
 #pragma unroll
     for (int r = 0; r < P; ++r) {
       if constexpr (KS == 3) offs[r] = slot_offset(r);
