@@ -961,3 +961,38 @@ def test_concurrent_calls_from_two_threads():
     assert not errors, errors
     for i in range(2):
         assert np.array_equal(got[i], ref[i]), f"thread {i}"
+
+
+# Each group's mask is dominated by one point: DCNv3 logits 0 at that point
+# and -30 elsewhere (a softmax weight of 1 - 8e-13), DCNv4 a one-hot mask.
+# The pairs cover the points that the group-pair kernels assign specially
+# (the first group's point 8 and the second group's point 0 ride in one
+# 16-byte chunk; lane 0 takes logit 8 from lane 3), so a point read from the
+# wrong group, slot or lane shows as a wrong sample, not a small drift.
+DOMINANT = [(8, 0), (0, 8), (8, 8), (0, 0), (4, 4), (7, 1), (1, 7)]
+
+
+def _dominated_mask(wl, t, points, softmax):
+    m = torch.full_like(t["mask"], -30.0 if softmax else 0.0)
+    for g in range(wl.groups):
+        m[..., g, points[g % 2]] = 0.0 if softmax else 1.0
+    return m
+
+
+@pytest.mark.parametrize("softmax", [True, False], ids=["dcnv3", "dcnv4"])
+@pytest.mark.parametrize("groups", [2, 4])
+@pytest.mark.parametrize("points", DOMINANT, ids=lambda p: f"p{p[0]}_{p[1]}")
+def test_pair_kernels_point_ownership(points, groups, softmax, monkeypatch):
+    wl = Workload("own", n=1, h=21, w=19, c=16 * groups, groups=groups, softmax=softmax,
+                  offset_dist=normal(2.0), seed=60 + groups)
+    print(f"ownership {points} groups={groups} softmax={softmax}", flush=True)
+    t = synth.make_inputs(wl, with_grad=True)
+    t["mask"] = _dominated_mask(wl, t, points, softmax)
+    monkeypatch.setenv("DCN_MI355X_FWD_PATH", "pair")
+    gate(_np(run_forward(wl, t)), oracle_full(wl, t), "f32", f"own {points} forward")
+    monkeypatch.setenv("DCN_MI355X_BWD_PATH", "quad")
+    gx, goff, gm = run_backward(wl, t)
+    rx, roff, rm = oracle_backward(wl, t)
+    gate(_np(gx), rx, "f32", f"own {points} grad_input")
+    gate(_np(goff), roff, "f32", f"own {points} grad_offset")
+    gate(_np(gm), rm, "f32", f"own {points} grad_mask")
